@@ -1,0 +1,203 @@
+"""fp8q oracle -- TEST INFRASTRUCTURE ONLY.
+
+ctypes wrapper around ``liboracle.so`` (built from ``fp8q_oracle.c`` with the
+host C compiler).  Only ``tests/``, the smoke check and the benchmark's
+CPU-baseline leg may import this package; the GPU product path never does.
+
+Every function takes and returns numpy arrays:
+
+* ``quant_act(x_bf16[M,K] uint16) -> (codes[M,K] uint8, scale[M,K/128] f32)``
+* ``scale_to_kmajor(scale_rm[M,G] f32) -> km[G, ceil16(M)] f32``
+* ``quant_weight_block(w[N,K] f32) -> (codes[N,K] uint8, scale[N/128,K/128] f32)``
+* ``gemm_ref(a, a_s_rm, w, w_s) -> out[M,N] f64``
+* ``gemm_ref_at(a, a_s_rm, w, w_s, ms, ns) -> out[len] f64``
+* ``e4m3_decode(codes) -> f64``, ``e4m3_encode(f32) -> uint8``
+
+See ``fp8q_oracle.c`` for the definitions and the passages they follow.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "fp8q_oracle.c")
+LIB_PATH = os.path.join(_HERE, "liboracle.so")
+
+GROUP = 128
+
+
+def build(force: bool = True) -> str:
+    """Compile liboracle.so with the host C compiler (no fast-math)."""
+    if not force and os.path.exists(LIB_PATH):
+        return LIB_PATH
+    tmp = LIB_PATH + ".tmp"
+    cmd = ["gcc", "-std=c11", "-O2", "-fopenmp", "-ffp-contract=off",
+           "-fno-fast-math", "-fPIC", "-shared", "-o", tmp, _SRC, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, LIB_PATH)
+    return LIB_PATH
+
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        build()
+    lib = ctypes.CDLL(LIB_PATH)
+    P = ctypes.c_void_p
+    I = ctypes.c_int64
+    lib.oracle_e4m3_decode.argtypes = [ctypes.c_uint8]
+    lib.oracle_e4m3_decode.restype = ctypes.c_double
+    lib.oracle_e4m3_encode.argtypes = [ctypes.c_float]
+    lib.oracle_e4m3_encode.restype = ctypes.c_uint8
+    lib.oracle_e4m3_encode_array.argtypes = [P, P, I]
+    lib.oracle_e4m3_encode_array.restype = None
+    lib.oracle_quant_act.argtypes = [P, P, P, I, I]
+    lib.oracle_quant_act.restype = None
+    lib.oracle_act_scales.argtypes = [P, P, I, I]
+    lib.oracle_act_scales.restype = None
+    lib.oracle_m_pad.argtypes = [I]
+    lib.oracle_m_pad.restype = I
+    lib.oracle_scale_to_kmajor.argtypes = [P, P, I, I]
+    lib.oracle_scale_to_kmajor.restype = None
+    lib.oracle_quant_weight_block.argtypes = [P, P, P, I, I]
+    lib.oracle_quant_weight_block.restype = None
+    lib.oracle_gemm_ref.argtypes = [P, P, P, P, P, I, I, I]
+    lib.oracle_gemm_ref.restype = None
+    lib.oracle_gemm_ref_at.argtypes = [P, P, P, P, P, P, P, I, I]
+    lib.oracle_gemm_ref_at.restype = None
+    lib.oracle_num_threads.argtypes = []
+    lib.oracle_num_threads.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _p(a: np.ndarray) -> int:
+    assert a.flags["C_CONTIGUOUS"]
+    return a.ctypes.data
+
+
+def num_threads() -> int:
+    return _load().oracle_num_threads()
+
+
+def m_pad(M: int) -> int:
+    return int(_load().oracle_m_pad(M))
+
+
+def e4m3_decode(codes) -> np.ndarray:
+    lib = _load()
+    c = np.asarray(codes, dtype=np.uint8)
+    table = np.array([lib.oracle_e4m3_decode(i) for i in range(256)])
+    return table[c]
+
+
+def e4m3_encode(q) -> np.ndarray:
+    q = np.ascontiguousarray(q, dtype=np.float32)
+    out = np.empty(q.shape, dtype=np.uint8)
+    _load().oracle_e4m3_encode_array(_p(q), _p(out), q.size)
+    return out
+
+
+def quant_act(x_bf16: np.ndarray):
+    x = np.ascontiguousarray(x_bf16, dtype=np.uint16)
+    M, K = x.shape
+    assert K % GROUP == 0
+    q = np.empty((M, K), dtype=np.uint8)
+    s = np.empty((M, K // GROUP), dtype=np.float32)
+    _load().oracle_quant_act(_p(x), _p(q), _p(s), M, K)
+    return q, s
+
+
+def act_scales(x_bf16: np.ndarray) -> np.ndarray:
+    x = np.ascontiguousarray(x_bf16, dtype=np.uint16)
+    M, K = x.shape
+    s = np.empty((M, K // GROUP), dtype=np.float32)
+    _load().oracle_act_scales(_p(x), _p(s), M, K)
+    return s
+
+
+def scale_to_kmajor(scale_rm: np.ndarray) -> np.ndarray:
+    s = np.ascontiguousarray(scale_rm, dtype=np.float32)
+    M, G = s.shape
+    km = np.empty((G, m_pad(M)), dtype=np.float32)
+    _load().oracle_scale_to_kmajor(_p(s), _p(km), M, G * GROUP)
+    return km
+
+
+def quant_weight_block(w: np.ndarray):
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    N, K = w.shape
+    assert N % GROUP == 0 and K % GROUP == 0
+    q = np.empty((N, K), dtype=np.uint8)
+    s = np.empty((N // GROUP, K // GROUP), dtype=np.float32)
+    _load().oracle_quant_weight_block(_p(w), _p(q), _p(s), N, K)
+    return q, s
+
+
+def gemm_ref(a, a_s_rm, w, w_s) -> np.ndarray:
+    a = np.ascontiguousarray(a, dtype=np.uint8)
+    w = np.ascontiguousarray(w, dtype=np.uint8)
+    a_s = np.ascontiguousarray(a_s_rm, dtype=np.float32)
+    w_s = np.ascontiguousarray(w_s, dtype=np.float32)
+    M, K = a.shape
+    N = w.shape[0]
+    assert w.shape[1] == K and a_s.shape == (M, K // GROUP)
+    assert w_s.shape == (N // GROUP, K // GROUP)
+    out = np.empty((M, N), dtype=np.float64)
+    _load().oracle_gemm_ref(_p(a), _p(a_s), _p(w), _p(w_s), _p(out), M, N, K)
+    return out
+
+
+def gemm_ref_at(a, a_s_rm, w, w_s, ms, ns) -> np.ndarray:
+    a = np.ascontiguousarray(a, dtype=np.uint8)
+    w = np.ascontiguousarray(w, dtype=np.uint8)
+    a_s = np.ascontiguousarray(a_s_rm, dtype=np.float32)
+    w_s = np.ascontiguousarray(w_s, dtype=np.float32)
+    ms = np.ascontiguousarray(ms, dtype=np.int64)
+    ns = np.ascontiguousarray(ns, dtype=np.int64)
+    M, K = a.shape
+    N = w.shape[0]
+    assert ms.shape == ns.shape
+    assert (ms >= 0).all() and (ms < M).all() and (ns >= 0).all() and (ns < N).all()
+    assert a_s.shape == (M, K // GROUP) and w_s.shape == (N // GROUP, K // GROUP)
+    out = np.empty(ms.shape, dtype=np.float64)
+    _load().oracle_gemm_ref_at(_p(a), _p(a_s), _p(w), _p(w_s), _p(ms), _p(ns),
+                               _p(out), ms.size, K)
+    return out
+
+
+# ---------------------------------------------------------------- tolerance
+def bf16_ulp(r: np.ndarray) -> np.ndarray:
+    """ulp of a bf16 number of magnitude |r|: 2^(max(floor(log2|r|), -126) - 7),
+    and 2^-133 (the smallest bf16 subnormal) for r == 0."""
+    r = np.abs(np.asarray(r, dtype=np.float64))
+    with np.errstate(divide="ignore"):
+        e = np.floor(np.log2(np.where(r > 0, r, 1.0)))
+    e = np.maximum(e, -126.0)
+    u = np.ldexp(1.0, (e - 7).astype(np.int64))
+    return np.where(r > 0, u, np.ldexp(1.0, -133))
+
+
+def gemm_errors(out_bf16_as_f64: np.ndarray, ref: np.ndarray, rms_ref: float | None = None):
+    """(rel_rms, worst per-element excess) of a GEMM output against the fp64
+    reference.  ``excess = max(|o-r| / (ulp_bf16(r) + 1e-3*RMS(ref)))``; the
+    accuracy contract is rel_rms <= 1e-3 and excess <= 1."""
+    o = np.asarray(out_bf16_as_f64, dtype=np.float64)
+    r = np.asarray(ref, dtype=np.float64)
+    if rms_ref is None:
+        rms_ref = float(np.sqrt(np.mean(r * r))) if r.size else 0.0
+    d = o - r
+    den = float(np.sum(r * r))
+    rel_rms = float(np.sqrt(np.sum(d * d) / den)) if den > 0 else float(np.sqrt(np.sum(d * d)))
+    bound = bf16_ulp(r) + 1e-3 * rms_ref
+    excess = float(np.max(np.abs(d) / bound)) if r.size else 0.0
+    return rel_rms, excess

@@ -1,0 +1,255 @@
+/*
+ * fp8q oracle -- TEST INFRASTRUCTURE ONLY.
+ *
+ * A plain, slow, obviously correct CPU implementation of the W8A8
+ * block-scaled FP8 projection.  Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load this library; the GPU product path
+ * never calls it and shares no code with it.
+ *
+ * What it computes (sources: the pages "dispatch_proj.rs" and
+ * "fp8_act_quant_floor.rs" of spark_model/layers/ops):
+ *
+ *   quantizer   bf16 activations [M,K] -> OCP FP8 e4m3 codes [M,K] plus one
+ *               fp32 scale per (token, 128-wide K group), row-major [M,K/128]
+ *               (dispatch_proj.rs, doc of cublas_fp8_proj: one scale per token
+ *               and 128 elements of K).  scale = amax/448 in fp32, code =
+ *               e4m3(x/scale) with round-to-nearest-even and saturation at
+ *               +-448.
+ *   relayout    row-major [M,K/128] -> K-major [K/128, ceil16(M)], tokens
+ *               contiguous, pad rows M..ceil16(M) zero (dispatch_proj.rs,
+ *               doc of cublas_scale_layout_kmajor and fp8_act_scale_to_kmajor;
+ *               cublas_fp8_m_pad for ceil16).
+ *   GEMM        out[M,N] = act[M,K] . W[N,K]^T with the activation scale of
+ *               (m, kb) and the weight scale of the 128x128 block (n/128, kb)
+ *               applied to each 128-deep K block (dispatch_proj.rs, doc of
+ *               cublas_fp8_proj: both operands 128-block-scaled; weight scale
+ *               index (n/128)*(K/128) + k/128 from dequant_fp8_bf16_into).
+ *               Computed in fp64 and not rounded.
+ *
+ * Readings where the pages are silent (each one is listed in the design
+ * notes): amax == 0 gives scale 0 and signed-zero codes; the scale is the
+ * IEEE fp32 quotient amax/448 (not amax * (1/448)); q = fl32(x/scale); the
+ * e4m3 variant is OCP e4m3fn (bias 7, max 448, no infinities, 0x7F/0xFF NaN);
+ * no flush of subnormals anywhere; K must be a multiple of 128.
+ *
+ * Build: gcc -O2 -fopenmp -ffp-contract=off (no -ffast-math), x86-64 SSE
+ * math, so every float operation below is a single IEEE-754 binary32 or
+ * binary64 operation rounded to nearest even.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#define GROUP 128
+
+/* ---------------------------------------------------------------- codecs */
+
+static float bf16_to_f32(uint16_t b) {
+  uint32_t u = (uint32_t)b << 16;
+  float f;
+  memcpy(&f, &u, sizeof f);
+  return f;
+}
+
+/* Value of an OCP e4m3fn code: sign, 4-bit exponent (bias 7), 3-bit
+ * mantissa; exponent field 0 is subnormal (m/8 * 2^-6); 0x7F/0xFF is NaN. */
+double oracle_e4m3_decode(uint8_t c) {
+  int s = c >> 7, e = (c >> 3) & 15, m = c & 7;
+  double v;
+  if (e == 15 && m == 7) return NAN;
+  if (e == 0)
+    v = ldexp((double)m / 8.0, -6);
+  else
+    v = ldexp(1.0 + (double)m / 8.0, e - 7);
+  return s ? -v : v;
+}
+
+/* Nearest e4m3fn code to q, ties to the even mantissa, saturating to
+ * +-448 (code 0x7E | sign).  The sign of q (including -0.0) is kept.  All
+ * arithmetic is exact in binary64 so rint() (nearest-even in the default
+ * rounding mode) makes the only rounding decision. */
+uint8_t oracle_e4m3_encode(float q) {
+  uint8_t s = signbit(q) ? 0x80 : 0x00;
+  double a = fabs((double)q);
+  int e;
+  double m;
+  if (a >= 448.0) return (uint8_t)(s | 0x7E);
+  if (a < ldexp(1.0, -6)) {
+    /* subnormal range: multiples of 2^-9; a result of 8 is 2^-6, which is
+     * exactly the code 0x08 (exponent field 1, mantissa 0). */
+    m = rint(a * 512.0);
+    return (uint8_t)(s | (uint8_t)m);
+  }
+  frexp(a, &e); /* a = f * 2^e, f in [0.5, 1) */
+  e -= 1;       /* now a = (1 + t) * 2^e, t in [0, 1) */
+  m = rint((ldexp(a, -e) - 1.0) * 8.0);
+  if (m == 8.0) {
+    e += 1;
+    m = 0.0;
+  }
+  if (e + 7 > 15 || (e + 7 == 15 && m == 7.0)) return (uint8_t)(s | 0x7E);
+  return (uint8_t)(s | (uint8_t)((e + 7) << 3) | (uint8_t)m);
+}
+
+/* Element-wise encode of n floats (test helper). */
+void oracle_e4m3_encode_array(const float *q, uint8_t *out, int64_t n) {
+  int64_t i;
+#pragma omp parallel for schedule(static)
+  for (i = 0; i < n; ++i) out[i] = oracle_e4m3_encode(q[i]);
+}
+
+/* Encode of x relative to scale, the quantizer's per-element step. */
+static uint8_t quant_elem(float x, float scale) {
+  if (scale == 0.0f) return signbit(x) ? 0x80 : 0x00;
+  return oracle_e4m3_encode(x / scale);
+}
+
+/* ------------------------------------------------------------- quantizer */
+
+/* bf16 x[M,K] -> codes q[M,K], scales[M,K/128] (row-major). */
+void oracle_quant_act(const uint16_t *x, uint8_t *q, float *scale, int64_t M,
+                      int64_t K) {
+  const int64_t G = K / GROUP;
+  int64_t r;
+#pragma omp parallel for schedule(static)
+  for (r = 0; r < M * G; ++r) {
+    const int64_t m = r / G, g = r % G;
+    const uint16_t *xs = x + m * K + g * GROUP;
+    uint8_t *qs = q + m * K + g * GROUP;
+    float amax = 0.0f, s;
+    int j;
+    for (j = 0; j < GROUP; ++j) {
+      float v = fabsf(bf16_to_f32(xs[j]));
+      if (v > amax) amax = v;
+    }
+    s = amax / 448.0f;
+    scale[m * G + g] = s;
+    for (j = 0; j < GROUP; ++j) qs[j] = quant_elem(bf16_to_f32(xs[j]), s);
+  }
+}
+
+/* Scales only (the quantizer's second output), for timing samples. */
+void oracle_act_scales(const uint16_t *x, float *scale, int64_t M, int64_t K) {
+  const int64_t G = K / GROUP;
+  int64_t r;
+#pragma omp parallel for schedule(static)
+  for (r = 0; r < M * G; ++r) {
+    const uint16_t *xs = x + (r / G) * K + (r % G) * GROUP;
+    float amax = 0.0f;
+    int j;
+    for (j = 0; j < GROUP; ++j) {
+      float v = fabsf(bf16_to_f32(xs[j]));
+      if (v > amax) amax = v;
+    }
+    scale[r] = amax / 448.0f;
+  }
+}
+
+/* -------------------------------------------------------------- relayout */
+
+int64_t oracle_m_pad(int64_t M) { return (M + 15) / 16 * 16; }
+
+/* row-major [M,G] -> K-major [G, Mp], Mp = ceil16(M), pad slots +0.0f. */
+void oracle_scale_to_kmajor(const float *rm, float *km, int64_t M, int64_t K) {
+  const int64_t G = K / GROUP, Mp = oracle_m_pad(M);
+  int64_t g, m;
+  for (g = 0; g < G; ++g)
+    for (m = 0; m < Mp; ++m) km[g * Mp + m] = (m < M) ? rm[m * G + g] : 0.0f;
+}
+
+/* ------------------------------------------------------ weight quantizer */
+
+/* fp32 W[N,K] -> codes [N,K] and one fp32 scale per 128x128 block,
+ * [N/128, K/128] row-major; scale = block amax / 448 (same element encoder
+ * as the activation quantizer).  Used only to make synthetic FP8 weights. */
+void oracle_quant_weight_block(const float *w, uint8_t *q, float *scale,
+                               int64_t N, int64_t K) {
+  const int64_t NB = N / GROUP, G = K / GROUP;
+  int64_t b;
+#pragma omp parallel for schedule(static)
+  for (b = 0; b < NB * G; ++b) {
+    const int64_t nb = b / G, g = b % G;
+    float amax = 0.0f, s;
+    int i, j;
+    for (i = 0; i < GROUP; ++i)
+      for (j = 0; j < GROUP; ++j) {
+        float v = fabsf(w[(nb * GROUP + i) * K + g * GROUP + j]);
+        if (v > amax) amax = v;
+      }
+    s = amax / 448.0f;
+    scale[b] = s;
+    for (i = 0; i < GROUP; ++i)
+      for (j = 0; j < GROUP; ++j) {
+        const int64_t o = (nb * GROUP + i) * K + g * GROUP + j;
+        q[o] = quant_elem(w[o], s);
+      }
+  }
+}
+
+/* ------------------------------------------------------------------ GEMM */
+
+/* One output element in block form:
+ *   ref[m,n] = sum_g a_s[m,g] * w_s[n/128,g] * S(m,n,g),
+ *   S(m,n,g) = sum_j dec(a[m,128g+j]) * dec(w[n,128g+j])   (exact in fp64).
+ * a_s is the row-major [M, K/128] activation scale. */
+static double gemm_elem(const uint8_t *a, const float *a_s, const uint8_t *w,
+                        const float *w_s, const double *dec, int64_t m,
+                        int64_t n, int64_t K) {
+  const int64_t G = K / GROUP;
+  double acc = 0.0;
+  int64_t g;
+  for (g = 0; g < G; ++g) {
+    const uint8_t *ar = a + m * K + g * GROUP;
+    const uint8_t *wr = w + n * K + g * GROUP;
+    double S = 0.0;
+    int j;
+    for (j = 0; j < GROUP; ++j) S += dec[ar[j]] * dec[wr[j]];
+    acc += (double)a_s[m * G + g] * (double)w_s[(n / GROUP) * G + g] * S;
+  }
+  return acc;
+}
+
+static void decode_table(double dec[256]) {
+  int c;
+  for (c = 0; c < 256; ++c) dec[c] = oracle_e4m3_decode((uint8_t)c);
+}
+
+/* Full reference out[M,N] (fp64). */
+void oracle_gemm_ref(const uint8_t *a, const float *a_s, const uint8_t *w,
+                     const float *w_s, double *out, int64_t M, int64_t N,
+                     int64_t K) {
+  double dec[256];
+  int64_t r;
+  decode_table(dec);
+#pragma omp parallel for schedule(dynamic, 16)
+  for (r = 0; r < M * N; ++r)
+    out[r] = gemm_elem(a, a_s, w, w_s, dec, r / N, r % N, K);
+}
+
+/* Reference at selected (m, n) pairs only: out[i] = ref[ms[i], ns[i]]. */
+void oracle_gemm_ref_at(const uint8_t *a, const float *a_s, const uint8_t *w,
+                        const float *w_s, const int64_t *ms, const int64_t *ns,
+                        double *out, int64_t count, int64_t K) {
+  double dec[256];
+  int64_t i;
+  decode_table(dec);
+#pragma omp parallel for schedule(dynamic, 16)
+  for (i = 0; i < count; ++i)
+    out[i] = gemm_elem(a, a_s, w, w_s, dec, ms[i], ns[i], K);
+}
+
+/* Number of OpenMP threads a parallel region here would use. */
+int oracle_num_threads(void) {
+  int n = 1;
+#pragma omp parallel
+  {
+#pragma omp single
+    {
+#ifdef _OPENMP
+      extern int omp_get_num_threads(void);
+      n = omp_get_num_threads();
+#endif
+    }
+  }
+  return n;
+}

@@ -1,0 +1,26 @@
+"""Shared pytest setup.
+
+Markers:
+  gpu   -- needs an MI355X (gfx950) and the built HIP library; deselect with
+           ``-m "not gpu"`` on machines without one.
+"""
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+
+def pytest_configure(config):
+    config.addinivalue_line("markers", "gpu: needs an MI355X GPU and the built HIP library")
+    config.addinivalue_line("markers", "slow: long-running (minutes); still part of the default run")
+
+
+@pytest.fixture(scope="session")
+def orc():
+    import oracle
+    oracle._load()
+    return oracle
