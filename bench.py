@@ -1,0 +1,225 @@
+#!/usr/bin/env python3
+"""Benchmark of the W8A8 block-scaled FP8 projection on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload large_prefill]
+
+One step = one pass of the whole projection over one batch of synthetic
+input, already resident in HBM: activation quantizer -> scale relayout ->
+block-scaled FP8 GEMM (the three calls fp8q_proj makes, issued separately
+so the GEMM can be bracketed by events on its own stream).
+
+Default workload: the large prefill projection M=4576, K=17408, N=5120,
+Laplace(0,1) activations with 0.5% outlier channels x50, weights N(0,0.02)
+quantized per 128x128 block.  Prints ONE JSON line:
+
+  value           whole-step TFLOP/s = 2*M*N*K / step time
+  roofline        the GEMM (dominant kernel) against the dense FP8 MFMA peak,
+                  duration from HIP events around each GEMM launch
+  act_quant       the quantizer's GB/s (algorithmic bytes) against HBM peak
+  cpu_baseline    the CPU oracle on a bounded sample of the same workload
+
+Only one GPU is used; --gpus above 1 exits with a message.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0      # MI355X HBM3E, GB/s
+FP8_PEAK_TFLOPS = 5000.0   # MI355X dense FP8 MFMA, TFLOP/s
+# HBM bytes the rocprofv3 FETCH_SIZE/WRITE_SIZE counters attribute to one
+# launch of the dominant GEMM at the default workload (profiles/); None when
+# the kernel has changed since the counters were taken.
+GEMM_TRAFFIC_BYTES = None
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--workload", default="large_prefill",
+                   choices=["tiny", "decode", "prefill", "large_prefill"])
+    p.add_argument("--M", type=int, default=None, help="row count for the decode sweep")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=10.0,
+                   help="approximate CPU time budget of the oracle sample")
+    return p.parse_args()
+
+
+def quantize_weights_gpu(wf):
+    """Synthetic FP8 weights: per 128x128 block, scale = amax/448, codes by
+    PyTorch's float8_e4m3fn cast (input preparation, outside the timed path)."""
+    import torch
+    N, K = wf.shape
+    blocks = wf.view(N // 128, 128, K // 128, 128)
+    amax = blocks.abs().amax(dim=(1, 3))
+    ws = (amax / 448.0).to(torch.float32)
+    safe = torch.where(ws > 0, ws, torch.ones_like(ws))
+    q = (blocks / safe[:, None, :, None]).clamp(-448, 448)
+    codes = q.to(torch.float8_e4m3fn).view(torch.uint8).reshape(N, K).contiguous()
+    return codes, ws.contiguous()
+
+
+def cpu_baseline(w, x_bits, wf, budget_s):
+    """Time the oracle (quantizer + relayout + fp64 GEMM) on the first R rows."""
+    import oracle
+    oracle._load()
+    wq, ws = oracle.quant_weight_block(wf)          # input preparation, not timed
+    threads = oracle.num_threads()
+    # calibrate on 2 rows, then size the sample to the budget
+    def run(R):
+        xs = np.ascontiguousarray(x_bits[:R])
+        t0 = time.perf_counter()
+        a, a_s = oracle.quant_act(xs)
+        oracle.scale_to_kmajor(a_s)
+        oracle.gemm_ref(a, a_s, wq, ws)
+        return time.perf_counter() - t0
+    t2 = run(2)
+    R = int(max(2, min(w.M, 2 * budget_s / max(t2, 1e-6))))
+    R = max(2, min(R, w.M))
+    t = run(R)
+    flops = 2.0 * R * w.N * w.K
+    return {
+        "value": round(flops / t / 1e12, 6),
+        "unit": "TFLOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"first {R} of {w.M} rows of {w.desc}: quantize + relayout + fp64 block GEMM "
+                  f"({t:.1f} s)",
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on exactly one GPU; --gpus {args.gpus} is not "
+              "supported (the projection's sharding is described in DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import synth
+    import w8a8_fp8_block_amd as fp8q
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    props = torch.cuda.get_device_properties(dev)
+
+    w = (synth.workload(args.workload, M=args.M) if args.workload == "decode"
+         else synth.workload(args.workload))
+    M, K, N = w.M, w.K, w.N
+    G = K // 128
+    print(f"[bench] inputs {w.desc} (seed {w.seed})", file=sys.stderr, flush=True)
+    x_bits, wf, _ = synth.make_inputs(w)
+    x = torch.from_numpy(x_bits.view(np.int16)).to(dev)
+    wq, ws = quantize_weights_gpu(torch.from_numpy(wf).to(dev))
+    act_q, act_s, act_km = fp8q.alloc_proj_scratch(M, K)
+    out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream()
+    variant, grid, why = fp8q.fp8q_quant_select(M, K, props.multi_processor_count)
+
+    def step(ev_q=None, ev_g=None):
+        if ev_q: ev_q[0].record(stream)
+        fp8q.fp8q_quant_act(x, act_q, act_s)
+        if ev_q: ev_q[1].record(stream)
+        fp8q.fp8q_scale_to_kmajor(act_s, act_km)
+        if ev_g: ev_g[0].record(stream)
+        fp8q.fp8q_gemm_blockscaled(act_q, act_km, wq, ws, out)
+        if ev_g: ev_g[1].record(stream)
+
+    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    evq = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    evg = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record(stream)
+    for i in range(args.steps):
+        step(evq[i], evg[i])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+
+    gpu_ms = t_start.elapsed_time(t_end)
+    ms_per_step = max(gpu_ms, wall * 1e3) / args.steps
+    gemm_ms = np.array([a.elapsed_time(b) for a, b in evg])
+    quant_ms = np.array([a.elapsed_time(b) for a, b in evq])
+    flops = 2.0 * M * N * K
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    gemm_avg_s = float(np.mean(gemm_ms)) * 1e-3
+    gemm_tflops = flops / gemm_avg_s / 1e12
+    quant_bytes = M * K * 2 + M * K + M * G * 4
+    quant_avg_s = float(np.mean(quant_ms)) * 1e-3
+    quant_gbs = quant_bytes / quant_avg_s / 1e9
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(w, x_bits, wf, args.cpu_seconds)
+
+    rec = {
+        "metric": "block-scaled FP8 proj TFLOP/s (M=4576) + act-quant GB/s vs HBM peak",
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{w.name} M={M} K={K} N={N}",
+            "M": M, "K": K, "N": N,
+            "activations": f"bf16 {w.dist}(0,1), {w.n_outliers} outlier channels x{w.outlier_factor:g}",
+            "weights": "fp8 e4m3 [N,K], fp32 scale per 128x128 block (from N(0,0.02))",
+            "output": "bf16 [M,N]",
+            "step": "act-quant + scale relayout + block-scaled FP8 GEMM",
+            "quant_variant": "B" if variant == 2 else "A",
+            "device": props.name, "gcn_arch": props.gcnArchName,
+            "cus": props.multi_processor_count,
+        },
+        "roofline": {
+            "bound": "mfma",
+            "kernel": "gemm_tiled_kernel",
+            "achieved": round(gemm_tflops, 2),
+            "peak": FP8_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(gemm_tflops / FP8_PEAK_TFLOPS, 4),
+            "traffic": GEMM_TRAFFIC_BYTES,
+            "avg_launch_us": round(gemm_avg_s * 1e6, 2),
+            "algorithmic_flops_per_launch": flops,
+        },
+        "act_quant": {
+            "achieved": round(quant_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(quant_gbs / HBM_PEAK_GBS, 4),
+            "avg_launch_us": round(quant_avg_s * 1e6, 2),
+            "algorithmic_bytes_per_launch": quant_bytes,
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

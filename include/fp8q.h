@@ -1,0 +1,221 @@
+/*
+ * fp8q -- W8A8 block-scaled FP8 projection for AMD MI355X (gfx950).
+ *
+ * C ABI of libfp8q.so.  The projection it implements is the one routed by
+ * the page "dispatch_proj.rs" (spark_model/layers/ops), functions
+ * cublas_fp8_proj and cublas_fp8_proj_prequant:
+ *
+ *   1. quantize bf16 activations [M,K] to OCP FP8 e4m3 with one fp32 scale
+ *      per (token, 128-wide K group), scale = amax/448      (fp8q_quant_act)
+ *   2. rewrite those scales from row-major [M,K/128] to the K-major
+ *      [K/128, ceil16(M)] layout, pad slots zero       (fp8q_scale_to_kmajor)
+ *   3. out[M,N] = act . W^T with FP8 weights [N,K] carrying one fp32 scale
+ *      per 128x128 block, applied per 128-deep K block  (fp8q_gemm_blockscaled)
+ *
+ * and fp8q_proj runs all three.  The choice between the two quantizer
+ * variants follows the workgroup-count floor of the page
+ * "fp8_act_quant_floor.rs" (fp8q_quant_select).
+ *
+ * Conventions shared by every entry point:
+ *
+ *  - Memory.  Every array argument is DEVICE memory owned by the caller, on
+ *    the current HIP device, 16-byte aligned, densely packed row-major.  The
+ *    library allocates nothing and frees nothing; scratch buffers are the
+ *    caller's (as the pages' arena buffers are).
+ *  - Streams.  Work is enqueued on `stream` (0 = the null stream) and is
+ *    ordered with the caller's other work on that stream.  No entry point
+ *    synchronizes the host.
+ *  - Errors.  Arguments are validated before anything is enqueued; on
+ *    failure nothing is launched and a status != FP8Q_OK is returned, with a
+ *    message naming the failed check in fp8q_last_error().  A launch failure
+ *    returns FP8Q_ERR_LAUNCH (earlier kernels of a composite call may have
+ *    been enqueued).
+ *  - Empty batch.  M == 0 is a successful no-op.
+ *  - Aliasing.  Outputs must not overlap inputs or each other.
+ *  - Inputs must be finite; NaN/Inf activations give unspecified codes.
+ *  - Concurrency.  Entry points are thread-safe; calls on different streams
+ *    may run concurrently as long as their buffers are disjoint.
+ *  - Logging.  With FP8Q_LOG=1 in the environment, the quantizer variant
+ *    choice prints one line to stderr per selector branch per process.
+ */
+#ifndef FP8Q_H
+#define FP8Q_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum fp8q_status {
+  FP8Q_OK = 0,
+  FP8Q_ERR_NULL = 1,    /* a required pointer is NULL                        */
+  FP8Q_ERR_SHAPE = 2,   /* K == 0, K % 128 != 0, N == 0, N % 128 != 0, or a
+                           size whose element count does not fit 2^32 - 1     */
+  FP8Q_ERR_ALIGN = 3,   /* an array pointer is not 16-byte aligned           */
+  FP8Q_ERR_DEVICE = 4,  /* the current HIP device is not gfx950, or the HIP
+                           runtime could not be queried                      */
+  FP8Q_ERR_LAUNCH = 5,  /* a kernel launch reported an error                  */
+  FP8Q_ERR_VARIANT = 6  /* a forced variant / kernel id is out of range       */
+} fp8q_status;
+
+/* ------------------------------------------------------------ utilities */
+
+/* ceil16(m) = the padded token count of the K-major scale layout
+ * (dispatch_proj.rs, cublas_fp8_m_pad: M rounded up to a multiple of 16).
+ * Pure; never fails. */
+uint32_t fp8q_m_pad(uint32_t m);
+
+/* Message of the last failed check on the calling thread ("" if none).  The
+ * pointer stays valid until the thread's next fp8q call. */
+const char *fp8q_last_error(void);
+
+/* Library version string, e.g. "fp8q 0.1.0 gfx950". */
+const char *fp8q_version(void);
+
+/* ----------------------------------------------------------- quantizer */
+
+/* Per-(token, 128-group) activation quantizer (dispatch_proj.rs, doc of
+ * cublas_fp8_proj; the kernel is called per_token_group_quant_fp8 there).
+ *
+ *   x_bf16    [M,K] bf16 bit patterns, read only
+ *   q_e4m3    [M,K] out: OCP e4m3fn codes; q = e4m3_rne_sat(x / scale), the
+ *             sign of zero kept; codes 0x7F/0xFF (NaN) are never written
+ *   scale_rm  [M,K/128] out: fp32 scale[m,g] = fl32(amax/448), amax the
+ *             largest |x| of the 128 elements x[m, 128g .. 128g+127];
+ *             an all-zero group gets scale +0.0 and codes 0x00/0x80
+ *   K % 128 == 0.  Results are bit-identical for every variant.
+ *
+ * The variant (fine-grained A or K-grouped B) is picked by fp8q_quant_select
+ * for the current device. */
+fp8q_status fp8q_quant_act(const uint16_t *x_bf16, uint8_t *q_e4m3,
+                           float *scale_rm, uint32_t M, uint32_t K,
+                           hipStream_t stream);
+
+/* As fp8q_quant_act with the variant forced: 0 = auto (selector),
+ * 1 = A (fine-grained), 2 = B (K-grouped).  Forcing an arm is how the
+ * pages' microtest measures each one (fp8_act_quant_floor.rs, doc of
+ * fp8_act_quant_hopper_reject).  Other values -> FP8Q_ERR_VARIANT. */
+fp8q_status fp8q_quant_act_ex(const uint16_t *x_bf16, uint8_t *q_e4m3,
+                              float *scale_rm, uint32_t M, uint32_t K,
+                              int variant, hipStream_t stream);
+
+/* Quantizer + relayout in one kernel: the outputs of fp8q_quant_act plus
+ * the K-major copy of the scales that fp8q_scale_to_kmajor would write
+ * (scale_km [K/128, ceil16(M)], pad slots +0.0).  scale_rm may be NULL when
+ * only the K-major copy is wanted.  Bit-identical to the two-call path. */
+fp8q_status fp8q_quant_act_kmajor(const uint16_t *x_bf16, uint8_t *q_e4m3,
+                                  float *scale_rm, float *scale_km,
+                                  uint32_t M, uint32_t K, hipStream_t stream);
+
+/* Parameters of the quantizer variant selection rule
+ * (fp8_act_quant_floor.rs, module header "The rule" and
+ * fp8_act_quant_hopper_reject).  The K-grouped variant B runs only when its
+ * own grid has at least min_wg_per_cu * cu_count workgroups. */
+typedef struct fp8q_select_params {
+  uint32_t cu_count;       /* compute units of the device (>= 1 assumed)     */
+  uint32_t min_wg_per_cu;  /* floor multiplier (workgroups per CU)           */
+  uint32_t b_groups_per_wg;/* K-groups one workgroup of variant B covers;
+                              its grid is M x ceil((K/128)/b_groups_per_wg)  */
+  uint32_t a_groups_per_wg;/* groups one workgroup of variant A covers; its
+                              grid is ceil(M*(K/128)/a_groups_per_wg)        */
+  int requested;           /* lever: 0 = never pick B                        */
+  int b_present;           /* 0 = variant B unavailable                      */
+  int a_present;           /* 0 = variant A unavailable                      */
+} fp8q_select_params;
+
+/* The parameters fp8q_quant_select uses on this library's gfx950 kernels
+ * for a device with cu_count compute units (requested from the
+ * FP8Q_QUANT_VARIANT environment variable: "a" -> 0, else 1). */
+fp8q_select_params fp8q_default_select_params(uint32_t cu_count);
+
+/* Pure selection rule.  Returns 2 when variant B runs and 1 when A runs,
+ * and writes that variant's launch grid to grid_out[3] (variant and grid are
+ * decided together, as the page's Fp8QuantPick carries both).  *reject is
+ * set to NULL when B runs, else to the named reason A runs instead:
+ *   "variant B not requested", "variant B absent", or
+ *   "too few workgroups for variant B to fill the device".
+ * Reasons are tested in the page's order: B absent -> A absent (B runs) ->
+ * not requested -> grid below the floor.  Returns -1 (FP8Q_ERR_SHAPE in
+ * fp8q_last_error) when K is 0 or not a multiple of 128, or when neither
+ * variant is present.  grid_out and reject may be NULL. */
+int fp8q_quant_select_with(uint32_t M, uint32_t K, const fp8q_select_params *p,
+                           uint32_t grid_out[3], const char **reject);
+
+/* fp8q_quant_select_with(M, K, fp8q_default_select_params(cu_count), ...) */
+int fp8q_quant_select(uint32_t M, uint32_t K, uint32_t cu_count,
+                      uint32_t grid_out[3], const char **reject);
+
+/* Smallest M at which variant B's grid reaches the floor for this K
+ * (fp8_act_quant_floor.rs, fp8_quant_hopper_min_m).  0 if K invalid. */
+uint32_t fp8q_quant_b_min_m(uint32_t K, const fp8q_select_params *p);
+
+/* Log slot of a verdict (fp8_act_quant_floor.rs, fp8_quant_log_slot): -1 =
+ * silent (B did not run and B was not requested), 0..2 = the index of the
+ * reject reason in the order listed above, 3 = B ran.  Pure. */
+int fp8q_quant_log_slot(int variant, const char *reject, int requested);
+
+/* ------------------------------------------------------------- relayout */
+
+/* Scale relayout (dispatch_proj.rs, fp8_act_scale_to_kmajor):
+ *   scale_km[g * Mp + m] = m < M ? scale_rm[m * (K/128) + g] : +0.0f
+ * for g < K/128, m < Mp = fp8q_m_pad(M).  Every slot is written.
+ *   scale_rm  [M, K/128] fp32, read only
+ *   scale_km  [K/128, Mp] fp32 out */
+fp8q_status fp8q_scale_to_kmajor(const float *scale_rm, float *scale_km,
+                                 uint32_t M, uint32_t K, hipStream_t stream);
+
+/* ----------------------------------------------------------------- GEMM */
+
+/* Block-scaled FP8 GEMM (dispatch_proj.rs, cublas_fp8_proj_prequant):
+ *
+ *   out[m,n] = bf16_rne( sum_kb a_scale_km[kb*Mp + m] * w_scale[(n/128)*(K/128) + kb]
+ *                               * sum_{j<128} dec(a[m,128kb+j]) * dec(w[n,128kb+j]) )
+ *
+ *   a_e4m3      [M,K] e4m3fn codes (activations), read only
+ *   a_scale_km  [K/128, Mp] fp32, Mp = fp8q_m_pad(M) (K-major, as written by
+ *               fp8q_scale_to_kmajor); slots m >= M are never read
+ *   w_e4m3      [N,K] e4m3fn codes (weights), read only
+ *   w_scale     [N/128, K/128] fp32, one scale per 128x128 weight block
+ *   out_bf16    [M,N] bf16 out; exactly the M*N real rows are written
+ *               (activation rows >= M are neither read nor written)
+ *   N % 128 == 0, K % 128 == 0.  Accumulation is fp32 with each 128-deep
+ *   block's partial product scaled before it is added; the summation order
+ *   is not specified, so outputs are reproducible run to run but not
+ *   bit-defined. */
+fp8q_status fp8q_gemm_blockscaled(const uint8_t *a_e4m3, const float *a_scale_km,
+                                  const uint8_t *w_e4m3, const float *w_scale,
+                                  uint16_t *out_bf16, uint32_t M, uint32_t N,
+                                  uint32_t K, hipStream_t stream);
+
+/* As fp8q_gemm_blockscaled with the kernel forced: 0 = auto, 1 = the
+ * LDS-tiled MFMA kernel (prefill widths), 2 = the skinny kernel (decode
+ * widths, needs M <= 64).  Other values -> FP8Q_ERR_VARIANT. */
+fp8q_status fp8q_gemm_blockscaled_ex(const uint8_t *a_e4m3, const float *a_scale_km,
+                                     const uint8_t *w_e4m3, const float *w_scale,
+                                     uint16_t *out_bf16, uint32_t M, uint32_t N,
+                                     uint32_t K, int kernel, hipStream_t stream);
+
+/* ----------------------------------------------------------- projection */
+
+/* Whole W8A8 projection (dispatch_proj.rs, cublas_fp8_proj): quantize x,
+ * relayout the scales, run the GEMM.
+ *   x_bf16               [M,K] bf16 activations, read only
+ *   w_e4m3, w_scale      as for fp8q_gemm_blockscaled
+ *   out_bf16             [M,N] bf16 out
+ *   act_q_scratch        >= M*K bytes       (receives the codes)
+ *   act_scale_scratch    >= M*(K/128) fp32  (receives the row-major scales)
+ *   act_scale_km_scratch >= Mp*(K/128) fp32 (receives the K-major scales)
+ * The scratch buffers hold the intermediate results afterwards. */
+fp8q_status fp8q_proj(const uint16_t *x_bf16, const uint8_t *w_e4m3,
+                      const float *w_scale, uint16_t *out_bf16,
+                      uint8_t *act_q_scratch, float *act_scale_scratch,
+                      float *act_scale_km_scratch, uint32_t M, uint32_t N,
+                      uint32_t K, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP8Q_H */

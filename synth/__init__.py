@@ -132,14 +132,14 @@ def make_inputs(w: Workload, M: int | None = None, with_weights: bool = True,
 # an element depends only on the element and the group's absolute maximum, so
 # every finite positive bf16 amax paired with every bf16 x, |x| <= amax, covers
 # the whole element map.  Each group holds its amax once followed by 127 test
-# values; the sign of the test values alternates with their position.
+# values.
 # --------------------------------------------------------------------------
 _MAX_FINITE_BF16 = 0x7F7F
 
 
 def _pairs_per_amax(a: int) -> int:
-    # test values 0..a (bit patterns), both signs except for +0
-    return 2 * (a + 1) - 1
+    # test values 0..a (bit patterns), both signs (+0 and -0 both included)
+    return 2 * (a + 1)
 
 
 def n_exhaustive_groups(amax_lo: int = 1, amax_hi: int = _MAX_FINITE_BF16) -> int:
@@ -152,13 +152,14 @@ def exhaustive_pair_groups(amax_lo: int, amax_hi: int) -> np.ndarray:
     with amax in the bit-pattern range [amax_lo, amax_hi] (positive, finite).
 
     Column 0 of each row is amax; columns 1..127 hold x values (bit patterns
-    0..amax with sign bit set or clear); unused slots of a row's tail repeat
-    +0, which never changes the group maximum.
+    0..amax with sign bit clear, then with sign bit set, -0.0 included);
+    unused slots of a row's tail repeat +0, which never changes the group
+    maximum.
     """
     rows = []
     for a in range(amax_lo, amax_hi + 1):
         mags = np.arange(0, a + 1, dtype=np.uint16)
-        vals = np.concatenate([mags, mags[1:] | np.uint16(0x8000)])
+        vals = np.concatenate([mags, mags | np.uint16(0x8000)])
         ng = (len(vals) + 126) // 127
         buf = np.zeros(ng * 127, dtype=np.uint16)
         buf[: len(vals)] = vals

@@ -1,0 +1,108 @@
+"""Host-side checks of the C ABI (no GPU needed, no kernel launched).
+
+* libfp8q.so loads and exports every function include/fp8q.h declares;
+* argument validation returns the documented status before anything is
+  enqueued (only arguments that fail a check before the device query are
+  used here, so no call reaches the GPU even where one is present);
+* fp8q_m_pad is ceil16 (page "dispatch_proj.rs", cublas_fp8_m_pad).
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import w8a8_fp8_block_amd as fp8q
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fp8q.h")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = set(re.findall(r"\b(fp8q_[a-z0-9_]+)\s*\(", src))
+    return sorted(names)
+
+
+def test_header_declares_the_entry_points():
+    names = _declared()
+    for n in ("fp8q_quant_act", "fp8q_scale_to_kmajor", "fp8q_gemm_blockscaled", "fp8q_proj",
+              "fp8q_quant_select", "fp8q_m_pad", "fp8q_last_error"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    out = subprocess.run(["nm", "-D", "--defined-only", fp8q.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (fp8q_[a-z0-9_]+)\b", out))
+    missing = [n for n in _declared() if n not in exported]
+    assert not missing, missing
+    lib = fp8q.lib()
+    for n in _declared():
+        assert getattr(lib, n) is not None
+
+
+def test_m_pad():
+    for m, want in ((0, 0), (1, 16), (15, 16), (16, 16), (17, 32), (25, 32), (1168, 1168),
+                    (4576, 4576), (16384, 16384), (16385, 16400)):
+        assert fp8q.fp8q_m_pad(m) == want
+
+
+def test_version():
+    assert "gfx950" in fp8q.fp8q_version()
+
+
+# ---- validation: raw ctypes calls with NULL / misaligned / bad shapes ----
+P = ctypes.c_void_p
+BAD = P(0x1001)   # misaligned, never dereferenced (rejected first)
+GOOD = P(0x1000)  # only ever passed together with an argument that fails
+
+
+def _err():
+    return fp8q.lib().fp8q_last_error().decode()
+
+
+def test_quant_validation():
+    L = fp8q.lib()
+    assert L.fp8q_quant_act(None, None, None, 4, 100, None) == 2          # K % 128
+    assert "K=100" in _err()
+    assert L.fp8q_quant_act(None, None, None, 4, 0, None) == 2            # K == 0
+    assert L.fp8q_quant_act(None, GOOD, GOOD, 4, 128, None) == 1          # NULL x
+    assert "x_bf16" in _err()
+    assert L.fp8q_quant_act(BAD, GOOD, GOOD, 4, 128, None) == 3           # misaligned
+    assert L.fp8q_quant_act(GOOD, GOOD, None, 4, 128, None) == 1
+    assert L.fp8q_quant_act_ex(GOOD, GOOD, GOOD, 4, 128, 3, None) == 6    # variant
+    assert L.fp8q_quant_act_ex(GOOD, GOOD, GOOD, 4, 128, -1, None) == 6
+    assert L.fp8q_quant_act(None, None, None, 1 << 20, 1 << 13, None) == 2  # > 2^32 elems
+    # M == 0 is a no-op that succeeds without touching memory
+    assert L.fp8q_quant_act(GOOD, GOOD, GOOD, 0, 128, None) == 0
+    assert _err() == ""
+
+
+def test_kmajor_validation():
+    L = fp8q.lib()
+    assert L.fp8q_scale_to_kmajor(GOOD, GOOD, 3, 129, None) == 2
+    assert L.fp8q_scale_to_kmajor(None, GOOD, 3, 128, None) == 1
+    assert L.fp8q_scale_to_kmajor(GOOD, BAD, 3, 128, None) == 3
+    assert L.fp8q_scale_to_kmajor(GOOD, GOOD, 0, 128, None) == 0
+    assert L.fp8q_quant_act_kmajor(GOOD, GOOD, BAD, GOOD, 3, 128, None) == 3
+    assert L.fp8q_quant_act_kmajor(GOOD, GOOD, None, None, 3, 128, None) == 1
+    assert L.fp8q_quant_act_kmajor(GOOD, GOOD, None, GOOD, 0, 128, None) == 0
+
+
+def test_gemm_validation():
+    L = fp8q.lib()
+    g = GOOD
+    assert L.fp8q_gemm_blockscaled(g, g, g, g, g, 4, 100, 128, None) == 2   # N % 128
+    assert L.fp8q_gemm_blockscaled(g, g, g, g, g, 4, 0, 128, None) == 2
+    assert L.fp8q_gemm_blockscaled(g, g, g, g, g, 4, 128, 130, None) == 2   # K % 128
+    assert L.fp8q_gemm_blockscaled(g, g, None, g, g, 4, 128, 128, None) == 1
+    assert L.fp8q_gemm_blockscaled(g, g, g, g, BAD, 4, 128, 128, None) == 3
+    assert L.fp8q_gemm_blockscaled_ex(g, g, g, g, g, 4, 128, 128, 7, None) == 6
+    assert L.fp8q_gemm_blockscaled(g, g, g, g, g, 0, 128, 128, None) == 0
+    assert L.fp8q_proj(g, g, g, g, g, g, None, 4, 128, 128, None) == 1
+    assert "act_scale_km_scratch" in _err()
+    assert L.fp8q_proj(g, g, g, g, g, g, g, 4, 128, 100, None) == 2
+    assert L.fp8q_proj(g, g, g, g, g, g, g, 0, 128, 128, None) == 0

@@ -1,0 +1,243 @@
+"""GPU parity of the block-scaled FP8 GEMM and of the whole projection.
+
+Accuracy contract against the oracle's fp64 block-form product r:
+  rel_rms = sqrt(sum (o-b)^2 / sum b^2) <= 1e-3 with b = r rounded to bf16
+  (the output format; rounding alone puts any bf16 output ~1.66e-3 away from
+  the unrounded r), and for every element |o - r| <= ulp_bf16(r) + 1e-3*RMS(r).
+At sizes the oracle finishes in seconds the whole output is compared; at the
+full prefill sizes a sample of outputs spanning every M tile (the ragged
+last one included) and every N tile is compared (RMS(ref) estimated from the
+sample).  Exact special cases (powers of two, one-hot rows, small integers)
+must match bit for bit, and a wrong scale layout must fail by a wide margin.
+"""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from gpu_util import Guarded, bf16_bits_to_f64, dev, host, log, require_gpu
+
+pytestmark = pytest.mark.gpu
+
+fp8q = None
+RTOL = 1e-3
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    global fp8q
+    require_gpu()
+    import w8a8_fp8_block_amd as m
+    fp8q = m
+    yield
+
+
+def _operands(orc, w: synth.Workload, M=None):
+    x, wf, _ = synth.make_inputs(w, M=M)
+    a, a_s = orc.quant_act(x)
+    wq, ws = orc.quant_weight_block(wf)
+    return x, a, a_s, wq, ws
+
+
+def _gemm_gpu(orc, a, a_s, wq, ws, kernel=0, km=None):
+    M, K = a.shape
+    N = wq.shape[0]
+    if km is None:
+        km = orc.scale_to_kmajor(a_s)
+    out = Guarded((M, N), torch.int16)
+    fp8q.fp8q_gemm_blockscaled(dev(a), dev(km), dev(wq), dev(ws), out.t, kernel=kernel)
+    torch.cuda.synchronize()
+    out.check_canary()
+    return bf16_bits_to_f64(host(out.t))
+
+
+def _assert_tol(o, r, what, rms=None):
+    rel, exc, relf = orc_errors(o, r, rms)
+    log(f"  {what}: rel_rms={rel:.3e} (vs fp64 {relf:.3e}) worst/bound={exc:.3f}")
+    assert rel <= RTOL, f"{what}: rel_rms {rel}"
+    assert exc <= 1.0, f"{what}: per-element error {exc} x bound"
+
+
+def orc_errors(o, r, rms=None):
+    import oracle
+    return oracle.gemm_errors(o, r, rms)
+
+
+def _kernels_for(M):
+    return (0, 1, 2) if M <= 64 else (0, 1)
+
+
+@pytest.mark.parametrize("M,N,K", [(16, 256, 512), (1, 128, 128), (17, 384, 640), (33, 256, 1152),
+                                   (64, 128, 256), (130, 384, 640), (257, 256, 384),
+                                   (300, 512, 896)])
+def test_gemm_small_full(orc, M, N, K):
+    rng = np.random.default_rng(M * 7 + N + K)
+    x = synth.f32_to_bf16_bits(rng.standard_normal((M, K)).astype(np.float32))
+    a, a_s = orc.quant_act(x)
+    wq, ws = orc.quant_weight_block(rng.normal(0, 0.02, (N, K)).astype(np.float32))
+    ref = orc.gemm_ref(a, a_s, wq, ws)
+    for kern in _kernels_for(M):
+        log(f"gemm M={M} N={N} K={K} kernel={kern}")
+        _assert_tol(_gemm_gpu(orc, a, a_s, wq, ws, kern), ref, f"M{M}N{N}K{K}k{kern}")
+
+
+def test_gemm_tiny_workload(orc):
+    w = synth.workload("tiny")
+    _, a, a_s, wq, ws = _operands(orc, w)
+    ref = orc.gemm_ref(a, a_s, wq, ws)
+    for kern in (0, 1, 2):
+        log(f"gemm tiny kernel={kern}")
+        _assert_tol(_gemm_gpu(orc, a, a_s, wq, ws, kern), ref, f"tiny k{kern}")
+
+
+@pytest.mark.parametrize("M", [16, 17, 25])
+def test_gemm_decode_workload_full(orc, M):
+    w = synth.workload("decode", M=M)
+    _, a, a_s, wq, ws = _operands(orc, w)
+    log(f"oracle decode M={M}")
+    ref = orc.gemm_ref(a, a_s, wq, ws)
+    for kern in (0, 1, 2):
+        log(f"gemm decode M={M} kernel={kern}")
+        _assert_tol(_gemm_gpu(orc, a, a_s, wq, ws, kern), ref, f"decode M{M} k{kern}")
+
+
+def _sample_idx(M, N, per_tile=24, seed=0):
+    rng = np.random.default_rng(seed)
+    ms, ns = [], []
+    for m0 in range(0, M, 128):
+        for n0 in range(0, N, 128):
+            ms.append(rng.integers(m0, min(m0 + 128, M), per_tile))
+            ns.append(rng.integers(n0, n0 + 128, per_tile))
+    # the last row and column always
+    ms.append(np.full(N // 128, M - 1))
+    ns.append(np.arange(0, N, 128) + 127)
+    return np.concatenate(ms), np.concatenate(ns)
+
+
+@pytest.mark.parametrize("name", ["prefill", "large_prefill"])
+def test_gemm_prefill_workloads_sampled(orc, name):
+    w = synth.WORKLOADS[name][0]
+    log(f"inputs {w.desc}")
+    _, a, a_s, wq, ws = _operands(orc, w)
+    ms, ns = _sample_idx(w.M, w.N, per_tile=8 if name == "large_prefill" else 16)
+    log(f"oracle {w.desc} samples={len(ms)}")
+    ref = orc.gemm_ref_at(a, a_s, wq, ws, ms, ns)
+    rms = float(np.sqrt(np.mean(ref * ref)))
+    log(f"gemm {w.desc}")
+    o = _gemm_gpu(orc, a, a_s, wq, ws, 0)
+    _assert_tol(o[ms, ns], ref, w.desc, rms)
+    # no NaN/Inf anywhere in the full output, and rows beyond the sample are sane
+    assert np.all(np.isfinite(o))
+
+
+def test_gemm_block_scale_isolation_exact(orc):
+    """All codes 1.0, a_s[m,g] = 2^(m%5), w_s[nb,g] = 2^g * (nb+1): the result
+    128 * (nb+1) * sum_g 2^(m%5+g) is exact in fp32 and in bf16."""
+    M, N, K = 40, 384, 512
+    G = K // 128
+    a = np.full((M, K), 0x38, dtype=np.uint8)
+    wq = np.full((N, K), 0x38, dtype=np.uint8)
+    a_s = np.array([[2.0 ** (m % 5)] * G for m in range(M)], dtype=np.float32)
+    ws = np.array([[2.0 ** g * (nb + 1) for g in range(G)] for nb in range(N // 128)], dtype=np.float32)
+    ref = orc.gemm_ref(a, a_s, wq, ws)
+    for kern in _kernels_for(M):
+        o = _gemm_gpu(orc, a, a_s, wq, ws, kern)
+        assert np.array_equal(o, ref), f"kernel {kern}"
+
+
+def test_gemm_one_hot_rows_exact(orc):
+    M, N, K = 48, 256, 640
+    G = K // 128
+    rng = np.random.default_rng(2)
+    x = synth.f32_to_bf16_bits(rng.standard_normal((M, K)).astype(np.float32))
+    a, _ = orc.quant_act(x)
+    a_s = np.exp2(rng.integers(-6, 6, (M, G))).astype(np.float32)  # exact products
+    kk = rng.integers(0, K, size=N)
+    wq = np.zeros((N, K), dtype=np.uint8)
+    wq[np.arange(N), kk] = 0x38
+    ws = np.exp2(rng.integers(-3, 4, (N // 128, G))).astype(np.float32)
+    ref = orc.gemm_ref(a, a_s, wq, ws)
+    want = bf16_bits_to_f64(synth.f32_to_bf16_bits(ref.astype(np.float32)))  # exact in fp32
+    assert np.array_equal(ref.astype(np.float32).astype(np.float64), ref)
+    for kern in _kernels_for(M):
+        o = _gemm_gpu(orc, a, a_s, wq, ws, kern)
+        assert np.array_equal(o, want), f"kernel {kern}"
+
+
+def test_gemm_small_integers_exact(orc):
+    """Codes of small integers and power-of-two scales: every partial sum is an
+    exact fp32 integer, so the GPU result must equal the bf16 rounding of the
+    exact value."""
+    M, N, K = 37, 256, 768
+    G = K // 128
+    rng = np.random.default_rng(4)
+    ints = rng.integers(-3, 4, (M, K)).astype(np.float32)
+    intw = rng.integers(-3, 4, (N, K)).astype(np.float32)
+    a = orc.e4m3_encode(ints)
+    wq = orc.e4m3_encode(intw)
+    a_s = np.exp2(rng.integers(-2, 3, (M, G))).astype(np.float32)
+    ws = np.exp2(rng.integers(-2, 3, (N // 128, G))).astype(np.float32)
+    ref = orc.gemm_ref(a, a_s, wq, ws)
+    assert np.array_equal(ref.astype(np.float32).astype(np.float64), ref)
+    want = bf16_bits_to_f64(synth.f32_to_bf16_bits(ref.astype(np.float32)))
+    for kern in _kernels_for(M):
+        o = _gemm_gpu(orc, a, a_s, wq, ws, kern)
+        assert np.array_equal(o, want), f"kernel {kern}"
+
+
+def test_gemm_rowmajor_scales_fail(orc):
+    """Negative control: the quantizer's row-major scales handed over as if they
+    were K-major (the measurement-control reading on the page
+    "dispatch_proj.rs", cublas_scale_layout_kmajor) must miss the tolerance by
+    far more than 10x."""
+    M, N, K = 32, 256, 2048
+    rng = np.random.default_rng(8)
+    x = synth.f32_to_bf16_bits((rng.standard_normal((M, K)) *
+                                np.exp(rng.uniform(-2, 2, (M, 1)))).astype(np.float32))
+    a, a_s = orc.quant_act(x)
+    wq, ws = orc.quant_weight_block(rng.normal(0, 0.02, (N, K)).astype(np.float32))
+    ref = orc.gemm_ref(a, a_s, wq, ws)
+    Mp = synth.ceil16(M)
+    wrong = np.zeros((K // 128) * Mp, dtype=np.float32)
+    wrong[: a_s.size] = a_s.ravel()
+    wrong = wrong.reshape(K // 128, Mp)
+    for kern in _kernels_for(M):
+        o = _gemm_gpu(orc, a, a_s, wq, ws, kern, km=wrong)
+        rel, exc, _ = orc_errors(o, ref)
+        log(f"  row-major control kernel {kern}: rel_rms={rel:.3e} worst/bound={exc:.1f}")
+        assert rel > 10 * RTOL and exc > 10
+
+
+@pytest.mark.parametrize("name,M", [("tiny", None), ("decode", 17), ("decode", 25),
+                                    ("prefill", 130)])
+def test_proj_end_to_end(orc, name, M):
+    w = synth.workload(name) if M is None or name != "decode" else synth.workload(name, M=M)
+    x, wf, _ = synth.make_inputs(w, M=M)
+    Mr = x.shape[0]
+    a, a_s = orc.quant_act(x)
+    km_ref = orc.scale_to_kmajor(a_s)
+    wq, ws = orc.quant_weight_block(wf)
+    ref = orc.gemm_ref(a, a_s, wq, ws)
+    log(f"proj {w.desc} M={Mr}")
+    out = Guarded((Mr, w.N), torch.int16)
+    aq = Guarded((Mr, w.K), torch.uint8)
+    asr = Guarded((Mr, w.K // 128), torch.float32)
+    askm = Guarded((w.K // 128, synth.ceil16(Mr)), torch.float32, fill=0x7F)
+    fp8q.fp8q_proj(dev(x), dev(wq), dev(ws), out.t, aq.t, asr.t, askm.t)
+    torch.cuda.synchronize()
+    for g in (out, aq, asr, askm):
+        g.check_canary()
+    assert np.array_equal(host(aq.t), a)
+    assert np.array_equal(host(asr.t).view(np.uint32), a_s.view(np.uint32))
+    assert np.array_equal(host(askm.t).view(np.uint32), km_ref.view(np.uint32))
+    _assert_tol(bf16_bits_to_f64(host(out.t)), ref, f"proj {w.desc}")
+
+
+def test_gemm_repeatable(orc):
+    """Same inputs, same bits, run to run (no data races in the reduction)."""
+    w = synth.workload("decode", M=25)
+    _, a, a_s, wq, ws = _operands(orc, w)
+    for kern in (1, 2):
+        o1 = _gemm_gpu(orc, a, a_s, wq, ws, kern)
+        o2 = _gemm_gpu(orc, a, a_s, wq, ws, kern)
+        assert np.array_equal(o1, o2)

@@ -95,7 +95,7 @@ def test_transposed_scale_is_caught(orc):
     km = orc.scale_to_kmajor(a_s)                        # [G, 16]
     wrong = np.ascontiguousarray(km.ravel()[: M * (K // 128)].reshape(M, K // 128))
     bad = orc.gemm_ref(a, wrong, w, w_s)
-    rel, exc = orc.gemm_errors(bad, ref)
+    rel, exc, _ = orc.gemm_errors(bad, ref)
     assert rel > 1e-2 and exc > 10
 
 
@@ -104,11 +104,37 @@ def test_bf16_ulp_and_metric(orc):
     want = np.array([2.0 ** -7, 2.0 ** -7, 2.0 ** -6, 2.0 ** -6, 2.0 ** -133, 2.0 ** -133, 2.0 ** -133])
     assert np.array_equal(orc.bf16_ulp(r), want)
     ref = np.linspace(-4, 4, 1001)
-    rel, exc = orc.gemm_errors(ref, ref)
-    assert rel == 0 and exc == 0
+    rel, exc, relf = orc.gemm_errors(orc.round_to_bf16(ref), ref)
+    assert rel == 0 and exc <= 0.5 / (1 + 1e-12) + 1e-12 and relf > 0
     rms = float(np.sqrt(np.mean(ref * ref)))
     off = ref + (orc.bf16_ulp(ref) + 1e-3 * rms) * 0.999
-    rel, exc = orc.gemm_errors(off, ref)
+    rel, exc, _ = orc.gemm_errors(off, ref)
     assert exc < 1.0
     off = ref + (orc.bf16_ulp(ref) + 1e-3 * rms) * 1.01
     assert orc.gemm_errors(off, ref)[1] > 1.0
+
+
+def test_round_to_bf16_matches_torch_and_ties(orc):
+    import torch
+    rng = np.random.default_rng(6)
+    v = (rng.standard_normal(200_000) * np.exp2(rng.integers(-40, 40, 200_000))).astype(np.float32)
+    want = torch.from_numpy(v).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(orc.round_to_bf16(v.astype(np.float64)), want)
+    # fp64 values just off a bf16 midpoint round by the sign of the offset
+    # (a detour through fp32 would lose the offset and tie to even)
+    lo = np.float64(1.0)
+    mid = lo + 2.0 ** -8                       # halfway between 1 and 1 + 2^-7
+    assert orc.round_to_bf16(np.array([mid]))[0] == 1.0            # tie -> even
+    assert orc.round_to_bf16(np.array([mid + 2.0 ** -40]))[0] == 1.0 + 2.0 ** -7
+    assert orc.round_to_bf16(np.array([mid - 2.0 ** -40]))[0] == 1.0
+    assert orc.round_to_bf16(np.array([-(mid + 2.0 ** -40)]))[0] == -(1.0 + 2.0 ** -7)
+
+
+def test_bf16_output_rounding_floor(orc):
+    """Rounding an exact result to bf16 alone gives a relative RMS error of
+    about 1.66e-3 (uniform rounding error of 2^-7 relative ulp), which is why
+    the 1e-3 relative-RMS bar is applied against the bf16-rounded reference."""
+    rng = np.random.default_rng(1)
+    r = rng.standard_normal(400_000) * 3.0
+    _, _, relf = orc.gemm_errors(orc.round_to_bf16(r), r)
+    assert 1.5e-3 < relf < 1.8e-3

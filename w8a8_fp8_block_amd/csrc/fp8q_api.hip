@@ -1,0 +1,358 @@
+// C-ABI entry points of libfp8q.so: argument validation, the quantizer
+// variant selection rule, once-per-branch logging and kernel dispatch.
+// Declarations and the contract of every function: include/fp8q.h.
+#include <atomic>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+
+#include "../../include/fp8q.h"
+#include "fp8q_internal.h"
+
+using namespace fp8q;
+
+namespace {
+
+thread_local char g_err[256] = "";
+
+fp8q_status fail(fp8q_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+fp8q_status ok() {
+  g_err[0] = '\0';
+  return FP8Q_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+#define REQUIRE_PTR(p)                                                              \
+  do {                                                                              \
+    if ((p) == nullptr) return fail(FP8Q_ERR_NULL, "%s: " #p " is NULL", fn);       \
+    if (!aligned16(p)) return fail(FP8Q_ERR_ALIGN, "%s: " #p " is not 16-byte aligned", fn); \
+  } while (0)
+
+constexpr uint64_t kMaxElems = 0xFFFFFFFFull;
+
+fp8q_status check_k(const char* fn, uint32_t K) {
+  if (K == 0 || K % kGroup != 0) return fail(FP8Q_ERR_SHAPE, "%s: K=%u is not a positive multiple of 128", fn, K);
+  return FP8Q_OK;
+}
+
+fp8q_status check_mk(const char* fn, uint32_t M, uint32_t K) {
+  fp8q_status st = check_k(fn, K);
+  if (st != FP8Q_OK) return st;
+  if ((uint64_t)M * K > kMaxElems) return fail(FP8Q_ERR_SHAPE, "%s: M*K=%llu exceeds 2^32-1", fn, (unsigned long long)M * K);
+  return FP8Q_OK;
+}
+
+fp8q_status check_n(const char* fn, uint32_t M, uint32_t N, uint32_t K) {
+  if (N == 0 || N % kGroup != 0) return fail(FP8Q_ERR_SHAPE, "%s: N=%u is not a positive multiple of 128", fn, N);
+  if ((uint64_t)N * K > kMaxElems || (uint64_t)M * N > kMaxElems)
+    return fail(FP8Q_ERR_SHAPE, "%s: N*K or M*N exceeds 2^32-1", fn);
+  return FP8Q_OK;
+}
+
+// ---- device check: the current device must be gfx950; cached per device ----
+constexpr int kMaxDev = 64;
+std::atomic<int> g_dev_state[kMaxDev];  // 0 unknown, 1 gfx950, 2 other
+std::atomic<uint32_t> g_dev_cus[kMaxDev];
+
+fp8q_status check_device(const char* fn, uint32_t* cu_count = nullptr) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0)
+    return fail(FP8Q_ERR_DEVICE, "%s: no current HIP device", fn);
+  if (dev >= kMaxDev) return fail(FP8Q_ERR_DEVICE, "%s: device index %d unsupported", fn, dev);
+  int st = g_dev_state[dev].load(std::memory_order_acquire);
+  if (st == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess)
+      return fail(FP8Q_ERR_DEVICE, "%s: hipGetDeviceProperties failed", fn);
+    st = (strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+    g_dev_cus[dev].store((uint32_t)prop.multiProcessorCount, std::memory_order_relaxed);
+    g_dev_state[dev].store(st, std::memory_order_release);
+  }
+  if (st != 1) return fail(FP8Q_ERR_DEVICE, "%s: current device %d is not gfx950", fn, dev);
+  if (cu_count) *cu_count = g_dev_cus[dev].load(std::memory_order_relaxed);
+  return FP8Q_OK;
+}
+
+fp8q_status launched(const char* fn, hipError_t e) {
+  if (e != hipSuccess) return fail(FP8Q_ERR_LAUNCH, "%s: launch failed: %s", fn, hipGetErrorString(e));
+  return ok();
+}
+
+// ---- selector lever and log ----
+// FP8Q_QUANT_VARIANT: "a" = variant B not requested, "b" = force B,
+// anything else / unset = auto.  Read once per process.
+int env_variant() {
+  static const int v = [] {
+    const char* e = getenv("FP8Q_QUANT_VARIANT");
+    if (e && (e[0] == 'a' || e[0] == 'A') && e[1] == '\0') return 1;
+    if (e && (e[0] == 'b' || e[0] == 'B') && e[1] == '\0') return 2;
+    return 0;
+  }();
+  return v;
+}
+
+bool log_enabled() {
+  static const bool on = [] {
+    const char* e = getenv("FP8Q_LOG");
+    return e && e[0] == '1';
+  }();
+  return on;
+}
+
+const char* const kRejects[3] = {
+    "variant B not requested",
+    "variant B absent",
+    "too few workgroups for variant B to fill the device",
+};
+
+std::once_flag g_log_once[4];
+
+void log_pick(int variant, const char* reject, int requested, uint32_t M, uint32_t K,
+              const uint32_t grid[3]) {
+  if (!log_enabled()) return;
+  const int slot = fp8q_quant_log_slot(variant, reject, requested);
+  if (slot < 0) return;
+  std::call_once(g_log_once[slot], [&] {
+    if (reject)
+      fprintf(stderr, "fp8q: act-quant variant B not used at M=%u K=%u: %s (FP8Q_QUANT_VARIANT)\n",
+              M, K, reject);
+    else
+      fprintf(stderr, "fp8q: act-quant variant B (K-grouped) at M=%u K=%u grid=(%u,%u,1) block=%u\n",
+              M, K, grid[0], grid[1], 64 * kQuantBWaves);
+  });
+}
+
+uint32_t ceil_div(uint64_t a, uint64_t b) { return (uint32_t)((a + b - 1) / b); }
+
+fp8q_status run_quant(const char* fn, const uint16_t* x, uint8_t* q, float* srm, float* skm,
+                      uint32_t M, uint32_t K, int variant, hipStream_t s) {
+  uint32_t cus = 0;
+  fp8q_status st = check_device(fn, &cus);
+  if (st != FP8Q_OK) return st;
+  if (variant == 0) {
+    const int env = env_variant();
+    if (env == 2) {
+      variant = 2;
+    } else {
+      uint32_t grid[3];
+      const char* reject = nullptr;
+      fp8q_select_params p = fp8q_default_select_params(cus);
+      variant = fp8q_quant_select_with(M, K, &p, grid, &reject);
+      log_pick(variant, reject, p.requested, M, K, grid);
+    }
+  }
+  hipError_t e = (variant == 2) ? launch_quant_b(x, q, srm, skm, M, K, s)
+                                : launch_quant_a(x, q, srm, skm, M, K, s);
+  if (e == hipSuccess && skm) e = launch_kmajor_pad(skm, M, K, s);
+  return launched(fn, e);
+}
+
+// GEMM kernel choice: the skinny kernel up to this many rows.
+constexpr uint32_t kSkinnyAutoMaxM = 32;
+
+fp8q_status run_gemm(const char* fn, const uint8_t* a, const float* as, const uint8_t* w,
+                     const float* ws, uint16_t* out, uint32_t M, uint32_t N, uint32_t K, int kernel,
+                     hipStream_t s) {
+  if (kernel == 0) kernel = (M <= kSkinnyAutoMaxM) ? 2 : 1;
+  if (kernel == 2 && M > kSkinnyMaxM)
+    return fail(FP8Q_ERR_VARIANT, "%s: skinny kernel needs M <= %u (M=%u)", fn, kSkinnyMaxM, M);
+  const hipError_t e = (kernel == 2) ? launch_gemm_skinny(a, as, w, ws, out, M, N, K, s)
+                                     : launch_gemm_tiled(a, as, w, ws, out, M, N, K, s);
+  return launched(fn, e);
+}
+
+}  // namespace
+
+extern "C" {
+
+uint32_t fp8q_m_pad(uint32_t m) { return m_pad16(m); }
+
+const char* fp8q_last_error(void) { return g_err; }
+
+const char* fp8q_version(void) { return "fp8q 0.1.0 gfx950"; }
+
+fp8q_select_params fp8q_default_select_params(uint32_t cu_count) {
+  fp8q_select_params p;
+  p.cu_count = cu_count;
+  p.min_wg_per_cu = kQuantMinWgPerCu;
+  p.b_groups_per_wg = kQuantBGroupsPerWg;
+  p.a_groups_per_wg = kQuantAGroupsPerWg;
+  p.requested = env_variant() != 1;
+  p.b_present = 1;
+  p.a_present = 1;
+  return p;
+}
+
+int fp8q_quant_select_with(uint32_t M, uint32_t K, const fp8q_select_params* p,
+                           uint32_t grid_out[3], const char** reject) {
+  const char* fn = "fp8q_quant_select";
+  if (p == nullptr) {
+    fail(FP8Q_ERR_NULL, "%s: params is NULL", fn);
+    return -1;
+  }
+  if (K == 0 || K % kGroup != 0 || p->b_groups_per_wg == 0 || p->a_groups_per_wg == 0 ||
+      (!p->a_present && !p->b_present)) {
+    fail(FP8Q_ERR_SHAPE, "%s: K=%u invalid or no variant present", fn, K);
+    return -1;
+  }
+  const uint32_t G = K / kGroup;
+  const uint32_t gx_b = ceil_div(G, p->b_groups_per_wg);
+  const uint64_t wg_b = (uint64_t)gx_b * M;
+  const uint64_t floor_wg = (uint64_t)p->min_wg_per_cu * (p->cu_count ? p->cu_count : 1);
+  const char* why = nullptr;
+  if (!p->b_present)
+    why = kRejects[1];
+  else if (!p->a_present)
+    why = nullptr;
+  else if (!p->requested)
+    why = kRejects[0];
+  else if (wg_b < floor_wg)
+    why = kRejects[2];
+  const int variant = why ? 1 : 2;
+  if (grid_out) {
+    if (variant == 2) {
+      grid_out[0] = M;
+      grid_out[1] = gx_b;
+    } else {
+      grid_out[0] = ceil_div((uint64_t)M * G, p->a_groups_per_wg);
+      grid_out[1] = 1;
+    }
+    grid_out[2] = 1;
+  }
+  if (reject) *reject = why;
+  return variant;
+}
+
+int fp8q_quant_select(uint32_t M, uint32_t K, uint32_t cu_count, uint32_t grid_out[3],
+                      const char** reject) {
+  const fp8q_select_params p = fp8q_default_select_params(cu_count);
+  return fp8q_quant_select_with(M, K, &p, grid_out, reject);
+}
+
+uint32_t fp8q_quant_b_min_m(uint32_t K, const fp8q_select_params* p) {
+  if (p == nullptr || K == 0 || K % kGroup != 0 || p->b_groups_per_wg == 0) return 0;
+  const uint32_t gx_b = ceil_div(K / kGroup, p->b_groups_per_wg);
+  const uint64_t floor_wg = (uint64_t)p->min_wg_per_cu * (p->cu_count ? p->cu_count : 1);
+  return ceil_div(floor_wg, gx_b);
+}
+
+int fp8q_quant_log_slot(int variant, const char* reject, int requested) {
+  if (variant == 2 && reject == nullptr) return 3;
+  if (!requested) return -1;
+  for (int i = 0; i < 3; ++i)
+    if (reject && strcmp(reject, kRejects[i]) == 0) return i;
+  return -1;
+}
+
+fp8q_status fp8q_quant_act_ex(const uint16_t* x_bf16, uint8_t* q_e4m3, float* scale_rm,
+                              uint32_t M, uint32_t K, int variant, hipStream_t stream) {
+  const char* fn = "fp8q_quant_act";
+  if (variant < 0 || variant > 2) return fail(FP8Q_ERR_VARIANT, "%s: variant %d out of range", fn, variant);
+  fp8q_status st = check_mk(fn, M, K);
+  if (st != FP8Q_OK) return st;
+  REQUIRE_PTR(x_bf16);
+  REQUIRE_PTR(q_e4m3);
+  REQUIRE_PTR(scale_rm);
+  if (M == 0) return ok();
+  return run_quant(fn, x_bf16, q_e4m3, scale_rm, nullptr, M, K, variant, stream);
+}
+
+fp8q_status fp8q_quant_act(const uint16_t* x_bf16, uint8_t* q_e4m3, float* scale_rm, uint32_t M,
+                           uint32_t K, hipStream_t stream) {
+  return fp8q_quant_act_ex(x_bf16, q_e4m3, scale_rm, M, K, 0, stream);
+}
+
+fp8q_status fp8q_quant_act_kmajor(const uint16_t* x_bf16, uint8_t* q_e4m3, float* scale_rm,
+                                  float* scale_km, uint32_t M, uint32_t K, hipStream_t stream) {
+  const char* fn = "fp8q_quant_act_kmajor";
+  fp8q_status st = check_mk(fn, M, K);
+  if (st != FP8Q_OK) return st;
+  if ((uint64_t)m_pad16(M) * K > kMaxElems) return fail(FP8Q_ERR_SHAPE, "%s: Mp*K exceeds 2^32-1", fn);
+  REQUIRE_PTR(x_bf16);
+  REQUIRE_PTR(q_e4m3);
+  REQUIRE_PTR(scale_km);
+  if (scale_rm != nullptr && !aligned16(scale_rm))
+    return fail(FP8Q_ERR_ALIGN, "%s: scale_rm is not 16-byte aligned", fn);
+  if (M == 0) return ok();
+  return run_quant(fn, x_bf16, q_e4m3, scale_rm, scale_km, M, K, 0, stream);
+}
+
+fp8q_status fp8q_scale_to_kmajor(const float* scale_rm, float* scale_km, uint32_t M, uint32_t K,
+                                 hipStream_t stream) {
+  const char* fn = "fp8q_scale_to_kmajor";
+  fp8q_status st = check_mk(fn, M, K);
+  if (st != FP8Q_OK) return st;
+  if ((uint64_t)m_pad16(M) * K > kMaxElems) return fail(FP8Q_ERR_SHAPE, "%s: Mp*K exceeds 2^32-1", fn);
+  REQUIRE_PTR(scale_rm);
+  REQUIRE_PTR(scale_km);
+  if (M == 0) return ok();
+  st = check_device(fn);
+  if (st != FP8Q_OK) return st;
+  return launched(fn, launch_relayout(scale_rm, scale_km, M, K, stream));
+}
+
+fp8q_status fp8q_gemm_blockscaled_ex(const uint8_t* a_e4m3, const float* a_scale_km,
+                                     const uint8_t* w_e4m3, const float* w_scale,
+                                     uint16_t* out_bf16, uint32_t M, uint32_t N, uint32_t K,
+                                     int kernel, hipStream_t stream) {
+  const char* fn = "fp8q_gemm_blockscaled";
+  if (kernel < 0 || kernel > 2) return fail(FP8Q_ERR_VARIANT, "%s: kernel %d out of range", fn, kernel);
+  fp8q_status st = check_mk(fn, M, K);
+  if (st != FP8Q_OK) return st;
+  st = check_n(fn, M, N, K);
+  if (st != FP8Q_OK) return st;
+  if ((uint64_t)m_pad16(M) * K > kMaxElems) return fail(FP8Q_ERR_SHAPE, "%s: Mp*K exceeds 2^32-1", fn);
+  REQUIRE_PTR(a_e4m3);
+  REQUIRE_PTR(a_scale_km);
+  REQUIRE_PTR(w_e4m3);
+  REQUIRE_PTR(w_scale);
+  REQUIRE_PTR(out_bf16);
+  if (M == 0) return ok();
+  st = check_device(fn);
+  if (st != FP8Q_OK) return st;
+  return run_gemm(fn, a_e4m3, a_scale_km, w_e4m3, w_scale, out_bf16, M, N, K, kernel, stream);
+}
+
+fp8q_status fp8q_gemm_blockscaled(const uint8_t* a_e4m3, const float* a_scale_km,
+                                  const uint8_t* w_e4m3, const float* w_scale, uint16_t* out_bf16,
+                                  uint32_t M, uint32_t N, uint32_t K, hipStream_t stream) {
+  return fp8q_gemm_blockscaled_ex(a_e4m3, a_scale_km, w_e4m3, w_scale, out_bf16, M, N, K, 0, stream);
+}
+
+fp8q_status fp8q_proj(const uint16_t* x_bf16, const uint8_t* w_e4m3, const float* w_scale,
+                      uint16_t* out_bf16, uint8_t* act_q_scratch, float* act_scale_scratch,
+                      float* act_scale_km_scratch, uint32_t M, uint32_t N, uint32_t K,
+                      hipStream_t stream) {
+  const char* fn = "fp8q_proj";
+  fp8q_status st = check_mk(fn, M, K);
+  if (st != FP8Q_OK) return st;
+  st = check_n(fn, M, N, K);
+  if (st != FP8Q_OK) return st;
+  if ((uint64_t)m_pad16(M) * K > kMaxElems) return fail(FP8Q_ERR_SHAPE, "%s: Mp*K exceeds 2^32-1", fn);
+  REQUIRE_PTR(x_bf16);
+  REQUIRE_PTR(w_e4m3);
+  REQUIRE_PTR(w_scale);
+  REQUIRE_PTR(out_bf16);
+  REQUIRE_PTR(act_q_scratch);
+  REQUIRE_PTR(act_scale_scratch);
+  REQUIRE_PTR(act_scale_km_scratch);
+  if (M == 0) return ok();
+  st = run_quant(fn, x_bf16, act_q_scratch, act_scale_scratch, nullptr, M, K, 0, stream);
+  if (st != FP8Q_OK) return st;
+  st = launched(fn, launch_relayout(act_scale_scratch, act_scale_km_scratch, M, K, stream));
+  if (st != FP8Q_OK) return st;
+  return run_gemm(fn, act_q_scratch, act_scale_km_scratch, w_e4m3, w_scale, out_bf16, M, N, K, 0,
+                  stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,52 @@
+// Internal launch interface between the C-ABI layer (fp8q_api.hip) and the
+// kernel translation units.  Launchers assume validated arguments: shapes
+// checked, pointers non-NULL and aligned, M > 0.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp8q {
+
+constexpr uint32_t kGroup = 128;  // K elements per scale group / weight block edge
+
+// native 128-/64-bit vectors (usable with the nontemporal builtins)
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// ---- quantizer geometry (shared with the selector) ----
+// Variant A: flat over all M*(K/128) groups, one 16-lane row per group,
+// 4 groups per wave, kQuantAWaves waves per workgroup.
+constexpr uint32_t kQuantAWaves = 4;
+constexpr uint32_t kQuantAGroupsPerWg = 4 * kQuantAWaves;
+// Variant B: K-grouped; a workgroup covers kQuantBGroupsPerWg consecutive
+// groups of one token row, kQuantBRounds groups per 16-lane row.
+constexpr uint32_t kQuantBWaves = 4;
+constexpr uint32_t kQuantBRounds = 2;
+constexpr uint32_t kQuantBGroupsPerWg = 4 * kQuantBWaves * kQuantBRounds;
+// Floor of the selection rule on gfx950 (workgroups per CU).
+constexpr uint32_t kQuantMinWgPerCu = 2;
+
+hipError_t launch_quant_a(const uint16_t* x, uint8_t* q, float* scale_rm,
+                          float* scale_km, uint32_t M, uint32_t K, hipStream_t s);
+hipError_t launch_quant_b(const uint16_t* x, uint8_t* q, float* scale_rm,
+                          float* scale_km, uint32_t M, uint32_t K, hipStream_t s);
+// K-major pad slots m in [M, ceil16(M)) of scale_km are written by this
+// launcher when the quantizer writes scale_km directly.
+hipError_t launch_kmajor_pad(float* scale_km, uint32_t M, uint32_t K, hipStream_t s);
+
+hipError_t launch_relayout(const float* scale_rm, float* scale_km, uint32_t M,
+                           uint32_t K, hipStream_t s);
+
+// GEMM kernels.  kind 1 = LDS-tiled MFMA, kind 2 = skinny (M <= 64).
+constexpr uint32_t kSkinnyMaxM = 64;
+hipError_t launch_gemm_tiled(const uint8_t* a, const float* a_s_km, const uint8_t* w,
+                             const float* w_s, uint16_t* out, uint32_t M, uint32_t N,
+                             uint32_t K, hipStream_t s);
+hipError_t launch_gemm_skinny(const uint8_t* a, const float* a_s_km, const uint8_t* w,
+                              const float* w_s, uint16_t* out, uint32_t M, uint32_t N,
+                              uint32_t K, hipStream_t s);
+
+inline uint32_t m_pad16(uint32_t m) { return (m + 15u) / 16u * 16u; }
+
+}  // namespace fp8q

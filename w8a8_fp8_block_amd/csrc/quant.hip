@@ -1,0 +1,179 @@
+// Per-(token, 128-group) FP8 e4m3 activation quantizer for gfx950.
+//
+// Method (page "dispatch_proj.rs", doc of cublas_fp8_proj; page
+// "fp8_act_quant_floor.rs" for the two launch shapes): for every group of 128
+// consecutive K elements of a token row, scale = fl32(amax / 448) and each
+// element becomes the OCP e4m3fn code of x / scale (round to nearest even,
+// saturating at +-448).  The input is a flat sequence of M*(K/128) groups of
+// 128 bf16, so group i lives at x + 128*i, its codes at q + 128*i and its
+// row-major scale at scale_rm[i].
+//
+// Work split: one 16-lane DPP row of a wave owns one group; each lane holds 8
+// bf16 (one 128-bit load) and produces 8 codes (one 64-bit store).  The group
+// maximum is an integer max over bf16 magnitudes (packed u16 max, then a
+// 4-step DPP butterfly inside the row), which is exact and needs no float
+// canonicalization.
+//
+// Exactness of q = fl32(x / scale) without a divide per element: with
+// r = fl32(1 / scale) (a correctly rounded divide, once per group),
+//   q0 = x * r,  en = fma(q0, scale, -x),  q1 = fma(-en, r, q0)
+// is the correctly rounded quotient, signed zeros included, for every bf16
+// pair (x, amax) whose scale is at least 2^-100; groups with a smaller (or zero) scale take an exact
+// per-element divide instead.  The e4m3 code is the hardware conversion of
+// q1 clamped to [-448, 448] (values in (448, 464) round to 448 anyway).
+// The exhaustive (x, amax) test checks the whole map on the device.
+#include "fp8q_internal.h"
+
+namespace fp8q {
+namespace {
+
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t dpp_row_max_u32(uint32_t v) {
+  // quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_half_mirror, row_mirror:
+  // after the four steps every lane of the 16-lane row holds the row max.
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, false));
+  return v;
+}
+
+__device__ __forceinline__ u16x2 as_u16x2(uint32_t v) { return __builtin_bit_cast(u16x2, v); }
+
+// bf16 pair in one dword -> two floats (exact)
+__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// Quantize the group held by this lane's 16-lane row.  v = this lane's 8 bf16;
+// returns the 8 codes (little-endian bytes in element order) and the scale.
+__device__ __forceinline__ u32x2 quant_group(u32x4 v, float& scale_out) {
+  const uint32_t mag = 0x7FFF7FFFu;
+  u16x2 m01 = __builtin_elementwise_max(as_u16x2(v.x & mag), as_u16x2(v.y & mag));
+  u16x2 m23 = __builtin_elementwise_max(as_u16x2(v.z & mag), as_u16x2(v.w & mag));
+  u16x2 mm = __builtin_elementwise_max(m01, m23);
+  uint32_t amax_bits = max((uint32_t)mm.x, (uint32_t)mm.y);
+  amax_bits = dpp_row_max_u32(amax_bits);
+  const float amax = __uint_as_float(amax_bits << 16);
+  const float s = amax / 448.0f;  // IEEE (correctly rounded) divide
+  scale_out = s;
+
+  float x[8] = {bf_lo(v.x), bf_hi(v.x), bf_lo(v.y), bf_hi(v.y),
+                bf_lo(v.z), bf_hi(v.z), bf_lo(v.w), bf_hi(v.w)};
+  float q[8];
+  const bool slow = !(s >= 0x1p-100f);  // zero or tiny scale
+  if (__builtin_amdgcn_ballot_w64(slow) == 0) {
+    const float r = 1.0f / s;  // correctly rounded reciprocal
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      // en = q0*s - x is the negated residual; q1 = q0 - en*r.  Written this
+      // way round, x = -0 gives en = +0 and q1 = -0 + -0 = -0, keeping the sign
+      // (the residual x - q0*s would be +0 and turn q1 into +0).
+      const float q0 = x[i] * r;
+      const float en = __builtin_fmaf(q0, s, -x[i]);
+      q[i] = __builtin_fmaf(-en, r, q0);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) q[i] = (s == 0.0f) ? x[i] : x[i] / s;
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) q[i] = __builtin_amdgcn_fmed3f(q[i], -448.0f, 448.0f);
+  int lo = __builtin_amdgcn_cvt_pk_fp8_f32(q[0], q[1], 0, false);
+  lo = __builtin_amdgcn_cvt_pk_fp8_f32(q[2], q[3], lo, true);
+  int hi = __builtin_amdgcn_cvt_pk_fp8_f32(q[4], q[5], 0, false);
+  hi = __builtin_amdgcn_cvt_pk_fp8_f32(q[6], q[7], hi, true);
+  return u32x2{(uint32_t)lo, (uint32_t)hi};
+}
+
+__device__ __forceinline__ void write_scales(float s, uint64_t g, float* __restrict__ srm,
+                                             float* __restrict__ skm, uint32_t G, uint32_t Mp) {
+  if (srm) srm[g] = s;
+  if (skm) {
+    const uint32_t m = (uint32_t)(g / G), gg = (uint32_t)(g % G);
+    skm[(uint64_t)gg * Mp + m] = s;
+  }
+}
+
+// Variant A (fine-grained): flat over groups, 4 groups per wave, one round.
+__global__ __launch_bounds__(64 * kQuantAWaves) void quant_a_kernel(
+    const u32x4* __restrict__ x, u32x2* __restrict__ q, float* __restrict__ srm,
+    float* __restrict__ skm, uint64_t ngroups, uint32_t G, uint32_t Mp) {
+  const uint64_t g = (uint64_t)blockIdx.x * kQuantAGroupsPerWg + (threadIdx.x >> 4);
+  if (g >= ngroups) return;  // whole 16-lane rows retire together
+  const uint64_t idx = g * 16 + (threadIdx.x & 15);
+  const u32x4 v = __builtin_nontemporal_load(&x[idx]);
+  float s;
+  const u32x2 c = quant_group(v, s);
+  q[idx] = c;
+  if ((threadIdx.x & 15) == 0) write_scales(s, g, srm, skm, G, Mp);
+}
+
+// Variant B (K-grouped): workgroup (m, by) covers groups
+// [by*kQuantBGroupsPerWg, ...) of token row m; each 16-lane row takes
+// kQuantBRounds groups, all loads issued before any is consumed.
+__global__ __launch_bounds__(64 * kQuantBWaves) void quant_b_kernel(
+    const u32x4* __restrict__ x, u32x2* __restrict__ q, float* __restrict__ srm,
+    float* __restrict__ skm, uint32_t G, uint32_t Mp) {
+  const uint32_t m = blockIdx.x;
+  const uint32_t wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const uint32_t g0 = blockIdx.y * kQuantBGroupsPerWg + wave * 4 * kQuantBRounds + (lane >> 4);
+  u32x4 v[kQuantBRounds];
+#pragma unroll
+  for (uint32_t r = 0; r < kQuantBRounds; ++r) {
+    const uint32_t gg = g0 + 4 * r;
+    if (gg < G) v[r] = __builtin_nontemporal_load(&x[((uint64_t)m * G + gg) * 16 + (lane & 15)]);
+  }
+#pragma unroll
+  for (uint32_t r = 0; r < kQuantBRounds; ++r) {
+    const uint32_t gg = g0 + 4 * r;
+    if (gg < G) {
+      float s;
+      const uint64_t g = (uint64_t)m * G + gg;
+      const u32x2 c = quant_group(v[r], s);
+      q[g * 16 + (lane & 15)] = c;
+      if ((lane & 15) == 0) write_scales(s, g, srm, skm, G, Mp);
+    }
+  }
+}
+
+// Zero the K-major pad slots m in [M, Mp) of every group column.
+__global__ __launch_bounds__(256) void kmajor_pad_kernel(float* __restrict__ skm, uint32_t M,
+                                                         uint32_t Mp, uint32_t G) {
+  const uint32_t padw = Mp - M;
+  const uint32_t i = blockIdx.x * 256 + threadIdx.x;
+  if (i < padw * G) skm[(uint64_t)(i / padw) * Mp + M + i % padw] = 0.0f;
+}
+
+}  // namespace
+
+hipError_t launch_quant_a(const uint16_t* x, uint8_t* q, float* scale_rm, float* scale_km,
+                          uint32_t M, uint32_t K, hipStream_t s) {
+  const uint32_t G = K / kGroup;
+  const uint64_t ngroups = (uint64_t)M * G;
+  const uint64_t grid = (ngroups + kQuantAGroupsPerWg - 1) / kQuantAGroupsPerWg;
+  quant_a_kernel<<<dim3((uint32_t)grid), dim3(64 * kQuantAWaves), 0, s>>>(
+      reinterpret_cast<const u32x4*>(x), reinterpret_cast<u32x2*>(q), scale_rm, scale_km,
+      ngroups, G, m_pad16(M));
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_b(const uint16_t* x, uint8_t* q, float* scale_rm, float* scale_km,
+                          uint32_t M, uint32_t K, hipStream_t s) {
+  const uint32_t G = K / kGroup;
+  const uint32_t gy = (G + kQuantBGroupsPerWg - 1) / kQuantBGroupsPerWg;
+  quant_b_kernel<<<dim3(M, gy), dim3(64 * kQuantBWaves), 0, s>>>(
+      reinterpret_cast<const u32x4*>(x), reinterpret_cast<u32x2*>(q), scale_rm, scale_km, G,
+      m_pad16(M));
+  return hipGetLastError();
+}
+
+hipError_t launch_kmajor_pad(float* scale_km, uint32_t M, uint32_t K, hipStream_t s) {
+  const uint32_t Mp = m_pad16(M), G = K / kGroup;
+  if (Mp == M) return hipSuccess;
+  const uint32_t n = (Mp - M) * G;
+  kmajor_pad_kernel<<<dim3((n + 255) / 256), dim3(256), 0, s>>>(scale_km, M, Mp, G);
+  return hipGetLastError();
+}
+
+}  // namespace fp8q
