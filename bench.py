@@ -36,9 +36,18 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0      # MI355X HBM3E, GB/s
 FP8_PEAK_TFLOPS = 5000.0   # MI355X dense FP8 MFMA, TFLOP/s
 # HBM bytes the rocprofv3 FETCH_SIZE/WRITE_SIZE counters attribute to one
-# launch of the dominant GEMM at the default workload (profiles/); None when
-# the kernel has changed since the counters were taken.
-GEMM_TRAFFIC_BYTES = None
+# launch of the dominant GEMM at the default workload, scaled by the counters'
+# readings for a plain 1 GiB copy (the HBM-bytes summary under profiles/).
+# Valid only for the GEMM source they were taken with: reported as null once
+# gemm.hip changes (its SHA-256 prefix is recorded here).
+GEMM_TRAFFIC = {"bytes": 1.399e9 + 46.86e6, "gemm_source_sha256": "935815a2f5bb8cf1"}
+
+
+def gemm_traffic():
+    import hashlib
+    src = os.path.join(ROOT, "w8a8_fp8_block_amd", "csrc", "gemm.hip")
+    h = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    return GEMM_TRAFFIC["bytes"] if h == GEMM_TRAFFIC["gemm_source_sha256"] else None
 
 
 def parse():
@@ -52,7 +61,21 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="approximate CPU time budget of the oracle sample")
+    p.add_argument("--copy-mib", type=int, default=0,
+                   help="instead of the benchmark, run 3 plain device copies of this many "
+                        "MiB (the reference kernel for scaling rocprofv3 byte counters)")
     return p.parse_args()
+
+
+def copy_calibration(mib: int):
+    import torch
+    n = mib << 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n, "launches": 3}), flush=True)
 
 
 def quantize_weights_gpu(wf):
@@ -101,9 +124,14 @@ def cpu_baseline(w, x_bits, wf, budget_s):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on exactly one GPU; --gpus {args.gpus} is not "
-              "supported (the projection's sharding is described in DESIGN.md)", file=sys.stderr)
+        print(f"bench.py: the projection runs on exactly one GPU here; --gpus {args.gpus} is "
+              "not supported (one GPU's share is the workload; multi-GPU sharding is not built)",
+              file=sys.stderr)
         sys.exit(2)
+
+    if args.copy_mib:
+        copy_calibration(args.copy_mib)
+        return
 
     import torch
     import synth
@@ -201,12 +229,12 @@ def main():
         },
         "roofline": {
             "bound": "mfma",
-            "kernel": "gemm_tiled_kernel",
+            "kernel": "gemm_skinny_kernel" if M <= 32 else "gemm_tiled_kernel",
             "achieved": round(gemm_tflops, 2),
             "peak": FP8_PEAK_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(gemm_tflops / FP8_PEAK_TFLOPS, 4),
-            "traffic": GEMM_TRAFFIC_BYTES,
+            "traffic": gemm_traffic() if args.workload == "large_prefill" else None,
             "avg_launch_us": round(gemm_avg_s * 1e6, 2),
             "algorithmic_flops_per_launch": flops,
         },

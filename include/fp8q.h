@@ -190,8 +190,11 @@ fp8q_status fp8q_gemm_blockscaled(const uint8_t *a_e4m3, const float *a_scale_km
                                   uint32_t K, hipStream_t stream);
 
 /* As fp8q_gemm_blockscaled with the kernel forced: 0 = auto, 1 = the
- * LDS-tiled MFMA kernel (prefill widths), 2 = the skinny kernel (decode
- * widths, needs M <= 64).  Other values -> FP8Q_ERR_VARIANT. */
+ * LDS-tiled MFMA kernel (prefill widths; 128x128 tiles, two workgroups per
+ * CU), 2 = the skinny kernel (decode widths, needs M <= 64), 3..4 = other
+ * shapes of the LDS-tiled kernel, kept for measurement (3 = 256x128 tiles
+ * with 8 waves, 4 = 256x128 tiles with 4 waves).  Other values ->
+ * FP8Q_ERR_VARIANT. */
 fp8q_status fp8q_gemm_blockscaled_ex(const uint8_t *a_e4m3, const float *a_scale_km,
                                      const uint8_t *w_e4m3, const float *w_scale,
                                      uint16_t *out_bf16, uint32_t M, uint32_t N,

@@ -100,7 +100,8 @@ def test_gemm_validation():
     assert L.fp8q_gemm_blockscaled(g, g, g, g, g, 4, 128, 130, None) == 2   # K % 128
     assert L.fp8q_gemm_blockscaled(g, g, None, g, g, 4, 128, 128, None) == 1
     assert L.fp8q_gemm_blockscaled(g, g, g, g, BAD, 4, 128, 128, None) == 3
-    assert L.fp8q_gemm_blockscaled_ex(g, g, g, g, g, 4, 128, 128, 7, None) == 6
+    assert L.fp8q_gemm_blockscaled_ex(g, g, g, g, g, 4, 128, 128, 5, None) == 6
+    assert L.fp8q_gemm_blockscaled_ex(g, g, g, g, g, 4, 128, 128, -1, None) == 6
     assert L.fp8q_gemm_blockscaled(g, g, g, g, g, 0, 128, 128, None) == 0
     assert L.fp8q_proj(g, g, g, g, g, g, None, 4, 128, 128, None) == 1
     assert "act_scale_km_scratch" in _err()

@@ -63,8 +63,13 @@ def orc_errors(o, r, rms=None):
     return oracle.gemm_errors(o, r, rms)
 
 
-def _kernels_for(M):
-    return (0, 1, 2) if M <= 64 else (0, 1)
+def _kernels_for(M, N=256):
+    """Every kernel the API can force for this shape: auto, the default tiled
+    kernel, the skinny kernel (M <= 64) and the other tile shapes."""
+    ks = [0, 1]
+    if M <= 64:
+        ks.append(2)
+    return tuple(ks + [3, 4])
 
 
 @pytest.mark.parametrize("M,N,K", [(16, 256, 512), (1, 128, 128), (17, 384, 640), (33, 256, 1152),
@@ -76,7 +81,7 @@ def test_gemm_small_full(orc, M, N, K):
     a, a_s = orc.quant_act(x)
     wq, ws = orc.quant_weight_block(rng.normal(0, 0.02, (N, K)).astype(np.float32))
     ref = orc.gemm_ref(a, a_s, wq, ws)
-    for kern in _kernels_for(M):
+    for kern in _kernels_for(M, N):
         log(f"gemm M={M} N={N} K={K} kernel={kern}")
         _assert_tol(_gemm_gpu(orc, a, a_s, wq, ws, kern), ref, f"M{M}N{N}K{K}k{kern}")
 
@@ -85,7 +90,7 @@ def test_gemm_tiny_workload(orc):
     w = synth.workload("tiny")
     _, a, a_s, wq, ws = _operands(orc, w)
     ref = orc.gemm_ref(a, a_s, wq, ws)
-    for kern in (0, 1, 2):
+    for kern in _kernels_for(w.M, w.N):
         log(f"gemm tiny kernel={kern}")
         _assert_tol(_gemm_gpu(orc, a, a_s, wq, ws, kern), ref, f"tiny k{kern}")
 
@@ -96,7 +101,7 @@ def test_gemm_decode_workload_full(orc, M):
     _, a, a_s, wq, ws = _operands(orc, w)
     log(f"oracle decode M={M}")
     ref = orc.gemm_ref(a, a_s, wq, ws)
-    for kern in (0, 1, 2):
+    for kern in _kernels_for(M, w.N):
         log(f"gemm decode M={M} kernel={kern}")
         _assert_tol(_gemm_gpu(orc, a, a_s, wq, ws, kern), ref, f"decode M{M} k{kern}")
 
@@ -123,11 +128,11 @@ def test_gemm_prefill_workloads_sampled(orc, name):
     log(f"oracle {w.desc} samples={len(ms)}")
     ref = orc.gemm_ref_at(a, a_s, wq, ws, ms, ns)
     rms = float(np.sqrt(np.mean(ref * ref)))
-    log(f"gemm {w.desc}")
-    o = _gemm_gpu(orc, a, a_s, wq, ws, 0)
-    _assert_tol(o[ms, ns], ref, w.desc, rms)
-    # no NaN/Inf anywhere in the full output, and rows beyond the sample are sane
-    assert np.all(np.isfinite(o))
+    for kern in _kernels_for(w.M, w.N):
+        log(f"gemm {w.desc} kernel={kern}")
+        o = _gemm_gpu(orc, a, a_s, wq, ws, kern)
+        _assert_tol(o[ms, ns], ref, f"{w.desc} k{kern}", rms)
+        assert np.all(np.isfinite(o))
 
 
 def test_gemm_block_scale_isolation_exact(orc):
@@ -140,7 +145,7 @@ def test_gemm_block_scale_isolation_exact(orc):
     a_s = np.array([[2.0 ** (m % 5)] * G for m in range(M)], dtype=np.float32)
     ws = np.array([[2.0 ** g * (nb + 1) for g in range(G)] for nb in range(N // 128)], dtype=np.float32)
     ref = orc.gemm_ref(a, a_s, wq, ws)
-    for kern in _kernels_for(M):
+    for kern in _kernels_for(M, N):
         o = _gemm_gpu(orc, a, a_s, wq, ws, kern)
         assert np.array_equal(o, ref), f"kernel {kern}"
 
@@ -159,7 +164,7 @@ def test_gemm_one_hot_rows_exact(orc):
     ref = orc.gemm_ref(a, a_s, wq, ws)
     want = bf16_bits_to_f64(synth.f32_to_bf16_bits(ref.astype(np.float32)))  # exact in fp32
     assert np.array_equal(ref.astype(np.float32).astype(np.float64), ref)
-    for kern in _kernels_for(M):
+    for kern in _kernels_for(M, N):
         o = _gemm_gpu(orc, a, a_s, wq, ws, kern)
         assert np.array_equal(o, want), f"kernel {kern}"
 
@@ -180,7 +185,7 @@ def test_gemm_small_integers_exact(orc):
     ref = orc.gemm_ref(a, a_s, wq, ws)
     assert np.array_equal(ref.astype(np.float32).astype(np.float64), ref)
     want = bf16_bits_to_f64(synth.f32_to_bf16_bits(ref.astype(np.float32)))
-    for kern in _kernels_for(M):
+    for kern in _kernels_for(M, N):
         o = _gemm_gpu(orc, a, a_s, wq, ws, kern)
         assert np.array_equal(o, want), f"kernel {kern}"
 
@@ -201,7 +206,7 @@ def test_gemm_rowmajor_scales_fail(orc):
     wrong = np.zeros((K // 128) * Mp, dtype=np.float32)
     wrong[: a_s.size] = a_s.ravel()
     wrong = wrong.reshape(K // 128, Mp)
-    for kern in _kernels_for(M):
+    for kern in _kernels_for(M, N):
         o = _gemm_gpu(orc, a, a_s, wq, ws, kern, km=wrong)
         rel, exc, _ = orc_errors(o, ref)
         log(f"  row-major control kernel {kern}: rel_rms={rel:.3e} worst/bound={exc:.1f}")
@@ -237,7 +242,24 @@ def test_gemm_repeatable(orc):
     """Same inputs, same bits, run to run (no data races in the reduction)."""
     w = synth.workload("decode", M=25)
     _, a, a_s, wq, ws = _operands(orc, w)
-    for kern in (1, 2):
+    for kern in _kernels_for(25, w.N):
         o1 = _gemm_gpu(orc, a, a_s, wq, ws, kern)
         o2 = _gemm_gpu(orc, a, a_s, wq, ws, kern)
         assert np.array_equal(o1, o2)
+
+
+def test_gemm_long_k_weight_scale_chunks(orc):
+    """K spanning more than 1024 scale blocks (the tiled kernel stages the
+    weight scales 1024 blocks at a time)."""
+    M, N, K = 40, 256, 1030 * 128
+    rng = np.random.default_rng(21)
+    x = synth.f32_to_bf16_bits(rng.standard_normal((M, K)).astype(np.float32))
+    a, a_s = orc.quant_act(x)
+    wq, ws = orc.quant_weight_block(rng.normal(0, 0.02, (N, K)).astype(np.float32))
+    # make the weight scales of the second chunk clearly different
+    ws[:, 1024:] *= 3.0
+    log(f"oracle M={M} N={N} K={K}")
+    ref = orc.gemm_ref(a, a_s, wq, ws)
+    for kern in _kernels_for(M, N):
+        log(f"gemm long-K kernel={kern}")
+        _assert_tol(_gemm_gpu(orc, a, a_s, wq, ws, kern), ref, f"long-K k{kern}")

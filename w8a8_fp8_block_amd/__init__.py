@@ -4,8 +4,8 @@ Argument marshalling only: every function takes torch tensors that already
 live on the current GPU, passes their device pointers and the current torch
 stream to the C ABI (include/fp8q.h) and raises on a non-OK status.  Every
 step of the computation runs in the library's HIP kernels; there is no CPU
-or PyTorch fallback, and importing this module fails if the library has not
-been built (``python -m w8a8_fp8_block_amd.build``).
+or PyTorch fallback: the first call raises if the library has not been built
+(``python -m w8a8_fp8_block_amd.build``).
 
 Names match the C entry points:
 
@@ -33,13 +33,6 @@ import torch  # noqa: F401  (device memory and streams)
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libfp8q.so")
 
-if not os.path.exists(LIB_PATH):
-    raise ImportError(
-        f"{LIB_PATH} is missing: build it with `python -m w8a8_fp8_block_amd.build` "
-        "(the projection has no fallback path)")
-
-_lib = ctypes.CDLL(LIB_PATH)
-
 _P = ctypes.c_void_p
 _U = ctypes.c_uint32
 _I = ctypes.c_int
@@ -52,30 +45,46 @@ class SelectParams(ctypes.Structure):
                 ("a_present", ctypes.c_int)]
 
 
-def _sig(name, res, args):
-    f = getattr(_lib, name)
-    f.restype = res
-    f.argtypes = args
-    return f
+_SIGS = {
+    "fp8q_m_pad": (_U, [_U]),
+    "fp8q_last_error": (ctypes.c_char_p, []),
+    "fp8q_version": (ctypes.c_char_p, []),
+    "fp8q_quant_act": (_I, [_P, _P, _P, _U, _U, _P]),
+    "fp8q_quant_act_ex": (_I, [_P, _P, _P, _U, _U, _I, _P]),
+    "fp8q_quant_act_kmajor": (_I, [_P, _P, _P, _P, _U, _U, _P]),
+    "fp8q_default_select_params": (SelectParams, [_U]),
+    "fp8q_quant_select_with": (_I, [_U, _U, ctypes.POINTER(SelectParams),
+                                    ctypes.POINTER(_U * 3), ctypes.POINTER(ctypes.c_char_p)]),
+    "fp8q_quant_select": (_I, [_U, _U, _U, ctypes.POINTER(_U * 3),
+                               ctypes.POINTER(ctypes.c_char_p)]),
+    "fp8q_quant_b_min_m": (_U, [_U, ctypes.POINTER(SelectParams)]),
+    "fp8q_quant_log_slot": (_I, [_I, ctypes.c_char_p, _I]),
+    "fp8q_scale_to_kmajor": (_I, [_P, _P, _U, _U, _P]),
+    "fp8q_gemm_blockscaled": (_I, [_P, _P, _P, _P, _P, _U, _U, _U, _P]),
+    "fp8q_gemm_blockscaled_ex": (_I, [_P, _P, _P, _P, _P, _U, _U, _U, _I, _P]),
+    "fp8q_proj": (_I, [_P, _P, _P, _P, _P, _P, _P, _U, _U, _U, _P]),
+}
+
+_lib = None
 
 
-_sig("fp8q_m_pad", _U, [_U])
-_sig("fp8q_last_error", ctypes.c_char_p, [])
-_sig("fp8q_version", ctypes.c_char_p, [])
-_sig("fp8q_quant_act", _I, [_P, _P, _P, _U, _U, _P])
-_sig("fp8q_quant_act_ex", _I, [_P, _P, _P, _U, _U, _I, _P])
-_sig("fp8q_quant_act_kmajor", _I, [_P, _P, _P, _P, _U, _U, _P])
-_sig("fp8q_default_select_params", SelectParams, [_U])
-_sig("fp8q_quant_select_with", _I, [_U, _U, ctypes.POINTER(SelectParams),
-                                    ctypes.POINTER(_U * 3), ctypes.POINTER(ctypes.c_char_p)])
-_sig("fp8q_quant_select", _I, [_U, _U, _U, ctypes.POINTER(_U * 3),
-                               ctypes.POINTER(ctypes.c_char_p)])
-_sig("fp8q_quant_b_min_m", _U, [_U, ctypes.POINTER(SelectParams)])
-_sig("fp8q_quant_log_slot", _I, [_I, ctypes.c_char_p, _I])
-_sig("fp8q_scale_to_kmajor", _I, [_P, _P, _U, _U, _P])
-_sig("fp8q_gemm_blockscaled", _I, [_P, _P, _P, _P, _P, _U, _U, _U, _P])
-_sig("fp8q_gemm_blockscaled_ex", _I, [_P, _P, _P, _P, _P, _U, _U, _U, _I, _P])
-_sig("fp8q_proj", _I, [_P, _P, _P, _P, _P, _P, _P, _U, _U, _U, _P])
+def lib():
+    """The ctypes handle of libfp8q.so (raw C ABI), loaded on first use.
+    Raises if the library has not been built: there is no fallback path."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(
+                f"{LIB_PATH} is missing: build it with `python -m w8a8_fp8_block_amd.build` "
+                "(the projection has no fallback path)")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
 
 STATUS = {0: "FP8Q_OK", 1: "FP8Q_ERR_NULL", 2: "FP8Q_ERR_SHAPE", 3: "FP8Q_ERR_ALIGN",
           4: "FP8Q_ERR_DEVICE", 5: "FP8Q_ERR_LAUNCH", 6: "FP8Q_ERR_VARIANT"}
@@ -87,14 +96,9 @@ class Fp8qError(RuntimeError):
         self.status = status
 
 
-def lib():
-    """The ctypes handle (raw C ABI)."""
-    return _lib
-
-
 def _check(st: int):
     if st != 0:
-        raise Fp8qError(st, _lib.fp8q_last_error().decode())
+        raise Fp8qError(st, lib().fp8q_last_error().decode())
 
 
 def _ptr(t) -> int:
@@ -126,28 +130,28 @@ def _dims(t, nd):
 
 # ------------------------------------------------------------------ API
 def fp8q_m_pad(m: int) -> int:
-    return int(_lib.fp8q_m_pad(m))
+    return int(lib().fp8q_m_pad(m))
 
 
 def fp8q_version() -> str:
-    return _lib.fp8q_version().decode()
+    return lib().fp8q_version().decode()
 
 
 def fp8q_quant_act(x, q, scale_rm, variant: int = 0, stream=None):
     M, K = _dims(x, 2)
-    _check(_lib.fp8q_quant_act_ex(_ptr(x), _ptr(q), _ptr(scale_rm), M, K, variant,
+    _check(lib().fp8q_quant_act_ex(_ptr(x), _ptr(q), _ptr(scale_rm), M, K, variant,
                                   _stream(stream)))
 
 
 def fp8q_quant_act_kmajor(x, q, scale_rm, scale_km, stream=None):
     M, K = _dims(x, 2)
-    _check(_lib.fp8q_quant_act_kmajor(_ptr(x), _ptr(q), _optr(scale_rm), _ptr(scale_km), M, K,
+    _check(lib().fp8q_quant_act_kmajor(_ptr(x), _ptr(q), _optr(scale_rm), _ptr(scale_km), M, K,
                                       _stream(stream)))
 
 
 def fp8q_scale_to_kmajor(scale_rm, scale_km, stream=None):
     M, G = _dims(scale_rm, 2)
-    _check(_lib.fp8q_scale_to_kmajor(_ptr(scale_rm), _ptr(scale_km), M, G * 128,
+    _check(lib().fp8q_scale_to_kmajor(_ptr(scale_rm), _ptr(scale_km), M, G * 128,
                                      _stream(stream)))
 
 
@@ -156,7 +160,7 @@ def fp8q_gemm_blockscaled(a, a_scale_km, w, w_scale, out, kernel: int = 0, strea
     N, K2 = _dims(w, 2)
     if K2 != K:
         raise ValueError("a and w disagree on K")
-    _check(_lib.fp8q_gemm_blockscaled_ex(_ptr(a), _ptr(a_scale_km), _ptr(w), _ptr(w_scale),
+    _check(lib().fp8q_gemm_blockscaled_ex(_ptr(a), _ptr(a_scale_km), _ptr(w), _ptr(w_scale),
                                          _ptr(out), M, N, K, kernel, _stream(stream)))
 
 
@@ -165,19 +169,19 @@ def fp8q_proj(x, w, w_scale, out, act_q, act_scale, act_scale_km, stream=None):
     N, K2 = _dims(w, 2)
     if K2 != K:
         raise ValueError("x and w disagree on K")
-    _check(_lib.fp8q_proj(_ptr(x), _ptr(w), _ptr(w_scale), _ptr(out), _ptr(act_q),
+    _check(lib().fp8q_proj(_ptr(x), _ptr(w), _ptr(w_scale), _ptr(out), _ptr(act_q),
                           _ptr(act_scale), _ptr(act_scale_km), M, N, K, _stream(stream)))
 
 
 def fp8q_default_select_params(cu_count: int) -> SelectParams:
-    return _lib.fp8q_default_select_params(cu_count)
+    return lib().fp8q_default_select_params(cu_count)
 
 
 def fp8q_quant_select_with(M: int, K: int, params: SelectParams):
     """-> (variant, grid tuple, reject reason or None); variant -1 on bad args."""
     grid = (_U * 3)()
     why = ctypes.c_char_p()
-    v = _lib.fp8q_quant_select_with(M, K, ctypes.byref(params), ctypes.byref(grid),
+    v = lib().fp8q_quant_select_with(M, K, ctypes.byref(params), ctypes.byref(grid),
                                     ctypes.byref(why))
     return v, tuple(grid), (why.value.decode() if why.value else None)
 
@@ -185,17 +189,17 @@ def fp8q_quant_select_with(M: int, K: int, params: SelectParams):
 def fp8q_quant_select(M: int, K: int, cu_count: int):
     grid = (_U * 3)()
     why = ctypes.c_char_p()
-    v = _lib.fp8q_quant_select(M, K, cu_count, ctypes.byref(grid), ctypes.byref(why))
+    v = lib().fp8q_quant_select(M, K, cu_count, ctypes.byref(grid), ctypes.byref(why))
     return v, tuple(grid), (why.value.decode() if why.value else None)
 
 
 def fp8q_quant_b_min_m(K: int, params: SelectParams) -> int:
-    return int(_lib.fp8q_quant_b_min_m(K, ctypes.byref(params)))
+    return int(lib().fp8q_quant_b_min_m(K, ctypes.byref(params)))
 
 
 def fp8q_quant_log_slot(variant: int, reject, requested: bool) -> int:
     r = None if reject is None else reject.encode()
-    return int(_lib.fp8q_quant_log_slot(variant, r, int(bool(requested))))
+    return int(lib().fp8q_quant_log_slot(variant, r, int(bool(requested))))
 
 
 # ------------------------------------------------------- allocation helpers

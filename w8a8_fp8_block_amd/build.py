@@ -8,6 +8,9 @@ hipcc cross-compiles for gfx950 without a GPU present.  Flags:
                                       keep the compiler from emitting packed
                                       fp32 VALU ops (the host pass warns that
                                       it does not know the feature: harmless)
+  -mllvm -amdgpu-mfma-vgpr-form       MFMA results in VGPRs: every GEMM partial
+                                      product is consumed by VALU fmas, which
+                                      cannot read AGPRs
   -fgpu-flush-denormals-to-zero is NOT given: the quantizer relies on IEEE
   subnormal fp32 arithmetic (the default).
 """
@@ -27,6 +30,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall", "-Wno-unused-function", "-Wno-unknown-pragmas",
     "-I", os.path.join(ROOT, "include"),
 ]

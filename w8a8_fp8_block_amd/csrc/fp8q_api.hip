@@ -167,7 +167,8 @@ fp8q_status run_gemm(const char* fn, const uint8_t* a, const float* as, const ui
   if (kernel == 2 && M > kSkinnyMaxM)
     return fail(FP8Q_ERR_VARIANT, "%s: skinny kernel needs M <= %u (M=%u)", fn, kSkinnyMaxM, M);
   const hipError_t e = (kernel == 2) ? launch_gemm_skinny(a, as, w, ws, out, M, N, K, s)
-                                     : launch_gemm_tiled(a, as, w, ws, out, M, N, K, s);
+                                     : launch_gemm_tiled(a, as, w, ws, out, M, N, K,
+                                                         kernel == 1 ? 1 : kernel - 1, s);
   return launched(fn, e);
 }
 
@@ -306,7 +307,7 @@ fp8q_status fp8q_gemm_blockscaled_ex(const uint8_t* a_e4m3, const float* a_scale
                                      uint16_t* out_bf16, uint32_t M, uint32_t N, uint32_t K,
                                      int kernel, hipStream_t stream) {
   const char* fn = "fp8q_gemm_blockscaled";
-  if (kernel < 0 || kernel > 2) return fail(FP8Q_ERR_VARIANT, "%s: kernel %d out of range", fn, kernel);
+  if (kernel < 0 || kernel > 4) return fail(FP8Q_ERR_VARIANT, "%s: kernel %d out of range", fn, kernel);
   fp8q_status st = check_mk(fn, M, K);
   if (st != FP8Q_OK) return st;
   st = check_n(fn, M, N, K);

@@ -47,125 +47,313 @@ __device__ __forceinline__ v8i join(u32x4 a, u32x4 b) {
 
 // ------------------------------------------------------------------------
 // LDS-tiled kernel.  Workgroup tile BM x BN, K step 128 (one scale block),
-// WAVES_M x WAVES_N waves, each owning a (BM/WAVES_M) x (BN/WAVES_N) sub-tile.
-// LDS holds two stages of [BM + BN rows][128 B]; 16-byte chunk c of row r is
-// stored at chunk position c ^ (r & 7) so that the 16 lanes reading the same
-// chunk column of 16 consecutive rows spread over the banks.
+// WGM x WGN waves, each owning a (BM/WGM) x (BN/WGN) sub-tile.
+//
+// Operands reach LDS through direct buffer->LDS loads (64 lanes x 16 B land in
+// 1 KB of consecutive LDS), so the ring of STAGES LDS buffers is filled
+// without staging registers.  A stage holds [BM rows][128 B] of activations,
+// [BN rows][128 B] of weights, the BM fp32 activation scales of that K block
+// (read from the K-major scale layout, where they are contiguous) and each
+// wave's weight scale.  16-byte chunk c of row r
+// sits at chunk position c ^ f(r), f(r) = (r & 7) ^ ((r >> 3) & 1), so the 16
+// lanes that read one chunk column of 16 consecutive rows hit 16 different
+// (row parity, chunk) bank groups; f depends on r mod 16 only, so every
+// fragment address is a per-lane constant plus a compile-time offset.  The
+// direct load realises the swizzle by choosing, per lane, which global chunk
+// lands in its fixed LDS slot.
+//
+// Fragments are double-buffered in registers: the LDS reads of K block kb+1
+// run under the MFMAs of block kb (the LDS, at ~128 B/clk per CU, needs about
+// as many cycles per block as the matrix cores do, so the two must overlap).
 // ------------------------------------------------------------------------
-template <int BM, int BN, int WAVES_M, int WAVES_N>
-__global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_tiled_kernel(
+// Direct global->LDS loads through a buffer resource: every lane of the wave
+// copies `bytes` (4 or 16) from base + voff (per lane, VGPR) + soff (uniform,
+// SGPR); lane i's data lands at lds + i * bytes, and lds must be the same for
+// the whole wave (it goes to M0).  With the per-K-block advance in soff the
+// loop spends no vector instructions on addresses.  Offsets at or beyond the
+// resource's byte count read as zero.  (Kept out of lambdas: HIP lambdas are
+// host+device, and a device-only builtin inside one called from a kernel
+// template makes the host pass drop that kernel's stub.)
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  // raw buffer (stride 0): bound = bytes; word 3 = 0x00020000 for gfx9-family
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+}
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, void* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff,
+                                           soff, 0, 0);
+}
+__device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, void* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 4, voff,
+                                           soff, 0, 0);
+}
+
+__device__ __forceinline__ uint32_t swz(uint32_t r) { return (r & 7u) ^ ((r >> 3) & 1u); }
+
+// s_waitcnt vmcnt(n) leaving expcnt/lgkmcnt unconstrained (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// wait until at most ahead*L of this wave's vector loads are outstanding
+template <int L, int A>
+__device__ __forceinline__ void wait_ahead(uint32_t ahead) {
+  if constexpr (A <= 0) {
+    wait_vmcnt<0>();
+  } else {
+    if (ahead >= (uint32_t)A) wait_vmcnt<A * L>();
+    else wait_ahead<L, A - 1>(ahead);
+  }
+}
+
+// Scheduling pattern for one K block: MFMA i is followed by the four fmas
+// that promote MFMA i-LAG, one LDS read of the next block's fragments and,
+// for the first NV MFMAs, one direct global->LDS load, so the VALU work, the
+// LDS traffic and the texture-unit queue all run under the matrix pipe.
+template <int I, int NP, int LAG, int NV>
+__device__ __forceinline__ void sched_interleave_from() {
+  if constexpr (I < NP) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                          // MFMA
+    if constexpr (I >= LAG) __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // VALU
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                          // DS read
+    if constexpr (I < NV) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);    // VMEM read
+    sched_interleave_from<I + 1, NP, LAG, NV>();
+  } else {
+    __builtin_amdgcn_sched_group_barrier(0x002, 4 * LAG, 0);
+  }
+}
+
+template <int BM, int BN, int WGM, int WGN, int STAGES>
+struct TileCfg {
+  static constexpr int NW = WGM * WGN, NT = 64 * NW;
+  static constexpr int WM = BM / WGM, WN = BN / WGN, TM = WM / 16, TN = WN / 16;
+  static constexpr int A_BYTES = BM * 128, W_BYTES = BN * 128;
+  static constexpr int S_BYTES = 1024;  // activation scales of the block (BM <= 256 used)
+  static constexpr int STAGE_BYTES = A_BYTES + W_BYTES + S_BYTES;
+  static constexpr int WS_FLOATS = 1024;  // weight scales staged per 1024 K blocks
+  static constexpr int LDS_BYTES = STAGES * STAGE_BYTES + WS_FLOATS * 4;
+  static constexpr int DA = BM * 8 / 64 / NW;  // 1 KB direct loads per wave: activations
+  static constexpr int DW = BN * 8 / 64 / NW;  //                              weights
+  static constexpr int LOADS = DA + DW;        // per stage, waves 1..NW-1
+  static constexpr int LOADS0 = DA + DW + 1;   // per stage, wave 0 (+ activation scales)
+  static_assert(BM * 8 % (64 * NW) == 0 && BN * 8 % (64 * NW) == 0, "tile/wave mismatch");
+  static_assert(BM <= 256 && BM % 16 == 0, "activation scales: one 1 KB load per block");
+  static_assert(BN <= 128 && 128 % BN == 0 && WN <= BN, "one weight-scale block per tile");
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+  static_assert(STAGES >= 2 && (STAGES - 2) * LOADS0 < 64, "vmcnt range");
+};
+
+// wait until at most `ahead` stages' worth of this wave's loads are
+// outstanding (wave 0 issues one load more per stage than the others)
+template <int L0, int L, int A>
+__device__ __forceinline__ void wait_stages(uint32_t ahead, bool wave0) {
+  if (wave0) wait_ahead<L0, A>(ahead);
+  else wait_ahead<L, A>(ahead);
+}
+
+template <int BM, int BN, int WGM, int WGN, int STAGES>
+__global__ __launch_bounds__(64 * WGM * WGN) void gemm_tiled_kernel(
     const uint8_t* __restrict__ A, const float* __restrict__ As, const uint8_t* __restrict__ W,
     const float* __restrict__ Ws, uint16_t* __restrict__ out, uint32_t M, uint32_t N, uint32_t K,
     uint32_t Mp, uint32_t tiles_m, uint32_t tiles_n) {
-  constexpr int NT = 64 * WAVES_M * WAVES_N;
-  constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
-  constexpr int TM = WM / 16, TN = WN / 16;
-  constexpr int CA = BM * 8 / NT, CW = BN * 8 / NT;
-  static_assert(BM * 8 % NT == 0 && BN * 8 % NT == 0, "tile/thread mismatch");
-  static_assert(WN <= 128 && 128 % WN == 0, "a wave's columns must sit in one 128-block");
-  __shared__ u32x4 lds[2][(BM + BN) * 8];
+  using C = TileCfg<BM, BN, WGM, WGN, STAGES>;
+  extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
 
-  const uint32_t tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const uint32_t wm = wave / WAVES_N, wn = wave % WAVES_N;
+  const uint32_t tid = threadIdx.x, lane = tid & 63;
+  const uint32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (SGPR)
+  const bool wave0 = wave == 0;
+  const uint32_t wm = wave / WGN, wn = wave % WGN;
 
-  // Tile order: consecutive workgroup ids walk down M inside a column strip
-  // of tiles so that concurrently running workgroups share weight tiles.
-  const uint32_t tile = blockIdx.x;
-  const uint32_t tmi = tile % tiles_m, tni = tile / tiles_m;
+  // ---- tile of this workgroup: XCD-aware, grouped order ----
+  // Workgroup ids are dealt round-robin to the 8 XCDs; give each XCD a
+  // contiguous run of tiles so that the tiles it runs together share L2.
+  const uint32_t ntiles = tiles_m * tiles_n;
+  const uint32_t bid = blockIdx.x, xcd = bid & 7, slot = bid >> 3;
+  const uint32_t q = ntiles >> 3, r8 = ntiles & 7;
+  const uint32_t t = (xcd < r8) ? xcd * (q + 1) + slot : r8 * (q + 1) + (xcd - r8) * q + slot;
+  // grouped order: blocks of GROUP_M tile rows, walking N inside a block
+  constexpr uint32_t GROUP_M = 8;
+  const uint32_t per_group = GROUP_M * tiles_n;
+  const uint32_t group = t / per_group, first_m = group * GROUP_M;
+  const uint32_t gm = min(tiles_m - first_m, GROUP_M);
+  const uint32_t tmi = first_m + (t % per_group) % gm, tni = (t % per_group) / gm;
   const uint32_t m0 = tmi * BM, n0 = tni * BN;
   const uint32_t G = K / kGroup;
-  const uint32_t nb = (n0 + wn * WN) / kGroup;
+  const uint32_t nb = n0 / kGroup;
 
-  u32x4 ra[CA], rw[CW];
-  auto gload = [&](uint32_t kb) {
+  // ---- buffer resources and per-lane source offsets (K block 0) ----
+  const __amdgpu_buffer_rsrc_t rA = make_rsrc(A, M * K);
+  const __amdgpu_buffer_rsrc_t rW = make_rsrc(W, N * K);
+  const __amdgpu_buffer_rsrc_t rS = make_rsrc(As, G * Mp * 4);
+  const __amdgpu_buffer_rsrc_t rWs = make_rsrc(Ws, (N / kGroup) * G * 4);
+  uint32_t a_off[C::DA], w_off[C::DW];
 #pragma unroll
-    for (int i = 0; i < CA; ++i) {
-      const uint32_t q = tid + i * NT, row = q >> 3, c = q & 7;
-      const uint32_t grow = min(m0 + row, M - 1);
-      ra[i] = *reinterpret_cast<const u32x4*>(A + (uint64_t)grow * K + kb * kGroup + c * 16);
-    }
+  for (int j = 0; j < C::DA; ++j) {
+    const uint32_t c = (wave * C::DA + j) * 64 + lane, row = c >> 3;
+    a_off[j] = min(m0 + row, M - 1) * K + ((c & 7) ^ swz(row)) * 16;
+  }
 #pragma unroll
-    for (int i = 0; i < CW; ++i) {
-      const uint32_t q = tid + i * NT, row = q >> 3, c = q & 7;
-      rw[i] = *reinterpret_cast<const u32x4*>(W + (uint64_t)(n0 + row) * K + kb * kGroup + c * 16);
-    }
+  for (int j = 0; j < C::DW; ++j) {
+    const uint32_t c = (wave * C::DW + j) * 64 + lane, row = c >> 3;
+    w_off[j] = (n0 + row) * K + ((c & 7) ^ swz(row)) * 16;
+  }
+  // activation scales: wave 0 loads rows m0 + 4*lane .. +3 of the block (16
+  // bytes per lane; rows past Mp are clamped in bounds and never used)
+  const uint32_t s_off = min(m0 + 4 * lane, Mp - 4) * 4;
+  float* ws_lds = reinterpret_cast<float*>(smem + STAGES * C::STAGE_BYTES);
+
+  auto issue_stage = [&](uint32_t kb, uint32_t stage) {
+    uint8_t* base = smem + stage * C::STAGE_BYTES;
+#pragma unroll
+    for (int j = 0; j < C::DA; ++j) dma16(rA, a_off[j], kb * kGroup, base + (wave * C::DA + j) * 1024);
+#pragma unroll
+    for (int j = 0; j < C::DW; ++j)
+      dma16(rW, w_off[j], kb * kGroup, base + C::A_BYTES + (wave * C::DW + j) * 1024);
+    if (wave0) dma16(rS, s_off, kb * Mp * 4, base + C::A_BYTES + C::W_BYTES);
   };
-  auto lstore = [&](int buf) {
+  // weight scales w_s[nb][kb0 .. kb0+1023] (wave 0; reads past the end of the
+  // row are never used, reads past the end of w_s return zero)
+  auto issue_ws = [&](uint32_t kb0) {
 #pragma unroll
-    for (int i = 0; i < CA; ++i) {
-      const uint32_t q = tid + i * NT, row = q >> 3, c = q & 7;
-      lds[buf][row * 8 + (c ^ (row & 7))] = ra[i];
-    }
-#pragma unroll
-    for (int i = 0; i < CW; ++i) {
-      const uint32_t q = tid + i * NT, row = q >> 3, c = q & 7;
-      lds[buf][(BM + row) * 8 + (c ^ (row & 7))] = rw[i];
-    }
-  };
-  auto frag = [&](int buf, uint32_t row) -> v8i {
-    const uint32_t c0 = 2 * (lane >> 4), sw = row & 7;
-    return join(lds[buf][row * 8 + (c0 ^ sw)], lds[buf][row * 8 + ((c0 + 1) ^ sw)]);
+    for (int j = 0; j < C::WS_FLOATS / 256; ++j)
+      dma16(rWs, (nb * G + kb0 + j * 256 + lane * 4) * 4, 0, ws_lds + j * 256);
   };
 
-  // activation-scale rows of this lane (clamped into the Mp-wide buffer;
-  // rows >= M are computed but never stored)
-  uint32_t srow[TM];
+  // Per-lane byte offsets of a fragment inside a 16-row slab: this lane's row
+  // (lane % 16) and its two chunks 2*(lane/16) and 2*(lane/16)+1, swizzled.
+  const uint32_t l16 = lane & 15, c0 = 2 * (lane >> 4);
+  const uint32_t lo0 = l16 * 128 + ((c0 ^ swz(l16)) * 16);
+  const uint32_t lo1 = l16 * 128 + (((c0 + 1) ^ swz(l16)) * 16);
+  auto frag = [&](const uint8_t* slab) -> v8i {
+    return join(*reinterpret_cast<const u32x4*>(slab + lo0),
+                *reinterpret_cast<const u32x4*>(slab + lo1));
+  };
+  auto slot_base = [&](uint32_t kb) -> const uint8_t* {
+    return smem + (kb % STAGES) * C::STAGE_BYTES;
+  };
+  auto read_a = [&](uint32_t kb, int tm) -> v8i {
+    return frag(slot_base(kb) + (wm * C::WM + tm * 16) * 128);
+  };
+  auto read_b = [&](uint32_t kb, int tn) -> v8i {
+    return frag(slot_base(kb) + C::A_BYTES + (wn * C::WN + tn * 16) * 128);
+  };
+  auto read_sc = [&](float (&sc)[C::TM], uint32_t kb) {
+    const float* s_lds = reinterpret_cast<const float*>(slot_base(kb) + C::A_BYTES + C::W_BYTES);
+    const float ws = ws_lds[kb % C::WS_FLOATS];
 #pragma unroll
-  for (int tm = 0; tm < TM; ++tm) srow[tm] = min(m0 + wm * WM + tm * 16 + (lane & 15), Mp - 1);
+    for (int tm = 0; tm < C::TM; ++tm) sc[tm] = s_lds[wm * C::WM + tm * 16 + l16] * ws;
+  };
 
-  v4f acc[TM][TN];
+  v4f acc[C::TM][C::TN];
 #pragma unroll
-  for (int tm = 0; tm < TM; ++tm)
+  for (int i = 0; i < C::TM; ++i)
 #pragma unroll
-    for (int tn = 0; tn < TN; ++tn) acc[tm][tn] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int j = 0; j < C::TN; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
-  float as_next[TM];
+  // Pipeline.  Stage s is loaded into LDS slot s % STAGES by direct loads
+  // issued during iteration s - STAGES (the prologue issues the first
+  // STAGES), and its fragments are read into registers during iteration
+  // s - 1, under the MFMAs of block s - 1: activation fragments in place,
+  // row by row, as the rows of block s-1 are issued; weight fragments and
+  // the combined scales a_s * w_s into the second of two register sets.  At
+  // the top of iteration kb each wave waits for its own LDS reads and for
+  // its loads of stage kb+1, and one barrier makes that hold for all waves;
+  // slot kb % STAGES (read during iteration kb-1) is then free to refill.
+  if (wave0) issue_ws(0);
 #pragma unroll
-  for (int tm = 0; tm < TM; ++tm) as_next[tm] = As[srow[tm]];
-  float ws_next = Ws[(uint64_t)nb * G];
+  for (int s = 0; s < STAGES; ++s)
+    if ((uint32_t)s < G) issue_stage(s, s);
+  wait_stages<C::LOADS0, C::LOADS, STAGES - 1>(min(G - 1, (uint32_t)(STAGES - 1)), wave0);
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 
-  gload(0);
-  lstore(0);
-  __syncthreads();
+  constexpr int NP = C::TM * C::TN, LAG = 2;
+  v8i af[C::TM], bf0[C::TN], bf1[C::TN];
+  float sc0[C::TM], sc1[C::TM];
+#pragma unroll
+  for (int tm = 0; tm < C::TM; ++tm) af[tm] = read_a(0, tm);
+#pragma unroll
+  for (int tn = 0; tn < C::TN; ++tn) bf0[tn] = read_b(0, tn);
+  read_sc(sc0, 0);
 
-  for (uint32_t kb = 0; kb < G; ++kb) {
-    const int cur = kb & 1;
-    float sc[TM];
-#pragma unroll
-    for (int tm = 0; tm < TM; ++tm) sc[tm] = as_next[tm] * ws_next;
-    if (kb + 1 < G) {
-      gload(kb + 1);
-#pragma unroll
-      for (int tm = 0; tm < TM; ++tm) as_next[tm] = As[(uint64_t)(kb + 1) * Mp + srow[tm]];
-      ws_next = Ws[(uint64_t)nb * G + kb + 1];
+  auto step = [&](uint32_t kb, const v8i (&bf)[C::TN], const float (&sc)[C::TM],
+                  v8i (&bf_n)[C::TN], float (&sc_n)[C::TM]) {
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt/expcnt unconstrained
+    if (kb + 1 < G)
+      wait_stages<C::LOADS0, C::LOADS, STAGES - 2>(min(G - 2 - kb, (uint32_t)(STAGES - 2)), wave0);
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if ((kb + 1) % C::WS_FLOATS == 0 && kb + 1 < G) {
+      // next chunk of weight scales (every 1024 K blocks): everyone has read
+      // the last scale of the old chunk (block kb's, during iteration kb-1)
+      if (wave0) {
+        issue_ws(kb + 1);
+        wait_vmcnt<0>();
+      }
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
     }
-    v8i bf[TN];
+    if (kb + STAGES < G) issue_stage(kb + STAGES, kb % STAGES);
+    // (reads of block kb+1 are issued unconditionally: on the last block they
+    // read a stale but in-bounds slot whose values are never used, which keeps
+    // the body one straight-line scheduling region)
 #pragma unroll
-    for (int tn = 0; tn < TN; ++tn) bf[tn] = frag(cur, BM + wn * WN + tn * 16 + (lane & 15));
+    for (int tn = 0; tn < C::TN; ++tn) bf_n[tn] = read_b(kb + 1, tn);
+    read_sc(sc_n, kb + 1);
+    v4f p[LAG + 1];
 #pragma unroll
-    for (int tm = 0; tm < TM; ++tm) {
-      const v8i af = frag(cur, wm * WM + tm * 16 + (lane & 15));
-#pragma unroll
-      for (int tn = 0; tn < TN; ++tn) {
-        const v4f p = mfma_e4m3_128(bf[tn], af);
-        acc[tm][tn] += p * sc[tm];
+    for (int i = 0; i < NP + LAG; ++i) {
+      if (i < NP) {
+        const int tm = i / C::TN, tn = i % C::TN;
+        p[i % (LAG + 1)] = mfma_e4m3_128(bf[tn], af[tm]);
+        if (tn == C::TN - 1) af[tm] = read_a(kb + 1, tm);
+      }
+      if (i >= LAG) {
+        const int j = i - LAG, tm = j / C::TN, tn = j % C::TN;
+        acc[tm][tn] += p[j % (LAG + 1)] * sc[tm];
       }
     }
-    if (kb + 1 < G) lstore(cur ^ 1);
-    __syncthreads();
+    sched_interleave_from<0, NP, LAG, C::LOADS0>();
+  };
+  uint32_t kb = 0;
+  for (; kb + 2 <= G; kb += 2) {
+    step(kb, bf0, sc0, bf1, sc1);
+    step(kb + 1, bf1, sc1, bf0, sc0);
   }
+  if (kb < G) step(kb, bf0, sc0, bf1, sc1);
 
 #pragma unroll
-  for (int tm = 0; tm < TM; ++tm) {
-    const uint32_t m = m0 + wm * WM + tm * 16 + (lane & 15);
+  for (int tm = 0; tm < C::TM; ++tm) {
+    const uint32_t m = m0 + wm * C::WM + tm * 16 + (lane & 15);
     if (m < M) {
 #pragma unroll
-      for (int tn = 0; tn < TN; ++tn) {
-        const uint32_t n = n0 + wn * WN + tn * 16 + 4 * (lane >> 4);
+      for (int tn = 0; tn < C::TN; ++tn) {
+        const uint32_t n = n0 + wn * C::WN + tn * 16 + 4 * (lane >> 4);
         *reinterpret_cast<uint2*>(out + (uint64_t)m * N + n) = pack_bf16x4(acc[tm][tn]);
       }
     }
   }
+}
+
+template <int BM, int BN, int WGM, int WGN, int STAGES>
+hipError_t launch_tiled_cfg(const uint8_t* a, const float* a_s_km, const uint8_t* w,
+                            const float* w_s, uint16_t* out, uint32_t M, uint32_t N, uint32_t K,
+                            hipStream_t s) {
+  using C = TileCfg<BM, BN, WGM, WGN, STAGES>;
+  if (N % BN != 0) return hipErrorInvalidValue;
+  static bool attr_set = false;  // idempotent; racing threads set the same value
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(&gemm_tiled_kernel<BM, BN, WGM, WGN, STAGES>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  const uint32_t tiles_m = (M + BM - 1) / BM, tiles_n = N / BN;
+  gemm_tiled_kernel<BM, BN, WGM, WGN, STAGES><<<dim3(tiles_m * tiles_n), dim3(C::NT), C::LDS_BYTES, s>>>(
+      a, a_s_km, w, w_s, out, M, N, K, m_pad16(M), tiles_m, tiles_n);
+  return hipGetLastError();
 }
 
 // ------------------------------------------------------------------------
@@ -257,12 +445,14 @@ __global__ __launch_bounds__(64 * kSkinnyWaves) void gemm_skinny_kernel(
 
 hipError_t launch_gemm_tiled(const uint8_t* a, const float* a_s_km, const uint8_t* w,
                              const float* w_s, uint16_t* out, uint32_t M, uint32_t N, uint32_t K,
-                             hipStream_t s) {
-  constexpr int BM = 128, BN = 128;
-  const uint32_t tiles_m = (M + BM - 1) / BM, tiles_n = N / BN;
-  gemm_tiled_kernel<BM, BN, 2, 2><<<dim3(tiles_m * tiles_n), dim3(256), 0, s>>>(
-      a, a_s_km, w, w_s, out, M, N, K, m_pad16(M), tiles_m, tiles_n);
-  return hipGetLastError();
+                             int cfg, hipStream_t s) {
+  switch (cfg) {
+    case 0:
+    case 1: return launch_tiled_cfg<128, 128, 2, 2, 2>(a, a_s_km, w, w_s, out, M, N, K, s);
+    case 2: return launch_tiled_cfg<256, 128, 4, 2, 3>(a, a_s_km, w, w_s, out, M, N, K, s);
+    case 3: return launch_tiled_cfg<256, 128, 2, 2, 3>(a, a_s_km, w, w_s, out, M, N, K, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 hipError_t launch_gemm_skinny(const uint8_t* a, const float* a_s_km, const uint8_t* w,
