@@ -40,7 +40,7 @@ FP8_PEAK_TFLOPS = 5000.0   # MI355X dense FP8 MFMA, TFLOP/s
 # readings for a plain 1 GiB copy (the HBM-bytes summary under profiles/).
 # Valid only for the GEMM source they were taken with: reported as null once
 # gemm.hip changes (its SHA-256 prefix is recorded here).
-GEMM_TRAFFIC = {"bytes": 1.399e9 + 46.86e6, "gemm_source_sha256": "935815a2f5bb8cf1"}
+GEMM_TRAFFIC = {"bytes": 1.1747e9 + 46.86e6, "gemm_source_sha256": "f4c28145b510a761"}
 
 
 def gemm_traffic():
@@ -61,6 +61,9 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="approximate CPU time budget of the oracle sample")
+    p.add_argument("--quant-sweep", action="store_true",
+                   help="instead of the benchmark, time quantizer variants A, B and the "
+                        "selector's choice over the token/K sweep (one JSON line per shape)")
     p.add_argument("--copy-mib", type=int, default=0,
                    help="instead of the benchmark, run 3 plain device copies of this many "
                         "MiB (the reference kernel for scaling rocprofv3 byte counters)")
@@ -76,6 +79,54 @@ def copy_calibration(mib: int):
         dst.copy_(src)
     torch.cuda.synchronize()
     print(json.dumps({"copy_calibration_bytes": n, "launches": 3}), flush=True)
+
+
+def quant_sweep(reps=25):
+    """Quantizer variants A and B and the automatic choice on every (M, K) of
+    the token/K sweep plus M in {17, 64, 128, 256, 512}: median kernel time
+    over `reps` launches, each after a 1 GiB write that evicts L2 and the
+    256 MB last-level cache, plus the selection rule check
+    t(auto) <= 1.03 * min(t_A, t_B) + 0.1 us."""
+    import torch
+    import synth
+    import w8a8_fp8_block_amd as fp8q
+    dev = torch.device("cuda:0")
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    sweep = synth.WORKLOADS["quant_sweep"]
+    Ks = sorted({w.K for w in sweep})
+    Ms = sorted({w.M for w in sweep} | {17, 64, 128, 256, 512})
+    for K in Ks:
+        G = K // 128
+        base = next(w for w in sweep if w.K == K)
+        for M in Ms:
+            x = torch.from_numpy(synth.make_inputs(base, M=M, with_weights=False)[0]
+                                 .view(np.int16)).to(dev)
+            q = torch.empty((M, K), dtype=torch.uint8, device=dev)
+            sc = torch.empty((M, G), dtype=torch.float32, device=dev)
+            times = {}
+            for name, var in (("A", 1), ("B", 2), ("auto", 0)):
+                ts = []
+                for _ in range(reps):
+                    flush.fill_(1)
+                    e0 = torch.cuda.Event(enable_timing=True)
+                    e1 = torch.cuda.Event(enable_timing=True)
+                    e0.record()
+                    fp8q.fp8q_quant_act(x, q, sc, variant=var)
+                    e1.record()
+                    torch.cuda.synchronize()
+                    ts.append(e0.elapsed_time(e1) * 1e3)
+                times[name] = float(np.median(ts))
+            v, grid, why = fp8q.fp8q_quant_select(M, K, cus)
+            nbytes = 3 * M * K + 4 * M * G
+            best = min(times["A"], times["B"])
+            print(json.dumps({
+                "M": M, "K": K, "t_A_us": round(times["A"], 2), "t_B_us": round(times["B"], 2),
+                "t_auto_us": round(times["auto"], 2), "auto": "B" if v == 2 else "A",
+                "grid_B": (M * ((G + 31) // 32)), "reject": why,
+                "best_GBs": round(nbytes / best / 1e3, 1),
+                "best_frac_hbm": round(nbytes / best / 1e3 / HBM_PEAK_GBS, 4),
+                "rule_ok": times["auto"] <= 1.03 * best + 0.1}), flush=True)
 
 
 def quantize_weights_gpu(wf):
@@ -131,6 +182,9 @@ def main():
 
     if args.copy_mib:
         copy_calibration(args.copy_mib)
+        return
+    if args.quant_sweep:
+        quant_sweep()
         return
 
     import torch
@@ -198,6 +252,24 @@ def main():
     quant_avg_s = float(np.mean(quant_ms)) * 1e-3
     quant_gbs = quant_bytes / quant_avg_s / 1e9
 
+    kern = fp8q.fp8q_gemm_select(M, N, K)
+    if kern == 2:
+        # decode widths: the GEMM streams the weight matrix once (HBM-bound)
+        gemm_bytes = N * K + M * K + 2 * M * N + 4 * (N // 128) * G + 4 * fp8q.fp8q_m_pad(M) * G
+        gemm_gbs = gemm_bytes / gemm_avg_s / 1e9
+        roofline = {"bound": "hbm", "kernel": fp8q.GEMM_KERNEL_NAMES[kern],
+                    "achieved": round(gemm_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(gemm_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                    "avg_launch_us": round(gemm_avg_s * 1e6, 2),
+                    "algorithmic_bytes_per_launch": gemm_bytes}
+    else:
+        roofline = {"bound": "mfma", "kernel": fp8q.GEMM_KERNEL_NAMES[kern],
+                    "achieved": round(gemm_tflops, 2), "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(gemm_tflops / FP8_PEAK_TFLOPS, 4),
+                    "traffic": gemm_traffic() if args.workload == "large_prefill" else None,
+                    "avg_launch_us": round(gemm_avg_s * 1e6, 2),
+                    "algorithmic_flops_per_launch": flops}
+
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
@@ -227,17 +299,7 @@ def main():
             "device": props.name, "gcn_arch": props.gcnArchName,
             "cus": props.multi_processor_count,
         },
-        "roofline": {
-            "bound": "mfma",
-            "kernel": "gemm_skinny_kernel" if M <= 32 else "gemm_tiled_kernel",
-            "achieved": round(gemm_tflops, 2),
-            "peak": FP8_PEAK_TFLOPS,
-            "unit": "TFLOP/s",
-            "frac": round(gemm_tflops / FP8_PEAK_TFLOPS, 4),
-            "traffic": gemm_traffic() if args.workload == "large_prefill" else None,
-            "avg_launch_us": round(gemm_avg_s * 1e6, 2),
-            "algorithmic_flops_per_launch": flops,
-        },
+        "roofline": roofline,
         "act_quant": {
             "achieved": round(quant_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(quant_gbs / HBM_PEAK_GBS, 4),

@@ -126,8 +126,11 @@ typedef struct fp8q_select_params {
 } fp8q_select_params;
 
 /* The parameters fp8q_quant_select uses on this library's gfx950 kernels
- * for a device with cu_count compute units (requested from the
- * FP8Q_QUANT_VARIANT environment variable: "a" -> 0, else 1). */
+ * for a device with cu_count compute units.  `requested` comes from the
+ * FP8Q_QUANT_VARIANT environment variable: "floor" or "b" -> 1, "a" -> 0,
+ * unset/other -> the gfx950 target default, 0 (variant B measured no faster
+ * than A at any swept shape on gfx950).  With "b" the automatic entry points
+ * run B unconditionally (measurement). */
 fp8q_select_params fp8q_default_select_params(uint32_t cu_count);
 
 /* Pure selection rule.  Returns 2 when variant B runs and 1 when A runs,
@@ -175,7 +178,8 @@ fp8q_status fp8q_scale_to_kmajor(const float *scale_rm, float *scale_km,
  *
  *   a_e4m3      [M,K] e4m3fn codes (activations), read only
  *   a_scale_km  [K/128, Mp] fp32, Mp = fp8q_m_pad(M) (K-major, as written by
- *               fp8q_scale_to_kmajor); slots m >= M are never read
+ *               fp8q_scale_to_kmajor); pad slots m >= M may be read but never
+ *               reach the output
  *   w_e4m3      [N,K] e4m3fn codes (weights), read only
  *   w_scale     [N/128, K/128] fp32, one scale per 128x128 weight block
  *   out_bf16    [M,N] bf16 out; exactly the M*N real rows are written
@@ -189,12 +193,19 @@ fp8q_status fp8q_gemm_blockscaled(const uint8_t *a_e4m3, const float *a_scale_km
                                   uint16_t *out_bf16, uint32_t M, uint32_t N,
                                   uint32_t K, hipStream_t stream);
 
-/* As fp8q_gemm_blockscaled with the kernel forced: 0 = auto, 1 = the
- * LDS-tiled MFMA kernel (prefill widths; 128x128 tiles, two workgroups per
- * CU), 2 = the skinny kernel (decode widths, needs M <= 64), 3..4 = other
- * shapes of the LDS-tiled kernel, kept for measurement (3 = 256x128 tiles
- * with 8 waves, 4 = 256x128 tiles with 4 waves).  Other values ->
- * FP8Q_ERR_VARIANT. */
+/* The kernel fp8q_gemm_blockscaled runs for this shape (the ids of
+ * fp8q_gemm_blockscaled_ex below), or -1 if N or K is not a positive
+ * multiple of 128.  Pure host function: no device access, thread-safe. */
+int fp8q_gemm_select(uint32_t M, uint32_t N, uint32_t K);
+
+/* As fp8q_gemm_blockscaled with the kernel forced: 0 = auto (2 for
+ * M <= 32, 3 for M >= 2048, else 1), 1 = the LDS-tiled MFMA kernel with
+ * 128x128 tiles and two workgroups per CU, 2 = the skinny kernel (decode
+ * widths, needs M <= 64), 3 = the LDS-tiled kernel with 256x128 tiles and
+ * 8 waves, 4 = 256x128 tiles with 4 waves (kept for measurement).  Kernels
+ * 1, 3 and 4 add the blocks' scaled partial products in the same order and
+ * give bit-identical outputs; the skinny kernel sums four K ranges
+ * separately.  Other values -> FP8Q_ERR_VARIANT. */
 fp8q_status fp8q_gemm_blockscaled_ex(const uint8_t *a_e4m3, const float *a_scale_km,
                                      const uint8_t *w_e4m3, const float *w_scale,
                                      uint16_t *out_bf16, uint32_t M, uint32_t N,

@@ -107,3 +107,13 @@ def test_gemm_validation():
     assert "act_scale_km_scratch" in _err()
     assert L.fp8q_proj(g, g, g, g, g, g, g, 4, 128, 100, None) == 2
     assert L.fp8q_proj(g, g, g, g, g, g, g, 0, 128, 128, None) == 0
+
+
+def test_gemm_select():
+    """Auto GEMM choice: skinny kernel up to 32 rows, 256x128 tiles from 2048
+    rows on, 128x128 tiles between; bad N/K -> -1 (pure host function)."""
+    for M, want in ((1, 2), (16, 2), (25, 2), (32, 2), (33, 1), (1168, 1), (2047, 1), (2048, 3),
+                    (4576, 3), (16384, 3)):
+        assert fp8q.fp8q_gemm_select(M, 5120, 17408) == want, M
+    assert fp8q.fp8q_gemm_select(64, 100, 128) == -1
+    assert fp8q.fp8q_gemm_select(64, 128, 0) == -1

@@ -249,8 +249,9 @@ def test_gemm_repeatable(orc):
 
 
 def test_gemm_long_k_weight_scale_chunks(orc):
-    """K spanning more than 1024 scale blocks (the tiled kernel stages the
-    weight scales 1024 blocks at a time)."""
+    """K spanning more than 1024 scale blocks, the weight scales of the later
+    blocks clearly different from the earlier ones (a scale taken from the
+    wrong K block shows)."""
     M, N, K = 40, 256, 1030 * 128
     rng = np.random.default_rng(21)
     x = synth.f32_to_bf16_bits(rng.standard_normal((M, K)).astype(np.float32))
@@ -263,3 +264,20 @@ def test_gemm_long_k_weight_scale_chunks(orc):
     for kern in _kernels_for(M, N):
         log(f"gemm long-K kernel={kern}")
         _assert_tol(_gemm_gpu(orc, a, a_s, wq, ws, kern), ref, f"long-K k{kern}")
+
+
+@pytest.mark.parametrize("M,N,K", [(300, 384, 1280), (1168, 512, 2048), (4576, 256, 640)])
+def test_tiled_kernels_bit_identical(orc, M, N, K):
+    """The tiled kernels (all tile shapes) add the scaled block products in the
+    same order, so their outputs agree bit for bit; the auto choice is one of
+    them."""
+    rng = np.random.default_rng(M + N + K)
+    x = synth.f32_to_bf16_bits(rng.laplace(0, 1, (M, K)).astype(np.float32))
+    a, a_s = orc.quant_act(x)
+    wq, ws = orc.quant_weight_block(rng.normal(0, 0.02, (N, K)).astype(np.float32))
+    outs = {}
+    for kern in (1, 3, 4, 0):
+        log(f"gemm M={M} N={N} K={K} kernel={kern}")
+        outs[kern] = _gemm_gpu(orc, a, a_s, wq, ws, kern)
+    for kern in (3, 4, 0):
+        assert np.array_equal(outs[kern], outs[1]), f"kernel {kern} differs from kernel 1"

@@ -60,6 +60,7 @@ _SIGS = {
     "fp8q_quant_b_min_m": (_U, [_U, ctypes.POINTER(SelectParams)]),
     "fp8q_quant_log_slot": (_I, [_I, ctypes.c_char_p, _I]),
     "fp8q_scale_to_kmajor": (_I, [_P, _P, _U, _U, _P]),
+    "fp8q_gemm_select": (_I, [_U, _U, _U]),
     "fp8q_gemm_blockscaled": (_I, [_P, _P, _P, _P, _P, _U, _U, _U, _P]),
     "fp8q_gemm_blockscaled_ex": (_I, [_P, _P, _P, _P, _P, _U, _U, _U, _I, _P]),
     "fp8q_proj": (_I, [_P, _P, _P, _P, _P, _P, _P, _U, _U, _U, _P]),
@@ -191,6 +192,15 @@ def fp8q_quant_select(M: int, K: int, cu_count: int):
     why = ctypes.c_char_p()
     v = lib().fp8q_quant_select(M, K, cu_count, ctypes.byref(grid), ctypes.byref(why))
     return v, tuple(grid), (why.value.decode() if why.value else None)
+
+
+def fp8q_gemm_select(M: int, N: int, K: int) -> int:
+    """Kernel id the auto GEMM runs for this shape (see fp8q_gemm_blockscaled_ex)."""
+    return int(lib().fp8q_gemm_select(M, N, K))
+
+
+GEMM_KERNEL_NAMES = {1: "gemm_tiled_kernel<128,128,2,2,2>", 2: "gemm_skinny_kernel",
+                     3: "gemm_tiled_kernel<256,128,4,2,3>", 4: "gemm_tiled_kernel<256,128,2,2,3>"}
 
 
 def fp8q_quant_b_min_m(K: int, params: SelectParams) -> int:

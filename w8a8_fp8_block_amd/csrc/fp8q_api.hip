@@ -90,12 +90,15 @@ fp8q_status launched(const char* fn, hipError_t e) {
 
 // ---- selector lever and log ----
 // FP8Q_QUANT_VARIANT: "a" = variant B not requested, "b" = force B,
-// anything else / unset = auto.  Read once per process.
+// "floor" = B requested (it runs when its grid reaches the floor), anything
+// else / unset = the target default (kQuantBRequestedByDefault).  Read once
+// per process.
 int env_variant() {
   static const int v = [] {
     const char* e = getenv("FP8Q_QUANT_VARIANT");
     if (e && (e[0] == 'a' || e[0] == 'A') && e[1] == '\0') return 1;
     if (e && (e[0] == 'b' || e[0] == 'B') && e[1] == '\0') return 2;
+    if (e && strcmp(e, "floor") == 0) return 3;
     return 0;
   }();
   return v;
@@ -157,13 +160,21 @@ fp8q_status run_quant(const char* fn, const uint16_t* x, uint8_t* q, float* srm,
   return launched(fn, e);
 }
 
-// GEMM kernel choice: the skinny kernel up to this many rows.
+// GEMM kernel choice: the skinny kernel up to this many rows; from this many
+// rows on, 256 x 128 tiles with 8 waves (one workgroup per CU), which move a
+// quarter less data per MFMA than two 128 x 128 workgroups and lose little
+// to a partial last tile row (measured crossover between M = 1168 and 4576).
 constexpr uint32_t kSkinnyAutoMaxM = 32;
+constexpr uint32_t kWideAutoMinM = 2048;
+
+int gemm_auto_kernel(uint32_t M) {
+  return (M <= kSkinnyAutoMaxM) ? 2 : (M >= kWideAutoMinM ? 3 : 1);
+}
 
 fp8q_status run_gemm(const char* fn, const uint8_t* a, const float* as, const uint8_t* w,
                      const float* ws, uint16_t* out, uint32_t M, uint32_t N, uint32_t K, int kernel,
                      hipStream_t s) {
-  if (kernel == 0) kernel = (M <= kSkinnyAutoMaxM) ? 2 : 1;
+  if (kernel == 0) kernel = gemm_auto_kernel(M);
   if (kernel == 2 && M > kSkinnyMaxM)
     return fail(FP8Q_ERR_VARIANT, "%s: skinny kernel needs M <= %u (M=%u)", fn, kSkinnyMaxM, M);
   const hipError_t e = (kernel == 2) ? launch_gemm_skinny(a, as, w, ws, out, M, N, K, s)
@@ -188,7 +199,8 @@ fp8q_select_params fp8q_default_select_params(uint32_t cu_count) {
   p.min_wg_per_cu = kQuantMinWgPerCu;
   p.b_groups_per_wg = kQuantBGroupsPerWg;
   p.a_groups_per_wg = kQuantAGroupsPerWg;
-  p.requested = env_variant() != 1;
+  const int env = env_variant();
+  p.requested = env == 3 || env == 2 || (env == 0 && kQuantBRequestedByDefault);
   p.b_present = 1;
   p.a_present = 1;
   return p;
@@ -322,6 +334,11 @@ fp8q_status fp8q_gemm_blockscaled_ex(const uint8_t* a_e4m3, const float* a_scale
   st = check_device(fn);
   if (st != FP8Q_OK) return st;
   return run_gemm(fn, a_e4m3, a_scale_km, w_e4m3, w_scale, out_bf16, M, N, K, kernel, stream);
+}
+
+int fp8q_gemm_select(uint32_t M, uint32_t N, uint32_t K) {
+  if (N == 0 || N % kGroup != 0 || K == 0 || K % kGroup != 0) return -1;
+  return gemm_auto_kernel(M);
 }
 
 fp8q_status fp8q_gemm_blockscaled(const uint8_t* a_e4m3, const float* a_scale_km,

@@ -15,10 +15,11 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // ---- quantizer geometry (shared with the selector) ----
-// Variant A: flat over all M*(K/128) groups, one 16-lane row per group,
-// 4 groups per wave, kQuantAWaves waves per workgroup.
+// Variant A: flat over all M*(K/128) groups; each 16-lane row takes
+// kQuantARounds consecutive groups, kQuantAWaves waves per workgroup.
 constexpr uint32_t kQuantAWaves = 4;
-constexpr uint32_t kQuantAGroupsPerWg = 4 * kQuantAWaves;
+constexpr uint32_t kQuantARounds = 2;
+constexpr uint32_t kQuantAGroupsPerWg = 4 * kQuantAWaves * kQuantARounds;
 // Variant B: K-grouped; a workgroup covers kQuantBGroupsPerWg consecutive
 // groups of one token row, kQuantBRounds groups per 16-lane row.
 constexpr uint32_t kQuantBWaves = 4;
@@ -26,6 +27,11 @@ constexpr uint32_t kQuantBRounds = 2;
 constexpr uint32_t kQuantBGroupsPerWg = 4 * kQuantBWaves * kQuantBRounds;
 // Floor of the selection rule on gfx950 (workgroups per CU).
 constexpr uint32_t kQuantMinWgPerCu = 2;
+// Target default of the lever that lets variant B run at all.  Off on
+// gfx950: timed with a cache flush before every launch over the token/K
+// sweep (M in 16..16384, K in 5120/6144/17408), B was never faster than A by
+// more than 0.1 us and was 3-15% slower wherever its grid fills the device.
+constexpr bool kQuantBRequestedByDefault = false;
 
 hipError_t launch_quant_a(const uint16_t* x, uint8_t* q, float* scale_rm,
                           float* scale_km, uint32_t M, uint32_t K, hipStream_t s);

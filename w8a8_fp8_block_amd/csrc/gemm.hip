@@ -18,10 +18,13 @@
 // full 128-term sum whatever order the hardware assigns to those bytes.
 #include "fp8q_internal.h"
 
+#include <utility>
+
 namespace fp8q {
 namespace {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v4i __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ v4f mfma_e4m3_128(const v8i& w, const v8i& a) {
@@ -47,33 +50,39 @@ __device__ __forceinline__ v8i join(u32x4 a, u32x4 b) {
 
 // ------------------------------------------------------------------------
 // LDS-tiled kernel.  Workgroup tile BM x BN, K step 128 (one scale block),
-// WGM x WGN waves, each owning a (BM/WGM) x (BN/WGN) sub-tile.
+// WGM x WGN waves, each owning a WM x WN = (BM/WGM) x (BN/WGN) sub-tile made
+// of TM x TN MFMA tiles of 16 x 16.
 //
 // Operands reach LDS through direct buffer->LDS loads (64 lanes x 16 B land in
 // 1 KB of consecutive LDS), so the ring of STAGES LDS buffers is filled
 // without staging registers.  A stage holds [BM rows][128 B] of activations,
-// [BN rows][128 B] of weights, the BM fp32 activation scales of that K block
-// (read from the K-major scale layout, where they are contiguous) and each
-// wave's weight scale.  16-byte chunk c of row r
-// sits at chunk position c ^ f(r), f(r) = (r & 7) ^ ((r >> 3) & 1), so the 16
-// lanes that read one chunk column of 16 consecutive rows hit 16 different
-// (row parity, chunk) bank groups; f depends on r mod 16 only, so every
-// fragment address is a per-lane constant plus a compile-time offset.  The
-// direct load realises the swizzle by choosing, per lane, which global chunk
-// lands in its fixed LDS slot.
+// [BN rows][128 B] of weights and, per wave, the activation scales of its WM
+// rows (read from the K-major scale layout, where they are contiguous) and 64
+// copies of the block's weight scale.  16-byte chunk c of row r sits at chunk
+// position c ^ f(r), f(r) = (r & 7) ^ ((r >> 3) & 1), so the 16 lanes that
+// read one chunk column of 16 consecutive rows hit 16 different (row parity,
+// chunk) bank groups; f depends on r mod 16 only, so every fragment address is
+// a per-lane constant plus a compile-time offset.  The direct load realises
+// the swizzle by choosing, per lane, which global chunk lands in its fixed
+// LDS slot.
 //
-// Fragments are double-buffered in registers: the LDS reads of K block kb+1
-// run under the MFMAs of block kb (the LDS, at ~128 B/clk per CU, needs about
-// as many cycles per block as the matrix cores do, so the two must overlap).
+// Register pipeline, per K block: the MFMAs of block kb run from registers
+// while the fragments of block kb+1 are read from LDS into a second register
+// set (activation fragments in place, as soon as the last MFMA of their row
+// has been issued).  The fp32 promotion of MFMA i is issued after MFMA i+2, so
+// the vector ALU never waits for the matrix pipe; the promotions of a block's
+// last two MFMAs run in the next block.  Each MFMA slot (the MFMA, the four
+// fmas, one or two LDS reads) is fenced off from the next with a scheduling
+// barrier: left to itself the compiler hoists all MFMAs of a block and then
+// has to serialise the next one on a single result register.
 // ------------------------------------------------------------------------
 // Direct global->LDS loads through a buffer resource: every lane of the wave
 // copies `bytes` (4 or 16) from base + voff (per lane, VGPR) + soff (uniform,
 // SGPR); lane i's data lands at lds + i * bytes, and lds must be the same for
 // the whole wave (it goes to M0).  With the per-K-block advance in soff the
-// loop spends no vector instructions on addresses.  Offsets at or beyond the
-// resource's byte count read as zero.  (Kept out of lambdas: HIP lambdas are
-// host+device, and a device-only builtin inside one called from a kernel
-// template makes the host pass drop that kernel's stub.)
+// loop spends no vector instructions on addresses.  (Kept out of lambdas: HIP
+// lambdas are host+device, and a device-only builtin inside one called from
+// a kernel template makes the host pass drop that kernel's stub.)
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   // raw buffer (stride 0): bound = bytes; word 3 = 0x00020000 for gfx9-family
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
@@ -95,6 +104,12 @@ __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+__device__ __forceinline__ void wg_barrier() {
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+__device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
 
 // wait until at most ahead*L of this wave's vector loads are outstanding
 template <int L, int A>
@@ -107,50 +122,36 @@ __device__ __forceinline__ void wait_ahead(uint32_t ahead) {
   }
 }
 
-// Scheduling pattern for one K block: MFMA i is followed by the four fmas
-// that promote MFMA i-LAG, one LDS read of the next block's fragments and,
-// for the first NV MFMAs, one direct global->LDS load, so the VALU work, the
-// LDS traffic and the texture-unit queue all run under the matrix pipe.
-template <int I, int NP, int LAG, int NV>
-__device__ __forceinline__ void sched_interleave_from() {
-  if constexpr (I < NP) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                          // MFMA
-    if constexpr (I >= LAG) __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // VALU
-    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                          // DS read
-    if constexpr (I < NV) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);    // VMEM read
-    sched_interleave_from<I + 1, NP, LAG, NV>();
-  } else {
-    __builtin_amdgcn_sched_group_barrier(0x002, 4 * LAG, 0);
-  }
+template <class F, int... Is>
+__device__ __forceinline__ void unroll_seq(F&& f, std::integer_sequence<int, Is...>) {
+  (f(std::integral_constant<int, Is>{}), ...);
 }
 
 template <int BM, int BN, int WGM, int WGN, int STAGES>
 struct TileCfg {
   static constexpr int NW = WGM * WGN, NT = 64 * NW;
-  static constexpr int WM = BM / WGM, WN = BN / WGN, TM = WM / 16, TN = WN / 16;
+  static constexpr int WM = BM / WGM, WN = BN / WGN, TM = WM / 16, TN = WN / 16, NP = TM * TN;
   static constexpr int A_BYTES = BM * 128, W_BYTES = BN * 128;
-  static constexpr int S_BYTES = 1024;  // activation scales of the block (BM <= 256 used)
-  static constexpr int STAGE_BYTES = A_BYTES + W_BYTES + S_BYTES;
-  static constexpr int WS_FLOATS = 1024;  // weight scales staged per 1024 K blocks
-  static constexpr int LDS_BYTES = STAGES * STAGE_BYTES + WS_FLOATS * 4;
+  static constexpr int SA = (WM + 63) / 64;        // activation-scale loads per wave and stage
+  static constexpr int SCW_BYTES = SA * 256 + 256;  // per wave: its scales + 64 weight-scale copies
+  static constexpr int STAGE_BYTES = A_BYTES + W_BYTES + NW * SCW_BYTES;
+  static constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
   static constexpr int DA = BM * 8 / 64 / NW;  // 1 KB direct loads per wave: activations
   static constexpr int DW = BN * 8 / 64 / NW;  //                              weights
-  static constexpr int LOADS = DA + DW;        // per stage, waves 1..NW-1
-  static constexpr int LOADS0 = DA + DW + 1;   // per stage, wave 0 (+ activation scales)
+  static constexpr int LOADS = DA + DW + SA + 1;  // direct loads per wave and stage
+  // LDS reads of the next block per MFMA slot: slot TN*tm + TN-1 (after the
+  // last MFMA of row tm) reads activation fragment tm; the other slots take,
+  // in order, the 2*TN weight-fragment halves, TM/2 activation-scale pairs
+  // and the weight scale.
+  static constexpr int FREE_OPS = 2 * TN + TM / 2 + 1;
+  static_assert(WM % 16 == 0 && WN % 16 == 0 && TN >= 2 && TM % 2 == 0 && NP % 4 == 0, "wave tile");
+  static_assert(NP - TM >= FREE_OPS, "too few MFMA slots for the LDS reads");
   static_assert(BM * 8 % (64 * NW) == 0 && BN * 8 % (64 * NW) == 0, "tile/wave mismatch");
-  static_assert(BM <= 256 && BM % 16 == 0, "activation scales: one 1 KB load per block");
-  static_assert(BN <= 128 && 128 % BN == 0 && WN <= BN, "one weight-scale block per tile");
+  static_assert(128 % WN == 0, "a wave's columns lie in one weight-scale block");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
-  static_assert(STAGES >= 2 && (STAGES - 2) * LOADS0 < 64, "vmcnt range");
+  static_assert(STAGES >= 2 && (STAGES - 2) * LOADS < 64, "vmcnt range");
+  static_assert(STAGE_BYTES % 256 == 0, "stage alignment");
 };
-
-// wait until at most `ahead` stages' worth of this wave's loads are
-// outstanding (wave 0 issues one load more per stage than the others)
-template <int L0, int L, int A>
-__device__ __forceinline__ void wait_stages(uint32_t ahead, bool wave0) {
-  if (wave0) wait_ahead<L0, A>(ahead);
-  else wait_ahead<L, A>(ahead);
-}
 
 template <int BM, int BN, int WGM, int WGN, int STAGES>
 __global__ __launch_bounds__(64 * WGM * WGN) void gemm_tiled_kernel(
@@ -158,11 +159,11 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_tiled_kernel(
     const float* __restrict__ Ws, uint16_t* __restrict__ out, uint32_t M, uint32_t N, uint32_t K,
     uint32_t Mp, uint32_t tiles_m, uint32_t tiles_n) {
   using C = TileCfg<BM, BN, WGM, WGN, STAGES>;
+  constexpr int TM = C::TM, TN = C::TN, NP = C::NP;
   extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
 
   const uint32_t tid = threadIdx.x, lane = tid & 63;
   const uint32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (SGPR)
-  const bool wave0 = wave == 0;
   const uint32_t wm = wave / WGN, wn = wave % WGN;
 
   // ---- tile of this workgroup: XCD-aware, grouped order ----
@@ -180,14 +181,14 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_tiled_kernel(
   const uint32_t tmi = first_m + (t % per_group) % gm, tni = (t % per_group) / gm;
   const uint32_t m0 = tmi * BM, n0 = tni * BN;
   const uint32_t G = K / kGroup;
-  const uint32_t nb = n0 / kGroup;
+  const uint32_t nb = (n0 + wn * C::WN) / kGroup;  // this wave's weight-scale block row
 
   // ---- buffer resources and per-lane source offsets (K block 0) ----
   const __amdgpu_buffer_rsrc_t rA = make_rsrc(A, M * K);
   const __amdgpu_buffer_rsrc_t rW = make_rsrc(W, N * K);
   const __amdgpu_buffer_rsrc_t rS = make_rsrc(As, G * Mp * 4);
   const __amdgpu_buffer_rsrc_t rWs = make_rsrc(Ws, (N / kGroup) * G * 4);
-  uint32_t a_off[C::DA], w_off[C::DW];
+  uint32_t a_off[C::DA], w_off[C::DW], s_off[C::SA];
 #pragma unroll
   for (int j = 0; j < C::DA; ++j) {
     const uint32_t c = (wave * C::DA + j) * 64 + lane, row = c >> 3;
@@ -198,10 +199,13 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_tiled_kernel(
     const uint32_t c = (wave * C::DW + j) * 64 + lane, row = c >> 3;
     w_off[j] = (n0 + row) * K + ((c & 7) ^ swz(row)) * 16;
   }
-  // activation scales: wave 0 loads rows m0 + 4*lane .. +3 of the block (16
-  // bytes per lane; rows past Mp are clamped in bounds and never used)
-  const uint32_t s_off = min(m0 + 4 * lane, Mp - 4) * 4;
-  float* ws_lds = reinterpret_cast<float*>(smem + STAGES * C::STAGE_BYTES);
+  // activation scales of this wave's rows (rows past Mp are clamped in
+  // bounds and never used; rows in [M, Mp) hold the layout's zero pad)
+#pragma unroll
+  for (int j = 0; j < C::SA; ++j) s_off[j] = min(m0 + wm * C::WM + j * 64 + lane, Mp - 1) * 4;
+  const uint32_t ws_off = nb * G * 4;  // every lane loads the same weight scale
+  const uint32_t sc_base = C::A_BYTES + C::W_BYTES + wave * C::SCW_BYTES;
+  const uint32_t ws_base = sc_base + C::SA * 256;
 
   auto issue_stage = [&](uint32_t kb, uint32_t stage) {
     uint8_t* base = smem + stage * C::STAGE_BYTES;
@@ -210,14 +214,9 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_tiled_kernel(
 #pragma unroll
     for (int j = 0; j < C::DW; ++j)
       dma16(rW, w_off[j], kb * kGroup, base + C::A_BYTES + (wave * C::DW + j) * 1024);
-    if (wave0) dma16(rS, s_off, kb * Mp * 4, base + C::A_BYTES + C::W_BYTES);
-  };
-  // weight scales w_s[nb][kb0 .. kb0+1023] (wave 0; reads past the end of the
-  // row are never used, reads past the end of w_s return zero)
-  auto issue_ws = [&](uint32_t kb0) {
 #pragma unroll
-    for (int j = 0; j < C::WS_FLOATS / 256; ++j)
-      dma16(rWs, (nb * G + kb0 + j * 256 + lane * 4) * 4, 0, ws_lds + j * 256);
+    for (int j = 0; j < C::SA; ++j) dma4(rS, s_off[j], kb * Mp * 4, base + sc_base + j * 256);
+    dma4(rWs, ws_off, kb * 4, base + ws_base);
   };
 
   // Per-lane byte offsets of a fragment inside a 16-row slab: this lane's row
@@ -225,110 +224,115 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_tiled_kernel(
   const uint32_t l16 = lane & 15, c0 = 2 * (lane >> 4);
   const uint32_t lo0 = l16 * 128 + ((c0 ^ swz(l16)) * 16);
   const uint32_t lo1 = l16 * 128 + (((c0 + 1) ^ swz(l16)) * 16);
-  auto frag = [&](const uint8_t* slab) -> v8i {
-    return join(*reinterpret_cast<const u32x4*>(slab + lo0),
-                *reinterpret_cast<const u32x4*>(slab + lo1));
-  };
+  auto ld16 = [](const uint8_t* p) -> v4i { return *reinterpret_cast<const v4i*>(p); };
+  auto ldf = [](const uint8_t* p) -> float { return *reinterpret_cast<const float*>(p); };
   auto slot_base = [&](uint32_t kb) -> const uint8_t* {
     return smem + (kb % STAGES) * C::STAGE_BYTES;
   };
-  auto read_a = [&](uint32_t kb, int tm) -> v8i {
-    return frag(slot_base(kb) + (wm * C::WM + tm * 16) * 128);
-  };
-  auto read_b = [&](uint32_t kb, int tn) -> v8i {
-    return frag(slot_base(kb) + C::A_BYTES + (wn * C::WN + tn * 16) * 128);
-  };
-  auto read_sc = [&](float (&sc)[C::TM], uint32_t kb) {
-    const float* s_lds = reinterpret_cast<const float*>(slot_base(kb) + C::A_BYTES + C::W_BYTES);
-    const float ws = ws_lds[kb % C::WS_FLOATS];
-#pragma unroll
-    for (int tm = 0; tm < C::TM; ++tm) sc[tm] = s_lds[wm * C::WM + tm * 16 + l16] * ws;
-  };
+  const uint32_t a_row0 = wm * C::WM * 128, w_row0 = C::A_BYTES + wn * C::WN * 128;
 
-  v4f acc[C::TM][C::TN];
+  v4f acc[TM][TN];
 #pragma unroll
-  for (int i = 0; i < C::TM; ++i)
+  for (int i = 0; i < TM; ++i)
 #pragma unroll
-    for (int j = 0; j < C::TN; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int j = 0; j < TN; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
-  // Pipeline.  Stage s is loaded into LDS slot s % STAGES by direct loads
-  // issued during iteration s - STAGES (the prologue issues the first
-  // STAGES), and its fragments are read into registers during iteration
-  // s - 1, under the MFMAs of block s - 1: activation fragments in place,
-  // row by row, as the rows of block s-1 are issued; weight fragments and
-  // the combined scales a_s * w_s into the second of two register sets.  At
-  // the top of iteration kb each wave waits for its own LDS reads and for
-  // its loads of stage kb+1, and one barrier makes that hold for all waves;
-  // slot kb % STAGES (read during iteration kb-1) is then free to refill.
-  if (wave0) issue_ws(0);
+  // ---- prologue: the first STAGES stages, then block 0 into registers ----
+  // Stages past the last K block reload the last block (in bounds, never
+  // read), so that every iteration issues the same loads and waits for the
+  // same count, and the loop body stays one basic block.
 #pragma unroll
-  for (int s = 0; s < STAGES; ++s)
-    if ((uint32_t)s < G) issue_stage(s, s);
-  wait_stages<C::LOADS0, C::LOADS, STAGES - 1>(min(G - 1, (uint32_t)(STAGES - 1)), wave0);
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
+  for (int s = 0; s < STAGES; ++s) issue_stage(min((uint32_t)s, G - 1), s);
+  wait_vmcnt<(STAGES - 1) * C::LOADS>();
+  wg_barrier();
 
-  constexpr int NP = C::TM * C::TN, LAG = 2;
-  v8i af[C::TM], bf0[C::TN], bf1[C::TN];
-  float sc0[C::TM], sc1[C::TM];
+  v8i af[TM], bf0[TN], bf1[TN];
+  float as0[TM], as1[TM], ws0, ws1;
+  {
+    const uint8_t* s0 = slot_base(0);
 #pragma unroll
-  for (int tm = 0; tm < C::TM; ++tm) af[tm] = read_a(0, tm);
-#pragma unroll
-  for (int tn = 0; tn < C::TN; ++tn) bf0[tn] = read_b(0, tn);
-  read_sc(sc0, 0);
-
-  auto step = [&](uint32_t kb, const v8i (&bf)[C::TN], const float (&sc)[C::TM],
-                  v8i (&bf_n)[C::TN], float (&sc_n)[C::TM]) {
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt/expcnt unconstrained
-    if (kb + 1 < G)
-      wait_stages<C::LOADS0, C::LOADS, STAGES - 2>(min(G - 2 - kb, (uint32_t)(STAGES - 2)), wave0);
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-    if ((kb + 1) % C::WS_FLOATS == 0 && kb + 1 < G) {
-      // next chunk of weight scales (every 1024 K blocks): everyone has read
-      // the last scale of the old chunk (block kb's, during iteration kb-1)
-      if (wave0) {
-        issue_ws(kb + 1);
-        wait_vmcnt<0>();
-      }
-      __builtin_amdgcn_s_barrier();
-      asm volatile("" ::: "memory");
+    for (int tm = 0; tm < TM; ++tm) {
+      af[tm].lo = ld16(s0 + a_row0 + tm * 2048 + lo0);
+      af[tm].hi = ld16(s0 + a_row0 + tm * 2048 + lo1);
+      as0[tm] = ldf(s0 + sc_base + (tm * 16 + l16) * 4);
     }
-    if (kb + STAGES < G) issue_stage(kb + STAGES, kb % STAGES);
-    // (reads of block kb+1 are issued unconditionally: on the last block they
-    // read a stale but in-bounds slot whose values are never used, which keeps
-    // the body one straight-line scheduling region)
 #pragma unroll
-    for (int tn = 0; tn < C::TN; ++tn) bf_n[tn] = read_b(kb + 1, tn);
-    read_sc(sc_n, kb + 1);
-    v4f p[LAG + 1];
-#pragma unroll
-    for (int i = 0; i < NP + LAG; ++i) {
-      if (i < NP) {
-        const int tm = i / C::TN, tn = i % C::TN;
-        p[i % (LAG + 1)] = mfma_e4m3_128(bf[tn], af[tm]);
-        if (tn == C::TN - 1) af[tm] = read_a(kb + 1, tm);
-      }
-      if (i >= LAG) {
-        const int j = i - LAG, tm = j / C::TN, tn = j % C::TN;
-        acc[tm][tn] += p[j % (LAG + 1)] * sc[tm];
-      }
+    for (int tn = 0; tn < TN; ++tn) {
+      bf0[tn].lo = ld16(s0 + w_row0 + tn * 2048 + lo0);
+      bf0[tn].hi = ld16(s0 + w_row0 + tn * 2048 + lo1);
     }
-    sched_interleave_from<0, NP, LAG, C::LOADS0>();
+    ws0 = ldf(s0 + ws_base);
+  }
+
+  // MFMA results rotate through 4 register sets; the promotions of the last
+  // two MFMAs of a block are pending when the next block starts (zero before
+  // the first block).
+  v4f p[4];
+  p[(NP - 2) & 3] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+  p[(NP - 1) & 3] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+  float sc[TM], sc_tail = 0.0f;
+
+  auto step = [&](uint32_t kb, const v8i(&bf)[TN], const float(&as)[TM], float ws, v8i(&bfn)[TN],
+                  float(&asn)[TM], float& wsn) {
+    wait_lgkm0();  // fragments and scales of block kb are in registers
+#pragma unroll
+    for (int tm = 0; tm < TM; ++tm) sc[tm] = as[tm] * ws;
+    wait_vmcnt<(STAGES - 2) * C::LOADS>();
+    wg_barrier();  // stage kb+1 is in LDS; slot kb % STAGES is free
+    issue_stage(min(kb + STAGES, G - 1), kb % STAGES);
+    // (on the last block the reads below fetch a slot holding a reloaded
+    // copy of the last block, never used; its load has completed)
+    const uint8_t* nx = slot_base(kb + 1);
+    unroll_seq(
+        [&](auto ic) {
+          constexpr int I = decltype(ic)::value;
+          constexpr int tm = I / TN, tn = I % TN;
+          p[I & 3] = mfma_e4m3_128(bf[tn], af[tm]);
+          if constexpr (I < 2) {
+            constexpr int J = NP - 2 + I;
+            acc[J / TN][J % TN] += p[J & 3] * sc_tail;
+          } else {
+            constexpr int J = I - 2;
+            acc[J / TN][J % TN] += p[J & 3] * sc[J / TN];
+          }
+          if constexpr (tn == TN - 1) {
+            af[tm].lo = ld16(nx + a_row0 + tm * 2048 + lo0);
+            af[tm].hi = ld16(nx + a_row0 + tm * 2048 + lo1);
+          } else {
+            constexpr int Q = I - I / TN;
+            if constexpr (Q < 2 * TN) {
+              if constexpr (Q & 1) bfn[Q / 2].hi = ld16(nx + w_row0 + (Q / 2) * 2048 + lo1);
+              else bfn[Q / 2].lo = ld16(nx + w_row0 + (Q / 2) * 2048 + lo0);
+            } else if constexpr (Q < 2 * TN + TM / 2) {
+              constexpr int T2 = 2 * (Q - 2 * TN);
+              asn[T2] = ldf(nx + sc_base + (T2 * 16 + l16) * 4);
+              asn[T2 + 1] = ldf(nx + sc_base + ((T2 + 1) * 16 + l16) * 4);
+            } else if constexpr (Q == 2 * TN + TM / 2) {
+              wsn = ldf(nx + ws_base);
+            }
+          }
+          sched_fence();
+        },
+        std::make_integer_sequence<int, NP>{});
+    sc_tail = sc[TM - 1];
   };
   uint32_t kb = 0;
   for (; kb + 2 <= G; kb += 2) {
-    step(kb, bf0, sc0, bf1, sc1);
-    step(kb + 1, bf1, sc1, bf0, sc0);
+    step(kb, bf0, as0, ws0, bf1, as1, ws1);
+    step(kb + 1, bf1, as1, ws1, bf0, as0, ws0);
   }
-  if (kb < G) step(kb, bf0, sc0, bf1, sc1);
+  if (kb < G) step(kb, bf0, as0, ws0, bf1, as1, ws1);
+  wait_vmcnt<0>();  // no direct load may still be writing LDS when the workgroup ends
+  // promotions of the last block's last two MFMAs (both in its last row)
+  acc[(NP - 2) / TN][(NP - 2) % TN] += p[(NP - 2) & 3] * sc_tail;
+  acc[(NP - 1) / TN][(NP - 1) % TN] += p[(NP - 1) & 3] * sc_tail;
 
 #pragma unroll
-  for (int tm = 0; tm < C::TM; ++tm) {
+  for (int tm = 0; tm < TM; ++tm) {
     const uint32_t m = m0 + wm * C::WM + tm * 16 + (lane & 15);
     if (m < M) {
 #pragma unroll
-      for (int tn = 0; tn < C::TN; ++tn) {
+      for (int tn = 0; tn < TN; ++tn) {
         const uint32_t n = n0 + wn * C::WN + tn * 16 + 4 * (lane >> 4);
         *reinterpret_cast<uint2*>(out + (uint64_t)m * N + n) = pack_bf16x4(acc[tm][tn]);
       }
@@ -355,7 +359,6 @@ hipError_t launch_tiled_cfg(const uint8_t* a, const float* a_s_km, const uint8_t
       a, a_s_km, w, w_s, out, M, N, K, m_pad16(M), tiles_m, tiles_n);
   return hipGetLastError();
 }
-
 // ------------------------------------------------------------------------
 // Skinny kernel for decode widths (M <= 16*TM <= 64).  The projection is then
 // bound by streaming the weight matrix once, so each workgroup owns 16 output

@@ -8,8 +8,9 @@
 // 128 bf16, so group i lives at x + 128*i, its codes at q + 128*i and its
 // row-major scale at scale_rm[i].
 //
-// Work split: one 16-lane DPP row of a wave owns one group; each lane holds 8
-// bf16 (one 128-bit load) and produces 8 codes (one 64-bit store).  The group
+// Work split: one 16-lane DPP row of a wave owns one group at a time; each
+// lane holds 8 bf16 (one 128-bit load) and produces 8 codes (one 64-bit
+// store).  The group
 // maximum is an integer max over bf16 magnitudes (packed u16 max, then a
 // 4-step DPP butterfly inside the row), which is exact and needs no float
 // canonicalization.
@@ -95,18 +96,30 @@ __device__ __forceinline__ void write_scales(float s, uint64_t g, float* __restr
   }
 }
 
-// Variant A (fine-grained): flat over groups, 4 groups per wave, one round.
+// Variant A (fine-grained): flat over groups; each 16-lane row takes
+// kQuantARounds consecutive groups, all loads issued before any is consumed
+// (two 128-bit loads in flight per lane: measured 5-8% faster than one on
+// gfx950 at prefill sizes), and the codes, which nothing reads back soon,
+// are stored non-temporally.
 __global__ __launch_bounds__(64 * kQuantAWaves) void quant_a_kernel(
     const u32x4* __restrict__ x, u32x2* __restrict__ q, float* __restrict__ srm,
     float* __restrict__ skm, uint64_t ngroups, uint32_t G, uint32_t Mp) {
-  const uint64_t g = (uint64_t)blockIdx.x * kQuantAGroupsPerWg + (threadIdx.x >> 4);
-  if (g >= ngroups) return;  // whole 16-lane rows retire together
-  const uint64_t idx = g * 16 + (threadIdx.x & 15);
-  const u32x4 v = __builtin_nontemporal_load(&x[idx]);
-  float s;
-  const u32x2 c = quant_group(v, s);
-  q[idx] = c;
-  if ((threadIdx.x & 15) == 0) write_scales(s, g, srm, skm, G, Mp);
+  const uint64_t g0 =
+      ((uint64_t)blockIdx.x * (kQuantAGroupsPerWg / kQuantARounds) + (threadIdx.x >> 4)) * kQuantARounds;
+  const uint32_t l = threadIdx.x & 15;
+  u32x4 v[kQuantARounds];
+#pragma unroll
+  for (uint32_t r = 0; r < kQuantARounds; ++r)
+    if (g0 + r < ngroups) v[r] = __builtin_nontemporal_load(&x[(g0 + r) * 16 + l]);
+#pragma unroll
+  for (uint32_t r = 0; r < kQuantARounds; ++r) {
+    if (g0 + r < ngroups) {  // uniform over the 16-lane row
+      float s;
+      const u32x2 c = quant_group(v[r], s);
+      __builtin_nontemporal_store(c, &q[(g0 + r) * 16 + l]);
+      if (l == 0) write_scales(s, g0 + r, srm, skm, G, Mp);
+    }
+  }
 }
 
 // Variant B (K-grouped): workgroup (m, by) covers groups
