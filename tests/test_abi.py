@@ -110,10 +110,20 @@ def test_gemm_validation():
 
 
 def test_gemm_select():
-    """Auto GEMM choice: skinny kernel up to 32 rows, 256x128 tiles from 2048
+    """Auto GEMM choice: skinny kernel up to 64 rows, 256x128 tiles from 2048
     rows on, 128x128 tiles between; bad N/K -> -1 (pure host function)."""
-    for M, want in ((1, 2), (16, 2), (25, 2), (32, 2), (33, 1), (1168, 1), (2047, 1), (2048, 3),
+    for M, want in ((1, 2), (16, 2), (25, 2), (64, 2), (65, 1), (1168, 1), (2047, 1), (2048, 3),
                     (4576, 3), (16384, 3)):
         assert fp8q.fp8q_gemm_select(M, 5120, 17408) == want, M
     assert fp8q.fp8q_gemm_select(64, 100, 128) == -1
     assert fp8q.fp8q_gemm_select(64, 128, 0) == -1
+
+
+def test_proj_quant_fused():
+    """fp8q_proj fuses the relayout into the quantizer up to 2^17 scale groups."""
+    assert fp8q.fp8q_proj_quant_fused(16, 5120)
+    assert fp8q.fp8q_proj_quant_fused(1168, 5120)           # 46720 groups
+    assert not fp8q.fp8q_proj_quant_fused(1168, 17408)      # 158848 groups
+    assert fp8q.fp8q_proj_quant_fused(3276, 5120)           # 131040 groups
+    assert not fp8q.fp8q_proj_quant_fused(3277, 5120)       # 131080 groups
+    assert not fp8q.fp8q_proj_quant_fused(4576, 17408)

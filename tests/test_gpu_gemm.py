@@ -213,11 +213,20 @@ def test_gemm_rowmajor_scales_fail(orc):
         assert rel > 10 * RTOL and exc > 10
 
 
+# a shape past the fused-quantizer limit (1000 * 17408/128 = 136000 scale
+# groups > 2^17), so fp8q_proj runs the quantizer and the relayout separately
+_PROJ_SPLIT = synth.Workload("proj_split", 1000, 17408, 256, "laplace", 87, 50.0)
+
+
 @pytest.mark.parametrize("name,M", [("tiny", None), ("decode", 17), ("decode", 25),
-                                    ("prefill", 130)])
+                                    ("prefill", 130), ("proj_split", None)])
 def test_proj_end_to_end(orc, name, M):
-    w = synth.workload(name) if M is None or name != "decode" else synth.workload(name, M=M)
+    if name == "proj_split":
+        w = _PROJ_SPLIT
+    else:
+        w = synth.workload(name) if M is None or name != "decode" else synth.workload(name, M=M)
     x, wf, _ = synth.make_inputs(w, M=M)
+    assert fp8q.fp8q_proj_quant_fused(x.shape[0], w.K) == (name != "proj_split")
     Mr = x.shape[0]
     a, a_s = orc.quant_act(x)
     km_ref = orc.scale_to_kmajor(a_s)

@@ -61,6 +61,7 @@ _SIGS = {
     "fp8q_quant_log_slot": (_I, [_I, ctypes.c_char_p, _I]),
     "fp8q_scale_to_kmajor": (_I, [_P, _P, _U, _U, _P]),
     "fp8q_gemm_select": (_I, [_U, _U, _U]),
+    "fp8q_proj_quant_fused": (_I, [_U, _U]),
     "fp8q_gemm_blockscaled": (_I, [_P, _P, _P, _P, _P, _U, _U, _U, _P]),
     "fp8q_gemm_blockscaled_ex": (_I, [_P, _P, _P, _P, _P, _U, _U, _U, _I, _P]),
     "fp8q_proj": (_I, [_P, _P, _P, _P, _P, _P, _P, _U, _U, _U, _P]),
@@ -197,6 +198,11 @@ def fp8q_quant_select(M: int, K: int, cu_count: int):
 def fp8q_gemm_select(M: int, N: int, K: int) -> int:
     """Kernel id the auto GEMM runs for this shape (see fp8q_gemm_blockscaled_ex)."""
     return int(lib().fp8q_gemm_select(M, N, K))
+
+
+def fp8q_proj_quant_fused(M: int, K: int) -> bool:
+    """True if fp8q_proj writes the K-major scales from the quantizer itself."""
+    return bool(lib().fp8q_proj_quant_fused(M, K))
 
 
 GEMM_KERNEL_NAMES = {1: "gemm_tiled_kernel<128,128,2,2,2>", 2: "gemm_skinny_kernel",

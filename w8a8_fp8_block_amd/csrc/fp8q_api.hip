@@ -160,11 +160,17 @@ fp8q_status run_quant(const char* fn, const uint16_t* x, uint8_t* q, float* srm,
   return launched(fn, e);
 }
 
-// GEMM kernel choice: the skinny kernel up to this many rows; from this many
+// GEMM kernel choice: the skinny kernel up to this many rows (at M = 64 it
+// streams the weights in half the tiled kernel's time); from this many
 // rows on, 256 x 128 tiles with 8 waves (one workgroup per CU), which move a
 // quarter less data per MFMA than two 128 x 128 workgroups and lose little
 // to a partial last tile row (measured crossover between M = 1168 and 4576).
-constexpr uint32_t kSkinnyAutoMaxM = 32;
+constexpr uint32_t kSkinnyAutoMaxM = 64;
+// fp8q_proj writes the K-major scales from the quantizer itself (one launch
+// fewer) up to this many scale groups; beyond it the quantizer's scattered
+// K-major stores cost more than the separate relayout launch (measured:
+// 8.5 vs 16.5 us at M*K/128 = 46720, 69 vs 56 us at 622336).
+constexpr uint64_t kFusedKmajorMaxGroups = 1u << 17;
 constexpr uint32_t kWideAutoMinM = 2048;
 
 int gemm_auto_kernel(uint32_t M) {
@@ -177,7 +183,10 @@ fp8q_status run_gemm(const char* fn, const uint8_t* a, const float* as, const ui
   if (kernel == 0) kernel = gemm_auto_kernel(M);
   if (kernel == 2 && M > kSkinnyMaxM)
     return fail(FP8Q_ERR_VARIANT, "%s: skinny kernel needs M <= %u (M=%u)", fn, kSkinnyMaxM, M);
-  const hipError_t e = (kernel == 2) ? launch_gemm_skinny(a, as, w, ws, out, M, N, K, s)
+  uint32_t cus = 0;
+  const fp8q_status st = check_device(fn, &cus);
+  if (st != FP8Q_OK) return st;
+  const hipError_t e = (kernel == 2) ? launch_gemm_skinny(a, as, w, ws, out, M, N, K, cus, s)
                                      : launch_gemm_tiled(a, as, w, ws, out, M, N, K,
                                                          kernel == 1 ? 1 : kernel - 1, s);
   return launched(fn, e);
@@ -347,6 +356,10 @@ fp8q_status fp8q_gemm_blockscaled(const uint8_t* a_e4m3, const float* a_scale_km
   return fp8q_gemm_blockscaled_ex(a_e4m3, a_scale_km, w_e4m3, w_scale, out_bf16, M, N, K, 0, stream);
 }
 
+int fp8q_proj_quant_fused(uint32_t M, uint32_t K) {
+  return (uint64_t)M * (K / kGroup) <= kFusedKmajorMaxGroups ? 1 : 0;
+}
+
 fp8q_status fp8q_proj(const uint16_t* x_bf16, const uint8_t* w_e4m3, const float* w_scale,
                       uint16_t* out_bf16, uint8_t* act_q_scratch, float* act_scale_scratch,
                       float* act_scale_km_scratch, uint32_t M, uint32_t N, uint32_t K,
@@ -365,10 +378,17 @@ fp8q_status fp8q_proj(const uint16_t* x_bf16, const uint8_t* w_e4m3, const float
   REQUIRE_PTR(act_scale_scratch);
   REQUIRE_PTR(act_scale_km_scratch);
   if (M == 0) return ok();
-  st = run_quant(fn, x_bf16, act_q_scratch, act_scale_scratch, nullptr, M, K, 0, stream);
-  if (st != FP8Q_OK) return st;
-  st = launched(fn, launch_relayout(act_scale_scratch, act_scale_km_scratch, M, K, stream));
-  if (st != FP8Q_OK) return st;
+  if (fp8q_proj_quant_fused(M, K)) {
+    // one kernel writes both scale layouts (saves a launch)
+    st = run_quant(fn, x_bf16, act_q_scratch, act_scale_scratch, act_scale_km_scratch, M, K, 0,
+                   stream);
+    if (st != FP8Q_OK) return st;
+  } else {
+    st = run_quant(fn, x_bf16, act_q_scratch, act_scale_scratch, nullptr, M, K, 0, stream);
+    if (st != FP8Q_OK) return st;
+    st = launched(fn, launch_relayout(act_scale_scratch, act_scale_km_scratch, M, K, stream));
+    if (st != FP8Q_OK) return st;
+  }
   return run_gemm(fn, act_q_scratch, act_scale_km_scratch, w_e4m3, w_scale, out_bf16, M, N, K, 0,
                   stream);
 }

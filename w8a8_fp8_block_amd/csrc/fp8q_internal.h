@@ -53,7 +53,7 @@ hipError_t launch_gemm_tiled(const uint8_t* a, const float* a_s_km, const uint8_
                              uint32_t K, int cfg, hipStream_t s);
 hipError_t launch_gemm_skinny(const uint8_t* a, const float* a_s_km, const uint8_t* w,
                               const float* w_s, uint16_t* out, uint32_t M, uint32_t N,
-                              uint32_t K, hipStream_t s);
+                              uint32_t K, uint32_t cu_count, hipStream_t s);
 
 inline uint32_t m_pad16(uint32_t m) { return (m + 15u) / 16u * 16u; }
 

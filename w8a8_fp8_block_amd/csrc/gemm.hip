@@ -361,87 +361,150 @@ hipError_t launch_tiled_cfg(const uint8_t* a, const float* a_s_km, const uint8_t
 }
 // ------------------------------------------------------------------------
 // Skinny kernel for decode widths (M <= 16*TM <= 64).  The projection is then
-// bound by streaming the weight matrix once, so each workgroup owns 16 output
-// columns for all M rows and its 4 waves split the K blocks; fragments come
-// straight from global memory (no reuse to stage) with kUnroll blocks of
-// loads in flight per wave, and the 4 partial tiles are summed through LDS.
+// bound by streaming the weight matrix once, and the weight bytes must be
+// spread evenly over the CUs: with one workgroup per 16 output columns
+// (384 workgroups at N = 6144 on 256 CUs) half the CUs stream twice as much
+// as the others.  So the grid has one workgroup per CU and workgroup w owns
+// the contiguous column range [c0, c0 + cw), cw = N/grid rounded to 4
+// columns, covered by ceil(cw/16) MFMA tiles of 16 columns (the last one
+// partial: its missing weight rows are zero fragments, its missing columns
+// are not stored).  The NWV waves take interleaved K blocks (wave w: blocks
+// w, w+NWV, ...) for all of the workgroup's tiles; each wave issues the loads
+// of U blocks before consuming any, the activation fragments of a block are
+// loaded once for all tiles, and the NWV partial tiles are summed through
+// LDS in wave order.
 // ------------------------------------------------------------------------
-constexpr int kSkinnyWaves = 4;
-constexpr int kSkinnyUnroll = 4;
-
-template <int TM>
-__global__ __launch_bounds__(64 * kSkinnyWaves) void gemm_skinny_kernel(
+template <int TM, int TN, int NWV, int U>
+__global__ __launch_bounds__(64 * NWV) void gemm_skinny_kernel(
     const uint8_t* __restrict__ A, const float* __restrict__ As, const uint8_t* __restrict__ W,
     const float* __restrict__ Ws, uint16_t* __restrict__ out, uint32_t M, uint32_t N, uint32_t K,
-    uint32_t Mp) {
-  __shared__ v4f red[kSkinnyWaves][TM][64];
-  const uint32_t lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const uint32_t n0 = blockIdx.x * 16;
-  const uint32_t G = K / kGroup, nb = n0 / kGroup;
-  const uint32_t kq = 32 * (lane >> 4);  // this lane's byte offset in a K block
-  const uint8_t* wrow = W + (uint64_t)(n0 + (lane & 15)) * K + kq;
+    uint32_t Mp, uint32_t units_base, uint32_t units_rem) {
+  __shared__ v4f red[NWV][TN][TM][64];
+  const uint32_t lane = threadIdx.x & 63, wave = threadIdx.x >> 6, w = blockIdx.x;
+  // this workgroup's columns, in units of 4
+  const uint32_t c0 = 4 * (w * units_base + min(w, units_rem));
+  const uint32_t c1 = c0 + 4 * (units_base + (w < units_rem ? 1u : 0u));
+  const uint32_t nt = (c1 - c0 + 15) / 16;
+  const uint32_t G = K / kGroup;
+  const uint32_t l16 = lane & 15, kq = 32 * (lane >> 4);  // this lane's byte offset in a K block
+  // operand rows: weight row c0 + 16t + l16 (zero beyond c1), activation row 16tm + l16
+  const uint8_t* wrow[TN];
+  bool wok[TN];
+  uint32_t wsi[TN];  // weight-scale row of this lane's four output columns
+#pragma unroll
+  for (int t = 0; t < TN; ++t) {
+    const uint32_t r = c0 + 16 * t + l16;
+    wok[t] = r < c1;
+    wrow[t] = W + (uint64_t)min(r, N - 1) * K + kq;
+    wsi[t] = min(c0 + 16 * t + 4 * (lane >> 4), N - 1) / kGroup * G;
+  }
   const uint8_t* arow[TM];
   uint32_t srow[TM];
 #pragma unroll
   for (int tm = 0; tm < TM; ++tm) {
-    const uint32_t m = tm * 16 + (lane & 15);
+    const uint32_t m = tm * 16 + l16;
     arow[tm] = A + (uint64_t)min(m, M - 1) * K + kq;
     srow[tm] = min(m, Mp - 1);
   }
 
-  v4f acc[TM];
+  v4f acc[TN][TM];
 #pragma unroll
-  for (int tm = 0; tm < TM; ++tm) acc[tm] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int t = 0; t < TN; ++t)
+#pragma unroll
+    for (int tm = 0; tm < TM; ++tm) acc[t][tm] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
-  // contiguous K-block range of this wave
-  const uint32_t per = (G + kSkinnyWaves - 1) / kSkinnyWaves;
-  const uint32_t kb_lo = min(wave * per, G), kb_hi = min(kb_lo + per, G);
-  for (uint32_t kb = kb_lo; kb < kb_hi; kb += kSkinnyUnroll) {
-    v8i wf[kSkinnyUnroll], af[kSkinnyUnroll][TM];
-    float as[kSkinnyUnroll][TM], ws[kSkinnyUnroll];
+  for (uint32_t kb0 = wave; kb0 < G; kb0 += NWV * U) {
+    v8i wf[U][TN], af[U][TM];
+    float as[U][TM], ws[U][TN];
 #pragma unroll
-    for (int u = 0; u < kSkinnyUnroll; ++u) {
-      const uint32_t k = kb + u;
-      if (k < kb_hi) {
-        const u32x4* wp = reinterpret_cast<const u32x4*>(wrow + (uint64_t)k * kGroup);
-        wf[u] = join(__builtin_nontemporal_load(wp), __builtin_nontemporal_load(wp + 1));
+    for (int u = 0; u < U; ++u) {
+      const uint32_t k = kb0 + u * NWV;
+      if (k < G) {
+#pragma unroll
+        for (int t = 0; t < TN; ++t) {
+          if ((uint32_t)t < nt) {
+            if (wok[t]) {
+              const u32x4* wp = reinterpret_cast<const u32x4*>(wrow[t] + (uint64_t)k * kGroup);
+              wf[u][t] = join(__builtin_nontemporal_load(wp), __builtin_nontemporal_load(wp + 1));
+            } else {
+              wf[u][t] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+            }
+            ws[u][t] = Ws[wsi[t] + k];
+          }
+        }
 #pragma unroll
         for (int tm = 0; tm < TM; ++tm) {
           const u32x4* ap = reinterpret_cast<const u32x4*>(arow[tm] + (uint64_t)k * kGroup);
           af[u][tm] = join(ap[0], ap[1]);
           as[u][tm] = As[(uint64_t)k * Mp + srow[tm]];
         }
-        ws[u] = Ws[(uint64_t)nb * G + k];
       }
     }
 #pragma unroll
-    for (int u = 0; u < kSkinnyUnroll; ++u) {
-      if (kb + u < kb_hi) {
+    for (int u = 0; u < U; ++u) {
+      if (kb0 + u * NWV < G) {
 #pragma unroll
-        for (int tm = 0; tm < TM; ++tm) {
-          const v4f p = mfma_e4m3_128(wf[u], af[u][tm]);
-          acc[tm] += p * (as[u][tm] * ws[u]);
+        for (int t = 0; t < TN; ++t) {
+          if ((uint32_t)t < nt) {
+#pragma unroll
+            for (int tm = 0; tm < TM; ++tm) {
+              const v4f p = mfma_e4m3_128(wf[u][t], af[u][tm]);
+              acc[t][tm] += p * (as[u][tm] * ws[u][t]);
+            }
+          }
         }
       }
     }
   }
 
 #pragma unroll
-  for (int tm = 0; tm < TM; ++tm) red[wave][tm][lane] = acc[tm];
+  for (int t = 0; t < TN; ++t)
+#pragma unroll
+    for (int tm = 0; tm < TM; ++tm) red[wave][t][tm][lane] = acc[t][tm];
   __syncthreads();
-  if (wave == 0) {
+  // waves share the final sums: wave v sums and stores tiles (t, tm) with
+  // t*TM + tm = v (mod NWV)
 #pragma unroll
-    for (int tm = 0; tm < TM; ++tm) {
-      v4f s = red[0][tm][lane];
+  for (int j = 0; j < TN * TM; ++j) {
+    const int t = j / TM, tm = j % TM;
+    if ((uint32_t)(j % NWV) == wave && (uint32_t)t < nt) {
+      v4f s = red[0][t][tm][lane];
 #pragma unroll
-      for (int w = 1; w < kSkinnyWaves; ++w) s += red[w][tm][lane];
-      const uint32_t m = tm * 16 + (lane & 15);
-      if (m < M) {
-        const uint32_t n = n0 + 4 * (lane >> 4);
-        *reinterpret_cast<uint2*>(out + (uint64_t)m * N + n) = pack_bf16x4(s);
-      }
+      for (int v = 1; v < NWV; ++v) s += red[v][t][tm][lane];
+      const uint32_t m = tm * 16 + l16;
+      const uint32_t n = c0 + 16 * t + 4 * (lane >> 4);
+      if (m < M && n < c1) *reinterpret_cast<uint2*>(out + (uint64_t)m * N + n) = pack_bf16x4(s);
     }
   }
+}
+
+template <int TM, int TN>
+hipError_t launch_skinny_tn(const uint8_t* a, const float* a_s_km, const uint8_t* w,
+                            const float* w_s, uint16_t* out, uint32_t M, uint32_t N, uint32_t K,
+                            uint32_t grid, uint32_t base, uint32_t rem, hipStream_t s) {
+  // static LDS for the partial sums: NWV*TN*TM KB <= 64 KB.  Registers: about
+  // 4*TN*TM accumulators + 4*TN + 3*TM + 20 fixed, 9*TN + 9*TM per K block in
+  // flight, within ~200 (two waves per SIMD, NWV = 8) or ~440 (one wave).
+  constexpr int NWV = (64 / (TN * TM) >= 8) ? 8 : (64 / (TN * TM) >= 4) ? 4 : 2;
+  constexpr int FIXED = 4 * TN * TM + 4 * TN + 3 * TM + 20;
+  constexpr int PER = 9 * TN + 9 * TM;
+  constexpr int BUDGET = NWV == 8 ? 200 : 440;
+  constexpr int UF = (BUDGET - FIXED) / PER;
+  constexpr int U = UF > 8 ? 8 : UF < 1 ? 1 : UF;
+  static_assert(NWV * TN * TM <= 64, "LDS for the partial sums");
+  gemm_skinny_kernel<TM, TN, NWV, U><<<dim3(grid), dim3(64 * NWV), 0, s>>>(
+      a, a_s_km, w, w_s, out, M, N, K, m_pad16(M), base, rem);
+  return hipGetLastError();
+}
+
+template <int TM>
+hipError_t launch_skinny_tm(const uint8_t* a, const float* a_s_km, const uint8_t* w,
+                            const float* w_s, uint16_t* out, uint32_t M, uint32_t N, uint32_t K,
+                            uint32_t grid, uint32_t base, uint32_t rem, uint32_t tn, hipStream_t s) {
+  if (tn <= 2) return launch_skinny_tn<TM, 2>(a, a_s_km, w, w_s, out, M, N, K, grid, base, rem, s);
+  if (tn <= 4) return launch_skinny_tn<TM, 4>(a, a_s_km, w, w_s, out, M, N, K, grid, base, rem, s);
+  if (tn <= 6) return launch_skinny_tn<TM, 6>(a, a_s_km, w, w_s, out, M, N, K, grid, base, rem, s);
+  return launch_skinny_tn<TM, 8>(a, a_s_km, w, w_s, out, M, N, K, grid, base, rem, s);
 }
 
 }  // namespace
@@ -460,17 +523,20 @@ hipError_t launch_gemm_tiled(const uint8_t* a, const float* a_s_km, const uint8_
 
 hipError_t launch_gemm_skinny(const uint8_t* a, const float* a_s_km, const uint8_t* w,
                               const float* w_s, uint16_t* out, uint32_t M, uint32_t N, uint32_t K,
-                              hipStream_t s) {
-  const dim3 grid(N / 16), block(64 * kSkinnyWaves);
-  const uint32_t Mp = m_pad16(M);
+                              uint32_t cu_count, hipStream_t s) {
+  // one workgroup per CU, at most 128 columns each, at least 16
+  const uint32_t units = N / 4;
+  uint32_t grid = max(cu_count, (N + 127) / 128);
+  grid = max(1u, min(grid, N / 16));
+  const uint32_t base = units / grid, rem = units % grid;
+  const uint32_t tn = (4 * (base + (rem ? 1 : 0)) + 15) / 16;
   switch ((M + 15) / 16) {
-    case 1: gemm_skinny_kernel<1><<<grid, block, 0, s>>>(a, a_s_km, w, w_s, out, M, N, K, Mp); break;
-    case 2: gemm_skinny_kernel<2><<<grid, block, 0, s>>>(a, a_s_km, w, w_s, out, M, N, K, Mp); break;
-    case 3: gemm_skinny_kernel<3><<<grid, block, 0, s>>>(a, a_s_km, w, w_s, out, M, N, K, Mp); break;
-    case 4: gemm_skinny_kernel<4><<<grid, block, 0, s>>>(a, a_s_km, w, w_s, out, M, N, K, Mp); break;
+    case 1: return launch_skinny_tm<1>(a, a_s_km, w, w_s, out, M, N, K, grid, base, rem, tn, s);
+    case 2: return launch_skinny_tm<2>(a, a_s_km, w, w_s, out, M, N, K, grid, base, rem, tn, s);
+    case 3:
+    case 4: return launch_skinny_tm<4>(a, a_s_km, w, w_s, out, M, N, K, grid, base, rem, tn, s);
     default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
 }
 
 }  // namespace fp8q
