@@ -43,7 +43,7 @@ FP8_PEAK_TFLOPS = 5000.0   # MI355X dense FP8 MFMA, TFLOP/s
 # readings for a plain 1 GiB copy (the HBM-bytes summary under profiles/).
 # Valid only for the GEMM source they were taken with: reported as null once
 # gemm.hip changes (its SHA-256 prefix is recorded here).
-GEMM_TRAFFIC = {"bytes": 1.1747e9 + 46.86e6, "gemm_source_sha256": "f4c28145b510a761"}
+GEMM_TRAFFIC = {"bytes": 1.1907e+09 + 4.7061e+07, "gemm_source_sha256": "b2622b8846c608d9"}
 
 
 def gemm_traffic():

@@ -100,7 +100,7 @@ def test_gemm_validation():
     assert L.fp8q_gemm_blockscaled(g, g, g, g, g, 4, 128, 130, None) == 2   # K % 128
     assert L.fp8q_gemm_blockscaled(g, g, None, g, g, 4, 128, 128, None) == 1
     assert L.fp8q_gemm_blockscaled(g, g, g, g, BAD, 4, 128, 128, None) == 3
-    assert L.fp8q_gemm_blockscaled_ex(g, g, g, g, g, 4, 128, 128, 5, None) == 6
+    assert L.fp8q_gemm_blockscaled_ex(g, g, g, g, g, 4, 128, 128, 6, None) == 6
     assert L.fp8q_gemm_blockscaled_ex(g, g, g, g, g, 4, 128, 128, -1, None) == 6
     assert L.fp8q_gemm_blockscaled(g, g, g, g, g, 0, 128, 128, None) == 0
     assert L.fp8q_proj(g, g, g, g, g, g, None, 4, 128, 128, None) == 1
@@ -110,10 +110,11 @@ def test_gemm_validation():
 
 
 def test_gemm_select():
-    """Auto GEMM choice: skinny kernel up to 64 rows, 256x128 tiles from 2048
-    rows on, 128x128 tiles between; bad N/K -> -1 (pure host function)."""
-    for M, want in ((1, 2), (16, 2), (25, 2), (64, 2), (65, 1), (1168, 1), (2047, 1), (2048, 3),
-                    (4576, 3), (16384, 3)):
+    """Auto GEMM choice: skinny kernel up to 64 rows, the ping-pong 256x128
+    kernel from 2048 rows on, 128x128 tiles between; bad N/K -> -1 (pure host
+    function)."""
+    for M, want in ((1, 2), (16, 2), (25, 2), (64, 2), (65, 1), (1168, 1), (2047, 1), (2048, 5),
+                    (4576, 5), (16384, 5)):
         assert fp8q.fp8q_gemm_select(M, 5120, 17408) == want, M
     assert fp8q.fp8q_gemm_select(64, 100, 128) == -1
     assert fp8q.fp8q_gemm_select(64, 128, 0) == -1

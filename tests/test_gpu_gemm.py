@@ -69,7 +69,7 @@ def _kernels_for(M, N=256):
     ks = [0, 1]
     if M <= 64:
         ks.append(2)
-    return tuple(ks + [3, 4])
+    return tuple(ks + [3, 4, 5])
 
 
 @pytest.mark.parametrize("M,N,K", [(16, 256, 512), (1, 128, 128), (17, 384, 640), (33, 256, 1152),
@@ -275,7 +275,8 @@ def test_gemm_long_k_weight_scale_chunks(orc):
         _assert_tol(_gemm_gpu(orc, a, a_s, wq, ws, kern), ref, f"long-K k{kern}")
 
 
-@pytest.mark.parametrize("M,N,K", [(300, 384, 1280), (1168, 512, 2048), (4576, 256, 640)])
+@pytest.mark.parametrize("M,N,K", [(300, 384, 1280), (1168, 512, 2048), (4576, 256, 640),
+                                   (2300, 384, 256)])
 def test_tiled_kernels_bit_identical(orc, M, N, K):
     """The tiled kernels (all tile shapes) add the scaled block products in the
     same order, so their outputs agree bit for bit; the auto choice is one of
@@ -285,8 +286,8 @@ def test_tiled_kernels_bit_identical(orc, M, N, K):
     a, a_s = orc.quant_act(x)
     wq, ws = orc.quant_weight_block(rng.normal(0, 0.02, (N, K)).astype(np.float32))
     outs = {}
-    for kern in (1, 3, 4, 0):
+    for kern in (1, 3, 4, 5, 0):
         log(f"gemm M={M} N={N} K={K} kernel={kern}")
         outs[kern] = _gemm_gpu(orc, a, a_s, wq, ws, kern)
-    for kern in (3, 4, 0):
+    for kern in (3, 4, 5, 0):
         assert np.array_equal(outs[kern], outs[1]), f"kernel {kern} differs from kernel 1"

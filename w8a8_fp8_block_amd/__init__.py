@@ -206,7 +206,8 @@ def fp8q_proj_quant_fused(M: int, K: int) -> bool:
 
 
 GEMM_KERNEL_NAMES = {1: "gemm_tiled_kernel<128,128,2,2,2>", 2: "gemm_skinny_kernel",
-                     3: "gemm_tiled_kernel<256,128,4,2,3>", 4: "gemm_tiled_kernel<256,128,2,2,3>"}
+                     3: "gemm_tiled_kernel<256,128,4,2,3>", 4: "gemm_tiled_kernel<256,128,2,2,3>",
+                     5: "gemm_pp_kernel<3>"}
 
 
 def fp8q_quant_b_min_m(K: int, params: SelectParams) -> int:

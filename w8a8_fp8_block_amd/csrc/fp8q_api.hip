@@ -160,11 +160,11 @@ fp8q_status run_quant(const char* fn, const uint16_t* x, uint8_t* q, float* srm,
   return launched(fn, e);
 }
 
-// GEMM kernel choice: the skinny kernel up to this many rows (at M = 64 it
-// streams the weights in half the tiled kernel's time); from this many
-// rows on, 256 x 128 tiles with 8 waves (one workgroup per CU), which move a
-// quarter less data per MFMA than two 128 x 128 workgroups and lose little
-// to a partial last tile row (measured crossover between M = 1168 and 4576).
+// GEMM kernel choice: the skinny kernel up to kSkinnyAutoMaxM rows (at M = 64
+// it streams the weights in half the tiled kernel's time); from
+// kWideAutoMinM rows on, the ping-pong 256 x 128 kernel (one workgroup per
+// CU; 10-20% faster than the other tile shapes at M = 4576, even with
+// 128 x 128 tiles at M = 1168, slower at M = 512); 128 x 128 tiles between.
 constexpr uint32_t kSkinnyAutoMaxM = 64;
 // fp8q_proj writes the K-major scales from the quantizer itself (one launch
 // fewer) up to this many scale groups; beyond it the quantizer's scattered
@@ -174,7 +174,7 @@ constexpr uint64_t kFusedKmajorMaxGroups = 1u << 17;
 constexpr uint32_t kWideAutoMinM = 2048;
 
 int gemm_auto_kernel(uint32_t M) {
-  return (M <= kSkinnyAutoMaxM) ? 2 : (M >= kWideAutoMinM ? 3 : 1);
+  return (M <= kSkinnyAutoMaxM) ? 2 : (M >= kWideAutoMinM ? 5 : 1);
 }
 
 fp8q_status run_gemm(const char* fn, const uint8_t* a, const float* as, const uint8_t* w,
@@ -328,7 +328,7 @@ fp8q_status fp8q_gemm_blockscaled_ex(const uint8_t* a_e4m3, const float* a_scale
                                      uint16_t* out_bf16, uint32_t M, uint32_t N, uint32_t K,
                                      int kernel, hipStream_t stream) {
   const char* fn = "fp8q_gemm_blockscaled";
-  if (kernel < 0 || kernel > 4) return fail(FP8Q_ERR_VARIANT, "%s: kernel %d out of range", fn, kernel);
+  if (kernel < 0 || kernel > 5) return fail(FP8Q_ERR_VARIANT, "%s: kernel %d out of range", fn, kernel);
   fp8q_status st = check_mk(fn, M, K);
   if (st != FP8Q_OK) return st;
   st = check_n(fn, M, N, K);

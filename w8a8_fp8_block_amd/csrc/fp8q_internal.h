@@ -44,9 +44,10 @@ hipError_t launch_kmajor_pad(float* scale_km, uint32_t M, uint32_t K, hipStream_
 hipError_t launch_relayout(const float* scale_rm, float* scale_km, uint32_t M,
                            uint32_t K, hipStream_t s);
 
-// GEMM kernels: LDS-tiled MFMA (tile configuration cfg: 0/1 = default
-// 128x128 tiles, 4 waves, 2 LDS stages so that two workgroups share a CU;
-// 2 = 256x128 with 8 waves; 3 = 256x128 with 4 waves) and skinny (M <= 64).
+// GEMM kernels: LDS-tiled MFMA (tile configuration cfg: 0/1 = 128x128
+// tiles, 4 waves, 2 LDS stages so that two workgroups share a CU; 2 =
+// 256x128 with 8 waves; 3 = 256x128 with 4 waves; 4 = 256x128 with two
+// ping-pong groups of 4 waves) and skinny (M <= 64).
 constexpr uint32_t kSkinnyMaxM = 64;
 hipError_t launch_gemm_tiled(const uint8_t* a, const float* a_s_km, const uint8_t* w,
                              const float* w_s, uint16_t* out, uint32_t M, uint32_t N,

@@ -360,6 +360,240 @@ hipError_t launch_tiled_cfg(const uint8_t* a, const float* a_s_km, const uint8_t
   return hipGetLastError();
 }
 // ------------------------------------------------------------------------
+// Ping-pong kernel: 256x128 workgroup tile, 8 waves of 64x64 in two groups.
+// Group 0 (waves 0-3, tile rows 0-127) and group 1 (waves 4-7, rows
+// 128-255) put one wave on each SIMD and take turns: while one group runs
+// the MFMAs and promotions of a K block from registers, the other reads its
+// fragments of the block from LDS, so each SIMD's matrix pipe is fed by one
+// wave at a time instead of two waves that leave every barrier together and
+// compete.  Per K block kb:
+//   phase A: group 0 computes block kb; group 1 reads block kb
+//   phase B: group 1 computes block kb; group 0 reads block kb+1
+// with a workgroup barrier after each phase.  A wave holds one fragment set
+// (loaded in its read phase, consumed in its compute phase).
+//
+// Direct loads: a stage is 48 1-KB operand chunks (chunk c at LDS offset
+// c*1024: activation rows 8c..8c+7 for c < 32, weight rows 8(c-32).. after)
+// plus every wave's scales.  Each wave issues 6 chunks and its own two scale
+// loads at the end of its read phase, so the compute phases hold nothing but
+// MFMAs and promotions and the texture unit gets 24 KB per phase.  Stage s
+// (block min(s, G-1): stages past the last block reload it, in bounds and
+// never read) goes to slot s % STAGES.  Before the phase-A barrier of block
+// kb each wave waits for its own part of stage kb+1.
+// ------------------------------------------------------------------------
+template <int STAGES>
+struct PpCfg {
+  static constexpr int BM = 256, BN = 128, NW = 8, NT = 512;
+  static constexpr int WM = 64, WN = 64, TM = 4, TN = 4, NP = 16;
+  static constexpr int A_BYTES = BM * 128, W_BYTES = BN * 128;
+  static constexpr int SCW_BYTES = 512;  // per wave: 64 activation scales + 64 weight-scale copies
+  static constexpr int STAGE_BYTES = A_BYTES + W_BYTES + NW * SCW_BYTES;
+  static constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
+  static constexpr int CHUNKS = (A_BYTES + W_BYTES) / 1024;  // 48
+  static constexpr int CW = CHUNKS / NW;                      // 6 operand chunks per wave
+  static constexpr int LW = CW + 2;                           // + own scales: loads per wave and stage
+  static_assert(CHUNKS % NW == 0 && 2 * LW < 64, "vmcnt range");
+  static_assert(LDS_BYTES <= 160 * 1024 && STAGES == 3, "config");
+};
+
+template <int STAGES>
+__global__ __launch_bounds__(512) void gemm_pp_kernel(
+    const uint8_t* __restrict__ A, const float* __restrict__ As, const uint8_t* __restrict__ W,
+    const float* __restrict__ Ws, uint16_t* __restrict__ out, uint32_t M, uint32_t N, uint32_t K,
+    uint32_t Mp, uint32_t tiles_m, uint32_t tiles_n) {
+  using C = PpCfg<STAGES>;
+  constexpr int TM = C::TM, TN = C::TN, NP = C::NP, BM = C::BM, BN = C::BN, CW = C::CW, LW = C::LW;
+  extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
+
+  const uint32_t tid = threadIdx.x, lane = tid & 63;
+  const uint32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const uint32_t grp = wave >> 2, gw = wave & 3;
+  const uint32_t wm = 2 * grp + (gw >> 1), wn = gw & 1;
+
+  // ---- tile of this workgroup: XCD-aware, grouped order ----
+  const uint32_t ntiles = tiles_m * tiles_n;
+  const uint32_t bid = blockIdx.x, xcd = bid & 7, slot = bid >> 3;
+  const uint32_t q = ntiles >> 3, r8 = ntiles & 7;
+  const uint32_t t = (xcd < r8) ? xcd * (q + 1) + slot : r8 * (q + 1) + (xcd - r8) * q + slot;
+  constexpr uint32_t GROUP_M = 8;
+  const uint32_t per_group = GROUP_M * tiles_n;
+  const uint32_t group = t / per_group, first_m = group * GROUP_M;
+  const uint32_t gm = min(tiles_m - first_m, GROUP_M);
+  const uint32_t tmi = first_m + (t % per_group) % gm, tni = (t % per_group) / gm;
+  const uint32_t m0 = tmi * BM, n0 = tni * BN;
+  const uint32_t G = K / kGroup;
+  const uint32_t nb = n0 / kGroup;
+
+  const __amdgpu_buffer_rsrc_t rA = make_rsrc(A, M * K);
+  const __amdgpu_buffer_rsrc_t rW = make_rsrc(W, N * K);
+  const __amdgpu_buffer_rsrc_t rS = make_rsrc(As, G * Mp * 4);
+  const __amdgpu_buffer_rsrc_t rWs = make_rsrc(Ws, (N / kGroup) * G * 4);
+  // this wave's operand chunks wave*CW + j: source resource and per-lane offset
+  uint32_t c_off[CW];
+  bool c_act[CW];
+#pragma unroll
+  for (int j = 0; j < CW; ++j) {
+    const uint32_t c = wave * CW + j;
+    const uint32_t ch = (c < (uint32_t)C::A_BYTES / 1024) ? c : c - C::A_BYTES / 1024;
+    const uint32_t e = ch * 64 + lane, row = e >> 3;  // row within the operand tile
+    c_act[j] = c < (uint32_t)C::A_BYTES / 1024;
+    c_off[j] = c_act[j] ? min(m0 + row, M - 1) * K + ((e & 7) ^ swz(row)) * 16
+                        : (n0 + row) * K + ((e & 7) ^ swz(row)) * 16;
+  }
+  const uint32_t s_off = min(m0 + wm * C::WM + lane, Mp - 1) * 4;  // own activation scales
+  const uint32_t ws_off = nb * G * 4;
+  const uint32_t my_sc = C::A_BYTES + C::W_BYTES + wave * C::SCW_BYTES;
+
+  // direct load number J (0 .. LW-1) of this wave for block kb into slot `stage`
+  auto issue_one = [&](auto jc, uint32_t kb, uint32_t stage) {
+    constexpr int J = decltype(jc)::value;
+    uint8_t* base = smem + stage * C::STAGE_BYTES;
+    if constexpr (J < CW) {
+      dma16(c_act[J] ? rA : rW, c_off[J], kb * kGroup, base + (wave * CW + J) * 1024);
+    } else if constexpr (J == CW) {
+      dma4(rS, s_off, kb * Mp * 4, base + my_sc);
+    } else {
+      dma4(rWs, ws_off, kb * 4, base + my_sc + 256);
+    }
+  };
+  auto issue_stage = [&](uint32_t kb, uint32_t stage) {
+    unroll_seq([&](auto jc) { issue_one(jc, kb, stage); }, std::make_integer_sequence<int, LW>{});
+  };
+
+  const uint32_t l16 = lane & 15, c0 = 2 * (lane >> 4);
+  const uint32_t lo0 = l16 * 128 + ((c0 ^ swz(l16)) * 16);
+  const uint32_t lo1 = l16 * 128 + (((c0 + 1) ^ swz(l16)) * 16);
+  auto ld16 = [](const uint8_t* p) -> v4i { return *reinterpret_cast<const v4i*>(p); };
+  auto ldf = [](const uint8_t* p) -> float { return *reinterpret_cast<const float*>(p); };
+  auto slot_base = [&](uint32_t kb) -> const uint8_t* {
+    return smem + (kb % STAGES) * C::STAGE_BYTES;
+  };
+  const uint32_t a_row0 = wm * C::WM * 128, w_row0 = C::A_BYTES + wn * C::WN * 128;
+
+  v4f acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+  v8i af[TM], bf[TN];
+  float as[TM], ws = 0.0f, sc[TM], sc_tail = 0.0f;
+  v4f p[4];
+  p[(NP - 2) & 3] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+  p[(NP - 1) & 3] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+
+  // read this wave's fragments and scales of block kb (18 LDS reads)
+  auto read_block = [&](uint32_t kb) {
+    const uint8_t* sb = slot_base(kb);
+#pragma unroll
+    for (int tn = 0; tn < TN; ++tn) {
+      bf[tn].lo = ld16(sb + w_row0 + tn * 2048 + lo0);
+      bf[tn].hi = ld16(sb + w_row0 + tn * 2048 + lo1);
+    }
+#pragma unroll
+    for (int tm = 0; tm < TM; ++tm) {
+      af[tm].lo = ld16(sb + a_row0 + tm * 2048 + lo0);
+      af[tm].hi = ld16(sb + a_row0 + tm * 2048 + lo1);
+      as[tm] = ldf(sb + my_sc + (tm * 16 + l16) * 4);
+    }
+    ws = ldf(sb + my_sc + 256);
+  };
+  // MFMAs and promotions of the block in registers; the promotions of its
+  // last two MFMAs are left pending for the next block's compute phase.
+  auto compute_block = [&]() {
+#pragma unroll
+    for (int tm = 0; tm < TM; ++tm) sc[tm] = as[tm] * ws;
+    unroll_seq(
+        [&](auto ic) {
+          constexpr int I = decltype(ic)::value;
+          constexpr int tm = I / TN, tn = I % TN;
+          p[I & 3] = mfma_e4m3_128(bf[tn], af[tm]);
+          if constexpr (I < 2) {
+            constexpr int J = NP - 2 + I;
+            acc[J / TN][J % TN] += p[J & 3] * sc_tail;
+          } else {
+            constexpr int J = I - 2;
+            acc[J / TN][J % TN] += p[J & 3] * sc[J / TN];
+          }
+          sched_fence();
+        },
+        std::make_integer_sequence<int, NP>{});
+    sc_tail = sc[TM - 1];
+  };
+
+  // Each group runs its own loop (one straight-line body each, so no value
+  // is live across a merge of the two roles); both execute the same
+  // sequence of workgroup barriers.  Every wave issues its part of stages
+  // 0 .. STAGES-1 up front and its part of stage kb+STAGES in its read phase
+  // of the iteration in which the slot of block kb has been read by both
+  // groups (group 1: after its own reads of block kb in phase A; group 0:
+  // in phase B, after its reads of block kb+1).
+#pragma unroll
+  for (int s = 0; s < STAGES; ++s) issue_stage(min((uint32_t)s, G - 1), s);
+  if (grp == 0) {
+    wait_vmcnt<(STAGES - 1) * LW>();  // own part of stage 0
+    wg_barrier();
+    read_block(0);
+    wait_lgkm0();
+    wg_barrier();
+    for (uint32_t kb = 0; kb < G; ++kb) {
+      compute_block();   // phase A
+      wait_vmcnt<LW>();  // own part of stage kb+1 (that of kb+2 may be in flight)
+      wg_barrier();
+      read_block(kb + 1);  // phase B (block G: a reloaded copy of the last block, unused)
+      wait_lgkm0();
+      issue_stage(min(kb + STAGES, G - 1), kb % STAGES);
+      wg_barrier();
+    }
+  } else {
+    wait_vmcnt<(STAGES - 1) * LW>();  // own part of stage 0
+    wg_barrier();
+    wg_barrier();
+    for (uint32_t kb = 0; kb < G; ++kb) {
+      read_block(kb);  // phase A
+      wait_lgkm0();
+      issue_stage(min(kb + STAGES, G - 1), kb % STAGES);
+      wait_vmcnt<2 * LW>();  // own part of stage kb+1 (kb+2, kb+3 may be in flight)
+      wg_barrier();
+      compute_block();  // phase B
+      wg_barrier();
+    }
+  }
+  wait_vmcnt<0>();  // no direct load may still be writing LDS at exit
+  acc[(NP - 2) / TN][(NP - 2) % TN] += p[(NP - 2) & 3] * sc_tail;
+  acc[(NP - 1) / TN][(NP - 1) % TN] += p[(NP - 1) & 3] * sc_tail;
+
+#pragma unroll
+  for (int tm = 0; tm < TM; ++tm) {
+    const uint32_t m = m0 + wm * C::WM + tm * 16 + l16;
+    if (m < M) {
+#pragma unroll
+      for (int tn = 0; tn < TN; ++tn) {
+        const uint32_t n = n0 + wn * C::WN + tn * 16 + 4 * (lane >> 4);
+        *reinterpret_cast<uint2*>(out + (uint64_t)m * N + n) = pack_bf16x4(acc[tm][tn]);
+      }
+    }
+  }
+}
+
+template <int STAGES>
+hipError_t launch_pp_cfg(const uint8_t* a, const float* a_s_km, const uint8_t* w, const float* w_s,
+                         uint16_t* out, uint32_t M, uint32_t N, uint32_t K, hipStream_t s) {
+  using C = PpCfg<STAGES>;
+  if (N % C::BN != 0) return hipErrorInvalidValue;
+  static bool attr_set = false;  // idempotent; racing threads set the same value
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_pp_kernel<STAGES>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  const uint32_t tiles_m = (M + C::BM - 1) / C::BM, tiles_n = N / C::BN;
+  gemm_pp_kernel<STAGES><<<dim3(tiles_m * tiles_n), dim3(C::NT), C::LDS_BYTES, s>>>(
+      a, a_s_km, w, w_s, out, M, N, K, m_pad16(M), tiles_m, tiles_n);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------------
 // Skinny kernel for decode widths (M <= 16*TM <= 64).  The projection is then
 // bound by streaming the weight matrix once, and the weight bytes must be
 // spread evenly over the CUs: with one workgroup per 16 output columns
@@ -517,6 +751,7 @@ hipError_t launch_gemm_tiled(const uint8_t* a, const float* a_s_km, const uint8_
     case 1: return launch_tiled_cfg<128, 128, 2, 2, 2>(a, a_s_km, w, w_s, out, M, N, K, s);
     case 2: return launch_tiled_cfg<256, 128, 4, 2, 3>(a, a_s_km, w, w_s, out, M, N, K, s);
     case 3: return launch_tiled_cfg<256, 128, 2, 2, 3>(a, a_s_km, w, w_s, out, M, N, K, s);
+    case 4: return launch_pp_cfg<3>(a, a_s_km, w, w_s, out, M, N, K, s);
     default: return hipErrorInvalidValue;
   }
 }
