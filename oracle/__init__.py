@@ -9,7 +9,9 @@ Every function takes and returns numpy arrays:
 * ``quant_act(x_bf16[M,K] uint16) -> (codes[M,K] uint8, scale[M,K/128] f32)``
 * ``scale_to_kmajor(scale_rm[M,G] f32) -> km[G, ceil16(M)] f32``
 * ``quant_weight_block(w[N,K] f32) -> (codes[N,K] uint8, scale[N/128,K/128] f32)``
-* ``gemm_ref(a, a_s_rm, w, w_s) -> out[M,N] f64``
+* ``quant_weight_row(w[N,K] f32) -> (codes[N,K] uint8, scale[N] f32)``
+* ``dequant_fp8_bf16(codes[N,K], scale) -> bf16 bits[N,K] uint16`` (either weight format)
+* ``gemm_ref(a, a_s_rm, w, w_s) -> out[M,N] f64`` (w_s block-scaled 2-D or per-row 1-D)
 * ``gemm_ref_at(a, a_s_rm, w, w_s, ms, ns) -> out[len] f64``
 * ``e4m3_decode(codes) -> f64``, ``e4m3_encode(f32) -> uint8``
 
@@ -74,6 +76,14 @@ def _load():
     lib.oracle_gemm_ref.restype = None
     lib.oracle_gemm_ref_at.argtypes = [P, P, P, P, P, P, P, I, I]
     lib.oracle_gemm_ref_at.restype = None
+    lib.oracle_quant_weight_row.argtypes = [P, P, P, I, I]
+    lib.oracle_quant_weight_row.restype = None
+    lib.oracle_dequant_fp8_bf16.argtypes = [P, P, P, I, I, I, I, I]
+    lib.oracle_dequant_fp8_bf16.restype = None
+    lib.oracle_gemm_ref_geom.argtypes = [P, P, P, P, P, I, I, I, I, I, I]
+    lib.oracle_gemm_ref_geom.restype = None
+    lib.oracle_gemm_ref_at_geom.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I]
+    lib.oracle_gemm_ref_at_geom.restype = None
     lib.oracle_num_threads.argtypes = []
     lib.oracle_num_threads.restype = ctypes.c_int
     _lib = lib
@@ -143,7 +153,40 @@ def quant_weight_block(w: np.ndarray):
     return q, s
 
 
+def quant_weight_row(w: np.ndarray):
+    """Per-row FP8 weights: codes [N,K] and scale[n] = row amax / 448."""
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    N, K = w.shape
+    q = np.empty((N, K), dtype=np.uint8)
+    s = np.empty((N,), dtype=np.float32)
+    _load().oracle_quant_weight_row(_p(w), _p(q), _p(s), N, K)
+    return q, s
+
+
+def weight_geometry(N: int, K: int, w_s: np.ndarray):
+    """(block_n, block_k, sk) of the pages' weight-scale index
+    scale[(n/block_n)*sk + k/block_k]: a 2-D [ceil(N/128), K/128] array is the
+    128x128 block-scaled format, a 1-D [N] array the per-row format."""
+    if w_s.ndim == 1:
+        assert w_s.shape == (N,)
+        return 1, K, 1
+    assert w_s.shape == ((N + GROUP - 1) // GROUP, K // GROUP), w_s.shape
+    return GROUP, GROUP, K // GROUP
+
+
+def dequant_fp8_bf16(w: np.ndarray, w_s: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns [N,K] of fl32(dec(w) * scale), either weight format."""
+    w = np.ascontiguousarray(w, dtype=np.uint8)
+    w_s = np.ascontiguousarray(w_s, dtype=np.float32)
+    N, K = w.shape
+    bn, bk, sk = weight_geometry(N, K, w_s)
+    out = np.empty((N, K), dtype=np.uint16)
+    _load().oracle_dequant_fp8_bf16(_p(w), _p(w_s), _p(out), N, K, bn, bk, sk)
+    return out
+
+
 def gemm_ref(a, a_s_rm, w, w_s) -> np.ndarray:
+    """fp64 block-form product; w_s block-scaled [N/128, K/128] or per-row [N]."""
     a = np.ascontiguousarray(a, dtype=np.uint8)
     w = np.ascontiguousarray(w, dtype=np.uint8)
     a_s = np.ascontiguousarray(a_s_rm, dtype=np.float32)
@@ -151,9 +194,10 @@ def gemm_ref(a, a_s_rm, w, w_s) -> np.ndarray:
     M, K = a.shape
     N = w.shape[0]
     assert w.shape[1] == K and a_s.shape == (M, K // GROUP)
-    assert w_s.shape == (N // GROUP, K // GROUP)
+    assert w_s.ndim == 1 or N % GROUP == 0
+    bn, bk, sk = weight_geometry(N, K, w_s)
     out = np.empty((M, N), dtype=np.float64)
-    _load().oracle_gemm_ref(_p(a), _p(a_s), _p(w), _p(w_s), _p(out), M, N, K)
+    _load().oracle_gemm_ref_geom(_p(a), _p(a_s), _p(w), _p(w_s), _p(out), M, N, K, bn, bk, sk)
     return out
 
 
@@ -168,10 +212,11 @@ def gemm_ref_at(a, a_s_rm, w, w_s, ms, ns) -> np.ndarray:
     N = w.shape[0]
     assert ms.shape == ns.shape
     assert (ms >= 0).all() and (ms < M).all() and (ns >= 0).all() and (ns < N).all()
-    assert a_s.shape == (M, K // GROUP) and w_s.shape == (N // GROUP, K // GROUP)
+    assert a_s.shape == (M, K // GROUP)
+    bn, bk, sk = weight_geometry(N, K, w_s)
     out = np.empty(ms.shape, dtype=np.float64)
-    _load().oracle_gemm_ref_at(_p(a), _p(a_s), _p(w), _p(w_s), _p(ms), _p(ns),
-                               _p(out), ms.size, K)
+    _load().oracle_gemm_ref_at_geom(_p(a), _p(a_s), _p(w), _p(w_s), _p(ms), _p(ns),
+                                    _p(out), ms.size, K, bn, bk, sk)
     return out
 
 

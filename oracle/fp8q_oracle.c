@@ -25,6 +25,12 @@
  *               cublas_fp8_proj: both operands 128-block-scaled; weight scale
  *               index (n/128)*(K/128) + k/128 from dequant_fp8_bf16_into).
  *               Computed in fp64 and not rounded.
+ *   per-row     the pages' other FP8 weight format: one fp32 scale per
+ *               weight row.  Both formats address their scales with one
+ *               formula, scale[(n/block_n)*sk + k/block_k], block-scaled
+ *               (128, 128, K/128) or per-row (1, K, 1) (dispatch_proj.rs, doc
+ *               of dequant_fp8_bf16_into); the GEMM and the FP8 -> bf16
+ *               dequantizer below take that geometry.
  *
  * Readings where the pages are silent (each one is listed in the design
  * notes): amax == 0 gives scale 0 and signed-zero codes; the scale is the
@@ -186,15 +192,66 @@ void oracle_quant_weight_block(const float *w, uint8_t *q, float *scale,
   }
 }
 
+/* fp32 W[N,K] -> codes [N,K] and one fp32 scale per row, scale[n] = row
+ * amax / 448 (the per-row format; same element encoder).  Synthetic weights
+ * only. */
+void oracle_quant_weight_row(const float *w, uint8_t *q, float *scale, int64_t N,
+                             int64_t K) {
+  int64_t n;
+#pragma omp parallel for schedule(static)
+  for (n = 0; n < N; ++n) {
+    float amax = 0.0f, s;
+    int64_t k;
+    for (k = 0; k < K; ++k) {
+      const float v = fabsf(w[n * K + k]);
+      if (v > amax) amax = v;
+    }
+    s = amax / 448.0f;
+    scale[n] = s;
+    for (k = 0; k < K; ++k) q[n * K + k] = quant_elem(w[n * K + k], s);
+  }
+}
+
+/* -------------------------------------------------- FP8 -> bf16 weights */
+
+/* fp32 -> bf16 bit pattern, round to nearest even (finite input). */
+static uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u;
+  memcpy(&u, &f, 4);
+  return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+
+/* dst[n,k] = bf16(fl32(dec(w[n,k]) * scale[(n/block_n)*sk + k/block_k]))
+ * (dispatch_proj.rs, dequant_fp8_bf16_into: the scale index formula and
+ * the two geometries).  The decoded value times the fp32 scale is formed
+ * exactly in fp64 (at most 4 + 24 significant bits), rounded once to fp32 and
+ * then once to bf16. */
+void oracle_dequant_fp8_bf16(const uint8_t *w, const float *scale, uint16_t *dst,
+                             int64_t N, int64_t K, int64_t block_n, int64_t block_k,
+                             int64_t sk) {
+  int64_t n;
+#pragma omp parallel for schedule(static)
+  for (n = 0; n < N; ++n) {
+    int64_t k;
+    for (k = 0; k < K; ++k) {
+      const double s = (double)scale[(n / block_n) * sk + k / block_k];
+      const float prod = (float)(oracle_e4m3_decode(w[n * K + k]) * s);
+      dst[n * K + k] = f32_to_bf16_rne(prod);
+    }
+  }
+}
+
 /* ------------------------------------------------------------------ GEMM */
 
 /* One output element in block form:
- *   ref[m,n] = sum_g a_s[m,g] * w_s[n/128,g] * S(m,n,g),
+ *   ref[m,n] = sum_g a_s[m,g] * w_s[(n/block_n)*sk + 128g/block_k] * S(m,n,g),
  *   S(m,n,g) = sum_j dec(a[m,128g+j]) * dec(w[n,128g+j])   (exact in fp64).
- * a_s is the row-major [M, K/128] activation scale. */
+ * a_s is the row-major [M, K/128] activation scale; the weight geometry is
+ * (128, 128, K/128) for 128x128 block scales and (1, K, 1) per row. */
 static double gemm_elem(const uint8_t *a, const float *a_s, const uint8_t *w,
                         const float *w_s, const double *dec, int64_t m,
-                        int64_t n, int64_t K) {
+                        int64_t n, int64_t K, int64_t block_n, int64_t block_k,
+                        int64_t sk) {
   const int64_t G = K / GROUP;
   double acc = 0.0;
   int64_t g;
@@ -204,7 +261,7 @@ static double gemm_elem(const uint8_t *a, const float *a_s, const uint8_t *w,
     double S = 0.0;
     int j;
     for (j = 0; j < GROUP; ++j) S += dec[ar[j]] * dec[wr[j]];
-    acc += (double)a_s[m * G + g] * (double)w_s[(n / GROUP) * G + g] * S;
+    acc += (double)a_s[m * G + g] * (double)w_s[(n / block_n) * sk + (g * GROUP) / block_k] * S;
   }
   return acc;
 }
@@ -214,28 +271,41 @@ static void decode_table(double dec[256]) {
   for (c = 0; c < 256; ++c) dec[c] = oracle_e4m3_decode((uint8_t)c);
 }
 
-/* Full reference out[M,N] (fp64). */
-void oracle_gemm_ref(const uint8_t *a, const float *a_s, const uint8_t *w,
-                     const float *w_s, double *out, int64_t M, int64_t N,
-                     int64_t K) {
+/* Full reference out[M,N] (fp64), weight-scale geometry as for gemm_elem. */
+void oracle_gemm_ref_geom(const uint8_t *a, const float *a_s, const uint8_t *w,
+                          const float *w_s, double *out, int64_t M, int64_t N,
+                          int64_t K, int64_t block_n, int64_t block_k, int64_t sk) {
   double dec[256];
   int64_t r;
   decode_table(dec);
 #pragma omp parallel for schedule(dynamic, 16)
   for (r = 0; r < M * N; ++r)
-    out[r] = gemm_elem(a, a_s, w, w_s, dec, r / N, r % N, K);
+    out[r] = gemm_elem(a, a_s, w, w_s, dec, r / N, r % N, K, block_n, block_k, sk);
 }
 
 /* Reference at selected (m, n) pairs only: out[i] = ref[ms[i], ns[i]]. */
-void oracle_gemm_ref_at(const uint8_t *a, const float *a_s, const uint8_t *w,
-                        const float *w_s, const int64_t *ms, const int64_t *ns,
-                        double *out, int64_t count, int64_t K) {
+void oracle_gemm_ref_at_geom(const uint8_t *a, const float *a_s, const uint8_t *w,
+                             const float *w_s, const int64_t *ms, const int64_t *ns,
+                             double *out, int64_t count, int64_t K, int64_t block_n,
+                             int64_t block_k, int64_t sk) {
   double dec[256];
   int64_t i;
   decode_table(dec);
 #pragma omp parallel for schedule(dynamic, 16)
   for (i = 0; i < count; ++i)
-    out[i] = gemm_elem(a, a_s, w, w_s, dec, ms[i], ns[i], K);
+    out[i] = gemm_elem(a, a_s, w, w_s, dec, ms[i], ns[i], K, block_n, block_k, sk);
+}
+
+/* The 128x128 block-scaled forms. */
+void oracle_gemm_ref(const uint8_t *a, const float *a_s, const uint8_t *w,
+                     const float *w_s, double *out, int64_t M, int64_t N,
+                     int64_t K) {
+  oracle_gemm_ref_geom(a, a_s, w, w_s, out, M, N, K, GROUP, GROUP, K / GROUP);
+}
+void oracle_gemm_ref_at(const uint8_t *a, const float *a_s, const uint8_t *w,
+                        const float *w_s, const int64_t *ms, const int64_t *ns,
+                        double *out, int64_t count, int64_t K) {
+  oracle_gemm_ref_at_geom(a, a_s, w, w_s, ms, ns, out, count, K, GROUP, GROUP, K / GROUP);
 }
 
 /* Number of OpenMP threads a parallel region here would use. */
