@@ -64,6 +64,11 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="approximate CPU time budget of the oracle sample")
+    p.add_argument("--weights", default="block", choices=["block", "row"],
+                   help="FP8 weight scales: one per 128x128 block (default) or one per row")
+    p.add_argument("--dequant", action="store_true",
+                   help="instead of the benchmark, time the FP8 -> bf16 weight dequantizer on "
+                        "the prefill and large-prefill weights, both scale formats")
     p.add_argument("--quant-sweep", action="store_true",
                    help="instead of the benchmark, time quantizer variants A, B and the "
                         "selector's choice over the token/K sweep (one JSON line per shape)")
@@ -132,11 +137,52 @@ def quant_sweep(reps=25):
                 "rule_ok": times["auto"] <= 1.03 * best + 0.1}), flush=True)
 
 
-def quantize_weights_gpu(wf):
-    """Synthetic FP8 weights: per 128x128 block, scale = amax/448, codes by
-    PyTorch's float8_e4m3fn cast (input preparation, outside the timed path)."""
+def dequant_bench(reps=20):
+    """FP8 -> bf16 weight expansion (HBM-bound: 1 byte read, 2 written per
+    element) on the prefill (N=17408, K=5120) and large-prefill (N=5120,
+    K=17408) weights, block-scaled and per-row, two weight copies alternated
+    so successive launches do not hit the cache."""
+    import torch
+    import synth
+    import w8a8_fp8_block_amd as fp8q
+    dev = torch.device("cuda:0")
+    for name in ("prefill", "large_prefill"):
+        w = synth.WORKLOADS[name][0]
+        _, wf, _ = synth.make_inputs(w, M=1)
+        wf = torch.from_numpy(wf).to(dev)
+        for per_row in (False, True):
+            codes, sc = quantize_weights_gpu(wf, per_row)
+            copies = [(codes, sc), (codes.clone(), sc.clone())]
+            dst = torch.empty((w.N, w.K), dtype=torch.bfloat16, device=dev)
+            for c, s_ in copies:
+                fp8q.fp8q_dequant_fp8_bf16(c, s_, dst, per_row)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for i in range(reps):
+                c, s_ = copies[i % 2]
+                fp8q.fp8q_dequant_fp8_bf16(c, s_, dst, per_row)
+            e1.record()
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / reps
+            nbytes = 3 * w.N * w.K + 4 * sc.numel()
+            print(json.dumps({"dequant": f"{name} N={w.N} K={w.K}",
+                              "scales": "per-row" if per_row else "128x128 blocks",
+                              "us": round(us, 2), "GB/s": round(nbytes / us / 1e3, 1),
+                              "frac_hbm": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4)}), flush=True)
+
+
+def quantize_weights_gpu(wf, per_row=False):
+    """Synthetic FP8 weights: per 128x128 block (or per row), scale = amax/448,
+    codes by PyTorch's float8_e4m3fn cast (input preparation, outside the timed
+    path)."""
     import torch
     N, K = wf.shape
+    if per_row:
+        ws = (wf.abs().amax(dim=1) / 448.0).to(torch.float32)
+        safe = torch.where(ws > 0, ws, torch.ones_like(ws))
+        q = (wf / safe[:, None]).clamp(-448, 448)
+        return q.to(torch.float8_e4m3fn).view(torch.uint8).contiguous(), ws.contiguous()
     blocks = wf.view(N // 128, 128, K // 128, 128)
     amax = blocks.abs().amax(dim=(1, 3))
     ws = (amax / 448.0).to(torch.float32)
@@ -146,11 +192,12 @@ def quantize_weights_gpu(wf):
     return codes, ws.contiguous()
 
 
-def cpu_baseline(w, x_bits, wf, budget_s):
+def cpu_baseline(w, x_bits, wf, budget_s, per_row=False):
     """Time the oracle (quantizer + relayout + fp64 GEMM) on the first R rows."""
     import oracle
     oracle._load()
-    wq, ws = oracle.quant_weight_block(wf)          # input preparation, not timed
+    # input preparation, not timed
+    wq, ws = oracle.quant_weight_row(wf) if per_row else oracle.quant_weight_block(wf)
     threads = oracle.num_threads()
     # calibrate on 2 rows, then size the sample to the budget
     def run(R):
@@ -189,6 +236,9 @@ def main():
     if args.quant_sweep:
         quant_sweep()
         return
+    if args.dequant:
+        dequant_bench()
+        return
 
     import torch
     import synth
@@ -207,7 +257,9 @@ def main():
     print(f"[bench] inputs {w.desc} (seed {w.seed})", file=sys.stderr, flush=True)
     x_bits, wf, _ = synth.make_inputs(w)
     x = torch.from_numpy(x_bits.view(np.int16)).to(dev)
-    wq, ws = quantize_weights_gpu(torch.from_numpy(wf).to(dev))
+    per_row = args.weights == "row"
+    wq, ws = quantize_weights_gpu(torch.from_numpy(wf).to(dev), per_row)
+    gemm = fp8q.fp8q_gemm_rowscaled if per_row else fp8q.fp8q_gemm_blockscaled
     act_q, act_s, act_km = fp8q.alloc_proj_scratch(M, K)
     out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
     stream = torch.cuda.current_stream()
@@ -225,7 +277,7 @@ def main():
         if not fused:
             fp8q.fp8q_scale_to_kmajor(act_s, act_km)
         if ev_g: ev_g[0].record(stream)
-        fp8q.fp8q_gemm_blockscaled(act_q, act_km, wq, ws, out)
+        gemm(act_q, act_km, wq, ws, out)
         if ev_g: ev_g[1].record(stream)
 
     print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
@@ -263,7 +315,7 @@ def main():
     b0, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     b0.record(stream)
     for i in range(R):
-        fp8q.fp8q_gemm_blockscaled(act_q, act_km, w_alt[i % len(w_alt)], ws, out)
+        gemm(act_q, act_km, w_alt[i % len(w_alt)], ws, out)
     b1.record(stream)
     torch.cuda.synchronize()
     gemm_b2b_us = b0.elapsed_time(b1) * 1e3 / R
@@ -303,7 +355,8 @@ def main():
         roofline = {"bound": "mfma", "kernel": fp8q.GEMM_KERNEL_NAMES[kern],
                     "achieved": round(gemm_tflops, 2), "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
                     "frac": round(gemm_tflops / FP8_PEAK_TFLOPS, 4),
-                    "traffic": gemm_traffic() if args.workload == "large_prefill" else None,
+                    "traffic": (gemm_traffic() if args.workload == "large_prefill" and not per_row
+                                else None),
                     "avg_launch_us": round(gemm_avg_s * 1e6, 2),
                     "back_to_back_us": round(gemm_b2b_us, 2),
                     "back_to_back_achieved": round(flops / gemm_b2b_us / 1e6, 2),
@@ -312,7 +365,7 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
-        cpu = cpu_baseline(w, x_bits, wf, args.cpu_seconds)
+        cpu = cpu_baseline(w, x_bits, wf, args.cpu_seconds, per_row)
 
     rec = {
         "metric": "block-scaled FP8 proj TFLOP/s (M=4576) + act-quant GB/s vs HBM peak",
@@ -331,10 +384,12 @@ def main():
             "workload": f"{w.name} M={M} K={K} N={N}",
             "M": M, "K": K, "N": N,
             "activations": f"bf16 {w.dist}(0,1), {w.n_outliers} outlier channels x{w.outlier_factor:g}",
-            "weights": "fp8 e4m3 [N,K], fp32 scale per 128x128 block (from N(0,0.02))",
+            "weights": ("fp8 e4m3 [N,K], fp32 scale per row (from N(0,0.02))" if per_row else
+                        "fp8 e4m3 [N,K], fp32 scale per 128x128 block (from N(0,0.02))"),
             "output": "bf16 [M,N]",
-            "step": ("act-quant writing both scale layouts + block-scaled FP8 GEMM" if fused else
-                     "act-quant + scale relayout + block-scaled FP8 GEMM"),
+            "step": (("act-quant writing both scale layouts" if fused else
+                      "act-quant + scale relayout") +
+                     (" + per-row-scaled FP8 GEMM" if per_row else " + block-scaled FP8 GEMM")),
             "quant_variant": "B" if variant == 2 else "A",
             "device": props.name, "gcn_arch": props.gcnArchName,
             "cus": props.multi_processor_count,

@@ -214,6 +214,43 @@ fp8q_status fp8q_gemm_blockscaled_ex(const uint8_t *a_e4m3, const float *a_scale
                                      uint16_t *out_bf16, uint32_t M, uint32_t N,
                                      uint32_t K, int kernel, hipStream_t stream);
 
+/* Per-row FP8 weights (the pages' other weight format, dispatch_proj.rs,
+ * dequant_fp8_bf16_into: WeightQuantFormat::Fp8PerRow; the scale index
+ * formula scale[(n/block_n)*sk + k/block_k] with block_n = 1, block_k = K,
+ * sk = 1 gives one multiplier per weight row):
+ *
+ *   out[m,n] = bf16_rne( w_scale_row[n] * sum_kb a_scale_km[kb*Mp + m]
+ *                               * sum_{j<128} dec(a[m,128kb+j]) * dec(w[n,128kb+j]) )
+ *
+ *   w_scale_row  [N] fp32, one scale per weight row (= output column), applied
+ *                to the fp32 accumulator before the bf16 rounding
+ *   all other arguments, conventions, kernels and errors as for
+ *   fp8q_gemm_blockscaled / fp8q_gemm_blockscaled_ex (same kernel ids and
+ *   automatic choice). */
+fp8q_status fp8q_gemm_rowscaled(const uint8_t *a_e4m3, const float *a_scale_km,
+                                const uint8_t *w_e4m3, const float *w_scale_row,
+                                uint16_t *out_bf16, uint32_t M, uint32_t N,
+                                uint32_t K, hipStream_t stream);
+fp8q_status fp8q_gemm_rowscaled_ex(const uint8_t *a_e4m3, const float *a_scale_km,
+                                   const uint8_t *w_e4m3, const float *w_scale_row,
+                                   uint16_t *out_bf16, uint32_t M, uint32_t N,
+                                   uint32_t K, int kernel, hipStream_t stream);
+
+/* FP8 weights -> bf16 into a caller-owned buffer (dispatch_proj.rs,
+ * dequant_fp8_bf16_into):
+ *   dst_bf16[n,k] = bf16_rne( fl32( dec(w_e4m3[n,k]) * scale[i] ) ),
+ *   i = (n/128)*(K/128) + k/128   (per_row = 0: 128x128 block scales,
+ *                                  scale [ceil(N/128), K/128], K % 128 == 0)
+ *   i = n                         (per_row = 1: one scale per row, scale [N],
+ *                                  K % 16 == 0)
+ * Any N.  The e4m3 value itself is exact in bf16, so with power-of-two
+ * scales the expansion is lossless.  Codes 0x7F/0xFF (NaN) give unspecified
+ * output.  Errors: FP8Q_ERR_SHAPE (K), FP8Q_ERR_VARIANT (per_row not 0/1),
+ * FP8Q_ERR_NULL / FP8Q_ERR_ALIGN, FP8Q_ERR_DEVICE, FP8Q_ERR_LAUNCH. */
+fp8q_status fp8q_dequant_fp8_bf16(const uint8_t *w_e4m3, const float *scale,
+                                  uint16_t *dst_bf16, uint32_t N, uint32_t K,
+                                  int per_row, hipStream_t stream);
+
 /* ----------------------------------------------------------- projection */
 
 /* 1 if fp8q_proj quantizes with the fused kernel that writes both scale
@@ -236,6 +273,14 @@ fp8q_status fp8q_proj(const uint16_t *x_bf16, const uint8_t *w_e4m3,
                       uint8_t *act_q_scratch, float *act_scale_scratch,
                       float *act_scale_km_scratch, uint32_t M, uint32_t N,
                       uint32_t K, hipStream_t stream);
+
+/* As fp8q_proj with per-row weight scales w_scale_row [N] (see
+ * fp8q_gemm_rowscaled). */
+fp8q_status fp8q_proj_rowscaled(const uint16_t *x_bf16, const uint8_t *w_e4m3,
+                                const float *w_scale_row, uint16_t *out_bf16,
+                                uint8_t *act_q_scratch, float *act_scale_scratch,
+                                float *act_scale_km_scratch, uint32_t M, uint32_t N,
+                                uint32_t K, hipStream_t stream);
 
 #ifdef __cplusplus
 }

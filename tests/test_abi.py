@@ -128,3 +128,22 @@ def test_proj_quant_fused():
     assert fp8q.fp8q_proj_quant_fused(3276, 5120)           # 131040 groups
     assert not fp8q.fp8q_proj_quant_fused(3277, 5120)       # 131080 groups
     assert not fp8q.fp8q_proj_quant_fused(4576, 17408)
+
+
+def test_rowscaled_and_dequant_validation():
+    L = fp8q.lib()
+    g = GOOD
+    assert L.fp8q_gemm_rowscaled(g, g, g, g, g, 4, 100, 128, None) == 2      # N % 128
+    assert L.fp8q_gemm_rowscaled(g, g, g, None, g, 4, 128, 128, None) == 1   # NULL row scales
+    assert "w_scale_row" in _err()
+    assert L.fp8q_gemm_rowscaled_ex(g, g, g, g, g, 4, 128, 128, 6, None) == 6
+    assert L.fp8q_gemm_rowscaled(g, g, g, g, g, 0, 128, 128, None) == 0
+    assert L.fp8q_proj_rowscaled(g, g, g, g, g, g, None, 4, 128, 128, None) == 1
+    assert L.fp8q_proj_rowscaled(g, g, g, g, g, g, g, 0, 128, 128, None) == 0
+    # dequant: per_row 0/1 only; K multiple of 128 (blocks) or 16 (rows); any N
+    assert L.fp8q_dequant_fp8_bf16(g, g, g, 4, 128, 2, None) == 6
+    assert L.fp8q_dequant_fp8_bf16(g, g, g, 4, 80, 0, None) == 2
+    assert L.fp8q_dequant_fp8_bf16(g, g, g, 4, 72, 1, None) == 2
+    assert L.fp8q_dequant_fp8_bf16(g, g, None, 4, 80, 1, None) == 1
+    assert L.fp8q_dequant_fp8_bf16(g, BAD, g, 4, 80, 1, None) == 3
+    assert L.fp8q_dequant_fp8_bf16(g, g, g, 0, 80, 1, None) == 0

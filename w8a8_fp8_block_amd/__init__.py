@@ -65,6 +65,10 @@ _SIGS = {
     "fp8q_gemm_blockscaled": (_I, [_P, _P, _P, _P, _P, _U, _U, _U, _P]),
     "fp8q_gemm_blockscaled_ex": (_I, [_P, _P, _P, _P, _P, _U, _U, _U, _I, _P]),
     "fp8q_proj": (_I, [_P, _P, _P, _P, _P, _P, _P, _U, _U, _U, _P]),
+    "fp8q_gemm_rowscaled": (_I, [_P, _P, _P, _P, _P, _U, _U, _U, _P]),
+    "fp8q_gemm_rowscaled_ex": (_I, [_P, _P, _P, _P, _P, _U, _U, _U, _I, _P]),
+    "fp8q_proj_rowscaled": (_I, [_P, _P, _P, _P, _P, _P, _P, _U, _U, _U, _P]),
+    "fp8q_dequant_fp8_bf16": (_I, [_P, _P, _P, _U, _U, _I, _P]),
 }
 
 _lib = None
@@ -173,6 +177,32 @@ def fp8q_proj(x, w, w_scale, out, act_q, act_scale, act_scale_km, stream=None):
         raise ValueError("x and w disagree on K")
     _check(lib().fp8q_proj(_ptr(x), _ptr(w), _ptr(w_scale), _ptr(out), _ptr(act_q),
                           _ptr(act_scale), _ptr(act_scale_km), M, N, K, _stream(stream)))
+
+
+def fp8q_gemm_rowscaled(a, a_scale_km, w, w_scale_row, out, kernel: int = 0, stream=None):
+    """As fp8q_gemm_blockscaled with one fp32 weight scale per row, w_scale_row [N]."""
+    M, K = _dims(a, 2)
+    N, K2 = _dims(w, 2)
+    if K2 != K:
+        raise ValueError("a and w disagree on K")
+    _check(lib().fp8q_gemm_rowscaled_ex(_ptr(a), _ptr(a_scale_km), _ptr(w), _ptr(w_scale_row),
+                                       _ptr(out), M, N, K, kernel, _stream(stream)))
+
+
+def fp8q_proj_rowscaled(x, w, w_scale_row, out, act_q, act_scale, act_scale_km, stream=None):
+    M, K = _dims(x, 2)
+    N, K2 = _dims(w, 2)
+    if K2 != K:
+        raise ValueError("x and w disagree on K")
+    _check(lib().fp8q_proj_rowscaled(_ptr(x), _ptr(w), _ptr(w_scale_row), _ptr(out), _ptr(act_q),
+                                    _ptr(act_scale), _ptr(act_scale_km), M, N, K, _stream(stream)))
+
+
+def fp8q_dequant_fp8_bf16(w, scale, dst, per_row: bool, stream=None):
+    """FP8 weights [N,K] -> bf16 [N,K] (dst), block-scaled or per-row scales."""
+    N, K = _dims(w, 2)
+    _check(lib().fp8q_dequant_fp8_bf16(_ptr(w), _ptr(scale), _ptr(dst), N, K, 1 if per_row else 0,
+                                      _stream(stream)))
 
 
 def fp8q_default_select_params(cu_count: int) -> SelectParams:

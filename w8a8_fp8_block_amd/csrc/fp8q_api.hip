@@ -179,17 +179,74 @@ int gemm_auto_kernel(uint32_t M) {
 
 fp8q_status run_gemm(const char* fn, const uint8_t* a, const float* as, const uint8_t* w,
                      const float* ws, uint16_t* out, uint32_t M, uint32_t N, uint32_t K, int kernel,
-                     hipStream_t s) {
+                     bool row_scaled, hipStream_t s) {
   if (kernel == 0) kernel = gemm_auto_kernel(M);
   if (kernel == 2 && M > kSkinnyMaxM)
     return fail(FP8Q_ERR_VARIANT, "%s: skinny kernel needs M <= %u (M=%u)", fn, kSkinnyMaxM, M);
   uint32_t cus = 0;
   const fp8q_status st = check_device(fn, &cus);
   if (st != FP8Q_OK) return st;
-  const hipError_t e = (kernel == 2) ? launch_gemm_skinny(a, as, w, ws, out, M, N, K, cus, s)
-                                     : launch_gemm_tiled(a, as, w, ws, out, M, N, K,
-                                                         kernel == 1 ? 1 : kernel - 1, s);
+  const hipError_t e =
+      (kernel == 2) ? launch_gemm_skinny(a, as, w, ws, out, M, N, K, cus, row_scaled, s)
+                    : launch_gemm_tiled(a, as, w, ws, out, M, N, K, kernel == 1 ? 1 : kernel - 1,
+                                        row_scaled, s);
   return launched(fn, e);
+}
+
+// Shared argument checks of the GEMM entry points.
+fp8q_status check_gemm_args(const char* fn, const uint8_t* a_e4m3, const float* a_scale_km,
+                            const uint8_t* w_e4m3, const float* w_scale, const char* w_scale_name,
+                            uint16_t* out_bf16, uint32_t M, uint32_t N, uint32_t K, int kernel) {
+  if (kernel < 0 || kernel > 5) return fail(FP8Q_ERR_VARIANT, "%s: kernel %d out of range", fn, kernel);
+  fp8q_status st = check_mk(fn, M, K);
+  if (st != FP8Q_OK) return st;
+  st = check_n(fn, M, N, K);
+  if (st != FP8Q_OK) return st;
+  if ((uint64_t)m_pad16(M) * K > kMaxElems) return fail(FP8Q_ERR_SHAPE, "%s: Mp*K exceeds 2^32-1", fn);
+  REQUIRE_PTR(a_e4m3);
+  REQUIRE_PTR(a_scale_km);
+  REQUIRE_PTR(w_e4m3);
+  if (w_scale == nullptr) return fail(FP8Q_ERR_NULL, "%s: %s is NULL", fn, w_scale_name);
+  if (!aligned16(w_scale)) return fail(FP8Q_ERR_ALIGN, "%s: %s is not 16-byte aligned", fn, w_scale_name);
+  REQUIRE_PTR(out_bf16);
+  return FP8Q_OK;
+}
+
+fp8q_status run_proj(const char* fn, const uint16_t* x_bf16, const uint8_t* w_e4m3,
+                     const float* w_scale, uint16_t* out_bf16, uint8_t* act_q_scratch,
+                     float* act_scale_scratch, float* act_scale_km_scratch, uint32_t M, uint32_t N,
+                     uint32_t K, bool row_scaled, hipStream_t stream);
+
+fp8q_status run_proj(const char* fn, const uint16_t* x_bf16, const uint8_t* w_e4m3,
+                     const float* w_scale, uint16_t* out_bf16, uint8_t* act_q_scratch,
+                     float* act_scale_scratch, float* act_scale_km_scratch, uint32_t M, uint32_t N,
+                     uint32_t K, bool row_scaled, hipStream_t stream) {
+  fp8q_status st = check_mk(fn, M, K);
+  if (st != FP8Q_OK) return st;
+  st = check_n(fn, M, N, K);
+  if (st != FP8Q_OK) return st;
+  if ((uint64_t)m_pad16(M) * K > kMaxElems) return fail(FP8Q_ERR_SHAPE, "%s: Mp*K exceeds 2^32-1", fn);
+  REQUIRE_PTR(x_bf16);
+  REQUIRE_PTR(w_e4m3);
+  REQUIRE_PTR(w_scale);
+  REQUIRE_PTR(out_bf16);
+  REQUIRE_PTR(act_q_scratch);
+  REQUIRE_PTR(act_scale_scratch);
+  REQUIRE_PTR(act_scale_km_scratch);
+  if (M == 0) return ok();
+  if ((uint64_t)M * (K / kGroup) <= kFusedKmajorMaxGroups) {
+    // one kernel writes both scale layouts (saves a launch)
+    st = run_quant(fn, x_bf16, act_q_scratch, act_scale_scratch, act_scale_km_scratch, M, K, 0,
+                   stream);
+    if (st != FP8Q_OK) return st;
+  } else {
+    st = run_quant(fn, x_bf16, act_q_scratch, act_scale_scratch, nullptr, M, K, 0, stream);
+    if (st != FP8Q_OK) return st;
+    st = launched(fn, launch_relayout(act_scale_scratch, act_scale_km_scratch, M, K, stream));
+    if (st != FP8Q_OK) return st;
+  }
+  return run_gemm(fn, act_q_scratch, act_scale_km_scratch, w_e4m3, w_scale, out_bf16, M, N, K, 0,
+                  row_scaled, stream);
 }
 
 }  // namespace
@@ -328,21 +385,54 @@ fp8q_status fp8q_gemm_blockscaled_ex(const uint8_t* a_e4m3, const float* a_scale
                                      uint16_t* out_bf16, uint32_t M, uint32_t N, uint32_t K,
                                      int kernel, hipStream_t stream) {
   const char* fn = "fp8q_gemm_blockscaled";
-  if (kernel < 0 || kernel > 5) return fail(FP8Q_ERR_VARIANT, "%s: kernel %d out of range", fn, kernel);
-  fp8q_status st = check_mk(fn, M, K);
+  fp8q_status st =
+      check_gemm_args(fn, a_e4m3, a_scale_km, w_e4m3, w_scale, "w_scale", out_bf16, M, N, K, kernel);
   if (st != FP8Q_OK) return st;
-  st = check_n(fn, M, N, K);
-  if (st != FP8Q_OK) return st;
-  if ((uint64_t)m_pad16(M) * K > kMaxElems) return fail(FP8Q_ERR_SHAPE, "%s: Mp*K exceeds 2^32-1", fn);
-  REQUIRE_PTR(a_e4m3);
-  REQUIRE_PTR(a_scale_km);
-  REQUIRE_PTR(w_e4m3);
-  REQUIRE_PTR(w_scale);
-  REQUIRE_PTR(out_bf16);
   if (M == 0) return ok();
   st = check_device(fn);
   if (st != FP8Q_OK) return st;
-  return run_gemm(fn, a_e4m3, a_scale_km, w_e4m3, w_scale, out_bf16, M, N, K, kernel, stream);
+  return run_gemm(fn, a_e4m3, a_scale_km, w_e4m3, w_scale, out_bf16, M, N, K, kernel, false, stream);
+}
+
+fp8q_status fp8q_gemm_rowscaled(const uint8_t* a_e4m3, const float* a_scale_km,
+                                const uint8_t* w_e4m3, const float* w_scale_row, uint16_t* out_bf16,
+                                uint32_t M, uint32_t N, uint32_t K, hipStream_t stream) {
+  return fp8q_gemm_rowscaled_ex(a_e4m3, a_scale_km, w_e4m3, w_scale_row, out_bf16, M, N, K, 0,
+                                stream);
+}
+
+fp8q_status fp8q_gemm_rowscaled_ex(const uint8_t* a_e4m3, const float* a_scale_km,
+                                   const uint8_t* w_e4m3, const float* w_scale_row,
+                                   uint16_t* out_bf16, uint32_t M, uint32_t N, uint32_t K,
+                                   int kernel, hipStream_t stream) {
+  const char* fn = "fp8q_gemm_rowscaled";
+  fp8q_status st =
+      check_gemm_args(fn, a_e4m3, a_scale_km, w_e4m3, w_scale_row, "w_scale_row", out_bf16, M, N,
+                      K, kernel);
+  if (st != FP8Q_OK) return st;
+  if (M == 0) return ok();
+  st = check_device(fn);
+  if (st != FP8Q_OK) return st;
+  return run_gemm(fn, a_e4m3, a_scale_km, w_e4m3, w_scale_row, out_bf16, M, N, K, kernel, true,
+                  stream);
+}
+
+fp8q_status fp8q_dequant_fp8_bf16(const uint8_t* w_e4m3, const float* scale, uint16_t* dst_bf16,
+                                  uint32_t N, uint32_t K, int per_row, hipStream_t stream) {
+  const char* fn = "fp8q_dequant_fp8_bf16";
+  if (per_row != 0 && per_row != 1)
+    return fail(FP8Q_ERR_VARIANT, "%s: per_row must be 0 or 1 (got %d)", fn, per_row);
+  if (K == 0 || K % (per_row ? 16u : kGroup) != 0)
+    return fail(FP8Q_ERR_SHAPE, "%s: K=%u is not a positive multiple of %u", fn, K,
+                per_row ? 16u : kGroup);
+  if ((uint64_t)N * K > kMaxElems) return fail(FP8Q_ERR_SHAPE, "%s: N*K exceeds 2^32-1", fn);
+  REQUIRE_PTR(w_e4m3);
+  REQUIRE_PTR(scale);
+  REQUIRE_PTR(dst_bf16);
+  if (N == 0) return ok();
+  fp8q_status st = check_device(fn);
+  if (st != FP8Q_OK) return st;
+  return launched(fn, launch_dequant(w_e4m3, scale, dst_bf16, N, K, per_row != 0, stream));
 }
 
 int fp8q_gemm_select(uint32_t M, uint32_t N, uint32_t K) {
@@ -364,33 +454,17 @@ fp8q_status fp8q_proj(const uint16_t* x_bf16, const uint8_t* w_e4m3, const float
                       uint16_t* out_bf16, uint8_t* act_q_scratch, float* act_scale_scratch,
                       float* act_scale_km_scratch, uint32_t M, uint32_t N, uint32_t K,
                       hipStream_t stream) {
-  const char* fn = "fp8q_proj";
-  fp8q_status st = check_mk(fn, M, K);
-  if (st != FP8Q_OK) return st;
-  st = check_n(fn, M, N, K);
-  if (st != FP8Q_OK) return st;
-  if ((uint64_t)m_pad16(M) * K > kMaxElems) return fail(FP8Q_ERR_SHAPE, "%s: Mp*K exceeds 2^32-1", fn);
-  REQUIRE_PTR(x_bf16);
-  REQUIRE_PTR(w_e4m3);
-  REQUIRE_PTR(w_scale);
-  REQUIRE_PTR(out_bf16);
-  REQUIRE_PTR(act_q_scratch);
-  REQUIRE_PTR(act_scale_scratch);
-  REQUIRE_PTR(act_scale_km_scratch);
-  if (M == 0) return ok();
-  if (fp8q_proj_quant_fused(M, K)) {
-    // one kernel writes both scale layouts (saves a launch)
-    st = run_quant(fn, x_bf16, act_q_scratch, act_scale_scratch, act_scale_km_scratch, M, K, 0,
-                   stream);
-    if (st != FP8Q_OK) return st;
-  } else {
-    st = run_quant(fn, x_bf16, act_q_scratch, act_scale_scratch, nullptr, M, K, 0, stream);
-    if (st != FP8Q_OK) return st;
-    st = launched(fn, launch_relayout(act_scale_scratch, act_scale_km_scratch, M, K, stream));
-    if (st != FP8Q_OK) return st;
-  }
-  return run_gemm(fn, act_q_scratch, act_scale_km_scratch, w_e4m3, w_scale, out_bf16, M, N, K, 0,
-                  stream);
+  return run_proj("fp8q_proj", x_bf16, w_e4m3, w_scale, out_bf16, act_q_scratch,
+                  act_scale_scratch, act_scale_km_scratch, M, N, K, false, stream);
+}
+
+fp8q_status fp8q_proj_rowscaled(const uint16_t* x_bf16, const uint8_t* w_e4m3,
+                                const float* w_scale_row, uint16_t* out_bf16,
+                                uint8_t* act_q_scratch, float* act_scale_scratch,
+                                float* act_scale_km_scratch, uint32_t M, uint32_t N, uint32_t K,
+                                hipStream_t stream) {
+  return run_proj("fp8q_proj_rowscaled", x_bf16, w_e4m3, w_scale_row, out_bf16, act_q_scratch,
+                  act_scale_scratch, act_scale_km_scratch, M, N, K, true, stream);
 }
 
 }  // extern "C"

@@ -49,12 +49,19 @@ hipError_t launch_relayout(const float* scale_rm, float* scale_km, uint32_t M,
 // 256x128 with 8 waves; 3 = 256x128 with 4 waves; 4 = 256x128 with two
 // ping-pong groups of 4 waves) and skinny (M <= 64).
 constexpr uint32_t kSkinnyMaxM = 64;
+// row_scaled: w_s is one fp32 scale per weight row [N] (applied to the
+// finished accumulator) instead of [N/128, K/128] block scales.
 hipError_t launch_gemm_tiled(const uint8_t* a, const float* a_s_km, const uint8_t* w,
                              const float* w_s, uint16_t* out, uint32_t M, uint32_t N,
-                             uint32_t K, int cfg, hipStream_t s);
+                             uint32_t K, int cfg, bool row_scaled, hipStream_t s);
 hipError_t launch_gemm_skinny(const uint8_t* a, const float* a_s_km, const uint8_t* w,
                               const float* w_s, uint16_t* out, uint32_t M, uint32_t N,
-                              uint32_t K, uint32_t cu_count, hipStream_t s);
+                              uint32_t K, uint32_t cu_count, bool row_scaled, hipStream_t s);
+
+// FP8 weights [N,K] -> bf16 [N,K]: dst = bf16(fl32(dec(w) * scale[(n/bn)*sk + k/bk]))
+// with (bn, bk, sk) = (128, 128, K/128) or, per_row, (1, K, 1).
+hipError_t launch_dequant(const uint8_t* w, const float* scale, uint16_t* dst, uint32_t N,
+                          uint32_t K, bool per_row, hipStream_t s);
 
 inline uint32_t m_pad16(uint32_t m) { return (m + 15u) / 16u * 16u; }
 

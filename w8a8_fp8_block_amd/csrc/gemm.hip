@@ -127,7 +127,7 @@ __device__ __forceinline__ void unroll_seq(F&& f, std::integer_sequence<int, Is.
   (f(std::integral_constant<int, Is>{}), ...);
 }
 
-template <int BM, int BN, int WGM, int WGN, int STAGES>
+template <int BM, int BN, int WGM, int WGN, int STAGES, bool ROW = false>
 struct TileCfg {
   static constexpr int NW = WGM * WGN, NT = 64 * NW;
   static constexpr int WM = BM / WGM, WN = BN / WGN, TM = WM / 16, TN = WN / 16, NP = TM * TN;
@@ -138,12 +138,12 @@ struct TileCfg {
   static constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
   static constexpr int DA = BM * 8 / 64 / NW;  // 1 KB direct loads per wave: activations
   static constexpr int DW = BN * 8 / 64 / NW;  //                              weights
-  static constexpr int LOADS = DA + DW + SA + 1;  // direct loads per wave and stage
+  static constexpr int LOADS = DA + DW + SA + (ROW ? 0 : 1);  // direct loads per wave and stage
   // LDS reads of the next block per MFMA slot: slot TN*tm + TN-1 (after the
   // last MFMA of row tm) reads activation fragment tm; the other slots take,
   // in order, the 2*TN weight-fragment halves, TM/2 activation-scale pairs
   // and the weight scale.
-  static constexpr int FREE_OPS = 2 * TN + TM / 2 + 1;
+  static constexpr int FREE_OPS = 2 * TN + TM / 2 + (ROW ? 0 : 1);
   static_assert(WM % 16 == 0 && WN % 16 == 0 && TN >= 2 && TM % 2 == 0 && NP % 4 == 0, "wave tile");
   static_assert(NP - TM >= FREE_OPS, "too few MFMA slots for the LDS reads");
   static_assert(BM * 8 % (64 * NW) == 0 && BN * 8 % (64 * NW) == 0, "tile/wave mismatch");
@@ -153,12 +153,15 @@ struct TileCfg {
   static_assert(STAGE_BYTES % 256 == 0, "stage alignment");
 };
 
-template <int BM, int BN, int WGM, int WGN, int STAGES>
+// ROW: per-row weight scales Ws[N] (one multiplier per output column,
+// applied to the finished accumulator) instead of 128x128 block scales
+// applied per K block.
+template <int BM, int BN, int WGM, int WGN, int STAGES, bool ROW>
 __global__ __launch_bounds__(64 * WGM * WGN) void gemm_tiled_kernel(
     const uint8_t* __restrict__ A, const float* __restrict__ As, const uint8_t* __restrict__ W,
     const float* __restrict__ Ws, uint16_t* __restrict__ out, uint32_t M, uint32_t N, uint32_t K,
     uint32_t Mp, uint32_t tiles_m, uint32_t tiles_n) {
-  using C = TileCfg<BM, BN, WGM, WGN, STAGES>;
+  using C = TileCfg<BM, BN, WGM, WGN, STAGES, ROW>;
   constexpr int TM = C::TM, TN = C::TN, NP = C::NP;
   extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
 
@@ -187,7 +190,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_tiled_kernel(
   const __amdgpu_buffer_rsrc_t rA = make_rsrc(A, M * K);
   const __amdgpu_buffer_rsrc_t rW = make_rsrc(W, N * K);
   const __amdgpu_buffer_rsrc_t rS = make_rsrc(As, G * Mp * 4);
-  const __amdgpu_buffer_rsrc_t rWs = make_rsrc(Ws, (N / kGroup) * G * 4);
+  const __amdgpu_buffer_rsrc_t rWs = make_rsrc(Ws, ROW ? N * 4 : (N / kGroup) * G * 4);
   uint32_t a_off[C::DA], w_off[C::DW], s_off[C::SA];
 #pragma unroll
   for (int j = 0; j < C::DA; ++j) {
@@ -216,7 +219,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_tiled_kernel(
       dma16(rW, w_off[j], kb * kGroup, base + C::A_BYTES + (wave * C::DW + j) * 1024);
 #pragma unroll
     for (int j = 0; j < C::SA; ++j) dma4(rS, s_off[j], kb * Mp * 4, base + sc_base + j * 256);
-    dma4(rWs, ws_off, kb * 4, base + ws_base);
+    if constexpr (!ROW) dma4(rWs, ws_off, kb * 4, base + ws_base);
   };
 
   // Per-lane byte offsets of a fragment inside a 16-row slab: this lane's row
@@ -261,8 +264,9 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_tiled_kernel(
       bf0[tn].lo = ld16(s0 + w_row0 + tn * 2048 + lo0);
       bf0[tn].hi = ld16(s0 + w_row0 + tn * 2048 + lo1);
     }
-    ws0 = ldf(s0 + ws_base);
+    ws0 = ROW ? 1.0f : ldf(s0 + ws_base);
   }
+  ws1 = 1.0f;
 
   // MFMA results rotate through 4 register sets; the promotions of the last
   // two MFMAs of a block are pending when the next block starts (zero before
@@ -307,7 +311,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_tiled_kernel(
               constexpr int T2 = 2 * (Q - 2 * TN);
               asn[T2] = ldf(nx + sc_base + (T2 * 16 + l16) * 4);
               asn[T2 + 1] = ldf(nx + sc_base + ((T2 + 1) * 16 + l16) * 4);
-            } else if constexpr (Q == 2 * TN + TM / 2) {
+            } else if constexpr (!ROW && Q == 2 * TN + TM / 2) {
               wsn = ldf(nx + ws_base);
             }
           }
@@ -327,6 +331,14 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_tiled_kernel(
   acc[(NP - 2) / TN][(NP - 2) % TN] += p[(NP - 2) & 3] * sc_tail;
   acc[(NP - 1) / TN][(NP - 1) % TN] += p[(NP - 1) & 3] * sc_tail;
 
+  if constexpr (ROW) {
+#pragma unroll
+    for (int tn = 0; tn < TN; ++tn) {
+      const float4 r = *reinterpret_cast<const float4*>(Ws + n0 + wn * C::WN + tn * 16 + 4 * (lane >> 4));
+#pragma unroll
+      for (int tm = 0; tm < TM; ++tm) acc[tm][tn] *= v4f{r.x, r.y, r.z, r.w};
+    }
+  }
 #pragma unroll
   for (int tm = 0; tm < TM; ++tm) {
     const uint32_t m = m0 + wm * C::WM + tm * 16 + (lane & 15);
@@ -340,22 +352,22 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_tiled_kernel(
   }
 }
 
-template <int BM, int BN, int WGM, int WGN, int STAGES>
+template <int BM, int BN, int WGM, int WGN, int STAGES, bool ROW>
 hipError_t launch_tiled_cfg(const uint8_t* a, const float* a_s_km, const uint8_t* w,
                             const float* w_s, uint16_t* out, uint32_t M, uint32_t N, uint32_t K,
                             hipStream_t s) {
-  using C = TileCfg<BM, BN, WGM, WGN, STAGES>;
+  using C = TileCfg<BM, BN, WGM, WGN, STAGES, ROW>;
   if (N % BN != 0) return hipErrorInvalidValue;
   static bool attr_set = false;  // idempotent; racing threads set the same value
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&gemm_tiled_kernel<BM, BN, WGM, WGN, STAGES>),
+        reinterpret_cast<const void*>(&gemm_tiled_kernel<BM, BN, WGM, WGN, STAGES, ROW>),
         hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
   const uint32_t tiles_m = (M + BM - 1) / BM, tiles_n = N / BN;
-  gemm_tiled_kernel<BM, BN, WGM, WGN, STAGES><<<dim3(tiles_m * tiles_n), dim3(C::NT), C::LDS_BYTES, s>>>(
+  gemm_tiled_kernel<BM, BN, WGM, WGN, STAGES, ROW><<<dim3(tiles_m * tiles_n), dim3(C::NT), C::LDS_BYTES, s>>>(
       a, a_s_km, w, w_s, out, M, N, K, m_pad16(M), tiles_m, tiles_n);
   return hipGetLastError();
 }
@@ -381,7 +393,7 @@ hipError_t launch_tiled_cfg(const uint8_t* a, const float* a_s_km, const uint8_t
 // never read) goes to slot s % STAGES.  Before the phase-A barrier of block
 // kb each wave waits for its own part of stage kb+1.
 // ------------------------------------------------------------------------
-template <int STAGES>
+template <int STAGES, bool ROW = false>
 struct PpCfg {
   static constexpr int BM = 256, BN = 128, NW = 8, NT = 512;
   static constexpr int WM = 64, WN = 64, TM = 4, TN = 4, NP = 16;
@@ -391,17 +403,17 @@ struct PpCfg {
   static constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
   static constexpr int CHUNKS = (A_BYTES + W_BYTES) / 1024;  // 48
   static constexpr int CW = CHUNKS / NW;                      // 6 operand chunks per wave
-  static constexpr int LW = CW + 2;                           // + own scales: loads per wave and stage
+  static constexpr int LW = CW + (ROW ? 1 : 2);               // + own scales: loads per wave and stage
   static_assert(CHUNKS % NW == 0 && 2 * LW < 64, "vmcnt range");
   static_assert(LDS_BYTES <= 160 * 1024 && STAGES == 3, "config");
 };
 
-template <int STAGES>
+template <int STAGES, bool ROW>
 __global__ __launch_bounds__(512) void gemm_pp_kernel(
     const uint8_t* __restrict__ A, const float* __restrict__ As, const uint8_t* __restrict__ W,
     const float* __restrict__ Ws, uint16_t* __restrict__ out, uint32_t M, uint32_t N, uint32_t K,
     uint32_t Mp, uint32_t tiles_m, uint32_t tiles_n) {
-  using C = PpCfg<STAGES>;
+  using C = PpCfg<STAGES, ROW>;
   constexpr int TM = C::TM, TN = C::TN, NP = C::NP, BM = C::BM, BN = C::BN, CW = C::CW, LW = C::LW;
   extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
 
@@ -427,7 +439,7 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(
   const __amdgpu_buffer_rsrc_t rA = make_rsrc(A, M * K);
   const __amdgpu_buffer_rsrc_t rW = make_rsrc(W, N * K);
   const __amdgpu_buffer_rsrc_t rS = make_rsrc(As, G * Mp * 4);
-  const __amdgpu_buffer_rsrc_t rWs = make_rsrc(Ws, (N / kGroup) * G * 4);
+  const __amdgpu_buffer_rsrc_t rWs = make_rsrc(Ws, ROW ? N * 4 : (N / kGroup) * G * 4);
   // this wave's operand chunks wave*CW + j: source resource and per-lane offset
   uint32_t c_off[CW];
   bool c_act[CW];
@@ -452,7 +464,7 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(
       dma16(c_act[J] ? rA : rW, c_off[J], kb * kGroup, base + (wave * CW + J) * 1024);
     } else if constexpr (J == CW) {
       dma4(rS, s_off, kb * Mp * 4, base + my_sc);
-    } else {
+    } else if constexpr (!ROW) {
       dma4(rWs, ws_off, kb * 4, base + my_sc + 256);
     }
   };
@@ -495,7 +507,7 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(
       af[tm].hi = ld16(sb + a_row0 + tm * 2048 + lo1);
       as[tm] = ldf(sb + my_sc + (tm * 16 + l16) * 4);
     }
-    ws = ldf(sb + my_sc + 256);
+    ws = ROW ? 1.0f : ldf(sb + my_sc + 256);
   };
   // MFMAs and promotions of the block in registers; the promotions of its
   // last two MFMAs are left pending for the next block's compute phase.
@@ -561,6 +573,14 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(
   wait_vmcnt<0>();  // no direct load may still be writing LDS at exit
   acc[(NP - 2) / TN][(NP - 2) % TN] += p[(NP - 2) & 3] * sc_tail;
   acc[(NP - 1) / TN][(NP - 1) % TN] += p[(NP - 1) & 3] * sc_tail;
+  if constexpr (ROW) {
+#pragma unroll
+    for (int tn = 0; tn < TN; ++tn) {
+      const float4 r = *reinterpret_cast<const float4*>(Ws + n0 + wn * C::WN + tn * 16 + 4 * (lane >> 4));
+#pragma unroll
+      for (int tm = 0; tm < TM; ++tm) acc[tm][tn] *= v4f{r.x, r.y, r.z, r.w};
+    }
+  }
 
 #pragma unroll
   for (int tm = 0; tm < TM; ++tm) {
@@ -575,20 +595,20 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(
   }
 }
 
-template <int STAGES>
+template <int STAGES, bool ROW>
 hipError_t launch_pp_cfg(const uint8_t* a, const float* a_s_km, const uint8_t* w, const float* w_s,
                          uint16_t* out, uint32_t M, uint32_t N, uint32_t K, hipStream_t s) {
-  using C = PpCfg<STAGES>;
+  using C = PpCfg<STAGES, ROW>;
   if (N % C::BN != 0) return hipErrorInvalidValue;
   static bool attr_set = false;  // idempotent; racing threads set the same value
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_pp_kernel<STAGES>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_pp_kernel<STAGES, ROW>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
   const uint32_t tiles_m = (M + C::BM - 1) / C::BM, tiles_n = N / C::BN;
-  gemm_pp_kernel<STAGES><<<dim3(tiles_m * tiles_n), dim3(C::NT), C::LDS_BYTES, s>>>(
+  gemm_pp_kernel<STAGES, ROW><<<dim3(tiles_m * tiles_n), dim3(C::NT), C::LDS_BYTES, s>>>(
       a, a_s_km, w, w_s, out, M, N, K, m_pad16(M), tiles_m, tiles_n);
   return hipGetLastError();
 }
@@ -608,7 +628,7 @@ hipError_t launch_pp_cfg(const uint8_t* a, const float* a_s_km, const uint8_t* w
 // loaded once for all tiles, and the NWV partial tiles are summed through
 // LDS in wave order.
 // ------------------------------------------------------------------------
-template <int TM, int TN, int NWV, int U>
+template <int TM, int TN, int NWV, int U, bool ROW>
 __global__ __launch_bounds__(64 * NWV) void gemm_skinny_kernel(
     const uint8_t* __restrict__ A, const float* __restrict__ As, const uint8_t* __restrict__ W,
     const float* __restrict__ Ws, uint16_t* __restrict__ out, uint32_t M, uint32_t N, uint32_t K,
@@ -663,7 +683,7 @@ __global__ __launch_bounds__(64 * NWV) void gemm_skinny_kernel(
             } else {
               wf[u][t] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
             }
-            ws[u][t] = Ws[wsi[t] + k];
+            ws[u][t] = ROW ? 1.0f : Ws[wsi[t] + k];
           }
         }
 #pragma unroll
@@ -707,12 +727,18 @@ __global__ __launch_bounds__(64 * NWV) void gemm_skinny_kernel(
       for (int v = 1; v < NWV; ++v) s += red[v][t][tm][lane];
       const uint32_t m = tm * 16 + l16;
       const uint32_t n = c0 + 16 * t + 4 * (lane >> 4);
+      if constexpr (ROW) {
+        if (n < c1) {
+          const float4 r = *reinterpret_cast<const float4*>(Ws + n);
+          s *= v4f{r.x, r.y, r.z, r.w};
+        }
+      }
       if (m < M && n < c1) *reinterpret_cast<uint2*>(out + (uint64_t)m * N + n) = pack_bf16x4(s);
     }
   }
 }
 
-template <int TM, int TN>
+template <int TM, int TN, bool ROW>
 hipError_t launch_skinny_tn(const uint8_t* a, const float* a_s_km, const uint8_t* w,
                             const float* w_s, uint16_t* out, uint32_t M, uint32_t N, uint32_t K,
                             uint32_t grid, uint32_t base, uint32_t rem, hipStream_t s) {
@@ -726,39 +752,42 @@ hipError_t launch_skinny_tn(const uint8_t* a, const float* a_s_km, const uint8_t
   constexpr int UF = (BUDGET - FIXED) / PER;
   constexpr int U = UF > 8 ? 8 : UF < 1 ? 1 : UF;
   static_assert(NWV * TN * TM <= 64, "LDS for the partial sums");
-  gemm_skinny_kernel<TM, TN, NWV, U><<<dim3(grid), dim3(64 * NWV), 0, s>>>(
+  gemm_skinny_kernel<TM, TN, NWV, U, ROW><<<dim3(grid), dim3(64 * NWV), 0, s>>>(
       a, a_s_km, w, w_s, out, M, N, K, m_pad16(M), base, rem);
   return hipGetLastError();
 }
 
-template <int TM>
+template <int TM, bool ROW>
 hipError_t launch_skinny_tm(const uint8_t* a, const float* a_s_km, const uint8_t* w,
                             const float* w_s, uint16_t* out, uint32_t M, uint32_t N, uint32_t K,
                             uint32_t grid, uint32_t base, uint32_t rem, uint32_t tn, hipStream_t s) {
-  if (tn <= 2) return launch_skinny_tn<TM, 2>(a, a_s_km, w, w_s, out, M, N, K, grid, base, rem, s);
-  if (tn <= 4) return launch_skinny_tn<TM, 4>(a, a_s_km, w, w_s, out, M, N, K, grid, base, rem, s);
-  if (tn <= 6) return launch_skinny_tn<TM, 6>(a, a_s_km, w, w_s, out, M, N, K, grid, base, rem, s);
-  return launch_skinny_tn<TM, 8>(a, a_s_km, w, w_s, out, M, N, K, grid, base, rem, s);
+  if (tn <= 2) return launch_skinny_tn<TM, 2, ROW>(a, a_s_km, w, w_s, out, M, N, K, grid, base, rem, s);
+  if (tn <= 4) return launch_skinny_tn<TM, 4, ROW>(a, a_s_km, w, w_s, out, M, N, K, grid, base, rem, s);
+  if (tn <= 6) return launch_skinny_tn<TM, 6, ROW>(a, a_s_km, w, w_s, out, M, N, K, grid, base, rem, s);
+  return launch_skinny_tn<TM, 8, ROW>(a, a_s_km, w, w_s, out, M, N, K, grid, base, rem, s);
 }
 
 }  // namespace
 
-hipError_t launch_gemm_tiled(const uint8_t* a, const float* a_s_km, const uint8_t* w,
-                             const float* w_s, uint16_t* out, uint32_t M, uint32_t N, uint32_t K,
-                             int cfg, hipStream_t s) {
+namespace {
+template <bool ROW>
+hipError_t launch_gemm_tiled_t(const uint8_t* a, const float* a_s_km, const uint8_t* w,
+                               const float* w_s, uint16_t* out, uint32_t M, uint32_t N, uint32_t K,
+                               int cfg, hipStream_t s) {
   switch (cfg) {
     case 0:
-    case 1: return launch_tiled_cfg<128, 128, 2, 2, 2>(a, a_s_km, w, w_s, out, M, N, K, s);
-    case 2: return launch_tiled_cfg<256, 128, 4, 2, 3>(a, a_s_km, w, w_s, out, M, N, K, s);
-    case 3: return launch_tiled_cfg<256, 128, 2, 2, 3>(a, a_s_km, w, w_s, out, M, N, K, s);
-    case 4: return launch_pp_cfg<3>(a, a_s_km, w, w_s, out, M, N, K, s);
+    case 1: return launch_tiled_cfg<128, 128, 2, 2, 2, ROW>(a, a_s_km, w, w_s, out, M, N, K, s);
+    case 2: return launch_tiled_cfg<256, 128, 4, 2, 3, ROW>(a, a_s_km, w, w_s, out, M, N, K, s);
+    case 3: return launch_tiled_cfg<256, 128, 2, 2, 3, ROW>(a, a_s_km, w, w_s, out, M, N, K, s);
+    case 4: return launch_pp_cfg<3, ROW>(a, a_s_km, w, w_s, out, M, N, K, s);
     default: return hipErrorInvalidValue;
   }
 }
 
-hipError_t launch_gemm_skinny(const uint8_t* a, const float* a_s_km, const uint8_t* w,
-                              const float* w_s, uint16_t* out, uint32_t M, uint32_t N, uint32_t K,
-                              uint32_t cu_count, hipStream_t s) {
+template <bool ROW>
+hipError_t launch_gemm_skinny_t(const uint8_t* a, const float* a_s_km, const uint8_t* w,
+                                const float* w_s, uint16_t* out, uint32_t M, uint32_t N,
+                                uint32_t K, uint32_t cu_count, hipStream_t s) {
   // one workgroup per CU, at most 128 columns each, at least 16
   const uint32_t units = N / 4;
   uint32_t grid = max(cu_count, (N + 127) / 128);
@@ -766,12 +795,27 @@ hipError_t launch_gemm_skinny(const uint8_t* a, const float* a_s_km, const uint8
   const uint32_t base = units / grid, rem = units % grid;
   const uint32_t tn = (4 * (base + (rem ? 1 : 0)) + 15) / 16;
   switch ((M + 15) / 16) {
-    case 1: return launch_skinny_tm<1>(a, a_s_km, w, w_s, out, M, N, K, grid, base, rem, tn, s);
-    case 2: return launch_skinny_tm<2>(a, a_s_km, w, w_s, out, M, N, K, grid, base, rem, tn, s);
+    case 1: return launch_skinny_tm<1, ROW>(a, a_s_km, w, w_s, out, M, N, K, grid, base, rem, tn, s);
+    case 2: return launch_skinny_tm<2, ROW>(a, a_s_km, w, w_s, out, M, N, K, grid, base, rem, tn, s);
     case 3:
-    case 4: return launch_skinny_tm<4>(a, a_s_km, w, w_s, out, M, N, K, grid, base, rem, tn, s);
+    case 4: return launch_skinny_tm<4, ROW>(a, a_s_km, w, w_s, out, M, N, K, grid, base, rem, tn, s);
     default: return hipErrorInvalidValue;
   }
+}
+}  // namespace
+
+hipError_t launch_gemm_tiled(const uint8_t* a, const float* a_s_km, const uint8_t* w,
+                             const float* w_s, uint16_t* out, uint32_t M, uint32_t N, uint32_t K,
+                             int cfg, bool row_scaled, hipStream_t s) {
+  return row_scaled ? launch_gemm_tiled_t<true>(a, a_s_km, w, w_s, out, M, N, K, cfg, s)
+                    : launch_gemm_tiled_t<false>(a, a_s_km, w, w_s, out, M, N, K, cfg, s);
+}
+
+hipError_t launch_gemm_skinny(const uint8_t* a, const float* a_s_km, const uint8_t* w,
+                              const float* w_s, uint16_t* out, uint32_t M, uint32_t N, uint32_t K,
+                              uint32_t cu_count, bool row_scaled, hipStream_t s) {
+  return row_scaled ? launch_gemm_skinny_t<true>(a, a_s_km, w, w_s, out, M, N, K, cu_count, s)
+                    : launch_gemm_skinny_t<false>(a, a_s_km, w, w_s, out, M, N, K, cu_count, s);
 }
 
 }  // namespace fp8q
