@@ -20,6 +20,8 @@ quantized per 128x128 block.  Prints ONE JSON line:
                   R back-to-back launches between two events (no host gaps)
   act_quant       the quantizer's GB/s (algorithmic bytes) against HBM peak
   cpu_baseline    the CPU oracle on a bounded sample of the same workload
+  bf16_comparator the same GEMM in bf16 over the dequantized weights (our
+                  bf16 MFMA kernel and hipBLASLt), and the FP8 speedup
 
 Only one GPU is used; --gpus above 1 exits with a message.
 """
@@ -38,6 +40,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0      # MI355X HBM3E, GB/s
 FP8_PEAK_TFLOPS = 5000.0   # MI355X dense FP8 MFMA, TFLOP/s
+BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
 # HBM bytes the rocprofv3 FETCH_SIZE/WRITE_SIZE counters attribute to one
 # launch of the dominant GEMM at the default workload, scaled by the counters'
 # readings for a plain 1 GiB copy (the HBM-bytes summary under profiles/).
@@ -327,6 +330,34 @@ def main():
     quant_b2b_us = b0.elapsed_time(b1) * 1e3 / R
     del w_alt, x_alt
 
+    # bf16 comparator: the same projection in bf16 over the weights
+    # dequantized once by fp8q_dequant_fp8_bf16 (outside the timing); our bf16
+    # MFMA kernel and, for context, the vendor library through torch.mm
+    # (hipBLASLt), each R back-to-back launches alternating two weight copies
+    wd = torch.empty((N, K), dtype=torch.bfloat16, device=dev)
+    fp8q.fp8q_dequant_fp8_bf16(wq, ws, wd, per_row)
+    xb = x.view(torch.bfloat16)
+    outb = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    wds = [wd, wd.clone()]
+    torch.cuda.synchronize()
+    b0.record(stream)
+    for i in range(R):
+        fp8q.fp8q_gemm_bf16(xb, wds[i % 2], outb)
+    b1.record(stream)
+    torch.cuda.synchronize()
+    bf16_own_us = b0.elapsed_time(b1) * 1e3 / R
+    wts = [t.t().contiguous() for t in wds]  # [K,N] for a plain (non-batched) mm
+    del wds
+    torch.mm(xb, wts[0], out=outb)
+    torch.cuda.synchronize()
+    b0.record(stream)
+    for i in range(R):
+        torch.mm(xb, wts[i % 2], out=outb)
+    b1.record(stream)
+    torch.cuda.synchronize()
+    bf16_lib_us = b0.elapsed_time(b1) * 1e3 / R
+    del wts, wd, outb
+
     gpu_ms = t_start.elapsed_time(t_end)
     ms_per_step = max(gpu_ms, wall * 1e3) / args.steps
     gemm_ms = np.array([a.elapsed_time(b) for a, b in evg])
@@ -404,6 +435,18 @@ def main():
             "algorithmic_bytes_per_launch": quant_bytes,
         },
         "cpu_baseline": cpu,
+        "bf16_comparator": {
+            "what": "the same projection's GEMM in bf16 over the dequantized weights, "
+                    "back-to-back launches",
+            "own_bf16_us": round(bf16_own_us, 2),
+            "own_bf16_tflops": round(flops / bf16_own_us / 1e6, 1),
+            "hipblaslt_bf16_us": round(bf16_lib_us, 2),
+            "hipblaslt_bf16_tflops": round(flops / bf16_lib_us / 1e6, 1),
+            "fp8_back_to_back_us": round(gemm_b2b_us, 2),
+            "fp8_over_own_bf16": round(bf16_own_us / gemm_b2b_us, 3),
+            "fp8_over_hipblaslt_bf16": round(bf16_lib_us / gemm_b2b_us, 3),
+            "bf16_peak_tflops": BF16_PEAK_TFLOPS,
+        },
     }
     print(json.dumps(rec), flush=True)
 

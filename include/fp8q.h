@@ -251,6 +251,17 @@ fp8q_status fp8q_dequant_fp8_bf16(const uint8_t *w_e4m3, const float *scale,
                                   uint16_t *dst_bf16, uint32_t N, uint32_t K,
                                   int per_row, hipStream_t stream);
 
+/* bf16 GEMM, the same-box comparator of the FP8 path (dispatch_proj.rs:
+ * the bf16 projection over the dequantized weight, against which the page
+ * quotes the FP8 path's speedup):
+ *   out_bf16[m,n] = bf16_rne( sum_k x_bf16[m,k] * w_bf16[n,k] )   (fp32 sum)
+ *   x_bf16 [M,K], w_bf16 [N,K] (e.g. from fp8q_dequant_fp8_bf16), out [M,N].
+ * N % 128 == 0, K % 64 == 0, M*K*2 and N*K*2 below 2^32 bytes.  Same
+ * conventions and errors as fp8q_gemm_blockscaled. */
+fp8q_status fp8q_gemm_bf16(const uint16_t *x_bf16, const uint16_t *w_bf16,
+                           uint16_t *out_bf16, uint32_t M, uint32_t N, uint32_t K,
+                           hipStream_t stream);
+
 /* ----------------------------------------------------------- projection */
 
 /* 1 if fp8q_proj quantizes with the fused kernel that writes both scale

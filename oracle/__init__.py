@@ -13,6 +13,7 @@ Every function takes and returns numpy arrays:
 * ``dequant_fp8_bf16(codes[N,K], scale) -> bf16 bits[N,K] uint16`` (either weight format)
 * ``gemm_ref(a, a_s_rm, w, w_s) -> out[M,N] f64`` (w_s block-scaled 2-D or per-row 1-D)
 * ``gemm_ref_at(a, a_s_rm, w, w_s, ms, ns) -> out[len] f64``
+* ``gemm_bf16_ref(x_bits[M,K], w_bits[N,K]) -> out[M,N] f64`` (bf16 comparator)
 * ``e4m3_decode(codes) -> f64``, ``e4m3_encode(f32) -> uint8``
 
 See ``fp8q_oracle.c`` for the definitions and the passages they follow.
@@ -218,6 +219,16 @@ def gemm_ref_at(a, a_s_rm, w, w_s, ms, ns) -> np.ndarray:
     _load().oracle_gemm_ref_at_geom(_p(a), _p(a_s), _p(w), _p(w_s), _p(ms), _p(ns),
                                     _p(out), ms.size, K, bn, bk, sk)
     return out
+
+
+def gemm_bf16_ref(x_bits: np.ndarray, w_bits: np.ndarray) -> np.ndarray:
+    """fp64 reference of the bf16 comparator GEMM, x[M,K] . w[N,K]^T: the bf16
+    values are exact in fp64, and the product is numpy's float64 matmul (a
+    library primitive as the one step; the pages' bf16 projection computes
+    act . W^T, dispatch_proj.rs)."""
+    xf = (np.ascontiguousarray(x_bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+    wf = (np.ascontiguousarray(w_bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+    return xf.astype(np.float64) @ wf.astype(np.float64).T
 
 
 # ---------------------------------------------------------------- tolerance

@@ -147,3 +147,14 @@ def test_rowscaled_and_dequant_validation():
     assert L.fp8q_dequant_fp8_bf16(g, g, None, 4, 80, 1, None) == 1
     assert L.fp8q_dequant_fp8_bf16(g, BAD, g, 4, 80, 1, None) == 3
     assert L.fp8q_dequant_fp8_bf16(g, g, g, 0, 80, 1, None) == 0
+
+
+def test_gemm_bf16_validation():
+    L = fp8q.lib()
+    g = GOOD
+    assert L.fp8q_gemm_bf16(g, g, g, 4, 128, 96, None) == 2     # K % 64
+    assert L.fp8q_gemm_bf16(g, g, g, 4, 100, 128, None) == 2    # N % 128
+    assert L.fp8q_gemm_bf16(g, None, g, 4, 128, 128, None) == 1
+    assert L.fp8q_gemm_bf16(g, g, BAD, 4, 128, 128, None) == 3
+    assert L.fp8q_gemm_bf16(g, g, g, 0, 128, 128, None) == 0
+    assert L.fp8q_gemm_bf16(None, None, None, 1 << 16, 128, 1 << 15, None) == 2  # M*K*2 >= 2^32

@@ -119,3 +119,14 @@ def test_gemm_rowscale_equals_block_when_constant_per_block(orc):
     s_row = np.repeat(s_blocks, 128)
     s_blk = np.repeat(s_blocks[:, None], K // 128, axis=1)
     assert np.array_equal(orc.gemm_ref(a, a_s, w, s_row), orc.gemm_ref(a, a_s, w, s_blk))
+
+
+def test_gemm_bf16_ref_integer_exact(orc):
+    """Small-integer bf16 operands: the reference equals exact integer
+    arithmetic."""
+    rng = np.random.default_rng(12)
+    xi = rng.integers(-8, 9, (7, 192))
+    wi = rng.integers(-8, 9, (130, 192))
+    xb = synth.f32_to_bf16_bits(xi.astype(np.float32))
+    wb = synth.f32_to_bf16_bits(wi.astype(np.float32))
+    assert np.array_equal(orc.gemm_bf16_ref(xb, wb), (xi @ wi.T).astype(np.float64))

@@ -69,6 +69,7 @@ _SIGS = {
     "fp8q_gemm_rowscaled_ex": (_I, [_P, _P, _P, _P, _P, _U, _U, _U, _I, _P]),
     "fp8q_proj_rowscaled": (_I, [_P, _P, _P, _P, _P, _P, _P, _U, _U, _U, _P]),
     "fp8q_dequant_fp8_bf16": (_I, [_P, _P, _P, _U, _U, _I, _P]),
+    "fp8q_gemm_bf16": (_I, [_P, _P, _P, _U, _U, _U, _P]),
 }
 
 _lib = None
@@ -203,6 +204,15 @@ def fp8q_dequant_fp8_bf16(w, scale, dst, per_row: bool, stream=None):
     N, K = _dims(w, 2)
     _check(lib().fp8q_dequant_fp8_bf16(_ptr(w), _ptr(scale), _ptr(dst), N, K, 1 if per_row else 0,
                                       _stream(stream)))
+
+
+def fp8q_gemm_bf16(x, w, out, stream=None):
+    """bf16 comparator GEMM: out[M,N] = bf16(x[M,K] . w[N,K]^T)."""
+    M, K = _dims(x, 2)
+    N, K2 = _dims(w, 2)
+    if K2 != K:
+        raise ValueError("x and w disagree on K")
+    _check(lib().fp8q_gemm_bf16(_ptr(x), _ptr(w), _ptr(out), M, N, K, _stream(stream)))
 
 
 def fp8q_default_select_params(cu_count: int) -> SelectParams:

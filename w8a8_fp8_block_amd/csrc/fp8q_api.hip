@@ -417,6 +417,22 @@ fp8q_status fp8q_gemm_rowscaled_ex(const uint8_t* a_e4m3, const float* a_scale_k
                   stream);
 }
 
+fp8q_status fp8q_gemm_bf16(const uint16_t* x_bf16, const uint16_t* w_bf16, uint16_t* out_bf16,
+                           uint32_t M, uint32_t N, uint32_t K, hipStream_t stream) {
+  const char* fn = "fp8q_gemm_bf16";
+  if (K == 0 || K % 64 != 0) return fail(FP8Q_ERR_SHAPE, "%s: K=%u is not a positive multiple of 64", fn, K);
+  if (N == 0 || N % kGroup != 0) return fail(FP8Q_ERR_SHAPE, "%s: N=%u is not a positive multiple of 128", fn, N);
+  if ((uint64_t)M * K * 2 > kMaxElems || (uint64_t)N * K * 2 > kMaxElems || (uint64_t)M * N > kMaxElems)
+    return fail(FP8Q_ERR_SHAPE, "%s: M*K*2, N*K*2 or M*N exceeds 2^32-1", fn);
+  REQUIRE_PTR(x_bf16);
+  REQUIRE_PTR(w_bf16);
+  REQUIRE_PTR(out_bf16);
+  if (M == 0) return ok();
+  fp8q_status st = check_device(fn);
+  if (st != FP8Q_OK) return st;
+  return launched(fn, launch_gemm_bf16(x_bf16, w_bf16, out_bf16, M, N, K, stream));
+}
+
 fp8q_status fp8q_dequant_fp8_bf16(const uint8_t* w_e4m3, const float* scale, uint16_t* dst_bf16,
                                   uint32_t N, uint32_t K, int per_row, hipStream_t stream) {
   const char* fn = "fp8q_dequant_fp8_bf16";

@@ -58,6 +58,11 @@ hipError_t launch_gemm_skinny(const uint8_t* a, const float* a_s_km, const uint8
                               const float* w_s, uint16_t* out, uint32_t M, uint32_t N,
                               uint32_t K, uint32_t cu_count, bool row_scaled, hipStream_t s);
 
+// bf16 comparator GEMM: out[M,N] = bf16(x[M,K] . w[N,K]^T), N % 128 == 0,
+// K % 64 == 0.
+hipError_t launch_gemm_bf16(const uint16_t* x, const uint16_t* w, uint16_t* out, uint32_t M,
+                            uint32_t N, uint32_t K, hipStream_t s);
+
 // FP8 weights [N,K] -> bf16 [N,K]: dst = bf16(fl32(dec(w) * scale[(n/bn)*sk + k/bk]))
 // with (bn, bk, sk) = (128, 128, K/128) or, per_row, (1, K, 1).
 hipError_t launch_dequant(const uint8_t* w, const float* scale, uint16_t* dst, uint32_t N,

@@ -1,0 +1,189 @@
+// bf16 GEMM, the same-box comparator of the FP8 projection (page
+// "dispatch_proj.rs": the bf16 projection act . W^T over the dequantized
+// weight, cublas_bf16_proj_dense / the CUTLASS bf16 arm, against which the
+// page quotes the FP8 path's speedup):
+//   out[m,n] = bf16( sum_k x[m,k] * w[n,k] ),  x [M,K], w [N,K] bf16, fp32 sum.
+//
+// Same structure as the FP8 ping-pong kernel (gemm.hip): 256x128 workgroup
+// tile, 8 waves of 64x64 in two groups taking turns between MFMAs and LDS
+// reads, LDS rows of 128 bytes per stage (here 64 bf16 of K), the same
+// swizzle and direct buffer->LDS loads.  Per 128-byte block each 16x16 tile
+// takes two v_mfma_f32_16x16x32_bf16 (K = 32 each) accumulating in the
+// matrix pipe: no scales, no vector-ALU promotion.  Lane l supplies row
+// l % 16 and bf16 elements [8*(l/16), +8) of each 32-deep half-block, for
+// both operands (same K permutation on both sides).
+#include "mfma_common.h"
+
+namespace fp8q {
+namespace {
+
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ v4f mfma_bf16_32(const v4i& w, const v4i& a, const v4f& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, w),
+                                                 __builtin_bit_cast(v8bf, a), c, 0, 0, 0);
+}
+
+constexpr int kBfStages = 3;
+
+struct Bf16Cfg {
+  static constexpr int BM = 256, BN = 128, NW = 8, NT = 512;
+  static constexpr int WM = 64, WN = 64, TM = 4, TN = 4;
+  static constexpr int A_BYTES = BM * 128, W_BYTES = BN * 128;
+  static constexpr int STAGE_BYTES = A_BYTES + W_BYTES;
+  static constexpr int LDS_BYTES = kBfStages * STAGE_BYTES;
+  static constexpr int CHUNKS = STAGE_BYTES / 1024;  // 48 1-KB chunks
+  static constexpr int LW = CHUNKS / NW;             // 6 loads per wave and stage
+  static_assert(LDS_BYTES <= 160 * 1024 && CHUNKS % NW == 0 && 2 * LW < 64, "config");
+};
+
+__global__ __launch_bounds__(512) void gemm_bf16_kernel(const uint16_t* __restrict__ X,
+                                                        const uint16_t* __restrict__ W,
+                                                        uint16_t* __restrict__ out, uint32_t M,
+                                                        uint32_t N, uint32_t K, uint32_t tiles_m,
+                                                        uint32_t tiles_n) {
+  using C = Bf16Cfg;
+  constexpr int TM = C::TM, TN = C::TN, LW = C::LW, STAGES = kBfStages;
+  extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
+
+  const uint32_t tid = threadIdx.x, lane = tid & 63;
+  const uint32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const uint32_t grp = wave >> 2, gw = wave & 3;
+  const uint32_t wm = 2 * grp + (gw >> 1), wn = gw & 1;
+  uint32_t tmi, tni;
+  tile_coords(tiles_m, tiles_n, tmi, tni);
+  const uint32_t m0 = tmi * C::BM, n0 = tni * C::BN;
+  const uint32_t G = K / 64;  // 128-byte K blocks
+  const uint32_t rowb = K * 2;
+
+  const __amdgpu_buffer_rsrc_t rA = make_rsrc(X, M * rowb);
+  const __amdgpu_buffer_rsrc_t rW = make_rsrc(W, N * rowb);
+  uint32_t c_off[LW];
+  bool c_act[LW];
+#pragma unroll
+  for (int j = 0; j < LW; ++j) {
+    const uint32_t c = wave * LW + j;
+    const uint32_t ch = (c < (uint32_t)C::A_BYTES / 1024) ? c : c - C::A_BYTES / 1024;
+    const uint32_t e = ch * 64 + lane, row = e >> 3;
+    c_act[j] = c < (uint32_t)C::A_BYTES / 1024;
+    c_off[j] = c_act[j] ? min(m0 + row, M - 1) * rowb + ((e & 7) ^ swz(row)) * 16
+                        : (n0 + row) * rowb + ((e & 7) ^ swz(row)) * 16;
+  }
+  auto issue_stage = [&](uint32_t kb, uint32_t stage) {
+    uint8_t* base = smem + stage * C::STAGE_BYTES;
+#pragma unroll
+    for (int j = 0; j < LW; ++j)
+      dma16(c_act[j] ? rA : rW, c_off[j], kb * 128, base + (wave * LW + j) * 1024);
+  };
+
+  // this lane's chunks: 2 x 16 bytes per 16-row slab, chunk (lane/16) for the
+  // first 32-deep half and 4 + lane/16 for the second
+  const uint32_t l16 = lane & 15, cq = lane >> 4;
+  const uint32_t lo0 = l16 * 128 + ((cq ^ swz(l16)) * 16);
+  const uint32_t lo1 = l16 * 128 + (((cq + 4) ^ swz(l16)) * 16);
+  auto ld16 = [](const uint8_t* p) -> v4i { return *reinterpret_cast<const v4i*>(p); };
+  auto slot_base = [&](uint32_t kb) -> const uint8_t* {
+    return smem + (kb % STAGES) * C::STAGE_BYTES;
+  };
+  const uint32_t a_row0 = wm * C::WM * 128, w_row0 = C::A_BYTES + wn * C::WN * 128;
+
+  v4f acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+  v4i af0[TM], af1[TM], bf0[TN], bf1[TN];
+
+  auto read_block = [&](uint32_t kb) {
+    const uint8_t* sb = slot_base(kb);
+#pragma unroll
+    for (int tn = 0; tn < TN; ++tn) {
+      bf0[tn] = ld16(sb + w_row0 + tn * 2048 + lo0);
+      bf1[tn] = ld16(sb + w_row0 + tn * 2048 + lo1);
+    }
+#pragma unroll
+    for (int tm = 0; tm < TM; ++tm) {
+      af0[tm] = ld16(sb + a_row0 + tm * 2048 + lo0);
+      af1[tm] = ld16(sb + a_row0 + tm * 2048 + lo1);
+    }
+  };
+  // 32 MFMAs: all tiles on the first half-block, then all on the second, so
+  // the two MFMAs that accumulate into one tile are 16 apart
+  auto compute_block = [&]() {
+    unroll_seq(
+        [&](auto ic) {
+          constexpr int I = decltype(ic)::value, tm = (I % 16) / TN, tn = I % TN;
+          if constexpr (I < 16) acc[tm][tn] = mfma_bf16_32(bf0[tn], af0[tm], acc[tm][tn]);
+          else acc[tm][tn] = mfma_bf16_32(bf1[tn], af1[tm], acc[tm][tn]);
+          sched_fence();
+        },
+        std::make_integer_sequence<int, 32>{});
+  };
+
+  // (schedule and waits as in the FP8 ping-pong kernel)
+#pragma unroll
+  for (int s = 0; s < STAGES; ++s) issue_stage(min((uint32_t)s, G - 1), s);
+  if (grp == 0) {
+    wait_vmcnt<(STAGES - 1) * LW>();
+    wg_barrier();
+    read_block(0);
+    wait_lgkm0();
+    wg_barrier();
+    for (uint32_t kb = 0; kb < G; ++kb) {
+      compute_block();
+      wait_vmcnt<LW>();
+      wg_barrier();
+      read_block(kb + 1);
+      wait_lgkm0();
+      issue_stage(min(kb + STAGES, G - 1), kb % STAGES);
+      wg_barrier();
+    }
+  } else {
+    wait_vmcnt<(STAGES - 1) * LW>();
+    wg_barrier();
+    wg_barrier();
+    for (uint32_t kb = 0; kb < G; ++kb) {
+      read_block(kb);
+      wait_lgkm0();
+      issue_stage(min(kb + STAGES, G - 1), kb % STAGES);
+      wait_vmcnt<2 * LW>();
+      wg_barrier();
+      compute_block();
+      wg_barrier();
+    }
+  }
+  wait_vmcnt<0>();
+
+#pragma unroll
+  for (int tm = 0; tm < TM; ++tm) {
+    const uint32_t m = m0 + wm * C::WM + tm * 16 + l16;
+    if (m < M) {
+#pragma unroll
+      for (int tn = 0; tn < TN; ++tn) {
+        const uint32_t n = n0 + wn * C::WN + tn * 16 + 4 * (lane >> 4);
+        *reinterpret_cast<uint2*>(out + (uint64_t)m * N + n) = pack_bf16x4(acc[tm][tn]);
+      }
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_gemm_bf16(const uint16_t* x, const uint16_t* w, uint16_t* out, uint32_t M,
+                            uint32_t N, uint32_t K, hipStream_t s) {
+  using C = Bf16Cfg;
+  if (N % C::BN != 0 || K % 64 != 0) return hipErrorInvalidValue;
+  static bool attr_set = false;  // idempotent; racing threads set the same value
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_bf16_kernel),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  const uint32_t tiles_m = (M + C::BM - 1) / C::BM, tiles_n = N / C::BN;
+  gemm_bf16_kernel<<<dim3(tiles_m * tiles_n), dim3(C::NT), C::LDS_BYTES, s>>>(x, w, out, M, N, K,
+                                                                            tiles_m, tiles_n);
+  return hipGetLastError();
+}
+
+}  // namespace fp8q
