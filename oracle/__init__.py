@@ -15,6 +15,11 @@ Every function takes and returns numpy arrays:
 * ``gemm_ref_at(a, a_s_rm, w, w_s, ms, ns) -> out[len] f64``
 * ``gemm_bf16_ref(x_bits[M,K], w_bits[N,K]) -> out[M,N] f64`` (bf16 comparator)
 * ``e4m3_decode(codes) -> f64``, ``e4m3_encode(f32) -> uint8``
+* ``f64_to_bf16(v) -> bf16 bits`` (one rounding, ties to even)
+* ``silu_mul(g_bits, u_bits) -> (h_bits, ambiguous)``: the FFN intermediate
+* ``ffn_ref(x_bits, wg, wg_s, wu, wu_s, wd, wd_s, rows=None) -> dict``: the
+  whole FFN chain (quantize x once, gate and up, SiLU * up, quantize the
+  intermediate once, down)
 
 See ``fp8q_oracle.c`` for the definitions and the passages they follow.
 """
@@ -85,6 +90,10 @@ def _load():
     lib.oracle_gemm_ref_geom.restype = None
     lib.oracle_gemm_ref_at_geom.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I]
     lib.oracle_gemm_ref_at_geom.restype = None
+    lib.oracle_f64_to_bf16_array.argtypes = [P, P, I]
+    lib.oracle_f64_to_bf16_array.restype = None
+    lib.oracle_silu_mul.argtypes = [P, P, P, P, I]
+    lib.oracle_silu_mul.restype = None
     lib.oracle_num_threads.argtypes = []
     lib.oracle_num_threads.restype = ctypes.c_int
     _lib = lib
@@ -229,6 +238,60 @@ def gemm_bf16_ref(x_bits: np.ndarray, w_bits: np.ndarray) -> np.ndarray:
     xf = (np.ascontiguousarray(x_bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
     wf = (np.ascontiguousarray(w_bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
     return xf.astype(np.float64) @ wf.astype(np.float64).T
+
+
+# ------------------------------------------------------------------- FFN
+def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
+    """Values of bf16 bit patterns (exact)."""
+    b = np.ascontiguousarray(bits, dtype=np.uint16).astype(np.uint32) << 16
+    return b.view(np.float32).astype(np.float64)
+
+
+def f64_to_bf16(v: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns of float64 values, one rounding to nearest even."""
+    v = np.ascontiguousarray(v, dtype=np.float64)
+    out = np.empty(v.shape, dtype=np.uint16)
+    _load().oracle_f64_to_bf16_array(_p(v), _p(out), v.size)
+    return out
+
+
+def silu_mul(g_bits: np.ndarray, u_bits: np.ndarray):
+    """h = bf16(silu(g) * u) of bf16 gate/up outputs, and the mask of the
+    elements a binary32 evaluation may round to the other bf16 neighbour
+    (see ``oracle_silu_mul``)."""
+    g = np.ascontiguousarray(g_bits, dtype=np.uint16)
+    u = np.ascontiguousarray(u_bits, dtype=np.uint16)
+    assert g.shape == u.shape
+    h = np.empty(g.shape, dtype=np.uint16)
+    amb = np.empty(g.shape, dtype=np.uint8)
+    _load().oracle_silu_mul(_p(g), _p(u), _p(h), _p(amb), g.size)
+    return h, amb.astype(bool)
+
+
+def ffn_ref(x_bits, wg, wg_s, wu, wu_s, wd, wd_s, rows=None) -> dict:
+    """The dense FFN on FP8 weights, stage by stage (dispatch_proj.rs, doc of
+    cublas_fp8_proj_prequant): the bf16 input x[M,H] is quantized once and
+    feeds both the gate and the up projection (weights [I,H]); each
+    projection's output is bf16 (the projection's output format); the
+    intermediate h = bf16(silu(gate) * up) [M,I] is quantized once and feeds
+    the down projection (weights [H,I]), whose fp64 result ``out`` [M,H] is
+    left unrounded.
+
+    ``rows`` restricts the chain to those token rows (every stage is
+    row-local), for sampled checks at large M.  Returns the stages as a dict:
+    xq, xs (x codes and row-major scales), g, u, h (bf16 bits), amb (the
+    ``silu_mul`` mask), hq, hs (intermediate codes and row-major scales) and
+    out."""
+    x = np.ascontiguousarray(x_bits, dtype=np.uint16)
+    if rows is not None:
+        x = np.ascontiguousarray(x[np.asarray(rows, dtype=np.int64)])
+    xq, xs = quant_act(x)
+    g = f64_to_bf16(gemm_ref(xq, xs, wg, wg_s))
+    u = f64_to_bf16(gemm_ref(xq, xs, wu, wu_s))
+    h, amb = silu_mul(g, u)
+    hq, hs = quant_act(h)
+    out = gemm_ref(hq, hs, wd, wd_s)
+    return dict(xq=xq, xs=xs, g=g, u=u, h=h, amb=amb, hq=hq, hs=hs, out=out)
 
 
 # ---------------------------------------------------------------- tolerance

@@ -31,6 +31,9 @@
  *               (128, 128, K/128) or per-row (1, K, 1) (dispatch_proj.rs, doc
  *               of dequant_fp8_bf16_into); the GEMM and the FP8 -> bf16
  *               dequantizer below take that geometry.
+ *   FFN         the SwiGLU intermediate h = bf16(silu(gate) * up) between
+ *               the gate/up projections and the down projection
+ *               (dispatch_proj.rs, doc of cublas_fp8_proj_prequant).
  *
  * Readings where the pages are silent (each one is listed in the design
  * notes): amax == 0 gives scale 0 and signed-zero codes; the scale is the
@@ -306,6 +309,74 @@ void oracle_gemm_ref_at(const uint8_t *a, const float *a_s, const uint8_t *w,
                         const float *w_s, const int64_t *ms, const int64_t *ns,
                         double *out, int64_t count, int64_t K) {
   oracle_gemm_ref_at_geom(a, a_s, w, w_s, ms, ns, out, count, K, GROUP, GROUP, K / GROUP);
+}
+
+/* ------------------------------------------------- FFN intermediate */
+
+/* Nearest bf16 value of a double, ties to even, as a bit pattern: the value
+ * divided by its bf16 ulp (an exact power-of-two rescaling) is rounded to an
+ * integer by nearbyint (the default mode, to nearest even), one rounding in
+ * all.  bf16 keeps 8 significant bits and fp32's exponent range: the ulp of
+ * a value in [2^e, 2^(e+1)) is 2^(max(e,-126)-7), subnormals included;
+ * magnitudes that round to 2^128 or beyond become infinities. */
+static uint16_t f64_to_bf16_bits(double v) {
+  int e;
+  double ulp, r;
+  float f;
+  uint32_t u;
+  if (isnan(v)) return 0x7FC0;
+  if (v == 0.0 || isinf(v)) {
+    f = (float)v; /* signed zero or infinity, exact */
+  } else {
+    (void)frexp(v, &e); /* v = f * 2^e with 0.5 <= |f| < 1: binade 2^(e-1) */
+    if (e - 1 < -126) e = -125;
+    ulp = ldexp(1.0, e - 1 - 7);
+    r = nearbyint(v / ulp) * ulp;
+    f = (fabs(r) >= ldexp(1.0, 128)) ? (float)copysign(INFINITY, v) : (float)r;
+  }
+  memcpy(&u, &f, 4);
+  return (uint16_t)(u >> 16);
+}
+
+void oracle_f64_to_bf16_array(const double *v, uint16_t *out, int64_t n) {
+  int64_t i;
+  for (i = 0; i < n; ++i) out[i] = f64_to_bf16_bits(v[i]);
+}
+
+/* The dense FFN's intermediate (dispatch_proj.rs, doc of
+ * cublas_fp8_proj_prequant: gate and up are two projections of the same
+ * quantized input; the post-SiLU intermediate is quantized once for down).
+ * The pages name SiLU and the product with up but print no formula; the
+ * plain reading: h = bf16(silu(g) * u) with silu(g) = g / (1 + e^-g), g and
+ * u the bf16 outputs of the gate and up projections.  The value is formed in
+ * double (one exp, one add, one divide, one multiply: relative error a few
+ * 2^-53) and rounded once to bf16.
+ *
+ * amb[i] = 1 marks an element whose double value lies within 2^-18 of its
+ * own magnitude (or within 2^-146 absolutely) of a bf16 rounding midpoint:
+ * there an evaluation in binary32 arithmetic, whose error is a few 2^-24,
+ * may round to either neighbour, and both results are correct roundings of
+ * a value inside the binary32 evaluation's error. */
+void oracle_silu_mul(const uint16_t *g, const uint16_t *u, uint16_t *h, uint8_t *amb,
+                     int64_t n) {
+  int64_t i;
+#pragma omp parallel for schedule(static)
+  for (i = 0; i < n; ++i) {
+    const double gv = (double)bf16_to_f32(g[i]), uv = (double)bf16_to_f32(u[i]);
+    const double v = gv / (1.0 + exp(-gv)) * uv;
+    int e;
+    double ulp, t, d;
+    h[i] = f64_to_bf16_bits(v);
+    amb[i] = 0;
+    if (v != 0.0 && isfinite(v)) {
+      (void)frexp(v, &e);
+      if (e - 1 < -126) e = -125;
+      ulp = ldexp(1.0, e - 1 - 7);
+      t = v / ulp;
+      d = fabs(t - (floor(t) + 0.5)) * ulp; /* distance to the nearest midpoint */
+      if (d <= ldexp(fabs(v), -18) || d <= ldexp(1.0, -146)) amb[i] = 1;
+    }
+  }
 }
 
 /* Number of OpenMP threads a parallel region here would use. */

@@ -32,6 +32,10 @@ __all__ = [
     "ceil16",
     "exhaustive_pair_groups",
     "n_exhaustive_groups",
+    "FfnWorkload",
+    "FFN_WORKLOADS",
+    "ffn_workload",
+    "make_ffn_inputs",
 ]
 
 
@@ -125,6 +129,65 @@ def make_inputs(w: Workload, M: int | None = None, with_weights: bool = True,
     if with_weights and w.N:
         wf = rng.normal(0.0, 0.02, (w.N, w.K)).astype(np.float32)
     return xb, wf, out_idx
+
+
+# --------------------------------------------------------------------------
+# Dense FFN chain: x [M,H] -> gate, up [I,H] -> SiLU(gate) * up -> down [H,I].
+# Sizes of the projections above: gate/up are the prefill shape (K=5120,
+# N=17408 each) and down the large-prefill shape (K=17408, N=5120).
+# --------------------------------------------------------------------------
+@dataclasses.dataclass(frozen=True)
+class FfnWorkload:
+    name: str
+    M: int
+    H: int  # model width: x and out are [M,H]
+    I: int  # intermediate width: gate/up are [I,H], down is [H,I]
+    n_outliers: int
+    outlier_factor: float
+    seed: int = 0
+
+    @property
+    def desc(self) -> str:
+        return f"{self.name}:M{self.M}xH{self.H}xI{self.I}"
+
+
+FFN_WORKLOADS: dict[str, list[FfnWorkload]] = {
+    "ffn_tiny": [FfnWorkload("ffn_tiny", 16, 256, 384, 2, 20.0)],
+    "ffn_decode": [FfnWorkload("ffn_decode", m, 5120, 17408, _n_out(0.01, 5120), 20.0)
+                   for m in (16, 25)],
+    "ffn_prefill": [FfnWorkload("ffn_prefill", 1168, 5120, 17408, _n_out(0.01, 5120), 20.0)],
+    "ffn_large": [FfnWorkload("ffn_large", 4576, 5120, 17408, _n_out(0.01, 5120), 20.0)],
+}
+
+
+def ffn_workload(name: str, M: int | None = None) -> FfnWorkload:
+    for w in FFN_WORKLOADS[name]:
+        if M is None or w.M == M:
+            return w
+    raise KeyError((name, M))
+
+
+def make_ffn_inputs(w: FfnWorkload, M: int | None = None, seed: int | None = None,
+                    with_weights: bool = True):
+    """Draw (x_bf16 [M,H] uint16, (w_gate [I,H], w_up [I,H], w_down [H,I])
+    float32 or None).  Activations: N(0,1) with outlier channels; weights:
+    N(0, 0.02), to be block-quantized to FP8 by whoever consumes them.  Draw
+    order: outlier indices, x, gate, up, down."""
+    M = w.M if M is None else M
+    rng = np.random.default_rng(w.seed if seed is None else seed)
+    out_idx = rng.choice(w.H, w.n_outliers, replace=False) if w.n_outliers else \
+        np.zeros(0, dtype=np.int64)
+    x = rng.standard_normal((M, w.H), dtype=np.float32)
+    if len(out_idx):
+        x[:, out_idx] *= np.float32(w.outlier_factor)
+    xb = f32_to_bf16_bits(x)
+    del x
+    if not with_weights:
+        return xb, None
+    wg = rng.normal(0.0, 0.02, (w.I, w.H)).astype(np.float32)
+    wu = rng.normal(0.0, 0.02, (w.I, w.H)).astype(np.float32)
+    wd = rng.normal(0.0, 0.02, (w.H, w.I)).astype(np.float32)
+    return xb, (wg, wu, wd)
 
 
 # --------------------------------------------------------------------------
