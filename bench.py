@@ -23,6 +23,10 @@ quantized per 128x128 block.  Prints ONE JSON line:
   bf16_comparator the same GEMM in bf16 over the dequantized weights (our
                   bf16 MFMA kernel and hipBLASLt), and the FP8 speedup
 
+Other modes (one JSON line each, not the benchmark line): --quant-sweep,
+--dequant, --ffn <workload> (the dense FFN chain), --ffn-sweep (its
+selector), --copy-mib N.
+
 Only one GPU is used; --gpus above 1 exits with a message.
 """
 from __future__ import annotations
@@ -75,6 +79,12 @@ def parse():
     p.add_argument("--quant-sweep", action="store_true",
                    help="instead of the benchmark, time quantizer variants A, B and the "
                         "selector's choice over the token/K sweep (one JSON line per shape)")
+    p.add_argument("--ffn", default=None, choices=["ffn_decode", "ffn_prefill", "ffn_large"],
+                   help="time the dense FFN chain (fp8q_ffn, both variants, and its kernels) "
+                        "on this workload instead of the projection")
+    p.add_argument("--ffn-sweep", action="store_true",
+                   help="fp8q_ffn's two variants over M at H=5120, I=17408 with cold caches, "
+                        "and the automatic choice (the selector's measurement)")
     p.add_argument("--copy-mib", type=int, default=0,
                    help="instead of the benchmark, run 3 plain device copies of this many "
                         "MiB (the reference kernel for scaling rocprofv3 byte counters)")
@@ -175,6 +185,141 @@ def dequant_bench(reps=20):
                               "frac_hbm": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4)}), flush=True)
 
 
+def ffn_bench(name: str, M=None, reps=20):
+    """The dense FFN chain x[M,H] -> gate, up [I,H] -> SiLU * up -> down [H,I]
+    (fp8q_ffn) on one synthetic workload: the whole call for both variants
+    (median with the caches flushed before each call, and back to back), and
+    its kernels one by one (R back-to-back launches between two events):
+    the input quantizer, the fused gate/up kernel, the separate path's two
+    GEMMs and fp8q_silu_mul_quant, and the down GEMM.  FLOPs: 2*M*H*I per
+    projection, three projections."""
+    import torch
+    import synth
+    import w8a8_fp8_block_amd as fp8q
+    dev = torch.device("cuda:0")
+    w = synth.ffn_workload(name, M)
+    M, H, I = w.M, w.H, w.I
+    print(f"[bench] ffn inputs {w.desc}", file=sys.stderr, flush=True)
+    xb, (wg, wu, wd) = synth.make_ffn_inputs(w)
+    x = torch.from_numpy(xb.view(np.int16)).to(dev)
+    (gq, gs), (uq, us), (dq, ds) = (quantize_weights_gpu(torch.from_numpy(a).to(dev))
+                                    for a in (wg, wu, wd))
+    del wg, wu, wd
+    out = torch.empty((M, H), dtype=torch.bfloat16, device=dev)
+    ws = {v: fp8q.alloc_ffn_workspace(M, H, I, v) for v in (1, 2)}
+
+    def timed(fn, n=reps):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / n
+
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+
+    def timed_cold(fn, n=reps):
+        """median over n calls, each after a 512 MiB write that evicts L2 and
+        the 256 MB last-level cache (one layer's weights are not resident)"""
+        fn()
+        ts = []
+        for _ in range(n):
+            flush.fill_(1)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e3)
+        return float(np.median(ts))
+
+    flops = 6.0 * M * H * I
+    res = {"ffn": w.desc, "auto_variant": fp8q.fp8q_ffn_select(M, H, I)}
+    fns = {v: (lambda v=v: fp8q.fp8q_ffn(x, gq, gs, uq, us, dq, ds, out, ws[v], variant=v))
+           for v in (1, 2)}
+    cold = {1: [], 2: []}
+    for r in range(2 * reps + 2):  # alternating, so clock drift hits both variants
+        v = 1 + (r & 1)
+        t1 = timed_cold(fns[v], n=1)
+        if r >= 2:
+            cold[v].append(t1)
+    for v in (1, 2):
+        us_ = float(np.median(cold[v]))
+        res[f"variant{v}_cold_us"] = round(us_, 2)
+        res[f"variant{v}_cold_tflops"] = round(flops / us_ / 1e6, 1)
+        res[f"variant{v}_back_to_back_us"] = round(timed(fns[v]), 2)
+    # the pieces
+    Mp = fp8q.fp8q_m_pad(M)
+    xq = torch.empty((M, H), dtype=torch.uint8, device=dev)
+    xs = torch.empty((M, H // 128), dtype=torch.float32, device=dev)
+    xkm = torch.empty((H // 128, Mp), dtype=torch.float32, device=dev)
+    fp8q.fp8q_quant_act_kmajor(x, xq, xs, xkm)
+    hq = torch.empty((M, I), dtype=torch.uint8, device=dev)
+    hkm = torch.empty((I // 128, Mp), dtype=torch.float32, device=dev)
+    g = torch.empty((M, I), dtype=torch.bfloat16, device=dev)
+    u = torch.empty((M, I), dtype=torch.bfloat16, device=dev)
+    res["quant_x_us"] = round(timed(lambda: fp8q.fp8q_quant_act_kmajor(x, xq, xs, xkm)), 2)
+    t = timed(lambda: fp8q.fp8q_ffn_gate_up(xq, xkm, gq, gs, uq, us, hq, hkm))
+    res["gate_up_fused_us"] = round(t, 2)
+    res["gate_up_fused_tflops"] = round(4.0 * M * H * I / t / 1e6, 1)
+    res["gate_up_fused_frac_fp8_peak"] = round(4.0 * M * H * I / t / 1e6 / FP8_PEAK_TFLOPS, 4)
+    res["gate_gemm_us"] = round(timed(lambda: fp8q.fp8q_gemm_blockscaled(xq, xkm, gq, gs, g)), 2)
+    res["up_gemm_us"] = round(timed(lambda: fp8q.fp8q_gemm_blockscaled(xq, xkm, uq, us, u)), 2)
+    t = timed(lambda: fp8q.fp8q_silu_mul_quant(g, u, hq, hkm))
+    nbytes = 4 * M * I + M * I + 4 * Mp * (I // 128)
+    res["silu_mul_quant_us"] = round(t, 2)
+    res["silu_mul_quant_frac_hbm"] = round(nbytes / t / 1e3 / HBM_PEAK_GBS, 4)
+    fp8q.fp8q_ffn_gate_up(xq, xkm, gq, gs, uq, us, hq, hkm)
+    res["down_gemm_us"] = round(timed(lambda: fp8q.fp8q_gemm_blockscaled(hq, hkm, dq, ds, out)), 2)
+    res["down_kernel"] = fp8q.GEMM_KERNEL_NAMES[fp8q.fp8q_gemm_select(M, H, I)]
+    print(json.dumps(res), flush=True)
+
+
+def ffn_sweep(reps=15):
+    """fp8q_ffn variants 1 (fused gate/up) and 2 (separate) over M at H=5120,
+    I=17408: median time of the whole call over `reps` calls of each, the
+    two variants alternating, each call after a 512 MiB write that evicts L2
+    and the last-level cache; and whether the automatic choice is within 3%
+    of the faster variant."""
+    import torch
+    import synth
+    import w8a8_fp8_block_amd as fp8q
+    dev = torch.device("cuda:0")
+    base = synth.ffn_workload("ffn_prefill")
+    H, I = base.H, base.I
+    _, (wg, wu, wd) = synth.make_ffn_inputs(base, M=1)
+    (gq, gs), (uq, us), (dq, ds) = (quantize_weights_gpu(torch.from_numpy(a).to(dev))
+                                    for a in (wg, wu, wd))
+    del wg, wu, wd
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    for M in (16, 25, 32, 33, 48, 64, 80, 128, 256, 512, 1168, 2048, 4576):
+        xb, _ = synth.make_ffn_inputs(base, M=M, with_weights=False)
+        x = torch.from_numpy(xb.view(np.int16)).to(dev)
+        out = torch.empty((M, H), dtype=torch.bfloat16, device=dev)
+        ws = {v: fp8q.alloc_ffn_workspace(M, H, I, v) for v in (1, 2)}
+        ts = {1: [], 2: []}
+        for r in range(2 * reps):  # the variants alternate: clock drift hits both
+            v = 1 + (r & 1)
+            flush.fill_(1)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fp8q.fp8q_ffn(x, gq, gs, uq, us, dq, ds, out, ws[v], variant=v)
+            e1.record()
+            torch.cuda.synchronize()
+            if r >= 2:
+                ts[v].append(e0.elapsed_time(e1) * 1e3)
+        t = {v: float(np.median(ts[v])) for v in (1, 2)}
+        del ws
+        auto = fp8q.fp8q_ffn_select(M, H, I)
+        print(json.dumps({"M": M, "H": H, "I": I, "fused_us": round(t[1], 1),
+                          "separate_us": round(t[2], 1), "auto": "fused" if auto == 1 else "separate",
+                          "auto_tflops": round(6.0 * M * H * I / t[auto] / 1e6, 1),
+                          "rule_ok": t[auto] <= 1.03 * min(t[1], t[2])}), flush=True)
+
+
 def quantize_weights_gpu(wf, per_row=False):
     """Synthetic FP8 weights: per 128x128 block (or per row), scale = amax/448,
     codes by PyTorch's float8_e4m3fn cast (input preparation, outside the timed
@@ -241,6 +386,12 @@ def main():
         return
     if args.dequant:
         dequant_bench()
+        return
+    if args.ffn:
+        ffn_bench(args.ffn, args.M)
+        return
+    if args.ffn_sweep:
+        ffn_sweep()
         return
 
     import torch

@@ -41,6 +41,7 @@
 #ifndef FP8Q_H
 #define FP8Q_H
 
+#include <stddef.h>
 #include <stdint.h>
 #include <hip/hip_runtime_api.h>
 
@@ -292,6 +293,76 @@ fp8q_status fp8q_proj_rowscaled(const uint16_t *x_bf16, const uint8_t *w_e4m3,
                                 uint8_t *act_q_scratch, float *act_scale_scratch,
                                 float *act_scale_km_scratch, uint32_t M, uint32_t N,
                                 uint32_t K, hipStream_t stream);
+
+/* ------------------------------------------------------------ dense FFN */
+
+/* The dense FFN on FP8 weights (dispatch_proj.rs, doc of
+ * cublas_fp8_proj_prequant: the gate and up projections read the same
+ * [M,H] input, so it is quantized once for both; the post-SiLU intermediate
+ * is quantized once for down):
+ *   out = down( quant( h ) ),  h = bf16( silu(gate) * up ),
+ *   gate = bf16(quant(x) . Wg^T), up = bf16(quant(x) . Wu^T),
+ *   silu(g) = g / (1 + e^-g), evaluated in binary32.
+ * Weights are FP8 e4m3 with 128x128 block scales: w_gate and w_up [I,H]
+ * with scales [I/128, H/128], w_down [H,I] with scales [H/128, I/128].
+ * H % 128 == 0 and I % 128 == 0. */
+
+/* The intermediate from bf16 gate/up projections:
+ *   gate_bf16, up_bf16  [M,I] bf16, read only
+ *   h_e4m3              [M,I] out: codes of h quantized per (token,
+ *                       128-group) exactly as fp8q_quant_act quantizes
+ *   h_scale_km          [I/128, ceil16(M)] fp32 out: K-major scales, pad
+ *                       slots written 0 (as fp8q_scale_to_kmajor)
+ * Same conventions and errors as fp8q_quant_act. */
+fp8q_status fp8q_silu_mul_quant(const uint16_t *gate_bf16, const uint16_t *up_bf16,
+                                uint8_t *h_e4m3, float *h_scale_km, uint32_t M,
+                                uint32_t I, hipStream_t stream);
+
+/* Fused gate/up projection: one kernel computes both projections of the
+ * quantized input and writes the quantized intermediate; gate, up and h
+ * never reach memory in bf16.
+ *   x_e4m3, x_scale_km   [M,H] codes and [H/128, ceil16(M)] K-major scales
+ *                        (as from fp8q_quant_act_kmajor), read only
+ *   w_gate, w_gate_scale, w_up, w_up_scale   as above, read only
+ *   h_e4m3, h_scale_km   as for fp8q_silu_mul_quant
+ * The result is bit-identical to fp8q_gemm_blockscaled for gate and for up
+ * followed by fp8q_silu_mul_quant.  Errors as fp8q_gemm_blockscaled. */
+fp8q_status fp8q_ffn_gate_up(const uint8_t *x_e4m3, const float *x_scale_km,
+                             const uint8_t *w_gate, const float *w_gate_scale,
+                             const uint8_t *w_up, const float *w_up_scale,
+                             uint8_t *h_e4m3, float *h_scale_km, uint32_t M,
+                             uint32_t H, uint32_t I, hipStream_t stream);
+
+/* Variant fp8q_ffn takes with variant 0: 1 (fused gate/up kernel) for
+ * M >= 33, 2 (separate gate and up GEMMs, then fp8q_silu_mul_quant) below;
+ * -1 if H or I is not a positive multiple of 128.  Pure host function. */
+int fp8q_ffn_select(uint32_t M, uint32_t H, uint32_t I);
+
+/* Bytes of device workspace fp8q_ffn needs for (M, H, I, variant); 0 for an
+ * invalid variant or shape.  Variant 2 also holds the bf16 gate and up
+ * outputs (4*M*I bytes more). */
+size_t fp8q_ffn_workspace_bytes(uint32_t M, uint32_t H, uint32_t I, int variant);
+
+/* The whole FFN:
+ *   x_bf16           [M,H] bf16, read only
+ *   weights          as above, read only
+ *   out_bf16         [M,H] bf16 out
+ *   workspace        device memory of >= fp8q_ffn_workspace_bytes(M,H,I,
+ *                    variant) bytes, 16-byte aligned; holds the x codes and
+ *                    scales, the intermediate's codes and scales (and for
+ *                    variant 2 gate and up) afterwards
+ *   variant          0 auto (fp8q_ffn_select), 1 fused gate/up, 2 separate;
+ *                    both give bit-identical results
+ * Launches: the quantizer (and the scale relayout beyond 2^17 scale groups,
+ * as fp8q_proj), the gate/up stage, the down GEMM; all on `stream`.
+ * Errors: FP8Q_ERR_SHAPE also for a short workspace; FP8Q_ERR_VARIANT for a
+ * variant outside 0..2; otherwise as fp8q_proj. */
+fp8q_status fp8q_ffn(const uint16_t *x_bf16, const uint8_t *w_gate,
+                     const float *w_gate_scale, const uint8_t *w_up,
+                     const float *w_up_scale, const uint8_t *w_down,
+                     const float *w_down_scale, uint16_t *out_bf16, void *workspace,
+                     size_t workspace_bytes, uint32_t M, uint32_t H, uint32_t I,
+                     int variant, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -158,3 +158,57 @@ def test_gemm_bf16_validation():
     assert L.fp8q_gemm_bf16(g, g, BAD, 4, 128, 128, None) == 3
     assert L.fp8q_gemm_bf16(g, g, g, 0, 128, 128, None) == 0
     assert L.fp8q_gemm_bf16(None, None, None, 1 << 16, 128, 1 << 15, None) == 2  # M*K*2 >= 2^32
+
+
+def test_ffn_select_and_workspace():
+    assert fp8q.fp8q_ffn_select(16, 5120, 17408) == 2
+    assert fp8q.fp8q_ffn_select(32, 5120, 17408) == 2
+    assert fp8q.fp8q_ffn_select(33, 5120, 17408) == 1
+    assert fp8q.fp8q_ffn_select(64, 5120, 17408) == 1
+    assert fp8q.fp8q_ffn_select(4576, 5120, 17408) == 1
+    assert fp8q.fp8q_ffn_select(16, 5000, 17408) == -1
+    M, H, I = 4576, 5120, 17408
+    Mp = fp8q.fp8q_m_pad(M)
+
+    def a256(v):
+        return (v + 255) // 256 * 256
+
+    base = (a256(M * H) + a256(M * H // 128 * 4) + a256(Mp * H // 128 * 4) + a256(M * I)
+            + a256(Mp * I // 128 * 4))
+    assert fp8q.fp8q_ffn_workspace_bytes(M, H, I, 1) == base
+    assert fp8q.fp8q_ffn_workspace_bytes(M, H, I, 2) == base + 2 * a256(2 * M * I)
+    assert fp8q.fp8q_ffn_workspace_bytes(M, H, I, 0) == base
+    assert fp8q.fp8q_ffn_workspace_bytes(16, H, I, 0) == fp8q.fp8q_ffn_workspace_bytes(16, H, I, 2)
+    assert fp8q.fp8q_ffn_workspace_bytes(33, H, I, 0) == fp8q.fp8q_ffn_workspace_bytes(33, H, I, 1)
+    assert fp8q.fp8q_ffn_workspace_bytes(M, H, I, 3) == 0
+    assert fp8q.fp8q_ffn_workspace_bytes(M, 100, I, 1) == 0
+
+
+def test_ffn_validation():
+    L = fp8q.lib()
+    g = GOOD
+    w = [g] * 6
+    # fp8q_silu_mul_quant
+    assert L.fp8q_silu_mul_quant(g, g, g, g, 4, 100, None) == 2
+    assert L.fp8q_silu_mul_quant(g, None, g, g, 4, 128, None) == 1
+    assert L.fp8q_silu_mul_quant(g, g, BAD, g, 4, 128, None) == 3
+    assert L.fp8q_silu_mul_quant(g, g, g, g, 0, 128, None) == 0
+    # fp8q_ffn_gate_up
+    assert L.fp8q_ffn_gate_up(g, g, g, g, g, g, g, g, 4, 100, 256, None) == 2
+    assert L.fp8q_ffn_gate_up(g, g, g, g, g, g, g, g, 4, 256, 200, None) == 2
+    assert L.fp8q_ffn_gate_up(g, g, g, g, None, g, g, g, 4, 256, 256, None) == 1
+    assert L.fp8q_ffn_gate_up(g, g, g, g, g, g, g, BAD, 4, 256, 256, None) == 3
+    assert L.fp8q_ffn_gate_up(g, g, g, g, g, g, g, g, 0, 256, 256, None) == 0
+    assert L.fp8q_ffn_gate_up(g, g, g, g, g, g, g, g, 1 << 16, 1 << 16, 256, None) == 2
+    # fp8q_ffn
+    need = fp8q.fp8q_ffn_workspace_bytes(8, 256, 384, 1)
+    assert L.fp8q_ffn(g, *w, g, g, need, 8, 256, 384, 3, None) == 6
+    assert L.fp8q_ffn(g, *w, g, g, need, 8, 256, 384, -1, None) == 6
+    assert L.fp8q_ffn(g, *w, g, g, need, 8, 250, 384, 0, None) == 2
+    assert L.fp8q_ffn(g, g, g, g, g, None, g, g, g, need, 8, 256, 384, 0, None) == 1
+    assert L.fp8q_ffn(g, *w, BAD, g, need, 8, 256, 384, 0, None) == 3
+    assert L.fp8q_ffn(g, *w, g, None, need, 8, 256, 384, 1, None) == 1
+    assert L.fp8q_ffn(g, *w, g, g, need - 1, 8, 256, 384, 1, None) == 2
+    assert b"workspace" in L.fp8q_last_error()
+    assert L.fp8q_ffn(g, *w, g, g, need, 8, 256, 384, 2, None) == 2  # variant 2 needs more
+    assert L.fp8q_ffn(g, *w, g, None, 0, 0, 256, 384, 0, None) == 0  # M == 0: nothing to do

@@ -14,6 +14,10 @@ Names match the C entry points:
   fp8q_scale_to_kmajor(scale_rm, scale_km)
   fp8q_gemm_blockscaled(a, a_scale_km, w, w_scale, out, kernel=0)
   fp8q_proj(x, w, w_scale, out, act_q, act_scale, act_scale_km)
+  fp8q_silu_mul_quant(gate, up, h, h_scale_km)
+  fp8q_ffn_gate_up(x_q, x_scale_km, w_gate, w_gate_scale, w_up, w_up_scale, h, h_scale_km)
+  fp8q_ffn(x, w_gate, w_gate_scale, w_up, w_up_scale, w_down, w_down_scale, out,
+           workspace, variant=0)
   fp8q_m_pad(m), fp8q_quant_select(M, K, cu_count), ...
 
 Dtypes: bf16 tensors may be torch.bfloat16 or torch.uint16/int16 views;
@@ -70,6 +74,11 @@ _SIGS = {
     "fp8q_proj_rowscaled": (_I, [_P, _P, _P, _P, _P, _P, _P, _U, _U, _U, _P]),
     "fp8q_dequant_fp8_bf16": (_I, [_P, _P, _P, _U, _U, _I, _P]),
     "fp8q_gemm_bf16": (_I, [_P, _P, _P, _U, _U, _U, _P]),
+    "fp8q_silu_mul_quant": (_I, [_P, _P, _P, _P, _U, _U, _P]),
+    "fp8q_ffn_gate_up": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _U, _U, _U, _P]),
+    "fp8q_ffn_select": (_I, [_U, _U, _U]),
+    "fp8q_ffn_workspace_bytes": (ctypes.c_size_t, [_U, _U, _U, _I]),
+    "fp8q_ffn": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _U, _U, _U, _I, _P]),
 }
 
 _lib = None
@@ -215,6 +224,52 @@ def fp8q_gemm_bf16(x, w, out, stream=None):
     _check(lib().fp8q_gemm_bf16(_ptr(x), _ptr(w), _ptr(out), M, N, K, _stream(stream)))
 
 
+def fp8q_silu_mul_quant(gate, up, h, h_scale_km, stream=None):
+    """FFN intermediate h = bf16(silu(gate) * up) of bf16 gate/up [M,I],
+    quantized: codes h [M,I], K-major scales h_scale_km [I/128, ceil16(M)]."""
+    M, I = _dims(gate, 2)
+    if _dims(up, 2) != (M, I):
+        raise ValueError("gate and up differ in shape")
+    _check(lib().fp8q_silu_mul_quant(_ptr(gate), _ptr(up), _ptr(h), _ptr(h_scale_km), M, I,
+                                    _stream(stream)))
+
+
+def fp8q_ffn_gate_up(x_q, x_scale_km, w_gate, w_gate_scale, w_up, w_up_scale, h, h_scale_km,
+                     stream=None):
+    """Fused gate/up projection of quantized x [M,H] with weights [I,H] to the
+    quantized intermediate h [M,I] and its K-major scales."""
+    M, H = _dims(x_q, 2)
+    I, H2 = _dims(w_gate, 2)
+    if H2 != H or _dims(w_up, 2) != (I, H):
+        raise ValueError("x, w_gate and w_up disagree in shape")
+    _check(lib().fp8q_ffn_gate_up(_ptr(x_q), _ptr(x_scale_km), _ptr(w_gate), _ptr(w_gate_scale),
+                                 _ptr(w_up), _ptr(w_up_scale), _ptr(h), _ptr(h_scale_km), M, H, I,
+                                 _stream(stream)))
+
+
+def fp8q_ffn_select(M: int, H: int, I: int) -> int:
+    """Variant fp8q_ffn runs with variant=0: 1 fused gate/up, 2 separate."""
+    return int(lib().fp8q_ffn_select(M, H, I))
+
+
+def fp8q_ffn_workspace_bytes(M: int, H: int, I: int, variant: int = 0) -> int:
+    return int(lib().fp8q_ffn_workspace_bytes(M, H, I, variant))
+
+
+def fp8q_ffn(x, w_gate, w_gate_scale, w_up, w_up_scale, w_down, w_down_scale, out, workspace,
+             variant: int = 0, stream=None):
+    """The dense FFN: out [M,H] = down(quant(bf16(silu(gate) * up))) of x [M,H];
+    workspace: a device byte tensor of fp8q_ffn_workspace_bytes(M, H, I, variant)."""
+    M, H = _dims(x, 2)
+    I, H2 = _dims(w_gate, 2)
+    if H2 != H or _dims(w_up, 2) != (I, H) or _dims(w_down, 2) != (H, I):
+        raise ValueError("x and the weights disagree in shape")
+    _check(lib().fp8q_ffn(_ptr(x), _ptr(w_gate), _ptr(w_gate_scale), _ptr(w_up), _ptr(w_up_scale),
+                         _ptr(w_down), _ptr(w_down_scale), _ptr(out), _ptr(workspace),
+                         workspace.numel() * workspace.element_size(), M, H, I, variant,
+                         _stream(stream)))
+
+
 def fp8q_default_select_params(cu_count: int) -> SelectParams:
     return lib().fp8q_default_select_params(cu_count)
 
@@ -247,7 +302,8 @@ def fp8q_proj_quant_fused(M: int, K: int) -> bool:
 
 GEMM_KERNEL_NAMES = {1: "gemm_tiled_kernel<128,128,2,2,2>", 2: "gemm_skinny_kernel",
                      3: "gemm_tiled_kernel<256,128,4,2,3>", 4: "gemm_tiled_kernel<256,128,2,2,3>",
-                     5: "gemm_pp_kernel<3>"}
+                     5: "gemm_pp_kernel<3,false,false>"}
+FFN_GATE_UP_KERNEL_NAME = "gemm_pp_kernel<3,false,true>"
 
 
 def fp8q_quant_b_min_m(K: int, params: SelectParams) -> int:
@@ -267,3 +323,12 @@ def alloc_proj_scratch(M: int, K: int, device="cuda"):
     return (torch.empty((M, K), dtype=torch.uint8, device=device),
             torch.empty((M, G), dtype=torch.float32, device=device),
             torch.empty((G, fp8q_m_pad(M)), dtype=torch.float32, device=device))
+
+
+def alloc_ffn_workspace(M: int, H: int, I: int, variant: int = 0, device="cuda"):
+    """Device byte tensor sized for fp8q_ffn(M, H, I, variant)."""
+    import torch
+    n = fp8q_ffn_workspace_bytes(M, H, I, variant)
+    if n == 0:
+        raise ValueError("invalid FFN shape or variant")
+    return torch.empty((n,), dtype=torch.uint8, device=device)

@@ -68,6 +68,22 @@ hipError_t launch_gemm_bf16(const uint16_t* x, const uint16_t* w, uint16_t* out,
 hipError_t launch_dequant(const uint8_t* w, const float* scale, uint16_t* dst, uint32_t N,
                           uint32_t K, bool per_row, hipStream_t s);
 
+// FFN intermediate: h = bf16(silu(gate) * up) for bf16 gate/up [M,I], then
+// quantized per (token, 128-group): codes [M,I] and K-major scales
+// [I/128, ceil16(M)] with the pad slots zeroed.
+hipError_t launch_silu_mul_quant(const uint16_t* gate, const uint16_t* up, uint8_t* q,
+                                 float* scale_km, uint32_t M, uint32_t I, hipStream_t s);
+
+// Fused gate/up projection of the dense FFN: x codes [M,H] with K-major
+// scales [H/128, ceil16(M)], gate and up weights [I,H] with block scales
+// [I/128, H/128] -> the intermediate's codes [M,I] and K-major scales
+// [I/128, ceil16(M)] (pad slots zeroed), equal to launch_silu_mul_quant of
+// the two bf16 projections.  I % 128 == 0, H % 128 == 0.
+hipError_t launch_ffn_gate_up(const uint8_t* x, const float* x_s_km, const uint8_t* w_gate,
+                              const float* ws_gate, const uint8_t* w_up, const float* ws_up,
+                              uint8_t* hq, float* hs_km, uint32_t M, uint32_t H, uint32_t I,
+                              hipStream_t s);
+
 inline uint32_t m_pad16(uint32_t m) { return (m + 15u) / 16u * 16u; }
 
 }  // namespace fp8q

@@ -17,6 +17,7 @@
 // operands, so both see the same K permutation and the dot product is the
 // full 128-term sum whatever order the hardware assigns to those bytes.
 #include "mfma_common.h"
+#include "quant_common.h"
 
 namespace fp8q {
 namespace {
@@ -304,45 +305,176 @@ hipError_t launch_tiled_cfg(const uint8_t* a, const float* a_s_km, const uint8_t
 //
 // Direct loads: a stage is 48 1-KB operand chunks (chunk c at LDS offset
 // c*1024: activation rows 8c..8c+7 for c < 32, weight rows 8(c-32).. after)
-// plus every wave's scales.  Each wave issues 6 chunks and its own two scale
-// loads at the end of its read phase, so the compute phases hold nothing but
-// MFMAs and promotions and the texture unit gets 24 KB per phase.  Stage s
+// plus every wave's scales.  Each wave issues 8 loads per block at the end
+// of its read phase (group 0: 8 operand chunks; group 1: 4 chunks and the
+// scales of two waves), so the texture unit gets 32 or 16 KB per phase and
+// the compute phases hold nothing but MFMAs and promotions.  Stage s
 // (block min(s, G-1): stages past the last block reload it, in bounds and
 // never read) goes to slot s % STAGES.  Before the phase-A barrier of block
 // kb each wave waits for its own part of stage kb+1.
+//
+// FFN mode (the dense FFN's fused gate/up projection): the workgroup tile is
+// 128 token rows by 256 weight rows, the 128 gate rows n0.. and the 128 up
+// rows n0.. of one intermediate column block; group 0 computes gate and group
+// 1 up, wave for wave on the same 64x64 output positions, and the epilogue
+// forms h = bf16(silu(bf16 gate) * bf16 up), quantizes it per (token,
+// 128-group) and writes the codes and the K-major scales (see
+// ffn_epilogue).  The main loop is the same code with the weight chunks
+// read from two sources.
 // ------------------------------------------------------------------------
-template <int STAGES, bool ROW = false>
+template <int STAGES, bool ROW = false, bool FFN = false>
 struct PpCfg {
-  static constexpr int BM = 256, BN = 128, NW = 8, NT = 512;
+  static constexpr int BM = FFN ? 128 : 256, BN = FFN ? 256 : 128, NW = 8, NT = 512;
   static constexpr int WM = 64, WN = 64, TM = 4, TN = 4, NP = 16;
   static constexpr int A_BYTES = BM * 128, W_BYTES = BN * 128;
   static constexpr int SCW_BYTES = 512;  // per wave: 64 activation scales + 64 weight-scale copies
   static constexpr int STAGE_BYTES = A_BYTES + W_BYTES + NW * SCW_BYTES;
   static constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
   static constexpr int CHUNKS = (A_BYTES + W_BYTES) / 1024;  // 48
-  static constexpr int CW = CHUNKS / NW;                      // 6 operand chunks per wave
-  static constexpr int LW = CW + (ROW ? 1 : 2);               // + own scales: loads per wave and stage
-  static_assert(CHUNKS % NW == 0 && 2 * LW < 64, "vmcnt range");
+  // loads per wave and stage: group 0 eight operand chunks; group 1 four
+  // operand chunks and the scales of itself and of its group-0 partner
+  static constexpr int CH0 = 8, CH1 = 4;
+  static constexpr int LW0 = CH0, LW1 = CH1 + 2 * (ROW ? 1 : 2);
+  static_assert(4 * (CH0 + CH1) == CHUNKS && 2 * LW1 < 64, "chunk split, vmcnt range");
   static_assert(LDS_BYTES <= 160 * 1024 && STAGES == 3, "config");
 };
 
-template <int STAGES, bool ROW>
+// Second weight operand and outputs of the FFN mode: W/Ws are the gate
+// weights and their block scales, these the up weights and scales, the
+// intermediate's codes [M,N] and its K-major scales [N/128, Mp].
+struct FfnArgs {
+  const uint8_t* w_up;
+  const float* ws_up;
+  uint8_t* hq;
+  float* hs;
+};
+
+// FFN-mode epilogue, after the main loop (all direct loads of this wave
+// complete).  Gate wave gw (group 0) and up wave gw (group 1, wave gw + 4)
+// hold the same 64x64 output positions in the same registers; they split
+// the rows: the gate wave finishes rows tm = 0, 1 of its band, the up wave
+// rows tm = 2, 3.
+//   1. each wave rounds its accumulators to bf16 (the projections' output
+//      format) and parks the half its partner finishes in LDS;
+//   2. each wave forms h = bf16(silu(g) * u) for its rows (silu_mul_f32, the
+//      same code as the standalone intermediate kernel) and the maximum |h|
+//      of each row over its 64 columns (integer max of bf16 magnitudes:
+//      within a lane, then across the 4 lanes of a row);
+//   3. the two waves of a group covering columns 0-63 and 64-127 of the
+//      128-column group combine their row maxima through LDS; scale =
+//      amax/448 and the codes of h / scale follow the activation quantizer's
+//      exact steps (quotients, encode4).  Codes of rows < M are stored; the
+//      wave on columns 0-63 stores the K-major scales of its rows < M and
+//      zeros for pad rows M .. Mp-1.
+// Every wave passes the same three workgroup barriers, each after its own LDS
+// writes have completed (s_barrier alone does not wait for them).
+template <int TM, int TN>
+__device__ __forceinline__ void ffn_epilogue(const v4f (&acc)[TM][TN], uint8_t* smem,
+                                             const FfnArgs& ffn, uint32_t wave, uint32_t lane,
+                                             uint32_t mrow0, uint32_t ncol0, uint32_t nb,
+                                             uint32_t M, uint32_t N, uint32_t Mp) {
+  static_assert(TM == 4 && TN == 4, "64x64 wave tile");
+  uint32_t* park = reinterpret_cast<uint32_t*>(smem);                // [8][4][64][4] u32: 32 KB
+  uint32_t* rmax = reinterpret_cast<uint32_t*>(smem + 32 * 1024);    // [8][2][16] u32
+  const uint32_t l16 = lane & 15, q4 = lane >> 4;
+  const bool up = wave >= 4;
+  auto lds_barrier = [] {
+    wait_lgkm0();
+    wg_barrier();
+  };
+  lds_barrier();  // every wave is done with the operand ring
+  // 1. park the partner's half: tiles of rows tm = 0, 1 (up waves) or 2, 3
+  //    (gate waves), two 16x16 tiles per 16-byte slot
+#pragma unroll
+  for (int t2 = 0; t2 < 4; ++t2) {
+    const int t = 2 * t2;  // tile index within the half
+    const uint2 a = up ? pack_bf16x4(acc[t / TN][t % TN]) : pack_bf16x4(acc[2 + t / TN][t % TN]);
+    const uint2 b = up ? pack_bf16x4(acc[(t + 1) / TN][(t + 1) % TN])
+                       : pack_bf16x4(acc[2 + (t + 1) / TN][(t + 1) % TN]);
+    *reinterpret_cast<uint4*>(park + ((wave * 4 + t2) * 64 + lane) * 4) = make_uint4(a.x, a.y, b.x, b.y);
+  }
+  lds_barrier();
+  // 2. h for this wave's rows
+  const uint32_t partner = wave ^ 4;
+  uint32_t hb[2][TN][2];  // h as packed bf16 pairs: rows i = 0, 1 of this wave's half
+  uint32_t amax[2];
+#pragma unroll
+  for (int t2 = 0; t2 < 4; ++t2) {
+    const uint4 pp = *reinterpret_cast<const uint4*>(park + ((partner * 4 + t2) * 64 + lane) * 4);
+    const uint32_t pw[4] = {pp.x, pp.y, pp.z, pp.w};
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int t = 2 * t2 + h, i = t / TN, tn = t % TN;
+      const uint2 own = up ? pack_bf16x4(acc[2 + i][tn]) : pack_bf16x4(acc[i][tn]);
+      const uint32_t ow[2] = {own.x, own.y};
+#pragma unroll
+      for (int d = 0; d < 2; ++d) {
+        const uint32_t g2 = up ? pw[2 * h + d] : ow[d], u2 = up ? ow[d] : pw[2 * h + d];
+        const float lo = silu_mul_f32(__uint_as_float(g2 << 16), __uint_as_float(u2 << 16));
+        const float hi = silu_mul_f32(__uint_as_float(g2 & 0xFFFF0000u), __uint_as_float(u2 & 0xFFFF0000u));
+        hb[i][tn][d] = bf16_bits_rne(lo) | (bf16_bits_rne(hi) << 16);
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    uint32_t mx = 0;
+#pragma unroll
+    for (int tn = 0; tn < TN; ++tn) {
+      const uint32_t a = hb[i][tn][0] & 0x7FFF7FFFu, b = hb[i][tn][1] & 0x7FFF7FFFu;
+      mx = max(mx, max(max(a & 0xFFFFu, a >> 16), max(b & 0xFFFFu, b >> 16)));
+    }
+    mx = max(mx, (uint32_t)__shfl_xor((int)mx, 16));
+    mx = max(mx, (uint32_t)__shfl_xor((int)mx, 32));
+    amax[i] = mx;
+    if (q4 == 0) rmax[(wave * 2 + i) * 16 + l16] = mx;
+  }
+  lds_barrier();
+  // 3. scales and codes
+  const uint32_t mate = wave ^ 1;  // the other 64 columns of the 128-column group
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const uint32_t a = max(amax[i], rmax[(mate * 2 + i) * 16 + l16]);
+    const float sc = group_scale(a);
+    float x[16], q[16];
+#pragma unroll
+    for (int tn = 0; tn < TN; ++tn) {
+      x[4 * tn + 0] = __uint_as_float(hb[i][tn][0] << 16);
+      x[4 * tn + 1] = __uint_as_float(hb[i][tn][0] & 0xFFFF0000u);
+      x[4 * tn + 2] = __uint_as_float(hb[i][tn][1] << 16);
+      x[4 * tn + 3] = __uint_as_float(hb[i][tn][1] & 0xFFFF0000u);
+    }
+    quotients<16>(x, sc, q);
+    const uint32_t m = mrow0 + ((up ? 2 : 0) + i) * 16 + l16;
+    if (m < M) {
+#pragma unroll
+      for (int tn = 0; tn < TN; ++tn)
+        *reinterpret_cast<uint32_t*>(ffn.hq + (uint64_t)m * N + ncol0 + tn * 16 + 4 * q4) =
+            encode4(q + 4 * tn);
+    }
+    if ((wave & 1) == 0 && q4 == 0 && m < Mp) ffn.hs[(uint64_t)nb * Mp + m] = (m < M) ? sc : 0.0f;
+  }
+}
+
+template <int STAGES, bool ROW, bool FFN>
 __global__ __launch_bounds__(512) void gemm_pp_kernel(
     const uint8_t* __restrict__ A, const float* __restrict__ As, const uint8_t* __restrict__ W,
     const float* __restrict__ Ws, uint16_t* __restrict__ out, uint32_t M, uint32_t N, uint32_t K,
-    uint32_t Mp, uint32_t tiles_m, uint32_t tiles_n) {
-  using C = PpCfg<STAGES, ROW>;
-  constexpr int TM = C::TM, TN = C::TN, NP = C::NP, BM = C::BM, BN = C::BN, CW = C::CW, LW = C::LW;
+    uint32_t Mp, uint32_t tiles_m, uint32_t tiles_n, FfnArgs ffn) {
+  using C = PpCfg<STAGES, ROW, FFN>;
+  constexpr int TM = C::TM, TN = C::TN, NP = C::NP, BM = C::BM, BN = C::BN;
+  constexpr int CH0 = C::CH0, CH1 = C::CH1, LW0 = C::LW0, LW1 = C::LW1;
   extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
 
   const uint32_t tid = threadIdx.x, lane = tid & 63;
   const uint32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const uint32_t grp = wave >> 2, gw = wave & 3;
-  const uint32_t wm = 2 * grp + (gw >> 1), wn = gw & 1;
+  const uint32_t wm = FFN ? gw >> 1 : 2 * grp + (gw >> 1);
+  const uint32_t wn = FFN ? 2 * grp + (gw & 1) : gw & 1;
 
   uint32_t tmi, tni;  // this workgroup's tile (XCD-aware, grouped order)
   tile_coords(tiles_m, tiles_n, tmi, tni);
-  const uint32_t m0 = tmi * BM, n0 = tni * BN;
+  const uint32_t m0 = tmi * BM, n0 = tni * (FFN ? kGroup : BN);
   const uint32_t G = K / kGroup;
   const uint32_t nb = n0 / kGroup;
 
@@ -350,36 +482,76 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(
   const __amdgpu_buffer_rsrc_t rW = make_rsrc(W, N * K);
   const __amdgpu_buffer_rsrc_t rS = make_rsrc(As, G * Mp * 4);
   const __amdgpu_buffer_rsrc_t rWs = make_rsrc(Ws, ROW ? N * 4 : (N / kGroup) * G * 4);
-  // this wave's operand chunks wave*CW + j: source resource and per-lane offset
-  uint32_t c_off[CW];
-  bool c_act[CW];
+  // FFN mode: the up weights and their scales
+  const __amdgpu_buffer_rsrc_t rW2 = FFN ? make_rsrc(ffn.w_up, N * K) : rW;
+  const __amdgpu_buffer_rsrc_t rWs2 = FFN ? make_rsrc(ffn.ws_up, (N / kGroup) * G * 4) : rWs;
+
+  // Operand chunks of this wave (LDS chunk c covers 8 rows of 128 bytes:
+  // activations first, then weights; FFN mode: activations 0-15, gate
+  // 16-31, up 32-47).  A wave may only overwrite, in its read phase, LDS
+  // rows that no other wave of its own group reads:
+  //   group 1 (loads in phase A, right after its own reads of block kb):
+  //     four chunks that only group 0 reads -- activation rows 0-127 (plain)
+  //     or the gate rows (FFN) -- and the scales of itself and of its
+  //     group-0 partner wave gw, which only their owners read;
+  //   group 0 (loads in phase B, after the phase-A barrier, when both groups
+  //     are done with block kb): the other 32 chunks, eight per wave.
+  uint32_t c_off[CH0], c_lds[CH0];
+  const bool g0_act = !FFN && gw < 2;  // plain group 0: activation rows 128-255 (gw 0, 1) or weights
 #pragma unroll
-  for (int j = 0; j < CW; ++j) {
-    const uint32_t c = wave * CW + j;
-    const uint32_t ch = (c < (uint32_t)C::A_BYTES / 1024) ? c : c - C::A_BYTES / 1024;
-    const uint32_t e = ch * 64 + lane, row = e >> 3;  // row within the operand tile
-    c_act[j] = c < (uint32_t)C::A_BYTES / 1024;
-    c_off[j] = c_act[j] ? min(m0 + row, M - 1) * K + ((e & 7) ^ swz(row)) * 16
-                        : (n0 + row) * K + ((e & 7) ^ swz(row)) * 16;
+  for (int j = 0; j < CH0; ++j) {
+    uint32_t c, ch;  // LDS chunk, chunk within its operand
+    bool act;
+    if (grp) {
+      c = (FFN ? 16 : 0) + 4 * gw + (j & 3);
+      ch = 4 * gw + (j & 3);
+      act = !FFN;
+    } else if constexpr (FFN) {
+      c = (j < 4) ? 4 * gw + j : 32 + 4 * gw + (j - 4);
+      ch = 4 * gw + (j & 3);
+      act = j < 4;
+    } else {
+      c = 16 + 8 * gw + j;
+      ch = g0_act ? c : c - 32;
+      act = g0_act;
+    }
+    const uint32_t row = ch * 8 + (lane >> 3), col = lane & 7;  // row within the operand
+    c_lds[j] = c;
+    c_off[j] = act ? min(m0 + row, M - 1) * K + (col ^ swz(row)) * 16
+                   : (n0 + row) * K + (col ^ swz(row)) * 16;  // swz: low 4 bits of the LDS row
   }
-  const uint32_t s_off = min(m0 + wm * C::WM + lane, Mp - 1) * 4;  // own activation scales
+  const uint32_t s_off = min(m0 + wm * C::WM + lane, Mp - 1) * 4;       // own activation scales
+  const uint32_t s_off_p = min(m0 + (gw >> 1) * C::WM + lane, Mp - 1) * 4;  // partner's (group 1)
   const uint32_t ws_off = nb * G * 4;
   const uint32_t my_sc = C::A_BYTES + C::W_BYTES + wave * C::SCW_BYTES;
+  const uint32_t p_sc = C::A_BYTES + C::W_BYTES + gw * C::SCW_BYTES;
 
-  // direct load number J (0 .. LW-1) of this wave for block kb into slot `stage`
-  auto issue_one = [&](auto jc, uint32_t kb, uint32_t stage) {
-    constexpr int J = decltype(jc)::value;
+  auto issue_g0 = [&](uint32_t kb, uint32_t stage) {
     uint8_t* base = smem + stage * C::STAGE_BYTES;
-    if constexpr (J < CW) {
-      dma16(c_act[J] ? rA : rW, c_off[J], kb * kGroup, base + (wave * CW + J) * 1024);
-    } else if constexpr (J == CW) {
-      dma4(rS, s_off, kb * Mp * 4, base + my_sc);
-    } else if constexpr (!ROW) {
-      dma4(rWs, ws_off, kb * 4, base + my_sc + 256);
-    }
+    unroll_seq(
+        [&](auto jc) {
+          constexpr int J = decltype(jc)::value;
+          if constexpr (FFN)
+            dma16(J < 4 ? rA : rW2, c_off[J], kb * kGroup, base + c_lds[J] * 1024);
+          else
+            dma16(g0_act ? rA : rW, c_off[J], kb * kGroup, base + c_lds[J] * 1024);
+        },
+        std::make_integer_sequence<int, CH0>{});
   };
-  auto issue_stage = [&](uint32_t kb, uint32_t stage) {
-    unroll_seq([&](auto jc) { issue_one(jc, kb, stage); }, std::make_integer_sequence<int, LW>{});
+  auto issue_g1 = [&](uint32_t kb, uint32_t stage) {
+    uint8_t* base = smem + stage * C::STAGE_BYTES;
+    unroll_seq(
+        [&](auto jc) {
+          constexpr int J = decltype(jc)::value;
+          dma16(FFN ? rW : rA, c_off[J], kb * kGroup, base + c_lds[J] * 1024);
+        },
+        std::make_integer_sequence<int, CH1>{});
+    dma4(rS, s_off, kb * Mp * 4, base + my_sc);
+    dma4(rS, s_off_p, kb * Mp * 4, base + p_sc);
+    if constexpr (!ROW) {
+      dma4(FFN ? rWs2 : rWs, ws_off, kb * 4, base + my_sc + 256);  // up scales in FFN mode
+      dma4(rWs, ws_off, kb * 4, base + p_sc + 256);
+    }
   };
 
   const uint32_t l16 = lane & 15, c0 = 2 * (lane >> 4);
@@ -445,36 +617,42 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(
   // Each group runs its own loop (one straight-line body each, so no value
   // is live across a merge of the two roles); both execute the same
   // sequence of workgroup barriers.  Every wave issues its part of stages
-  // 0 .. STAGES-1 up front and its part of stage kb+STAGES in its read phase
-  // of the iteration in which the slot of block kb has been read by both
-  // groups (group 1: after its own reads of block kb in phase A; group 0:
-  // in phase B, after its reads of block kb+1).
-#pragma unroll
-  for (int s = 0; s < STAGES; ++s) issue_stage(min((uint32_t)s, G - 1), s);
+  // 0 .. STAGES-1 up front and its part of stage kb+STAGES (slot kb %
+  // STAGES) in its read phase of iteration kb: group 1 in phase A, after its
+  // own reads of block kb, only rows that group 0 alone reads (group 0 read
+  // them one phase earlier); group 0 in phase B, after the phase-A barrier,
+  // when both groups are done with block kb.  (A group-1 load of rows that
+  // another group-1 wave reads could overwrite them before that wave has
+  // read them: the direct loads land within a few hundred cycles when the
+  // operands sit in L2.)
   if (grp == 0) {
-    wait_vmcnt<(STAGES - 1) * LW>();  // own part of stage 0
+#pragma unroll
+    for (int s = 0; s < STAGES; ++s) issue_g0(min((uint32_t)s, G - 1), s);
+    wait_vmcnt<(STAGES - 1) * LW0>();  // own part of stage 0
     wg_barrier();
     read_block(0);
     wait_lgkm0();
     wg_barrier();
     for (uint32_t kb = 0; kb < G; ++kb) {
-      compute_block();   // phase A
-      wait_vmcnt<LW>();  // own part of stage kb+1 (that of kb+2 may be in flight)
+      compute_block();    // phase A
+      wait_vmcnt<LW0>();  // own part of stage kb+1 (that of kb+2 may be in flight)
       wg_barrier();
       read_block(kb + 1);  // phase B (block G: a reloaded copy of the last block, unused)
       wait_lgkm0();
-      issue_stage(min(kb + STAGES, G - 1), kb % STAGES);
+      issue_g0(min(kb + STAGES, G - 1), kb % STAGES);
       wg_barrier();
     }
   } else {
-    wait_vmcnt<(STAGES - 1) * LW>();  // own part of stage 0
+#pragma unroll
+    for (int s = 0; s < STAGES; ++s) issue_g1(min((uint32_t)s, G - 1), s);
+    wait_vmcnt<(STAGES - 1) * LW1>();  // own part of stage 0
     wg_barrier();
     wg_barrier();
     for (uint32_t kb = 0; kb < G; ++kb) {
       read_block(kb);  // phase A
       wait_lgkm0();
-      issue_stage(min(kb + STAGES, G - 1), kb % STAGES);
-      wait_vmcnt<2 * LW>();  // own part of stage kb+1 (kb+2, kb+3 may be in flight)
+      issue_g1(min(kb + STAGES, G - 1), kb % STAGES);
+      wait_vmcnt<2 * LW1>();  // own part of stage kb+1 (kb+2, kb+3 may be in flight)
       wg_barrier();
       compute_block();  // phase B
       wg_barrier();
@@ -483,6 +661,11 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(
   wait_vmcnt<0>();  // no direct load may still be writing LDS at exit
   acc[(NP - 2) / TN][(NP - 2) % TN] += p[(NP - 2) & 3] * sc_tail;
   acc[(NP - 1) / TN][(NP - 1) % TN] += p[(NP - 1) & 3] * sc_tail;
+  if constexpr (FFN) {
+    ffn_epilogue<TM, TN>(acc, smem, ffn, wave, lane, m0 + wm * C::WM, n0 + (wn & 1) * C::WN, nb,
+                         M, N, Mp);
+    return;
+  }
   if constexpr (ROW) {
 #pragma unroll
     for (int tn = 0; tn < TN; ++tn) {
@@ -505,21 +688,23 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(
   }
 }
 
-template <int STAGES, bool ROW>
+template <int STAGES, bool ROW, bool FFN = false>
 hipError_t launch_pp_cfg(const uint8_t* a, const float* a_s_km, const uint8_t* w, const float* w_s,
-                         uint16_t* out, uint32_t M, uint32_t N, uint32_t K, hipStream_t s) {
-  using C = PpCfg<STAGES, ROW>;
-  if (N % C::BN != 0) return hipErrorInvalidValue;
+                         uint16_t* out, uint32_t M, uint32_t N, uint32_t K, hipStream_t s,
+                         FfnArgs ffn = FfnArgs{nullptr, nullptr, nullptr, nullptr}) {
+  using C = PpCfg<STAGES, ROW, FFN>;
+  constexpr uint32_t BNO = FFN ? kGroup : C::BN;  // output columns per tile
+  if (N % BNO != 0) return hipErrorInvalidValue;
   static bool attr_set = false;  // idempotent; racing threads set the same value
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_pp_kernel<STAGES, ROW>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_pp_kernel<STAGES, ROW, FFN>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  const uint32_t tiles_m = (M + C::BM - 1) / C::BM, tiles_n = N / C::BN;
-  gemm_pp_kernel<STAGES, ROW><<<dim3(tiles_m * tiles_n), dim3(C::NT), C::LDS_BYTES, s>>>(
-      a, a_s_km, w, w_s, out, M, N, K, m_pad16(M), tiles_m, tiles_n);
+  const uint32_t tiles_m = (M + C::BM - 1) / C::BM, tiles_n = N / BNO;
+  gemm_pp_kernel<STAGES, ROW, FFN><<<dim3(tiles_m * tiles_n), dim3(C::NT), C::LDS_BYTES, s>>>(
+      a, a_s_km, w, w_s, out, M, N, K, m_pad16(M), tiles_m, tiles_n, ffn);
   return hipGetLastError();
 }
 
@@ -726,6 +911,14 @@ hipError_t launch_gemm_skinny(const uint8_t* a, const float* a_s_km, const uint8
                               uint32_t cu_count, bool row_scaled, hipStream_t s) {
   return row_scaled ? launch_gemm_skinny_t<true>(a, a_s_km, w, w_s, out, M, N, K, cu_count, s)
                     : launch_gemm_skinny_t<false>(a, a_s_km, w, w_s, out, M, N, K, cu_count, s);
+}
+
+hipError_t launch_ffn_gate_up(const uint8_t* x, const float* x_s_km, const uint8_t* w_gate,
+                              const float* ws_gate, const uint8_t* w_up, const float* ws_up,
+                              uint8_t* hq, float* hs_km, uint32_t M, uint32_t H, uint32_t I,
+                              hipStream_t s) {
+  return launch_pp_cfg<3, false, true>(x, x_s_km, w_gate, ws_gate, nullptr, M, I, H, s,
+                                       FfnArgs{w_up, ws_up, hq, hs_km});
 }
 
 }  // namespace fp8q

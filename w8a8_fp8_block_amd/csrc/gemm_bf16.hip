@@ -27,14 +27,16 @@ __device__ __forceinline__ v4f mfma_bf16_32(const v4i& w, const v4i& a, const v4
 constexpr int kBfStages = 3;
 
 struct Bf16Cfg {
-  static constexpr int BM = 256, BN = 128, NW = 8, NT = 512;
+  static constexpr int BM = 256, BN = 128, NT = 512;
   static constexpr int WM = 64, WN = 64, TM = 4, TN = 4;
   static constexpr int A_BYTES = BM * 128, W_BYTES = BN * 128;
   static constexpr int STAGE_BYTES = A_BYTES + W_BYTES;
   static constexpr int LDS_BYTES = kBfStages * STAGE_BYTES;
   static constexpr int CHUNKS = STAGE_BYTES / 1024;  // 48 1-KB chunks
-  static constexpr int LW = CHUNKS / NW;             // 6 loads per wave and stage
-  static_assert(LDS_BYTES <= 160 * 1024 && CHUNKS % NW == 0 && 2 * LW < 64, "config");
+  // loads per wave and stage: group 0 eight chunks, group 1 four (see the
+  // FP8 ping-pong kernel: group 1 loads only rows that group 0 alone reads)
+  static constexpr int LW0 = 8, LW1 = 4;
+  static_assert(LDS_BYTES <= 160 * 1024 && 4 * (LW0 + LW1) == CHUNKS, "config");
 };
 
 __global__ __launch_bounds__(512) void gemm_bf16_kernel(const uint16_t* __restrict__ X,
@@ -43,7 +45,7 @@ __global__ __launch_bounds__(512) void gemm_bf16_kernel(const uint16_t* __restri
                                                         uint32_t N, uint32_t K, uint32_t tiles_m,
                                                         uint32_t tiles_n) {
   using C = Bf16Cfg;
-  constexpr int TM = C::TM, TN = C::TN, LW = C::LW, STAGES = kBfStages;
+  constexpr int TM = C::TM, TN = C::TN, LW0 = C::LW0, LW1 = C::LW1, STAGES = kBfStages;
   extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
 
   const uint32_t tid = threadIdx.x, lane = tid & 63;
@@ -58,22 +60,32 @@ __global__ __launch_bounds__(512) void gemm_bf16_kernel(const uint16_t* __restri
 
   const __amdgpu_buffer_rsrc_t rA = make_rsrc(X, M * rowb);
   const __amdgpu_buffer_rsrc_t rW = make_rsrc(W, N * rowb);
-  uint32_t c_off[LW];
-  bool c_act[LW];
+  // LDS chunk c = 8 rows of 128 bytes: activation rows 8c.. for c < 32,
+  // weight rows 8(c-32).. after.  Group 1 (loading in phase A, right after
+  // its own reads) takes chunks 4gw..4gw+3, activation rows 0-127, which
+  // only group 0 reads; group 0 (loading in phase B, when both groups are
+  // done with the block) takes chunks 16+8gw.. (activation rows 128-255 and
+  // the weights).
+  uint32_t c_off[LW0], c_lds[LW0];
+  const bool act = grp || gw < 2;
 #pragma unroll
-  for (int j = 0; j < LW; ++j) {
-    const uint32_t c = wave * LW + j;
-    const uint32_t ch = (c < (uint32_t)C::A_BYTES / 1024) ? c : c - C::A_BYTES / 1024;
-    const uint32_t e = ch * 64 + lane, row = e >> 3;
-    c_act[j] = c < (uint32_t)C::A_BYTES / 1024;
-    c_off[j] = c_act[j] ? min(m0 + row, M - 1) * rowb + ((e & 7) ^ swz(row)) * 16
-                        : (n0 + row) * rowb + ((e & 7) ^ swz(row)) * 16;
+  for (int j = 0; j < LW0; ++j) {
+    const uint32_t c = grp ? 4 * gw + (j & 3) : 16 + 8 * gw + j;
+    const uint32_t ch = act ? c : c - 32;
+    const uint32_t row = ch * 8 + (lane >> 3), col = lane & 7;
+    c_lds[j] = c;
+    c_off[j] = act ? min(m0 + row, M - 1) * rowb + (col ^ swz(row)) * 16
+                   : (n0 + row) * rowb + (col ^ swz(row)) * 16;
   }
-  auto issue_stage = [&](uint32_t kb, uint32_t stage) {
+  auto issue_g0 = [&](uint32_t kb, uint32_t stage) {
     uint8_t* base = smem + stage * C::STAGE_BYTES;
 #pragma unroll
-    for (int j = 0; j < LW; ++j)
-      dma16(c_act[j] ? rA : rW, c_off[j], kb * 128, base + (wave * LW + j) * 1024);
+    for (int j = 0; j < LW0; ++j) dma16(act ? rA : rW, c_off[j], kb * 128, base + c_lds[j] * 1024);
+  };
+  auto issue_g1 = [&](uint32_t kb, uint32_t stage) {
+    uint8_t* base = smem + stage * C::STAGE_BYTES;
+#pragma unroll
+    for (int j = 0; j < LW1; ++j) dma16(rA, c_off[j], kb * 128, base + c_lds[j] * 1024);
   };
 
   // this lane's chunks: 2 x 16 bytes per 16-row slab, chunk (lane/16) for the
@@ -121,32 +133,34 @@ __global__ __launch_bounds__(512) void gemm_bf16_kernel(const uint16_t* __restri
   };
 
   // (schedule and waits as in the FP8 ping-pong kernel)
-#pragma unroll
-  for (int s = 0; s < STAGES; ++s) issue_stage(min((uint32_t)s, G - 1), s);
   if (grp == 0) {
-    wait_vmcnt<(STAGES - 1) * LW>();
+#pragma unroll
+    for (int s = 0; s < STAGES; ++s) issue_g0(min((uint32_t)s, G - 1), s);
+    wait_vmcnt<(STAGES - 1) * LW0>();
     wg_barrier();
     read_block(0);
     wait_lgkm0();
     wg_barrier();
     for (uint32_t kb = 0; kb < G; ++kb) {
       compute_block();
-      wait_vmcnt<LW>();
+      wait_vmcnt<LW0>();
       wg_barrier();
       read_block(kb + 1);
       wait_lgkm0();
-      issue_stage(min(kb + STAGES, G - 1), kb % STAGES);
+      issue_g0(min(kb + STAGES, G - 1), kb % STAGES);
       wg_barrier();
     }
   } else {
-    wait_vmcnt<(STAGES - 1) * LW>();
+#pragma unroll
+    for (int s = 0; s < STAGES; ++s) issue_g1(min((uint32_t)s, G - 1), s);
+    wait_vmcnt<(STAGES - 1) * LW1>();
     wg_barrier();
     wg_barrier();
     for (uint32_t kb = 0; kb < G; ++kb) {
       read_block(kb);
       wait_lgkm0();
-      issue_stage(min(kb + STAGES, G - 1), kb % STAGES);
-      wait_vmcnt<2 * LW>();
+      issue_g1(min(kb + STAGES, G - 1), kb % STAGES);
+      wait_vmcnt<2 * LW1>();
       wg_barrier();
       compute_block();
       wg_barrier();

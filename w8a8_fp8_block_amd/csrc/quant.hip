@@ -23,69 +23,10 @@
 // per-element divide instead.  The e4m3 code is the hardware conversion of
 // q1 clamped to [-448, 448] (values in (448, 464) round to 448 anyway).
 // The exhaustive (x, amax) test checks the whole map on the device.
-#include "fp8q_internal.h"
+#include "quant_common.h"
 
 namespace fp8q {
 namespace {
-
-typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ uint32_t dpp_row_max_u32(uint32_t v) {
-  // quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_half_mirror, row_mirror:
-  // after the four steps every lane of the 16-lane row holds the row max.
-  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));
-  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));
-  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false));
-  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, false));
-  return v;
-}
-
-__device__ __forceinline__ u16x2 as_u16x2(uint32_t v) { return __builtin_bit_cast(u16x2, v); }
-
-// bf16 pair in one dword -> two floats (exact)
-__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
-
-// Quantize the group held by this lane's 16-lane row.  v = this lane's 8 bf16;
-// returns the 8 codes (little-endian bytes in element order) and the scale.
-__device__ __forceinline__ u32x2 quant_group(u32x4 v, float& scale_out) {
-  const uint32_t mag = 0x7FFF7FFFu;
-  u16x2 m01 = __builtin_elementwise_max(as_u16x2(v.x & mag), as_u16x2(v.y & mag));
-  u16x2 m23 = __builtin_elementwise_max(as_u16x2(v.z & mag), as_u16x2(v.w & mag));
-  u16x2 mm = __builtin_elementwise_max(m01, m23);
-  uint32_t amax_bits = max((uint32_t)mm.x, (uint32_t)mm.y);
-  amax_bits = dpp_row_max_u32(amax_bits);
-  const float amax = __uint_as_float(amax_bits << 16);
-  const float s = amax / 448.0f;  // IEEE (correctly rounded) divide
-  scale_out = s;
-
-  float x[8] = {bf_lo(v.x), bf_hi(v.x), bf_lo(v.y), bf_hi(v.y),
-                bf_lo(v.z), bf_hi(v.z), bf_lo(v.w), bf_hi(v.w)};
-  float q[8];
-  const bool slow = !(s >= 0x1p-100f);  // zero or tiny scale
-  if (__builtin_amdgcn_ballot_w64(slow) == 0) {
-    const float r = 1.0f / s;  // correctly rounded reciprocal
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      // en = q0*s - x is the negated residual; q1 = q0 - en*r.  Written this
-      // way round, x = -0 gives en = +0 and q1 = -0 + -0 = -0, keeping the sign
-      // (the residual x - q0*s would be +0 and turn q1 into +0).
-      const float q0 = x[i] * r;
-      const float en = __builtin_fmaf(q0, s, -x[i]);
-      q[i] = __builtin_fmaf(-en, r, q0);
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) q[i] = (s == 0.0f) ? x[i] : x[i] / s;
-  }
-#pragma unroll
-  for (int i = 0; i < 8; ++i) q[i] = __builtin_amdgcn_fmed3f(q[i], -448.0f, 448.0f);
-  int lo = __builtin_amdgcn_cvt_pk_fp8_f32(q[0], q[1], 0, false);
-  lo = __builtin_amdgcn_cvt_pk_fp8_f32(q[2], q[3], lo, true);
-  int hi = __builtin_amdgcn_cvt_pk_fp8_f32(q[4], q[5], 0, false);
-  hi = __builtin_amdgcn_cvt_pk_fp8_f32(q[6], q[7], hi, true);
-  return u32x2{(uint32_t)lo, (uint32_t)hi};
-}
 
 __device__ __forceinline__ void write_scales(float s, uint64_t g, float* __restrict__ srm,
                                              float* __restrict__ skm, uint32_t G, uint32_t Mp) {
