@@ -50,7 +50,7 @@ BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
 # readings for a plain 1 GiB copy (the HBM-bytes summary under profiles/).
 # Valid only for the GEMM source they were taken with: reported as null once
 # gemm.hip changes (its SHA-256 prefix is recorded here).
-GEMM_TRAFFIC = {"bytes": 1.1907e+09 + 4.7061e+07, "gemm_source_sha256": "b2622b8846c608d9"}
+GEMM_TRAFFIC = {"bytes": 1.1945e+09 + 4.7153e+07, "gemm_source_sha256": "388d9b39f7110e14"}
 
 
 def gemm_traffic():
