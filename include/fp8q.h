@@ -200,10 +200,12 @@ fp8q_status fp8q_gemm_blockscaled(const uint8_t *a_e4m3, const float *a_scale_km
 int fp8q_gemm_select(uint32_t M, uint32_t N, uint32_t K);
 
 /* As fp8q_gemm_blockscaled with the kernel forced: 0 = auto (2 for
- * M <= 64, 5 for M >= 2048, else 1), 1 = the LDS-tiled MFMA kernel with
- * 128x128 tiles and two workgroups per CU, 2 = the skinny kernel (decode
- * widths, needs M <= 64; one workgroup per CU, each streaming an equal
- * column range of the weights), 3 = the LDS-tiled kernel with 256x128 tiles
+ * M <= 64 and for M <= 128 when N <= 8192, 5 for M >= 2048, else 1), 1 =
+ * the LDS-tiled MFMA kernel with 128x128 tiles and two workgroups per CU,
+ * 2 = the skinny kernel (decode and small-batch widths; rows in
+ * tiles of up to 64, up to 64 rows one workgroup per CU, each streaming an
+ * equal column range of the weights, beyond that workgroups of 64 columns
+ * per row tile), 3 = the LDS-tiled kernel with 256x128 tiles
  * and 8 waves, 4 = 256x128 tiles with 4 waves (kept for measurement), 5 =
  * 256x128 tiles with two groups of 4 waves taking turns between MFMAs and
  * LDS reads.  Kernels 1, 3, 4 and 5 add the blocks' scaled partial products

@@ -110,12 +110,16 @@ def test_gemm_validation():
 
 
 def test_gemm_select():
-    """Auto GEMM choice: skinny kernel up to 64 rows, the ping-pong 256x128
-    kernel from 2048 rows on, 128x128 tiles between; bad N/K -> -1 (pure host
-    function)."""
-    for M, want in ((1, 2), (16, 2), (25, 2), (64, 2), (65, 1), (1168, 1), (2047, 1), (2048, 5),
-                    (4576, 5), (16384, 5)):
+    """Auto GEMM choice: skinny kernel up to 64 rows (and up to 128 rows when
+    N <= 8192), the ping-pong 256x128 kernel from 2048 rows on, 128x128
+    tiles between; bad N/K -> -1 (pure host function)."""
+    for M, want in ((1, 2), (16, 2), (25, 2), (64, 2), (65, 2), (128, 2), (129, 1), (1168, 1),
+                    (2047, 1), (2048, 5), (4576, 5), (16384, 5)):
         assert fp8q.fp8q_gemm_select(M, 5120, 17408) == want, M
+    for M, want in ((64, 2), (65, 1), (128, 1), (1168, 1), (4576, 5)):
+        assert fp8q.fp8q_gemm_select(M, 17408, 5120) == want, M
+    assert fp8q.fp8q_gemm_select(128, 8192, 5120) == 2
+    assert fp8q.fp8q_gemm_select(128, 8320, 5120) == 1
     assert fp8q.fp8q_gemm_select(64, 100, 128) == -1
     assert fp8q.fp8q_gemm_select(64, 128, 0) == -1
 

@@ -65,11 +65,9 @@ def orc_errors(o, r, rms=None):
 
 def _kernels_for(M, N=256):
     """Every kernel the API can force for this shape: auto, the default tiled
-    kernel, the skinny kernel (M <= 64) and the other tile shapes."""
-    ks = [0, 1]
-    if M <= 64:
-        ks.append(2)
-    return tuple(ks + [3, 4, 5])
+    kernel, the skinny kernel (row tiles of 64 beyond 64 rows) and the other
+    tile shapes."""
+    return (0, 1, 2, 3, 4, 5)
 
 
 @pytest.mark.parametrize("M,N,K", [(16, 256, 512), (1, 128, 128), (17, 384, 640), (33, 256, 1152),

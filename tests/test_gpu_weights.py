@@ -78,10 +78,7 @@ def test_dequant_prefill_weights(orc):
 
 # ---------------------------------------------------------------- GEMM
 def _kernels_for(M):
-    ks = [0, 1]
-    if M <= 64:
-        ks.append(2)
-    return tuple(ks + [3, 4, 5])
+    return (0, 1, 2, 3, 4, 5)
 
 
 def _gemm_row_gpu(orc, a, a_s, wq, s_row, kernel=0):

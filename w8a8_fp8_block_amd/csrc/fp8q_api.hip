@@ -161,11 +161,18 @@ fp8q_status run_quant(const char* fn, const uint16_t* x, uint8_t* q, float* srm,
 }
 
 // GEMM kernel choice: the skinny kernel up to kSkinnyAutoMaxM rows (at M = 64
-// it streams the weights in half the tiled kernel's time); from
-// kWideAutoMinM rows on, the ping-pong 256 x 128 kernel (one workgroup per
-// CU; 10-20% faster than the other tile shapes at M = 4576, even with
-// 128 x 128 tiles at M = 1168, slower at M = 512); 128 x 128 tiles between.
+// it streams the weights in half the tiled kernel's time), and up to
+// kSkinnyWideMaxM rows when N <= kSkinnyWideMaxN (few 128-column tiles:
+// with the last-level cache flushed before each call, at K = 17408,
+// N = 5120: 88 / 90 / 92 us at M = 80 / 128 / 192 against 112-134 /
+// 117-146 / 134 us for the tiled kernels; at N = 6144, K = 5120: 32-34 us
+// against 41-52 us up to M = 128, no gain beyond); from kWideAutoMinM rows
+// on, the ping-pong 256 x 128 kernel (one workgroup per CU; 10-20% faster
+// than the other tile shapes at M = 4576, even with 128 x 128 tiles at
+// M = 1168, slower at M = 512); 128 x 128 tiles between.
 constexpr uint32_t kSkinnyAutoMaxM = 64;
+constexpr uint32_t kSkinnyWideMaxM = 128;
+constexpr uint32_t kSkinnyWideMaxN = 8192;
 // fp8q_proj writes the K-major scales from the quantizer itself (one launch
 // fewer) up to this many scale groups; beyond it the quantizer's scattered
 // K-major stores cost more than the separate relayout launch (measured:
@@ -173,14 +180,15 @@ constexpr uint32_t kSkinnyAutoMaxM = 64;
 constexpr uint64_t kFusedKmajorMaxGroups = 1u << 17;
 constexpr uint32_t kWideAutoMinM = 2048;
 
-int gemm_auto_kernel(uint32_t M) {
-  return (M <= kSkinnyAutoMaxM) ? 2 : (M >= kWideAutoMinM ? 5 : 1);
+int gemm_auto_kernel(uint32_t M, uint32_t N) {
+  if (M <= kSkinnyAutoMaxM || (M <= kSkinnyWideMaxM && N <= kSkinnyWideMaxN)) return 2;
+  return M >= kWideAutoMinM ? 5 : 1;
 }
 
 fp8q_status run_gemm(const char* fn, const uint8_t* a, const float* as, const uint8_t* w,
                      const float* ws, uint16_t* out, uint32_t M, uint32_t N, uint32_t K, int kernel,
                      bool row_scaled, hipStream_t s) {
-  if (kernel == 0) kernel = gemm_auto_kernel(M);
+  if (kernel == 0) kernel = gemm_auto_kernel(M, N);
   if (kernel == 2 && M > kSkinnyMaxM)
     return fail(FP8Q_ERR_VARIANT, "%s: skinny kernel needs M <= %u (M=%u)", fn, kSkinnyMaxM, M);
   uint32_t cus = 0;
@@ -501,7 +509,7 @@ fp8q_status fp8q_dequant_fp8_bf16(const uint8_t* w_e4m3, const float* scale, uin
 
 int fp8q_gemm_select(uint32_t M, uint32_t N, uint32_t K) {
   if (N == 0 || N % kGroup != 0 || K == 0 || K % kGroup != 0) return -1;
-  return gemm_auto_kernel(M);
+  return gemm_auto_kernel(M, N);
 }
 
 fp8q_status fp8q_gemm_blockscaled(const uint8_t* a_e4m3, const float* a_scale_km,

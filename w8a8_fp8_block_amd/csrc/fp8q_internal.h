@@ -48,7 +48,7 @@ hipError_t launch_relayout(const float* scale_rm, float* scale_km, uint32_t M,
 // tiles, 4 waves, 2 LDS stages so that two workgroups share a CU; 2 =
 // 256x128 with 8 waves; 3 = 256x128 with 4 waves; 4 = 256x128 with two
 // ping-pong groups of 4 waves) and skinny (M <= 64).
-constexpr uint32_t kSkinnyMaxM = 64;
+constexpr uint32_t kSkinnyMaxM = 65535u * 64u;  // skinny kernel: row tiles of 64 (grid y <= 65535)
 // row_scaled: w_s is one fp32 scale per weight row [N] (applied to the
 // finished accumulator) instead of [N/128, K/128] block scales.
 hipError_t launch_gemm_tiled(const uint8_t* a, const float* a_s_km, const uint8_t* w,
