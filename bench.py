@@ -48,16 +48,25 @@ BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
 # HBM bytes the rocprofv3 FETCH_SIZE/WRITE_SIZE counters attribute to one
 # launch of the dominant GEMM at the default workload, scaled by the counters'
 # readings for a plain 1 GiB copy (the HBM-bytes summary under profiles/).
-# Valid only for the GEMM source they were taken with: reported as null once
-# gemm.hip changes (its SHA-256 prefix is recorded here).
-GEMM_TRAFFIC = {"bytes": 1.1945e+09 + 4.7153e+07, "gemm_source_sha256": "388d9b39f7110e14"}
+# Valid only for the kernel source they were taken with: reported as null
+# once the ping-pong kernel's source changes (gemm_source_hash).
+GEMM_TRAFFIC = {"bytes": 1.1945e+09 + 4.7153e+07, "gemm_source_sha256": "302cf7661c1b3f7d"}
+
+
+def gemm_source_hash():
+    """SHA-256 prefix of the ping-pong kernel's source (its section of
+    gemm.hip, from its header comment to the skinny kernel's, and the shared
+    tile helpers): the traffic figure stays valid while these are unchanged."""
+    import hashlib
+    csrc = os.path.join(ROOT, "w8a8_fp8_block_amd", "csrc")
+    g = open(os.path.join(csrc, "gemm.hip")).read()
+    i, j = g.index("// Ping-pong kernel:"), g.index("// Skinny kernel for decode")
+    text = g[i:j] + open(os.path.join(csrc, "mfma_common.h")).read()
+    return hashlib.sha256(text.encode()).hexdigest()[:16]
 
 
 def gemm_traffic():
-    import hashlib
-    src = os.path.join(ROOT, "w8a8_fp8_block_amd", "csrc", "gemm.hip")
-    h = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
-    return GEMM_TRAFFIC["bytes"] if h == GEMM_TRAFFIC["gemm_source_sha256"] else None
+    return GEMM_TRAFFIC["bytes"] if gemm_source_hash() == GEMM_TRAFFIC["gemm_source_sha256"] else None
 
 
 def parse():
