@@ -50,7 +50,7 @@ BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
 # readings for a plain 1 GiB copy (the HBM-bytes summary under profiles/).
 # Valid only for the kernel source they were taken with: reported as null
 # once the ping-pong kernel's source changes (gemm_source_hash).
-GEMM_TRAFFIC = {"bytes": 1.1945e+09 + 4.7153e+07, "gemm_source_sha256": "302cf7661c1b3f7d"}
+GEMM_TRAFFIC = {"bytes": 1.1945e+09 + 4.7153e+07, "gemm_source_sha256": "1d754cb174a4de31"}
 
 
 def gemm_source_hash():
@@ -94,6 +94,9 @@ def parse():
     p.add_argument("--ffn-sweep", action="store_true",
                    help="fp8q_ffn's two variants over M at H=5120, I=17408 with cold caches, "
                         "and the automatic choice (the selector's measurement)")
+    p.add_argument("--gemm-sweep", action="store_true",
+                   help="the GEMM's single-pass kernels and split-K counts over M at three "
+                        "projection shapes with cold caches (the split-K selector's measurement)")
     p.add_argument("--copy-mib", type=int, default=0,
                    help="instead of the benchmark, run 3 plain device copies of this many "
                         "MiB (the reference kernel for scaling rocprofv3 byte counters)")
@@ -329,6 +332,62 @@ def ffn_sweep(reps=15):
                           "rule_ok": t[auto] <= 1.03 * min(t[1], t[2])}), flush=True)
 
 
+def gemm_sweep(reps=10):
+    """The block-scaled GEMM over M at three projection shapes, cold caches:
+    the automatic single-pass kernel, the 128x128 tiled kernel and its split-K
+    form at 2..12 splits (median of `reps` calls each, all variants taking turns,
+    each call after a 512 MiB write that evicts L2 and the last-level cache);
+    and whether fp8q_gemm_blockscaled_splitk's automatic choice is within 3% of
+    the fastest variant.  Normal activations, quantized by the library;
+    weights normal(0, 0.02), block-quantized."""
+    import torch
+    import w8a8_fp8_block_amd as fp8q
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(5)
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    for N, K in ((5120, 17408), (6144, 5120), (17408, 5120)):
+        wq, wsc = quantize_weights_gpu(torch.randn((N, K), generator=gen, device=dev) * 0.02)
+        for M in (16, 32, 64, 65, 96, 128, 192, 256, 384, 512, 768, 1024, 1168, 1536, 2048):
+            x = torch.randn((M, K), generator=gen, device=dev).to(torch.bfloat16)
+            q = torch.empty((M, K), dtype=torch.uint8, device=dev)
+            srm = torch.empty((M, K // 128), dtype=torch.float32, device=dev)
+            skm = torch.empty((K // 128, fp8q.fp8q_m_pad(M)), dtype=torch.float32, device=dev)
+            fp8q.fp8q_quant_act_kmajor(x, q, srm, skm)
+            out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+            auto_k = fp8q.fp8q_gemm_select(M, N, K)
+            variants = {"auto": ("k", 0), "k1": ("k", 1)}
+            for S in (2, 3, 4, 6, 8, 12):
+                variants[f"s{S}"] = ("s", S)
+            wsp = torch.empty((12 * M * N,), dtype=torch.float32, device=dev)
+            names = list(variants)
+            ts = {v: [] for v in names}
+            for r in range(reps + 1):
+                for v in names:
+                    kind, arg = variants[v]
+                    flush.fill_(1)
+                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    e0.record()
+                    if kind == "k":
+                        fp8q.fp8q_gemm_blockscaled(q, skm, wq, wsc, out, kernel=arg)
+                    else:
+                        fp8q.fp8q_gemm_blockscaled_splitk(q, skm, wq, wsc, out, wsp, splits=arg)
+                    e1.record()
+                    torch.cuda.synchronize()
+                    if r >= 1:
+                        ts[v].append(e0.elapsed_time(e1) * 1e3)
+            t = {v: round(float(np.median(ts[v])), 1) for v in names}
+            best = min(t, key=t.get)
+            sel = fp8q.fp8q_gemm_splitk_select(M, N, K)
+            chosen = t["auto"] if sel < 2 else t[f"s{sel}"] if f"s{sel}" in t else None
+            print(json.dumps({"M": M, "N": N, "K": K, "auto_kernel": auto_k, "us": t,
+                              "best": best, "splitk_auto": sel,
+                              "rule_ok": None if chosen is None else chosen <= 1.03 * t[best]}),
+                  flush=True)
+            del wsp, x, q, srm, skm, out
+        del wq, wsc
+
+
 def quantize_weights_gpu(wf, per_row=False):
     """Synthetic FP8 weights: per 128x128 block (or per row), scale = amax/448,
     codes by PyTorch's float8_e4m3fn cast (input preparation, outside the timed
@@ -401,6 +460,9 @@ def main():
         return
     if args.ffn_sweep:
         ffn_sweep()
+        return
+    if args.gemm_sweep:
+        gemm_sweep()
         return
 
     import torch

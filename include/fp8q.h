@@ -217,6 +217,45 @@ fp8q_status fp8q_gemm_blockscaled_ex(const uint8_t *a_e4m3, const float *a_scale
                                      uint16_t *out_bf16, uint32_t M, uint32_t N,
                                      uint32_t K, int kernel, hipStream_t stream);
 
+/* Split-K form of fp8q_gemm_blockscaled for row counts whose 128x128 tiles
+ * are too few to fill the device (the same operation, same argument
+ * conventions and errors): the K blocks are cut into `splits` contiguous
+ * ranges, block range s covering [s*(K/128)/splits, (s+1)*(K/128)/splits);
+ * each tile's range sums are written in fp32 to the workspace as
+ * part[s][M][N], then a second kernel forms out = bf16_rne(part[0] + part[1]
+ * + ... + part[splits-1]), added in that order.  Results are reproducible
+ * run to run; they differ from the single-pass kernels by the fp32
+ * summation order only.
+ *   workspace        device memory, 16-byte aligned, at least
+ *                    fp8q_gemm_splitk_workspace_bytes(M, N, K, splits) bytes
+ *                    (may be NULL when that is 0); contents on entry are
+ *                    ignored, on return undefined; owned by the caller, who
+ *                    must not let two calls in flight share it
+ *   splits           0 = automatic (fp8q_gemm_splitk_select; when it gives
+ *                    1, fp8q_gemm_blockscaled's automatic kernel runs and the
+ *                    workspace is not touched), else 2 <= splits <=
+ *                    min(K/128, 64); 1 or a larger count -> FP8Q_ERR_VARIANT
+ *   workspace_bytes  smaller than needed -> FP8Q_ERR_SHAPE */
+fp8q_status fp8q_gemm_blockscaled_splitk(const uint8_t *a_e4m3, const float *a_scale_km,
+                                         const uint8_t *w_e4m3, const float *w_scale,
+                                         uint16_t *out_bf16, void *workspace,
+                                         size_t workspace_bytes, uint32_t M, uint32_t N,
+                                         uint32_t K, uint32_t splits, hipStream_t stream);
+
+/* The split count fp8q_gemm_blockscaled_splitk takes for splits = 0, with
+ * T = ceil(M/128) * (N/128) tiles of 128x128:
+ *   min(floor(512 / T), floor(K / 1280), 6)   (one round of two workgroups
+ *   per CU on 256 CUs; at least 10 K blocks a split)
+ * when M > 64 and fp8q_gemm_select does not pick the 256x128 kernel (id 5),
+ * and 1 (no split) otherwise or when that minimum is below 2.  0 if N or K
+ * is not a positive multiple of 128.  Pure host function. */
+uint32_t fp8q_gemm_splitk_select(uint32_t M, uint32_t N, uint32_t K);
+
+/* Workspace bytes of fp8q_gemm_blockscaled_splitk: splits * M * N * 4 for
+ * splits >= 2 (splits = 0: the automatic count), 0 for no split or for an
+ * invalid shape or count.  Pure host function. */
+size_t fp8q_gemm_splitk_workspace_bytes(uint32_t M, uint32_t N, uint32_t K, uint32_t splits);
+
 /* Per-row FP8 weights (the pages' other weight format, dispatch_proj.rs,
  * dequant_fp8_bf16_into: WeightQuantFormat::Fp8PerRow; the scale index
  * formula scale[(n/block_n)*sk + k/block_k] with block_n = 1, block_k = K,
@@ -342,7 +381,8 @@ int fp8q_ffn_select(uint32_t M, uint32_t H, uint32_t I);
 
 /* Bytes of device workspace fp8q_ffn needs for (M, H, I, variant); 0 for an
  * invalid variant or shape.  Variant 2 also holds the bf16 gate and up
- * outputs (4*M*I bytes more). */
+ * outputs (4*M*I bytes more); where fp8q_gemm_splitk_select(M, H, I) splits
+ * the down projection, its partials add splits*M*H*4 bytes. */
 size_t fp8q_ffn_workspace_bytes(uint32_t M, uint32_t H, uint32_t I, int variant);
 
 /* The whole FFN:
@@ -356,7 +396,9 @@ size_t fp8q_ffn_workspace_bytes(uint32_t M, uint32_t H, uint32_t I, int variant)
  *   variant          0 auto (fp8q_ffn_select), 1 fused gate/up, 2 separate;
  *                    both give bit-identical results
  * Launches: the quantizer (and the scale relayout beyond 2^17 scale groups,
- * as fp8q_proj), the gate/up stage, the down GEMM; all on `stream`.
+ * as fp8q_proj), the gate/up stage, the down GEMM (split-K, as
+ * fp8q_gemm_blockscaled_splitk with splits = 0, where that splits); all on
+ * `stream`.
  * Errors: FP8Q_ERR_SHAPE also for a short workspace; FP8Q_ERR_VARIANT for a
  * variant outside 0..2; otherwise as fp8q_proj. */
 fp8q_status fp8q_ffn(const uint16_t *x_bf16, const uint8_t *w_gate,

@@ -216,3 +216,74 @@ def test_ffn_validation():
     assert b"workspace" in L.fp8q_last_error()
     assert L.fp8q_ffn(g, *w, g, g, need, 8, 256, 384, 2, None) == 2  # variant 2 needs more
     assert L.fp8q_ffn(g, *w, g, None, 0, 0, 256, 384, 0, None) == 0  # M == 0: nothing to do
+
+
+def test_splitk_validation():
+    L = fp8q.lib()
+    g = GOOD
+    # fp8q_gemm_blockscaled_splitk(a, as, w, ws, out, work, bytes, M, N, K, splits, stream)
+    assert L.fp8q_gemm_blockscaled_splitk(g, g, g, g, g, g, 1 << 20, 4, 100, 256, 2, None) == 2
+    assert L.fp8q_gemm_blockscaled_splitk(g, g, g, g, g, g, 1 << 20, 4, 128, 200, 2, None) == 2
+    assert L.fp8q_gemm_blockscaled_splitk(g, g, None, g, g, g, 1 << 20, 4, 128, 256, 2, None) == 1
+    assert L.fp8q_gemm_blockscaled_splitk(g, g, g, g, BAD, g, 1 << 20, 4, 128, 256, 2, None) == 3
+    # split counts: 1 and more than K/128 (or 64) are rejected
+    assert L.fp8q_gemm_blockscaled_splitk(g, g, g, g, g, g, 1 << 20, 4, 128, 256, 1, None) == 6
+    assert L.fp8q_gemm_blockscaled_splitk(g, g, g, g, g, g, 1 << 20, 4, 128, 256, 3, None) == 6
+    assert "splits=3" in _err()
+    assert L.fp8q_gemm_blockscaled_splitk(g, g, g, g, g, g, 1 << 30, 4, 128, 128 * 80, 65,
+                                          None) == 6
+    # workspace: NULL, misaligned, too small
+    need = fp8q.fp8q_gemm_splitk_workspace_bytes(4, 128, 256, 2)
+    assert need == 2 * 4 * 128 * 4
+    assert L.fp8q_gemm_blockscaled_splitk(g, g, g, g, g, None, need, 4, 128, 256, 2, None) == 1
+    assert L.fp8q_gemm_blockscaled_splitk(g, g, g, g, g, BAD, need, 4, 128, 256, 2, None) == 3
+    assert L.fp8q_gemm_blockscaled_splitk(g, g, g, g, g, g, need - 1, 4, 128, 256, 2, None) == 2
+    assert "workspace" in _err()
+    # M == 0: nothing to do, no workspace needed
+    assert L.fp8q_gemm_blockscaled_splitk(g, g, g, g, g, None, 0, 0, 128, 256, 2, None) == 0
+
+
+def test_splitk_workspace_bytes():
+    ws = fp8q.fp8q_gemm_splitk_workspace_bytes
+    assert ws(300, 512, 2048, 5) == 5 * 300 * 512 * 4
+    assert ws(300, 512, 2048, 1) == 0
+    assert ws(300, 512, 2048, 17) == 0          # more splits than K blocks
+    assert ws(300, 500, 2048, 2) == 0           # N % 128
+    assert ws(300, 512, 0, 2) == 0
+    for M, N, K in ((512, 5120, 17408), (200, 6144, 5120), (4576, 5120, 17408), (16, 6144, 5120)):
+        s = fp8q.fp8q_gemm_splitk_select(M, N, K)
+        assert ws(M, N, K, 0) == (0 if s < 2 else s * M * N * 4)
+
+
+def test_splitk_select():
+    """Split count: min(floor(512 / tiles), floor(K/1280), 6) above 64 rows,
+    outside the 256x128 kernel's range, 1 below 2; 0 for a bad N or K."""
+    sel = fp8q.fp8q_gemm_splitk_select
+    for M, want in ((16, 1), (64, 1), (65, 6), (128, 6), (129, 6), (256, 6), (257, 4), (384, 4),
+                    (385, 3), (512, 3), (513, 2), (768, 2), (769, 1), (1168, 1), (2048, 1)):
+        assert sel(M, 5120, 17408) == want, M
+    for M, want in ((65, 4), (256, 4), (384, 3), (512, 2), (640, 2), (768, 1)):
+        assert sel(M, 6144, 5120) == want, M
+    for M, want in ((65, 3), (128, 3), (129, 1)):
+        assert sel(M, 17408, 5120) == want, M
+    assert sel(300, 128, 2560) == 2        # K/1280 = 2 caps it
+    assert sel(300, 128, 2432) == 1        # fewer than 20 K blocks: no split
+    assert sel(4096, 128, 17408) == 1      # the 256x128 kernel's range
+    assert sel(100, 100, 1280) == 0
+    assert sel(100, 128, 0) == 0
+
+
+def test_ffn_workspace_holds_split_partials():
+    H, I = 5120, 17408
+    for M in (300, 512, 1168):
+        s = fp8q.fp8q_gemm_splitk_select(M, H, I)
+        extra = s * M * H * 4 if s >= 2 else 0
+        Mp = fp8q.fp8q_m_pad(M)
+
+        def a256(v):
+            return (v + 255) // 256 * 256
+
+        base = (a256(M * H) + a256(M * H // 128 * 4) + a256(Mp * H // 128 * 4) + a256(M * I)
+                + a256(Mp * I // 128 * 4))
+        assert fp8q.fp8q_ffn_workspace_bytes(M, H, I, 1) == base + a256(extra), M
+        assert fp8q.fp8q_ffn_workspace_bytes(M, H, I, 2) == base + 2 * a256(2 * M * I) + a256(extra)

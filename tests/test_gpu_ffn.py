@@ -25,6 +25,7 @@ input; the post-SiLU intermediate is quantized once for down).
     codes; full FFN sizes (H=5120, I=17408) at decode, prefill (M=1168) and
     large prefill (M=4576) widths on sampled rows.
 """
+import dataclasses
 import itertools
 
 import numpy as np
@@ -364,10 +365,14 @@ def test_ffn_random_small_widths(orc, M):
         assert np.array_equal(outs[1][0], outs[2][0]) and np.array_equal(outs[1][1], outs[2][1])
 
 
-@pytest.mark.parametrize("name,M", [("ffn_decode", 16), ("ffn_decode", 25), ("ffn_prefill", 1168),
-                                    ("ffn_large", 4576)])
+@pytest.mark.parametrize("name,M", [("ffn_decode", 16), ("ffn_decode", 25), ("ffn_prefill", 256),
+                                    ("ffn_prefill", 1168), ("ffn_large", 4576)])
 def test_ffn_full_size_sampled_rows(orc, name, M):
-    w = synth.ffn_workload(name, M)
+    """Full model widths; M = 256 at the prefill widths is a row count whose
+    down projection runs split-K."""
+    base = synth.ffn_workload(name)
+    w = synth.ffn_workload(name, M) if M in [v.M for v in synth.FFN_WORKLOADS[name]] else \
+        dataclasses.replace(base, M=M)
     log(f"ffn {w.desc}: drawing inputs")
     x, wf = synth.make_ffn_inputs(w)
     W = _weights(orc, wf)

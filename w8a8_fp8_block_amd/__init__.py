@@ -40,6 +40,7 @@ LIB_PATH = os.path.join(_HERE, "libfp8q.so")
 _P = ctypes.c_void_p
 _U = ctypes.c_uint32
 _I = ctypes.c_int
+_SZ = ctypes.c_size_t
 
 
 class SelectParams(ctypes.Structure):
@@ -68,6 +69,9 @@ _SIGS = {
     "fp8q_proj_quant_fused": (_I, [_U, _U]),
     "fp8q_gemm_blockscaled": (_I, [_P, _P, _P, _P, _P, _U, _U, _U, _P]),
     "fp8q_gemm_blockscaled_ex": (_I, [_P, _P, _P, _P, _P, _U, _U, _U, _I, _P]),
+    "fp8q_gemm_blockscaled_splitk": (_I, [_P, _P, _P, _P, _P, _P, _SZ, _U, _U, _U, _U, _P]),
+    "fp8q_gemm_splitk_select": (_U, [_U, _U, _U]),
+    "fp8q_gemm_splitk_workspace_bytes": (_SZ, [_U, _U, _U, _U]),
     "fp8q_proj": (_I, [_P, _P, _P, _P, _P, _P, _P, _U, _U, _U, _P]),
     "fp8q_gemm_rowscaled": (_I, [_P, _P, _P, _P, _P, _U, _U, _U, _P]),
     "fp8q_gemm_rowscaled_ex": (_I, [_P, _P, _P, _P, _P, _U, _U, _U, _I, _P]),
@@ -178,6 +182,30 @@ def fp8q_gemm_blockscaled(a, a_scale_km, w, w_scale, out, kernel: int = 0, strea
         raise ValueError("a and w disagree on K")
     _check(lib().fp8q_gemm_blockscaled_ex(_ptr(a), _ptr(a_scale_km), _ptr(w), _ptr(w_scale),
                                          _ptr(out), M, N, K, kernel, _stream(stream)))
+
+
+def fp8q_gemm_splitk_select(M: int, N: int, K: int) -> int:
+    """Split count fp8q_gemm_blockscaled_splitk takes with splits=0 (1 = no split)."""
+    return int(lib().fp8q_gemm_splitk_select(M, N, K))
+
+
+def fp8q_gemm_splitk_workspace_bytes(M: int, N: int, K: int, splits: int = 0) -> int:
+    return int(lib().fp8q_gemm_splitk_workspace_bytes(M, N, K, splits))
+
+
+def fp8q_gemm_blockscaled_splitk(a, a_scale_km, w, w_scale, out, workspace, splits: int = 0,
+                                 stream=None):
+    """fp8q_gemm_blockscaled with the K blocks split over `splits` workgroups
+    per tile (0 = automatic); workspace: a device tensor of at least
+    fp8q_gemm_splitk_workspace_bytes(M, N, K, splits) bytes, or None when that is 0."""
+    M, K = _dims(a, 2)
+    N, K2 = _dims(w, 2)
+    if K2 != K:
+        raise ValueError("a and w disagree on K")
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().fp8q_gemm_blockscaled_splitk(_ptr(a), _ptr(a_scale_km), _ptr(w), _ptr(w_scale),
+                                             _ptr(out), _optr(workspace), nbytes, M, N, K,
+                                             splits, _stream(stream)))
 
 
 def fp8q_proj(x, w, w_scale, out, act_q, act_scale, act_scale_km, stream=None):
@@ -304,6 +332,7 @@ GEMM_KERNEL_NAMES = {1: "gemm_tiled_kernel<128,128,2,2,2>", 2: "gemm_skinny_kern
                      3: "gemm_tiled_kernel<256,128,4,2,3>", 4: "gemm_tiled_kernel<256,128,2,2,3>",
                      5: "gemm_pp_kernel<3,false,false>"}
 FFN_GATE_UP_KERNEL_NAME = "gemm_pp_kernel<3,false,true>"
+SPLITK_KERNEL_NAMES = ("gemm_tiled_kernel<128,128,2,2,2,false,true>", "splitk_reduce_kernel")
 
 
 def fp8q_quant_b_min_m(K: int, params: SelectParams) -> int:

@@ -1,6 +1,7 @@
 // C-ABI entry points of libfp8q.so: argument validation, the quantizer
 // variant selection rule, once-per-branch logging and kernel dispatch.
 // Declarations and the contract of every function: include/fp8q.h.
+#include <algorithm>
 #include <atomic>
 #include <cstdarg>
 #include <cstdio>
@@ -185,6 +186,34 @@ int gemm_auto_kernel(uint32_t M, uint32_t N) {
   return M >= kWideAutoMinM ? 5 : 1;
 }
 
+// Split-K (fp8q_gemm_blockscaled_splitk): splits = floor(512 / tiles) (the
+// split grid stays within one round of two 128x128 workgroups per CU), at
+// most K/1280 (10 K blocks a split) and 6, for more than kSplitMinM rows
+// and wherever the single-pass choice is not the 256 x 128 kernel.  Cold
+// caches (bench.py --gemm-sweep), us single-pass -> split-K: N=5120,
+// K=17408: 87 -> 46 at M=65, 135 -> 55 at M=192, 143 -> 73 at M=384, 143 ->
+// 87 at M=512, 144 -> 109 at M=768; N=6144, K=5120: 32 -> 23 at M=65, 47 ->
+// 32 at M=192, 51 -> 39 at M=384; N=17408, K=5120: 55 -> 47 at M=65.  A
+// count past one round (M=512, N=5120: 4 splits, 640 workgroups) was up to
+// 30% slower than the one below it; beyond 512 tiles no count helped.
+constexpr uint32_t kSplitTargetWgs = 512;
+constexpr uint32_t kSplitMinBlocks = 10;
+constexpr uint32_t kSplitMax = 6;
+constexpr uint32_t kSplitMinM = 64;
+constexpr uint32_t kSplitMaxUser = 64;  // bound of an explicit split count
+
+uint32_t splitk_auto(uint32_t M, uint32_t N, uint32_t K) {
+  if (M <= kSplitMinM || gemm_auto_kernel(M, N) == 5) return 1;
+  const uint64_t tiles = (uint64_t)((M + 127) / 128) * (N / 128);
+  const uint64_t s = std::min<uint64_t>(
+      kSplitTargetWgs / tiles, std::min<uint64_t>(K / kGroup / kSplitMinBlocks, kSplitMax));
+  return s < 2 ? 1 : (uint32_t)s;
+}
+
+uint64_t splitk_workspace(uint32_t M, uint32_t N, uint32_t splits) {
+  return splits < 2 ? 0 : (uint64_t)splits * M * N * 4;
+}
+
 fp8q_status run_gemm(const char* fn, const uint8_t* a, const float* as, const uint8_t* w,
                      const float* ws, uint16_t* out, uint32_t M, uint32_t N, uint32_t K, int kernel,
                      bool row_scaled, hipStream_t s) {
@@ -199,6 +228,17 @@ fp8q_status run_gemm(const char* fn, const uint8_t* a, const float* as, const ui
                     : launch_gemm_tiled(a, as, w, ws, out, M, N, K, kernel == 1 ? 1 : kernel - 1,
                                         row_scaled, s);
   return launched(fn, e);
+}
+
+// The automatic block-scaled GEMM where a split-K workspace is at hand:
+// split-K when splitk_auto picks it (part holds the partials), else the
+// automatic single-pass kernel.
+fp8q_status run_gemm_ws(const char* fn, const uint8_t* a, const float* as, const uint8_t* w,
+                        const float* ws, uint16_t* out, float* part, uint32_t M, uint32_t N,
+                        uint32_t K, hipStream_t s) {
+  const uint32_t splits = splitk_auto(M, N, K);
+  if (splits < 2) return run_gemm(fn, a, as, w, ws, out, M, N, K, 0, false, s);
+  return launched(fn, launch_splitk_128(a, as, w, ws, out, part, M, N, K, splits, s));
 }
 
 // Shared argument checks of the GEMM entry points.
@@ -273,7 +313,7 @@ int ffn_auto_variant(uint32_t M) { return M >= kFfnFusedMinM ? 1 : 2; }
 // Workspace carve-up of fp8q_ffn: regions in this order, each starting on a
 // 256-byte boundary.
 struct FfnWorkspace {
-  uint64_t xq, xs_rm, xs_km, hq, hs_km, g, u, total;
+  uint64_t xq, xs_rm, xs_km, hq, hs_km, g, u, part, total;
 };
 
 uint64_t align256(uint64_t v) { return (v + 255u) & ~uint64_t(255); }
@@ -292,6 +332,11 @@ FfnWorkspace ffn_workspace(uint32_t M, uint32_t H, uint32_t I, int variant) {
     w.g = o; o = align256(o + (uint64_t)M * I * 2);
     w.u = o; o = align256(o + (uint64_t)M * I * 2);
   }
+  // split-K partials of the down projection (empty when it does not split;
+  // gate and up never split, so that the variants stay bit-identical)
+  const uint64_t part = splitk_workspace(M, H, splitk_auto(M, H, I));
+  w.part = part ? o : 0;
+  o = align256(o + part);
   w.total = o;
   return w;
 }
@@ -507,6 +552,46 @@ fp8q_status fp8q_dequant_fp8_bf16(const uint8_t* w_e4m3, const float* scale, uin
   return launched(fn, launch_dequant(w_e4m3, scale, dst_bf16, N, K, per_row != 0, stream));
 }
 
+uint32_t fp8q_gemm_splitk_select(uint32_t M, uint32_t N, uint32_t K) {
+  if (N == 0 || N % kGroup != 0 || K == 0 || K % kGroup != 0) return 0;
+  return splitk_auto(M, N, K);
+}
+
+size_t fp8q_gemm_splitk_workspace_bytes(uint32_t M, uint32_t N, uint32_t K, uint32_t splits) {
+  if (N % kGroup != 0 || K == 0 || K % kGroup != 0 || splits > K / kGroup) return 0;
+  if (splits == 0) splits = splitk_auto(M, N, K);
+  return (size_t)splitk_workspace(M, N, splits);
+}
+
+fp8q_status fp8q_gemm_blockscaled_splitk(const uint8_t* a_e4m3, const float* a_scale_km,
+                                         const uint8_t* w_e4m3, const float* w_scale,
+                                         uint16_t* out_bf16, void* workspace,
+                                         size_t workspace_bytes, uint32_t M, uint32_t N,
+                                         uint32_t K, uint32_t splits, hipStream_t stream) {
+  const char* fn = "fp8q_gemm_blockscaled_splitk";
+  fp8q_status st =
+      check_gemm_args(fn, a_e4m3, a_scale_km, w_e4m3, w_scale, "w_scale", out_bf16, M, N, K, 0);
+  if (st != FP8Q_OK) return st;
+  if (splits == 1 || splits > std::min(K / kGroup, kSplitMaxUser))
+    return fail(FP8Q_ERR_VARIANT, "%s: splits=%u (0 = auto, else 2..min(K/128, %u))", fn, splits,
+                kSplitMaxUser);
+  if (M == 0) return ok();
+  if (splits == 0) splits = splitk_auto(M, N, K);
+  if (splits >= 2) {
+    const uint64_t need = splitk_workspace(M, N, splits);
+    REQUIRE_PTR(workspace);
+    if (workspace_bytes < need)
+      return fail(FP8Q_ERR_SHAPE, "%s: workspace of %llu bytes, %llu needed", fn,
+                  (unsigned long long)workspace_bytes, (unsigned long long)need);
+  }
+  st = check_device(fn);
+  if (st != FP8Q_OK) return st;
+  if (splits < 2)
+    return run_gemm(fn, a_e4m3, a_scale_km, w_e4m3, w_scale, out_bf16, M, N, K, 0, false, stream);
+  return launched(fn, launch_splitk_128(a_e4m3, a_scale_km, w_e4m3, w_scale, out_bf16,
+                                        static_cast<float*>(workspace), M, N, K, splits, stream));
+}
+
 int fp8q_gemm_select(uint32_t M, uint32_t N, uint32_t K) {
   if (N == 0 || N % kGroup != 0 || K == 0 || K % kGroup != 0) return -1;
   return gemm_auto_kernel(M, N);
@@ -620,6 +705,7 @@ fp8q_status fp8q_ffn(const uint16_t* x_bf16, const uint8_t* w_gate, const float*
   float* xs_km = reinterpret_cast<float*>(ws + w.xs_km);
   uint8_t* hq = ws + w.hq;
   float* hs_km = reinterpret_cast<float*>(ws + w.hs_km);
+  float* part = reinterpret_cast<float*>(ws + w.part);
 
   // x is quantized once for both gate and up
   if ((uint64_t)M * (H / kGroup) <= kFusedKmajorMaxGroups) {
@@ -640,7 +726,7 @@ fp8q_status fp8q_ffn(const uint16_t* x_bf16, const uint8_t* w_gate, const float*
     if (st == FP8Q_OK) st = launched(fn, launch_silu_mul_quant(g, u, hq, hs_km, M, I, stream));
   }
   if (st != FP8Q_OK) return st;
-  return run_gemm(fn, hq, hs_km, w_down, w_down_scale, out_bf16, M, H, I, 0, false, stream);
+  return run_gemm_ws(fn, hq, hs_km, w_down, w_down_scale, out_bf16, part, M, H, I, stream);
 }
 
 }  // extern "C"

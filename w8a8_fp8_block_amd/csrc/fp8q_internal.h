@@ -54,6 +54,13 @@ constexpr uint32_t kSkinnyMaxM = 65535u * 64u;  // skinny kernel: row tiles of 6
 hipError_t launch_gemm_tiled(const uint8_t* a, const float* a_s_km, const uint8_t* w,
                              const float* w_s, uint16_t* out, uint32_t M, uint32_t N,
                              uint32_t K, int cfg, bool row_scaled, hipStream_t s);
+// Split-K form of the 128x128 tiled kernel (block-scaled weights): splits
+// workgroups per tile, each over a contiguous range of K blocks, write fp32
+// partial tiles to part [splits, M, N]; a reduction adds them in split order
+// into out.  2 <= splits <= K/128.
+hipError_t launch_splitk_128(const uint8_t* a, const float* a_s_km, const uint8_t* w,
+                             const float* w_s, uint16_t* out, float* part, uint32_t M,
+                             uint32_t N, uint32_t K, uint32_t splits, hipStream_t s);
 hipError_t launch_gemm_skinny(const uint8_t* a, const float* a_s_km, const uint8_t* w,
                               const float* w_s, uint16_t* out, uint32_t M, uint32_t N,
                               uint32_t K, uint32_t cu_count, bool row_scaled, hipStream_t s);

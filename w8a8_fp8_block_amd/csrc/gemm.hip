@@ -86,30 +86,43 @@ struct TileCfg {
 // ROW: per-row weight scales Ws[N] (one multiplier per output column,
 // applied to the finished accumulator) instead of 128x128 block scales
 // applied per K block.
-template <int BM, int BN, int WGM, int WGN, int STAGES, bool ROW>
+//
+// SPLIT: split-K.  The grid holds `splits` workgroups per tile; split s takes
+// the K blocks [s*G/splits, (s+1)*G/splits) and stores its fp32 partial tile
+// to part[s][M][N]; a second kernel (splitk_reduce_kernel) adds the splits'
+// partials in split order and rounds to bf16.  Block-scaled weights only.
+template <int BM, int BN, int WGM, int WGN, int STAGES, bool ROW, bool SPLIT = false>
 __global__ __launch_bounds__(64 * WGM * WGN) void gemm_tiled_kernel(
     const uint8_t* __restrict__ A, const float* __restrict__ As, const uint8_t* __restrict__ W,
     const float* __restrict__ Ws, uint16_t* __restrict__ out, uint32_t M, uint32_t N, uint32_t K,
-    uint32_t Mp, uint32_t tiles_m, uint32_t tiles_n) {
+    uint32_t Mp, uint32_t tiles_m, uint32_t tiles_n, uint32_t splits = 1,
+    float* __restrict__ part = nullptr) {
   using C = TileCfg<BM, BN, WGM, WGN, STAGES, ROW>;
   constexpr int TM = C::TM, TN = C::TN, NP = C::NP;
+  static_assert(!(SPLIT && ROW), "split-K for block-scaled weights only");
   extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
 
   const uint32_t tid = threadIdx.x, lane = tid & 63;
   const uint32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (SGPR)
   const uint32_t wm = wave / WGN, wn = wave % WGN;
 
-  uint32_t tmi, tni;  // this workgroup's tile (XCD-aware, grouped order)
-  tile_coords(tiles_m, tiles_n, tmi, tni);
+  uint32_t tmi, tni, split = 0;  // this workgroup's tile (XCD-aware, grouped order)
+  if constexpr (SPLIT)
+    tile_split_coords(tiles_m, tiles_n, splits, tmi, tni, split);
+  else
+    tile_coords(tiles_m, tiles_n, tmi, tni);
   const uint32_t m0 = tmi * BM, n0 = tni * BN;
-  const uint32_t G = K / kGroup;
+  const uint32_t GK = K / kGroup;  // K blocks in all
+  // this workgroup's K blocks: kbeg .. kbeg + G - 1
+  const uint32_t kbeg = SPLIT ? split * GK / splits : 0;
+  const uint32_t G = SPLIT ? (split + 1) * GK / splits - kbeg : GK;
   const uint32_t nb = (n0 + wn * C::WN) / kGroup;  // this wave's weight-scale block row
 
   // ---- buffer resources and per-lane source offsets (K block 0) ----
   const __amdgpu_buffer_rsrc_t rA = make_rsrc(A, M * K);
   const __amdgpu_buffer_rsrc_t rW = make_rsrc(W, N * K);
-  const __amdgpu_buffer_rsrc_t rS = make_rsrc(As, G * Mp * 4);
-  const __amdgpu_buffer_rsrc_t rWs = make_rsrc(Ws, ROW ? N * 4 : (N / kGroup) * G * 4);
+  const __amdgpu_buffer_rsrc_t rS = make_rsrc(As, GK * Mp * 4);
+  const __amdgpu_buffer_rsrc_t rWs = make_rsrc(Ws, ROW ? N * 4 : (N / kGroup) * GK * 4);
   uint32_t a_off[C::DA], w_off[C::DW], s_off[C::SA];
 #pragma unroll
   for (int j = 0; j < C::DA; ++j) {
@@ -125,11 +138,13 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_tiled_kernel(
   // bounds and never used; rows in [M, Mp) hold the layout's zero pad)
 #pragma unroll
   for (int j = 0; j < C::SA; ++j) s_off[j] = min(m0 + wm * C::WM + j * 64 + lane, Mp - 1) * 4;
-  const uint32_t ws_off = nb * G * 4;  // every lane loads the same weight scale
+  const uint32_t ws_off = nb * GK * 4;  // every lane loads the same weight scale
   const uint32_t sc_base = C::A_BYTES + C::W_BYTES + wave * C::SCW_BYTES;
   const uint32_t ws_base = sc_base + C::SA * 256;
 
-  auto issue_stage = [&](uint32_t kb, uint32_t stage) {
+  // K block kbeg + kl (kl counted from this workgroup's first block)
+  auto issue_stage = [&](uint32_t kl, uint32_t stage) {
+    const uint32_t kb = kbeg + kl;
     uint8_t* base = smem + stage * C::STAGE_BYTES;
 #pragma unroll
     for (int j = 0; j < C::DA; ++j) dma16(rA, a_off[j], kb * kGroup, base + (wave * C::DA + j) * 1024);
@@ -265,9 +280,25 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_tiled_kernel(
 #pragma unroll
       for (int tn = 0; tn < TN; ++tn) {
         const uint32_t n = n0 + wn * C::WN + tn * 16 + 4 * (lane >> 4);
-        *reinterpret_cast<uint2*>(out + (uint64_t)m * N + n) = pack_bf16x4(acc[tm][tn]);
+        if constexpr (SPLIT)
+          *reinterpret_cast<v4f*>(part + ((uint64_t)split * M + m) * N + n) = acc[tm][tn];
+        else
+          *reinterpret_cast<uint2*>(out + (uint64_t)m * N + n) = pack_bf16x4(acc[tm][tn]);
       }
     }
+  }
+}
+
+// out[m, n] = bf16(sum over s < splits, in order, of part[s][m][n]); four
+// columns per thread.
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const v4f* __restrict__ part,
+                                                            uint2* __restrict__ out,
+                                                            uint64_t quads, uint32_t splits) {
+  for (uint64_t i = (uint64_t)blockIdx.x * 256 + threadIdx.x; i < quads;
+       i += (uint64_t)gridDim.x * 256) {
+    v4f s = __builtin_nontemporal_load(&part[i]);
+    for (uint32_t k = 1; k < splits; ++k) s += __builtin_nontemporal_load(&part[k * quads + i]);
+    out[i] = pack_bf16x4(s);
   }
 }
 
@@ -288,6 +319,36 @@ hipError_t launch_tiled_cfg(const uint8_t* a, const float* a_s_km, const uint8_t
   const uint32_t tiles_m = (M + BM - 1) / BM, tiles_n = N / BN;
   gemm_tiled_kernel<BM, BN, WGM, WGN, STAGES, ROW><<<dim3(tiles_m * tiles_n), dim3(C::NT), C::LDS_BYTES, s>>>(
       a, a_s_km, w, w_s, out, M, N, K, m_pad16(M), tiles_m, tiles_n);
+  return hipGetLastError();
+}
+
+// split-K launch of the 128x128 tiled kernel and the reduction
+hipError_t launch_splitk_128_t(const uint8_t* a, const float* a_s_km, const uint8_t* w,
+                               const float* w_s, uint16_t* out, float* part, uint32_t M,
+                               uint32_t N, uint32_t K, uint32_t splits, hipStream_t s) {
+  constexpr int BM = 128, BN = 128, WGM = 2, WGN = 2, STAGES = 2;
+  using C = TileCfg<BM, BN, WGM, WGN, STAGES, false>;
+  if (N % BN != 0 || splits < 2 || splits > K / kGroup) return hipErrorInvalidValue;
+  static bool attr_set = false;  // idempotent; racing threads set the same value
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(&gemm_tiled_kernel<BM, BN, WGM, WGN, STAGES, false, true>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  const uint32_t tiles_m = (M + BM - 1) / BM, tiles_n = N / BN;
+  gemm_tiled_kernel<BM, BN, WGM, WGN, STAGES, false, true>
+      <<<dim3(tiles_m * tiles_n * splits), dim3(C::NT), C::LDS_BYTES, s>>>(
+          a, a_s_km, w, w_s, out, M, N, K, m_pad16(M), tiles_m, tiles_n, splits, part);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const uint64_t quads = (uint64_t)M * N / 4;
+  const uint64_t blocks = (quads + 255) / 256;
+  const uint32_t grid = (uint32_t)(blocks < 4096 ? blocks : 4096);
+  splitk_reduce_kernel<<<dim3(grid), dim3(256), 0, s>>>(reinterpret_cast<const v4f*>(part),
+                                                          reinterpret_cast<uint2*>(out), quads,
+                                                          splits);
   return hipGetLastError();
 }
 // ------------------------------------------------------------------------
@@ -927,6 +988,12 @@ hipError_t launch_ffn_gate_up(const uint8_t* x, const float* x_s_km, const uint8
                               hipStream_t s) {
   return launch_pp_cfg<3, false, true>(x, x_s_km, w_gate, ws_gate, nullptr, M, I, H, s,
                                        FfnArgs{w_up, ws_up, hq, hs_km});
+}
+
+hipError_t launch_splitk_128(const uint8_t* a, const float* a_s_km, const uint8_t* w,
+                             const float* w_s, uint16_t* out, float* part, uint32_t M,
+                             uint32_t N, uint32_t K, uint32_t splits, hipStream_t s) {
+  return launch_splitk_128_t(a, a_s_km, w, w_s, out, part, M, N, K, splits, s);
 }
 
 }  // namespace fp8q

@@ -99,5 +99,25 @@ __device__ __forceinline__ void tile_coords(uint32_t tiles_m, uint32_t tiles_n, 
   tni = (t % per_group) / gm;
 }
 
+// Split-K form: the grid holds splits workgroups per tile.  Workgroup ids
+// are dealt to the XCDs as above over tiles_m * tiles_n * splits slots; the
+// slot picks the tile (grouped order) and the split.
+__device__ __forceinline__ void tile_split_coords(uint32_t tiles_m, uint32_t tiles_n,
+                                                  uint32_t splits, uint32_t& tmi, uint32_t& tni,
+                                                  uint32_t& split) {
+  const uint32_t nslots = tiles_m * tiles_n * splits;
+  const uint32_t bid = blockIdx.x, xcd = bid & 7, slot = bid >> 3;
+  const uint32_t q = nslots >> 3, r8 = nslots & 7;
+  const uint32_t v = (xcd < r8) ? xcd * (q + 1) + slot : r8 * (q + 1) + (xcd - r8) * q + slot;
+  split = v % splits;
+  const uint32_t t = v / splits;
+  constexpr uint32_t GROUP_M = 8;
+  const uint32_t per_group = GROUP_M * tiles_n;
+  const uint32_t group = t / per_group, first_m = group * GROUP_M;
+  const uint32_t gm = min(tiles_m - first_m, GROUP_M);
+  tmi = first_m + (t % per_group) % gm;
+  tni = (t % per_group) / gm;
+}
+
 }  // namespace
 }  // namespace fp8q
