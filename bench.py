@@ -22,6 +22,8 @@ quantized per 128x128 block.  Prints ONE JSON line:
   cpu_baseline    the CPU oracle on a bounded sample of the same workload
   bf16_comparator the same GEMM in bf16 over the dequantized weights (our
                   bf16 MFMA kernel and hipBLASLt), and the FP8 speedup
+  fp8_library_comparator  hipBLASLt's FP8 GEMM (torch._scaled_mm) on the same
+                  codes with per-tensor / per-row scales, for context
 
 Other modes (one JSON line each, not the benchmark line): --quant-sweep,
 --dequant, --ffn <workload> (the dense FFN chain), --ffn-sweep (its
@@ -578,7 +580,36 @@ def main():
     b1.record(stream)
     torch.cuda.synchronize()
     bf16_lib_us = b0.elapsed_time(b1) * 1e3 / R
-    del wts, wd, outb
+    del wts, wd
+
+    # FP8 library comparator (context): the vendor library's FP8 GEMM through
+    # torch._scaled_mm on the same code bytes, with the scaling modes it
+    # offers (one scale per tensor; one per activation row and weight row)
+    # instead of 128x128 blocks -- a different, simpler operation
+    fp8_lib = {}
+    if not per_row and hasattr(torch, "_scaled_mm"):
+        a8 = act_q.view(torch.float8_e4m3fn)
+        w8s = [wq.view(torch.float8_e4m3fn), wq.clone().view(torch.float8_e4m3fn)]
+        one = torch.ones((), dtype=torch.float32, device=dev)
+        modes = {"per_tensor": (one, one),
+                 "rowwise": (torch.ones((M, 1), dtype=torch.float32, device=dev),
+                             torch.ones((1, N), dtype=torch.float32, device=dev))}
+        for name, (sa, sb) in modes.items():
+            try:
+                torch._scaled_mm(a8, w8s[0].t(), scale_a=sa, scale_b=sb, out_dtype=torch.bfloat16)
+                torch.cuda.synchronize()
+                b0.record(stream)
+                for i in range(R):
+                    torch._scaled_mm(a8, w8s[i % 2].t(), scale_a=sa, scale_b=sb,
+                                     out_dtype=torch.bfloat16)
+                b1.record(stream)
+                torch.cuda.synchronize()
+                us = b0.elapsed_time(b1) * 1e3 / R
+                fp8_lib[name] = {"us": round(us, 2), "tflops": round(2.0 * M * N * K / us / 1e6, 1)}
+            except Exception as ex:  # not offered on this build / device
+                fp8_lib[name] = {"error": str(ex).splitlines()[0][:160]}
+        del w8s
+    del outb
 
     gpu_ms = t_start.elapsed_time(t_end)
     ms_per_step = max(gpu_ms, wall * 1e3) / args.steps
@@ -668,6 +699,11 @@ def main():
             "fp8_over_own_bf16": round(bf16_own_us / gemm_b2b_us, 3),
             "fp8_over_hipblaslt_bf16": round(bf16_lib_us / gemm_b2b_us, 3),
             "bf16_peak_tflops": BF16_PEAK_TFLOPS,
+        },
+        "fp8_library_comparator": {
+            "what": "hipBLASLt FP8 GEMM via torch._scaled_mm on the same code bytes with "
+                    "per-tensor or per-row scales (not block scales), back-to-back launches",
+            **fp8_lib,
         },
     }
     print(json.dumps(rec), flush=True)
