@@ -423,12 +423,36 @@ def cpu_baseline(w, x_bits, wf, budget_s, per_row=False):
         t0 = time.perf_counter()
         a, a_s = oracle.quant_act(xs)
         oracle.scale_to_kmajor(a_s)
+        t1 = time.perf_counter()
         oracle.gemm_ref(a, a_s, wq, ws)
-        return time.perf_counter() - t0
-    t2 = run(2)
+        return t1 - t0, time.perf_counter() - t1
+    t2 = sum(run(2))
     R = int(max(2, min(w.M, 2 * budget_s / max(t2, 1e-6))))
     R = max(2, min(R, w.M))
-    t = run(R)
+    tq, tg = run(R)
+    t = tq + tg
+    # the quantizer and relayout on one thread as well (OpenMP runtime of the oracle)
+    tq1 = None
+    try:
+        import ctypes
+        gomp = ctypes.CDLL("libgomp.so.1")
+        gomp.omp_set_num_threads(1)
+        try:
+            xs = np.ascontiguousarray(x_bits[:R])
+            t0 = time.perf_counter()
+            _, a_s = oracle.quant_act(xs)
+            oracle.scale_to_kmajor(a_s)
+            tq1 = time.perf_counter() - t0
+        finally:
+            gomp.omp_set_num_threads(threads)
+    except OSError:
+        pass
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), None)
+    except OSError:
+        pass
     flops = 2.0 * R * w.N * w.K
     return {
         "value": round(flops / t / 1e12, 6),
@@ -436,7 +460,11 @@ def cpu_baseline(w, x_bits, wf, budget_s, per_row=False):
         "cores": threads,
         "kind": "oracle",
         "sample": f"first {R} of {w.M} rows of {w.desc}: quantize + relayout + fp64 block GEMM "
-                  f"({t:.1f} s)",
+                  f"({t:.1f} s, one run)",
+        "cpu_model": model,
+        "quant_relayout_s": round(tq, 4),
+        "gemm_s": round(tg, 3),
+        "quant_relayout_1thread_s": None if tq1 is None else round(tq1, 4),
     }
 
 
@@ -623,6 +651,12 @@ def main():
     quant_avg_s = float(np.mean(quant_ms)) * 1e-3
     quant_gbs = quant_bytes / quant_avg_s / 1e9
 
+    def pct(ms):  # per-launch event times of the timed steps
+        p10, p50, p90 = np.percentile(np.asarray(ms) * 1e3, [10, 50, 90])
+        return {"p10_us": round(float(p10), 2), "median_us": round(float(p50), 2),
+                "p90_us": round(float(p90), 2)}
+    gemm_pct = pct(gemm_ms)
+
     kern = fp8q.fp8q_gemm_select(M, N, K)
     if kern == 2:
         # decode widths: the GEMM streams the weight matrix once (HBM-bound)
@@ -632,6 +666,7 @@ def main():
                     "achieved": round(gemm_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": round(gemm_gbs / HBM_PEAK_GBS, 4), "traffic": None,
                     "avg_launch_us": round(gemm_avg_s * 1e6, 2),
+                    **gemm_pct,
                     "back_to_back_us": round(gemm_b2b_us, 2),
                     "back_to_back_achieved": round(gemm_bytes / gemm_b2b_us / 1e3, 1),
                     "algorithmic_bytes_per_launch": gemm_bytes}
@@ -642,6 +677,7 @@ def main():
                     "traffic": (gemm_traffic() if args.workload == "large_prefill" and not per_row
                                 else None),
                     "avg_launch_us": round(gemm_avg_s * 1e6, 2),
+                    **gemm_pct,
                     "back_to_back_us": round(gemm_b2b_us, 2),
                     "back_to_back_achieved": round(flops / gemm_b2b_us / 1e6, 2),
                     "algorithmic_flops_per_launch": flops}
@@ -683,6 +719,7 @@ def main():
             "achieved": round(quant_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(quant_gbs / HBM_PEAK_GBS, 4),
             "avg_launch_us": round(quant_avg_s * 1e6, 2),
+            **pct(quant_ms),
             "back_to_back_us": round(quant_b2b_us, 2),
             "back_to_back_achieved": round(quant_bytes / quant_b2b_us / 1e3, 1),
             "algorithmic_bytes_per_launch": quant_bytes,
