@@ -27,7 +27,8 @@ quantized per 128x128 block.  Prints ONE JSON line:
 
 Other modes (one JSON line each, not the benchmark line): --quant-sweep,
 --dequant, --ffn <workload> (the dense FFN chain), --ffn-sweep (its
-selector), --copy-mib N.
+selector), --gemm-sweep (split-K), --cpu-sweep (the CPU oracle baseline
+per shape), --copy-mib N.
 
 Only one GPU is used; --gpus above 1 exits with a message.
 """
@@ -99,6 +100,10 @@ def parse():
     p.add_argument("--gemm-sweep", action="store_true",
                    help="the GEMM's single-pass kernels and split-K counts over M at three "
                         "projection shapes with cold caches (the split-K selector's measurement)")
+    p.add_argument("--cpu-sweep", action="store_true",
+                   help="instead of the benchmark, time the CPU oracle on the host cores: "
+                        "quantizer + relayout per quantizer-sweep shape (all threads and one), "
+                        "fp64 GEMM per GEMM workload (no GPU used)")
     p.add_argument("--copy-mib", type=int, default=0,
                    help="instead of the benchmark, run 3 plain device copies of this many "
                         "MiB (the reference kernel for scaling rocprofv3 byte counters)")
@@ -390,6 +395,68 @@ def gemm_sweep(reps=10):
         del wq, wsc
 
 
+def cpu_sweep():
+    """The oracle on the host cores, as the CPU baseline plan lays out: the
+    quantizer + relayout on every quantizer-sweep shape (all threads and one
+    thread) and the fp64 block GEMM on every GEMM workload; the median of 3
+    runs (one run where a run exceeds 30 s).  One JSON line per item."""
+    import ctypes
+    import oracle
+    import synth
+    oracle._load()
+    threads = oracle.num_threads()
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), None)
+    except OSError:
+        pass
+    gomp = ctypes.CDLL("libgomp.so.1")
+
+    def med3(fn):
+        t0 = time.perf_counter()
+        fn()
+        t = [time.perf_counter() - t0]
+        if t[0] <= 30.0:
+            for _ in range(2):
+                t0 = time.perf_counter()
+                fn()
+                t.append(time.perf_counter() - t0)
+        return float(np.median(t)), len(t)
+
+    print(json.dumps({"cpu_model": model, "threads": threads}), flush=True)
+    for w in synth.WORKLOADS["quant_sweep"]:
+        x, _, _ = synth.make_inputs(w)
+        nbytes = w.M * w.K * 2 + w.M * w.K + w.M * (w.K // 128) * 4      # quantizer
+        nbytes += w.M * (w.K // 128) * 4 + synth.ceil16(w.M) * (w.K // 128) * 4  # relayout
+
+        def q():
+            _, a_s = oracle.quant_act(x)
+            oracle.scale_to_kmajor(a_s)
+        t, n = med3(q)
+        gomp.omp_set_num_threads(1)
+        try:
+            t1, n1 = med3(q)
+        finally:
+            gomp.omp_set_num_threads(threads)
+        print(json.dumps({"item": "quant+relayout", "M": w.M, "K": w.K, "s": round(t, 5),
+                          "GBps": round(nbytes / t / 1e9, 2), "runs": n,
+                          "s_1thread": round(t1, 5), "GBps_1thread": round(nbytes / t1 / 1e9, 3)}),
+              flush=True)
+        del x
+    for name in ("tiny", "decode", "prefill", "large_prefill"):
+        for w in synth.WORKLOADS[name]:
+            x, wf, _ = synth.make_inputs(w)
+            a, a_s = oracle.quant_act(x)
+            wq, ws = oracle.quant_weight_block(wf)
+            del wf
+            t, n = med3(lambda: oracle.gemm_ref(a, a_s, wq, ws))
+            print(json.dumps({"item": "fp64 block GEMM", "workload": w.desc, "s": round(t, 4),
+                              "GFLOPs": round(2.0 * w.M * w.N * w.K / t / 1e9, 2), "runs": n}),
+                  flush=True)
+            del x, a, wq
+
+
 def quantize_weights_gpu(wf, per_row=False):
     """Synthetic FP8 weights: per 128x128 block (or per row), scale = amax/448,
     codes by PyTorch's float8_e4m3fn cast (input preparation, outside the timed
@@ -478,6 +545,9 @@ def main():
 
     if args.copy_mib:
         copy_calibration(args.copy_mib)
+        return
+    if args.cpu_sweep:
+        cpu_sweep()
         return
     if args.quant_sweep:
         quant_sweep()
