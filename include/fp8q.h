@@ -243,11 +243,12 @@ fp8q_status fp8q_gemm_blockscaled_splitk(const uint8_t *a_e4m3, const float *a_s
                                          uint32_t K, uint32_t splits, hipStream_t stream);
 
 /* The split count fp8q_gemm_blockscaled_splitk takes for splits = 0, with
- * T = ceil(M/128) * (N/128) tiles of 128x128:
- *   min(floor(512 / T), floor(K / 1280), 6)   (one round of two workgroups
- *   per CU on 256 CUs; at least 10 K blocks a split)
+ * T = ceil(M/128) * (N/128) tiles of 128x128 and c = min(floor(K/1280), 6)
+ * (at least 10 K blocks a split):
+ *   min(floor(256 / T), c) if that is at least 2 (one workgroup per CU on
+ *   256 CUs), else min(floor(512 / T), c) (two per CU)
  * when M > 64 and fp8q_gemm_select does not pick the 256x128 kernel (id 5),
- * and 1 (no split) otherwise or when that minimum is below 2.  0 if N or K
+ * and 1 (no split) otherwise or when that count is below 2.  0 if N or K
  * is not a positive multiple of 128.  Pure host function. */
 uint32_t fp8q_gemm_splitk_select(uint32_t M, uint32_t N, uint32_t K);
 

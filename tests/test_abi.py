@@ -256,13 +256,14 @@ def test_splitk_workspace_bytes():
 
 
 def test_splitk_select():
-    """Split count: min(floor(512 / tiles), floor(K/1280), 6) above 64 rows,
-    outside the 256x128 kernel's range, 1 below 2; 0 for a bad N or K."""
+    """Split count above 64 rows, outside the 256x128 kernel's range, with
+    c = min(floor(K/1280), 6): min(floor(256 / tiles), c) if at least 2,
+    else min(floor(512 / tiles), c), 1 below 2; 0 for a bad N or K."""
     sel = fp8q.fp8q_gemm_splitk_select
-    for M, want in ((16, 1), (64, 1), (65, 6), (128, 6), (129, 6), (256, 6), (257, 4), (384, 4),
+    for M, want in ((16, 1), (64, 1), (65, 6), (128, 6), (129, 3), (256, 3), (257, 2), (384, 2),
                     (385, 3), (512, 3), (513, 2), (768, 2), (769, 1), (1168, 1), (2048, 1)):
         assert sel(M, 5120, 17408) == want, M
-    for M, want in ((65, 4), (256, 4), (384, 3), (512, 2), (640, 2), (768, 1)):
+    for M, want in ((65, 4), (256, 2), (384, 3), (512, 2), (640, 2), (768, 1)):
         assert sel(M, 6144, 5120) == want, M
     for M, want in ((65, 3), (128, 3), (129, 1)):
         assert sel(M, 17408, 5120) == want, M

@@ -186,10 +186,12 @@ int gemm_auto_kernel(uint32_t M, uint32_t N) {
   return M >= kWideAutoMinM ? 5 : 1;
 }
 
-// Split-K (fp8q_gemm_blockscaled_splitk): splits = floor(512 / tiles) (the
-// split grid stays within one round of two 128x128 workgroups per CU), at
-// most K/1280 (10 K blocks a split) and 6, for more than kSplitMinM rows
-// and wherever the single-pass choice is not the 256 x 128 kernel.  Cold
+// Split-K (fp8q_gemm_blockscaled_splitk): splits = floor(256 / tiles) when
+// that is at least 2 (the split grid fits one workgroup per CU and runs the
+// three-stage form), else floor(512 / tiles) (one round of two 128x128
+// workgroups per CU, two stages), at most K/1280 (10 K blocks a split) and
+// 6, for more than kSplitMinM rows and wherever the single-pass choice is
+// not the 256 x 128 kernel.  Cold
 // caches (bench.py --gemm-sweep), us single-pass -> split-K: N=5120,
 // K=17408: 87 -> 46 at M=65, 135 -> 55 at M=192, 143 -> 73 at M=384, 143 ->
 // 87 at M=512, 144 -> 109 at M=768; N=6144, K=5120: 32 -> 23 at M=65, 47 ->
@@ -205,9 +207,13 @@ constexpr uint32_t kSplitMaxUser = 64;  // bound of an explicit split count
 uint32_t splitk_auto(uint32_t M, uint32_t N, uint32_t K) {
   if (M <= kSplitMinM || gemm_auto_kernel(M, N) == 5) return 1;
   const uint64_t tiles = (uint64_t)((M + 127) / 128) * (N / 128);
-  const uint64_t s = std::min<uint64_t>(
-      kSplitTargetWgs / tiles, std::min<uint64_t>(K / kGroup / kSplitMinBlocks, kSplitMax));
-  return s < 2 ? 1 : (uint32_t)s;
+  const uint64_t cap = std::min<uint64_t>(K / kGroup / kSplitMinBlocks, kSplitMax);
+  // prefer a count whose grid fits one workgroup per CU (the three-stage
+  // form), else one round of two per CU
+  const uint64_t s1 = std::min<uint64_t>(kSplitTargetWgs / 2 / tiles, cap);
+  if (s1 >= 2) return (uint32_t)s1;
+  const uint64_t s2 = std::min<uint64_t>(kSplitTargetWgs / tiles, cap);
+  return s2 < 2 ? 1 : (uint32_t)s2;
 }
 
 uint64_t splitk_workspace(uint32_t M, uint32_t N, uint32_t splits) {

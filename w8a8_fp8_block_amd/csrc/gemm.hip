@@ -323,12 +323,12 @@ hipError_t launch_tiled_cfg(const uint8_t* a, const float* a_s_km, const uint8_t
 }
 
 // split-K launch of the 128x128 tiled kernel and the reduction
-hipError_t launch_splitk_128_t(const uint8_t* a, const float* a_s_km, const uint8_t* w,
-                               const float* w_s, uint16_t* out, float* part, uint32_t M,
-                               uint32_t N, uint32_t K, uint32_t splits, hipStream_t s) {
-  constexpr int BM = 128, BN = 128, WGM = 2, WGN = 2, STAGES = 2;
+template <int STAGES>
+hipError_t launch_splitk_cfg(const uint8_t* a, const float* a_s_km, const uint8_t* w,
+                             const float* w_s, float* part, uint32_t M, uint32_t N, uint32_t K,
+                             uint32_t splits, hipStream_t s) {
+  constexpr int BM = 128, BN = 128, WGM = 2, WGN = 2;
   using C = TileCfg<BM, BN, WGM, WGN, STAGES, false>;
-  if (N % BN != 0 || splits < 2 || splits > K / kGroup) return hipErrorInvalidValue;
   static bool attr_set = false;  // idempotent; racing threads set the same value
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute(
@@ -340,8 +340,26 @@ hipError_t launch_splitk_128_t(const uint8_t* a, const float* a_s_km, const uint
   const uint32_t tiles_m = (M + BM - 1) / BM, tiles_n = N / BN;
   gemm_tiled_kernel<BM, BN, WGM, WGN, STAGES, false, true>
       <<<dim3(tiles_m * tiles_n * splits), dim3(C::NT), C::LDS_BYTES, s>>>(
-          a, a_s_km, w, w_s, out, M, N, K, m_pad16(M), tiles_m, tiles_n, splits, part);
-  hipError_t e = hipGetLastError();
+          a, a_s_km, w, w_s, nullptr, M, N, K, m_pad16(M), tiles_m, tiles_n, splits, part);
+  return hipGetLastError();
+}
+
+// Split grids that fit one workgroup per CU (kSplitOneRoundWgs) take three
+// LDS stages (99 KB: one workgroup per CU, two blocks of loads in flight);
+// larger ones two (two workgroups per CU).  Measured with cold caches at
+// N = 5120, K = 17408: 44.2 / 47.8 / 56.5 us against 46.0 / 50.9 / 64.5 us
+// at M = 65 / 128 / 256; at N = 6144, K = 5120: 22.2 / 25.4 / 32.3 against
+// 23.2 / 27.5 / 36.3 us.
+constexpr uint32_t kSplitOneRoundWgs = 256;
+
+hipError_t launch_splitk_128_t(const uint8_t* a, const float* a_s_km, const uint8_t* w,
+                               const float* w_s, uint16_t* out, float* part, uint32_t M,
+                               uint32_t N, uint32_t K, uint32_t splits, hipStream_t s) {
+  if (N % 128 != 0 || splits < 2 || splits > K / kGroup) return hipErrorInvalidValue;
+  const uint64_t wgs = (uint64_t)((M + 127) / 128) * (N / 128) * splits;
+  hipError_t e = wgs <= kSplitOneRoundWgs
+                     ? launch_splitk_cfg<3>(a, a_s_km, w, w_s, part, M, N, K, splits, s)
+                     : launch_splitk_cfg<2>(a, a_s_km, w, w_s, part, M, N, K, splits, s);
   if (e != hipSuccess) return e;
   const uint64_t quads = (uint64_t)M * N / 4;
   const uint64_t blocks = (quads + 255) / 256;
