@@ -328,6 +328,24 @@ fp8q_status fp8q_proj(const uint16_t *x_bf16, const uint8_t *w_e4m3,
                       float *act_scale_km_scratch, uint32_t M, uint32_t N,
                       uint32_t K, hipStream_t stream);
 
+/* As fp8q_proj, with the GEMM run as fp8q_gemm_blockscaled_splitk with
+ * splits = 0 (the automatic count of fp8q_gemm_splitk_select; where that is
+ * 1, fp8q_gemm_blockscaled's automatic kernel and the workspace is not
+ * touched):
+ *   workspace        device memory, 16-byte aligned, at least
+ *                    fp8q_gemm_splitk_workspace_bytes(M, N, K, 0) bytes (may
+ *                    be NULL when that is 0); contents undefined on return;
+ *                    calls in flight must not share it
+ *   workspace_bytes  smaller than needed -> FP8Q_ERR_SHAPE (before any launch)
+ * The codes and scales written to the scratch buffers are those of
+ * fp8q_proj; the output is fp8q_gemm_blockscaled_splitk's on them. */
+fp8q_status fp8q_proj_splitk(const uint16_t *x_bf16, const uint8_t *w_e4m3,
+                             const float *w_scale, uint16_t *out_bf16,
+                             uint8_t *act_q_scratch, float *act_scale_scratch,
+                             float *act_scale_km_scratch, void *workspace,
+                             size_t workspace_bytes, uint32_t M, uint32_t N, uint32_t K,
+                             hipStream_t stream);
+
 /* As fp8q_proj with per-row weight scales w_scale_row [N] (see
  * fp8q_gemm_rowscaled). */
 fp8q_status fp8q_proj_rowscaled(const uint16_t *x_bf16, const uint8_t *w_e4m3,

@@ -288,3 +288,19 @@ def test_ffn_workspace_holds_split_partials():
                 + a256(Mp * I // 128 * 4))
         assert fp8q.fp8q_ffn_workspace_bytes(M, H, I, 1) == base + a256(extra), M
         assert fp8q.fp8q_ffn_workspace_bytes(M, H, I, 2) == base + 2 * a256(2 * M * I) + a256(extra)
+
+
+def test_proj_splitk_validation():
+    L = fp8q.lib()
+    g = GOOD
+    M, N, K = 200, 1024, 5120
+    assert fp8q.fp8q_gemm_splitk_select(M, N, K) == 4
+    need = fp8q.fp8q_gemm_splitk_workspace_bytes(M, N, K, 0)
+    assert need == 4 * M * N * 4
+    # fp8q_proj_splitk(x, w, ws, out, aq, as, askm, work, bytes, M, N, K, stream)
+    assert L.fp8q_proj_splitk(g, g, g, g, g, g, g, g, need - 1, M, N, K, None) == 2
+    assert "workspace" in _err()
+    assert L.fp8q_proj_splitk(g, g, g, g, g, g, g, None, need, M, N, K, None) == 1
+    assert L.fp8q_proj_splitk(g, g, g, g, g, g, g, BAD, need, M, N, K, None) == 3
+    assert L.fp8q_proj_splitk(g, g, g, g, g, g, g, g, need, M, N, 100, None) == 2
+    assert L.fp8q_proj_splitk(g, g, g, g, g, g, g, None, 0, 0, N, K, None) == 0

@@ -164,3 +164,43 @@ def test_splitk_projection_shapes_sampled(orc, M, N, K):
         o = _splitk_gpu(orc, a, a_s, wq, ws, splits)
         assert np.all(np.isfinite(o))
         _assert_tol(o[ms, ns], ref, f"M{M}N{N}K{K}s{splits}", rms)
+
+
+@pytest.mark.parametrize("M,N,K", [(200, 1024, 5120), (96, 6144, 5120), (40, 512, 2048)])
+def test_proj_splitk(orc, M, N, K):
+    """fp8q_proj_splitk: the quantizer's codes and both scale layouts as
+    fp8q_proj writes them (bit-exact against the oracle), the output equal bit
+    for bit to fp8q_gemm_blockscaled_splitk (splits = 0) on those codes, and
+    within the projection tolerance of the oracle; where the selector does not
+    split (M = 40) the workspace may be absent and the output is fp8q_proj's."""
+    rng = np.random.default_rng(M + N)
+    x = synth.f32_to_bf16_bits((rng.standard_normal((M, K)) *
+                                np.exp(rng.uniform(-2, 2, (M, 1)))).astype(np.float32))
+    wq, ws = orc.quant_weight_block(rng.normal(0, 0.02, (N, K)).astype(np.float32))
+    a, a_s = orc.quant_act(x)
+    splits = fp8q.fp8q_gemm_splitk_select(M, N, K)
+    need = fp8q.fp8q_gemm_splitk_workspace_bytes(M, N, K, 0)
+    log(f"proj_splitk M={M} N={N} K={K} splits={splits}")
+    out = Guarded((M, N), torch.int16)
+    aq = Guarded((M, K), torch.uint8)
+    asr = Guarded((M, K // 128), torch.float32)
+    askm = Guarded((K // 128, synth.ceil16(M)), torch.float32, fill=0x7F)
+    work = Guarded((need // 4,), torch.float32, fill=0x7F) if need else None
+    fp8q.fp8q_proj_splitk(dev(x), dev(wq), dev(ws), out.t, aq.t, asr.t, askm.t,
+                          None if work is None else work.t)
+    torch.cuda.synchronize()
+    for gd in (out, aq, asr, askm) + ((work,) if work is not None else ()):
+        gd.check_canary()
+    assert np.array_equal(host(aq.t), a)
+    assert np.array_equal(host(asr.t).view(np.uint32), a_s.view(np.uint32))
+    assert np.array_equal(host(askm.t).view(np.uint32), orc.scale_to_kmajor(a_s).view(np.uint32))
+    o = bf16_bits_to_f64(host(out.t))
+    if splits >= 2:
+        assert np.array_equal(o, _splitk_gpu(orc, a, a_s, wq, ws, 0))
+    else:
+        assert need == 0
+        ref_out = torch.empty((M, N), dtype=torch.int16, device="cuda")
+        fp8q.fp8q_proj(dev(x), dev(wq), dev(ws), ref_out, aq.t, asr.t, askm.t)
+        torch.cuda.synchronize()
+        assert np.array_equal(o, bf16_bits_to_f64(host(ref_out)))
+    _assert_tol(o, orc.gemm_ref(a, a_s, wq, ws), f"proj_splitk M{M}N{N}K{K}")

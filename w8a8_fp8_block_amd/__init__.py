@@ -73,6 +73,7 @@ _SIGS = {
     "fp8q_gemm_splitk_select": (_U, [_U, _U, _U]),
     "fp8q_gemm_splitk_workspace_bytes": (_SZ, [_U, _U, _U, _U]),
     "fp8q_proj": (_I, [_P, _P, _P, _P, _P, _P, _P, _U, _U, _U, _P]),
+    "fp8q_proj_splitk": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _SZ, _U, _U, _U, _P]),
     "fp8q_gemm_rowscaled": (_I, [_P, _P, _P, _P, _P, _U, _U, _U, _P]),
     "fp8q_gemm_rowscaled_ex": (_I, [_P, _P, _P, _P, _P, _U, _U, _U, _I, _P]),
     "fp8q_proj_rowscaled": (_I, [_P, _P, _P, _P, _P, _P, _P, _U, _U, _U, _P]),
@@ -215,6 +216,20 @@ def fp8q_proj(x, w, w_scale, out, act_q, act_scale, act_scale_km, stream=None):
         raise ValueError("x and w disagree on K")
     _check(lib().fp8q_proj(_ptr(x), _ptr(w), _ptr(w_scale), _ptr(out), _ptr(act_q),
                           _ptr(act_scale), _ptr(act_scale_km), M, N, K, _stream(stream)))
+
+
+def fp8q_proj_splitk(x, w, w_scale, out, act_q, act_scale, act_scale_km, workspace, stream=None):
+    """fp8q_proj with the GEMM split over K where fp8q_gemm_splitk_select says
+    so; workspace: a device tensor of at least
+    fp8q_gemm_splitk_workspace_bytes(M, N, K) bytes, or None when that is 0."""
+    M, K = _dims(x, 2)
+    N, K2 = _dims(w, 2)
+    if K2 != K:
+        raise ValueError("x and w disagree on K")
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().fp8q_proj_splitk(_ptr(x), _ptr(w), _ptr(w_scale), _ptr(out), _ptr(act_q),
+                                 _ptr(act_scale), _ptr(act_scale_km), _optr(workspace), nbytes,
+                                 M, N, K, _stream(stream)))
 
 
 def fp8q_gemm_rowscaled(a, a_scale_km, w, w_scale_row, out, kernel: int = 0, stream=None):

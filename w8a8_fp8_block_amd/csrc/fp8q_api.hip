@@ -266,15 +266,20 @@ fp8q_status check_gemm_args(const char* fn, const uint8_t* a_e4m3, const float* 
   return FP8Q_OK;
 }
 
+// split_k: fp8q_proj_splitk (the GEMM takes the automatic split count and
+// split_ws, a caller workspace of split_ws_bytes, holds the partials); the
+// other projections run the single-pass automatic kernel.
 fp8q_status run_proj(const char* fn, const uint16_t* x_bf16, const uint8_t* w_e4m3,
                      const float* w_scale, uint16_t* out_bf16, uint8_t* act_q_scratch,
                      float* act_scale_scratch, float* act_scale_km_scratch, uint32_t M, uint32_t N,
-                     uint32_t K, bool row_scaled, hipStream_t stream);
+                     uint32_t K, bool row_scaled, hipStream_t stream, bool split_k = false,
+                     void* split_ws = nullptr, size_t split_ws_bytes = 0);
 
 fp8q_status run_proj(const char* fn, const uint16_t* x_bf16, const uint8_t* w_e4m3,
                      const float* w_scale, uint16_t* out_bf16, uint8_t* act_q_scratch,
                      float* act_scale_scratch, float* act_scale_km_scratch, uint32_t M, uint32_t N,
-                     uint32_t K, bool row_scaled, hipStream_t stream) {
+                     uint32_t K, bool row_scaled, hipStream_t stream, bool split_k,
+                     void* split_ws, size_t split_ws_bytes) {
   fp8q_status st = check_mk(fn, M, K);
   if (st != FP8Q_OK) return st;
   st = check_n(fn, M, N, K);
@@ -288,6 +293,15 @@ fp8q_status run_proj(const char* fn, const uint16_t* x_bf16, const uint8_t* w_e4
   REQUIRE_PTR(act_scale_scratch);
   REQUIRE_PTR(act_scale_km_scratch);
   if (M == 0) return ok();
+  const uint32_t splits = split_k ? splitk_auto(M, N, K) : 1;
+  if (splits >= 2) {
+    const uint64_t need = splitk_workspace(M, N, splits);
+    void* workspace = split_ws;
+    REQUIRE_PTR(workspace);
+    if (split_ws_bytes < need)
+      return fail(FP8Q_ERR_SHAPE, "%s: workspace of %llu bytes, %llu needed", fn,
+                  (unsigned long long)split_ws_bytes, (unsigned long long)need);
+  }
   if ((uint64_t)M * (K / kGroup) <= kFusedKmajorMaxGroups) {
     // one kernel writes both scale layouts (saves a launch)
     st = run_quant(fn, x_bf16, act_q_scratch, act_scale_scratch, act_scale_km_scratch, M, K, 0,
@@ -299,6 +313,10 @@ fp8q_status run_proj(const char* fn, const uint16_t* x_bf16, const uint8_t* w_e4
     st = launched(fn, launch_relayout(act_scale_scratch, act_scale_km_scratch, M, K, stream));
     if (st != FP8Q_OK) return st;
   }
+  if (splits >= 2)
+    return launched(fn, launch_splitk_128(act_q_scratch, act_scale_km_scratch, w_e4m3, w_scale,
+                                          out_bf16, static_cast<float*>(split_ws), M, N, K, splits,
+                                          stream));
   return run_gemm(fn, act_q_scratch, act_scale_km_scratch, w_e4m3, w_scale, out_bf16, M, N, K, 0,
                   row_scaled, stream);
 }
@@ -619,6 +637,15 @@ fp8q_status fp8q_proj(const uint16_t* x_bf16, const uint8_t* w_e4m3, const float
                       hipStream_t stream) {
   return run_proj("fp8q_proj", x_bf16, w_e4m3, w_scale, out_bf16, act_q_scratch,
                   act_scale_scratch, act_scale_km_scratch, M, N, K, false, stream);
+}
+
+fp8q_status fp8q_proj_splitk(const uint16_t* x_bf16, const uint8_t* w_e4m3, const float* w_scale,
+                             uint16_t* out_bf16, uint8_t* act_q_scratch, float* act_scale_scratch,
+                             float* act_scale_km_scratch, void* workspace, size_t workspace_bytes,
+                             uint32_t M, uint32_t N, uint32_t K, hipStream_t stream) {
+  return run_proj("fp8q_proj_splitk", x_bf16, w_e4m3, w_scale, out_bf16, act_q_scratch,
+                  act_scale_scratch, act_scale_km_scratch, M, N, K, false, stream, true, workspace,
+                  workspace_bytes);
 }
 
 fp8q_status fp8q_proj_rowscaled(const uint16_t* x_bf16, const uint8_t* w_e4m3,
