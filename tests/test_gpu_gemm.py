@@ -289,3 +289,30 @@ def test_tiled_kernels_bit_identical(orc, M, N, K):
         outs[kern] = _gemm_gpu(orc, a, a_s, wq, ws, kern)
     for kern in (3, 4, 5, 0):
         assert np.array_equal(outs[kern], outs[1]), f"kernel {kern} differs from kernel 1"
+
+
+@pytest.mark.parametrize("M,N,K", [(17, 384, 640), (25, 256, 1152), (130, 640, 896)])
+def test_proj_deterministic_pattern(orc, M, N, K):
+    """The whole projection on deterministic, seed-free data of the form
+    ((k * 7919) mod 1013 - 506) / 97 over the flat element index (activations)
+    and the same form scaled by 1/50 with an offset index (weights), at widths
+    that are not tile multiples: codes and scales bit-exact, output within the
+    projection tolerance of the oracle."""
+    k = np.arange(M * K, dtype=np.int64)
+    x = synth.f32_to_bf16_bits((((k * 7919) % 1013 - 506) / 97.0).astype(np.float32).reshape(M, K))
+    kw = np.arange(N * K, dtype=np.int64) + 12345
+    wf = ((((kw * 7919) % 1013 - 506) / 97.0) / 50.0).astype(np.float32).reshape(N, K)
+    a, a_s = orc.quant_act(x)
+    wq, ws = orc.quant_weight_block(wf)
+    out = Guarded((M, N), torch.int16)
+    aq = Guarded((M, K), torch.uint8)
+    asr = Guarded((M, K // 128), torch.float32)
+    askm = Guarded((K // 128, synth.ceil16(M)), torch.float32, fill=0x7F)
+    fp8q.fp8q_proj(dev(x), dev(wq), dev(ws), out.t, aq.t, asr.t, askm.t)
+    torch.cuda.synchronize()
+    for g in (out, aq, asr, askm):
+        g.check_canary()
+    assert np.array_equal(host(aq.t), a)
+    assert np.array_equal(host(asr.t).view(np.uint32), a_s.view(np.uint32))
+    assert np.array_equal(host(askm.t).view(np.uint32), orc.scale_to_kmajor(a_s).view(np.uint32))
+    _assert_tol(bf16_bits_to_f64(host(out.t)), orc.gemm_ref(a, a_s, wq, ws), f"pattern M{M}N{N}K{K}")
