@@ -15,11 +15,10 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // ---- quantizer geometry (shared with the selector) ----
-// Variant A: flat over all M*(K/128) groups; each 16-lane row takes
-// kQuantARounds consecutive groups, kQuantAWaves waves per workgroup.
+// Variant A: flat over all M*(K/128) groups, 8 lanes per group,
+// kQuantAWaves waves per workgroup.
 constexpr uint32_t kQuantAWaves = 4;
-constexpr uint32_t kQuantARounds = 2;
-constexpr uint32_t kQuantAGroupsPerWg = 4 * kQuantAWaves * kQuantARounds;
+constexpr uint32_t kQuantAGroupsPerWg = 8 * kQuantAWaves;
 // Variant B: K-grouped; a workgroup covers kQuantBGroupsPerWg consecutive
 // groups of one token row, kQuantBRounds groups per 16-lane row.
 constexpr uint32_t kQuantBWaves = 4;

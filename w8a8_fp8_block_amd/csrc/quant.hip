@@ -8,20 +8,24 @@
 // 128 bf16, so group i lives at x + 128*i, its codes at q + 128*i and its
 // row-major scale at scale_rm[i].
 //
-// Work split: one 16-lane DPP row of a wave owns one group at a time; each
-// lane holds 8 bf16 (one 128-bit load) and produces 8 codes (one 64-bit
-// store).  The group
-// maximum is an integer max over bf16 magnitudes (packed u16 max, then a
-// 4-step DPP butterfly inside the row), which is exact and needs no float
-// canonicalization.
+// Work split: variant A gives each group 8 lanes of a wave, 16 values per
+// lane (two 128-bit loads, two 64-bit stores), variant B one 16-lane DPP row,
+// 8 values per lane.  The group maximum is an integer max over bf16
+// magnitudes (packed u16 max, then a DPP butterfly inside the 8 or 16
+// lanes), which is exact and needs no float canonicalization.  The scale
+// amax/448 and its reciprocal take no divide (quant_common.h), so the vector
+// ALU work per value is the unpack, three fp32 operations and half a packed
+// conversion: at prefill sizes the kernel then runs close to a pure stream
+// with the same access pattern.
 //
 // Exactness of q = fl32(x / scale) without a divide per element: with
-// r = fl32(1 / scale) (a correctly rounded divide, once per group),
+// r = fl32(1 / scale) (correctly rounded, once per group),
 //   q0 = x * r,  en = fma(q0, scale, -x),  q1 = fma(-en, r, q0)
 // is the correctly rounded quotient, signed zeros included, for every bf16
-// pair (x, amax) whose scale is at least 2^-100; groups with a smaller (or zero) scale take an exact
-// per-element divide instead.  The e4m3 code is the hardware conversion of
-// q1 clamped to [-448, 448] (values in (448, 464) round to 448 anyway).
+// pair (x, amax) whose scale is at least 2^-100; groups with a smaller (or
+// zero) scale take an exact per-element divide instead.  The e4m3 code is
+// the hardware conversion of q1, which rounds the largest quotients (448 and
+// at most one fp32 ulp above) to 448 just as the pages' clamp to +-448 does.
 // The exhaustive (x, amax) test checks the whole map on the device.
 #include "quant_common.h"
 
@@ -37,30 +41,38 @@ __device__ __forceinline__ void write_scales(float s, uint64_t g, float* __restr
   }
 }
 
-// Variant A (fine-grained): flat over groups; each 16-lane row takes
-// kQuantARounds consecutive groups, all loads issued before any is consumed
-// (two 128-bit loads in flight per lane: measured 5-8% faster than one on
-// gfx950 at prefill sizes), and the codes, which nothing reads back soon,
-// are stored non-temporally.
+// Variant A (fine-grained): flat over groups; 8 lanes per group, lane l
+// holding elements 8l..8l+7 and 64+8l..64+8l+7 (each of the two loads covers
+// the group's 256 bytes contiguously across its 8 lanes).  Against 16 lanes
+// of 8 values this halves the per-group work per value (butterfly, scale,
+// reciprocal, addresses) at the same bytes in flight per lane.  The codes,
+// which nothing reads back soon, are stored non-temporally.
 __global__ __launch_bounds__(64 * kQuantAWaves) void quant_a_kernel(
     const u32x4* __restrict__ x, u32x2* __restrict__ q, float* __restrict__ srm,
     float* __restrict__ skm, uint64_t ngroups, uint32_t G, uint32_t Mp) {
-  const uint64_t g0 =
-      ((uint64_t)blockIdx.x * (kQuantAGroupsPerWg / kQuantARounds) + (threadIdx.x >> 4)) * kQuantARounds;
-  const uint32_t l = threadIdx.x & 15;
-  u32x4 v[kQuantARounds];
-#pragma unroll
-  for (uint32_t r = 0; r < kQuantARounds; ++r)
-    if (g0 + r < ngroups) v[r] = __builtin_nontemporal_load(&x[(g0 + r) * 16 + l]);
-#pragma unroll
-  for (uint32_t r = 0; r < kQuantARounds; ++r) {
-    if (g0 + r < ngroups) {  // uniform over the 16-lane row
-      float s;
-      const u32x2 c = quant_group(v[r], s);
-      __builtin_nontemporal_store(c, &q[(g0 + r) * 16 + l]);
-      if (l == 0) write_scales(s, g0 + r, srm, skm, G, Mp);
-    }
-  }
+  const uint64_t g = (uint64_t)blockIdx.x * kQuantAGroupsPerWg + (threadIdx.x >> 3);
+  const uint32_t l = threadIdx.x & 7;
+  if (g >= ngroups) return;  // uniform over the group's 8 lanes
+  const u32x4 v0 = __builtin_nontemporal_load(&x[g * 16 + l]);
+  const u32x4 v1 = __builtin_nontemporal_load(&x[g * 16 + 8 + l]);
+  const uint32_t mag = 0x7FFF7FFFu;
+  const u16x2 m0 = __builtin_elementwise_max(as_u16x2(v0.x & mag), as_u16x2(v0.y & mag));
+  const u16x2 m1 = __builtin_elementwise_max(as_u16x2(v0.z & mag), as_u16x2(v0.w & mag));
+  const u16x2 m2 = __builtin_elementwise_max(as_u16x2(v1.x & mag), as_u16x2(v1.y & mag));
+  const u16x2 m3 = __builtin_elementwise_max(as_u16x2(v1.z & mag), as_u16x2(v1.w & mag));
+  const u16x2 mm = __builtin_elementwise_max(__builtin_elementwise_max(m0, m1),
+                                             __builtin_elementwise_max(m2, m3));
+  const uint32_t amax = dpp_half_row_max_u32(max((uint32_t)mm.x, (uint32_t)mm.y));
+  const float s = group_scale(amax);
+  const float xv[16] = {bf_lo(v0.x), bf_hi(v0.x), bf_lo(v0.y), bf_hi(v0.y), bf_lo(v0.z),
+                        bf_hi(v0.z), bf_lo(v0.w), bf_hi(v0.w), bf_lo(v1.x), bf_hi(v1.x),
+                        bf_lo(v1.y), bf_hi(v1.y), bf_lo(v1.z), bf_hi(v1.z), bf_lo(v1.w),
+                        bf_hi(v1.w)};
+  float qv[16];
+  quotients<16>(xv, s, qv);
+  __builtin_nontemporal_store(u32x2{encode4(qv), encode4(qv + 4)}, &q[g * 16 + l]);
+  __builtin_nontemporal_store(u32x2{encode4(qv + 8), encode4(qv + 12)}, &q[g * 16 + 8 + l]);
+  if (l == 0) write_scales(s, g, srm, skm, G, Mp);
 }
 
 // Variant B (K-grouped): workgroup (m, by) covers groups

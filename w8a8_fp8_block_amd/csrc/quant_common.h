@@ -23,6 +23,15 @@ __device__ __forceinline__ uint32_t dpp_row_max_u32(uint32_t v) {
   return v;
 }
 
+// The same over the 8-lane halves of each row: quad_perm [1,0,3,2],
+// quad_perm [2,3,0,1], row_half_mirror.
+__device__ __forceinline__ uint32_t dpp_half_row_max_u32(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false));
+  return v;
+}
+
 __device__ __forceinline__ u16x2 as_u16x2(uint32_t v) { return __builtin_bit_cast(u16x2, v); }
 
 // bf16 pair in one dword -> two floats (exact)
@@ -37,7 +46,12 @@ template <int N>
 __device__ __forceinline__ void quotients(const float* x, float s, float* q) {
   const bool slow = !(s >= 0x1p-100f);  // zero or tiny scale
   if (__builtin_amdgcn_ballot_w64(slow) == 0) {
-    const float r = 1.0f / s;  // correctly rounded reciprocal
+    // r = fl32(1/s): the hardware reciprocal (within 1 ulp) and one
+    // Newton-Raphson step with fmas, r = r0 + r0*(1 - s*r0).  From any start
+    // within one ulp of the correctly rounded reciprocal the step lands on
+    // it, for every scale >= 2^-100 that a bf16 group maximum can produce.
+    const float r0 = __builtin_amdgcn_rcpf(s);
+    const float r = __builtin_fmaf(__builtin_fmaf(-s, r0, 1.0f), r0, r0);
 #pragma unroll
     for (int i = 0; i < N; ++i) {
       // en = q0*s - x is the negated residual; q1 = q0 - en*r.  Written this
@@ -54,18 +68,27 @@ __device__ __forceinline__ void quotients(const float* x, float s, float* q) {
 }
 
 // Four quotients -> four e4m3 codes (little-endian bytes in element order):
-// clamp to [-448, 448], then the hardware conversion (round to nearest even).
+// the hardware conversion, round to nearest even.  No clamp is needed: with
+// |x| <= amax and s = fl32(amax/448), |x/s| is at most 448 plus one fp32 ulp,
+// which the conversion rounds to 448 (every (x, amax) pair is checked on the
+// device against the oracle's clamp-then-round).
 __device__ __forceinline__ uint32_t encode4(const float* q) {
-  int c = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_fmed3f(q[0], -448.0f, 448.0f),
-                                          __builtin_amdgcn_fmed3f(q[1], -448.0f, 448.0f), 0, false);
-  c = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_fmed3f(q[2], -448.0f, 448.0f),
-                                      __builtin_amdgcn_fmed3f(q[3], -448.0f, 448.0f), c, true);
+  int c = __builtin_amdgcn_cvt_pk_fp8_f32(q[0], q[1], 0, false);
+  c = __builtin_amdgcn_cvt_pk_fp8_f32(q[2], q[3], c, true);
   return (uint32_t)c;
 }
 
 // Scale of a group from the bit pattern of its bf16 magnitude maximum.
+// fl32(a/448) without a divide: q0 = a*k with k = fl32(1/448), then one
+// fma correction, q0 - (q0*448 - a)*k.  Equal to the correctly rounded
+// quotient for every finite bf16 magnitude a, subnormal results included
+// (all 32640 of them checked); a non-finite maximum keeps a/448 = a.
 __device__ __forceinline__ float group_scale(uint32_t amax_bits) {
-  return __uint_as_float(amax_bits << 16) / 448.0f;  // IEEE (correctly rounded) divide
+  const float a = __uint_as_float(amax_bits << 16);
+  constexpr float k = 1.0f / 448.0f;
+  const float q0 = a * k;
+  const float s = __builtin_fmaf(-__builtin_fmaf(q0, 448.0f, -a), k, q0);
+  return amax_bits >= 0x7F80u ? a : s;
 }
 
 // Quantize the group held by this lane's 16-lane row.  v = this lane's 8 bf16;
