@@ -16,6 +16,7 @@
 // 32 bytes [32*(l/16), 32*(l/16)+32) of the 128-byte K block, for both
 // operands, so both see the same K permutation and the dot product is the
 // full 128-term sum whatever order the hardware assigns to those bytes.
+#include <atomic>
 #include "mfma_common.h"
 #include "quant_common.h"
 
@@ -308,13 +309,13 @@ hipError_t launch_tiled_cfg(const uint8_t* a, const float* a_s_km, const uint8_t
                             hipStream_t s) {
   using C = TileCfg<BM, BN, WGM, WGN, STAGES, ROW>;
   if (N % BN != 0) return hipErrorInvalidValue;
-  static bool attr_set = false;  // idempotent; racing threads set the same value
-  if (!attr_set) {
+  static std::atomic<bool> attr_set{false};  // the call is idempotent: racing threads repeat it
+  if (!attr_set.load(std::memory_order_acquire)) {
     hipError_t e = hipFuncSetAttribute(
         reinterpret_cast<const void*>(&gemm_tiled_kernel<BM, BN, WGM, WGN, STAGES, ROW>),
         hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
     if (e != hipSuccess) return e;
-    attr_set = true;
+    attr_set.store(true, std::memory_order_release);
   }
   const uint32_t tiles_m = (M + BM - 1) / BM, tiles_n = N / BN;
   gemm_tiled_kernel<BM, BN, WGM, WGN, STAGES, ROW><<<dim3(tiles_m * tiles_n), dim3(C::NT), C::LDS_BYTES, s>>>(
@@ -329,13 +330,13 @@ hipError_t launch_splitk_cfg(const uint8_t* a, const float* a_s_km, const uint8_
                              uint32_t splits, hipStream_t s) {
   constexpr int BM = 128, BN = 128, WGM = 2, WGN = 2;
   using C = TileCfg<BM, BN, WGM, WGN, STAGES, false>;
-  static bool attr_set = false;  // idempotent; racing threads set the same value
-  if (!attr_set) {
+  static std::atomic<bool> attr_set{false};  // the call is idempotent: racing threads repeat it
+  if (!attr_set.load(std::memory_order_acquire)) {
     hipError_t e = hipFuncSetAttribute(
         reinterpret_cast<const void*>(&gemm_tiled_kernel<BM, BN, WGM, WGN, STAGES, false, true>),
         hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
     if (e != hipSuccess) return e;
-    attr_set = true;
+    attr_set.store(true, std::memory_order_release);
   }
   const uint32_t tiles_m = (M + BM - 1) / BM, tiles_n = N / BN;
   gemm_tiled_kernel<BM, BN, WGM, WGN, STAGES, false, true>
@@ -774,12 +775,12 @@ hipError_t launch_pp_cfg(const uint8_t* a, const float* a_s_km, const uint8_t* w
   using C = PpCfg<STAGES, ROW, FFN>;
   constexpr uint32_t BNO = FFN ? kGroup : C::BN;  // output columns per tile
   if (N % BNO != 0) return hipErrorInvalidValue;
-  static bool attr_set = false;  // idempotent; racing threads set the same value
-  if (!attr_set) {
+  static std::atomic<bool> attr_set{false};  // the call is idempotent: racing threads repeat it
+  if (!attr_set.load(std::memory_order_acquire)) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_pp_kernel<STAGES, ROW, FFN>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
     if (e != hipSuccess) return e;
-    attr_set = true;
+    attr_set.store(true, std::memory_order_release);
   }
   const uint32_t tiles_m = (M + C::BM - 1) / C::BM, tiles_n = N / BNO;
   gemm_pp_kernel<STAGES, ROW, FFN><<<dim3(tiles_m * tiles_n), dim3(C::NT), C::LDS_BYTES, s>>>(

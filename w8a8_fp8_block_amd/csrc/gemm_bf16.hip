@@ -12,6 +12,7 @@
 // matrix pipe: no scales, no vector-ALU promotion.  Lane l supplies row
 // l % 16 and bf16 elements [8*(l/16), +8) of each 32-deep half-block, for
 // both operands (same K permutation on both sides).
+#include <atomic>
 #include "mfma_common.h"
 
 namespace fp8q {
@@ -187,12 +188,12 @@ hipError_t launch_gemm_bf16(const uint16_t* x, const uint16_t* w, uint16_t* out,
                             uint32_t N, uint32_t K, hipStream_t s) {
   using C = Bf16Cfg;
   if (N % C::BN != 0 || K % 64 != 0) return hipErrorInvalidValue;
-  static bool attr_set = false;  // idempotent; racing threads set the same value
-  if (!attr_set) {
+  static std::atomic<bool> attr_set{false};  // the call is idempotent: racing threads repeat it
+  if (!attr_set.load(std::memory_order_acquire)) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_bf16_kernel),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
     if (e != hipSuccess) return e;
-    attr_set = true;
+    attr_set.store(true, std::memory_order_release);
   }
   const uint32_t tiles_m = (M + C::BM - 1) / C::BM, tiles_n = N / C::BN;
   gemm_bf16_kernel<<<dim3(tiles_m * tiles_n), dim3(C::NT), C::LDS_BYTES, s>>>(x, w, out, M, N, K,
