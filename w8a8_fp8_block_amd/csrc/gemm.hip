@@ -164,9 +164,6 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_tiled_kernel(
   const uint32_t lo1 = l16 * 128 + (((c0 + 1) ^ swz(l16)) * 16);
   auto ld16 = [](const uint8_t* p) -> v4i { return *reinterpret_cast<const v4i*>(p); };
   auto ldf = [](const uint8_t* p) -> float { return *reinterpret_cast<const float*>(p); };
-  auto slot_base = [&](uint32_t kb) -> const uint8_t* {
-    return smem + (kb % STAGES) * C::STAGE_BYTES;
-  };
   const uint32_t a_row0 = wm * C::WM * 128, w_row0 = C::A_BYTES + wn * C::WN * 128;
 
   v4f acc[TM][TN];
@@ -178,7 +175,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_tiled_kernel(
   // ---- prologue: the first STAGES stages, then block 0 into registers ----
   // Stages past the last K block reload the last block (in bounds, never
   // read), so that every iteration issues the same loads and waits for the
-  // same count, and the loop body stays one basic block.
+  // same count, and the loop body stays one basic block per K block.
 #pragma unroll
   for (int s = 0; s < STAGES; ++s) issue_stage(min((uint32_t)s, G - 1), s);
   wait_vmcnt<(STAGES - 1) * C::LOADS>();
@@ -187,7 +184,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_tiled_kernel(
   v8i af[TM], bf0[TN], bf1[TN];
   float as0[TM], as1[TM], ws0, ws1;
   {
-    const uint8_t* s0 = slot_base(0);
+    const uint8_t* s0 = smem;  // slot 0
 #pragma unroll
     for (int tm = 0; tm < TM; ++tm) {
       af[tm].lo = ld16(s0 + a_row0 + tm * 2048 + lo0);
@@ -211,17 +208,21 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_tiled_kernel(
   p[(NP - 1) & 3] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
   float sc[TM], sc_tail = 0.0f;
 
-  auto step = [&](uint32_t kb, const v8i(&bf)[TN], const float(&as)[TM], float ws, v8i(&bfn)[TN],
-                  float(&asn)[TM], float& wsn) {
+  // one K block; S = kb % STAGES, a compile-time constant (the loop below is
+  // unrolled by a multiple of STAGES), so that the LDS addresses of the next
+  // block's fragments are loop-invariant registers plus immediate offsets
+  auto step = [&](uint32_t kb, auto slot_c, const v8i(&bf)[TN], const float(&as)[TM], float ws,
+                  v8i(&bfn)[TN], float(&asn)[TM], float& wsn) {
+    constexpr int S = decltype(slot_c)::value;
     wait_lgkm0();  // fragments and scales of block kb are in registers
 #pragma unroll
     for (int tm = 0; tm < TM; ++tm) sc[tm] = as[tm] * ws;
     wait_vmcnt<(STAGES - 2) * C::LOADS>();
     wg_barrier();  // stage kb+1 is in LDS; slot kb % STAGES is free
-    issue_stage(min(kb + STAGES, G - 1), kb % STAGES);
+    issue_stage(min(kb + STAGES, G - 1), S);
     // (on the last block the reads below fetch a slot holding a reloaded
     // copy of the last block, never used; its load has completed)
-    const uint8_t* nx = slot_base(kb + 1);
+    const uint8_t* nx = smem + ((S + 1) % STAGES) * C::STAGE_BYTES;
     unroll_seq(
         [&](auto ic) {
           constexpr int I = decltype(ic)::value;
@@ -255,12 +256,24 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_tiled_kernel(
         std::make_integer_sequence<int, NP>{});
     sc_tail = sc[TM - 1];
   };
+  // block kb0 + I: register set I % 2, LDS slot I % STAGES
+  auto step_i = [&](uint32_t kb0, auto ic) {
+    constexpr int I = decltype(ic)::value;
+    using Slot = std::integral_constant<int, I % STAGES>;
+    if constexpr (I % 2 == 0)
+      step(kb0 + I, Slot{}, bf0, as0, ws0, bf1, as1, ws1);
+    else
+      step(kb0 + I, Slot{}, bf1, as1, ws1, bf0, as0, ws0);
+  };
+  constexpr int U = STAGES % 2 == 0 ? STAGES : 2 * STAGES;  // blocks per loop iteration
   uint32_t kb = 0;
-  for (; kb + 2 <= G; kb += 2) {
-    step(kb, bf0, as0, ws0, bf1, as1, ws1);
-    step(kb + 1, bf1, as1, ws1, bf0, as0, ws0);
-  }
-  if (kb < G) step(kb, bf0, as0, ws0, bf1, as1, ws1);
+  for (; kb + U <= G; kb += U)
+    unroll_seq([&](auto ic) { step_i(kb, ic); }, std::make_integer_sequence<int, U>{});
+  unroll_seq(
+      [&](auto ic) {
+        if (kb + decltype(ic)::value < G) step_i(kb, ic);
+      },
+      std::make_integer_sequence<int, U - 1>{});
   wait_vmcnt<0>();  // no direct load may still be writing LDS when the workgroup ends
   // promotions of the last block's last two MFMAs (both in its last row)
   acc[(NP - 2) / TN][(NP - 2) % TN] += p[(NP - 2) & 3] * sc_tail;
@@ -639,9 +652,6 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(
   const uint32_t lo1 = l16 * 128 + (((c0 + 1) ^ swz(l16)) * 16);
   auto ld16 = [](const uint8_t* p) -> v4i { return *reinterpret_cast<const v4i*>(p); };
   auto ldf = [](const uint8_t* p) -> float { return *reinterpret_cast<const float*>(p); };
-  auto slot_base = [&](uint32_t kb) -> const uint8_t* {
-    return smem + (kb % STAGES) * C::STAGE_BYTES;
-  };
   const uint32_t a_row0 = wm * C::WM * 128, w_row0 = C::A_BYTES + wn * C::WN * 128;
 
   v4f acc[TM][TN];
@@ -655,9 +665,11 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(
   p[(NP - 2) & 3] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
   p[(NP - 1) & 3] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
-  // read this wave's fragments and scales of block kb (18 LDS reads)
-  auto read_block = [&](uint32_t kb) {
-    const uint8_t* sb = slot_base(kb);
+  // read this wave's fragments and scales from LDS slot S (18 LDS reads);
+  // the slot is a compile-time constant, so every address is a loop-invariant
+  // register plus an immediate offset
+  auto read_block = [&](auto slot_c) {
+    const uint8_t* sb = smem + decltype(slot_c)::value * C::STAGE_BYTES;
 #pragma unroll
     for (int tn = 0; tn < TN; ++tn) {
       bf[tn].lo = ld16(sb + w_row0 + tn * 2048 + lo0);
@@ -694,8 +706,8 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(
     sc_tail = sc[TM - 1];
   };
 
-  // Each group runs its own loop (one straight-line body each, so no value
-  // is live across a merge of the two roles); both execute the same
+  // Each group runs its own loop (its own body, so no value is live across
+  // a merge of the two roles); both execute the same
   // sequence of workgroup barriers.  Every wave issues its part of stages
   // 0 .. STAGES-1 up front and its part of stage kb+STAGES (slot kb %
   // STAGES) in its read phase of iteration kb: group 1 in phase A, after its
@@ -705,38 +717,67 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(
   // another group-1 wave reads could overwrite them before that wave has
   // read them: the direct loads land within a few hundred cycles when the
   // operands sit in L2.)
+  // The K loop is unrolled by STAGES so that each copy's slot (kb % STAGES)
+  // is a compile-time constant.
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  using S2 = std::integral_constant<int, 2>;
+  static_assert(STAGES == 3, "the unrolled loop below assumes three slots");
   if (grp == 0) {
+    // iteration kb: phase A computes block kb, phase B reads block kb+1
+    // (block G: a reloaded copy of the last block, unused) and refills slot
+    // kb % STAGES with block kb+STAGES
+    auto step = [&](uint32_t kb, auto slot_c) {
+      constexpr int S = decltype(slot_c)::value;
+      compute_block();    // phase A
+      wait_vmcnt<LW0>();  // own part of stage kb+1 (that of kb+2 may be in flight)
+      wg_barrier();
+      read_block(std::integral_constant<int, (S + 1) % STAGES>{});  // phase B
+      wait_lgkm0();
+      issue_g0(min(kb + STAGES, G - 1), S);
+      wg_barrier();
+    };
 #pragma unroll
     for (int s = 0; s < STAGES; ++s) issue_g0(min((uint32_t)s, G - 1), s);
     wait_vmcnt<(STAGES - 1) * LW0>();  // own part of stage 0
     wg_barrier();
-    read_block(0);
+    read_block(S0{});
     wait_lgkm0();
     wg_barrier();
-    for (uint32_t kb = 0; kb < G; ++kb) {
-      compute_block();    // phase A
-      wait_vmcnt<LW0>();  // own part of stage kb+1 (that of kb+2 may be in flight)
-      wg_barrier();
-      read_block(kb + 1);  // phase B (block G: a reloaded copy of the last block, unused)
-      wait_lgkm0();
-      issue_g0(min(kb + STAGES, G - 1), kb % STAGES);
-      wg_barrier();
+    uint32_t kb = 0;
+    for (; kb + 3 <= G; kb += 3) {
+      step(kb, S0{});
+      step(kb + 1, S1{});
+      step(kb + 2, S2{});
     }
+    if (kb < G) step(kb, S0{});
+    if (kb + 1 < G) step(kb + 1, S1{});
   } else {
+    // iteration kb: phase A reads block kb and refills its slot, phase B
+    // computes it
+    auto step = [&](uint32_t kb, auto slot_c) {
+      constexpr int S = decltype(slot_c)::value;
+      read_block(slot_c);  // phase A
+      wait_lgkm0();
+      issue_g1(min(kb + STAGES, G - 1), S);
+      wait_vmcnt<2 * LW1>();  // own part of stage kb+1 (kb+2, kb+3 may be in flight)
+      wg_barrier();
+      compute_block();  // phase B
+      wg_barrier();
+    };
 #pragma unroll
     for (int s = 0; s < STAGES; ++s) issue_g1(min((uint32_t)s, G - 1), s);
     wait_vmcnt<(STAGES - 1) * LW1>();  // own part of stage 0
     wg_barrier();
     wg_barrier();
-    for (uint32_t kb = 0; kb < G; ++kb) {
-      read_block(kb);  // phase A
-      wait_lgkm0();
-      issue_g1(min(kb + STAGES, G - 1), kb % STAGES);
-      wait_vmcnt<2 * LW1>();  // own part of stage kb+1 (kb+2, kb+3 may be in flight)
-      wg_barrier();
-      compute_block();  // phase B
-      wg_barrier();
+    uint32_t kb = 0;
+    for (; kb + 3 <= G; kb += 3) {
+      step(kb, S0{});
+      step(kb + 1, S1{});
+      step(kb + 2, S2{});
     }
+    if (kb < G) step(kb, S0{});
+    if (kb + 1 < G) step(kb + 1, S1{});
   }
   wait_vmcnt<0>();  // no direct load may still be writing LDS at exit
   acc[(NP - 2) / TN][(NP - 2) % TN] += p[(NP - 2) & 3] * sc_tail;
