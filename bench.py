@@ -53,7 +53,7 @@ BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
 # readings for a plain 1 GiB copy (the HBM-bytes summary under profiles/).
 # Valid only for the kernel source they were taken with: reported as null
 # once the ping-pong kernel's source changes (gemm_source_hash).
-GEMM_TRAFFIC = {"bytes": 1.1996e+09 + 4.7190e+07, "gemm_source_sha256": "591e9c0e9a1dfee5"}
+GEMM_TRAFFIC = {"bytes": 1.2274e+09 + 4.7088e+07, "gemm_source_sha256": "e3d4b625424f3c35"}
 
 
 def gemm_source_hash():
