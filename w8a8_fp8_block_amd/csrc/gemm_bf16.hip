@@ -95,9 +95,6 @@ __global__ __launch_bounds__(512) void gemm_bf16_kernel(const uint16_t* __restri
   const uint32_t lo0 = l16 * 128 + ((cq ^ swz(l16)) * 16);
   const uint32_t lo1 = l16 * 128 + (((cq + 4) ^ swz(l16)) * 16);
   auto ld16 = [](const uint8_t* p) -> v4i { return *reinterpret_cast<const v4i*>(p); };
-  auto slot_base = [&](uint32_t kb) -> const uint8_t* {
-    return smem + (kb % STAGES) * C::STAGE_BYTES;
-  };
   const uint32_t a_row0 = wm * C::WM * 128, w_row0 = C::A_BYTES + wn * C::WN * 128;
 
   v4f acc[TM][TN];
@@ -107,8 +104,9 @@ __global__ __launch_bounds__(512) void gemm_bf16_kernel(const uint16_t* __restri
     for (int j = 0; j < TN; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
   v4i af0[TM], af1[TM], bf0[TN], bf1[TN];
 
-  auto read_block = [&](uint32_t kb) {
-    const uint8_t* sb = slot_base(kb);
+  // fragments from LDS slot S, a compile-time constant (see the loops below)
+  auto read_block = [&](auto slot_c) {
+    const uint8_t* sb = smem + decltype(slot_c)::value * C::STAGE_BYTES;
 #pragma unroll
     for (int tn = 0; tn < TN; ++tn) {
       bf0[tn] = ld16(sb + w_row0 + tn * 2048 + lo0);
@@ -133,39 +131,63 @@ __global__ __launch_bounds__(512) void gemm_bf16_kernel(const uint16_t* __restri
         std::make_integer_sequence<int, 32>{});
   };
 
-  // (schedule and waits as in the FP8 ping-pong kernel)
+  // (schedule and waits as in the FP8 ping-pong kernel, whose K loop is
+  // likewise unrolled by the stage count so that each block's LDS slot is a
+  // compile-time constant)
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  using S2 = std::integral_constant<int, 2>;
+  static_assert(STAGES == 3, "the unrolled loops below assume three slots");
   if (grp == 0) {
+    auto step = [&](uint32_t kb, auto slot_c) {
+      constexpr int S = decltype(slot_c)::value;
+      compute_block();
+      wait_vmcnt<LW0>();
+      wg_barrier();
+      read_block(std::integral_constant<int, (S + 1) % STAGES>{});
+      wait_lgkm0();
+      issue_g0(min(kb + STAGES, G - 1), S);
+      wg_barrier();
+    };
 #pragma unroll
     for (int s = 0; s < STAGES; ++s) issue_g0(min((uint32_t)s, G - 1), s);
     wait_vmcnt<(STAGES - 1) * LW0>();
     wg_barrier();
-    read_block(0);
+    read_block(S0{});
     wait_lgkm0();
     wg_barrier();
-    for (uint32_t kb = 0; kb < G; ++kb) {
-      compute_block();
-      wait_vmcnt<LW0>();
-      wg_barrier();
-      read_block(kb + 1);
-      wait_lgkm0();
-      issue_g0(min(kb + STAGES, G - 1), kb % STAGES);
-      wg_barrier();
+    uint32_t kb = 0;
+    for (; kb + 3 <= G; kb += 3) {
+      step(kb, S0{});
+      step(kb + 1, S1{});
+      step(kb + 2, S2{});
     }
+    if (kb < G) step(kb, S0{});
+    if (kb + 1 < G) step(kb + 1, S1{});
   } else {
+    auto step = [&](uint32_t kb, auto slot_c) {
+      constexpr int S = decltype(slot_c)::value;
+      read_block(slot_c);
+      wait_lgkm0();
+      issue_g1(min(kb + STAGES, G - 1), S);
+      wait_vmcnt<2 * LW1>();
+      wg_barrier();
+      compute_block();
+      wg_barrier();
+    };
 #pragma unroll
     for (int s = 0; s < STAGES; ++s) issue_g1(min((uint32_t)s, G - 1), s);
     wait_vmcnt<(STAGES - 1) * LW1>();
     wg_barrier();
     wg_barrier();
-    for (uint32_t kb = 0; kb < G; ++kb) {
-      read_block(kb);
-      wait_lgkm0();
-      issue_g1(min(kb + STAGES, G - 1), kb % STAGES);
-      wait_vmcnt<2 * LW1>();
-      wg_barrier();
-      compute_block();
-      wg_barrier();
+    uint32_t kb = 0;
+    for (; kb + 3 <= G; kb += 3) {
+      step(kb, S0{});
+      step(kb + 1, S1{});
+      step(kb + 2, S2{});
     }
+    if (kb < G) step(kb, S0{});
+    if (kb + 1 < G) step(kb + 1, S1{});
   }
   wait_vmcnt<0>();
 
