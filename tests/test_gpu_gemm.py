@@ -274,11 +274,15 @@ def test_gemm_long_k_weight_scale_chunks(orc):
 
 
 @pytest.mark.parametrize("M,N,K", [(300, 384, 1280), (1168, 512, 2048), (4576, 256, 640),
-                                   (2300, 384, 256)])
+                                   (2300, 384, 256), (260, 384, 384), (300, 256, 768),
+                                   (520, 384, 896), (300, 256, 1152), (260, 128, 128)])
 def test_tiled_kernels_bit_identical(orc, M, N, K):
     """The tiled kernels (all tile shapes) add the scaled block products in the
     same order, so their outputs agree bit for bit; the auto choice is one of
-    them."""
+    them.  The K loops are unrolled by the LDS stage count (3, or 6 where the
+    register double buffer alternates too): K/128 here, 1, 2, 3, 5, 6, 7, 9,
+    10 and 16, takes every residue mod 6, so each unrolled loop's tail length
+    is exercised."""
     rng = np.random.default_rng(M + N + K)
     x = synth.f32_to_bf16_bits(rng.laplace(0, 1, (M, K)).astype(np.float32))
     a, a_s = orc.quant_act(x)
