@@ -200,7 +200,10 @@ fp8q_status fp8q_gemm_blockscaled(const uint8_t *a_e4m3, const float *a_scale_km
 int fp8q_gemm_select(uint32_t M, uint32_t N, uint32_t K);
 
 /* As fp8q_gemm_blockscaled with the kernel forced: 0 = auto (2 for
- * M <= 64 and for M <= 128 when N <= 8192, 5 for M >= 2048, else 1), 1 =
+ * M <= 64 and for M <= 128 when N <= 8192, 1 below 512 rows; from 512 rows
+ * on 5 or 1, whichever needs fewer rounds of workgroups on the 256 CUs when
+ * a last round of at most one 128x128 workgroup per CU counts as half a
+ * round; 5 on a tie), 1 =
  * the LDS-tiled MFMA kernel with 128x128 tiles and two workgroups per CU,
  * 2 = the skinny kernel (decode and small-batch widths; rows in
  * tiles of up to 64, up to 64 rows one workgroup per CU, each streaming an

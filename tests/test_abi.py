@@ -111,13 +111,21 @@ def test_gemm_validation():
 
 def test_gemm_select():
     """Auto GEMM choice: skinny kernel up to 64 rows (and up to 128 rows when
-    N <= 8192), the ping-pong 256x128 kernel from 2048 rows on, 128x128
-    tiles between; bad N/K -> -1 (pure host function)."""
-    for M, want in ((1, 2), (16, 2), (25, 2), (64, 2), (65, 2), (128, 2), (129, 1), (1168, 1),
-                    (2047, 1), (2048, 5), (4576, 5), (16384, 5)):
+    N <= 8192), 128x128 tiles below 512 rows; from 512 rows on the kernel with
+    fewer rounds of workgroups on 256 CUs (ping-pong: tiles of 256x128 in
+    rounds of 256; 128x128: workgroups in rounds of 512, a last round of at
+    most 256 counting half), ties to the ping-pong kernel; bad N/K -> -1 (pure
+    host function).  The expected values are the faster kernel measured at
+    each of these shapes."""
+    for M, want in ((1, 2), (16, 2), (25, 2), (64, 2), (65, 2), (128, 2), (129, 1), (511, 1),
+                    (512, 1), (768, 1), (1024, 5), (1168, 5), (1536, 5), (2047, 1), (2048, 1),
+                    (3072, 5), (4576, 5), (16384, 5)):
         assert fp8q.fp8q_gemm_select(M, 5120, 17408) == want, M
-    for M, want in ((64, 2), (65, 1), (128, 1), (1168, 1), (4576, 5)):
+    for M, want in ((64, 2), (65, 1), (128, 1), (640, 1), (768, 5), (1024, 1), (1168, 5),
+                    (1536, 1), (2048, 1), (3072, 1), (4576, 5)):
         assert fp8q.fp8q_gemm_select(M, 17408, 5120) == want, M
+    for M, want in ((768, 5), (1024, 5), (1168, 5), (1536, 1), (2048, 1), (3072, 1), (4576, 1)):
+        assert fp8q.fp8q_gemm_select(M, 6144, 5120) == want, M
     assert fp8q.fp8q_gemm_select(128, 8192, 5120) == 2
     assert fp8q.fp8q_gemm_select(128, 8320, 5120) == 1
     assert fp8q.fp8q_gemm_select(64, 100, 128) == -1
@@ -269,7 +277,8 @@ def test_splitk_select():
         assert sel(M, 17408, 5120) == want, M
     assert sel(300, 128, 2560) == 2        # K/1280 = 2 caps it
     assert sel(300, 128, 2432) == 1        # fewer than 20 K blocks: no split
-    assert sel(4096, 128, 17408) == 1      # the 256x128 kernel's range
+    assert sel(4576, 5120, 17408) == 1     # the 256x128 kernel's pick: no split
+    assert sel(4096, 128, 17408) == 6      # 32 128x128 tiles: six splits
     assert sel(100, 100, 1280) == 0
     assert sel(100, 128, 0) == 0
 

@@ -167,10 +167,18 @@ fp8q_status run_quant(const char* fn, const uint16_t* x, uint8_t* q, float* srm,
 // with the last-level cache flushed before each call, at K = 17408,
 // N = 5120: 88 / 90 / 92 us at M = 80 / 128 / 192 against 112-134 /
 // 117-146 / 134 us for the tiled kernels; at N = 6144, K = 5120: 32-34 us
-// against 41-52 us up to M = 128, no gain beyond); from kWideAutoMinM rows
-// on, the ping-pong 256 x 128 kernel (one workgroup per CU; 10-20% faster
-// than the other tile shapes at M = 4576, even with 128 x 128 tiles at
-// M = 1168, slower at M = 512); 128 x 128 tiles between.
+// against 41-52 us up to M = 128, no gain beyond); 128 x 128 tiles (two
+// workgroups per CU) below kTailRuleMinM rows.  From there on the choice
+// between them and the ping-pong 256 x 128 kernel (one workgroup per CU, a
+// few percent faster per full round) follows the last, partial round of
+// workgroups, on kGfx950Cus CUs: a ping-pong round costs one unit whether
+// full or not, a 128 x 128 round one unit when more than one workgroup per
+// CU remains and about half a unit when at most one per CU does (a lone
+// workgroup has its CU to itself).  The kernel with fewer units wins; ties
+// go to the ping-pong kernel.  Back-to-back launches on one box at N = 17408
+// and 6144 (K = 5120) and N = 5120 (K = 17408), M = 640 .. 4576: the rule
+// picks the faster kernel at all 22 shapes, by 3-12% (M = 1168, N = 5120:
+// 108 vs 124 us; N = 6144, M = 4576: 128 x 128 tiles, 159 vs 164 us).
 constexpr uint32_t kSkinnyAutoMaxM = 64;
 constexpr uint32_t kSkinnyWideMaxM = 128;
 constexpr uint32_t kSkinnyWideMaxN = 8192;
@@ -179,11 +187,19 @@ constexpr uint32_t kSkinnyWideMaxN = 8192;
 // K-major stores cost more than the separate relayout launch (measured:
 // 8.5 vs 16.5 us at M*K/128 = 46720, 69 vs 56 us at 622336).
 constexpr uint64_t kFusedKmajorMaxGroups = 1u << 17;
-constexpr uint32_t kWideAutoMinM = 2048;
+constexpr uint32_t kTailRuleMinM = 512;
+constexpr uint64_t kGfx950Cus = 256;
 
 int gemm_auto_kernel(uint32_t M, uint32_t N) {
   if (M <= kSkinnyAutoMaxM || (M <= kSkinnyWideMaxM && N <= kSkinnyWideMaxN)) return 2;
-  return M >= kWideAutoMinM ? 5 : 1;
+  if (M < kTailRuleMinM) return 1;
+  const uint64_t nt = N / kGroup;
+  const uint64_t t_pp = (M + 255) / 256 * nt, t_128 = (M + 127) / 128 * nt;
+  // costs in half rounds
+  const uint64_t c_pp = 2 * ((t_pp + kGfx950Cus - 1) / kGfx950Cus);
+  const uint64_t tail = t_128 % (2 * kGfx950Cus);
+  const uint64_t c_128 = 2 * (t_128 / (2 * kGfx950Cus)) + (tail == 0 ? 0 : tail > kGfx950Cus ? 2 : 1);
+  return c_pp <= c_128 ? 5 : 1;
 }
 
 // Split-K (fp8q_gemm_blockscaled_splitk): splits = floor(256 / tiles) when
