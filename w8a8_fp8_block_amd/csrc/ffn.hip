@@ -28,39 +28,45 @@ __device__ __forceinline__ u32x4 silu_mul_8(u32x4 g, u32x4 u) {
   return u32x4{hw[0], hw[1], hw[2], hw[3]};
 }
 
-// One 16-lane row per group of 128 (gate, up) pairs, kSiluRounds groups per
-// row with all loads issued first.  Gate and up are read once
-// (non-temporal); the codes and scales are left in the caches for the down
-// projection that reads them next.
-constexpr uint32_t kSiluWaves = 4, kSiluRounds = 2;
-constexpr uint32_t kSiluGroupsPerWg = 4 * kSiluWaves * kSiluRounds;
+// Eight lanes per group of 128 (gate, up) pairs, 16 pairs per lane:
+// elements 8l..8l+7 and 64+8l..64+8l+7 of the group, as in the activation
+// quantizer's flat variant (each 128-bit load covers 128 contiguous bytes
+// across the 8 lanes).  Gate and up are read once (non-temporal); the codes
+// and scales are left in the caches for the down projection that reads them
+// next.  The K-major scale slot takes a 32-bit divide (M * I/128 < 2^32).
+constexpr uint32_t kSiluWaves = 4;
+constexpr uint32_t kSiluGroupsPerWg = 8 * kSiluWaves;
 
 __global__ __launch_bounds__(64 * kSiluWaves) void silu_mul_quant_kernel(
     const u32x4* __restrict__ g, const u32x4* __restrict__ u, u32x2* __restrict__ q,
-    float* __restrict__ skm, uint64_t ngroups, uint32_t G, uint32_t Mp) {
-  const uint64_t g0 =
-      ((uint64_t)blockIdx.x * (kSiluGroupsPerWg / kSiluRounds) + (threadIdx.x >> 4)) * kSiluRounds;
-  const uint32_t l = threadIdx.x & 15;
-  u32x4 gv[kSiluRounds], uv[kSiluRounds];
-#pragma unroll
-  for (uint32_t r = 0; r < kSiluRounds; ++r) {
-    if (g0 + r < ngroups) {
-      gv[r] = __builtin_nontemporal_load(&g[(g0 + r) * 16 + l]);
-      uv[r] = __builtin_nontemporal_load(&u[(g0 + r) * 16 + l]);
-    }
-  }
-#pragma unroll
-  for (uint32_t r = 0; r < kSiluRounds; ++r) {
-    if (g0 + r < ngroups) {  // uniform over the 16-lane row
-      float s;
-      const u32x2 c = quant_group(silu_mul_8(gv[r], uv[r]), s);
-      q[(g0 + r) * 16 + l] = c;
-      if (l == 0) {
-        const uint64_t gi = g0 + r;
-        skm[(gi % G) * Mp + gi / G] = s;
-      }
-    }
-  }
+    float* __restrict__ skm, uint32_t ngroups, uint32_t G, uint32_t Mp) {
+  const uint32_t gi = blockIdx.x * kSiluGroupsPerWg + (threadIdx.x >> 3);
+  const uint32_t l = threadIdx.x & 7;
+  if (gi >= ngroups) return;  // uniform over the group's 8 lanes
+  const uint64_t base = (uint64_t)gi * 16;
+  const u32x4 g0 = __builtin_nontemporal_load(&g[base + l]);
+  const u32x4 g1 = __builtin_nontemporal_load(&g[base + 8 + l]);
+  const u32x4 u0 = __builtin_nontemporal_load(&u[base + l]);
+  const u32x4 u1 = __builtin_nontemporal_load(&u[base + 8 + l]);
+  const u32x4 h0 = silu_mul_8(g0, u0), h1 = silu_mul_8(g1, u1);
+  const uint32_t mag = 0x7FFF7FFFu;
+  const u16x2 m0 = __builtin_elementwise_max(as_u16x2(h0.x & mag), as_u16x2(h0.y & mag));
+  const u16x2 m1 = __builtin_elementwise_max(as_u16x2(h0.z & mag), as_u16x2(h0.w & mag));
+  const u16x2 m2 = __builtin_elementwise_max(as_u16x2(h1.x & mag), as_u16x2(h1.y & mag));
+  const u16x2 m3 = __builtin_elementwise_max(as_u16x2(h1.z & mag), as_u16x2(h1.w & mag));
+  const u16x2 mm = __builtin_elementwise_max(__builtin_elementwise_max(m0, m1),
+                                             __builtin_elementwise_max(m2, m3));
+  const uint32_t amax = dpp_half_row_max_u32(max((uint32_t)mm.x, (uint32_t)mm.y));
+  const float sc = group_scale(amax);
+  const float xv[16] = {bf_lo(h0.x), bf_hi(h0.x), bf_lo(h0.y), bf_hi(h0.y), bf_lo(h0.z),
+                        bf_hi(h0.z), bf_lo(h0.w), bf_hi(h0.w), bf_lo(h1.x), bf_hi(h1.x),
+                        bf_lo(h1.y), bf_hi(h1.y), bf_lo(h1.z), bf_hi(h1.z), bf_lo(h1.w),
+                        bf_hi(h1.w)};
+  float qv[16];
+  quotients<16>(xv, sc, qv);
+  q[base + l] = u32x2{encode4(qv), encode4(qv + 4)};
+  q[base + 8 + l] = u32x2{encode4(qv + 8), encode4(qv + 12)};
+  if (l == 0) skm[(uint64_t)(gi % G) * Mp + gi / G] = sc;
 }
 
 }  // namespace
@@ -68,9 +74,9 @@ __global__ __launch_bounds__(64 * kSiluWaves) void silu_mul_quant_kernel(
 hipError_t launch_silu_mul_quant(const uint16_t* gate, const uint16_t* up, uint8_t* q,
                                  float* scale_km, uint32_t M, uint32_t I, hipStream_t s) {
   const uint32_t G = I / kGroup;
-  const uint64_t ngroups = (uint64_t)M * G;
-  const uint64_t grid = (ngroups + kSiluGroupsPerWg - 1) / kSiluGroupsPerWg;
-  silu_mul_quant_kernel<<<dim3((uint32_t)grid), dim3(64 * kSiluWaves), 0, s>>>(
+  const uint32_t ngroups = M * G;  // M * I < 2^32 (checked by the caller)
+  const uint32_t grid = (ngroups + kSiluGroupsPerWg - 1) / kSiluGroupsPerWg;
+  silu_mul_quant_kernel<<<dim3(grid), dim3(64 * kSiluWaves), 0, s>>>(
       reinterpret_cast<const u32x4*>(gate), reinterpret_cast<const u32x4*>(up),
       reinterpret_cast<u32x2*>(q), scale_km, ngroups, G, m_pad16(M));
   hipError_t e = hipGetLastError();
