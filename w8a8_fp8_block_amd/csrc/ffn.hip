@@ -33,13 +33,14 @@ __device__ __forceinline__ u32x4 silu_mul_8(u32x4 g, u32x4 u) {
 // quantizer's flat variant (each 128-bit load covers 128 contiguous bytes
 // across the 8 lanes).  Gate and up are read once (non-temporal); the codes
 // and scales are left in the caches for the down projection that reads them
-// next.  The K-major scale slot takes a 32-bit divide (M * I/128 < 2^32).
+// next.  The K-major scale slot takes a 32-bit divide (M * I/128 < 2^32);
+// the pad slots M..Mp-1 are written by the last row's groups.
 constexpr uint32_t kSiluWaves = 4;
 constexpr uint32_t kSiluGroupsPerWg = 8 * kSiluWaves;
 
 __global__ __launch_bounds__(64 * kSiluWaves) void silu_mul_quant_kernel(
     const u32x4* __restrict__ g, const u32x4* __restrict__ u, u32x2* __restrict__ q,
-    float* __restrict__ skm, uint32_t ngroups, uint32_t G, uint32_t Mp) {
+    float* __restrict__ skm, uint32_t ngroups, uint32_t M, uint32_t G, uint32_t Mp) {
   const uint32_t gi = blockIdx.x * kSiluGroupsPerWg + (threadIdx.x >> 3);
   const uint32_t l = threadIdx.x & 7;
   if (gi >= ngroups) return;  // uniform over the group's 8 lanes
@@ -66,7 +67,14 @@ __global__ __launch_bounds__(64 * kSiluWaves) void silu_mul_quant_kernel(
   quotients<16>(xv, sc, qv);
   q[base + l] = u32x2{encode4(qv), encode4(qv + 4)};
   q[base + 8 + l] = u32x2{encode4(qv + 8), encode4(qv + 12)};
-  if (l == 0) skm[(uint64_t)(gi % G) * Mp + gi / G] = sc;
+  if (l == 0) {
+    // the last token row's groups also clear their column's pad slots
+    float* col = skm + (uint64_t)(gi % G) * Mp;
+    const uint32_t m = gi / G;
+    col[m] = sc;
+    if (m + 1 == M)
+      for (uint32_t p = M; p < Mp; ++p) col[p] = 0.0f;
+  }
 }
 
 }  // namespace
@@ -78,10 +86,8 @@ hipError_t launch_silu_mul_quant(const uint16_t* gate, const uint16_t* up, uint8
   const uint32_t grid = (ngroups + kSiluGroupsPerWg - 1) / kSiluGroupsPerWg;
   silu_mul_quant_kernel<<<dim3(grid), dim3(64 * kSiluWaves), 0, s>>>(
       reinterpret_cast<const u32x4*>(gate), reinterpret_cast<const u32x4*>(up),
-      reinterpret_cast<u32x2*>(q), scale_km, ngroups, G, m_pad16(M));
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  return launch_kmajor_pad(scale_km, M, I, s);
+      reinterpret_cast<u32x2*>(q), scale_km, ngroups, M, G, m_pad16(M));
+  return hipGetLastError();
 }
 
 }  // namespace fp8q

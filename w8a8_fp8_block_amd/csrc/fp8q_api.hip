@@ -155,9 +155,9 @@ fp8q_status run_quant(const char* fn, const uint16_t* x, uint8_t* q, float* srm,
       log_pick(variant, reject, p.requested, M, K, grid);
     }
   }
-  hipError_t e = (variant == 2) ? launch_quant_b(x, q, srm, skm, M, K, s)
-                                : launch_quant_a(x, q, srm, skm, M, K, s);
-  if (e == hipSuccess && skm) e = launch_kmajor_pad(skm, M, K, s);
+  // (with skm, the quantizer also writes the K-major pad slots)
+  const hipError_t e = (variant == 2) ? launch_quant_b(x, q, srm, skm, M, K, s)
+                                      : launch_quant_a(x, q, srm, skm, M, K, s);
   return launched(fn, e);
 }
 

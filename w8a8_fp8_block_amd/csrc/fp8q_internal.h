@@ -38,7 +38,6 @@ hipError_t launch_quant_b(const uint16_t* x, uint8_t* q, float* scale_rm,
                           float* scale_km, uint32_t M, uint32_t K, hipStream_t s);
 // K-major pad slots m in [M, ceil16(M)) of scale_km are written by this
 // launcher when the quantizer writes scale_km directly.
-hipError_t launch_kmajor_pad(float* scale_km, uint32_t M, uint32_t K, hipStream_t s);
 
 hipError_t launch_relayout(const float* scale_rm, float* scale_km, uint32_t M,
                            uint32_t K, hipStream_t s);

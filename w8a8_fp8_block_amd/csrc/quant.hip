@@ -32,12 +32,19 @@
 namespace fp8q {
 namespace {
 
+// Scale of group g in the row-major layout and/or the K-major one; the
+// groups of the last token row also clear their K-major column's pad slots
+// M..Mp-1, so the K-major layout needs no separate pad pass.
 __device__ __forceinline__ void write_scales(float s, uint64_t g, float* __restrict__ srm,
-                                             float* __restrict__ skm, uint32_t G, uint32_t Mp) {
+                                             float* __restrict__ skm, uint32_t M, uint32_t G,
+                                             uint32_t Mp) {
   if (srm) srm[g] = s;
   if (skm) {
     const uint32_t m = (uint32_t)(g / G), gg = (uint32_t)(g % G);
-    skm[(uint64_t)gg * Mp + m] = s;
+    float* col = skm + (uint64_t)gg * Mp;
+    col[m] = s;
+    if (m + 1 == M)
+      for (uint32_t p = M; p < Mp; ++p) col[p] = 0.0f;
   }
 }
 
@@ -49,7 +56,7 @@ __device__ __forceinline__ void write_scales(float s, uint64_t g, float* __restr
 // which nothing reads back soon, are stored non-temporally.
 __global__ __launch_bounds__(64 * kQuantAWaves) void quant_a_kernel(
     const u32x4* __restrict__ x, u32x2* __restrict__ q, float* __restrict__ srm,
-    float* __restrict__ skm, uint64_t ngroups, uint32_t G, uint32_t Mp) {
+    float* __restrict__ skm, uint64_t ngroups, uint32_t M, uint32_t G, uint32_t Mp) {
   const uint64_t g = (uint64_t)blockIdx.x * kQuantAGroupsPerWg + (threadIdx.x >> 3);
   const uint32_t l = threadIdx.x & 7;
   if (g >= ngroups) return;  // uniform over the group's 8 lanes
@@ -72,7 +79,7 @@ __global__ __launch_bounds__(64 * kQuantAWaves) void quant_a_kernel(
   quotients<16>(xv, s, qv);
   __builtin_nontemporal_store(u32x2{encode4(qv), encode4(qv + 4)}, &q[g * 16 + l]);
   __builtin_nontemporal_store(u32x2{encode4(qv + 8), encode4(qv + 12)}, &q[g * 16 + 8 + l]);
-  if (l == 0) write_scales(s, g, srm, skm, G, Mp);
+  if (l == 0) write_scales(s, g, srm, skm, M, G, Mp);
 }
 
 // Variant B (K-grouped): workgroup (m, by) covers groups
@@ -80,7 +87,7 @@ __global__ __launch_bounds__(64 * kQuantAWaves) void quant_a_kernel(
 // kQuantBRounds groups, all loads issued before any is consumed.
 __global__ __launch_bounds__(64 * kQuantBWaves) void quant_b_kernel(
     const u32x4* __restrict__ x, u32x2* __restrict__ q, float* __restrict__ srm,
-    float* __restrict__ skm, uint32_t G, uint32_t Mp) {
+    float* __restrict__ skm, uint32_t M, uint32_t G, uint32_t Mp) {
   const uint32_t m = blockIdx.x;
   const uint32_t wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const uint32_t g0 = blockIdx.y * kQuantBGroupsPerWg + wave * 4 * kQuantBRounds + (lane >> 4);
@@ -98,17 +105,9 @@ __global__ __launch_bounds__(64 * kQuantBWaves) void quant_b_kernel(
       const uint64_t g = (uint64_t)m * G + gg;
       const u32x2 c = quant_group(v[r], s);
       q[g * 16 + (lane & 15)] = c;
-      if ((lane & 15) == 0) write_scales(s, g, srm, skm, G, Mp);
+      if ((lane & 15) == 0) write_scales(s, g, srm, skm, M, G, Mp);
     }
   }
-}
-
-// Zero the K-major pad slots m in [M, Mp) of every group column.
-__global__ __launch_bounds__(256) void kmajor_pad_kernel(float* __restrict__ skm, uint32_t M,
-                                                         uint32_t Mp, uint32_t G) {
-  const uint32_t padw = Mp - M;
-  const uint32_t i = blockIdx.x * 256 + threadIdx.x;
-  if (i < padw * G) skm[(uint64_t)(i / padw) * Mp + M + i % padw] = 0.0f;
 }
 
 }  // namespace
@@ -120,7 +119,7 @@ hipError_t launch_quant_a(const uint16_t* x, uint8_t* q, float* scale_rm, float*
   const uint64_t grid = (ngroups + kQuantAGroupsPerWg - 1) / kQuantAGroupsPerWg;
   quant_a_kernel<<<dim3((uint32_t)grid), dim3(64 * kQuantAWaves), 0, s>>>(
       reinterpret_cast<const u32x4*>(x), reinterpret_cast<u32x2*>(q), scale_rm, scale_km,
-      ngroups, G, m_pad16(M));
+      ngroups, M, G, m_pad16(M));
   return hipGetLastError();
 }
 
@@ -129,16 +128,8 @@ hipError_t launch_quant_b(const uint16_t* x, uint8_t* q, float* scale_rm, float*
   const uint32_t G = K / kGroup;
   const uint32_t gy = (G + kQuantBGroupsPerWg - 1) / kQuantBGroupsPerWg;
   quant_b_kernel<<<dim3(M, gy), dim3(64 * kQuantBWaves), 0, s>>>(
-      reinterpret_cast<const u32x4*>(x), reinterpret_cast<u32x2*>(q), scale_rm, scale_km, G,
+      reinterpret_cast<const u32x4*>(x), reinterpret_cast<u32x2*>(q), scale_rm, scale_km, M, G,
       m_pad16(M));
-  return hipGetLastError();
-}
-
-hipError_t launch_kmajor_pad(float* scale_km, uint32_t M, uint32_t K, hipStream_t s) {
-  const uint32_t Mp = m_pad16(M), G = K / kGroup;
-  if (Mp == M) return hipSuccess;
-  const uint32_t n = (Mp - M) * G;
-  kmajor_pad_kernel<<<dim3((n + 255) / 256), dim3(256), 0, s>>>(scale_km, M, Mp, G);
   return hipGetLastError();
 }
 
