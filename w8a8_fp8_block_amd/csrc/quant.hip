@@ -40,7 +40,8 @@ __device__ __forceinline__ void write_scales(float s, uint64_t g, float* __restr
                                              uint32_t Mp) {
   if (srm) srm[g] = s;
   if (skm) {
-    const uint32_t m = (uint32_t)(g / G), gg = (uint32_t)(g % G);
+    // g < M*K/128 < 2^25 (Mp*K < 2^32 is checked on the host): 32-bit divide
+    const uint32_t g32 = (uint32_t)g, m = g32 / G, gg = g32 % G;
     float* col = skm + (uint64_t)gg * Mp;
     col[m] = s;
     if (m + 1 == M)
