@@ -23,6 +23,16 @@
 namespace fp8q {
 namespace {
 
+// Promotion distance: the fp32 promotion of MFMA i is issued in the slot of
+// MFMA i + kPromoteDist.  A VALU read of an MFMA result waits until the
+// matrix pipe has written it; measured with one wave per SIMD issuing
+// 16x16x128 FP8 MFMAs and four promotion fmas per MFMA from registers, the
+// matrix pipe is busy 51% / 75% / 91% of the time at distance 1 / 2 / 3
+// (99% without the fmas).  The results rotate through four register sets,
+// so the distance is at most 3, and the last kPromoteDist MFMAs of a K block
+// (promoted in the next block, with that block's scale) lie in one row.
+constexpr int kPromoteDist = 3;
+
 __device__ __forceinline__ v4f mfma_e4m3_128(const v8i& w, const v8i& a) {
   const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
   // cbsz = blgp = 0: both operands OCP e4m3; zero scale operands select the
@@ -51,11 +61,11 @@ __device__ __forceinline__ v4f mfma_e4m3_128(const v8i& w, const v8i& a) {
 // Register pipeline, per K block: the MFMAs of block kb run from registers
 // while the fragments of block kb+1 are read from LDS into a second register
 // set (activation fragments in place, as soon as the last MFMA of their row
-// has been issued).  The fp32 promotion of MFMA i is issued after MFMA i+2, so
-// the vector ALU never waits for the matrix pipe; the promotions of a block's
-// last two MFMAs run in the next block.  Each MFMA slot (the MFMA, the four
-// fmas, one or two LDS reads) is fenced off from the next with a scheduling
-// barrier: left to itself the compiler hoists all MFMAs of a block and then
+// has been issued).  The fp32 promotion of MFMA i is issued after MFMA
+// i + kPromoteDist, by which time the matrix pipe has written its result; the
+// promotions of a block's last kPromoteDist MFMAs run in the next block.
+// Each MFMA slot (the MFMA, the four fmas, one or two LDS reads) is fenced
+// off from the next with a scheduling barrier: left to itself the compiler hoists all MFMAs of a block and then
 // has to serialise the next one on a single result register.
 // ------------------------------------------------------------------------
 template <int BM, int BN, int WGM, int WGN, int STAGES, bool ROW = false>
@@ -77,6 +87,8 @@ struct TileCfg {
   static constexpr int FREE_OPS = 2 * TN + TM / 2 + (ROW ? 0 : 1);
   static_assert(WM % 16 == 0 && WN % 16 == 0 && TN >= 2 && TM % 2 == 0 && NP % 4 == 0, "wave tile");
   static_assert(NP - TM >= FREE_OPS, "too few MFMA slots for the LDS reads");
+  static_assert(kPromoteDist >= 1 && kPromoteDist <= 3 && kPromoteDist <= TN && NP % 4 == 0,
+                "pending promotions lie in the last row; four result registers");
   static_assert(BM * 8 % (64 * NW) == 0 && BN * 8 % (64 * NW) == 0, "tile/wave mismatch");
   static_assert(128 % WN == 0, "a wave's columns lie in one weight-scale block");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
@@ -201,11 +213,11 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_tiled_kernel(
   ws1 = 1.0f;
 
   // MFMA results rotate through 4 register sets; the promotions of the last
-  // two MFMAs of a block are pending when the next block starts (zero before
-  // the first block).
+  // kPromoteDist MFMAs of a block are pending when the next block starts
+  // (zero before the first block).
   v4f p[4];
-  p[(NP - 2) & 3] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-  p[(NP - 1) & 3] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) p[i] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
   float sc[TM], sc_tail = 0.0f;
 
   // one K block; S = kb % STAGES, a compile-time constant (the loop below is
@@ -228,11 +240,11 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_tiled_kernel(
           constexpr int I = decltype(ic)::value;
           constexpr int tm = I / TN, tn = I % TN;
           p[I & 3] = mfma_e4m3_128(bf[tn], af[tm]);
-          if constexpr (I < 2) {
-            constexpr int J = NP - 2 + I;
+          if constexpr (I < kPromoteDist) {
+            constexpr int J = NP - kPromoteDist + I;
             acc[J / TN][J % TN] += p[J & 3] * sc_tail;
           } else {
-            constexpr int J = I - 2;
+            constexpr int J = I - kPromoteDist;
             acc[J / TN][J % TN] += p[J & 3] * sc[J / TN];
           }
           if constexpr (tn == TN - 1) {
@@ -275,9 +287,9 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_tiled_kernel(
       },
       std::make_integer_sequence<int, U - 1>{});
   wait_vmcnt<0>();  // no direct load may still be writing LDS when the workgroup ends
-  // promotions of the last block's last two MFMAs (both in its last row)
-  acc[(NP - 2) / TN][(NP - 2) % TN] += p[(NP - 2) & 3] * sc_tail;
-  acc[(NP - 1) / TN][(NP - 1) % TN] += p[(NP - 1) & 3] * sc_tail;
+  // promotions of the last block's last kPromoteDist MFMAs (all in its last row)
+#pragma unroll
+  for (int j = NP - kPromoteDist; j < NP; ++j) acc[j / TN][j % TN] += p[j & 3] * sc_tail;
 
   if constexpr (ROW) {
 #pragma unroll
@@ -430,6 +442,8 @@ struct PpCfg {
   static constexpr int LW0 = CH0, LW1 = CH1 + 2 * (ROW ? 1 : 2);
   static_assert(4 * (CH0 + CH1) == CHUNKS && 2 * LW1 < 64, "chunk split, vmcnt range");
   static_assert(LDS_BYTES <= 160 * 1024 && STAGES == 3, "config");
+  static_assert(kPromoteDist >= 1 && kPromoteDist <= 3 && kPromoteDist <= TN && NP % 4 == 0,
+                "pending promotions lie in the last row; four result registers");
 };
 
 // Second weight operand and outputs of the FFN mode: W/Ws are the gate
@@ -662,8 +676,8 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(
   v8i af[TM], bf[TN];
   float as[TM], ws = 0.0f, sc[TM], sc_tail = 0.0f;
   v4f p[4];
-  p[(NP - 2) & 3] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-  p[(NP - 1) & 3] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) p[i] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
   // read this wave's fragments and scales from LDS slot S (18 LDS reads);
   // the slot is a compile-time constant, so every address is a loop-invariant
@@ -684,7 +698,8 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(
     ws = ROW ? 1.0f : ldf(sb + my_sc + 256);
   };
   // MFMAs and promotions of the block in registers; the promotions of its
-  // last two MFMAs are left pending for the next block's compute phase.
+  // last kPromoteDist MFMAs are left pending for the next block's compute
+  // phase.
   auto compute_block = [&]() {
 #pragma unroll
     for (int tm = 0; tm < TM; ++tm) sc[tm] = as[tm] * ws;
@@ -693,11 +708,11 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(
           constexpr int I = decltype(ic)::value;
           constexpr int tm = I / TN, tn = I % TN;
           p[I & 3] = mfma_e4m3_128(bf[tn], af[tm]);
-          if constexpr (I < 2) {
-            constexpr int J = NP - 2 + I;
+          if constexpr (I < kPromoteDist) {
+            constexpr int J = NP - kPromoteDist + I;
             acc[J / TN][J % TN] += p[J & 3] * sc_tail;
           } else {
-            constexpr int J = I - 2;
+            constexpr int J = I - kPromoteDist;
             acc[J / TN][J % TN] += p[J & 3] * sc[J / TN];
           }
           sched_fence();
@@ -780,8 +795,8 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(
     if (kb + 1 < G) step(kb + 1, S1{});
   }
   wait_vmcnt<0>();  // no direct load may still be writing LDS at exit
-  acc[(NP - 2) / TN][(NP - 2) % TN] += p[(NP - 2) & 3] * sc_tail;
-  acc[(NP - 1) / TN][(NP - 1) % TN] += p[(NP - 1) & 3] * sc_tail;
+#pragma unroll
+  for (int j = NP - kPromoteDist; j < NP; ++j) acc[j / TN][j % TN] += p[j & 3] * sc_tail;
   if constexpr (FFN) {
     ffn_epilogue<TM, TN>(acc, smem, ffn, wave, lane, m0 + wm * C::WM, n0 + (wn & 1) * C::WN, nb,
                          M, N, Mp);
