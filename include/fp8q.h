@@ -110,6 +110,15 @@ fp8q_status fp8q_quant_act_kmajor(const uint16_t *x_bf16, uint8_t *q_e4m3,
                                   float *scale_rm, float *scale_km,
                                   uint32_t M, uint32_t K, hipStream_t stream);
 
+/* As fp8q_quant_act_kmajor with the variant forced (0 = auto, 1 = A,
+ * 2 = B), as fp8q_quant_act_ex forces it for the row-major form; the pad
+ * slots of scale_km are written by either variant.  Other values ->
+ * FP8Q_ERR_VARIANT. */
+fp8q_status fp8q_quant_act_kmajor_ex(const uint16_t *x_bf16, uint8_t *q_e4m3,
+                                     float *scale_rm, float *scale_km,
+                                     uint32_t M, uint32_t K, int variant,
+                                     hipStream_t stream);
+
 /* Parameters of the quantizer variant selection rule
  * (fp8_act_quant_floor.rs, module header "The rule" and
  * fp8_act_quant_hopper_reject).  The K-grouped variant B runs only when its
@@ -194,15 +203,21 @@ fp8q_status fp8q_gemm_blockscaled(const uint8_t *a_e4m3, const float *a_scale_km
                                   uint16_t *out_bf16, uint32_t M, uint32_t N,
                                   uint32_t K, hipStream_t stream);
 
-/* The kernel fp8q_gemm_blockscaled runs for this shape (the ids of
- * fp8q_gemm_blockscaled_ex below), or -1 if N or K is not a positive
- * multiple of 128.  Pure host function: no device access, thread-safe. */
+/* The kernel fp8q_gemm_blockscaled runs for this shape on a device with
+ * cu_count compute units (the ids of fp8q_gemm_blockscaled_ex below), or -1
+ * if N or K is not a positive multiple of 128 or cu_count is 0.  Pure host
+ * function, thread-safe. */
+int fp8q_gemm_select_cus(uint32_t M, uint32_t N, uint32_t K, uint32_t cu_count);
+
+/* fp8q_gemm_select_cus with the compute-unit count of the current HIP
+ * device (256, a full MI355X, when no device can be queried): the choice
+ * the launching entry points make on that device. */
 int fp8q_gemm_select(uint32_t M, uint32_t N, uint32_t K);
 
 /* As fp8q_gemm_blockscaled with the kernel forced: 0 = auto (2 for
  * M <= 64 and for M <= 128 when N <= 8192, 1 below 512 rows; from 512 rows
- * on 5 or 1, whichever needs fewer rounds of workgroups on the 256 CUs when
- * a last round of at most one 128x128 workgroup per CU counts as half a
+ * on 5 or 1, whichever needs fewer rounds of workgroups on the device's CUs
+ * when a last round of at most one 128x128 workgroup per CU counts as half a
  * round; 5 on a tie), 1 =
  * the LDS-tiled MFMA kernel with 128x128 tiles and two workgroups per CU,
  * 2 = the skinny kernel (decode and small-batch widths; rows in
@@ -245,19 +260,25 @@ fp8q_status fp8q_gemm_blockscaled_splitk(const uint8_t *a_e4m3, const float *a_s
                                          size_t workspace_bytes, uint32_t M, uint32_t N,
                                          uint32_t K, uint32_t splits, hipStream_t stream);
 
-/* The split count fp8q_gemm_blockscaled_splitk takes for splits = 0, with
- * T = ceil(M/128) * (N/128) tiles of 128x128 and c = min(floor(K/1280), 6)
- * (at least 10 K blocks a split):
- *   min(floor(256 / T), c) if that is at least 2 (one workgroup per CU on
- *   256 CUs), else min(floor(512 / T), c) (two per CU)
- * when M > 64 and fp8q_gemm_select does not pick the 256x128 kernel (id 5),
- * and 1 (no split) otherwise or when that count is below 2.  0 if N or K
- * is not a positive multiple of 128.  Pure host function. */
+/* The split count fp8q_gemm_blockscaled_splitk takes for splits = 0 on a
+ * device with C = cu_count compute units, with T = ceil(M/128) * (N/128)
+ * tiles of 128x128 and c = min(floor(K/1280), 6) (at least 10 K blocks a
+ * split):
+ *   min(floor(C / T), c) if that is at least 2 (one workgroup per CU),
+ *   else min(floor(2C / T), c) (two per CU)
+ * when M > 64 and fp8q_gemm_select_cus does not pick the 256x128 kernel
+ * (id 5), and 1 (no split) otherwise or when that count is below 2.  0 if N
+ * or K is not a positive multiple of 128 or cu_count is 0.  Pure host
+ * function. */
+uint32_t fp8q_gemm_splitk_select_cus(uint32_t M, uint32_t N, uint32_t K, uint32_t cu_count);
+
+/* fp8q_gemm_splitk_select_cus for the current HIP device (256 compute
+ * units when no device can be queried). */
 uint32_t fp8q_gemm_splitk_select(uint32_t M, uint32_t N, uint32_t K);
 
 /* Workspace bytes of fp8q_gemm_blockscaled_splitk: splits * M * N * 4 for
- * splits >= 2 (splits = 0: the automatic count), 0 for no split or for an
- * invalid shape or count.  Pure host function. */
+ * splits >= 2 (splits = 0: the automatic count on the current device), 0
+ * for no split or for an invalid shape or count.  Host function. */
 size_t fp8q_gemm_splitk_workspace_bytes(uint32_t M, uint32_t N, uint32_t K, uint32_t splits);
 
 /* Per-row FP8 weights (the pages' other weight format, dispatch_proj.rs,
@@ -401,10 +422,11 @@ fp8q_status fp8q_ffn_gate_up(const uint8_t *x_e4m3, const float *x_scale_km,
  * -1 if H or I is not a positive multiple of 128.  Pure host function. */
 int fp8q_ffn_select(uint32_t M, uint32_t H, uint32_t I);
 
-/* Bytes of device workspace fp8q_ffn needs for (M, H, I, variant); 0 for an
- * invalid variant or shape.  Variant 2 also holds the bf16 gate and up
- * outputs (4*M*I bytes more); where fp8q_gemm_splitk_select(M, H, I) splits
- * the down projection, its partials add splits*M*H*4 bytes. */
+/* Bytes of device workspace fp8q_ffn needs for (M, H, I, variant) on the
+ * current HIP device; 0 for an invalid variant or shape.  Variant 2 also
+ * holds the bf16 gate and up outputs (4*M*I bytes more); where
+ * fp8q_gemm_splitk_select(M, H, I) splits the down projection, its partials
+ * add splits*M*H*4 bytes. */
 size_t fp8q_ffn_workspace_bytes(uint32_t M, uint32_t H, uint32_t I, int variant);
 
 /* The whole FFN:

@@ -70,8 +70,6 @@ def _load():
     lib.oracle_e4m3_encode_array.restype = None
     lib.oracle_quant_act.argtypes = [P, P, P, I, I]
     lib.oracle_quant_act.restype = None
-    lib.oracle_act_scales.argtypes = [P, P, I, I]
-    lib.oracle_act_scales.restype = None
     lib.oracle_m_pad.argtypes = [I]
     lib.oracle_m_pad.restype = I
     lib.oracle_scale_to_kmajor.argtypes = [P, P, I, I]
@@ -135,14 +133,6 @@ def quant_act(x_bf16: np.ndarray):
     s = np.empty((M, K // GROUP), dtype=np.float32)
     _load().oracle_quant_act(_p(x), _p(q), _p(s), M, K)
     return q, s
-
-
-def act_scales(x_bf16: np.ndarray) -> np.ndarray:
-    x = np.ascontiguousarray(x_bf16, dtype=np.uint16)
-    M, K = x.shape
-    s = np.empty((M, K // GROUP), dtype=np.float32)
-    _load().oracle_act_scales(_p(x), _p(s), M, K)
-    return s
 
 
 def scale_to_kmajor(scale_rm: np.ndarray) -> np.ndarray:

@@ -137,23 +137,6 @@ void oracle_quant_act(const uint16_t *x, uint8_t *q, float *scale, int64_t M,
   }
 }
 
-/* Scales only (the quantizer's second output), for timing samples. */
-void oracle_act_scales(const uint16_t *x, float *scale, int64_t M, int64_t K) {
-  const int64_t G = K / GROUP;
-  int64_t r;
-#pragma omp parallel for schedule(static)
-  for (r = 0; r < M * G; ++r) {
-    const uint16_t *xs = x + (r / G) * K + (r % G) * GROUP;
-    float amax = 0.0f;
-    int j;
-    for (j = 0; j < GROUP; ++j) {
-      float v = fabsf(bf16_to_f32(xs[j]));
-      if (v > amax) amax = v;
-    }
-    scale[r] = amax / 448.0f;
-  }
-}
-
 /* -------------------------------------------------------------- relayout */
 
 int64_t oracle_m_pad(int64_t M) { return (M + 15) / 16 * 16; }

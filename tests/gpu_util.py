@@ -65,3 +65,18 @@ def require_gpu():
         pytest.skip("no GPU")
     name = torch.cuda.get_device_properties(0).gcnArchName
     assert name.startswith("gfx950"), f"expected gfx950, got {name}"
+
+
+RTOL = 1e-3  # relative-RMS bar of the GEMM outputs
+
+
+def assert_tol(o, r, what, rms=None):
+    """The GEMM accuracy contract against the oracle's fp64 product r:
+    rel_rms <= RTOL against r rounded to bf16 (the output format) and, for
+    every element, |o - r| <= ulp_bf16(r) + 1e-3 * RMS(r).  rms: RMS(r) when
+    r is a sample of the output (else it is taken from r)."""
+    import oracle
+    rel, exc, relf = oracle.gemm_errors(o, r, rms)
+    log(f"  {what}: rel_rms={rel:.3e} (vs fp64 {relf:.3e}) worst/bound={exc:.3f}")
+    assert rel <= RTOL, f"{what}: rel_rms {rel}"
+    assert exc <= 1.0, f"{what}: per-element error {exc} x bound"

@@ -90,6 +90,11 @@ def test_kmajor_validation():
     assert L.fp8q_quant_act_kmajor(GOOD, GOOD, BAD, GOOD, 3, 128, None) == 3
     assert L.fp8q_quant_act_kmajor(GOOD, GOOD, None, None, 3, 128, None) == 1
     assert L.fp8q_quant_act_kmajor(GOOD, GOOD, None, GOOD, 0, 128, None) == 0
+    assert L.fp8q_quant_act_kmajor_ex(GOOD, GOOD, None, GOOD, 3, 128, 3, None) == 6   # variant
+    assert L.fp8q_quant_act_kmajor_ex(GOOD, GOOD, None, GOOD, 3, 128, -1, None) == 6
+    assert L.fp8q_quant_act_kmajor_ex(GOOD, GOOD, None, GOOD, 3, 100, 2, None) == 2   # K % 128
+    assert L.fp8q_quant_act_kmajor_ex(GOOD, GOOD, BAD, GOOD, 3, 128, 2, None) == 3
+    assert L.fp8q_quant_act_kmajor_ex(GOOD, GOOD, None, GOOD, 0, 128, 2, None) == 0
 
 
 def test_gemm_validation():
@@ -117,19 +122,65 @@ def test_gemm_select():
     most 256 counting half), ties to the ping-pong kernel; bad N/K -> -1 (pure
     host function).  The expected values are the faster kernel measured at
     each of these shapes."""
+    sel = fp8q.fp8q_gemm_select
     for M, want in ((1, 2), (16, 2), (25, 2), (64, 2), (65, 2), (128, 2), (129, 1), (511, 1),
                     (512, 1), (768, 1), (1024, 5), (1168, 5), (1536, 5), (2047, 1), (2048, 1),
                     (3072, 5), (4576, 5), (16384, 5)):
-        assert fp8q.fp8q_gemm_select(M, 5120, 17408) == want, M
+        assert sel(M, 5120, 17408, 256) == want, M
     for M, want in ((64, 2), (65, 1), (128, 1), (640, 1), (768, 5), (1024, 1), (1168, 5),
                     (1536, 1), (2048, 1), (3072, 1), (4576, 5)):
-        assert fp8q.fp8q_gemm_select(M, 17408, 5120) == want, M
+        assert sel(M, 17408, 5120, 256) == want, M
     for M, want in ((768, 5), (1024, 5), (1168, 5), (1536, 1), (2048, 1), (3072, 1), (4576, 1)):
-        assert fp8q.fp8q_gemm_select(M, 6144, 5120) == want, M
-    assert fp8q.fp8q_gemm_select(128, 8192, 5120) == 2
-    assert fp8q.fp8q_gemm_select(128, 8320, 5120) == 1
-    assert fp8q.fp8q_gemm_select(64, 100, 128) == -1
-    assert fp8q.fp8q_gemm_select(64, 128, 0) == -1
+        assert sel(M, 6144, 5120, 256) == want, M
+    assert sel(128, 8192, 5120, 256) == 2
+    assert sel(128, 8320, 5120, 256) == 1
+    assert sel(64, 100, 128, 256) == -1
+    assert sel(64, 128, 0, 256) == -1
+    assert sel(640, 128, 128, 0) == -1
+
+
+def _rounds_rule(M, N, cus):
+    """The documented round-count rule from 512 rows on, in half rounds."""
+    nt = N // 128
+    t_pp, t_128 = (M + 255) // 256 * nt, (M + 127) // 128 * nt
+    c_pp = 2 * -(-t_pp // cus)
+    tail = t_128 % (2 * cus)
+    c_128 = 2 * (t_128 // (2 * cus)) + (0 if tail == 0 else 2 if tail > cus else 1)
+    return 5 if c_pp <= c_128 else 1
+
+
+def test_gemm_select_follows_the_cu_count():
+    """The kernel choice counts rounds of workgroups on the device's own CUs.
+    Hand-worked cases at N = 5120 (40 column tiles): M = 1024 on 128 CUs has
+    160 ping-pong tiles (2 rounds = 4 half rounds) against 320 128x128
+    workgroups (one round of 256 and a light tail of 64 = 3 half rounds):
+    kernel 1, where 256 CUs take kernel 5; M = 4576 on 128 CUs: 720 tiles =
+    12 half rounds against 1440 workgroups = 5 rounds + 160 > 128 = 12: a tie,
+    kernel 5.  A 32-CU partition of the device: M = 640 at N = 17408 (136
+    tiles): 3 x 136 = 408 ping-pong tiles (13 rounds) against 5 x 136 = 680
+    workgroups (10 rounds + 40): kernel 1 (25 half rounds)."""
+    sel = fp8q.fp8q_gemm_select
+    assert sel(1024, 5120, 17408, 256) == 5 and sel(1024, 5120, 17408, 128) == 1
+    assert sel(4576, 5120, 17408, 128) == 5
+    assert sel(640, 17408, 5120, 32) == 1
+    for cus in (32, 80, 128, 200, 256, 304):
+        for N in (5120, 6144, 17408):
+            for M in (512, 640, 1000, 1168, 2048, 3000, 4576, 9999):
+                assert sel(M, N, 5120, cus) == _rounds_rule(M, N, cus), (M, N, cus)
+    # below the round rule's range the CU count does not matter
+    for cus in (32, 256):
+        assert sel(64, 5120, 17408, cus) == 2 and sel(300, 17408, 5120, cus) == 1
+
+
+def test_selectors_default_to_a_full_device_without_one():
+    """Without a HIP device (this host) the device-free queries assume the
+    256 CUs of a full MI355X; with one they use its CU count."""
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a device is present: the queries use its CU count")
+    for M, N, K in ((1024, 5120, 17408), (300, 6144, 5120), (65, 5120, 17408)):
+        assert fp8q.fp8q_gemm_select(M, N, K) == fp8q.fp8q_gemm_select(M, N, K, 256)
+        assert fp8q.fp8q_gemm_splitk_select(M, N, K) == fp8q.fp8q_gemm_splitk_select(M, N, K, 256)
 
 
 def test_proj_quant_fused():
@@ -267,7 +318,8 @@ def test_splitk_select():
     """Split count above 64 rows, outside the 256x128 kernel's range, with
     c = min(floor(K/1280), 6): min(floor(256 / tiles), c) if at least 2,
     else min(floor(512 / tiles), c), 1 below 2; 0 for a bad N or K."""
-    sel = fp8q.fp8q_gemm_splitk_select
+    def sel(M, N, K):
+        return fp8q.fp8q_gemm_splitk_select(M, N, K, 256)
     for M, want in ((16, 1), (64, 1), (65, 6), (128, 6), (129, 3), (256, 3), (257, 2), (384, 2),
                     (385, 3), (512, 3), (513, 2), (768, 2), (769, 1), (1168, 1), (2048, 1)):
         assert sel(M, 5120, 17408) == want, M
@@ -281,6 +333,20 @@ def test_splitk_select():
     assert sel(4096, 128, 17408) == 6      # 32 128x128 tiles: six splits
     assert sel(100, 100, 1280) == 0
     assert sel(100, 128, 0) == 0
+
+
+def test_splitk_select_follows_the_cu_count():
+    """The split counts are sized to the device's CUs: at N = 5120, K = 17408
+    (40 column tiles, at most 6 splits), M = 65 takes floor(128 / 40) = 3
+    splits on 128 CUs (one workgroup per CU) and 6 on 256; M = 300 (120
+    tiles) takes floor(256 / 120) = 2 on 128 CUs (two per CU) and on 304 CUs
+    floor(304 / 120) = 2; M = 129 (80 tiles) on 32 CUs: floor(64 / 80) = 0,
+    no split."""
+    sel = fp8q.fp8q_gemm_splitk_select
+    assert sel(65, 5120, 17408, 128) == 3 and sel(65, 5120, 17408, 256) == 6
+    assert sel(300, 5120, 17408, 128) == 2 and sel(300, 5120, 17408, 304) == 2
+    assert sel(129, 5120, 17408, 32) == 1
+    assert sel(65, 5120, 17408, 0) == 0
 
 
 def test_ffn_workspace_holds_split_partials():

@@ -23,7 +23,7 @@ input; the post-SiLU intermediate is quantized once for down).
     and the output
     is within the projection tolerance plus the derived effect of those
     codes; full FFN sizes (H=5120, I=17408) at decode, prefill (M=1168) and
-    large prefill (M=4576) widths on sampled rows.
+    large prefill (M=4576) widths on one row of every 128-row tile.
 """
 import dataclasses
 import itertools
@@ -368,7 +368,8 @@ def test_ffn_random_small_widths(orc, M):
 @pytest.mark.parametrize("name,M", [("ffn_decode", 16), ("ffn_decode", 25), ("ffn_prefill", 256),
                                     ("ffn_prefill", 1168), ("ffn_large", 4576)])
 def test_ffn_full_size_sampled_rows(orc, name, M):
-    """Full model widths; M = 256 at the prefill widths is a row count whose
+    """Full model widths, checked on one row of every 128-row tile (every row
+    at decode widths); M = 256 at the prefill widths is a row count whose
     down projection runs split-K."""
     base = synth.ffn_workload(name)
     w = synth.ffn_workload(name, M) if M in [v.M for v in synth.FFN_WORKLOADS[name]] else \
@@ -378,7 +379,10 @@ def test_ffn_full_size_sampled_rows(orc, name, M):
     W = _weights(orc, wf)
     del wf
     rng = np.random.default_rng(M)
-    rows = np.unique(np.concatenate([[0, M - 1], rng.integers(0, M, 6 if M > 64 else M)]))
+    # the first and last rows and one random row of every 128-row tile
+    # (all rows at decode widths)
+    per_tile = [rng.integers(m0, min(m0 + 128, M), 1) for m0 in range(0, M, 128)]
+    rows = np.arange(M) if M <= 64 else np.unique(np.concatenate([[0, M - 1], *per_tile]))
     log(f"  oracle on rows {rows.tolist()}")
     ref = orc.ffn_ref(x, *W[0], *W[1], *W[2], rows=rows)
     log(f"  fp8q_ffn variant {fp8q.fp8q_ffn_select(M, w.H, w.I)}")

@@ -4,23 +4,24 @@ Accuracy contract against the oracle's fp64 block-form product r:
   rel_rms = sqrt(sum (o-b)^2 / sum b^2) <= 1e-3 with b = r rounded to bf16
   (the output format; rounding alone puts any bf16 output ~1.66e-3 away from
   the unrounded r), and for every element |o - r| <= ulp_bf16(r) + 1e-3*RMS(r).
-At sizes the oracle finishes in seconds the whole output is compared; at the
-full prefill sizes a sample of outputs spanning every M tile (the ragged
-last one included) and every N tile is compared (RMS(ref) estimated from the
-sample).  Exact special cases (powers of two, one-hot rows, small integers)
-must match bit for bit, and a wrong scale layout must fail by a wide margin.
+The whole output is compared at every size, the full prefill projections
+(M=1168, N=17408, K=5120 and M=4576, N=5120, K=17408) included: every kernel
+the API can force, the split-K form, and the whole projection (fp8q_proj)
+against the oracle's full fp64 product; the tiled kernels' outputs must be
+bit-identical to each other and to a repeated launch of themselves.  Exact
+special cases (powers of two, one-hot rows, small integers) must match bit
+for bit, and a wrong scale layout must fail by a wide margin.
 """
 import numpy as np
 import pytest
 import torch
 
 import synth
-from gpu_util import Guarded, bf16_bits_to_f64, dev, host, log, require_gpu
+from gpu_util import RTOL, Guarded, bf16_bits_to_f64, dev, host, log, require_gpu, assert_tol
 
 pytestmark = pytest.mark.gpu
 
 fp8q = None
-RTOL = 1e-3
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -51,13 +52,6 @@ def _gemm_gpu(orc, a, a_s, wq, ws, kernel=0, km=None):
     return bf16_bits_to_f64(host(out.t))
 
 
-def _assert_tol(o, r, what, rms=None):
-    rel, exc, relf = orc_errors(o, r, rms)
-    log(f"  {what}: rel_rms={rel:.3e} (vs fp64 {relf:.3e}) worst/bound={exc:.3f}")
-    assert rel <= RTOL, f"{what}: rel_rms {rel}"
-    assert exc <= 1.0, f"{what}: per-element error {exc} x bound"
-
-
 def orc_errors(o, r, rms=None):
     import oracle
     return oracle.gemm_errors(o, r, rms)
@@ -81,7 +75,7 @@ def test_gemm_small_full(orc, M, N, K):
     ref = orc.gemm_ref(a, a_s, wq, ws)
     for kern in _kernels_for(M, N):
         log(f"gemm M={M} N={N} K={K} kernel={kern}")
-        _assert_tol(_gemm_gpu(orc, a, a_s, wq, ws, kern), ref, f"M{M}N{N}K{K}k{kern}")
+        assert_tol(_gemm_gpu(orc, a, a_s, wq, ws, kern), ref, f"M{M}N{N}K{K}k{kern}")
 
 
 def test_gemm_tiny_workload(orc):
@@ -90,7 +84,7 @@ def test_gemm_tiny_workload(orc):
     ref = orc.gemm_ref(a, a_s, wq, ws)
     for kern in _kernels_for(w.M, w.N):
         log(f"gemm tiny kernel={kern}")
-        _assert_tol(_gemm_gpu(orc, a, a_s, wq, ws, kern), ref, f"tiny k{kern}")
+        assert_tol(_gemm_gpu(orc, a, a_s, wq, ws, kern), ref, f"tiny k{kern}")
 
 
 @pytest.mark.parametrize("M", [16, 17, 25])
@@ -101,36 +95,130 @@ def test_gemm_decode_workload_full(orc, M):
     ref = orc.gemm_ref(a, a_s, wq, ws)
     for kern in _kernels_for(M, w.N):
         log(f"gemm decode M={M} kernel={kern}")
-        _assert_tol(_gemm_gpu(orc, a, a_s, wq, ws, kern), ref, f"decode M{M} k{kern}")
+        assert_tol(_gemm_gpu(orc, a, a_s, wq, ws, kern), ref, f"decode M{M} k{kern}")
 
 
-def _sample_idx(M, N, per_tile=24, seed=0):
-    rng = np.random.default_rng(seed)
-    ms, ns = [], []
-    for m0 in range(0, M, 128):
-        for n0 in range(0, N, 128):
-            ms.append(rng.integers(m0, min(m0 + 128, M), per_tile))
-            ns.append(rng.integers(n0, n0 + 128, per_tile))
-    # the last row and column always
-    ms.append(np.full(N // 128, M - 1))
-    ns.append(np.arange(0, N, 128) + 127)
-    return np.concatenate(ms), np.concatenate(ns)
+_FULL = {}
 
 
+def _full_size(orc, name):
+    """Operands of a full-size projection workload on host and device and the
+    oracle's fp64 product over all M*N outputs (one workload kept at a time)."""
+    if name not in _FULL:
+        _FULL.clear()
+        w = synth.WORKLOADS[name][0]
+        log(f"inputs {w.desc}")
+        x, a, a_s, wq, ws = _operands(orc, w)
+        log(f"oracle {w.desc}: full fp64 product")
+        ref = orc.gemm_ref(a, a_s, wq, ws)
+        d = {"w": w, "x": x, "a": a, "a_s": a_s, "wq": wq, "ws": ws, "ref": ref,
+             "a_d": dev(a), "km_d": dev(orc.scale_to_kmajor(a_s)), "wq_d": dev(wq),
+             "ws_d": dev(ws)}
+        _FULL[name] = d
+    return _FULL[name]
+
+
+def _gemm_dev(d, kernel, canary=True):
+    """fp8q_gemm_blockscaled on the resident operands of d; the raw bf16 bits."""
+    M, N = d["w"].M, d["w"].N
+    out = Guarded((M, N), torch.int16)
+    fp8q.fp8q_gemm_blockscaled(d["a_d"], d["km_d"], d["wq_d"], d["ws_d"], out.t, kernel=kernel)
+    torch.cuda.synchronize()
+    if canary:
+        out.check_canary()
+    return host(out.t).view(np.uint16)
+
+
+@pytest.mark.slow
 @pytest.mark.parametrize("name", ["prefill", "large_prefill"])
-def test_gemm_prefill_workloads_sampled(orc, name):
-    w = synth.WORKLOADS[name][0]
-    log(f"inputs {w.desc}")
-    _, a, a_s, wq, ws = _operands(orc, w)
-    ms, ns = _sample_idx(w.M, w.N, per_tile=8 if name == "large_prefill" else 16)
-    log(f"oracle {w.desc} samples={len(ms)}")
-    ref = orc.gemm_ref_at(a, a_s, wq, ws, ms, ns)
-    rms = float(np.sqrt(np.mean(ref * ref)))
-    for kern in _kernels_for(w.M, w.N):
-        log(f"gemm {w.desc} kernel={kern}")
-        o = _gemm_gpu(orc, a, a_s, wq, ws, kern)
-        _assert_tol(o[ms, ns], ref, f"{w.desc} k{kern}", rms)
-        assert np.all(np.isfinite(o))
+def test_gemm_full_size_every_kernel(orc, name):
+    """Every forceable kernel at the full prefill sizes, all M*N outputs against
+    the oracle; the tiled kernels (1, 3, 4, 5) and the automatic choice are
+    bit-identical (they add the scaled block products in the same order)."""
+    d = _full_size(orc, name)
+    bits = {}
+    for kern in (0, 1, 2, 3, 4, 5):
+        log(f"gemm {d['w'].desc} kernel={kern}")
+        o = _gemm_dev(d, kern)
+        assert_tol(bf16_bits_to_f64(o), d["ref"], f"{d['w'].desc} k{kern}")
+        if kern != 2:
+            bits[kern] = o
+    for kern in (0, 3, 4, 5):
+        assert np.array_equal(bits[kern], bits[1]), f"kernel {kern} differs from kernel 1"
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("name", ["prefill", "large_prefill"])
+def test_gemm_full_size_repeat_bit_identical(orc, name):
+    """Race detector: four launches of the automatic kernel back to back (no
+    host synchronization between them) into four outputs, and two more of the
+    128x128 kernel, all M*N outputs compared bit for bit."""
+    d = _full_size(orc, name)
+    M, N = d["w"].M, d["w"].N
+    for kern in (0, 1):
+        outs = [Guarded((M, N), torch.int16) for _ in range(4 if kern == 0 else 2)]
+        log(f"gemm {d['w'].desc} kernel={kern} x{len(outs)} back to back")
+        for g in outs:
+            fp8q.fp8q_gemm_blockscaled(d["a_d"], d["km_d"], d["wq_d"], d["ws_d"], g.t, kernel=kern)
+        torch.cuda.synchronize()
+        first = host(outs[0].t)
+        for i, g in enumerate(outs):
+            g.check_canary()
+            assert np.array_equal(host(g.t), first), f"kernel {kern}: launch {i} differs"
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("name", ["prefill", "large_prefill"])
+def test_gemm_splitk_full_size(orc, name):
+    """The split-K form at the full prefill sizes (the automatic count, which
+    is no split here, and two forced counts), all M*N outputs against the
+    oracle, workspace canaries checked."""
+    d = _full_size(orc, name)
+    w = d["w"]
+    M, N, K = w.M, w.N, w.K
+    for splits in (0, 2, 3):
+        need = fp8q.fp8q_gemm_splitk_workspace_bytes(M, N, K, splits)
+        log(f"splitk {w.desc} splits={splits} workspace={need}")
+        out = Guarded((M, N), torch.int16)
+        work = Guarded((max(need, 16) // 4,), torch.float32, fill=0x7F) if need else None
+        fp8q.fp8q_gemm_blockscaled_splitk(d["a_d"], d["km_d"], d["wq_d"], d["ws_d"], out.t,
+                                          None if work is None else work.t, splits=splits)
+        torch.cuda.synchronize()
+        out.check_canary()
+        if work is not None:
+            work.check_canary()
+        assert_tol(bf16_bits_to_f64(host(out.t)), d["ref"], f"{w.desc} splitk s{splits}")
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("name", ["prefill", "large_prefill"])
+def test_proj_full_size(orc, name):
+    """fp8q_proj end to end at the full prefill sizes (M=1168: one kernel
+    writes both scale layouts; M=4576: the quantizer and the relayout run
+    separately): codes and both scale layouts bit-exact, all M*N outputs
+    within the tolerance of the oracle."""
+    d = _full_size(orc, name)
+    w = d["w"]
+    M, N, K = w.M, w.N, w.K
+    assert fp8q.fp8q_proj_quant_fused(M, K) == (name == "prefill")
+    out = Guarded((M, N), torch.int16)
+    aq = Guarded((M, K), torch.uint8)
+    asr = Guarded((M, K // 128), torch.float32)
+    askm = Guarded((K // 128, synth.ceil16(M)), torch.float32, fill=0x7F)
+    log(f"proj {w.desc}")
+    fp8q.fp8q_proj(dev(d["x"]), d["wq_d"], d["ws_d"], out.t, aq.t, asr.t, askm.t)
+    torch.cuda.synchronize()
+    for g in (out, aq, asr, askm):
+        g.check_canary()
+    assert np.array_equal(host(aq.t), d["a"])
+    assert np.array_equal(host(asr.t).view(np.uint32), d["a_s"].view(np.uint32))
+    assert np.array_equal(host(askm.t).view(np.uint32),
+                          orc.scale_to_kmajor(d["a_s"]).view(np.uint32))
+    assert_tol(bf16_bits_to_f64(host(out.t)), d["ref"], f"proj {w.desc}")
+
+
+def test_full_size_release():
+    _FULL.clear()
 
 
 def test_gemm_block_scale_isolation_exact(orc):
@@ -216,7 +304,7 @@ def test_gemm_rowmajor_scales_fail(orc):
 _PROJ_SPLIT = synth.Workload("proj_split", 1000, 17408, 256, "laplace", 87, 50.0)
 
 
-@pytest.mark.parametrize("name,M", [("tiny", None), ("decode", 17), ("decode", 25),
+@pytest.mark.parametrize("name,M", [("tiny", None), ("decode", 16), ("decode", 17), ("decode", 25),
                                     ("prefill", 130), ("proj_split", None)])
 def test_proj_end_to_end(orc, name, M):
     if name == "proj_split":
@@ -242,7 +330,7 @@ def test_proj_end_to_end(orc, name, M):
     assert np.array_equal(host(aq.t), a)
     assert np.array_equal(host(asr.t).view(np.uint32), a_s.view(np.uint32))
     assert np.array_equal(host(askm.t).view(np.uint32), km_ref.view(np.uint32))
-    _assert_tol(bf16_bits_to_f64(host(out.t)), ref, f"proj {w.desc}")
+    assert_tol(bf16_bits_to_f64(host(out.t)), ref, f"proj {w.desc}")
 
 
 def test_gemm_repeatable(orc):
@@ -270,7 +358,7 @@ def test_gemm_long_k_weight_scale_chunks(orc):
     ref = orc.gemm_ref(a, a_s, wq, ws)
     for kern in _kernels_for(M, N):
         log(f"gemm long-K kernel={kern}")
-        _assert_tol(_gemm_gpu(orc, a, a_s, wq, ws, kern), ref, f"long-K k{kern}")
+        assert_tol(_gemm_gpu(orc, a, a_s, wq, ws, kern), ref, f"long-K k{kern}")
 
 
 @pytest.mark.parametrize("M,N,K", [(300, 384, 1280), (1168, 512, 2048), (4576, 256, 640),
@@ -319,4 +407,4 @@ def test_proj_deterministic_pattern(orc, M, N, K):
     assert np.array_equal(host(aq.t), a)
     assert np.array_equal(host(asr.t).view(np.uint32), a_s.view(np.uint32))
     assert np.array_equal(host(askm.t).view(np.uint32), orc.scale_to_kmajor(a_s).view(np.uint32))
-    _assert_tol(bf16_bits_to_f64(host(out.t)), orc.gemm_ref(a, a_s, wq, ws), f"pattern M{M}N{N}K{K}")
+    assert_tol(bf16_bits_to_f64(host(out.t)), orc.gemm_ref(a, a_s, wq, ws), f"pattern M{M}N{N}K{K}")

@@ -1,11 +1,14 @@
 """GPU parity of the activation quantizer and the scale relayout, bit-exact
 against the oracle (codes byte for byte, scales bit for bit).
 
-Covers both quantizer variants, the selector's choice and the fused
-quantizer + K-major kernel on every quantizer workload shape (M in {16, 25,
-1168, 4576, 16384} x K in {5120, 6144, 17408}), the activations of the GEMM
-workloads, ragged and degenerate inputs, and the exhaustive (x, amax) element
-map through the real kernels.  Output buffers carry canaries on both sides.
+Covers both quantizer variants and the selector's choice, each in the
+row-major form and in the fused form that writes the K-major scales (pad
+slots included, into a buffer that starts non-zero), on every quantizer
+workload shape (M in {16, 25, 1168, 4576, 16384} x K in {5120, 6144,
+17408}), the activations of the GEMM workloads, ragged and degenerate
+inputs, and the exhaustive (x, amax) element map through the real kernels
+with both variants on every chunk.  Output buffers carry canaries on both
+sides.
 """
 import numpy as np
 import pytest
@@ -53,21 +56,25 @@ def _run_all_variants(orc, x_bits, label):
         torch.cuda.synchronize()
         km.check_canary()
         assert np.array_equal(host(km.t).view(np.uint32), km_ref.view(np.uint32))
-    # fused quantizer writing both layouts, and the K-major-only form
-    log(f"quant fused {label} M={M} K={K}")
-    for with_rm in (True, False):
-        q = Guarded((M, K), torch.uint8)
-        s = Guarded((M, G), torch.float32) if with_rm else None
-        km = Guarded((G, synth.ceil16(M)), torch.float32, fill=0x7F)
-        fp8q.fp8q_quant_act_kmajor(x, q.t, s.t if s else None, km.t)
-        torch.cuda.synchronize()
-        q.check_canary()
-        km.check_canary()
-        assert np.array_equal(host(q.t), q_ref)
-        assert np.array_equal(host(km.t).view(np.uint32), km_ref.view(np.uint32))
-        if s:
-            s.check_canary()
-            assert np.array_equal(host(s.t).view(np.uint32), s_ref.view(np.uint32))
+    # fused quantizer writing both layouts, and the K-major-only form, for
+    # each variant: the K-major buffer starts non-zero (0x7F7F7F7F) so that
+    # unwritten pad slots show
+    for variant in (1, 2, 0):
+        log(f"quant fused {label} M={M} K={K} variant={variant}")
+        for with_rm in (True, False):
+            q = Guarded((M, K), torch.uint8)
+            s = Guarded((M, G), torch.float32) if with_rm else None
+            km = Guarded((G, synth.ceil16(M)), torch.float32, fill=0x7F)
+            fp8q.fp8q_quant_act_kmajor(x, q.t, s.t if s else None, km.t, variant=variant)
+            torch.cuda.synchronize()
+            q.check_canary()
+            km.check_canary()
+            assert np.array_equal(host(q.t), q_ref), f"codes differ (fused, variant {variant})"
+            assert np.array_equal(host(km.t).view(np.uint32), km_ref.view(np.uint32)), \
+                f"K-major scales or pad slots differ (fused, variant {variant})"
+            if s:
+                s.check_canary()
+                assert np.array_equal(host(s.t).view(np.uint32), s_ref.view(np.uint32))
 
 
 QUANT_SHAPES = [(w.M, w.K) for w in synth.WORKLOADS["quant_sweep"]]
@@ -87,7 +94,8 @@ def test_quant_gemm_workload_activations(orc, name):
         _run_all_variants(orc, x, w.desc)
 
 
-@pytest.mark.parametrize("M,K", [(1, 128), (1, 5120), (2, 384), (17, 640), (33, 17408), (255, 1152)])
+@pytest.mark.parametrize("M,K", [(1, 128), (1, 5120), (2, 384), (17, 640), (25, 6144), (33, 17408),
+                                 (255, 1152)])
 def test_quant_ragged(orc, M, K):
     rng = np.random.default_rng(M * 1000 + K)
     x = synth.f32_to_bf16_bits((rng.standard_normal((M, K)) *
@@ -123,27 +131,29 @@ def test_quant_empty_batch():
 @pytest.mark.slow
 def test_quant_exhaustive_element_map(orc):
     """Every finite (x, amax) bf16 pair with |x| <= amax through the real
-    kernels (variant A and B on alternate chunks), against the oracle."""
+    kernels, both variants A and B on every chunk, against the oracle."""
     total = 0
     for i, (lo, hi) in enumerate(synth.exhaustive_chunks(1 << 20)):
         g = synth.exhaustive_pair_groups(lo, hi)
         n = g.shape[0]
         q_ref, s_ref = orc.quant_act(g.reshape(1, -1))
-        variant = 1 + (i % 2)
-        log(f"exhaustive chunk {i} amax {lo:#06x}..{hi:#06x} groups={n} variant={variant}")
         x = dev(g)  # [n, 128]: one group per row
-        q = torch.empty((n, 128), dtype=torch.uint8, device="cuda")
-        s = torch.empty((n, 1), dtype=torch.float32, device="cuda")
-        fp8q.fp8q_quant_act(x, q, s, variant=variant)
-        torch.cuda.synchronize()
-        qh = host(q)
-        sh = host(s).reshape(1, -1)
-        assert np.array_equal(sh.view(np.uint32), s_ref.view(np.uint32)), f"scales, chunk {i}"
-        if not np.array_equal(qh.reshape(1, -1), q_ref):
-            bad = np.argwhere(qh.reshape(1, -1) != q_ref)[:5]
-            rows = [(int(b[1]) // 128, int(b[1]) % 128) for b in bad]
-            pytest.fail(f"chunk {i}: codes differ at (group, elem) {rows}: "
-                        f"x={[hex(g[r][c]) for r, c in rows]}")
+        for variant in (1, 2):
+            log(f"exhaustive chunk {i} amax {lo:#06x}..{hi:#06x} groups={n} variant={variant}")
+            q = torch.empty((n, 128), dtype=torch.uint8, device="cuda")
+            s = torch.empty((n, 1), dtype=torch.float32, device="cuda")
+            fp8q.fp8q_quant_act(x, q, s, variant=variant)
+            torch.cuda.synchronize()
+            qh = host(q)
+            sh = host(s).reshape(1, -1)
+            assert np.array_equal(sh.view(np.uint32), s_ref.view(np.uint32)), \
+                f"scales, chunk {i}, variant {variant}"
+            if not np.array_equal(qh.reshape(1, -1), q_ref):
+                bad = np.argwhere(qh.reshape(1, -1) != q_ref)[:5]
+                rows = [(int(b[1]) // 128, int(b[1]) % 128) for b in bad]
+                pytest.fail(f"chunk {i}, variant {variant}: codes differ at (group, elem) {rows}: "
+                            f"x={[hex(g[r][c]) for r, c in rows]}")
+            del q, s
         total += n
-        del x, q, s
+        del x
     assert total == synth.n_exhaustive_groups()

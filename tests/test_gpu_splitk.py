@@ -11,12 +11,11 @@ import pytest
 import torch
 
 import synth
-from gpu_util import Guarded, bf16_bits_to_f64, dev, host, log, require_gpu
+from gpu_util import Guarded, bf16_bits_to_f64, dev, host, log, require_gpu, assert_tol
 
 pytestmark = pytest.mark.gpu
 
 fp8q = None
-RTOL = 1e-3
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -45,14 +44,6 @@ def _splitk_gpu(orc, a, a_s, wq, ws, splits, km=None):
     return bf16_bits_to_f64(host(out.t))
 
 
-def _assert_tol(o, r, what, rms=None):
-    import oracle
-    rel, exc, relf = oracle.gemm_errors(o, r, rms)
-    log(f"  {what}: rel_rms={rel:.3e} (vs fp64 {relf:.3e}) worst/bound={exc:.3f}")
-    assert rel <= RTOL, f"{what}: rel_rms {rel}"
-    assert exc <= 1.0, f"{what}: per-element error {exc} x bound"
-
-
 def _random_operands(orc, M, N, K, seed, dist="normal"):
     rng = np.random.default_rng(seed)
     v = rng.laplace(0, 1, (M, K)) if dist == "laplace" else rng.standard_normal((M, K))
@@ -72,7 +63,7 @@ def test_splitk_full(orc, M, N, K, splits):
     a, a_s, wq, ws = _random_operands(orc, M, N, K, M * 31 + N + K + splits)
     ref = orc.gemm_ref(a, a_s, wq, ws)
     log(f"splitk M={M} N={N} K={K} splits={splits}")
-    _assert_tol(_splitk_gpu(orc, a, a_s, wq, ws, splits), ref, f"M{M}N{N}K{K}s{splits}")
+    assert_tol(_splitk_gpu(orc, a, a_s, wq, ws, splits), ref, f"M{M}N{N}K{K}s{splits}")
 
 
 def test_splitk_auto_falls_back_without_workspace(orc):
@@ -136,34 +127,19 @@ def test_splitk_repeatable(orc):
         assert np.array_equal(o1, o2)
 
 
-def _sample_idx(M, N, per_tile, seed=0):
-    rng = np.random.default_rng(seed)
-    ms, ns = [], []
-    for m0 in range(0, M, 128):
-        for n0 in range(0, N, 128):
-            ms.append(rng.integers(m0, min(m0 + 128, M), per_tile))
-            ns.append(rng.integers(n0, n0 + 128, per_tile))
-    ms.append(np.full(N // 128, M - 1))
-    ns.append(np.arange(0, N, 128) + 127)
-    return np.concatenate(ms), np.concatenate(ns)
-
-
 @pytest.mark.parametrize("M,N,K", [(512, 5120, 17408), (200, 6144, 5120)])
-def test_splitk_projection_shapes_sampled(orc, M, N, K):
+def test_splitk_projection_shapes_full(orc, M, N, K):
     """Medium row counts at the down- and a gate/up-projection shape, with the
-    automatic split count and one more: outputs sampled in every tile (the
-    ragged last row tile included) against the oracle."""
+    automatic split count and one more: all M*N outputs against the oracle."""
     a, a_s, wq, ws = _random_operands(orc, M, N, K, M + K, "laplace")
-    ms, ns = _sample_idx(M, N, per_tile=6)
-    log(f"oracle M={M} N={N} K={K} samples={len(ms)}")
-    ref = orc.gemm_ref_at(a, a_s, wq, ws, ms, ns)
-    rms = float(np.sqrt(np.mean(ref * ref)))
+    log(f"oracle M={M} N={N} K={K}: full fp64 product")
+    ref = orc.gemm_ref(a, a_s, wq, ws)
     auto = fp8q.fp8q_gemm_splitk_select(M, N, K)
     for splits in sorted({0, 2, max(auto, 2) + 1}):
         log(f"splitk M={M} N={N} K={K} splits={splits} (auto {auto})")
         o = _splitk_gpu(orc, a, a_s, wq, ws, splits)
         assert np.all(np.isfinite(o))
-        _assert_tol(o[ms, ns], ref, f"M{M}N{N}K{K}s{splits}", rms)
+        assert_tol(o, ref, f"M{M}N{N}K{K}s{splits}")
 
 
 @pytest.mark.parametrize("M,N,K", [(200, 1024, 5120), (96, 6144, 5120), (40, 512, 2048)])
@@ -203,4 +179,4 @@ def test_proj_splitk(orc, M, N, K):
         fp8q.fp8q_proj(dev(x), dev(wq), dev(ws), ref_out, aq.t, asr.t, askm.t)
         torch.cuda.synchronize()
         assert np.array_equal(o, bf16_bits_to_f64(host(ref_out)))
-    _assert_tol(o, orc.gemm_ref(a, a_s, wq, ws), f"proj_splitk M{M}N{N}K{K}")
+    assert_tol(o, orc.gemm_ref(a, a_s, wq, ws), f"proj_splitk M{M}N{N}K{K}")

@@ -10,7 +10,7 @@ or PyTorch fallback: the first call raises if the library has not been built
 Names match the C entry points:
 
   fp8q_quant_act(x, q, scale_rm, variant=0)
-  fp8q_quant_act_kmajor(x, q, scale_rm, scale_km)
+  fp8q_quant_act_kmajor(x, q, scale_rm, scale_km, variant=0)
   fp8q_scale_to_kmajor(scale_rm, scale_km)
   fp8q_gemm_blockscaled(a, a_scale_km, w, w_scale, out, kernel=0)
   fp8q_proj(x, w, w_scale, out, act_q, act_scale, act_scale_km)
@@ -57,6 +57,7 @@ _SIGS = {
     "fp8q_quant_act": (_I, [_P, _P, _P, _U, _U, _P]),
     "fp8q_quant_act_ex": (_I, [_P, _P, _P, _U, _U, _I, _P]),
     "fp8q_quant_act_kmajor": (_I, [_P, _P, _P, _P, _U, _U, _P]),
+    "fp8q_quant_act_kmajor_ex": (_I, [_P, _P, _P, _P, _U, _U, _I, _P]),
     "fp8q_default_select_params": (SelectParams, [_U]),
     "fp8q_quant_select_with": (_I, [_U, _U, ctypes.POINTER(SelectParams),
                                     ctypes.POINTER(_U * 3), ctypes.POINTER(ctypes.c_char_p)]),
@@ -66,11 +67,13 @@ _SIGS = {
     "fp8q_quant_log_slot": (_I, [_I, ctypes.c_char_p, _I]),
     "fp8q_scale_to_kmajor": (_I, [_P, _P, _U, _U, _P]),
     "fp8q_gemm_select": (_I, [_U, _U, _U]),
+    "fp8q_gemm_select_cus": (_I, [_U, _U, _U, _U]),
     "fp8q_proj_quant_fused": (_I, [_U, _U]),
     "fp8q_gemm_blockscaled": (_I, [_P, _P, _P, _P, _P, _U, _U, _U, _P]),
     "fp8q_gemm_blockscaled_ex": (_I, [_P, _P, _P, _P, _P, _U, _U, _U, _I, _P]),
     "fp8q_gemm_blockscaled_splitk": (_I, [_P, _P, _P, _P, _P, _P, _SZ, _U, _U, _U, _U, _P]),
     "fp8q_gemm_splitk_select": (_U, [_U, _U, _U]),
+    "fp8q_gemm_splitk_select_cus": (_U, [_U, _U, _U, _U]),
     "fp8q_gemm_splitk_workspace_bytes": (_SZ, [_U, _U, _U, _U]),
     "fp8q_proj": (_I, [_P, _P, _P, _P, _P, _P, _P, _U, _U, _U, _P]),
     "fp8q_proj_splitk": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _SZ, _U, _U, _U, _P]),
@@ -164,10 +167,10 @@ def fp8q_quant_act(x, q, scale_rm, variant: int = 0, stream=None):
                                   _stream(stream)))
 
 
-def fp8q_quant_act_kmajor(x, q, scale_rm, scale_km, stream=None):
+def fp8q_quant_act_kmajor(x, q, scale_rm, scale_km, variant: int = 0, stream=None):
     M, K = _dims(x, 2)
-    _check(lib().fp8q_quant_act_kmajor(_ptr(x), _ptr(q), _optr(scale_rm), _ptr(scale_km), M, K,
-                                      _stream(stream)))
+    _check(lib().fp8q_quant_act_kmajor_ex(_ptr(x), _ptr(q), _optr(scale_rm), _ptr(scale_km), M,
+                                         K, variant, _stream(stream)))
 
 
 def fp8q_scale_to_kmajor(scale_rm, scale_km, stream=None):
@@ -185,8 +188,11 @@ def fp8q_gemm_blockscaled(a, a_scale_km, w, w_scale, out, kernel: int = 0, strea
                                          _ptr(out), M, N, K, kernel, _stream(stream)))
 
 
-def fp8q_gemm_splitk_select(M: int, N: int, K: int) -> int:
-    """Split count fp8q_gemm_blockscaled_splitk takes with splits=0 (1 = no split)."""
+def fp8q_gemm_splitk_select(M: int, N: int, K: int, cu_count: int = None) -> int:
+    """Split count fp8q_gemm_blockscaled_splitk takes with splits=0 (1 = no split)
+    on the current device, or on a device with cu_count compute units."""
+    if cu_count is not None:
+        return int(lib().fp8q_gemm_splitk_select_cus(M, N, K, cu_count))
     return int(lib().fp8q_gemm_splitk_select(M, N, K))
 
 
@@ -333,8 +339,11 @@ def fp8q_quant_select(M: int, K: int, cu_count: int):
     return v, tuple(grid), (why.value.decode() if why.value else None)
 
 
-def fp8q_gemm_select(M: int, N: int, K: int) -> int:
-    """Kernel id the auto GEMM runs for this shape (see fp8q_gemm_blockscaled_ex)."""
+def fp8q_gemm_select(M: int, N: int, K: int, cu_count: int = None) -> int:
+    """Kernel id the auto GEMM runs for this shape (see fp8q_gemm_blockscaled_ex)
+    on the current device, or on a device with cu_count compute units."""
+    if cu_count is not None:
+        return int(lib().fp8q_gemm_select_cus(M, N, K, cu_count))
     return int(lib().fp8q_gemm_select(M, N, K))
 
 

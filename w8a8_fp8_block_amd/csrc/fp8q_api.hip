@@ -65,23 +65,45 @@ constexpr int kMaxDev = 64;
 std::atomic<int> g_dev_state[kMaxDev];  // 0 unknown, 1 gfx950, 2 other
 std::atomic<uint32_t> g_dev_cus[kMaxDev];
 
+// State of device dev (0 <= dev < kMaxDev): 1 gfx950, 2 other, 0 when its
+// properties cannot be read; the first query caches the state and the CU
+// count.
+int probe_device(int dev) {
+  int st = g_dev_state[dev].load(std::memory_order_acquire);
+  if (st == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return 0;
+    st = (strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+    g_dev_cus[dev].store((uint32_t)prop.multiProcessorCount, std::memory_order_relaxed);
+    g_dev_state[dev].store(st, std::memory_order_release);
+  }
+  return st;
+}
+
 fp8q_status check_device(const char* fn, uint32_t* cu_count = nullptr) {
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0)
     return fail(FP8Q_ERR_DEVICE, "%s: no current HIP device", fn);
   if (dev >= kMaxDev) return fail(FP8Q_ERR_DEVICE, "%s: device index %d unsupported", fn, dev);
-  int st = g_dev_state[dev].load(std::memory_order_acquire);
-  if (st == 0) {
-    hipDeviceProp_t prop;
-    if (hipGetDeviceProperties(&prop, dev) != hipSuccess)
-      return fail(FP8Q_ERR_DEVICE, "%s: hipGetDeviceProperties failed", fn);
-    st = (strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
-    g_dev_cus[dev].store((uint32_t)prop.multiProcessorCount, std::memory_order_relaxed);
-    g_dev_state[dev].store(st, std::memory_order_release);
-  }
+  const int st = probe_device(dev);
+  if (st == 0) return fail(FP8Q_ERR_DEVICE, "%s: hipGetDeviceProperties failed", fn);
   if (st != 1) return fail(FP8Q_ERR_DEVICE, "%s: current device %d is not gfx950", fn, dev);
   if (cu_count) *cu_count = g_dev_cus[dev].load(std::memory_order_relaxed);
   return FP8Q_OK;
+}
+
+// CU count the selector queries without a device argument assume when no
+// HIP device can be queried: a full MI355X.
+constexpr uint32_t kDefaultCus = 256;
+
+// CU count of the current device (what the launching entry points use), or
+// kDefaultCus when there is none.
+uint32_t current_cus() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) return kDefaultCus;
+  if (probe_device(dev) == 0) return kDefaultCus;
+  const uint32_t c = g_dev_cus[dev].load(std::memory_order_relaxed);
+  return c ? c : kDefaultCus;
 }
 
 fp8q_status launched(const char* fn, hipError_t e) {
@@ -171,7 +193,7 @@ fp8q_status run_quant(const char* fn, const uint16_t* x, uint8_t* q, float* srm,
 // workgroups per CU) below kTailRuleMinM rows.  From there on the choice
 // between them and the ping-pong 256 x 128 kernel (one workgroup per CU, a
 // few percent faster per full round) follows the last, partial round of
-// workgroups, on kGfx950Cus CUs: a ping-pong round costs one unit whether
+// workgroups on the device's CUs: a ping-pong round costs one unit whether
 // full or not, a 128 x 128 round one unit when more than one workgroup per
 // CU remains and about half a unit when at most one per CU does (a lone
 // workgroup has its CU to itself).  The kernel with fewer units wins; ties
@@ -188,47 +210,46 @@ constexpr uint32_t kSkinnyWideMaxN = 8192;
 // 8.5 vs 16.5 us at M*K/128 = 46720, 69 vs 56 us at 622336).
 constexpr uint64_t kFusedKmajorMaxGroups = 1u << 17;
 constexpr uint32_t kTailRuleMinM = 512;
-constexpr uint64_t kGfx950Cus = 256;
 
-int gemm_auto_kernel(uint32_t M, uint32_t N) {
+int gemm_auto_kernel(uint32_t M, uint32_t N, uint32_t cus) {
   if (M <= kSkinnyAutoMaxM || (M <= kSkinnyWideMaxM && N <= kSkinnyWideMaxN)) return 2;
   if (M < kTailRuleMinM) return 1;
+  const uint64_t c = cus ? cus : 1;
   const uint64_t nt = N / kGroup;
   const uint64_t t_pp = (M + 255) / 256 * nt, t_128 = (M + 127) / 128 * nt;
   // costs in half rounds
-  const uint64_t c_pp = 2 * ((t_pp + kGfx950Cus - 1) / kGfx950Cus);
-  const uint64_t tail = t_128 % (2 * kGfx950Cus);
-  const uint64_t c_128 = 2 * (t_128 / (2 * kGfx950Cus)) + (tail == 0 ? 0 : tail > kGfx950Cus ? 2 : 1);
+  const uint64_t c_pp = 2 * ((t_pp + c - 1) / c);
+  const uint64_t tail = t_128 % (2 * c);
+  const uint64_t c_128 = 2 * (t_128 / (2 * c)) + (tail == 0 ? 0 : tail > c ? 2 : 1);
   return c_pp <= c_128 ? 5 : 1;
 }
 
-// Split-K (fp8q_gemm_blockscaled_splitk): splits = floor(256 / tiles) when
+// Split-K (fp8q_gemm_blockscaled_splitk): splits = floor(CUs / tiles) when
 // that is at least 2 (the split grid fits one workgroup per CU and runs the
-// three-stage form), else floor(512 / tiles) (one round of two 128x128
+// three-stage form), else floor(2 CUs / tiles) (one round of two 128x128
 // workgroups per CU, two stages), at most K/1280 (10 K blocks a split) and
 // 6, for more than kSplitMinM rows and wherever the single-pass choice is
 // not the 256 x 128 kernel.  Cold
-// caches (bench.py --gemm-sweep), us single-pass -> split-K: N=5120,
+// caches (bench.py --gemm-sweep, 256 CUs), us single-pass -> split-K: N=5120,
 // K=17408: 87 -> 46 at M=65, 135 -> 55 at M=192, 143 -> 73 at M=384, 143 ->
 // 87 at M=512, 144 -> 109 at M=768; N=6144, K=5120: 32 -> 23 at M=65, 47 ->
 // 32 at M=192, 51 -> 39 at M=384; N=17408, K=5120: 55 -> 47 at M=65.  A
 // count past one round (M=512, N=5120: 4 splits, 640 workgroups) was up to
 // 30% slower than the one below it; beyond 512 tiles no count helped.
-constexpr uint32_t kSplitTargetWgs = 512;
 constexpr uint32_t kSplitMinBlocks = 10;
 constexpr uint32_t kSplitMax = 6;
 constexpr uint32_t kSplitMinM = 64;
 constexpr uint32_t kSplitMaxUser = 64;  // bound of an explicit split count
 
-uint32_t splitk_auto(uint32_t M, uint32_t N, uint32_t K) {
-  if (M <= kSplitMinM || gemm_auto_kernel(M, N) == 5) return 1;
+uint32_t splitk_auto(uint32_t M, uint32_t N, uint32_t K, uint32_t cus) {
+  if (M <= kSplitMinM || gemm_auto_kernel(M, N, cus) == 5) return 1;
   const uint64_t tiles = (uint64_t)((M + 127) / 128) * (N / 128);
   const uint64_t cap = std::min<uint64_t>(K / kGroup / kSplitMinBlocks, kSplitMax);
   // prefer a count whose grid fits one workgroup per CU (the three-stage
   // form), else one round of two per CU
-  const uint64_t s1 = std::min<uint64_t>(kSplitTargetWgs / 2 / tiles, cap);
+  const uint64_t s1 = std::min<uint64_t>(cus / tiles, cap);
   if (s1 >= 2) return (uint32_t)s1;
-  const uint64_t s2 = std::min<uint64_t>(kSplitTargetWgs / tiles, cap);
+  const uint64_t s2 = std::min<uint64_t>(2ull * cus / tiles, cap);
   return s2 < 2 ? 1 : (uint32_t)s2;
 }
 
@@ -239,12 +260,12 @@ uint64_t splitk_workspace(uint32_t M, uint32_t N, uint32_t splits) {
 fp8q_status run_gemm(const char* fn, const uint8_t* a, const float* as, const uint8_t* w,
                      const float* ws, uint16_t* out, uint32_t M, uint32_t N, uint32_t K, int kernel,
                      bool row_scaled, hipStream_t s) {
-  if (kernel == 0) kernel = gemm_auto_kernel(M, N);
-  if (kernel == 2 && M > kSkinnyMaxM)
-    return fail(FP8Q_ERR_VARIANT, "%s: skinny kernel needs M <= %u (M=%u)", fn, kSkinnyMaxM, M);
   uint32_t cus = 0;
   const fp8q_status st = check_device(fn, &cus);
   if (st != FP8Q_OK) return st;
+  if (kernel == 0) kernel = gemm_auto_kernel(M, N, cus);
+  if (kernel == 2 && M > kSkinnyMaxM)
+    return fail(FP8Q_ERR_VARIANT, "%s: skinny kernel needs M <= %u (M=%u)", fn, kSkinnyMaxM, M);
   const hipError_t e =
       (kernel == 2) ? launch_gemm_skinny(a, as, w, ws, out, M, N, K, cus, row_scaled, s)
                     : launch_gemm_tiled(a, as, w, ws, out, M, N, K, kernel == 1 ? 1 : kernel - 1,
@@ -258,9 +279,12 @@ fp8q_status run_gemm(const char* fn, const uint8_t* a, const float* as, const ui
 fp8q_status run_gemm_ws(const char* fn, const uint8_t* a, const float* as, const uint8_t* w,
                         const float* ws, uint16_t* out, float* part, uint32_t M, uint32_t N,
                         uint32_t K, hipStream_t s) {
-  const uint32_t splits = splitk_auto(M, N, K);
+  uint32_t cus = 0;
+  const fp8q_status st = check_device(fn, &cus);
+  if (st != FP8Q_OK) return st;
+  const uint32_t splits = splitk_auto(M, N, K, cus);
   if (splits < 2) return run_gemm(fn, a, as, w, ws, out, M, N, K, 0, false, s);
-  return launched(fn, launch_splitk_128(a, as, w, ws, out, part, M, N, K, splits, s));
+  return launched(fn, launch_splitk_128(a, as, w, ws, out, part, M, N, K, splits, cus, s));
 }
 
 // Shared argument checks of the GEMM entry points.
@@ -309,7 +333,10 @@ fp8q_status run_proj(const char* fn, const uint16_t* x_bf16, const uint8_t* w_e4
   REQUIRE_PTR(act_scale_scratch);
   REQUIRE_PTR(act_scale_km_scratch);
   if (M == 0) return ok();
-  const uint32_t splits = split_k ? splitk_auto(M, N, K) : 1;
+  // the workspace is sized for the current device (as the size query is);
+  // the device itself is checked once the arguments are
+  const uint32_t cus = current_cus();
+  const uint32_t splits = split_k ? splitk_auto(M, N, K, cus) : 1;
   if (splits >= 2) {
     const uint64_t need = splitk_workspace(M, N, splits);
     void* workspace = split_ws;
@@ -318,6 +345,8 @@ fp8q_status run_proj(const char* fn, const uint16_t* x_bf16, const uint8_t* w_e4
       return fail(FP8Q_ERR_SHAPE, "%s: workspace of %llu bytes, %llu needed", fn,
                   (unsigned long long)split_ws_bytes, (unsigned long long)need);
   }
+  st = check_device(fn);
+  if (st != FP8Q_OK) return st;
   if ((uint64_t)M * (K / kGroup) <= kFusedKmajorMaxGroups) {
     // one kernel writes both scale layouts (saves a launch)
     st = run_quant(fn, x_bf16, act_q_scratch, act_scale_scratch, act_scale_km_scratch, M, K, 0,
@@ -332,7 +361,7 @@ fp8q_status run_proj(const char* fn, const uint16_t* x_bf16, const uint8_t* w_e4
   if (splits >= 2)
     return launched(fn, launch_splitk_128(act_q_scratch, act_scale_km_scratch, w_e4m3, w_scale,
                                           out_bf16, static_cast<float*>(split_ws), M, N, K, splits,
-                                          stream));
+                                          cus, stream));
   return run_gemm(fn, act_q_scratch, act_scale_km_scratch, w_e4m3, w_scale, out_bf16, M, N, K, 0,
                   row_scaled, stream);
 }
@@ -358,7 +387,7 @@ struct FfnWorkspace {
 
 uint64_t align256(uint64_t v) { return (v + 255u) & ~uint64_t(255); }
 
-FfnWorkspace ffn_workspace(uint32_t M, uint32_t H, uint32_t I, int variant) {
+FfnWorkspace ffn_workspace(uint32_t M, uint32_t H, uint32_t I, int variant, uint32_t cus) {
   const uint64_t Mp = m_pad16(M);
   FfnWorkspace w;
   uint64_t o = 0;
@@ -374,7 +403,7 @@ FfnWorkspace ffn_workspace(uint32_t M, uint32_t H, uint32_t I, int variant) {
   }
   // split-K partials of the down projection (empty when it does not split;
   // gate and up never split, so that the variants stay bit-identical)
-  const uint64_t part = splitk_workspace(M, H, splitk_auto(M, H, I));
+  const uint64_t part = splitk_workspace(M, H, splitk_auto(M, H, I, cus));
   w.part = part ? o : 0;
   o = align256(o + part);
   w.total = o;
@@ -494,7 +523,14 @@ fp8q_status fp8q_quant_act(const uint16_t* x_bf16, uint8_t* q_e4m3, float* scale
 
 fp8q_status fp8q_quant_act_kmajor(const uint16_t* x_bf16, uint8_t* q_e4m3, float* scale_rm,
                                   float* scale_km, uint32_t M, uint32_t K, hipStream_t stream) {
+  return fp8q_quant_act_kmajor_ex(x_bf16, q_e4m3, scale_rm, scale_km, M, K, 0, stream);
+}
+
+fp8q_status fp8q_quant_act_kmajor_ex(const uint16_t* x_bf16, uint8_t* q_e4m3, float* scale_rm,
+                                     float* scale_km, uint32_t M, uint32_t K, int variant,
+                                     hipStream_t stream) {
   const char* fn = "fp8q_quant_act_kmajor";
+  if (variant < 0 || variant > 2) return fail(FP8Q_ERR_VARIANT, "%s: variant %d out of range", fn, variant);
   fp8q_status st = check_mk(fn, M, K);
   if (st != FP8Q_OK) return st;
   if ((uint64_t)m_pad16(M) * K > kMaxElems) return fail(FP8Q_ERR_SHAPE, "%s: Mp*K exceeds 2^32-1", fn);
@@ -504,7 +540,7 @@ fp8q_status fp8q_quant_act_kmajor(const uint16_t* x_bf16, uint8_t* q_e4m3, float
   if (scale_rm != nullptr && !aligned16(scale_rm))
     return fail(FP8Q_ERR_ALIGN, "%s: scale_rm is not 16-byte aligned", fn);
   if (M == 0) return ok();
-  return run_quant(fn, x_bf16, q_e4m3, scale_rm, scale_km, M, K, 0, stream);
+  return run_quant(fn, x_bf16, q_e4m3, scale_rm, scale_km, M, K, variant, stream);
 }
 
 fp8q_status fp8q_scale_to_kmajor(const float* scale_rm, float* scale_km, uint32_t M, uint32_t K,
@@ -592,14 +628,18 @@ fp8q_status fp8q_dequant_fp8_bf16(const uint8_t* w_e4m3, const float* scale, uin
   return launched(fn, launch_dequant(w_e4m3, scale, dst_bf16, N, K, per_row != 0, stream));
 }
 
+uint32_t fp8q_gemm_splitk_select_cus(uint32_t M, uint32_t N, uint32_t K, uint32_t cu_count) {
+  if (N == 0 || N % kGroup != 0 || K == 0 || K % kGroup != 0 || cu_count == 0) return 0;
+  return splitk_auto(M, N, K, cu_count);
+}
+
 uint32_t fp8q_gemm_splitk_select(uint32_t M, uint32_t N, uint32_t K) {
-  if (N == 0 || N % kGroup != 0 || K == 0 || K % kGroup != 0) return 0;
-  return splitk_auto(M, N, K);
+  return fp8q_gemm_splitk_select_cus(M, N, K, current_cus());
 }
 
 size_t fp8q_gemm_splitk_workspace_bytes(uint32_t M, uint32_t N, uint32_t K, uint32_t splits) {
   if (N % kGroup != 0 || K == 0 || K % kGroup != 0 || splits > K / kGroup) return 0;
-  if (splits == 0) splits = splitk_auto(M, N, K);
+  if (splits == 0) splits = splitk_auto(M, N, K, current_cus());
   return (size_t)splitk_workspace(M, N, splits);
 }
 
@@ -616,7 +656,8 @@ fp8q_status fp8q_gemm_blockscaled_splitk(const uint8_t* a_e4m3, const float* a_s
     return fail(FP8Q_ERR_VARIANT, "%s: splits=%u (0 = auto, else 2..min(K/128, %u))", fn, splits,
                 kSplitMaxUser);
   if (M == 0) return ok();
-  if (splits == 0) splits = splitk_auto(M, N, K);
+  const uint32_t cus = current_cus();  // as fp8q_gemm_splitk_workspace_bytes sizes it
+  if (splits == 0) splits = splitk_auto(M, N, K, cus);
   if (splits >= 2) {
     const uint64_t need = splitk_workspace(M, N, splits);
     REQUIRE_PTR(workspace);
@@ -629,12 +670,17 @@ fp8q_status fp8q_gemm_blockscaled_splitk(const uint8_t* a_e4m3, const float* a_s
   if (splits < 2)
     return run_gemm(fn, a_e4m3, a_scale_km, w_e4m3, w_scale, out_bf16, M, N, K, 0, false, stream);
   return launched(fn, launch_splitk_128(a_e4m3, a_scale_km, w_e4m3, w_scale, out_bf16,
-                                        static_cast<float*>(workspace), M, N, K, splits, stream));
+                                        static_cast<float*>(workspace), M, N, K, splits, cus,
+                                        stream));
+}
+
+int fp8q_gemm_select_cus(uint32_t M, uint32_t N, uint32_t K, uint32_t cu_count) {
+  if (N == 0 || N % kGroup != 0 || K == 0 || K % kGroup != 0 || cu_count == 0) return -1;
+  return gemm_auto_kernel(M, N, cu_count);
 }
 
 int fp8q_gemm_select(uint32_t M, uint32_t N, uint32_t K) {
-  if (N == 0 || N % kGroup != 0 || K == 0 || K % kGroup != 0) return -1;
-  return gemm_auto_kernel(M, N);
+  return fp8q_gemm_select_cus(M, N, K, current_cus());
 }
 
 fp8q_status fp8q_gemm_blockscaled(const uint8_t* a_e4m3, const float* a_scale_km,
@@ -721,7 +767,7 @@ int fp8q_ffn_select(uint32_t M, uint32_t H, uint32_t I) {
 size_t fp8q_ffn_workspace_bytes(uint32_t M, uint32_t H, uint32_t I, int variant) {
   if (variant < 0 || variant > 2 || H % kGroup != 0 || I % kGroup != 0) return 0;
   if (variant == 0) variant = ffn_auto_variant(M);
-  return (size_t)ffn_workspace(M, H, I, variant).total;
+  return (size_t)ffn_workspace(M, H, I, variant, current_cus()).total;
 }
 
 fp8q_status fp8q_ffn(const uint16_t* x_bf16, const uint8_t* w_gate, const float* w_gate_scale,
@@ -744,7 +790,8 @@ fp8q_status fp8q_ffn(const uint16_t* x_bf16, const uint8_t* w_gate, const float*
   if (M == 0) return ok();
   REQUIRE_PTR(workspace);
   if (variant == 0) variant = ffn_auto_variant(M);
-  const FfnWorkspace w = ffn_workspace(M, H, I, variant);
+  // sized for the current device, as fp8q_ffn_workspace_bytes sizes it
+  const FfnWorkspace w = ffn_workspace(M, H, I, variant, current_cus());
   if (workspace_bytes < w.total)
     return fail(FP8Q_ERR_SHAPE, "%s: workspace of %llu bytes, %llu needed", fn,
                 (unsigned long long)workspace_bytes, (unsigned long long)w.total);

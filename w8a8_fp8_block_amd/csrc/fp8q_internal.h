@@ -32,12 +32,14 @@ constexpr uint32_t kQuantMinWgPerCu = 2;
 // more than 0.1 us and was 3-15% slower wherever its grid fills the device.
 constexpr bool kQuantBRequestedByDefault = false;
 
+// Quantizer variants A and B: codes q [M,K], row-major scales scale_rm
+// [M,K/128] (may be NULL) and, when scale_km is not NULL, the K-major scales
+// [K/128, ceil16(M)] as well; the groups of the last token row then also
+// write +0.0 to the pad slots M .. ceil16(M)-1 of their column.
 hipError_t launch_quant_a(const uint16_t* x, uint8_t* q, float* scale_rm,
                           float* scale_km, uint32_t M, uint32_t K, hipStream_t s);
 hipError_t launch_quant_b(const uint16_t* x, uint8_t* q, float* scale_rm,
                           float* scale_km, uint32_t M, uint32_t K, hipStream_t s);
-// K-major pad slots m in [M, ceil16(M)) of scale_km are written by this
-// launcher when the quantizer writes scale_km directly.
 
 hipError_t launch_relayout(const float* scale_rm, float* scale_km, uint32_t M,
                            uint32_t K, hipStream_t s);
@@ -55,10 +57,12 @@ hipError_t launch_gemm_tiled(const uint8_t* a, const float* a_s_km, const uint8_
 // Split-K form of the 128x128 tiled kernel (block-scaled weights): splits
 // workgroups per tile, each over a contiguous range of K blocks, write fp32
 // partial tiles to part [splits, M, N]; a reduction adds them in split order
-// into out.  2 <= splits <= K/128.
+// into out.  2 <= splits <= K/128; cus = the device's compute units (a grid
+// of at most one workgroup per CU takes the three-stage form).
 hipError_t launch_splitk_128(const uint8_t* a, const float* a_s_km, const uint8_t* w,
                              const float* w_s, uint16_t* out, float* part, uint32_t M,
-                             uint32_t N, uint32_t K, uint32_t splits, hipStream_t s);
+                             uint32_t N, uint32_t K, uint32_t splits, uint32_t cus,
+                             hipStream_t s);
 hipError_t launch_gemm_skinny(const uint8_t* a, const float* a_s_km, const uint8_t* w,
                               const float* w_s, uint16_t* out, uint32_t M, uint32_t N,
                               uint32_t K, uint32_t cu_count, bool row_scaled, hipStream_t s);

@@ -370,20 +370,19 @@ hipError_t launch_splitk_cfg(const uint8_t* a, const float* a_s_km, const uint8_
   return hipGetLastError();
 }
 
-// Split grids that fit one workgroup per CU (kSplitOneRoundWgs) take three
-// LDS stages (99 KB: one workgroup per CU, two blocks of loads in flight);
-// larger ones two (two workgroups per CU).  Measured with cold caches at
-// N = 5120, K = 17408: 44.2 / 47.8 / 56.5 us against 46.0 / 50.9 / 64.5 us
-// at M = 65 / 128 / 256; at N = 6144, K = 5120: 22.2 / 25.4 / 32.3 against
-// 23.2 / 27.5 / 36.3 us.
-constexpr uint32_t kSplitOneRoundWgs = 256;
-
+// Split grids that fit one workgroup per CU take three LDS stages (99 KB:
+// one workgroup per CU, two blocks of loads in flight); larger ones two (two
+// workgroups per CU).  Measured with cold caches at N = 5120, K = 17408 on
+// 256 CUs: 44.2 / 47.8 / 56.5 us against 46.0 / 50.9 / 64.5 us at M = 65 /
+// 128 / 256; at N = 6144, K = 5120: 22.2 / 25.4 / 32.3 against 23.2 / 27.5 /
+// 36.3 us.
 hipError_t launch_splitk_128_t(const uint8_t* a, const float* a_s_km, const uint8_t* w,
                                const float* w_s, uint16_t* out, float* part, uint32_t M,
-                               uint32_t N, uint32_t K, uint32_t splits, hipStream_t s) {
+                               uint32_t N, uint32_t K, uint32_t splits, uint32_t cus,
+                               hipStream_t s) {
   if (N % 128 != 0 || splits < 2 || splits > K / kGroup) return hipErrorInvalidValue;
   const uint64_t wgs = (uint64_t)((M + 127) / 128) * (N / 128) * splits;
-  hipError_t e = wgs <= kSplitOneRoundWgs
+  hipError_t e = wgs <= cus
                      ? launch_splitk_cfg<3>(a, a_s_km, w, w_s, part, M, N, K, splits, s)
                      : launch_splitk_cfg<2>(a, a_s_km, w, w_s, part, M, N, K, splits, s);
   if (e != hipSuccess) return e;
@@ -1067,8 +1066,9 @@ hipError_t launch_ffn_gate_up(const uint8_t* x, const float* x_s_km, const uint8
 
 hipError_t launch_splitk_128(const uint8_t* a, const float* a_s_km, const uint8_t* w,
                              const float* w_s, uint16_t* out, float* part, uint32_t M,
-                             uint32_t N, uint32_t K, uint32_t splits, hipStream_t s) {
-  return launch_splitk_128_t(a, a_s_km, w, w_s, out, part, M, N, K, splits, s);
+                             uint32_t N, uint32_t K, uint32_t splits, uint32_t cus,
+                             hipStream_t s) {
+  return launch_splitk_128_t(a, a_s_km, w, w_s, out, part, M, N, K, splits, cus, s);
 }
 
 }  // namespace fp8q
