@@ -281,6 +281,34 @@ uint32_t fp8q_gemm_splitk_select(uint32_t M, uint32_t N, uint32_t K);
  * for no split or for an invalid shape or count.  Host function. */
 size_t fp8q_gemm_splitk_workspace_bytes(uint32_t M, uint32_t N, uint32_t K, uint32_t splits);
 
+/* Bytes of static device scratch behind fp8q_gemm_blockscaled_splitk_noalloc
+ * (per GPU, held until the process ends): 32 MiB. */
+#define FP8Q_NOALLOC_SCRATCH_BYTES (32u << 20)
+
+/* fp8q_gemm_blockscaled_splitk for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation): the same operation, kernels, split choice, results
+ * (bit-identical to fp8q_gemm_blockscaled_splitk with the same splits) and
+ * errors, with the split-K partials kept in a static device array of
+ * FP8Q_NOALLOC_SCRATCH_BYTES instead of a caller workspace.  No entry
+ * point allocates; this one takes no workspace either.
+ *   splits  0 = automatic (fp8q_gemm_splitk_select; when it gives 1 the
+ *           single-pass automatic kernel runs and the scratch is not
+ *           touched), else 2 <= splits <= min(K/128, 64)
+ * splits * M * N * 4 > FP8Q_NOALLOC_SCRATCH_BYTES -> FP8Q_ERR_SHAPE, before
+ * anything is enqueued.  The first call on a device looks the array's
+ * device address up (hipGetSymbolAddress) and keeps it.  All calls on one
+ * GPU share its array: calls that may overlap on one GPU (different
+ * streams, or graphs replayed concurrently) race and give undefined
+ * results; calls in order on one stream are safe.  No scratch contents
+ * need to start at zero (every partial read is written first). */
+fp8q_status fp8q_gemm_blockscaled_splitk_noalloc(const uint8_t *a_e4m3,
+                                                 const float *a_scale_km,
+                                                 const uint8_t *w_e4m3,
+                                                 const float *w_scale, uint16_t *out_bf16,
+                                                 uint32_t M, uint32_t N, uint32_t K,
+                                                 uint32_t splits, hipStream_t stream);
+
 /* Per-row FP8 weights (the pages' other weight format, dispatch_proj.rs,
  * dequant_fp8_bf16_into: WeightQuantFormat::Fp8PerRow; the scale index
  * formula scale[(n/block_n)*sk + k/block_k] with block_n = 1, block_k = K,

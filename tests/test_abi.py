@@ -302,6 +302,24 @@ def test_splitk_validation():
     assert L.fp8q_gemm_blockscaled_splitk(g, g, g, g, g, None, 0, 0, 128, 256, 2, None) == 0
 
 
+def test_splitk_noalloc_validation():
+    """The allocation-free split-K entry point validates like the workspace
+    one and refuses partials past its static scratch before the device is
+    touched (the sizes here assume no device: 256 CUs)."""
+    L = fp8q.lib()
+    g = GOOD
+    assert L.fp8q_gemm_blockscaled_splitk_noalloc(g, g, g, g, g, 4, 100, 256, 2, None) == 2  # N
+    assert L.fp8q_gemm_blockscaled_splitk_noalloc(g, g, g, g, None, 4, 128, 256, 2, None) == 1
+    assert L.fp8q_gemm_blockscaled_splitk_noalloc(g, g, g, g, g, 4, 128, 256, 1, None) == 6
+    assert L.fp8q_gemm_blockscaled_splitk_noalloc(g, g, g, g, g, 4, 128, 256, 3, None) == 6
+    assert L.fp8q_gemm_blockscaled_splitk_noalloc(g, g, g, g, g, 0, 128, 256, 2, None) == 0
+    # 3 * 600 * 5120 * 4 = 36.9 MB of partials > 32 MiB
+    assert L.fp8q_gemm_blockscaled_splitk_noalloc(g, g, g, g, g, 600, 5120, 17408, 3, None) == 2
+    assert "static scratch" in _err()
+    # the largest automatic split that fits: 3 * 512 * 5120 * 4 = 31.5 MB
+    assert 3 * 512 * 5120 * 4 <= fp8q.NOALLOC_SCRATCH_BYTES == 32 << 20
+
+
 def test_splitk_workspace_bytes():
     ws = fp8q.fp8q_gemm_splitk_workspace_bytes
     assert ws(300, 512, 2048, 5) == 5 * 300 * 512 * 4

@@ -75,6 +75,7 @@ _SIGS = {
     "fp8q_gemm_splitk_select": (_U, [_U, _U, _U]),
     "fp8q_gemm_splitk_select_cus": (_U, [_U, _U, _U, _U]),
     "fp8q_gemm_splitk_workspace_bytes": (_SZ, [_U, _U, _U, _U]),
+    "fp8q_gemm_blockscaled_splitk_noalloc": (_I, [_P, _P, _P, _P, _P, _U, _U, _U, _U, _P]),
     "fp8q_proj": (_I, [_P, _P, _P, _P, _P, _P, _P, _U, _U, _U, _P]),
     "fp8q_proj_splitk": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _SZ, _U, _U, _U, _P]),
     "fp8q_gemm_rowscaled": (_I, [_P, _P, _P, _P, _P, _U, _U, _U, _P]),
@@ -213,6 +214,22 @@ def fp8q_gemm_blockscaled_splitk(a, a_scale_km, w, w_scale, out, workspace, spli
     _check(lib().fp8q_gemm_blockscaled_splitk(_ptr(a), _ptr(a_scale_km), _ptr(w), _ptr(w_scale),
                                              _ptr(out), _optr(workspace), nbytes, M, N, K,
                                              splits, _stream(stream)))
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20  # FP8Q_NOALLOC_SCRATCH_BYTES
+
+
+def fp8q_gemm_blockscaled_splitk_noalloc(a, a_scale_km, w, w_scale, out, splits: int = 0,
+                                         stream=None):
+    """fp8q_gemm_blockscaled_splitk with the partials in the library's static
+    device scratch (no workspace; splits * M * N * 4 <= NOALLOC_SCRATCH_BYTES)."""
+    M, K = _dims(a, 2)
+    N, K2 = _dims(w, 2)
+    if K2 != K:
+        raise ValueError("a and w disagree on K")
+    _check(lib().fp8q_gemm_blockscaled_splitk_noalloc(_ptr(a), _ptr(a_scale_km), _ptr(w),
+                                                     _ptr(w_scale), _ptr(out), M, N, K, splits,
+                                                     _stream(stream)))
 
 
 def fp8q_proj(x, w, w_scale, out, act_q, act_scale, act_scale_km, stream=None):

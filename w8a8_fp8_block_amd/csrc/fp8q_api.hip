@@ -14,6 +14,13 @@
 
 using namespace fp8q;
 
+// Device memory of fp8q_gemm_blockscaled_splitk_noalloc's split-K partials,
+// for callers that cannot allocate.  Every GPU the library runs on holds its
+// own copy (until the process ends); in host code the name is a host-side
+// stand-in, and the device address comes from hipGetSymbolAddress.
+static_assert(FP8Q_NOALLOC_SCRATCH_BYTES % 256 == 0, "scratch size");
+static __device__ __align__(256) uint8_t scratch[FP8Q_NOALLOC_SCRATCH_BYTES];
+
 namespace {
 
 thread_local char g_err[256] = "";
@@ -104,6 +111,31 @@ uint32_t current_cus() {
   if (probe_device(dev) == 0) return kDefaultCus;
   const uint32_t c = g_dev_cus[dev].load(std::memory_order_relaxed);
   return c ? c : kDefaultCus;
+}
+
+// Device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept.
+std::atomic<void*> g_scratch[kMaxDev];
+std::mutex g_scratch_mu;
+
+fp8q_status scratch_address(const char* fn, void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev)
+    return fail(FP8Q_ERR_DEVICE, "%s: no current HIP device", fn);
+  void* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch[dev].load(std::memory_order_relaxed);
+    if (p == nullptr) {
+      const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess || p == nullptr)
+        return fail(FP8Q_ERR_DEVICE, "%s: hipGetSymbolAddress(scratch) failed on device %d: %s", fn,
+                    dev, hipGetErrorString(e));
+      g_scratch[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return FP8Q_OK;
 }
 
 fp8q_status launched(const char* fn, hipError_t e) {
@@ -672,6 +704,42 @@ fp8q_status fp8q_gemm_blockscaled_splitk(const uint8_t* a_e4m3, const float* a_s
   return launched(fn, launch_splitk_128(a_e4m3, a_scale_km, w_e4m3, w_scale, out_bf16,
                                         static_cast<float*>(workspace), M, N, K, splits, cus,
                                         stream));
+}
+
+fp8q_status fp8q_gemm_blockscaled_splitk_noalloc(const uint8_t* a_e4m3, const float* a_scale_km,
+                                                 const uint8_t* w_e4m3, const float* w_scale,
+                                                 uint16_t* out_bf16, uint32_t M, uint32_t N,
+                                                 uint32_t K, uint32_t splits, hipStream_t stream) {
+  const char* fn = "fp8q_gemm_blockscaled_splitk_noalloc";
+  fp8q_status st =
+      check_gemm_args(fn, a_e4m3, a_scale_km, w_e4m3, w_scale, "w_scale", out_bf16, M, N, K, 0);
+  if (st != FP8Q_OK) return st;
+  if (splits == 1 || splits > std::min(K / kGroup, kSplitMaxUser))
+    return fail(FP8Q_ERR_VARIANT, "%s: splits=%u (0 = auto, else 2..min(K/128, %u))", fn, splits,
+                kSplitMaxUser);
+  if (M == 0) return ok();
+  const uint32_t cus = current_cus();
+  if (splits == 0) splits = splitk_auto(M, N, K, cus);
+  if (splits >= 2) {
+    const uint64_t need = splitk_workspace(M, N, splits);
+    if (need > FP8Q_NOALLOC_SCRATCH_BYTES)
+      return fail(FP8Q_ERR_SHAPE,
+                  "%s: %u splits of M=%u x N=%u need %llu bytes of partials, more than the %llu "
+                  "bytes of static scratch",
+                  fn, splits, M, N, (unsigned long long)need,
+                  (unsigned long long)FP8Q_NOALLOC_SCRATCH_BYTES);
+  }
+  st = check_device(fn);
+  if (st != FP8Q_OK) return st;
+  if (splits < 2)
+    return run_gemm(fn, a_e4m3, a_scale_km, w_e4m3, w_scale, out_bf16, M, N, K, 0, false, stream);
+  // every partial slot the reduction reads is written by the split kernel of
+  // the same call: nothing in the scratch has to start at zero
+  void* part = nullptr;
+  st = scratch_address(fn, &part);
+  if (st != FP8Q_OK) return st;
+  return launched(fn, launch_splitk_128(a_e4m3, a_scale_km, w_e4m3, w_scale, out_bf16,
+                                        static_cast<float*>(part), M, N, K, splits, cus, stream));
 }
 
 int fp8q_gemm_select_cus(uint32_t M, uint32_t N, uint32_t K, uint32_t cu_count) {
