@@ -5,9 +5,9 @@
 
 One step = one pass of the whole projection over one batch of synthetic
 input, already resident in HBM: activation quantizer -> scale relayout ->
-block-scaled FP8 GEMM (the calls fp8q_proj makes, issued separately so the
-GEMM can be bracketed by events; for small batches the quantizer writes the
-K-major scales itself, as fp8q_proj does).
+block-scaled FP8 GEMM (the calls fp8q_proj makes, issued separately so that
+each kernel can be bracketed by events; for small batches the quantizer
+writes the K-major scales itself, as fp8q_proj does).
 
 Default workload: the large prefill projection M=4576, K=17408, N=5120,
 Laplace(0,1) activations with 0.5% outlier channels x50, weights N(0,0.02)
@@ -15,15 +15,26 @@ quantized per 128x128 block.  Prints ONE JSON line:
 
   value           whole-step TFLOP/s = 2*M*N*K / step time
   roofline        the GEMM (dominant kernel) against the dense FP8 MFMA peak
-                  (HBM peak for the skinny decode kernel), duration from HIP
-                  events around each GEMM launch of the timed steps; also
-                  R back-to-back launches between two events (no host gaps)
-  act_quant       the quantizer's GB/s (algorithmic bytes) against HBM peak
+                  (HBM peak for the weight-streaming skinny kernel): duration
+                  from HIP events around each GEMM launch of the timed steps;
+                  also R back-to-back launches between two events cycling
+                  through weight copies of >= 600 MB (streamed from HBM, not
+                  the 256 MB last-level cache), with the shader clock then
+  act_quant       the quantizer's GB/s (algorithmic bytes) against HBM peak,
+                  the same two ways
+  clock           sustained shader clock over the timed steps, per XCD, from
+                  clock stamps (fp8q_clock_stamp) before and after
   cpu_baseline    the CPU oracle on a bounded sample of the same workload
   bf16_comparator the same GEMM in bf16 over the dequantized weights (our
                   bf16 MFMA kernel and hipBLASLt), and the FP8 speedup
   fp8_library_comparator  hipBLASLt's FP8 GEMM (torch._scaled_mm) on the same
                   codes with per-tensor / per-row scales, for context
+  configs         the other workloads, each with its own step time, roofline,
+                  act_quant, clock and oracle baseline: tiny (M=16, K=512,
+                  N=256), decode_M16/17/25 (K=5120, N=6144), prefill
+                  (M=1168, K=5120, N=17408) and quant_sweep (the 15
+                  act-quant + scale-relayout shapes, M in {16, 25, 1168,
+                  4576, 16384} x K in {5120, 6144, 17408})
 
 Other modes (one JSON line each, not the benchmark line): --quant-sweep,
 --dequant, --ffn <workload> (the dense FFN chain), --ffn-sweep (its
@@ -81,6 +92,8 @@ def parse():
                    choices=["tiny", "decode", "prefill", "large_prefill"])
     p.add_argument("--M", type=int, default=None, help="row count for the decode sweep")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--only-workload", action="store_true",
+                   help="time only --workload (skip the other configurations in the line)")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="approximate CPU time budget of the oracle sample")
     p.add_argument("--weights", default="block", choices=["block", "row"],
@@ -477,6 +490,14 @@ def quantize_weights_gpu(wf, per_row=False):
     return codes, ws.contiguous()
 
 
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            return next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), None)
+    except OSError:
+        return None
+
+
 def cpu_baseline(w, x_bits, wf, budget_s, per_row=False):
     """Time the oracle (quantizer + relayout + fp64 GEMM) on the first R rows."""
     import oracle
@@ -493,9 +514,9 @@ def cpu_baseline(w, x_bits, wf, budget_s, per_row=False):
         t1 = time.perf_counter()
         oracle.gemm_ref(a, a_s, wq, ws)
         return t1 - t0, time.perf_counter() - t1
-    t2 = sum(run(2))
+    t2 = sum(run(min(2, w.M)))
     R = int(max(2, min(w.M, 2 * budget_s / max(t2, 1e-6))))
-    R = max(2, min(R, w.M))
+    R = max(1, min(R, w.M))
     tq, tg = run(R)
     t = tq + tg
     # the quantizer and relayout on one thread as well (OpenMP runtime of the oracle)
@@ -514,12 +535,6 @@ def cpu_baseline(w, x_bits, wf, budget_s, per_row=False):
             gomp.omp_set_num_threads(threads)
     except OSError:
         pass
-    model = None
-    try:
-        with open("/proc/cpuinfo") as f:
-            model = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), None)
-    except OSError:
-        pass
     flops = 2.0 * R * w.N * w.K
     return {
         "value": round(flops / t / 1e12, 6),
@@ -527,12 +542,386 @@ def cpu_baseline(w, x_bits, wf, budget_s, per_row=False):
         "cores": threads,
         "kind": "oracle",
         "sample": f"first {R} of {w.M} rows of {w.desc}: quantize + relayout + fp64 block GEMM "
-                  f"({t:.1f} s, one run)",
-        "cpu_model": model,
+                  f"({t:.2f} s, one run)",
+        "cpu_model": _cpu_model(),
         "quant_relayout_s": round(tq, 4),
         "gemm_s": round(tg, 3),
         "quant_relayout_1thread_s": None if tq1 is None else round(tq1, 4),
     }
+
+
+def cpu_baseline_quant(w, x_bits, budget_s):
+    """Time the oracle's quantizer + relayout on the first R rows (R sized to
+    about budget_s), as GB/s of the quantizer's and relayout's algorithmic
+    bytes."""
+    import oracle
+    oracle._load()
+    G = w.K // 128
+
+    def run(R):
+        xs = np.ascontiguousarray(x_bits[:R])
+        t0 = time.perf_counter()
+        _, a_s = oracle.quant_act(xs)
+        oracle.scale_to_kmajor(a_s)
+        return time.perf_counter() - t0
+    t1 = run(1)
+    R = max(1, min(w.M, int(budget_s / max(t1, 1e-6))))
+    t = run(R)
+    nbytes = quant_bytes(R, w.K) + 4 * R * G + 4 * m_pad(R) * G
+    return {"value": round(nbytes / t / 1e9, 3), "unit": "GB/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"first {R} of {w.M} rows of {w.desc}: quantize + relayout ({t:.3f} s, one run)",
+            "cpu_model": _cpu_model()}
+
+
+def m_pad(m):
+    return (m + 15) // 16 * 16
+
+
+def quant_bytes(M, K):
+    """Algorithmic bytes of the quantizer: 2 read + 1 written per element and
+    one fp32 scale per 128-group."""
+    return 3 * M * K + 4 * M * (K // 128)
+
+
+def gemm_stream_bytes(M, N, K):
+    """Algorithmic bytes of the GEMM: weights, activation codes, output and
+    both scale arrays (the roofline of the weight-streaming decode widths)."""
+    G = K // 128
+    return N * K + M * K + 2 * M * N + 4 * (N // 128) * G + 4 * m_pad(M) * G
+
+
+def _rotation(t, target_bytes=600 << 20, cap=64):
+    """t and copies of it, at least 2 and at most cap, together at least
+    target_bytes where the cap allows: back-to-back launches that cycle
+    through them stream from HBM, not from the 256 MB last-level cache."""
+    nb = max(1, t.numel() * t.element_size())
+    n = int(max(2, min(cap, -(-target_bytes // nb))))
+    return [t] + [t.clone() for _ in range(n - 1)]
+
+
+B2B_METHOD = {"graph": "one HIP graph of R launches (torch.cuda.CUDAGraph), timed replay",
+              "stream": "R launches from the host between two events"}
+
+
+def _b2b_us(fn, R, graph=True):
+    """Mean time per launch of R back-to-back launches fn(i): captured into
+    one HIP graph and replayed between two HIP events, so that no host launch
+    gap sits between the kernels (launches from Python are ~10 us apart,
+    longer than the small kernels); plain launches between two events if the
+    capture fails.  Returns (us, method)."""
+    import torch
+    fn(0)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    if graph:
+        try:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for i in range(R):
+                    fn(i)
+            g.replay()
+            torch.cuda.synchronize()
+            e0.record()
+            g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / R
+            del g
+            return us, "graph"
+        except Exception as ex:  # capture not possible here: plain launches
+            print(f"[bench] graph capture failed ({str(ex).splitlines()[0][:120]}); "
+                  "timing plain launches", file=sys.stderr, flush=True)
+            torch.cuda.synchronize()
+    e0.record()
+    for i in range(R):
+        fn(i)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / R, "stream"
+
+
+class ClockStamps:
+    """Shader clock over a stretch of the stream: a clock stamp before and
+    after (fp8q_clock_stamp, 1024 one-wave workgroups over the 8 XCDs),
+    paired by CU."""
+
+    def __init__(self, fp8q, dev):
+        import torch
+        self.fp8q = fp8q
+        self.buf = [torch.empty((1024, 4), dtype=torch.int64, device=dev) for _ in range(2)]
+
+    def start(self):
+        self.fp8q.fp8q_clock_stamp(self.buf[0])
+
+    def stop(self):
+        self.fp8q.fp8q_clock_stamp(self.buf[1])
+
+    def result(self):
+        per, pairs = self.fp8q.shader_clock_ghz(self.buf[0].cpu().numpy(), self.buf[1].cpu().numpy())
+        if not per:
+            return None
+        return {"shader_ghz": round(float(np.median(list(per.values()))), 3),
+                "per_xcd": {str(k): round(v, 3) for k, v in sorted(per.items())},
+                "cu_pairs": pairs,
+                "method": "s_memtime / s_memrealtime stamps before and after, paired by CU"}
+
+
+def _pct(us):
+    p10, p50, p90 = np.percentile(np.asarray(us), [10, 50, 90])
+    return {"p10_us": round(float(p10), 2), "median_us": round(float(p50), 2),
+            "p90_us": round(float(p90), 2)}
+
+
+def measure_projection(w, steps, warmup, per_row=False, comparators=False, cpu_budget=2.0,
+                       R=20):
+    """One projection workload on the GPU: the whole step (quantizer, relayout
+    or the fused quantizer, GEMM) over `steps` timed steps with HIP events
+    around every kernel, the shader clock over those steps, back-to-back
+    launches of each kernel over rotating input copies, and the oracle on a
+    bounded sample.  Returns (entry dict, extras for the benchmark line)."""
+    import torch
+    import synth
+    import w8a8_fp8_block_amd as fp8q
+    dev = torch.device("cuda:0")
+    props = torch.cuda.get_device_properties(dev)
+    M, K, N = w.M, w.K, w.N
+    G = K // 128
+    print(f"[bench] inputs {w.desc} (seed {w.seed})", file=sys.stderr, flush=True)
+    x_bits, wf, _ = synth.make_inputs(w)
+    x = torch.from_numpy(x_bits.view(np.int16)).to(dev)
+    wq, ws = quantize_weights_gpu(torch.from_numpy(wf).to(dev), per_row)
+    gemm = fp8q.fp8q_gemm_rowscaled if per_row else fp8q.fp8q_gemm_blockscaled
+    act_q, act_s, act_km = fp8q.alloc_proj_scratch(M, K)
+    out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream()
+    variant, _, _ = fp8q.fp8q_quant_select(M, K, props.multi_processor_count)
+    fused = fp8q.fp8q_proj_quant_fused(M, K)  # the same choice fp8q_proj makes
+    clock = ClockStamps(fp8q, dev)
+
+    def step(ev=None):
+        if ev: ev[0].record(stream)
+        if fused:
+            fp8q.fp8q_quant_act_kmajor(x, act_q, act_s, act_km)
+        else:
+            fp8q.fp8q_quant_act(x, act_q, act_s)
+        if ev: ev[1].record(stream)
+        if not fused:
+            fp8q.fp8q_scale_to_kmajor(act_s, act_km)
+        if ev: ev[2].record(stream)
+        gemm(act_q, act_km, wq, ws, out)
+        if ev: ev[3].record(stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    print(f"[bench] timing {steps} steps of {w.desc}", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    clock.start()
+    t_start.record(stream)
+    for i in range(steps):
+        step(evs[i])
+    t_end.record(stream)
+    clock.stop()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    gpu_ms = t_start.elapsed_time(t_end)
+    ms_per_step = max(gpu_ms, wall * 1e3) / steps
+    quant_us = np.array([e[0].elapsed_time(e[1]) for e in evs]) * 1e3
+    relay_us = np.array([e[1].elapsed_time(e[2]) for e in evs]) * 1e3
+    gemm_us = np.array([e[2].elapsed_time(e[3]) for e in evs]) * 1e3
+    step_clock = clock.result()
+    # the same step captured R times into one HIP graph (no host launch gaps)
+    step_graph_us, step_graph_how = _b2b_us(lambda i: step(), R)
+
+    # back-to-back launches of each kernel, cycling through input copies
+    w_rot = _rotation(wq)
+    gclock = ClockStamps(fp8q, dev)
+    gclock.start()
+    gemm_b2b, b2b_how = _b2b_us(lambda i: gemm(act_q, act_km, w_rot[i % len(w_rot)], ws, out), R)
+    gclock.stop()
+    torch.cuda.synchronize()
+    gemm_b2b_clock = gclock.result()
+    del w_rot
+    x_rot = _rotation(x)
+    if fused:
+        quant_b2b, _ = _b2b_us(lambda i: fp8q.fp8q_quant_act_kmajor(x_rot[i % len(x_rot)], act_q,
+                                                                   act_s, act_km), R)
+        relay_b2b = None
+    else:
+        quant_b2b, _ = _b2b_us(lambda i: fp8q.fp8q_quant_act(x_rot[i % len(x_rot)], act_q, act_s), R)
+        relay_b2b, _ = _b2b_us(lambda i: fp8q.fp8q_scale_to_kmajor(act_s, act_km), R)
+    del x_rot
+
+    flops = 2.0 * M * N * K
+    kern = fp8q.fp8q_gemm_select(M, N, K)
+    gemm_avg = float(np.mean(gemm_us))
+    if kern == 2:
+        # decode and small widths: the GEMM streams the weight matrix (HBM-bound)
+        gbytes = gemm_stream_bytes(M, N, K)
+        roofline = {"bound": "hbm", "kernel": fp8q.GEMM_KERNEL_NAMES[kern],
+                    "achieved": round(gbytes / gemm_avg / 1e3, 1), "peak": HBM_PEAK_GBS,
+                    "unit": "GB/s", "frac": round(gbytes / gemm_avg / 1e3 / HBM_PEAK_GBS, 4),
+                    "traffic": None, "avg_launch_us": round(gemm_avg, 2), **_pct(gemm_us),
+                    "back_to_back_us": round(gemm_b2b, 2),
+                    "back_to_back_achieved": round(gbytes / gemm_b2b / 1e3, 1),
+                    "back_to_back_frac": round(gbytes / gemm_b2b / 1e3 / HBM_PEAK_GBS, 4),
+                    "algorithmic_bytes_per_launch": gbytes}
+    else:
+        roofline = {"bound": "mfma", "kernel": fp8q.GEMM_KERNEL_NAMES[kern],
+                    "achieved": round(flops / gemm_avg / 1e6, 2), "peak": FP8_PEAK_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(flops / gemm_avg / 1e6 / FP8_PEAK_TFLOPS, 4),
+                    "traffic": (gemm_traffic() if w.name == "large_prefill" and not per_row
+                                else None),
+                    "avg_launch_us": round(gemm_avg, 2), **_pct(gemm_us),
+                    "back_to_back_us": round(gemm_b2b, 2),
+                    "back_to_back_achieved": round(flops / gemm_b2b / 1e6, 2),
+                    "back_to_back_frac": round(flops / gemm_b2b / 1e6 / FP8_PEAK_TFLOPS, 4),
+                    "algorithmic_flops_per_launch": flops}
+    roofline["back_to_back_method"] = B2B_METHOD[b2b_how]
+    if gemm_b2b_clock:
+        roofline["back_to_back_shader_ghz"] = gemm_b2b_clock["shader_ghz"]
+    qb = quant_bytes(M, K) + (4 * m_pad(M) * G if fused else 0)
+    qavg = float(np.mean(quant_us))
+    act_quant = {"kernel": "quant_a_kernel (K-major scales too)" if fused else "quant_a_kernel",
+                 "achieved": round(qb / qavg / 1e3, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                 "frac": round(qb / qavg / 1e3 / HBM_PEAK_GBS, 4),
+                 "avg_launch_us": round(qavg, 2), **_pct(quant_us),
+                 "back_to_back_us": round(quant_b2b, 2),
+                 "back_to_back_achieved": round(qb / quant_b2b / 1e3, 1),
+                 "back_to_back_frac": round(qb / quant_b2b / 1e3 / HBM_PEAK_GBS, 4),
+                 "algorithmic_bytes_per_launch": qb}
+    entry = {
+        "workload": f"{w.name} M={M} K={K} N={N}",
+        "ms_per_step": round(ms_per_step, 5),
+        "tflops": round(flops / (ms_per_step * 1e-3) / 1e12, 3),
+        "step_graph_us": round(step_graph_us, 2),
+        "step_graph_tflops": round(flops / step_graph_us / 1e6, 2),
+        "step_graph_method": B2B_METHOD[step_graph_how],
+        "step": ("act-quant writing both scale layouts" if fused else
+                 "act-quant + scale relayout") +
+                (" + per-row-scaled FP8 GEMM" if per_row else " + block-scaled FP8 GEMM"),
+        "quant_variant": "B" if variant == 2 else "A",
+        "roofline": roofline,
+        "act_quant": act_quant,
+        "clock": step_clock,
+    }
+    if not fused:
+        rb = 4 * M * G + 4 * m_pad(M) * G
+        entry["relayout"] = {"kernel": "relayout_kernel", "avg_launch_us": round(float(np.mean(relay_us)), 2),
+                             "back_to_back_us": round(relay_b2b, 2),
+                             "back_to_back_GBs": round(rb / relay_b2b / 1e3, 1),
+                             "algorithmic_bytes_per_launch": rb}
+
+    extras = {}
+    if comparators:
+        extras = _comparators(fp8q, dev, stream, x, act_q, wq, ws, per_row, M, N, K, gemm_b2b, R)
+    del x, wq, ws, act_q, act_s, act_km, out
+    torch.cuda.empty_cache()
+    if cpu_budget:
+        print(f"[bench] cpu baseline (oracle) {w.desc}", file=sys.stderr, flush=True)
+        entry["cpu_baseline"] = cpu_baseline(w, x_bits, wf, cpu_budget, per_row)
+    return entry, extras
+
+
+def _comparators(fp8q, dev, stream, x, act_q, wq, ws, per_row, M, N, K, gemm_b2b_us, R):
+    """bf16 comparator (our bf16 MFMA kernel and hipBLASLt) on the weights
+    dequantized once by fp8q_dequant_fp8_bf16, and, for context, hipBLASLt's
+    FP8 GEMM with per-tensor / per-row scales; back-to-back launches."""
+    import torch
+    flops = 2.0 * M * N * K
+    wd = torch.empty((N, K), dtype=torch.bfloat16, device=dev)
+    fp8q.fp8q_dequant_fp8_bf16(wq, ws, wd, per_row)
+    xb = x.view(torch.bfloat16)
+    outb = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    wds = [wd, wd.clone()]
+    bf16_own_us, _ = _b2b_us(lambda i: fp8q.fp8q_gemm_bf16(xb, wds[i % 2], outb), R)
+    wts = [t.t().contiguous() for t in wds]  # [K,N] for a plain (non-batched) mm
+    del wds
+    bf16_lib_us, _ = _b2b_us(lambda i: torch.mm(xb, wts[i % 2], out=outb), R, graph=False)
+    del wts, wd
+    fp8_lib = {}
+    if not per_row and hasattr(torch, "_scaled_mm"):
+        a8 = act_q.view(torch.float8_e4m3fn)
+        w8s = [wq.view(torch.float8_e4m3fn), wq.clone().view(torch.float8_e4m3fn)]
+        one = torch.ones((), dtype=torch.float32, device=dev)
+        modes = {"per_tensor": (one, one),
+                 "rowwise": (torch.ones((M, 1), dtype=torch.float32, device=dev),
+                             torch.ones((1, N), dtype=torch.float32, device=dev))}
+        for name, (sa, sb) in modes.items():
+            try:
+                us, _ = _b2b_us(lambda i: torch._scaled_mm(a8, w8s[i % 2].t(), scale_a=sa, scale_b=sb,
+                                                           out_dtype=torch.bfloat16), R, graph=False)
+                fp8_lib[name] = {"us": round(us, 2), "tflops": round(flops / us / 1e6, 1)}
+            except Exception as ex:  # not offered on this build / device
+                fp8_lib[name] = {"error": str(ex).splitlines()[0][:160]}
+        del w8s
+    del outb
+    return {
+        "bf16_comparator": {
+            "what": "the same projection's GEMM in bf16 over the dequantized weights, "
+                    "back-to-back launches",
+            "own_bf16_us": round(bf16_own_us, 2),
+            "own_bf16_tflops": round(flops / bf16_own_us / 1e6, 1),
+            "hipblaslt_bf16_us": round(bf16_lib_us, 2),
+            "hipblaslt_bf16_tflops": round(flops / bf16_lib_us / 1e6, 1),
+            "fp8_back_to_back_us": round(gemm_b2b_us, 2),
+            "fp8_over_own_bf16": round(bf16_own_us / gemm_b2b_us, 3),
+            "fp8_over_hipblaslt_bf16": round(bf16_lib_us / gemm_b2b_us, 3),
+            "bf16_peak_tflops": BF16_PEAK_TFLOPS,
+        },
+        "fp8_library_comparator": {
+            "what": "hipBLASLt FP8 GEMM via torch._scaled_mm on the same code bytes with "
+                    "per-tensor or per-row scales (not block scales), back-to-back launches",
+            **fp8_lib,
+        },
+    }
+
+
+def measure_quant_shape(w, R=20, cpu_budget=0.3):
+    """The act-quant + scale-relayout step on one quantizer-sweep shape, as
+    fp8q_proj runs it (one kernel writing both scale layouts up to 2^17 scale
+    groups, else the quantizer and the relayout): back-to-back launches over
+    rotating input copies (at least 600 MB where 64 copies reach it), the
+    quantizer's GB/s against the HBM peak, and the oracle on a bounded
+    sample."""
+    import torch
+    import synth
+    import w8a8_fp8_block_amd as fp8q
+    dev = torch.device("cuda:0")
+    M, K = w.M, w.K
+    G = K // 128
+    x_bits, _, _ = synth.make_inputs(w, with_weights=False)
+    x = torch.from_numpy(x_bits.view(np.int16)).to(dev)
+    q, s, km = fp8q.alloc_proj_scratch(M, K)
+    fused = fp8q.fp8q_proj_quant_fused(M, K)
+    x_rot = _rotation(x)
+    if fused:
+        tq, how = _b2b_us(lambda i: fp8q.fp8q_quant_act_kmajor(x_rot[i % len(x_rot)], q, s, km), R)
+        tr = 0.0
+    else:
+        tq, how = _b2b_us(lambda i: fp8q.fp8q_quant_act(x_rot[i % len(x_rot)], q, s), R)
+        tr, _ = _b2b_us(lambda i: fp8q.fp8q_scale_to_kmajor(s, km), R)
+    del x_rot, x, q, s, km
+    qb = quant_bytes(M, K) + (4 * m_pad(M) * G if fused else 0)
+    rb = 4 * M * G + 4 * m_pad(M) * G
+    e = {"M": M, "K": K, "path": "fused (both scale layouts)" if fused else "quantizer + relayout",
+         "roofline": {"bound": "hbm", "kernel": "quant_a_kernel", "achieved": round(qb / tq / 1e3, 1),
+                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                      "frac": round(qb / tq / 1e3 / HBM_PEAK_GBS, 4), "traffic": None,
+                      "back_to_back_us": round(tq, 2), "back_to_back_method": B2B_METHOD[how],
+                      "algorithmic_bytes_per_launch": qb},
+         "step_us": round(tq + tr, 2),
+         "step_GBs": round((qb + (rb if not fused else 0)) / (tq + tr) / 1e3, 1)}
+    if not fused:
+        e["relayout_back_to_back_us"] = round(tr, 2)
+    if cpu_budget:
+        e["cpu_baseline"] = cpu_baseline_quant(w, x_bits, cpu_budget)
+    return e
 
 
 def main():
@@ -567,252 +956,71 @@ def main():
 
     import torch
     import synth
-    import w8a8_fp8_block_amd as fp8q
 
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(1)
     dev = torch.device("cuda:0")
     props = torch.cuda.get_device_properties(dev)
-
     w = (synth.workload(args.workload, M=args.M) if args.workload == "decode"
          else synth.workload(args.workload))
-    M, K, N = w.M, w.K, w.N
-    G = K // 128
-    print(f"[bench] inputs {w.desc} (seed {w.seed})", file=sys.stderr, flush=True)
-    x_bits, wf, _ = synth.make_inputs(w)
-    x = torch.from_numpy(x_bits.view(np.int16)).to(dev)
     per_row = args.weights == "row"
-    wq, ws = quantize_weights_gpu(torch.from_numpy(wf).to(dev), per_row)
-    gemm = fp8q.fp8q_gemm_rowscaled if per_row else fp8q.fp8q_gemm_blockscaled
-    act_q, act_s, act_km = fp8q.alloc_proj_scratch(M, K)
-    out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-    stream = torch.cuda.current_stream()
-    variant, grid, why = fp8q.fp8q_quant_select(M, K, props.multi_processor_count)
+    budget = 0 if args.no_cpu_baseline else args.cpu_seconds
+    main_entry, extras = measure_projection(w, args.steps, args.warmup, per_row=per_row,
+                                            comparators=True, cpu_budget=budget)
 
-    fused = fp8q.fp8q_proj_quant_fused(M, K)  # the same choice fp8q_proj makes
+    # the other configurations, each with its own roofline and oracle baseline
+    configs = {}
+    if not args.only_workload:
+        small = 0 if args.no_cpu_baseline else 2.0
+        for name in ("tiny", "decode", "prefill", "large_prefill"):
+            for cw in synth.WORKLOADS[name]:
+                if cw == w:
+                    continue
+                key = name if len(synth.WORKLOADS[name]) == 1 else f"{name}_M{cw.M}"
+                configs[key], _ = measure_projection(cw, args.steps, args.warmup, per_row=per_row,
+                                                     cpu_budget=small)
+        print("[bench] quantizer sweep", file=sys.stderr, flush=True)
+        configs["quant_sweep"] = [
+            measure_quant_shape(qw, cpu_budget=0 if args.no_cpu_baseline else 0.3)
+            for qw in synth.WORKLOADS["quant_sweep"]]
 
-    def step(ev_q=None, ev_g=None):
-        if ev_q: ev_q[0].record(stream)
-        if fused:
-            fp8q.fp8q_quant_act_kmajor(x, act_q, act_s, act_km)
-        else:
-            fp8q.fp8q_quant_act(x, act_q, act_s)
-        if ev_q: ev_q[1].record(stream)
-        if not fused:
-            fp8q.fp8q_scale_to_kmajor(act_s, act_km)
-        if ev_g: ev_g[0].record(stream)
-        gemm(act_q, act_km, wq, ws, out)
-        if ev_g: ev_g[1].record(stream)
-
-    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-
-    evq = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
-    evg = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    t_start.record(stream)
-    for i in range(args.steps):
-        step(evq[i], evg[i])
-    t_end.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-
-    # Back-to-back kernel timings: R launches of one kernel between two events
-    # (no host gaps inside; at decode widths the Python-driven step above is
-    # host-launch-bound and its per-launch events include those gaps).  The
-    # GEMM alternates between two weight copies when they fit, so its weight
-    # stream is not served from the previous launch's cache lines.
-    R = 20
-    w_alt = [wq]
-    if N * K <= (1 << 30):
-        w_alt.append(wq.clone())
-    x_alt = [x, x.clone()] if M * K * 2 <= (1 << 30) else [x]
-    torch.cuda.synchronize()
-    b0, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    b0.record(stream)
-    for i in range(R):
-        gemm(act_q, act_km, w_alt[i % len(w_alt)], ws, out)
-    b1.record(stream)
-    torch.cuda.synchronize()
-    gemm_b2b_us = b0.elapsed_time(b1) * 1e3 / R
-    b0.record(stream)
-    for i in range(R):
-        fp8q.fp8q_quant_act(x_alt[i % len(x_alt)], act_q, act_s)
-    b1.record(stream)
-    torch.cuda.synchronize()
-    quant_b2b_us = b0.elapsed_time(b1) * 1e3 / R
-    del w_alt, x_alt
-
-    # bf16 comparator: the same projection in bf16 over the weights
-    # dequantized once by fp8q_dequant_fp8_bf16 (outside the timing); our bf16
-    # MFMA kernel and, for context, the vendor library through torch.mm
-    # (hipBLASLt), each R back-to-back launches alternating two weight copies
-    wd = torch.empty((N, K), dtype=torch.bfloat16, device=dev)
-    fp8q.fp8q_dequant_fp8_bf16(wq, ws, wd, per_row)
-    xb = x.view(torch.bfloat16)
-    outb = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-    wds = [wd, wd.clone()]
-    torch.cuda.synchronize()
-    b0.record(stream)
-    for i in range(R):
-        fp8q.fp8q_gemm_bf16(xb, wds[i % 2], outb)
-    b1.record(stream)
-    torch.cuda.synchronize()
-    bf16_own_us = b0.elapsed_time(b1) * 1e3 / R
-    wts = [t.t().contiguous() for t in wds]  # [K,N] for a plain (non-batched) mm
-    del wds
-    torch.mm(xb, wts[0], out=outb)
-    torch.cuda.synchronize()
-    b0.record(stream)
-    for i in range(R):
-        torch.mm(xb, wts[i % 2], out=outb)
-    b1.record(stream)
-    torch.cuda.synchronize()
-    bf16_lib_us = b0.elapsed_time(b1) * 1e3 / R
-    del wts, wd
-
-    # FP8 library comparator (context): the vendor library's FP8 GEMM through
-    # torch._scaled_mm on the same code bytes, with the scaling modes it
-    # offers (one scale per tensor; one per activation row and weight row)
-    # instead of 128x128 blocks -- a different, simpler operation
-    fp8_lib = {}
-    if not per_row and hasattr(torch, "_scaled_mm"):
-        a8 = act_q.view(torch.float8_e4m3fn)
-        w8s = [wq.view(torch.float8_e4m3fn), wq.clone().view(torch.float8_e4m3fn)]
-        one = torch.ones((), dtype=torch.float32, device=dev)
-        modes = {"per_tensor": (one, one),
-                 "rowwise": (torch.ones((M, 1), dtype=torch.float32, device=dev),
-                             torch.ones((1, N), dtype=torch.float32, device=dev))}
-        for name, (sa, sb) in modes.items():
-            try:
-                torch._scaled_mm(a8, w8s[0].t(), scale_a=sa, scale_b=sb, out_dtype=torch.bfloat16)
-                torch.cuda.synchronize()
-                b0.record(stream)
-                for i in range(R):
-                    torch._scaled_mm(a8, w8s[i % 2].t(), scale_a=sa, scale_b=sb,
-                                     out_dtype=torch.bfloat16)
-                b1.record(stream)
-                torch.cuda.synchronize()
-                us = b0.elapsed_time(b1) * 1e3 / R
-                fp8_lib[name] = {"us": round(us, 2), "tflops": round(2.0 * M * N * K / us / 1e6, 1)}
-            except Exception as ex:  # not offered on this build / device
-                fp8_lib[name] = {"error": str(ex).splitlines()[0][:160]}
-        del w8s
-    del outb
-
-    gpu_ms = t_start.elapsed_time(t_end)
-    ms_per_step = max(gpu_ms, wall * 1e3) / args.steps
-    gemm_ms = np.array([a.elapsed_time(b) for a, b in evg])
-    quant_ms = np.array([a.elapsed_time(b) for a, b in evq])
+    M, K, N = w.M, w.K, w.N
     flops = 2.0 * M * N * K
-    value = flops / (ms_per_step * 1e-3) / 1e12
-    gemm_avg_s = float(np.mean(gemm_ms)) * 1e-3
-    gemm_tflops = flops / gemm_avg_s / 1e12
-    quant_bytes = M * K * 2 + M * K + M * G * 4
-    quant_avg_s = float(np.mean(quant_ms)) * 1e-3
-    quant_gbs = quant_bytes / quant_avg_s / 1e9
-
-    def pct(ms):  # per-launch event times of the timed steps
-        p10, p50, p90 = np.percentile(np.asarray(ms) * 1e3, [10, 50, 90])
-        return {"p10_us": round(float(p10), 2), "median_us": round(float(p50), 2),
-                "p90_us": round(float(p90), 2)}
-    gemm_pct = pct(gemm_ms)
-
-    kern = fp8q.fp8q_gemm_select(M, N, K)
-    if kern == 2:
-        # decode widths: the GEMM streams the weight matrix once (HBM-bound)
-        gemm_bytes = N * K + M * K + 2 * M * N + 4 * (N // 128) * G + 4 * fp8q.fp8q_m_pad(M) * G
-        gemm_gbs = gemm_bytes / gemm_avg_s / 1e9
-        roofline = {"bound": "hbm", "kernel": fp8q.GEMM_KERNEL_NAMES[kern],
-                    "achieved": round(gemm_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                    "frac": round(gemm_gbs / HBM_PEAK_GBS, 4), "traffic": None,
-                    "avg_launch_us": round(gemm_avg_s * 1e6, 2),
-                    **gemm_pct,
-                    "back_to_back_us": round(gemm_b2b_us, 2),
-                    "back_to_back_achieved": round(gemm_bytes / gemm_b2b_us / 1e3, 1),
-                    "algorithmic_bytes_per_launch": gemm_bytes}
-    else:
-        roofline = {"bound": "mfma", "kernel": fp8q.GEMM_KERNEL_NAMES[kern],
-                    "achieved": round(gemm_tflops, 2), "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
-                    "frac": round(gemm_tflops / FP8_PEAK_TFLOPS, 4),
-                    "traffic": (gemm_traffic() if args.workload == "large_prefill" and not per_row
-                                else None),
-                    "avg_launch_us": round(gemm_avg_s * 1e6, 2),
-                    **gemm_pct,
-                    "back_to_back_us": round(gemm_b2b_us, 2),
-                    "back_to_back_achieved": round(flops / gemm_b2b_us / 1e6, 2),
-                    "algorithmic_flops_per_launch": flops}
-
-    cpu = None
-    if not args.no_cpu_baseline:
-        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
-        cpu = cpu_baseline(w, x_bits, wf, args.cpu_seconds, per_row)
-
     rec = {
         "metric": "block-scaled FP8 proj TFLOP/s (M=4576) + act-quant GB/s vs HBM peak",
-        "value": round(value, 3),
+        "value": main_entry["tflops"],
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 5),
+        "ms_per_step": main_entry["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "fp8_e4m3",
         "data": "synthetic",
         "config": {
-            "workload": f"{w.name} M={M} K={K} N={N}",
+            "workload": main_entry["workload"],
             "M": M, "K": K, "N": N,
             "activations": f"bf16 {w.dist}(0,1), {w.n_outliers} outlier channels x{w.outlier_factor:g}",
             "weights": ("fp8 e4m3 [N,K], fp32 scale per row (from N(0,0.02))" if per_row else
                         "fp8 e4m3 [N,K], fp32 scale per 128x128 block (from N(0,0.02))"),
             "output": "bf16 [M,N]",
-            "step": (("act-quant writing both scale layouts" if fused else
-                      "act-quant + scale relayout") +
-                     (" + per-row-scaled FP8 GEMM" if per_row else " + block-scaled FP8 GEMM")),
-            "quant_variant": "B" if variant == 2 else "A",
+            "step": main_entry["step"],
+            "quant_variant": main_entry["quant_variant"],
             "device": props.name, "gcn_arch": props.gcnArchName,
             "cus": props.multi_processor_count,
         },
-        "roofline": roofline,
-        "act_quant": {
-            "achieved": round(quant_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(quant_gbs / HBM_PEAK_GBS, 4),
-            "avg_launch_us": round(quant_avg_s * 1e6, 2),
-            **pct(quant_ms),
-            "back_to_back_us": round(quant_b2b_us, 2),
-            "back_to_back_achieved": round(quant_bytes / quant_b2b_us / 1e3, 1),
-            "algorithmic_bytes_per_launch": quant_bytes,
-        },
-        "cpu_baseline": cpu,
-        "bf16_comparator": {
-            "what": "the same projection's GEMM in bf16 over the dequantized weights, "
-                    "back-to-back launches",
-            "own_bf16_us": round(bf16_own_us, 2),
-            "own_bf16_tflops": round(flops / bf16_own_us / 1e6, 1),
-            "hipblaslt_bf16_us": round(bf16_lib_us, 2),
-            "hipblaslt_bf16_tflops": round(flops / bf16_lib_us / 1e6, 1),
-            "fp8_back_to_back_us": round(gemm_b2b_us, 2),
-            "fp8_over_own_bf16": round(bf16_own_us / gemm_b2b_us, 3),
-            "fp8_over_hipblaslt_bf16": round(bf16_lib_us / gemm_b2b_us, 3),
-            "bf16_peak_tflops": BF16_PEAK_TFLOPS,
-        },
-        "fp8_library_comparator": {
-            "what": "hipBLASLt FP8 GEMM via torch._scaled_mm on the same code bytes with "
-                    "per-tensor or per-row scales (not block scales), back-to-back launches",
-            **fp8_lib,
-        },
+        "roofline": main_entry["roofline"],
+        "act_quant": main_entry["act_quant"],
+        "cpu_baseline": main_entry.get("cpu_baseline"),
+        "clock": main_entry["clock"],
     }
+    if "relayout" in main_entry:
+        rec["relayout"] = main_entry["relayout"]
+    rec.update(extras)
+    rec["configs"] = configs
     print(json.dumps(rec), flush=True)
 
 

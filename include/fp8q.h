@@ -480,6 +480,21 @@ fp8q_status fp8q_ffn(const uint16_t *x_bf16, const uint8_t *w_gate,
                      size_t workspace_bytes, uint32_t M, uint32_t H, uint32_t I,
                      int variant, hipStream_t stream);
 
+/* ------------------------------------------------- measurement support */
+
+/* Clock stamp, for measuring the sustained shader clock over a region of a
+ * stream (not part of the projection): n one-wave workgroups (1 <= n <=
+ * 1024, dealt round robin to the XCDs) each write four values to
+ * stamps[4*i .. 4*i+3]: the id of the XCD the workgroup ran on, the
+ * hardware id of its wave slot (HW_ID; bits 8-15 name the CU), the shader
+ * clock counter of that CU (s_memtime) and the constant 100 MHz counter
+ * (s_memrealtime).  The shader clock counters of different CUs are not
+ * aligned, so two stamps around a region are paired by (XCD, CU): each pair
+ * gives that XCD's average shader clock d(memtime) / d(memrealtime) *
+ * 100 MHz over the region.
+ *   stamps   device memory of 4*n uint64, 16-byte aligned, written */
+fp8q_status fp8q_clock_stamp(unsigned long long *stamps, uint32_t n, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

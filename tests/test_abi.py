@@ -397,3 +397,18 @@ def test_proj_splitk_validation():
     assert L.fp8q_proj_splitk(g, g, g, g, g, g, g, BAD, need, M, N, K, None) == 3
     assert L.fp8q_proj_splitk(g, g, g, g, g, g, g, g, need, M, N, 100, None) == 2
     assert L.fp8q_proj_splitk(g, g, g, g, g, g, g, None, 0, 0, N, K, None) == 0
+
+
+def test_shader_clock_pairs_stamps_by_cu():
+    """fp8q.shader_clock_ghz pairs the two stamps of the same (XCD, CU) (HW_ID
+    bits 8-15) and takes d(shader counter) / d(100 MHz counter): a CU seen
+    only once is ignored, and an XCD's clock is the median over its CUs."""
+    import numpy as np
+    before = np.array([[0, 0x0100, 1000, 10], [0, 0x0200, 50000, 10], [1, 0x0305, 7, 3],
+                       [2, 0x0100, 0, 0]], dtype=np.int64)
+    after = np.array([[0, 0x0100, 1000 + 1800, 110], [0, 0x0210, 50000 + 2000, 110],
+                      [1, 0x0301, 7 + 2100, 103], [3, 0x0100, 5, 5]], dtype=np.int64)
+    per, pairs = fp8q.shader_clock_ghz(before, after)
+    assert pairs == 3 and set(per) == {0, 1}
+    assert abs(per[1] - 2.1) < 1e-12                   # 2100 ticks in 100 * 10 ns
+    assert abs(per[0] - (1.8 + 2.0) / 2) < 1e-12       # two CUs of XCD 0

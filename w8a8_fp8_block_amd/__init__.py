@@ -76,6 +76,7 @@ _SIGS = {
     "fp8q_gemm_splitk_select_cus": (_U, [_U, _U, _U, _U]),
     "fp8q_gemm_splitk_workspace_bytes": (_SZ, [_U, _U, _U, _U]),
     "fp8q_gemm_blockscaled_splitk_noalloc": (_I, [_P, _P, _P, _P, _P, _U, _U, _U, _U, _P]),
+    "fp8q_clock_stamp": (_I, [_P, _U, _P]),
     "fp8q_proj": (_I, [_P, _P, _P, _P, _P, _P, _P, _U, _U, _U, _P]),
     "fp8q_proj_splitk": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _SZ, _U, _U, _U, _P]),
     "fp8q_gemm_rowscaled": (_I, [_P, _P, _P, _P, _P, _U, _U, _U, _P]),
@@ -383,6 +384,32 @@ def fp8q_quant_b_min_m(K: int, params: SelectParams) -> int:
 def fp8q_quant_log_slot(variant: int, reject, requested: bool) -> int:
     r = None if reject is None else reject.encode()
     return int(lib().fp8q_quant_log_slot(variant, r, int(bool(requested))))
+
+
+def fp8q_clock_stamp(stamps, stream=None):
+    """Clock stamp into stamps (int64 device tensor [n, 4]): per one-wave
+    workgroup {XCD id, HW_ID, shader clock counter, 100 MHz counter}."""
+    n, four = _dims(stamps, 2)
+    if four != 4:
+        raise ValueError("stamps must be [n, 4]")
+    _check(lib().fp8q_clock_stamp(_ptr(stamps), n, _stream(stream)))
+
+
+def shader_clock_ghz(before, after):
+    """Average shader clock per XCD between two clock stamps (host arrays
+    [n, 4] from fp8q_clock_stamp), pairing the stamps of the same CU:
+    ({xcd: median GHz over its CU pairs}, number of pairs)."""
+    first = {}
+    for r in before:
+        first.setdefault((int(r[0]), (int(r[1]) >> 8) & 0xFF), r)
+    per = {}
+    for r in after:
+        b = first.get((int(r[0]), (int(r[1]) >> 8) & 0xFF))
+        if b is None or int(r[3]) <= int(b[3]):
+            continue
+        per.setdefault(int(r[0]), []).append((int(r[2]) - int(b[2])) / (int(r[3]) - int(b[3])) * 0.1)
+    import statistics
+    return {x: statistics.median(v) for x, v in per.items()}, sum(len(v) for v in per.values())
 
 
 # ------------------------------------------------------- allocation helpers

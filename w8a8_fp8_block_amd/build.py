@@ -25,7 +25,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB_PATH = os.path.join(HERE, "libfp8q.so")
 SOURCES = ["fp8q_api.hip", "quant.hip", "relayout.hip", "gemm.hip", "gemm_bf16.hip", "dequant.hip",
-           "ffn.hip"]
+           "ffn.hip", "clock.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

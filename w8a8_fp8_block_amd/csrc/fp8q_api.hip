@@ -706,6 +706,15 @@ fp8q_status fp8q_gemm_blockscaled_splitk(const uint8_t* a_e4m3, const float* a_s
                                         stream));
 }
 
+fp8q_status fp8q_clock_stamp(unsigned long long* stamps, uint32_t n, hipStream_t stream) {
+  const char* fn = "fp8q_clock_stamp";
+  REQUIRE_PTR(stamps);
+  if (n == 0 || n > 1024) return fail(FP8Q_ERR_SHAPE, "%s: n=%u (1..1024 workgroups)", fn, n);
+  const fp8q_status st = check_device(fn);
+  if (st != FP8Q_OK) return st;
+  return launched(fn, launch_clock_stamp(stamps, n, stream));
+}
+
 fp8q_status fp8q_gemm_blockscaled_splitk_noalloc(const uint8_t* a_e4m3, const float* a_scale_km,
                                                  const uint8_t* w_e4m3, const float* w_scale,
                                                  uint16_t* out_bf16, uint32_t M, uint32_t N,

@@ -93,6 +93,10 @@ hipError_t launch_ffn_gate_up(const uint8_t* x, const float* x_s_km, const uint8
                               uint8_t* hq, float* hs_km, uint32_t M, uint32_t H, uint32_t I,
                               hipStream_t s);
 
+// Clock stamps (measurement support): n one-wave workgroups each write
+// {XCD id, HW_ID, shader clock counter, 100 MHz counter} to dst[4*i .. 4*i+3].
+hipError_t launch_clock_stamp(unsigned long long* dst, uint32_t n, hipStream_t s);
+
 inline uint32_t m_pad16(uint32_t m) { return (m + 15u) / 16u * 16u; }
 
 }  // namespace fp8q
