@@ -691,7 +691,25 @@ def measure_projection(w, steps, warmup, per_row=False, comparators=False, cpu_b
     x_bits, wf, _ = synth.make_inputs(w)
     x = torch.from_numpy(x_bits.view(np.int16)).to(dev)
     wq, ws = quantize_weights_gpu(torch.from_numpy(wf).to(dev), per_row)
-    gemm = fp8q.fp8q_gemm_rowscaled if per_row else fp8q.fp8q_gemm_blockscaled
+    # the GEMM with a caller workspace (as fp8q_proj_splitk runs it: stream-K
+    # or split-K where the automatic choice takes them); per-row weight
+    # scales have the single-pass kernels only
+    work = None
+    if per_row:
+        gemm = fp8q.fp8q_gemm_rowscaled
+        gemm_name = fp8q.GEMM_KERNEL_NAMES[fp8q.fp8q_gemm_select(M, N, K)]
+    else:
+        need = fp8q.fp8q_gemm_splitk_workspace_bytes(M, N, K, 0)
+        work = torch.empty((max(need, 16),), dtype=torch.uint8, device=dev)
+
+        def gemm(a_, s_, w_, ws_, o_):
+            fp8q.fp8q_gemm_blockscaled_splitk(a_, s_, w_, ws_, o_, work)
+        if fp8q.fp8q_gemm_streamk_select(M, N, K) == 1:
+            gemm_name = fp8q.STREAMK_KERNEL_NAME
+        elif fp8q.fp8q_gemm_splitk_select(M, N, K) >= 2:
+            gemm_name = "+".join(fp8q.SPLITK_KERNEL_NAMES)
+        else:
+            gemm_name = fp8q.GEMM_KERNEL_NAMES[fp8q.fp8q_gemm_select(M, N, K)]
     act_q, act_s, act_km = fp8q.alloc_proj_scratch(M, K)
     out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
     stream = torch.cuda.current_stream()
@@ -763,7 +781,7 @@ def measure_projection(w, steps, warmup, per_row=False, comparators=False, cpu_b
     if kern == 2:
         # decode and small widths: the GEMM streams the weight matrix (HBM-bound)
         gbytes = gemm_stream_bytes(M, N, K)
-        roofline = {"bound": "hbm", "kernel": fp8q.GEMM_KERNEL_NAMES[kern],
+        roofline = {"bound": "hbm", "kernel": gemm_name,
                     "achieved": round(gbytes / gemm_avg / 1e3, 1), "peak": HBM_PEAK_GBS,
                     "unit": "GB/s", "frac": round(gbytes / gemm_avg / 1e3 / HBM_PEAK_GBS, 4),
                     "traffic": None, "avg_launch_us": round(gemm_avg, 2), **_pct(gemm_us),
@@ -772,7 +790,7 @@ def measure_projection(w, steps, warmup, per_row=False, comparators=False, cpu_b
                     "back_to_back_frac": round(gbytes / gemm_b2b / 1e3 / HBM_PEAK_GBS, 4),
                     "algorithmic_bytes_per_launch": gbytes}
     else:
-        roofline = {"bound": "mfma", "kernel": fp8q.GEMM_KERNEL_NAMES[kern],
+        roofline = {"bound": "mfma", "kernel": gemm_name,
                     "achieved": round(flops / gemm_avg / 1e6, 2), "peak": FP8_PEAK_TFLOPS,
                     "unit": "TFLOP/s", "frac": round(flops / gemm_avg / 1e6 / FP8_PEAK_TFLOPS, 4),
                     "traffic": (gemm_traffic() if w.name == "large_prefill" and not per_row
@@ -804,7 +822,8 @@ def measure_projection(w, steps, warmup, per_row=False, comparators=False, cpu_b
         "step_graph_method": B2B_METHOD[step_graph_how],
         "step": ("act-quant writing both scale layouts" if fused else
                  "act-quant + scale relayout") +
-                (" + per-row-scaled FP8 GEMM" if per_row else " + block-scaled FP8 GEMM"),
+                (" + per-row-scaled FP8 GEMM" if per_row else
+                 " + block-scaled FP8 GEMM (workspace form, automatic choice)"),
         "quant_variant": "B" if variant == 2 else "A",
         "roofline": roofline,
         "act_quant": act_quant,
@@ -820,7 +839,7 @@ def measure_projection(w, steps, warmup, per_row=False, comparators=False, cpu_b
     extras = {}
     if comparators:
         extras = _comparators(fp8q, dev, stream, x, act_q, wq, ws, per_row, M, N, K, gemm_b2b, R)
-    del x, wq, ws, act_q, act_s, act_km, out
+    del x, wq, ws, act_q, act_s, act_km, out, work
     torch.cuda.empty_cache()
     if cpu_budget:
         print(f"[bench] cpu baseline (oracle) {w.desc}", file=sys.stderr, flush=True)

@@ -235,15 +235,19 @@ fp8q_status fp8q_gemm_blockscaled_ex(const uint8_t *a_e4m3, const float *a_scale
                                      uint16_t *out_bf16, uint32_t M, uint32_t N,
                                      uint32_t K, int kernel, hipStream_t stream);
 
-/* Split-K form of fp8q_gemm_blockscaled for row counts whose 128x128 tiles
- * are too few to fill the device (the same operation, same argument
- * conventions and errors): the K blocks are cut into `splits` contiguous
- * ranges, block range s covering [s*(K/128)/splits, (s+1)*(K/128)/splits);
- * each tile's range sums are written in fp32 to the workspace as
- * part[s][M][N], then a second kernel forms out = bf16_rne(part[0] + part[1]
- * + ... + part[splits-1]), added in that order.  Results are reproducible
- * run to run; they differ from the single-pass kernels by the fp32
- * summation order only.
+/* fp8q_gemm_blockscaled with the K blocks shared out over more workgroups
+ * than the output tiles give (the same operation, same argument conventions
+ * and errors), with a caller workspace:
+ *  - split-K, for row counts whose 128x128 tiles are too few to fill the
+ *    device: the K blocks are cut into `splits` contiguous ranges, block
+ *    range s covering [s*(K/128)/splits, (s+1)*(K/128)/splits); each tile's
+ *    range sums are written in fp32 to the workspace as part[s][M][N], then a
+ *    second kernel forms out = bf16_rne(part[0] + part[1] + ... +
+ *    part[splits-1]), added in that order;
+ *  - stream-K (splits = 0 where fp8q_gemm_streamk_select says 1): the form
+ *    of fp8q_gemm_blockscaled_streamk below on one workgroup per CU.
+ * Results are reproducible run to run; they differ from the single-pass
+ * kernels by the fp32 summation order only.
  *   workspace        device memory, 16-byte aligned, at least
  *                    fp8q_gemm_splitk_workspace_bytes(M, N, K, splits) bytes
  *                    (may be NULL when that is 0); contents on entry are
@@ -277,9 +281,65 @@ uint32_t fp8q_gemm_splitk_select_cus(uint32_t M, uint32_t N, uint32_t K, uint32_
 uint32_t fp8q_gemm_splitk_select(uint32_t M, uint32_t N, uint32_t K);
 
 /* Workspace bytes of fp8q_gemm_blockscaled_splitk: splits * M * N * 4 for
- * splits >= 2 (splits = 0: the automatic count on the current device), 0
- * for no split or for an invalid shape or count.  Host function. */
+ * splits >= 2; for splits = 0 the automatic choice on the current device
+ * (stream-K: 64 * CUs rounded up to 256, plus 128 KiB per CU; split-K as
+ * above; 0 for the single-pass kernel); 0 for an invalid shape or count.
+ * Host function. */
 size_t fp8q_gemm_splitk_workspace_bytes(uint32_t M, uint32_t N, uint32_t K, uint32_t splits);
+
+/* 1 if fp8q_gemm_blockscaled_splitk with splits = 0 (and fp8q_proj_splitk)
+ * runs the stream-K form on a device with cu_count compute units: M >= 512
+ * and a stream-K plan exists whose longest workgroup is predicted at least
+ * 10% shorter than the 256x128 kernel's last round (see
+ * fp8q_gemm_blockscaled_streamk; in K-block times, with each partial read
+ * costed at 5 and the flag wait at 8, and a partial last round of Tt tiles
+ * at max(Tt/cu_count, 0.73) of a full one); 0 otherwise; -1 for a bad N, K
+ * or cu_count.  In practice: a last round of few tiles and a long K (M =
+ * 1792, N = 5120, K = 17408 on 256 CUs), not where most CUs have a tile in
+ * the last round.  Pure host function.  fp8q_gemm_streamk_select: for the
+ * current device (256 CUs when none can be queried). */
+int fp8q_gemm_streamk_select_cus(uint32_t M, uint32_t N, uint32_t K, uint32_t cu_count);
+int fp8q_gemm_streamk_select(uint32_t M, uint32_t N, uint32_t K);
+
+/* The block-scaled GEMM (fp8q_gemm_blockscaled: same operation, operand
+ * conventions and errors) in its stream-K form, run wherever a plan exists
+ * (the automatic choice above takes it only where it is predicted to pay).
+ * With T = ceil(M/256) * (N/128) tiles of 256x128, G = K/128 blocks, C =
+ * `workgroups` persistent workgroups (all resident at once, one per CU):
+ * workgroup q computes the whole tiles q, q + C, ... of R = floor(T/C)
+ * rounds; the Tt = T mod C remaining tiles are cut along K into P pieces at
+ * blocks 0 < b_1 < ... < G, workgroup q < Tt computing piece 0 of tail tile
+ * q, the other C - Tt workgroups the later pieces (piece p of tail tile t is
+ * unit (p-1)*Tt + t, taken by the workgroup Tt + (unit mod (C - Tt)) in round
+ * unit / (C - Tt)).  With Tt > C/2, P = 2 and b_1 balances piece 0 against
+ * the rounds of second pieces; else P <= min(C/Tt, G, 16) near-equal pieces.
+ * Each later piece's fp32 partial goes to the workspace with a flag holding
+ * the call's generation number; the piece-0 workgroup waits for the flags,
+ * adds the partials in piece order and stores the bf16 tile, then clears
+ * the flags (so a captured launch replays correctly).  A wait gives up after
+ * a bounded number of polls and stores NaN.  Results are reproducible run
+ * to run and differ from fp8q_gemm_blockscaled only in the fp32 summation
+ * order of the K blocks.
+ *   workspace        device memory, 16-byte aligned, at least
+ *                    fp8q_gemm_streamk_workspace_bytes(workgroups) bytes;
+ *                    contents on entry ignored, on return undefined; owned
+ *                    by the caller, who must not let two calls in flight
+ *                    share it
+ *   workgroups       0 = the current device's CU count, else a multiple of
+ *                    8 no larger than it -> else FP8Q_ERR_VARIANT
+ *   no plan (T <= C, T a multiple of C, or K < 256) or a short workspace ->
+ *   FP8Q_ERR_SHAPE; M = 0 -> nothing launched. */
+fp8q_status fp8q_gemm_blockscaled_streamk(const uint8_t *a_e4m3, const float *a_scale_km,
+                                          const uint8_t *w_e4m3, const float *w_scale,
+                                          uint16_t *out_bf16, void *workspace,
+                                          size_t workspace_bytes, uint32_t M, uint32_t N,
+                                          uint32_t K, uint32_t workgroups, hipStream_t stream);
+
+/* Workspace bytes of fp8q_gemm_blockscaled_streamk on `workgroups` (0 = the
+ * current device's CU count): 64 per workgroup rounded up to 256, plus 128
+ * KiB per workgroup; 0 if workgroups is not a multiple of 8.  Host
+ * function. */
+size_t fp8q_gemm_streamk_workspace_bytes(uint32_t workgroups);
 
 /* Bytes of static device scratch behind fp8q_gemm_blockscaled_splitk_noalloc
  * (per GPU, held until the process ends): 32 MiB. */
@@ -292,9 +352,10 @@ size_t fp8q_gemm_splitk_workspace_bytes(uint32_t M, uint32_t N, uint32_t K, uint
  * errors, with the split-K partials kept in a static device array of
  * FP8Q_NOALLOC_SCRATCH_BYTES instead of a caller workspace.  No entry
  * point allocates; this one takes no workspace either.
- *   splits  0 = automatic (fp8q_gemm_splitk_select; when it gives 1 the
- *           single-pass automatic kernel runs and the scratch is not
- *           touched), else 2 <= splits <= min(K/128, 64)
+ *   splits  0 = automatic split count (fp8q_gemm_splitk_select; when it
+ *           gives 1 the single-pass automatic kernel runs and the scratch
+ *           is not touched; the stream-K form is not used here), else
+ *           2 <= splits <= min(K/128, 64)
  * splits * M * N * 4 > FP8Q_NOALLOC_SCRATCH_BYTES -> FP8Q_ERR_SHAPE, before
  * anything is enqueued.  The first call on a device looks the array's
  * device address up (hipGetSymbolAddress) and keeps it.  All calls on one
@@ -381,8 +442,8 @@ fp8q_status fp8q_proj(const uint16_t *x_bf16, const uint8_t *w_e4m3,
                       uint32_t K, hipStream_t stream);
 
 /* As fp8q_proj, with the GEMM run as fp8q_gemm_blockscaled_splitk with
- * splits = 0 (the automatic count of fp8q_gemm_splitk_select; where that is
- * 1, fp8q_gemm_blockscaled's automatic kernel and the workspace is not
+ * splits = 0 (stream-K or split-K where that takes them; elsewhere
+ * fp8q_gemm_blockscaled's automatic kernel, and the workspace is not
  * touched):
  *   workspace        device memory, 16-byte aligned, at least
  *                    fp8q_gemm_splitk_workspace_bytes(M, N, K, 0) bytes (may

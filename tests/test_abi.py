@@ -238,6 +238,10 @@ def test_ffn_select_and_workspace():
 
     base = (a256(M * H) + a256(M * H // 128 * 4) + a256(Mp * H // 128 * 4) + a256(M * I)
             + a256(Mp * I // 128 * 4))
+    # the down projection (N = H = 5120, K = I = 17408) at M = 4576: the
+    # single-pass 256x128 kernel (no stream-K, no split), no extra workspace
+    assert fp8q.fp8q_gemm_streamk_select(M, H, I) == 0
+    assert fp8q.fp8q_gemm_splitk_workspace_bytes(M, H, I, 0) == 0
     assert fp8q.fp8q_ffn_workspace_bytes(M, H, I, 1) == base
     assert fp8q.fp8q_ffn_workspace_bytes(M, H, I, 2) == base + 2 * a256(2 * M * I)
     assert fp8q.fp8q_ffn_workspace_bytes(M, H, I, 0) == base
@@ -329,7 +333,10 @@ def test_splitk_workspace_bytes():
     assert ws(300, 512, 0, 2) == 0
     for M, N, K in ((512, 5120, 17408), (200, 6144, 5120), (4576, 5120, 17408), (16, 6144, 5120)):
         s = fp8q.fp8q_gemm_splitk_select(M, N, K)
-        assert ws(M, N, K, 0) == (0 if s < 2 else s * M * N * 4)
+        if fp8q.fp8q_gemm_streamk_select(M, N, K) == 1:
+            assert ws(M, N, K, 0) == 256 * 64 + 256 * 131072   # flags + partials, 256 CUs
+        else:
+            assert ws(M, N, K, 0) == (0 if s < 2 else s * M * N * 4)
 
 
 def test_splitk_select():
@@ -412,3 +419,60 @@ def test_shader_clock_pairs_stamps_by_cu():
     assert pairs == 3 and set(per) == {0, 1}
     assert abs(per[1] - 2.1) < 1e-12                   # 2100 ticks in 100 * 10 ns
     assert abs(per[0] - (1.8 + 2.0) / 2) < 1e-12       # two CUs of XCD 0
+
+
+def test_streamk_select():
+    """Stream-K from 512 rows where a plan exists (more 256x128 tiles than
+    CUs, not a multiple of them, the CU count a multiple of 8, K >= 256) and
+    is predicted 10% shorter than the ping-pong kernel's last round.  The
+    decisions follow graph-timed measurements on 256 CUs: stream-K 13%
+    faster at M = 1792, N = 5120, K = 17408 (280 tiles, 24 in the last
+    round); 4-7% slower at the two prefill projections (720 and 680 tiles,
+    most CUs busy in the last round); no faster at N = 8448, K = 8192 and at
+    N = 4224, K = 17408."""
+    sel = fp8q.fp8q_gemm_streamk_select
+    assert sel(1792, 5120, 17408, 256) == 1
+    assert sel(2560, 6656, 17408, 256) == 1      # 520 tiles: two rounds + 8
+    assert sel(1792, 5120, 17408, 240) == 1      # 280 tiles on 240 CUs: one round + 40
+    assert sel(4576, 5120, 17408, 256) == 0 and sel(1168, 17408, 5120, 256) == 0
+    assert sel(2048, 8448, 8192, 256) == 0 and sel(3072, 4224, 17408, 256) == 0
+    assert sel(16384, 5120, 17408, 256) == 0     # 2560 tiles: 10 whole rounds
+    assert sel(1024, 5120, 17408, 256) == 0      # 160 tiles: fewer than the CUs
+    assert sel(1792, 5120, 17408, 304) == 0      # 280 tiles: fewer than the CUs
+    assert sel(1792, 5120, 17408, 252) == 0      # not a multiple of 8 workgroups
+    assert sel(1792, 5120, 1024, 256) == 0       # short K: the partial reads dominate
+    assert sel(500, 40960, 17408, 256) == 0      # under 512 rows
+    assert sel(4576, 5000, 17408, 256) == -1 and sel(4576, 5120, 17408, 0) == -1
+
+
+def test_streamk_workspace_bytes():
+    ws = fp8q.fp8q_gemm_streamk_workspace_bytes
+    assert ws(256) == 256 * 64 + 256 * 131072     # flags, then one partial slot a workgroup
+    assert ws(8) == 512 + 8 * 131072              # 8 waves x 8 bytes of flags a workgroup
+    assert ws(24) == 1536 + 24 * 131072
+    assert ws(12) == 0                            # not a multiple of 8
+
+
+def test_streamk_validation():
+    """The explicit stream-K entry point: argument checks, then the plan,
+    then the workspace, all before the device is touched."""
+    L = fp8q.lib()
+    g = GOOD
+    # fp8q_gemm_blockscaled_streamk(a, as, w, ws, out, work, bytes, M, N, K, workgroups, stream)
+    f = L.fp8q_gemm_blockscaled_streamk
+    assert f(g, g, g, g, g, g, 1 << 30, 300, 100, 1024, 8, None) == 2        # N % 128
+    assert f(g, g, None, g, g, g, 1 << 30, 300, 128, 1024, 8, None) == 1     # NULL operand
+    assert f(g, g, g, g, BAD, g, 1 << 30, 300, 128, 1024, 8, None) == 3      # misaligned
+    assert f(g, g, g, g, g, g, 1 << 30, 300, 1664, 1024, 12, None) == 6      # workgroups % 8
+    assert "workgroups=12" in _err()
+    # plans: 2 x 5 = 10 tiles on 8 workgroups; 8 tiles (a multiple); one K block
+    assert f(g, g, g, g, g, None, 0, 300, 640, 1024, 8, None) == 1           # NULL workspace
+    assert f(g, g, g, g, g, g, 1 << 30, 300, 1024, 1024, 8, None) == 2
+    assert "no stream-K plan" in _err()
+    assert f(g, g, g, g, g, g, 1 << 30, 300, 640, 128, 8, None) == 2
+    assert f(g, g, g, g, g, g, 1 << 30, 256, 1024, 1024, 8, None) == 2      # 8 tiles: T <= C
+    need = fp8q.fp8q_gemm_streamk_workspace_bytes(8)
+    assert f(g, g, g, g, g, BAD, need, 300, 640, 1024, 8, None) == 3
+    assert f(g, g, g, g, g, g, need - 1, 300, 640, 1024, 8, None) == 2
+    assert "workspace" in _err()
+    assert f(g, g, g, g, g, None, 0, 0, 640, 1024, 8, None) == 0            # M == 0

@@ -151,8 +151,10 @@ def test_gemm_full_size_every_kernel(orc, name):
 @pytest.mark.parametrize("name", ["prefill", "large_prefill"])
 def test_gemm_full_size_repeat_bit_identical(orc, name):
     """Race detector: four launches of the automatic kernel back to back (no
-    host synchronization between them) into four outputs, and two more of the
-    128x128 kernel, all M*N outputs compared bit for bit."""
+    host synchronization between them) into four outputs, two more of the
+    128x128 kernel and three of the stream-K form (fp8q_gemm_blockscaled_
+    streamk on one workgroup per CU, one workspace shared by the three), all
+    M*N outputs compared bit for bit."""
     d = _full_size(orc, name)
     M, N = d["w"].M, d["w"].N
     for kern in (0, 1):
@@ -165,14 +167,28 @@ def test_gemm_full_size_repeat_bit_identical(orc, name):
         for i, g in enumerate(outs):
             g.check_canary()
             assert np.array_equal(host(g.t), first), f"kernel {kern}: launch {i} differs"
+    w = d["w"]
+    need = fp8q.fp8q_gemm_streamk_workspace_bytes(0)
+    work = torch.empty((need // 4,), dtype=torch.float32, device="cuda")
+    outs = [Guarded((M, N), torch.int16) for _ in range(3)]
+    log(f"gemm {w.desc} stream-K x3 back to back")
+    for g in outs:
+        fp8q.fp8q_gemm_blockscaled_streamk(d["a_d"], d["km_d"], d["wq_d"], d["ws_d"], g.t, work)
+    torch.cuda.synchronize()
+    first = host(outs[0].t)
+    for i, g in enumerate(outs):
+        g.check_canary()
+        assert np.array_equal(host(g.t), first), f"stream-K: launch {i} differs"
 
 
 @pytest.mark.slow
 @pytest.mark.parametrize("name", ["prefill", "large_prefill"])
 def test_gemm_splitk_full_size(orc, name):
-    """The split-K form at the full prefill sizes (the automatic count, which
-    is no split here, and two forced counts), all M*N outputs against the
-    oracle, workspace canaries checked."""
+    """The workspace forms at the full prefill sizes (the automatic choice,
+    the single-pass kernel at both; split-K at two forced counts; the
+    stream-K form on one workgroup per CU: 720 and 680 tiles, two whole
+    rounds and a tail of 208 and 168 tiles cut in two pieces along K), all
+    M*N outputs against the oracle, workspace canaries checked."""
     d = _full_size(orc, name)
     w = d["w"]
     M, N, K = w.M, w.N, w.K
@@ -188,6 +204,15 @@ def test_gemm_splitk_full_size(orc, name):
         if work is not None:
             work.check_canary()
         assert_tol(bf16_bits_to_f64(host(out.t)), d["ref"], f"{w.desc} splitk s{splits}")
+    need = fp8q.fp8q_gemm_streamk_workspace_bytes(0)
+    log(f"streamk {w.desc} workspace={need}")
+    out = Guarded((M, N), torch.int16)
+    work = Guarded((need // 4,), torch.float32, fill=0x7F)
+    fp8q.fp8q_gemm_blockscaled_streamk(d["a_d"], d["km_d"], d["wq_d"], d["ws_d"], out.t, work.t)
+    torch.cuda.synchronize()
+    out.check_canary()
+    work.check_canary()
+    assert_tol(bf16_bits_to_f64(host(out.t)), d["ref"], f"{w.desc} streamk")
 
 
 @pytest.mark.slow

@@ -180,3 +180,131 @@ def test_proj_splitk(orc, M, N, K):
         torch.cuda.synchronize()
         assert np.array_equal(o, bf16_bits_to_f64(host(ref_out)))
     assert_tol(o, orc.gemm_ref(a, a_s, wq, ws), f"proj_splitk M{M}N{N}K{K}")
+
+
+def _streamk_gpu(orc, a, a_s, wq, ws, workgroups, repeat=1):
+    """fp8q_gemm_blockscaled_streamk `repeat` times back to back into separate
+    outputs (one workspace, which starts non-zero), canaries checked."""
+    M, K = a.shape
+    N = wq.shape[0]
+    km = orc.scale_to_kmajor(a_s)
+    need = fp8q.fp8q_gemm_streamk_workspace_bytes(workgroups)
+    work = Guarded((need // 4,), torch.float32, fill=0x7F)
+    outs = [Guarded((M, N), torch.int16) for _ in range(repeat)]
+    a_d, km_d, w_d, ws_d = dev(a), dev(km), dev(wq), dev(ws)
+    for o in outs:
+        fp8q.fp8q_gemm_blockscaled_streamk(a_d, km_d, w_d, ws_d, o.t, work.t, workgroups)
+    torch.cuda.synchronize()
+    work.check_canary()
+    res = []
+    for o in outs:
+        o.check_canary()
+        res.append(bf16_bits_to_f64(host(o.t)))
+    return res
+
+
+# (M, N, K, workgroups C): T = ceil(M/256) * N/128 tiles, R whole rounds, Tt
+# tail tiles, P pieces a tail tile.
+#   256 x 1664 x 1024 on 8:  T = 13, R = 1, Tt = 5 > C/2: P = 2, the 3
+#                            secondaries take the second pieces in 2 rounds
+#   300 x 1152 x 8192 on 8:  T = 18, R = 2, Tt = 2: P = 4, ragged last row tile
+#   256 x 1152 x 17408 on 8: T = 9, R = 1, Tt = 1: P = 5 (G = 136)
+#   520 x 1280 x 2048 on 16: T = 30, R = 1, Tt = 14: P = 2 in 7 rounds, an
+#                            8-row last row tile
+#   1168 x 17408 x 1024 and 4576 x 5120 x 1024 on one workgroup per CU (the
+#   prefill shapes at short K): 680 / 720 tiles, Tt = 168 / 208, P = 2
+STREAMK_CASES = [(256, 1664, 1024, 8), (300, 1152, 8192, 8), (256, 1152, 17408, 8),
+                 (520, 1280, 2048, 16), (1168, 17408, 1024, 0), (4576, 5120, 1024, 0)]
+
+
+@pytest.mark.parametrize("M,N,K,C", STREAMK_CASES,
+                         ids=[f"M{m}N{n}K{k}C{c}" for m, n, k, c in STREAMK_CASES])
+def test_streamk_plans_full(orc, M, N, K, C):
+    """The stream-K form under every kind of plan: all M*N outputs against
+    the oracle, and the same bits from two more launches back to back on the
+    same workspace (the flags of one call must not release the next)."""
+    a, a_s, wq, ws = _random_operands(orc, M, N, K, M + N + K + C, "laplace")
+    log(f"oracle M={M} N={N} K={K}")
+    ref = orc.gemm_ref(a, a_s, wq, ws)
+    log(f"streamk M={M} N={N} K={K} workgroups={C}")
+    outs = _streamk_gpu(orc, a, a_s, wq, ws, C, repeat=3)
+    assert_tol(outs[0], ref, f"streamk M{M}N{N}K{K}C{C}")
+    for i, o in enumerate(outs[1:]):
+        assert np.array_equal(o, outs[0]), f"stream-K launch {i + 1} differs"
+
+
+def test_streamk_exact_cases(orc):
+    """Codes 1.0 (0x38) and power-of-two scales: each block adds 128 *
+    2^e, e in [-12, 2], and the 64 blocks' sum spans under 2^20, so every
+    partial sum is exact in fp32 whatever its order: the output is the
+    oracle's value rounded to bf16, bit for bit (P = 4 pieces, ragged row
+    tile)."""
+    M, N, K, C = 300, 1152, 8192, 8
+    a = np.full((M, K), 0x38, dtype=np.uint8)
+    wq = np.full((N, K), 0x38, dtype=np.uint8)
+    rng = np.random.default_rng(4)
+    a_s = np.ldexp(1.0, rng.integers(-6, 2, (M, K // 128))).astype(np.float32)
+    ws = np.ldexp(1.0, rng.integers(-6, 2, (N // 128, K // 128))).astype(np.float32)
+    out, = _streamk_gpu(orc, a, a_s, wq, ws, C)
+    assert np.array_equal(out, orc.round_to_bf16(orc.gemm_ref(a, a_s, wq, ws)))
+
+
+def test_streamk_graph_replay(orc):
+    """A captured stream-K launch replays with the same generation number:
+    each replay must wait for its own partials.  Three replays, with eager
+    stream-K calls on the same workspace and a host synchronization between
+    them, each checked bit for bit against the eager result."""
+    M, N, K, C = 300, 1152, 8192, 8
+    a, a_s, wq, ws = _random_operands(orc, M, N, K, 77)
+    km = orc.scale_to_kmajor(a_s)
+    a_d, km_d, w_d, ws_d = dev(a), dev(km), dev(wq), dev(ws)
+    work = torch.empty((fp8q.fp8q_gemm_streamk_workspace_bytes(C) // 4,), dtype=torch.float32,
+                       device="cuda")
+    eager = torch.empty((M, N), dtype=torch.int16, device="cuda")
+    fp8q.fp8q_gemm_blockscaled_streamk(a_d, km_d, w_d, ws_d, eager, work, C)
+    torch.cuda.synchronize()
+    ref = host(eager).copy()
+    assert_tol(bf16_bits_to_f64(ref), orc.gemm_ref(a, a_s, wq, ws), "streamk eager")
+    out = torch.zeros((M, N), dtype=torch.int16, device="cuda")
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fp8q.fp8q_gemm_blockscaled_streamk(a_d, km_d, w_d, ws_d, out, work, C)
+    for r in range(3):
+        out.fill_(0)
+        log(f"streamk graph replay {r}")
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(host(out), ref), f"replay {r} differs from the eager result"
+        other = torch.empty_like(eager)
+        fp8q.fp8q_gemm_blockscaled_streamk(a_d, km_d, w_d, ws_d, other, work, C)
+        torch.cuda.synchronize()
+        assert np.array_equal(host(other), ref)
+
+
+def test_streamk_auto_sampled(orc):
+    """The automatic choice of the workspace form at a shape where it takes
+    stream-K (M = 1792, N = 5120, K = 17408: 280 tiles on 256 CUs, 24 in the
+    last round, P = 5): the same bits as the explicit entry point, and every
+    output of 56 sampled rows (8 from each 256-row tile) against the oracle."""
+    M, N, K = 1792, 5120, 17408
+    if fp8q.fp8q_gemm_streamk_select(M, N, K) != 1:
+        pytest.skip("the automatic choice on this device's CU count is not stream-K here")
+    a, a_s, wq, ws = _random_operands(orc, M, N, K, 5)
+    km = orc.scale_to_kmajor(a_s)
+    need = fp8q.fp8q_gemm_splitk_workspace_bytes(M, N, K, 0)
+    assert need == fp8q.fp8q_gemm_streamk_workspace_bytes(0)
+    work = Guarded((need // 4,), torch.float32, fill=0x7F)
+    out = Guarded((M, N), torch.int16)
+    log(f"streamk auto M={M} N={N} K={K}")
+    fp8q.fp8q_gemm_blockscaled_splitk(dev(a), dev(km), dev(wq), dev(ws), out.t, work.t)
+    torch.cuda.synchronize()
+    out.check_canary()
+    work.check_canary()
+    got = bf16_bits_to_f64(host(out.t))
+    explicit, = _streamk_gpu(orc, a, a_s, wq, ws, 0)
+    assert np.array_equal(got, explicit)
+    rows = np.concatenate([t * 256 + np.random.default_rng(t).choice(256, 8, replace=False)
+                           for t in range(M // 256)])
+    log(f"oracle M={M} N={N} K={K}: {rows.size} rows")
+    ref = orc.gemm_ref(a[rows], a_s[rows], wq, ws)
+    assert_tol(got[rows], ref, f"streamk auto M{M}N{N}K{K} sampled rows")

@@ -74,7 +74,11 @@ _SIGS = {
     "fp8q_gemm_blockscaled_splitk": (_I, [_P, _P, _P, _P, _P, _P, _SZ, _U, _U, _U, _U, _P]),
     "fp8q_gemm_splitk_select": (_U, [_U, _U, _U]),
     "fp8q_gemm_splitk_select_cus": (_U, [_U, _U, _U, _U]),
+    "fp8q_gemm_streamk_select": (_I, [_U, _U, _U]),
+    "fp8q_gemm_streamk_select_cus": (_I, [_U, _U, _U, _U]),
     "fp8q_gemm_splitk_workspace_bytes": (_SZ, [_U, _U, _U, _U]),
+    "fp8q_gemm_blockscaled_streamk": (_I, [_P, _P, _P, _P, _P, _P, _SZ, _U, _U, _U, _U, _P]),
+    "fp8q_gemm_streamk_workspace_bytes": (_SZ, [_U]),
     "fp8q_gemm_blockscaled_splitk_noalloc": (_I, [_P, _P, _P, _P, _P, _U, _U, _U, _U, _P]),
     "fp8q_clock_stamp": (_I, [_P, _U, _P]),
     "fp8q_proj": (_I, [_P, _P, _P, _P, _P, _P, _P, _U, _U, _U, _P]),
@@ -198,6 +202,14 @@ def fp8q_gemm_splitk_select(M: int, N: int, K: int, cu_count: int = None) -> int
     return int(lib().fp8q_gemm_splitk_select(M, N, K))
 
 
+def fp8q_gemm_streamk_select(M: int, N: int, K: int, cu_count: int = None) -> int:
+    """1 if fp8q_gemm_blockscaled_splitk with splits=0 runs the stream-K form
+    (on the current device, or one with cu_count compute units)."""
+    if cu_count is not None:
+        return int(lib().fp8q_gemm_streamk_select_cus(M, N, K, cu_count))
+    return int(lib().fp8q_gemm_streamk_select(M, N, K))
+
+
 def fp8q_gemm_splitk_workspace_bytes(M: int, N: int, K: int, splits: int = 0) -> int:
     return int(lib().fp8q_gemm_splitk_workspace_bytes(M, N, K, splits))
 
@@ -215,6 +227,25 @@ def fp8q_gemm_blockscaled_splitk(a, a_scale_km, w, w_scale, out, workspace, spli
     _check(lib().fp8q_gemm_blockscaled_splitk(_ptr(a), _ptr(a_scale_km), _ptr(w), _ptr(w_scale),
                                              _ptr(out), _optr(workspace), nbytes, M, N, K,
                                              splits, _stream(stream)))
+
+
+def fp8q_gemm_streamk_workspace_bytes(workgroups: int = 0) -> int:
+    return int(lib().fp8q_gemm_streamk_workspace_bytes(workgroups))
+
+
+def fp8q_gemm_blockscaled_streamk(a, a_scale_km, w, w_scale, out, workspace, workgroups: int = 0,
+                                  stream=None):
+    """fp8q_gemm_blockscaled in its stream-K form on `workgroups` persistent
+    workgroups (0 = the device's CU count); workspace: a device tensor of at
+    least fp8q_gemm_streamk_workspace_bytes(workgroups) bytes."""
+    M, K = _dims(a, 2)
+    N, K2 = _dims(w, 2)
+    if K2 != K:
+        raise ValueError("a and w disagree on K")
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().fp8q_gemm_blockscaled_streamk(_ptr(a), _ptr(a_scale_km), _ptr(w), _ptr(w_scale),
+                                              _ptr(out), _optr(workspace), nbytes, M, N, K,
+                                              workgroups, _stream(stream)))
 
 
 NOALLOC_SCRATCH_BYTES = 32 << 20  # FP8Q_NOALLOC_SCRATCH_BYTES
@@ -375,6 +406,7 @@ GEMM_KERNEL_NAMES = {1: "gemm_tiled_kernel<128,128,2,2,2>", 2: "gemm_skinny_kern
                      5: "gemm_pp_kernel<3,false,false>"}
 FFN_GATE_UP_KERNEL_NAME = "gemm_pp_kernel<3,false,true>"
 SPLITK_KERNEL_NAMES = ("gemm_tiled_kernel<128,128,2,2,2,false,true>", "splitk_reduce_kernel")
+STREAMK_KERNEL_NAME = "gemm_pp_sk_kernel<3>"
 
 
 def fp8q_quant_b_min_m(K: int, params: SelectParams) -> int:

@@ -289,6 +289,28 @@ uint64_t splitk_workspace(uint32_t M, uint32_t N, uint32_t splits) {
   return splits < 2 ? 0 : (uint64_t)splits * M * N * 4;
 }
 
+// The automatic GEMM where a caller workspace is at hand: the stream-K form
+// of the 256 x 128 ping-pong kernel where its plan applies (sk_make_plan: a
+// last round of data-parallel tiles small enough that the balanced split is
+// predicted 10% shorter), from kTailRuleMinM rows, else split-K where
+// splitk_auto splits, else the single-pass kernel.  Measured, graph-timed
+// back-to-back launches on 256 CUs, single-pass -> stream-K: M = 1792,
+// N = 5120, K = 17408 (280 tiles, 24 in the last round) 215 -> 203 us with 10
+// pieces a tail tile, before the partial-read cost entered the plan.  Where
+// most CUs have a tile in the last round (the prefill shapes: M = 4576,
+// N = 5120, K = 17408, 720 tiles; M = 1168, N = 17408, K = 5120, 680) the
+// stream-K form was 4-7% slower than the data-parallel kernel: on this
+// power-limited chip a partial last round clocks higher, and the split
+// tiles' partial reads cost more than the balance gains.
+bool streamk_auto(uint32_t M, uint32_t N, uint32_t K, uint32_t cus) {
+  return M >= kTailRuleMinM && gemm_streamk_applies(M, N, K, cus, false);
+}
+
+uint64_t auto_workspace(uint32_t M, uint32_t N, uint32_t K, uint32_t cus) {
+  if (streamk_auto(M, N, K, cus)) return gemm_streamk_workspace_bytes(cus);
+  return splitk_workspace(M, N, splitk_auto(M, N, K, cus));
+}
+
 fp8q_status run_gemm(const char* fn, const uint8_t* a, const float* as, const uint8_t* w,
                      const float* ws, uint16_t* out, uint32_t M, uint32_t N, uint32_t K, int kernel,
                      bool row_scaled, hipStream_t s) {
@@ -305,15 +327,17 @@ fp8q_status run_gemm(const char* fn, const uint8_t* a, const float* as, const ui
   return launched(fn, e);
 }
 
-// The automatic block-scaled GEMM where a split-K workspace is at hand:
-// split-K when splitk_auto picks it (part holds the partials), else the
-// automatic single-pass kernel.
+// The automatic block-scaled GEMM where a workspace is at hand (part, of
+// auto_workspace bytes): stream-K or split-K where auto_workspace says so,
+// else the automatic single-pass kernel.
 fp8q_status run_gemm_ws(const char* fn, const uint8_t* a, const float* as, const uint8_t* w,
                         const float* ws, uint16_t* out, float* part, uint32_t M, uint32_t N,
                         uint32_t K, hipStream_t s) {
   uint32_t cus = 0;
   const fp8q_status st = check_device(fn, &cus);
   if (st != FP8Q_OK) return st;
+  if (streamk_auto(M, N, K, cus))
+    return launched(fn, launch_gemm_streamk(a, as, w, ws, out, part, M, N, K, cus, false, s));
   const uint32_t splits = splitk_auto(M, N, K, cus);
   if (splits < 2) return run_gemm(fn, a, as, w, ws, out, M, N, K, 0, false, s);
   return launched(fn, launch_splitk_128(a, as, w, ws, out, part, M, N, K, splits, cus, s));
@@ -368,9 +392,10 @@ fp8q_status run_proj(const char* fn, const uint16_t* x_bf16, const uint8_t* w_e4
   // the workspace is sized for the current device (as the size query is);
   // the device itself is checked once the arguments are
   const uint32_t cus = current_cus();
-  const uint32_t splits = split_k ? splitk_auto(M, N, K, cus) : 1;
-  if (splits >= 2) {
-    const uint64_t need = splitk_workspace(M, N, splits);
+  const bool streamk = split_k && streamk_auto(M, N, K, cus);
+  const uint32_t splits = split_k && !streamk ? splitk_auto(M, N, K, cus) : 1;
+  if (splits >= 2 || streamk) {
+    const uint64_t need = streamk ? gemm_streamk_workspace_bytes(cus) : splitk_workspace(M, N, splits);
     void* workspace = split_ws;
     REQUIRE_PTR(workspace);
     if (split_ws_bytes < need)
@@ -390,6 +415,9 @@ fp8q_status run_proj(const char* fn, const uint16_t* x_bf16, const uint8_t* w_e4
     st = launched(fn, launch_relayout(act_scale_scratch, act_scale_km_scratch, M, K, stream));
     if (st != FP8Q_OK) return st;
   }
+  if (streamk)
+    return launched(fn, launch_gemm_streamk(act_q_scratch, act_scale_km_scratch, w_e4m3, w_scale,
+                                            out_bf16, split_ws, M, N, K, cus, false, stream));
   if (splits >= 2)
     return launched(fn, launch_splitk_128(act_q_scratch, act_scale_km_scratch, w_e4m3, w_scale,
                                           out_bf16, static_cast<float*>(split_ws), M, N, K, splits,
@@ -433,9 +461,10 @@ FfnWorkspace ffn_workspace(uint32_t M, uint32_t H, uint32_t I, int variant, uint
     w.g = o; o = align256(o + (uint64_t)M * I * 2);
     w.u = o; o = align256(o + (uint64_t)M * I * 2);
   }
-  // split-K partials of the down projection (empty when it does not split;
-  // gate and up never split, so that the variants stay bit-identical)
-  const uint64_t part = splitk_workspace(M, H, splitk_auto(M, H, I, cus));
+  // stream-K or split-K workspace of the down projection (empty when it runs
+  // single-pass; gate and up never split, so that the variants stay
+  // bit-identical)
+  const uint64_t part = auto_workspace(M, H, I, cus);
   w.part = part ? o : 0;
   o = align256(o + part);
   w.total = o;
@@ -671,8 +700,58 @@ uint32_t fp8q_gemm_splitk_select(uint32_t M, uint32_t N, uint32_t K) {
 
 size_t fp8q_gemm_splitk_workspace_bytes(uint32_t M, uint32_t N, uint32_t K, uint32_t splits) {
   if (N % kGroup != 0 || K == 0 || K % kGroup != 0 || splits > K / kGroup) return 0;
-  if (splits == 0) splits = splitk_auto(M, N, K, current_cus());
+  if (splits == 0) return (size_t)auto_workspace(M, N, K, current_cus());
   return (size_t)splitk_workspace(M, N, splits);
+}
+
+int fp8q_gemm_streamk_select_cus(uint32_t M, uint32_t N, uint32_t K, uint32_t cu_count) {
+  if (N == 0 || N % kGroup != 0 || K == 0 || K % kGroup != 0 || cu_count == 0) return -1;
+  return streamk_auto(M, N, K, cu_count) ? 1 : 0;
+}
+
+int fp8q_gemm_streamk_select(uint32_t M, uint32_t N, uint32_t K) {
+  return fp8q_gemm_streamk_select_cus(M, N, K, current_cus());
+}
+
+size_t fp8q_gemm_streamk_workspace_bytes(uint32_t workgroups) {
+  if (workgroups == 0) workgroups = current_cus();
+  if (workgroups % 8 != 0) return 0;
+  return gemm_streamk_workspace_bytes(workgroups);
+}
+
+fp8q_status fp8q_gemm_blockscaled_streamk(const uint8_t* a_e4m3, const float* a_scale_km,
+                                          const uint8_t* w_e4m3, const float* w_scale,
+                                          uint16_t* out_bf16, void* workspace,
+                                          size_t workspace_bytes, uint32_t M, uint32_t N,
+                                          uint32_t K, uint32_t workgroups, hipStream_t stream) {
+  const char* fn = "fp8q_gemm_blockscaled_streamk";
+  fp8q_status st =
+      check_gemm_args(fn, a_e4m3, a_scale_km, w_e4m3, w_scale, "w_scale", out_bf16, M, N, K, 0);
+  if (st != FP8Q_OK) return st;
+  if (workgroups % 8 != 0)
+    return fail(FP8Q_ERR_VARIANT, "%s: workgroups=%u (0 = the CU count, else a multiple of 8)",
+                fn, workgroups);
+  if (M == 0) return ok();
+  const uint32_t wg = workgroups ? workgroups : current_cus();
+  if (!gemm_streamk_applies(M, N, K, wg, true))
+    return fail(FP8Q_ERR_SHAPE,
+                "%s: no stream-K plan for M=%u N=%u K=%u on %u workgroups (needs more 256x128 "
+                "tiles than workgroups, not a multiple of them, and K >= 256)",
+                fn, M, N, K, wg);
+  REQUIRE_PTR(workspace);
+  const uint64_t need = gemm_streamk_workspace_bytes(wg);
+  if (workspace_bytes < need)
+    return fail(FP8Q_ERR_SHAPE, "%s: workspace of %llu bytes, %llu needed", fn,
+                (unsigned long long)workspace_bytes, (unsigned long long)need);
+  uint32_t cus = 0;
+  st = check_device(fn, &cus);
+  if (st != FP8Q_OK) return st;
+  // every workgroup must be resident at once (they wait on one another)
+  if (wg > cus)
+    return fail(FP8Q_ERR_VARIANT, "%s: workgroups=%u exceeds the device's %u compute units", fn,
+                wg, cus);
+  return launched(fn, launch_gemm_streamk(a_e4m3, a_scale_km, w_e4m3, w_scale, out_bf16,
+                                          workspace, M, N, K, wg, true, stream));
 }
 
 fp8q_status fp8q_gemm_blockscaled_splitk(const uint8_t* a_e4m3, const float* a_scale_km,
@@ -689,6 +768,17 @@ fp8q_status fp8q_gemm_blockscaled_splitk(const uint8_t* a_e4m3, const float* a_s
                 kSplitMaxUser);
   if (M == 0) return ok();
   const uint32_t cus = current_cus();  // as fp8q_gemm_splitk_workspace_bytes sizes it
+  if (splits == 0 && streamk_auto(M, N, K, cus)) {
+    const uint64_t need = gemm_streamk_workspace_bytes(cus);
+    REQUIRE_PTR(workspace);
+    if (workspace_bytes < need)
+      return fail(FP8Q_ERR_SHAPE, "%s: workspace of %llu bytes, %llu needed", fn,
+                  (unsigned long long)workspace_bytes, (unsigned long long)need);
+    st = check_device(fn);
+    if (st != FP8Q_OK) return st;
+    return launched(fn, launch_gemm_streamk(a_e4m3, a_scale_km, w_e4m3, w_scale, out_bf16,
+                                            workspace, M, N, K, cus, false, stream));
+  }
   if (splits == 0) splits = splitk_auto(M, N, K, cus);
   if (splits >= 2) {
     const uint64_t need = splitk_workspace(M, N, splits);

@@ -63,6 +63,19 @@ hipError_t launch_splitk_128(const uint8_t* a, const float* a_s_km, const uint8_
                              const float* w_s, uint16_t* out, float* part, uint32_t M,
                              uint32_t N, uint32_t K, uint32_t splits, uint32_t cus,
                              hipStream_t s);
+// Stream-K form of the 256x128 ping-pong kernel (block-scaled weights): cus
+// persistent workgroups (a multiple of 8, at most the device's CUs); whole
+// tiles in data-parallel rounds, the last partial round's tiles cut along K
+// into pieces for the otherwise idle workgroups, the pieces summed through
+// fp32 partials and per-wave flags in the caller's workspace of
+// gemm_streamk_workspace_bytes(cus) bytes (contents on entry ignored).
+// gemm_streamk_applies: whether a plan exists for the shape and, unless
+// forced, is predicted at least 10% shorter than the data-parallel kernel.
+bool gemm_streamk_applies(uint32_t M, uint32_t N, uint32_t K, uint32_t cus, bool forced);
+uint64_t gemm_streamk_workspace_bytes(uint32_t cus);
+hipError_t launch_gemm_streamk(const uint8_t* a, const float* a_s_km, const uint8_t* w,
+                               const float* w_s, uint16_t* out, void* workspace, uint32_t M,
+                               uint32_t N, uint32_t K, uint32_t cus, bool forced, hipStream_t s);
 hipError_t launch_gemm_skinny(const uint8_t* a, const float* a_s_km, const uint8_t* w,
                               const float* w_s, uint16_t* out, uint32_t M, uint32_t N,
                               uint32_t K, uint32_t cu_count, bool row_scaled, hipStream_t s);

@@ -17,6 +17,7 @@
 // operands, so both see the same K permutation and the dot product is the
 // full 128-term sum whatever order the hardware assigns to those bytes.
 #include <atomic>
+#include <chrono>
 #include "mfma_common.h"
 #include "quant_common.h"
 
@@ -844,6 +845,480 @@ hipError_t launch_pp_cfg(const uint8_t* a, const float* a_s_km, const uint8_t* w
 }
 
 // ------------------------------------------------------------------------
+// Stream-K form of the ping-pong kernel (block-scaled weights).  The grid
+// holds C persistent workgroups, one per CU.  With T tiles of 256x128 and
+// G = K/128 blocks each, workgroup q first computes whole tiles r*C + q for
+// r < R = floor(T/C) (the data-parallel rounds).  The Tt = T - R*C tail
+// tiles are cut along K into P pieces at block boundaries 0 = b_0 < b_1 <
+// ... < b_P = G: workgroup q < Tt (a primary) computes piece 0 of tail tile
+// q; the other S = C - Tt workgroups (secondaries) share the (P-1)*Tt later
+// pieces, unit u = (p-1)*Tt + t (piece p of tail tile t) going to secondary
+// u mod S in round u / S.  This keeps what makes the data-parallel rounds
+// fast: at any moment the primaries run the same K block of consecutive
+// tiles, and so do the secondaries, so the workgroups of one XCD read the
+// same activation and weight panels and share them in its L2.  (Cutting the
+// tail's iterations into one contiguous range per workgroup instead puts
+// neighbouring workgroups at unrelated K offsets; the tail then runs at the
+// rate of the memory behind the L2, slower than the data-parallel kernel's
+// partly idle last wave.)  P and b_1 balance the two sides (sk_make_plan).
+//
+// All of a workgroup's segments run as one LDS pipeline: the loads of
+// iteration i + STAGES may belong to the next segment, so a segment boundary
+// costs no refill.  q numbers the workgroups XCD by XCD (workgroup ids are
+// dealt round robin to the 8 XCDs), so consecutive tiles sit on one XCD.
+//
+// A secondary writes each piece's fp32 partial tile to the piece's slot of
+// the workspace (slot t*(P-1) + p-1: a tile's partials are contiguous) (each wave its 64x64 part, in register order, with
+// device-coherent stores), waits for the stores to complete, then writes the
+// slot's per-wave flag with the call's generation number.  The primary, once
+// its own piece is done, waits for the flags of pieces 1 .. P-1, reads those
+// partials with device-coherent loads, adds them in piece order and stores
+// the bf16 tile.  A wave gives up waiting after kSkSpinLimit polls and writes
+// NaN, so every wave ends even if a partner never ran.  The sum differs from
+// the single-pass kernels only in the fp32 association of the K blocks, and
+// is the same run to run.
+// ------------------------------------------------------------------------
+struct SkPlan {
+  uint32_t C;          // persistent workgroups (the grid)
+  uint32_t rounds;     // data-parallel rounds R
+  uint32_t tail_base;  // first tail tile = R * C
+  uint32_t tail;       // tail tiles Tt, 0 < Tt < C
+  uint32_t pieces;     // pieces per tail tile P >= 2; (P-1) * Tt <= C - Tt
+  uint32_t b1;         // end of piece 0; pieces 1 .. P-1 split blocks [b1, G) evenly
+};
+struct SkArgs {
+  float* part;                // [C][8 waves][16 MFMA tiles][64 lanes] x 4 fp32
+  unsigned long long* flags;  // [C][8 waves]
+  unsigned long long gen;     // generation number of this call
+};
+constexpr uint32_t kSkSpinLimit = 1u << 22;
+// at most this many pieces per tail tile: a piece's partial costs its
+// primary a 128 KB read, and one lane polls each piece's flags
+constexpr uint32_t kSkMaxPieces = 16;
+// minimum by value (a min returning a reference to its argument keeps the
+// cursor fields in private memory, and loads from there count as per-lane)
+__device__ __forceinline__ uint32_t umin(uint32_t a, uint32_t b) { return a < b ? a : b; }
+// Cache policy of the partials' buffer stores and loads: sc1, the
+// device-coherent form (coherent across the XCDs' L2 caches without an L2
+// write-back or invalidate, which would stall every wave of the XCD).
+constexpr int kCoherent = 16;
+
+template <int STAGES>
+__global__ __launch_bounds__(512) void gemm_pp_sk_kernel(
+    const uint8_t* __restrict__ A, const float* __restrict__ As, const uint8_t* __restrict__ W,
+    const float* __restrict__ Ws, uint16_t* __restrict__ out, uint32_t M, uint32_t N, uint32_t K,
+    uint32_t Mp, uint32_t tiles_m, uint32_t tiles_n, SkPlan plan, SkArgs sk) {
+  using C = PpCfg<STAGES, false, false>;
+  constexpr int TM = C::TM, TN = C::TN, NP = C::NP, BM = C::BM, BN = C::BN;
+  constexpr int CH0 = C::CH0, CH1 = C::CH1, LW0 = C::LW0, LW1 = C::LW1;
+  static_assert(STAGES == 3, "the unrolled loop below assumes three slots");
+  extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
+
+  const uint32_t tid = threadIdx.x, lane = tid & 63;
+  const uint32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const uint32_t G = K / kGroup;
+  const uint32_t w = blockIdx.x;
+  const uint32_t q = (plan.C % 8 == 0) ? (w % 8) * (plan.C / 8) + w / 8 : w;
+  const uint32_t R = plan.rounds, Tt = plan.tail, S = plan.C - Tt;
+  const uint32_t units = Tt * (plan.pieces - 1);
+  const bool primary = q < Tt;
+  // segments of this workgroup: R data-parallel tiles, then its tail work
+  const uint32_t n_seg =
+      R + (primary ? 1u : (q - Tt < units ? (units - (q - Tt) + S - 1) / S : 0u));
+  if (n_seg == 0) return;  // uniform over the workgroup
+  // first block of piece p >= 1
+  auto bound = [&](uint32_t p) __attribute__((always_inline)) -> uint32_t {
+    return plan.b1 + ((p - 1) * (G - plan.b1)) / (plan.pieces - 1);
+  };
+  // unit of segment k >= R of a secondary
+  auto unit_of = [&](uint32_t k) __attribute__((always_inline)) -> uint32_t {
+    return (q - Tt) + (k - R) * S;
+  };
+  // segment k: tile and K blocks kb0 .. kb1-1
+  auto segment = [&](uint32_t k, uint32_t& tile, uint32_t& kb0, uint32_t& kb1)
+      __attribute__((always_inline)) {
+    if (k < R) {
+      tile = q + k * plan.C;
+      kb0 = 0;
+      kb1 = G;
+    } else if (primary) {
+      tile = plan.tail_base + q;
+      kb0 = 0;
+      kb1 = plan.b1;
+    } else {
+      const uint32_t u = unit_of(k), p = 1 + u / Tt;
+      tile = plan.tail_base + u % Tt;
+      kb0 = bound(p);
+      kb1 = bound(p + 1);
+    }
+  };
+
+  // ---- iteration cursors (the load side runs STAGES iterations ahead) ----
+  // Plain scalars, so that they stay in scalar registers.  Past the last
+  // segment the load cursor stays on the last block, which the load side
+  // then reloads (in bounds, unused).
+  uint32_t l_seg = 0, l_tile, l_kb, l_kb1;  // load cursor
+  segment(0, l_tile, l_kb, l_kb1);
+  uint32_t c_seg = 0, c_tile = l_tile, c_kb0 = l_kb, c_kb1 = l_kb1;  // compute cursor
+  const __amdgpu_buffer_rsrc_t rP = make_rsrc(sk.part, plan.C * 8 * NP * 64 * 16);
+
+  // The two wave groups run different halves of each step; each is compiled
+  // for its group (grp a constant), so that every choice below that
+  // depends on it folds away.
+  auto body = [&](auto grp_c) __attribute__((always_inline)) {
+    constexpr uint32_t grp = decltype(grp_c)::value;
+    const uint32_t gw = wave & 3;
+    const uint32_t wm = 2 * grp + (gw >> 1), wn = gw & 1;
+    // Operand chunks of this wave, as in gemm_pp_kernel: group 1 loads
+    // activation rows 0-127 (chunks 4*gw .. 4*gw+3) and the scales of itself
+    // and of its group-0 partner; in group 0, waves 0 and 1 load activation
+    // rows 128-255 (chunks 16 + 8*gw + j), waves 2 and 3 weight rows
+    // (chunks 32 .. 47).  Each chunk is 8 rows of 128 bytes, row + lane/8 per
+    // lane.  The per-lane offsets are relative to the tile's first row and
+    // the same for every tile; the tile's origin is in the buffer resource
+    // (rebuilt when the load cursor moves to another tile), whose bound ends
+    // at row M: activation rows past M fall outside it and load as zeros
+    // (without a memory access), and their outputs are not stored.
+    constexpr int CH = grp ? CH1 : CH0;
+    const bool act = grp || gw < 2;
+    auto chunk = [&](int j) __attribute__((always_inline)) -> uint32_t {
+      return grp ? 4 * gw + j : 16 + 8 * gw + j;
+    };
+    uint32_t c_off[CH];
+#pragma unroll
+    for (int j = 0; j < CH; ++j) {
+      const uint32_t row = (act ? chunk(j) : chunk(j) - 32) * 8 + (lane >> 3), col = lane & 7;
+      c_off[j] = row * K + (col ^ swz(row)) * 16;
+    }
+    const uint32_t my_sc = C::A_BYTES + C::W_BYTES + wave * C::SCW_BYTES;
+    const uint32_t p_sc = C::A_BYTES + C::W_BYTES + gw * C::SCW_BYTES;
+    __amdgpu_buffer_rsrc_t rOp;  // this wave's operand from the tile's origin
+    uint32_t s_off = 0, s_off_p = 0, ws_off = 0;
+    const __amdgpu_buffer_rsrc_t rS = make_rsrc(As, G * Mp * 4);
+    const __amdgpu_buffer_rsrc_t rWs = make_rsrc(Ws, (N / kGroup) * G * 4);
+    auto load_offsets = [&](uint32_t tile) __attribute__((always_inline)) {
+      uint32_t tmi, tni;
+      grouped_tile(tile, tiles_m, tiles_n, tmi, tni);
+      const uint32_t m0 = tmi * BM, n0 = tni * BN;
+      rOp = act ? make_rsrc(A + (uint64_t)m0 * K, (M - m0) * K)
+                : make_rsrc(W + (uint64_t)n0 * K, BN * K);
+      if constexpr (grp == 1) {
+        s_off = min(m0 + wm * C::WM + lane, Mp - 1) * 4;
+        s_off_p = min(m0 + (gw >> 1) * C::WM + lane, Mp - 1) * 4;
+        ws_off = (n0 / kGroup) * G * 4;
+      }
+    };
+    load_offsets(l_tile);
+    // after each issue: the next block, or the first of the next segment
+    // (with the origin of its tile)
+    auto load_next = [&]() __attribute__((always_inline)) {
+      if (l_kb + 1 < l_kb1) {
+        ++l_kb;
+      } else if (l_seg + 1 < n_seg) {
+        segment(++l_seg, l_tile, l_kb, l_kb1);
+        load_offsets(l_tile);
+      }
+    };
+    auto issue = [&](uint32_t stage) __attribute__((always_inline)) {
+      // the LDS address of each chunk is formed here, from a base the
+      // compiler cannot hoist (hoisted, the 3 x 8 chunk addresses would hold
+      // 24 scalar registers through the loop)
+      uint32_t lds = lds_addr(smem) + stage * C::STAGE_BYTES;
+      asm volatile("" : "+s"(lds));
+      const uint32_t kb = l_kb;
+      unroll_seq(
+          [&](auto jc) {
+            constexpr int J = decltype(jc)::value;
+            dma16_at(rOp, c_off[J], kb * kGroup, lds + chunk(J) * 1024);
+          },
+          std::make_integer_sequence<int, CH>{});
+      if constexpr (grp == 1) {
+        dma4_at(rS, s_off, kb * Mp * 4, lds + my_sc);
+        dma4_at(rS, s_off_p, kb * Mp * 4, lds + p_sc);
+        dma4_at(rWs, 0, ws_off + kb * 4, lds + my_sc + 256);
+        dma4_at(rWs, 0, ws_off + kb * 4, lds + p_sc + 256);
+      }
+      load_next();
+    };
+
+    const uint32_t l16 = lane & 15, c0 = 2 * (lane >> 4);
+    const uint32_t lo0 = l16 * 128 + ((c0 ^ swz(l16)) * 16);
+    const uint32_t lo1 = l16 * 128 + (((c0 + 1) ^ swz(l16)) * 16);
+    auto ld16 = [](const uint8_t* p) __attribute__((always_inline)) -> v4i { return *reinterpret_cast<const v4i*>(p); };
+    auto ldf = [](const uint8_t* p) __attribute__((always_inline)) -> float { return *reinterpret_cast<const float*>(p); };
+    const uint32_t a_row0 = wm * C::WM * 128, w_row0 = C::A_BYTES + wn * C::WN * 128;
+
+    v4f acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+    v8i af[TM], bf[TN];
+    float as[TM], ws = 0.0f, sc[TM], sc_tail = 0.0f;
+    v4f p[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) p[i] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+
+    auto read_block = [&](auto slot_c) __attribute__((always_inline)) {
+      const uint8_t* sb = smem + decltype(slot_c)::value * C::STAGE_BYTES;
+#pragma unroll
+      for (int tn = 0; tn < TN; ++tn) {
+        bf[tn].lo = ld16(sb + w_row0 + tn * 2048 + lo0);
+        bf[tn].hi = ld16(sb + w_row0 + tn * 2048 + lo1);
+      }
+#pragma unroll
+      for (int tm = 0; tm < TM; ++tm) {
+        af[tm].lo = ld16(sb + a_row0 + tm * 2048 + lo0);
+        af[tm].hi = ld16(sb + a_row0 + tm * 2048 + lo1);
+        as[tm] = ldf(sb + my_sc + (tm * 16 + l16) * 4);
+      }
+      ws = ldf(sb + my_sc + 256);
+    };
+    auto compute_block = [&]() __attribute__((always_inline)) {
+#pragma unroll
+      for (int tm = 0; tm < TM; ++tm) sc[tm] = as[tm] * ws;
+      unroll_seq(
+          [&](auto ic) {
+            constexpr int I = decltype(ic)::value;
+            constexpr int tm = I / TN, tn = I % TN;
+            p[I & 3] = mfma_e4m3_128(bf[tn], af[tm]);
+            // each promotion is pinned to its slot: with the segment-end
+            // branches after the block the compiler would otherwise sink them
+            // past the barrier (and keep every MFMA result live until then)
+            if constexpr (I < kPromoteDist) {
+              constexpr int J = NP - kPromoteDist + I;
+              acc[J / TN][J % TN] += p[J & 3] * sc_tail;
+              asm volatile("" : "+v"(acc[J / TN][J % TN]));
+            } else {
+              constexpr int J = I - kPromoteDist;
+              acc[J / TN][J % TN] += p[J & 3] * sc[J / TN];
+              asm volatile("" : "+v"(acc[J / TN][J % TN]));
+            }
+            sched_fence();
+          },
+          std::make_integer_sequence<int, NP>{});
+      sc_tail = sc[TM - 1];
+    };
+    // the promotions still pending after a tile's last block; the next
+    // block's pending slots then add zero
+    auto flush = [&]() __attribute__((always_inline)) {
+#pragma unroll
+      for (int j = NP - kPromoteDist; j < NP; ++j) acc[j / TN][j % TN] += p[j & 3] * sc_tail;
+      sc_tail = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) p[i] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+    };
+    // end of the compute cursor's segment: store, publish or finalize the
+    // tile, then clear the accumulators
+    auto epilogue = [&]() __attribute__((always_inline)) {
+      flush();
+      if (c_kb0 > 0) {
+        // a later piece of a split tile: publish the partial (device-coherent
+        // stores, complete before the flag is written)
+        const uint32_t u = unit_of(c_seg);
+        const uint32_t slot = (u % Tt) * (plan.pieces - 1) + u / Tt;
+        const uint32_t voff = ((slot * 8 + wave) * NP * 64 + lane) * 16;
+#pragma unroll
+        for (int i = 0; i < NP; ++i)
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[i / TN][i % TN]),
+                                                 rP, voff, i * 1024, kCoherent);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        if (lane == 0)
+          __hip_atomic_store(&sk.flags[slot * 8 + wave], sk.gen, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+      } else {
+        if (c_kb1 < G) {
+          // piece 0 of a tail tile: add the later pieces' partials.  Lane j
+          // polls the flag of piece j + 1 (all pieces at once); the partials
+          // are then read and added in piece order.  A
+          // flag is cleared once its partial has been read, so that a replay
+          // of the same launch (same generation number) waits afresh.
+          const uint32_t np = plan.pieces - 1, slot0 = (c_tile - plan.tail_base) * np;
+          unsigned long long* flag = &sk.flags[(slot0 + lane) * 8 + wave];
+          uint32_t ok = 1;
+          if (lane < np) {
+            uint32_t n = 0;
+            while (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != sk.gen) {
+              if (++n >= kSkSpinLimit) {
+                ok = 0;
+                break;
+              }
+              __builtin_amdgcn_s_sleep(2);
+            }
+          }
+          const float bad = __builtin_amdgcn_ballot_w64(ok == 0) == 0 ? 0.0f : __builtin_nanf("");
+          asm volatile("" ::: "memory");
+          // device-coherent loads of the partials
+          constexpr uint32_t vstride = 8 * NP * 64 * 16;  // from piece p to piece p + 1
+          uint32_t voff = ((slot0 * 8 + wave) * NP * 64 + lane) * 16;
+          for (uint32_t j = 0; j < np; ++j, voff += vstride) {
+#pragma unroll
+            for (int i = 0; i < NP; ++i)
+              acc[i / TN][i % TN] += __builtin_bit_cast(
+                                         v4f, __builtin_amdgcn_raw_buffer_load_b128(
+                                                  rP, voff, i * 1024, kCoherent)) +
+                                     bad;
+          }
+          if (lane < np && ok)
+            __hip_atomic_store(flag, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        uint32_t tmi, tni;
+        grouped_tile(c_tile, tiles_m, tiles_n, tmi, tni);
+        const uint32_t m0 = tmi * BM, n0 = tni * BN;
+#pragma unroll
+        for (int tm = 0; tm < TM; ++tm) {
+          const uint32_t m = m0 + wm * C::WM + tm * 16 + l16;
+          if (m < M) {
+#pragma unroll
+            for (int tn = 0; tn < TN; ++tn) {
+              const uint32_t n = n0 + wn * C::WN + tn * 16 + 4 * (lane >> 4);
+              *reinterpret_cast<uint2*>(out + (uint64_t)m * N + n) = pack_bf16x4(acc[tm][tn]);
+            }
+          }
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+    };
+
+    // One pipeline step on LDS slot S, in two halves split by a barrier.
+    // Group 0: compute the block read in the previous step | read the next
+    // slot, issue the loads of iteration i + 3.  Group 1: read slot S, issue
+    // | compute.  A segment's epilogue goes where the group holds nothing
+    // but its accumulators: for group 0 between the halves of the segment's
+    // last step (before it reads the next segment's first block), for
+    // group 1 after it.
+    auto half0 = [&](auto slot_c) __attribute__((always_inline)) {
+      constexpr int S = decltype(slot_c)::value;
+      if constexpr (grp == 0) {
+        compute_block();
+        wait_vmcnt<LW0>();
+        wg_barrier();
+      } else {
+        read_block(slot_c);
+        wait_lgkm0();
+        issue(S);
+        wait_vmcnt<2 * LW1>();
+        wg_barrier();
+      }
+    };
+    auto half1 = [&](auto slot_c) __attribute__((always_inline)) {
+      constexpr int S = decltype(slot_c)::value;
+      if constexpr (grp == 0) {
+        read_block(std::integral_constant<int, (S + 1) % STAGES>{});
+        wait_lgkm0();
+        issue(S);
+        wg_barrier();
+      } else {
+        compute_block();
+        wg_barrier();
+      }
+    };
+    auto step = [&](auto slot_c) __attribute__((always_inline)) {
+      half0(slot_c);
+      half1(slot_c);
+    };
+    // a half step on the slot known at run time
+    auto dispatch = [&](uint32_t sl, auto&& half) __attribute__((always_inline)) {
+      if (sl == 0)
+        half(std::integral_constant<int, 0>{});
+      else if (sl == 1)
+        half(std::integral_constant<int, 1>{});
+      else
+        half(std::integral_constant<int, 2>{});
+    };
+    // The last step of a segment, with its epilogue.  In the workgroup's
+    // final segment group 0 has no next block to hold, and runs its epilogue
+    // after the second half, at the same time as group 1 (a tail tile's
+    // final sum then costs one epilogue, not two in turn).
+    auto last_step = [&](uint32_t sl) __attribute__((always_inline)) {
+      const bool final_seg = c_seg + 1 >= n_seg;
+      dispatch(sl, half0);
+      if constexpr (grp == 0) {
+        if (!final_seg) epilogue();
+      }
+      dispatch(sl, half1);
+      if (grp == 1 || final_seg) epilogue();
+    };
+    using S0 = std::integral_constant<int, 0>;
+    using S1 = std::integral_constant<int, 1>;
+    using S2 = std::integral_constant<int, 2>;
+
+    // prologue: the first STAGES loads; group 0 reads slot 0
+#pragma unroll
+    for (int st = 0; st < STAGES; ++st) issue(st);
+    if constexpr (grp == 0) {
+      wait_vmcnt<(STAGES - 1) * LW0>();
+      wg_barrier();
+      read_block(S0{});
+      wait_lgkm0();
+      wg_barrier();
+    } else {
+      wait_vmcnt<(STAGES - 1) * LW1>();
+      wg_barrier();
+      wg_barrier();
+    }
+    // Iterations of each compute segment, i counting over the workgroup's
+    // iterations (slot i % 3): all but the segment's last through the loop
+    // unrolled by the three slots, the last one with the epilogue.
+    uint32_t i = 0;
+    while (true) {
+      const uint32_t last = i + (c_kb1 - c_kb0) - 1;
+      const uint32_t ph = i % 3;
+      if (ph == 1 && i < last) {
+        step(S1{});
+        ++i;
+      }
+      if (i % 3 == 2 && i < last) {
+        step(S2{});
+        ++i;
+      }
+      for (; i + 3 <= last; i += 3) {
+        step(S0{});
+        step(S1{});
+        step(S2{});
+      }
+      if (i < last) {
+        step(S0{});
+        ++i;
+      }
+      if (i < last) {
+        step(S1{});
+        ++i;
+      }
+      last_step(i % 3);
+      ++i;
+      if (c_seg + 1 >= n_seg) break;
+      segment(++c_seg, c_tile, c_kb0, c_kb1);
+    }
+    wait_vmcnt<0>();  // no direct load may still be writing LDS at exit
+  };
+  if (wave >> 2)
+    body(std::integral_constant<uint32_t, 1>{});
+  else
+    body(std::integral_constant<uint32_t, 0>{});
+}
+
+hipError_t launch_pp_sk_cfg(const uint8_t* a, const float* a_s_km, const uint8_t* w,
+                            const float* w_s, uint16_t* out, uint32_t M, uint32_t N, uint32_t K,
+                            const SkPlan& plan, const SkArgs& args, hipStream_t s) {
+  using C = PpCfg<3, false, false>;
+  static std::atomic<bool> attr_set{false};  // the call is idempotent: racing threads repeat it
+  if (!attr_set.load(std::memory_order_acquire)) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_pp_sk_kernel<3>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
+    if (e != hipSuccess) return e;
+    attr_set.store(true, std::memory_order_release);
+  }
+  const uint32_t tiles_m = (M + C::BM - 1) / C::BM, tiles_n = N / C::BN;
+  gemm_pp_sk_kernel<3><<<dim3(plan.C), dim3(C::NT), C::LDS_BYTES, s>>>(
+      a, a_s_km, w, w_s, out, M, N, K, m_pad16(M), tiles_m, tiles_n, plan, args);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------------
 // Skinny kernel for decode and small-batch widths.  Rows come in tiles of
 // 16*TM <= 64 (grid dimension y; beyond 64 rows every row tile streams the
 // weights again, mostly from the last-level cache).  The projection is then
@@ -1069,6 +1544,93 @@ hipError_t launch_splitk_128(const uint8_t* a, const float* a_s_km, const uint8_
                              uint32_t N, uint32_t K, uint32_t splits, uint32_t cus,
                              hipStream_t s) {
   return launch_splitk_128_t(a, a_s_km, w, w_s, out, part, M, N, K, splits, cus, s);
+}
+
+namespace {
+// Stream-K plan on `cus` CUs, or false where the data-parallel kernel is as
+// good: no tail (the tiles fill whole rounds), fewer tiles than CUs, a tail
+// round more than 90% full, or fewer than 4 tail iterations a workgroup.
+// The stream-K plan for M x N x K on cus workgroups, or false where the
+// data-parallel kernels are expected to be as fast (unless forced: then
+// wherever the structure allows one).  In units of one K
+// block's time: the longest workgroup runs R*G + crit + (P-1)*kSkPartialCost
+// + kSkPollCost (its own blocks, then reading P-1 partials and waiting on
+// their flags, measured at about 4.5 and 8 block times), against R*G +
+// G*max(Tt/cus, kSkLastWave) for the data-parallel kernel, whose last wave
+// of Tt tiles runs at a higher clock while the other CUs idle (the chip is
+// power-limited: 24 tiles alone took 0.73 of a full wave's time).  The plan
+// is kept where it is at least 10% shorter.  With more than cus/2 tail
+// tiles, P = 2: the S secondaries take the tiles' second pieces in r =
+// ceil(Tt/S) rounds, and b1 minimizes crit = max(b1, r*(G - b1)).  With
+// fewer, near-equal pieces, P in [2, min(cus/Tt, G, kSkMaxPieces)] chosen
+// for the least crit + (P-1)*kSkPartialCost, at most one unit per secondary.
+constexpr uint64_t kSkPartialCost = 5, kSkPollCost = 8;
+constexpr double kSkLastWave = 0.73;
+bool sk_make_plan(uint32_t M, uint32_t N, uint32_t K, uint32_t cus, bool forced, SkPlan& p) {
+  const uint64_t T = (uint64_t)((M + 255) / 256) * (N / 128), G = K / kGroup;
+  if (cus < 8 || cus % 8 != 0 || N % 128 != 0 || G < 2 || T <= cus || T % cus == 0)
+    return false;
+  const uint64_t R = T / cus, Tt = T % cus, S = cus - Tt;
+  uint64_t P = 2, b1, crit;
+  if (2 * Tt > cus) {
+    const uint64_t r = (Tt + S - 1) / S;
+    auto cost = [&](uint64_t b) { return std::max(b, r * (G - b)); };
+    b1 = std::min<uint64_t>(std::max<uint64_t>((r * G) / (r + 1), 1), G - 1);
+    if (b1 + 1 < G && cost(b1 + 1) < cost(b1)) ++b1;
+    crit = cost(b1);
+  } else {
+    const uint64_t pmax = std::min<uint64_t>(std::min<uint64_t>(cus / Tt, G), kSkMaxPieces);
+    auto cost = [&](uint64_t q) { return std::max(G / q, (G - G / q + q - 2) / (q - 1)); };
+    for (uint64_t q = 3; q <= pmax; ++q)
+      if (cost(q) + (q - 1) * kSkPartialCost < cost(P) + (P - 1) * kSkPartialCost) P = q;
+    b1 = G / P;
+    crit = cost(P);
+  }
+  const double sk = (double)(R * G + crit + (P - 1) * kSkPartialCost + kSkPollCost);
+  const double dp = (double)(R * G) + (double)G * std::max((double)Tt / cus, kSkLastWave);
+  if (!forced && sk > 0.9 * dp) return false;
+  p.C = cus;
+  p.rounds = (uint32_t)R;
+  p.tail_base = (uint32_t)(R * cus);
+  p.tail = (uint32_t)Tt;
+  p.pieces = (uint32_t)P;
+  p.b1 = (uint32_t)b1;
+  return true;
+}
+
+// generation numbers: a per-process random start, then one per call
+std::atomic<unsigned long long> g_sk_gen{0};
+unsigned long long sk_next_gen() {
+  static const unsigned long long base = [] {
+    unsigned long long v = (unsigned long long)std::chrono::steady_clock::now().time_since_epoch().count();
+    v ^= (unsigned long long)(uintptr_t)&g_sk_gen;
+    return v * 0x9E3779B97F4A7C15ull;
+  }();
+  return base + 0xD1B54A32D192ED03ull * (g_sk_gen.fetch_add(1, std::memory_order_relaxed) + 1);
+}
+
+uint64_t sk_flag_bytes(uint32_t cus) { return ((uint64_t)cus * 8 * 8 + 255) / 256 * 256; }
+}  // namespace
+
+bool gemm_streamk_applies(uint32_t M, uint32_t N, uint32_t K, uint32_t cus, bool forced) {
+  SkPlan p;
+  return sk_make_plan(M, N, K, cus, forced, p);
+}
+
+uint64_t gemm_streamk_workspace_bytes(uint32_t cus) {
+  return sk_flag_bytes(cus) + (uint64_t)cus * 8 * 16 * 64 * 16;
+}
+
+hipError_t launch_gemm_streamk(const uint8_t* a, const float* a_s_km, const uint8_t* w,
+                               const float* w_s, uint16_t* out, void* workspace, uint32_t M,
+                               uint32_t N, uint32_t K, uint32_t cus, bool forced, hipStream_t s) {
+  SkPlan plan;
+  if (!sk_make_plan(M, N, K, cus, forced, plan)) return hipErrorInvalidValue;
+  SkArgs args;
+  args.flags = static_cast<unsigned long long*>(workspace);
+  args.part = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + sk_flag_bytes(cus));
+  args.gen = sk_next_gen();
+  return launch_pp_sk_cfg(a, a_s_km, w, w_s, out, M, N, K, plan, args, s);
 }
 
 }  // namespace fp8q

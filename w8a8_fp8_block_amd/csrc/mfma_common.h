@@ -50,6 +50,23 @@ __device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, uint32_t voff, ui
                                            soff, 0, 0);
 }
 
+// The same with the LDS destination as a byte address in the workgroup's
+// LDS (for addresses formed at run time; no generic-pointer null check).
+__device__ __forceinline__ void dma16_at(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff,
+                                         uint32_t lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(size_t)lds,
+                                           16, voff, soff, 0, 0);
+}
+__device__ __forceinline__ void dma4_at(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff,
+                                        uint32_t lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(size_t)lds,
+                                           4, voff, soff, 0, 0);
+}
+// LDS byte address of a pointer into a __shared__ array
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(size_t)(const __attribute__((address_space(3))) void*)p;
+}
+
 __device__ __forceinline__ uint32_t swz(uint32_t r) { return (r & 7u) ^ ((r >> 3) & 1u); }
 
 // s_waitcnt vmcnt(n) leaving expcnt/lgkmcnt unconstrained (gfx9 encoding).
@@ -81,22 +98,30 @@ __device__ __forceinline__ void unroll_seq(F&& f, std::integer_sequence<int, Is.
   (f(std::integral_constant<int, Is>{}), ...);
 }
 
-// Tile of a workgroup in an XCD-aware, grouped order.  Workgroup ids are
-// dealt round-robin to the 8 XCDs; each XCD gets a contiguous run of tile
-// ids so that the tiles it runs together share its L2, and tile ids walk
-// blocks of GROUP_M tile rows, N fastest inside a block.
-__device__ __forceinline__ void tile_coords(uint32_t tiles_m, uint32_t tiles_n, uint32_t& tmi,
-                                            uint32_t& tni) {
-  const uint32_t ntiles = tiles_m * tiles_n;
-  const uint32_t bid = blockIdx.x, xcd = bid & 7, slot = bid >> 3;
-  const uint32_t q = ntiles >> 3, r8 = ntiles & 7;
-  const uint32_t t = (xcd < r8) ? xcd * (q + 1) + slot : r8 * (q + 1) + (xcd - r8) * q + slot;
+// Tile t of the grouped order: tile ids walk blocks of GROUP_M tile rows, N
+// fastest inside a block, so that the tiles that run together share their
+// activation rows and weight columns.
+__device__ __forceinline__ void grouped_tile(uint32_t t, uint32_t tiles_m, uint32_t tiles_n,
+                                             uint32_t& tmi, uint32_t& tni) {
   constexpr uint32_t GROUP_M = 8;
   const uint32_t per_group = GROUP_M * tiles_n;
   const uint32_t group = t / per_group, first_m = group * GROUP_M;
   const uint32_t gm = min(tiles_m - first_m, GROUP_M);
   tmi = first_m + (t % per_group) % gm;
   tni = (t % per_group) / gm;
+}
+
+// Tile of a workgroup in an XCD-aware, grouped order.  Workgroup ids are
+// dealt round-robin to the 8 XCDs; each XCD gets a contiguous run of tile
+// ids so that the tiles it runs together share its L2, and tile ids follow
+// the grouped order above.
+__device__ __forceinline__ void tile_coords(uint32_t tiles_m, uint32_t tiles_n, uint32_t& tmi,
+                                            uint32_t& tni) {
+  const uint32_t ntiles = tiles_m * tiles_n;
+  const uint32_t bid = blockIdx.x, xcd = bid & 7, slot = bid >> 3;
+  const uint32_t q = ntiles >> 3, r8 = ntiles & 7;
+  const uint32_t t = (xcd < r8) ? xcd * (q + 1) + slot : r8 * (q + 1) + (xcd - r8) * q + slot;
+  grouped_tile(t, tiles_m, tiles_n, tmi, tni);
 }
 
 // Split-K form: the grid holds splits workgroups per tile.  Workgroup ids
@@ -110,13 +135,7 @@ __device__ __forceinline__ void tile_split_coords(uint32_t tiles_m, uint32_t til
   const uint32_t q = nslots >> 3, r8 = nslots & 7;
   const uint32_t v = (xcd < r8) ? xcd * (q + 1) + slot : r8 * (q + 1) + (xcd - r8) * q + slot;
   split = v % splits;
-  const uint32_t t = v / splits;
-  constexpr uint32_t GROUP_M = 8;
-  const uint32_t per_group = GROUP_M * tiles_n;
-  const uint32_t group = t / per_group, first_m = group * GROUP_M;
-  const uint32_t gm = min(tiles_m - first_m, GROUP_M);
-  tmi = first_m + (t % per_group) % gm;
-  tni = (t % per_group) / gm;
+  grouped_tile(v / splits, tiles_m, tiles_n, tmi, tni);
 }
 
 }  // namespace
