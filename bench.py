@@ -64,7 +64,7 @@ BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
 # readings for a plain 1 GiB copy (the HBM-bytes summary under profiles/).
 # Valid only for the kernel source they were taken with: reported as null
 # once the ping-pong kernel's source changes (gemm_source_hash).
-GEMM_TRAFFIC = {"bytes": 1.2274e+09 + 4.7088e+07, "gemm_source_sha256": "e3d4b625424f3c35"}
+GEMM_TRAFFIC = {"bytes": 1.1792e+09 + 4.7075e+07, "gemm_source_sha256": "95986a9d81cfde74"}
 
 
 def gemm_source_hash():
@@ -117,10 +117,103 @@ def parse():
                    help="instead of the benchmark, time the CPU oracle on the host cores: "
                         "quantizer + relayout per quantizer-sweep shape (all threads and one), "
                         "fp64 GEMM per GEMM workload (no GPU used)")
+    p.add_argument("--streamk-sweep", action="store_true",
+                   help="instead of the benchmark, the stream-K GEMM against the single-pass "
+                        "kernels at the shapes its automatic rule was fixed on")
+    p.add_argument("--quant-vs-copy", action="store_true",
+                   help="instead of the benchmark, the quantizer (variant A) and a plain device "
+                        "copy of its input at the M >= 1168 sweep shapes, 20 launches each after "
+                        "a 1 GiB read that evicts the caches (for a kernel trace)")
     p.add_argument("--copy-mib", type=int, default=0,
                    help="instead of the benchmark, run 3 plain device copies of this many "
                         "MiB (the reference kernel for scaling rocprofv3 byte counters)")
     return p.parse_args()
+
+
+def streamk_sweep(R=20, rounds=5):
+    """The stream-K form of the 256x128 GEMM (fp8q_gemm_blockscaled_streamk,
+    one workgroup per CU) against the single-pass kernels: the automatic one
+    and the ping-pong kernel (id 5), graph-timed back-to-back launches over
+    rotating weight copies (each launch streams its weights from HBM), the
+    three variants taking turns `rounds` times (median).  The shapes are the
+    ones the automatic stream-K rule was fixed on: a last round of few tiles
+    and a long K (M = 1792 and 2560), and shapes where most CUs have a tile
+    in the last round (the two prefill projections among them).  Random FP8
+    codes (no NaN code), scales uniform in [0, 0.01)."""
+    import torch
+    import w8a8_fp8_block_amd as fp8q
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(11)
+    work = torch.empty((fp8q.fp8q_gemm_streamk_workspace_bytes(0),), dtype=torch.uint8, device=dev)
+
+    def codes(shape):
+        c = torch.randint(0, 256, shape, generator=gen, dtype=torch.uint8, device=dev)
+        c[(c & 0x7F) == 0x7F] = 0
+        return c
+
+    for M, N, K in ((1792, 5120, 17408), (2560, 6656, 17408), (2304, 5120, 17408),
+                    (2048, 8448, 8192), (3072, 4224, 17408), (4576, 5120, 17408),
+                    (1168, 17408, 5120)):
+        a = codes((M, K))
+        km = torch.rand((K // 128, fp8q.fp8q_m_pad(M)), generator=gen, device=dev) * 0.01
+        w_rot = _rotation(codes((N, K)))
+        ws = torch.rand((N // 128, K // 128), generator=gen, device=dev) * 0.01
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        fns = {
+            "auto": lambda i: fp8q.fp8q_gemm_blockscaled(a, km, w_rot[i % len(w_rot)], ws, out),
+            "pingpong": lambda i: fp8q.fp8q_gemm_blockscaled(a, km, w_rot[i % len(w_rot)], ws, out,
+                                                             kernel=5),
+            "streamk": lambda i: fp8q.fp8q_gemm_blockscaled_streamk(a, km, w_rot[i % len(w_rot)], ws,
+                                                                     out, work),
+        }
+        ts = {k: [] for k in fns}
+        for _ in range(rounds):
+            for k, fn in fns.items():
+                ts[k].append(_b2b_us(fn, R)[0])
+        t = {k: round(float(np.median(v)), 2) for k, v in ts.items()}
+        tiles = (M + 255) // 256 * (N // 128)
+        print(json.dumps({"M": M, "N": N, "K": K, "tiles_256x128": tiles,
+                          "auto_kernel": fp8q.fp8q_gemm_select(M, N, K),
+                          "streamk_auto": fp8q.fp8q_gemm_streamk_select(M, N, K),
+                          "us": t, "streamk_vs_best_single_pass":
+                              round(t["streamk"] / min(t["auto"], t["pingpong"]), 3)}), flush=True)
+        del a, km, w_rot, ws, out
+        torch.cuda.empty_cache()
+
+
+def quant_vs_copy(reps=20):
+    """The quantizer (variant A, row-major scales) beside a plain device copy
+    of its bf16 input (torch's copy kernel: 2MK bytes read, 2MK written) at
+    the act-quant sweep's M >= 1168 shapes, `reps` launches of each, every one
+    after a sum over a 1 GiB buffer (a read, so no write-back of the eviction
+    is still draining when the kernel starts).  The durations come from a
+    kernel trace of this run; the launches of each shape and kind are
+    consecutive, in the order of the JSON lines printed."""
+    import torch
+    import synth
+    import w8a8_fp8_block_amd as fp8q
+    dev = torch.device("cuda:0")
+    big = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    sweep = synth.WORKLOADS["quant_sweep"]
+    for K in sorted({w.K for w in sweep}):
+        base = next(w for w in sweep if w.K == K)
+        for M in sorted({w.M for w in sweep if w.M >= 1168}):
+            x = torch.from_numpy(synth.make_inputs(base, M=M, with_weights=False)[0]
+                                 .view(np.int16)).to(dev)
+            q = torch.empty((M, K), dtype=torch.uint8, device=dev)
+            sc = torch.empty((M, K // 128), dtype=torch.float32, device=dev)
+            y = torch.empty_like(x)
+            for _ in range(reps):
+                torch.sum(big)
+                fp8q.fp8q_quant_act(x, q, sc, variant=1)
+            for _ in range(reps):
+                torch.sum(big)
+                y.copy_(x)
+            torch.cuda.synchronize()
+            print(json.dumps({"M": M, "K": K, "quant_bytes": quant_bytes(M, K),
+                              "copy_bytes": 4 * M * K, "launches": reps}), flush=True)
+            del x, q, sc, y
 
 
 def copy_calibration(mib: int):
@@ -959,6 +1052,12 @@ def main():
         return
     if args.quant_sweep:
         quant_sweep()
+        return
+    if args.quant_vs_copy:
+        quant_vs_copy()
+        return
+    if args.streamk_sweep:
+        streamk_sweep()
         return
     if args.dequant:
         dequant_bench()

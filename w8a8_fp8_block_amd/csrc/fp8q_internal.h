@@ -24,12 +24,18 @@ constexpr uint32_t kQuantAGroupsPerWg = 8 * kQuantAWaves;
 constexpr uint32_t kQuantBWaves = 4;
 constexpr uint32_t kQuantBRounds = 2;
 constexpr uint32_t kQuantBGroupsPerWg = 4 * kQuantBWaves * kQuantBRounds;
-// Floor of the selection rule on gfx950 (workgroups per CU).
+// Floor of the selection rule (workgroups per CU variant B's grid must
+// reach before it may run).  The value is the page's: on gfx950 there is no
+// crossover to derive another one from.  Timed by kernel duration over the
+// 30 shapes of the token/K sweep (M in 16..16384, K in 5120/6144/17408, cold
+// input), B was never faster than A by more than 0.1 us, and it was 12-33%
+// slower from M = 4576 on, where its grid (9152-81920 workgroups on 256 CUs)
+// fills the device many times over.  The floor only matters where B is
+// requested.
 constexpr uint32_t kQuantMinWgPerCu = 2;
-// Target default of the lever that lets variant B run at all.  Off on
-// gfx950: timed with a cache flush before every launch over the token/K
-// sweep (M in 16..16384, K in 5120/6144/17408), B was never faster than A by
-// more than 0.1 us and was 3-15% slower wherever its grid fills the device.
+// Target default of the lever that lets variant B run at all: off on gfx950,
+// for the measurements above (FP8Q_QUANT_VARIANT=floor requests B, "b"
+// forces it).
 constexpr bool kQuantBRequestedByDefault = false;
 
 // Quantizer variants A and B: codes q [M,K], row-major scales scale_rm
