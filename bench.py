@@ -399,7 +399,7 @@ def ffn_bench(name: str, M=None, reps=20):
     res["silu_mul_quant_frac_hbm"] = round(nbytes / t / 1e3 / HBM_PEAK_GBS, 4)
     fp8q.fp8q_ffn_gate_up(xq, xkm, gq, gs, uq, us, hq, hkm)
     res["down_gemm_us"] = round(timed(lambda: fp8q.fp8q_gemm_blockscaled(hq, hkm, dq, ds, out)), 2)
-    res["down_kernel"] = fp8q.GEMM_KERNEL_NAMES[fp8q.fp8q_gemm_select(M, H, I)]
+    res["down_kernel"] = fp8q.fp8q_gemm_kernel_name(M, H, I)
     print(json.dumps(res), flush=True)
 
 
@@ -790,7 +790,7 @@ def measure_projection(w, steps, warmup, per_row=False, comparators=False, cpu_b
     work = None
     if per_row:
         gemm = fp8q.fp8q_gemm_rowscaled
-        gemm_name = fp8q.GEMM_KERNEL_NAMES[fp8q.fp8q_gemm_select(M, N, K)]
+        gemm_name = fp8q.fp8q_gemm_kernel_name(M, N, K) + " (its per-row weight-scale form)"
     else:
         need = fp8q.fp8q_gemm_splitk_workspace_bytes(M, N, K, 0)
         work = torch.empty((max(need, 16),), dtype=torch.uint8, device=dev)
@@ -802,7 +802,7 @@ def measure_projection(w, steps, warmup, per_row=False, comparators=False, cpu_b
         elif fp8q.fp8q_gemm_splitk_select(M, N, K) >= 2:
             gemm_name = "+".join(fp8q.SPLITK_KERNEL_NAMES)
         else:
-            gemm_name = fp8q.GEMM_KERNEL_NAMES[fp8q.fp8q_gemm_select(M, N, K)]
+            gemm_name = fp8q.fp8q_gemm_kernel_name(M, N, K)
     act_q, act_s, act_km = fp8q.alloc_proj_scratch(M, K)
     out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
     stream = torch.cuda.current_stream()

@@ -214,6 +214,14 @@ int fp8q_gemm_select_cus(uint32_t M, uint32_t N, uint32_t K, uint32_t cu_count);
  * the launching entry points make on that device. */
 int fp8q_gemm_select(uint32_t M, uint32_t N, uint32_t K);
 
+/* The name, with its template arguments as a kernel trace shows it, of the
+ * kernel fp8q_gemm_blockscaled_ex launches for this shape with this kernel
+ * id (0 = the automatic choice) on the current device; for id 2 the decode
+ * kernel (gemm_decode_kernel, where a workgroup's weight slice fits in LDS)
+ * or the fragment-layout skinny kernel.  "" for a bad N, K or id.  Host
+ * function; the string is valid until the calling thread's next call. */
+const char *fp8q_gemm_kernel_name(uint32_t M, uint32_t N, uint32_t K, int kernel);
+
 /* As fp8q_gemm_blockscaled with the kernel forced: 0 = auto (2 for
  * M <= 64 and for M <= 128 when N <= 8192, 1 below 512 rows; from 512 rows
  * on 5 or 1, whichever needs fewer rounds of workgroups on the device's CUs

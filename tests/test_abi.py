@@ -476,3 +476,21 @@ def test_streamk_validation():
     assert f(g, g, g, g, g, g, need - 1, 300, 640, 1024, 8, None) == 2
     assert "workspace" in _err()
     assert f(g, g, g, g, g, None, 0, 0, 640, 1024, 8, None) == 0            # M == 0
+
+
+def test_gemm_kernel_name():
+    """The kernel names the benchmark line and the profiles use, as a kernel
+    trace shows them (no device here: 256 CUs assumed)."""
+    name = fp8q.fp8q_gemm_kernel_name
+    # decode widths at N = 6144, K = 5120: 24 columns a workgroup, 5 K blocks a wave
+    assert name(16, 6144, 5120) == "gemm_decode_kernel<1, 5, false>"
+    assert name(25, 6144, 5120) == "gemm_decode_kernel<2, 5, false>"
+    assert name(16, 256, 512) == "gemm_decode_kernel<1, 2, false>"
+    # wider slices (68 columns), more rows, or longer K: the fragment-layout kernel
+    assert name(16, 17408, 5120) == "gemm_skinny_kernel<1, 6, 8, 2, false>"
+    assert name(64, 6144, 5120) == "gemm_skinny_kernel<4, 2, 8, 2, false>"
+    assert name(16, 5120, 17408).startswith("gemm_skinny_kernel<")
+    assert name(4576, 5120, 17408) == "gemm_pp_kernel<3, false, false>"
+    assert name(300, 512, 896) == "gemm_tiled_kernel<128, 128, 2, 2, 2, false, false>"
+    assert name(4576, 5120, 17408, 1) == "gemm_tiled_kernel<128, 128, 2, 2, 2, false, false>"
+    assert name(16, 100, 512) == "" and name(16, 128, 512, 9) == ""

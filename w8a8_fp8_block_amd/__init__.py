@@ -78,6 +78,7 @@ _SIGS = {
     "fp8q_gemm_streamk_select_cus": (_I, [_U, _U, _U, _U]),
     "fp8q_gemm_splitk_workspace_bytes": (_SZ, [_U, _U, _U, _U]),
     "fp8q_gemm_blockscaled_streamk": (_I, [_P, _P, _P, _P, _P, _P, _SZ, _U, _U, _U, _U, _P]),
+    "fp8q_gemm_kernel_name": (ctypes.c_char_p, [_U, _U, _U, _I]),
     "fp8q_gemm_streamk_workspace_bytes": (_SZ, [_U]),
     "fp8q_gemm_blockscaled_splitk_noalloc": (_I, [_P, _P, _P, _P, _P, _U, _U, _U, _U, _P]),
     "fp8q_clock_stamp": (_I, [_P, _U, _P]),
@@ -401,11 +402,14 @@ def fp8q_proj_quant_fused(M: int, K: int) -> bool:
     return bool(lib().fp8q_proj_quant_fused(M, K))
 
 
-GEMM_KERNEL_NAMES = {1: "gemm_tiled_kernel<128,128,2,2,2>", 2: "gemm_skinny_kernel",
-                     3: "gemm_tiled_kernel<256,128,4,2,3>", 4: "gemm_tiled_kernel<256,128,2,2,3>",
-                     5: "gemm_pp_kernel<3,false,false>"}
-FFN_GATE_UP_KERNEL_NAME = "gemm_pp_kernel<3,false,true>"
-SPLITK_KERNEL_NAMES = ("gemm_tiled_kernel<128,128,2,2,2,false,true>", "splitk_reduce_kernel")
+def fp8q_gemm_kernel_name(M: int, N: int, K: int, kernel: int = 0) -> str:
+    """Name (as a kernel trace shows it) of the kernel fp8q_gemm_blockscaled
+    runs for this shape and kernel id (0 = automatic) on the current device."""
+    return lib().fp8q_gemm_kernel_name(M, N, K, kernel).decode()
+
+
+FFN_GATE_UP_KERNEL_NAME = "gemm_pp_kernel<3, false, true>"
+SPLITK_KERNEL_NAMES = ("gemm_tiled_kernel<128, 128, 2, 2, 2, false, true>", "splitk_reduce_kernel")
 STREAMK_KERNEL_NAME = "gemm_pp_sk_kernel<3>"
 
 

@@ -850,6 +850,23 @@ int fp8q_gemm_select(uint32_t M, uint32_t N, uint32_t K) {
   return fp8q_gemm_select_cus(M, N, K, current_cus());
 }
 
+const char* fp8q_gemm_kernel_name(uint32_t M, uint32_t N, uint32_t K, int kernel) {
+  static thread_local char buf[96];
+  const uint32_t cus = current_cus();
+  if (N == 0 || N % kGroup != 0 || K == 0 || K % kGroup != 0 || kernel < 0 || kernel > 5)
+    return "";
+  if (kernel == 0) kernel = gemm_auto_kernel(M, N, cus);
+  switch (kernel) {
+    case 1: return "gemm_tiled_kernel<128, 128, 2, 2, 2, false, false>";
+    case 3: return "gemm_tiled_kernel<256, 128, 4, 2, 3, false, false>";
+    case 4: return "gemm_tiled_kernel<256, 128, 2, 2, 3, false, false>";
+    case 5: return "gemm_pp_kernel<3, false, false>";
+    default:
+      gemm_skinny_kernel_name(M, N, K, cus, false, buf, sizeof buf);
+      return buf;
+  }
+}
+
 fp8q_status fp8q_gemm_blockscaled(const uint8_t* a_e4m3, const float* a_scale_km,
                                   const uint8_t* w_e4m3, const float* w_scale, uint16_t* out_bf16,
                                   uint32_t M, uint32_t N, uint32_t K, hipStream_t stream) {

@@ -85,6 +85,10 @@ hipError_t launch_gemm_streamk(const uint8_t* a, const float* a_s_km, const uint
 hipError_t launch_gemm_skinny(const uint8_t* a, const float* a_s_km, const uint8_t* w,
                               const float* w_s, uint16_t* out, uint32_t M, uint32_t N,
                               uint32_t K, uint32_t cu_count, bool row_scaled, hipStream_t s);
+// Name (with template arguments) of the kernel launch_gemm_skinny runs for
+// this shape: the decode kernel or the fragment-layout skinny kernel.
+void gemm_skinny_kernel_name(uint32_t M, uint32_t N, uint32_t K, uint32_t cu_count,
+                             bool row_scaled, char* buf, size_t len);
 
 // bf16 comparator GEMM: out[M,N] = bf16(x[M,K] . w[N,K]^T), N % 128 == 0,
 // K % 64 == 0.

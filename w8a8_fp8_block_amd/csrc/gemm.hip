@@ -1600,31 +1600,56 @@ hipError_t launch_decode_cfg(const uint8_t* a, const float* a_s_km, const uint8_
   return hipGetLastError();
 }
 
+// Whether the decode kernel takes the shape (its limits: at most 32 rows and
+// kDecodeMaxRows columns a workgroup, 48 K blocks, the slice within
+// kDecodeLds), and then its template arguments and LDS bytes.
+bool decode_plan(uint32_t M, uint32_t K, uint32_t base, uint32_t rem, uint32_t& tm, uint32_t& gw,
+                 uint32_t& lds) {
+  const uint32_t rmax = 4 * (base + (rem ? 1 : 0)), g = (K / kGroup + 7) / 8;
+  const uint64_t l = std::max<uint64_t>((uint64_t)rmax * (K + 16), 8 * 2 * 2 * 64 * 16);
+  if (M > 32 || rmax > kDecodeMaxRows || g > 6 || l > kDecodeLds) return false;
+  tm = M <= 16 ? 1 : 2;
+  gw = g <= 2 ? 2 : g <= 4 ? 4 : g == 5 ? 5 : 6;
+  lds = (uint32_t)l;
+  return true;
+}
+
 // the decode kernel where its shape limits hold (else false)
 template <bool ROW>
 bool launch_decode(const uint8_t* a, const float* a_s_km, const uint8_t* w, const float* w_s,
                    uint16_t* out, uint32_t M, uint32_t N, uint32_t K, uint32_t grid,
                    uint32_t base, uint32_t rem, hipStream_t s, hipError_t& err) {
-  const uint32_t rmax = 4 * (base + (rem ? 1 : 0)), G = K / kGroup, gw = (G + 7) / 8;
-  const uint64_t lds = std::max<uint64_t>((uint64_t)rmax * (K + 16), 8 * 2 * 2 * 64 * 16);
-  if (M > 32 || rmax > kDecodeMaxRows || gw > 6 || lds > kDecodeLds) return false;
-  const uint32_t l = (uint32_t)lds;
+  uint32_t tm = 0, gw = 0, l = 0;
+  if (!decode_plan(M, K, base, rem, tm, gw, l)) return false;
 #define FP8Q_DECODE(TM_, GW_) \
   err = launch_decode_cfg<TM_, GW_, ROW>(a, a_s_km, w, w_s, out, M, N, K, grid, base, rem, l, s)
-  if (M <= 16) {
-    if (gw <= 2) FP8Q_DECODE(1, 2);
-    else if (gw <= 4) FP8Q_DECODE(1, 4);
+  if (tm == 1) {
+    if (gw == 2) FP8Q_DECODE(1, 2);
+    else if (gw == 4) FP8Q_DECODE(1, 4);
     else if (gw == 5) FP8Q_DECODE(1, 5);
     else FP8Q_DECODE(1, 6);
   } else {
-    if (gw <= 2) FP8Q_DECODE(2, 2);
-    else if (gw <= 4) FP8Q_DECODE(2, 4);
+    if (gw == 2) FP8Q_DECODE(2, 2);
+    else if (gw == 4) FP8Q_DECODE(2, 4);
     else if (gw == 5) FP8Q_DECODE(2, 5);
     else FP8Q_DECODE(2, 6);
   }
 #undef FP8Q_DECODE
   return true;
 }
+
+constexpr int skinny_waves(int tm, int tn) {
+  return (64 / (tn * tm) >= 8) ? 8 : (64 / (tn * tm) >= 4) ? 4 : 2;
+}
+constexpr int skinny_unroll(int tm, int tn) {
+  const int fixed = 4 * tn * tm + 4 * tn + 3 * tm + 20, per = 9 * tn + 9 * tm;
+  const int uf = ((skinny_waves(tm, tn) == 8 ? 200 : 440) - fixed) / per;
+  return uf > 8 ? 8 : uf < 1 ? 1 : uf;
+}
+// the template arguments the skinny dispatch picks: row tiles TM of 16 rows,
+// column tiles TN of 16 columns
+uint32_t skinny_tm(uint32_t M) { return M <= 16 ? 1 : M <= 32 ? 2 : 4; }
+uint32_t skinny_tn(uint32_t tn) { return tn <= 2 ? 2 : tn <= 4 ? 4 : tn <= 6 ? 6 : 8; }
 
 template <int TM, int TN, bool ROW>
 hipError_t launch_skinny_tn(const uint8_t* a, const float* a_s_km, const uint8_t* w,
@@ -1633,12 +1658,8 @@ hipError_t launch_skinny_tn(const uint8_t* a, const float* a_s_km, const uint8_t
   // static LDS for the partial sums: NWV*TN*TM KB <= 64 KB.  Registers: about
   // 4*TN*TM accumulators + 4*TN + 3*TM + 20 fixed, 9*TN + 9*TM per K block in
   // flight, within ~200 (two waves per SIMD, NWV = 8) or ~440 (one wave).
-  constexpr int NWV = (64 / (TN * TM) >= 8) ? 8 : (64 / (TN * TM) >= 4) ? 4 : 2;
-  constexpr int FIXED = 4 * TN * TM + 4 * TN + 3 * TM + 20;
-  constexpr int PER = 9 * TN + 9 * TM;
-  constexpr int BUDGET = NWV == 8 ? 200 : 440;
-  constexpr int UF = (BUDGET - FIXED) / PER;
-  constexpr int U = UF > 8 ? 8 : UF < 1 ? 1 : UF;
+  constexpr int NWV = skinny_waves(TM, TN);
+  constexpr int U = skinny_unroll(TM, TN);
   static_assert(NWV * TN * TM <= 64, "LDS for the partial sums");
   const uint32_t row_tiles = (M + 16 * TM - 1) / (16 * TM);
   gemm_skinny_kernel<TM, TN, NWV, U, ROW><<<dim3(grid, row_tiles), dim3(64 * NWV), 0, s>>>(
@@ -1673,22 +1694,30 @@ hipError_t launch_gemm_tiled_t(const uint8_t* a, const float* a_s_km, const uint
   }
 }
 
+// The skinny path's grid.  Up to 64 rows (one row tile): one workgroup per
+// CU, at most 128 columns each, at least 16.  Beyond (several row tiles,
+// each streaming the weights again): workgroups of 64 columns, so that a row
+// tile re-reads the activations once per 64 columns rather than once per CU
+// (measured at M = 128, N = 5120, K = 17408: 90 us with 64-column
+// workgroups, 108 us with one per CU, 117 us for the ping-pong kernel).
+// Workgroup w owns 4*(base + (w < rem)) columns; tn 16-column tiles at most.
+void skinny_grid(uint32_t M, uint32_t N, uint32_t cu_count, uint32_t& grid, uint32_t& base,
+                 uint32_t& rem, uint32_t& tn) {
+  const uint32_t units = N / 4;
+  grid = max(cu_count, (N + 127) / 128);
+  grid = max(1u, min(grid, N / 16));
+  if (M > 64) grid = N / 64;
+  base = units / grid;
+  rem = units % grid;
+  tn = (4 * (base + (rem ? 1 : 0)) + 15) / 16;
+}
+
 template <bool ROW>
 hipError_t launch_gemm_skinny_t(const uint8_t* a, const float* a_s_km, const uint8_t* w,
                                 const float* w_s, uint16_t* out, uint32_t M, uint32_t N,
                                 uint32_t K, uint32_t cu_count, hipStream_t s) {
-  // Up to 64 rows (one row tile): one workgroup per CU, at most 128 columns
-  // each, at least 16.  Beyond (several row tiles, each streaming the
-  // weights again): workgroups of 64 columns, so that a row tile re-reads
-  // the activations once per 64 columns rather than once per CU (measured
-  // at M = 128, N = 5120, K = 17408: 90 us with 64-column workgroups, 108 us
-  // with one per CU, 117 us for the ping-pong kernel).
-  const uint32_t units = N / 4;
-  uint32_t grid = max(cu_count, (N + 127) / 128);
-  grid = max(1u, min(grid, N / 16));
-  if (M > 64) grid = N / 64;
-  const uint32_t base = units / grid, rem = units % grid;
-  const uint32_t tn = (4 * (base + (rem ? 1 : 0)) + 15) / 16;
+  uint32_t grid = 0, base = 0, rem = 0, tn = 0;
+  skinny_grid(M, N, cu_count, grid, base, rem, tn);
   hipError_t err = hipSuccess;
   if (launch_decode<ROW>(a, a_s_km, w, w_s, out, M, N, K, grid, base, rem, s, err)) return err;
   switch ((M + 15) / 16) {
@@ -1711,6 +1740,20 @@ hipError_t launch_gemm_skinny(const uint8_t* a, const float* a_s_km, const uint8
                               uint32_t cu_count, bool row_scaled, hipStream_t s) {
   return row_scaled ? launch_gemm_skinny_t<true>(a, a_s_km, w, w_s, out, M, N, K, cu_count, s)
                     : launch_gemm_skinny_t<false>(a, a_s_km, w, w_s, out, M, N, K, cu_count, s);
+}
+
+void gemm_skinny_kernel_name(uint32_t M, uint32_t N, uint32_t K, uint32_t cu_count,
+                             bool row_scaled, char* buf, size_t len) {
+  uint32_t grid = 0, base = 0, rem = 0, tn = 0, tm = 0, gw = 0, lds = 0;
+  skinny_grid(M, N, cu_count, grid, base, rem, tn);
+  const char* row = row_scaled ? "true" : "false";
+  if (decode_plan(M, K, base, rem, tm, gw, lds)) {
+    snprintf(buf, len, "gemm_decode_kernel<%u, %u, %s>", tm, gw, row);
+  } else {
+    const int t = (int)skinny_tm(M), n = (int)skinny_tn(tn);
+    snprintf(buf, len, "gemm_skinny_kernel<%d, %d, %d, %d, %s>", t, n, skinny_waves(t, n),
+             skinny_unroll(t, n), row);
+  }
 }
 
 hipError_t launch_ffn_gate_up(const uint8_t* x, const float* x_s_km, const uint8_t* w_gate,
