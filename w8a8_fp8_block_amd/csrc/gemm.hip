@@ -682,7 +682,15 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(
   // read this wave's fragments and scales from LDS slot S (18 LDS reads);
   // the slot is a compile-time constant, so every address is a loop-invariant
   // register plus an immediate offset
-  auto read_block = [&](auto slot_c) {
+  // 16-row sub-tiles of this wave's band that hold rows below M (all TM
+  // but in a last row tile that M ends inside; uniform over the wave)
+  const uint32_t band0 = m0 + wm * C::WM;
+  const uint32_t vt = FFN ? TM : (M <= band0 ? 0u : min((uint32_t)TM, (M - band0 + 15) / 16));
+  // read this wave's fragments and scales from LDS slot S (18 LDS reads);
+  // the slot is a compile-time constant, so every address is a loop-invariant
+  // register plus an immediate offset.  Partial bands (FULL false) skip the
+  // activation fragments of sub-tiles past M.
+  auto read_block = [&](auto slot_c, auto full_c) {
     const uint8_t* sb = smem + decltype(slot_c)::value * C::STAGE_BYTES;
 #pragma unroll
     for (int tn = 0; tn < TN; ++tn) {
@@ -691,35 +699,43 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(
     }
 #pragma unroll
     for (int tm = 0; tm < TM; ++tm) {
-      af[tm].lo = ld16(sb + a_row0 + tm * 2048 + lo0);
-      af[tm].hi = ld16(sb + a_row0 + tm * 2048 + lo1);
-      as[tm] = ldf(sb + my_sc + (tm * 16 + l16) * 4);
+      if (decltype(full_c)::value || (uint32_t)tm < vt) {
+        af[tm].lo = ld16(sb + a_row0 + tm * 2048 + lo0);
+        af[tm].hi = ld16(sb + a_row0 + tm * 2048 + lo1);
+        as[tm] = ldf(sb + my_sc + (tm * 16 + l16) * 4);
+      }
     }
     ws = ROW ? 1.0f : ldf(sb + my_sc + 256);
   };
   // MFMAs and promotions of the block in registers; the promotions of its
   // last kPromoteDist MFMAs are left pending for the next block's compute
-  // phase.
-  auto compute_block = [&]() {
+  // phase.  A partial band runs only the MFMAs of its sub-tiles below M
+  // (the others' accumulators hold rows that are never stored): in a last
+  // row tile that M ends inside, the group's compute phase shrinks and the
+  // matrix pipe spends no power on rows past M.
+  auto compute_block = [&](auto full_c) {
+    constexpr bool FULL = decltype(full_c)::value;
 #pragma unroll
     for (int tm = 0; tm < TM; ++tm) sc[tm] = as[tm] * ws;
     unroll_seq(
         [&](auto ic) {
           constexpr int I = decltype(ic)::value;
           constexpr int tm = I / TN, tn = I % TN;
-          p[I & 3] = mfma_e4m3_128(bf[tn], af[tm]);
+          if (FULL || (uint32_t)tm < vt) p[I & 3] = mfma_e4m3_128(bf[tn], af[tm]);
           if constexpr (I < kPromoteDist) {
             constexpr int J = NP - kPromoteDist + I;
-            acc[J / TN][J % TN] += p[J & 3] * sc_tail;
+            if (FULL || (uint32_t)(J / TN) < vt) acc[J / TN][J % TN] += p[J & 3] * sc_tail;
           } else {
             constexpr int J = I - kPromoteDist;
-            acc[J / TN][J % TN] += p[J & 3] * sc[J / TN];
+            if (FULL || (uint32_t)(J / TN) < vt) acc[J / TN][J % TN] += p[J & 3] * sc[J / TN];
           }
           sched_fence();
         },
         std::make_integer_sequence<int, NP>{});
     sc_tail = sc[TM - 1];
   };
+  using FullT = std::true_type;
+  using PartT = std::false_type;
 
   // Each group runs its own loop (its own body, so no value is live across
   // a merge of the two roles); both execute the same
@@ -742,57 +758,69 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(
     // iteration kb: phase A computes block kb, phase B reads block kb+1
     // (block G: a reloaded copy of the last block, unused) and refills slot
     // kb % STAGES with block kb+STAGES
-    auto step = [&](uint32_t kb, auto slot_c) {
-      constexpr int S = decltype(slot_c)::value;
-      compute_block();    // phase A
-      wait_vmcnt<LW0>();  // own part of stage kb+1 (that of kb+2 may be in flight)
-      wg_barrier();
-      read_block(std::integral_constant<int, (S + 1) % STAGES>{});  // phase B
-      wait_lgkm0();
-      issue_g0(min(kb + STAGES, G - 1), S);
-      wg_barrier();
-    };
+    auto run = [&](auto full_c) {
+      auto step = [&](uint32_t kb, auto slot_c) {
+        constexpr int S = decltype(slot_c)::value;
+        compute_block(full_c);  // phase A
+        wait_vmcnt<LW0>();      // own part of stage kb+1 (that of kb+2 may be in flight)
+        wg_barrier();
+        read_block(std::integral_constant<int, (S + 1) % STAGES>{}, full_c);  // phase B
+        wait_lgkm0();
+        issue_g0(min(kb + STAGES, G - 1), S);
+        wg_barrier();
+      };
 #pragma unroll
-    for (int s = 0; s < STAGES; ++s) issue_g0(min((uint32_t)s, G - 1), s);
-    wait_vmcnt<(STAGES - 1) * LW0>();  // own part of stage 0
-    wg_barrier();
-    read_block(S0{});
-    wait_lgkm0();
-    wg_barrier();
-    uint32_t kb = 0;
-    for (; kb + 3 <= G; kb += 3) {
-      step(kb, S0{});
-      step(kb + 1, S1{});
-      step(kb + 2, S2{});
-    }
-    if (kb < G) step(kb, S0{});
-    if (kb + 1 < G) step(kb + 1, S1{});
+      for (int s = 0; s < STAGES; ++s) issue_g0(min((uint32_t)s, G - 1), s);
+      wait_vmcnt<(STAGES - 1) * LW0>();  // own part of stage 0
+      wg_barrier();
+      read_block(S0{}, full_c);
+      wait_lgkm0();
+      wg_barrier();
+      uint32_t kb = 0;
+      for (; kb + 3 <= G; kb += 3) {
+        step(kb, S0{});
+        step(kb + 1, S1{});
+        step(kb + 2, S2{});
+      }
+      if (kb < G) step(kb, S0{});
+      if (kb + 1 < G) step(kb + 1, S1{});
+    };
+    if (vt == (uint32_t)TM)
+      run(FullT{});
+    else
+      run(PartT{});
   } else {
     // iteration kb: phase A reads block kb and refills its slot, phase B
     // computes it
-    auto step = [&](uint32_t kb, auto slot_c) {
-      constexpr int S = decltype(slot_c)::value;
-      read_block(slot_c);  // phase A
-      wait_lgkm0();
-      issue_g1(min(kb + STAGES, G - 1), S);
-      wait_vmcnt<2 * LW1>();  // own part of stage kb+1 (kb+2, kb+3 may be in flight)
-      wg_barrier();
-      compute_block();  // phase B
-      wg_barrier();
-    };
+    auto run = [&](auto full_c) {
+      auto step = [&](uint32_t kb, auto slot_c) {
+        constexpr int S = decltype(slot_c)::value;
+        read_block(slot_c, full_c);  // phase A
+        wait_lgkm0();
+        issue_g1(min(kb + STAGES, G - 1), S);
+        wait_vmcnt<2 * LW1>();  // own part of stage kb+1 (kb+2, kb+3 may be in flight)
+        wg_barrier();
+        compute_block(full_c);  // phase B
+        wg_barrier();
+      };
 #pragma unroll
-    for (int s = 0; s < STAGES; ++s) issue_g1(min((uint32_t)s, G - 1), s);
-    wait_vmcnt<(STAGES - 1) * LW1>();  // own part of stage 0
-    wg_barrier();
-    wg_barrier();
-    uint32_t kb = 0;
-    for (; kb + 3 <= G; kb += 3) {
-      step(kb, S0{});
-      step(kb + 1, S1{});
-      step(kb + 2, S2{});
-    }
-    if (kb < G) step(kb, S0{});
-    if (kb + 1 < G) step(kb + 1, S1{});
+      for (int s = 0; s < STAGES; ++s) issue_g1(min((uint32_t)s, G - 1), s);
+      wait_vmcnt<(STAGES - 1) * LW1>();  // own part of stage 0
+      wg_barrier();
+      wg_barrier();
+      uint32_t kb = 0;
+      for (; kb + 3 <= G; kb += 3) {
+        step(kb, S0{});
+        step(kb + 1, S1{});
+        step(kb + 2, S2{});
+      }
+      if (kb < G) step(kb, S0{});
+      if (kb + 1 < G) step(kb + 1, S1{});
+    };
+    if (vt == (uint32_t)TM)
+      run(FullT{});
+    else
+      run(PartT{});
   }
   wait_vmcnt<0>();  // no direct load may still be writing LDS at exit
 #pragma unroll
