@@ -1490,8 +1490,8 @@ __global__ __launch_bounds__(64 * NWV) void gemm_skinny_kernel(
 // activation fragments and the scales of the K blocks its waves take (wave
 // v: blocks v, v+8, ..., every row tile, as gemm_skinny_kernel), all before
 // the first wait.  Then the waves compute their blocks and add the 8 partial
-// tiles in wave order through LDS: the same products and the same order of
-// additions as gemm_skinny_kernel.  Measured at N = 6144, K = 5120 (weights
+// tiles in wave order through LDS: the same products as gemm_skinny_kernel,
+// each wave's blocks added in an order rotated by the workgroup index.  Measured at N = 6144, K = 5120 (weights
 // from HBM, graph-timed back-to-back launches): 10.3 / 12.7 / 13.3 us at M =
 // 16 / 17 / 25 against 12.6 / 14.0 / 14.8 us for gemm_skinny_kernel.  What
 // remains above the bare weight stream is mostly the activation reads: every
@@ -1517,13 +1517,20 @@ __global__ __launch_bounds__(512) void gemm_decode_kernel(
 
   // this wave's activation fragments and scales (L2-resident: every
   // workgroup reads them; rows past M are zero fragments, not loaded), and
-  // weight scales: issued first, ahead of the weight stream
-  const uint32_t nb_last = N / kGroup - 1;
+  // weight scales: issued first, ahead of the weight stream.  Slot j holds
+  // block wave + 8*((j + w) mod GW): the workgroups start their activation
+  // reads at different blocks, so that the 32 CUs of an XCD do not all ask
+  // its L2 for the same lines at once.
+  const uint32_t nb_last = N / kGroup - 1, rot = w % GW;
+  auto blk = [&](int j) __attribute__((always_inline)) -> uint32_t {
+    const uint32_t jr = (uint32_t)j + rot;
+    return wave + 8 * (jr >= (uint32_t)GW ? jr - GW : jr);
+  };
   v8i af[GW][TM];
   float as[GW][TM], ws[GW][NT];
 #pragma unroll
   for (int j = 0; j < GW; ++j) {
-    const uint32_t b = min(wave + 8 * j, G - 1);  // blocks past G: loaded, not used
+    const uint32_t b = min(blk(j), G - 1);  // blocks past G: loaded, not used
 #pragma unroll
     for (int tm = 0; tm < TM; ++tm) {
       const uint32_t m = 16 * tm + l16;
@@ -1569,10 +1576,10 @@ __global__ __launch_bounds__(512) void gemm_decode_kernel(
   for (int j = 0; j < GW; ++j)
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-      const uint32_t r = 16 * t + l16, b = min(wave + 8 * j, G - 1);
+      const uint32_t r = 16 * t + l16, b = min(blk(j), G - 1);
       const uint8_t* wr = smem + min(r, R - 1) * rowb + b * kGroup + 32 * q;
       wf[j][t] = join(*reinterpret_cast<const u32x4*>(wr), *reinterpret_cast<const u32x4*>(wr + 16));
-      if (r >= R || wave + 8 * j >= G) wf[j][t] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+      if (r >= R || blk(j) >= G) wf[j][t] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
     }
   v4f acc[NT][TM];
 #pragma unroll
