@@ -1491,12 +1491,16 @@ __global__ __launch_bounds__(64 * NWV) void gemm_skinny_kernel(
 // v: blocks v, v+8, ..., every row tile, as gemm_skinny_kernel), all before
 // the first wait.  Then the waves compute their blocks and add the 8 partial
 // tiles in wave order through LDS: the same products as gemm_skinny_kernel,
-// each wave's blocks added in an order rotated by the workgroup index.  Measured at N = 6144, K = 5120 (weights
-// from HBM, graph-timed back-to-back launches): 10.3 / 12.7 / 13.3 us at M =
-// 16 / 17 / 25 against 12.6 / 14.0 / 14.8 us for gemm_skinny_kernel.  What
-// remains above the bare weight stream is mostly the activation reads: every
-// workgroup reads all M x K activation bytes (at M = 25 more than its weight
-// slice), and the two row tiles' fragments cost about 3 us more than one.
+// each wave's blocks added in an order rotated by the workgroup index.
+// Measured at N = 6144, K = 5120 (weights from HBM, graph-timed back-to-back
+// launches): 9.8 / 11.0 / 11.9 us at M = 16 / 17 / 25 against 12.6 / 14.0 /
+// 14.8 us for gemm_skinny_kernel.  What remains above the bare weight stream
+// is the activation reads (every workgroup reads all M x K activation bytes
+// through its vector memory unit ahead of its weight loads: 0.7 us at M = 16,
+// 2 us at M = 25) and the products, the reduction and the store after the
+// single wait (about 1.8 us).  Waiting for the weight loads stage by stage,
+// one K slot at a time, was slower: the barriers cost more than the overlap
+// gains.
 // ------------------------------------------------------------------------
 constexpr uint32_t kDecodeMaxRows = 32, kDecodeLds = 150 * 1024;
 
@@ -1516,8 +1520,8 @@ __global__ __launch_bounds__(512) void gemm_decode_kernel(
   const uint32_t l16 = lane & 15, q = lane >> 4;
 
   // this wave's activation fragments and scales (L2-resident: every
-  // workgroup reads them; rows past M are zero fragments, not loaded), and
-  // weight scales: issued first, ahead of the weight stream.  Slot j holds
+  // workgroup reads them), and weight scales: issued first, ahead of the
+  // weight stream.  Slot j holds
   // block wave + 8*((j + w) mod GW): the workgroups start their activation
   // reads at different blocks, so that the 32 CUs of an XCD do not all ask
   // its L2 for the same lines at once.
@@ -1533,12 +1537,12 @@ __global__ __launch_bounds__(512) void gemm_decode_kernel(
     const uint32_t b = min(blk(j), G - 1);  // blocks past G: loaded, not used
 #pragma unroll
     for (int tm = 0; tm < TM; ++tm) {
+      // rows past M load row M - 1 again (their outputs are not stored): a
+      // load under a branch would be waited for inside the branch, one L2
+      // round trip per fragment
       const uint32_t m = 16 * tm + l16;
-      af[j][tm] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
-      if (m < M) {
-        const u32x4* ap = reinterpret_cast<const u32x4*>(A + (uint64_t)m * K + b * kGroup + 32 * q);
-        af[j][tm] = join(ap[0], ap[1]);
-      }
+      const u32x4* ap = reinterpret_cast<const u32x4*>(A + (uint64_t)min(m, M - 1) * K + b * kGroup + 32 * q);
+      af[j][tm] = join(ap[0], ap[1]);
       as[j][tm] = As[(uint64_t)b * Mp + min(m, Mp - 1)];
     }
 #pragma unroll
