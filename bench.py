@@ -61,10 +61,11 @@ FP8_PEAK_TFLOPS = 5000.0   # MI355X dense FP8 MFMA, TFLOP/s
 BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
 # HBM bytes the rocprofv3 FETCH_SIZE/WRITE_SIZE counters attribute to one
 # launch of the dominant GEMM at the default workload, scaled by the counters'
-# readings for a plain 1 GiB copy (the HBM-bytes summary under profiles/).
+# readings for a plain 64 MiB device copy (FETCH_SIZE x2, WRITE_SIZE x1;
+# the HBM-bytes summary under profiles/).
 # Valid only for the kernel source they were taken with: reported as null
 # once the ping-pong kernel's source changes (gemm_source_hash).
-GEMM_TRAFFIC = {"bytes": 1.1792e+09 + 4.7075e+07, "gemm_source_sha256": "95986a9d81cfde74"}
+GEMM_TRAFFIC = {"bytes": 1.2248e+09 + 4.7087e+07, "gemm_source_sha256": "ed4c14be68341a65"}
 
 
 def gemm_source_hash():
@@ -771,8 +772,11 @@ def measure_projection(w, steps, warmup, per_row=False, comparators=False, cpu_b
     """One projection workload on the GPU: the whole step (quantizer, relayout
     or the fused quantizer, GEMM) over `steps` timed steps with HIP events
     around every kernel, the shader clock over those steps, back-to-back
-    launches of each kernel over rotating input copies, and the oracle on a
-    bounded sample.  Returns (entry dict, extras for the benchmark line)."""
+    launches of each kernel, and the oracle on a bounded sample.  Every step
+    and every back-to-back launch takes the next of several copies of the
+    activations and of the weights (each set at least 600 MB where 64 copies
+    reach it), so that its reads come from HBM and not from the 256 MB
+    last-level cache.  Returns (entry dict, extras for the benchmark line)."""
     import torch
     import synth
     import w8a8_fp8_block_amd as fp8q
@@ -809,22 +813,24 @@ def measure_projection(w, steps, warmup, per_row=False, comparators=False, cpu_b
     variant, _, _ = fp8q.fp8q_quant_select(M, K, props.multi_processor_count)
     fused = fp8q.fp8q_proj_quant_fused(M, K)  # the same choice fp8q_proj makes
     clock = ClockStamps(fp8q, dev)
+    x_rot, w_rot = _rotation(x), _rotation(wq)
 
-    def step(ev=None):
+    def step(i, ev=None):
+        xi, wi = x_rot[i % len(x_rot)], w_rot[i % len(w_rot)]
         if ev: ev[0].record(stream)
         if fused:
-            fp8q.fp8q_quant_act_kmajor(x, act_q, act_s, act_km)
+            fp8q.fp8q_quant_act_kmajor(xi, act_q, act_s, act_km)
         else:
-            fp8q.fp8q_quant_act(x, act_q, act_s)
+            fp8q.fp8q_quant_act(xi, act_q, act_s)
         if ev: ev[1].record(stream)
         if not fused:
             fp8q.fp8q_scale_to_kmajor(act_s, act_km)
         if ev: ev[2].record(stream)
-        gemm(act_q, act_km, wq, ws, out)
+        gemm(act_q, act_km, wi, ws, out)
         if ev: ev[3].record(stream)
 
-    for _ in range(warmup):
-        step()
+    for i in range(warmup):
+        step(i)
     torch.cuda.synchronize()
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
     t_start = torch.cuda.Event(enable_timing=True)
@@ -835,7 +841,7 @@ def measure_projection(w, steps, warmup, per_row=False, comparators=False, cpu_b
     clock.start()
     t_start.record(stream)
     for i in range(steps):
-        step(evs[i])
+        step(warmup + i, evs[i])
     t_end.record(stream)
     clock.stop()
     torch.cuda.synchronize()
@@ -847,18 +853,15 @@ def measure_projection(w, steps, warmup, per_row=False, comparators=False, cpu_b
     gemm_us = np.array([e[2].elapsed_time(e[3]) for e in evs]) * 1e3
     step_clock = clock.result()
     # the same step captured R times into one HIP graph (no host launch gaps)
-    step_graph_us, step_graph_how = _b2b_us(lambda i: step(), R)
+    step_graph_us, step_graph_how = _b2b_us(lambda i: step(i), R)
 
-    # back-to-back launches of each kernel, cycling through input copies
-    w_rot = _rotation(wq)
+    # back-to-back launches of each kernel, cycling through the input copies
     gclock = ClockStamps(fp8q, dev)
     gclock.start()
     gemm_b2b, b2b_how = _b2b_us(lambda i: gemm(act_q, act_km, w_rot[i % len(w_rot)], ws, out), R)
     gclock.stop()
     torch.cuda.synchronize()
     gemm_b2b_clock = gclock.result()
-    del w_rot
-    x_rot = _rotation(x)
     if fused:
         quant_b2b, _ = _b2b_us(lambda i: fp8q.fp8q_quant_act_kmajor(x_rot[i % len(x_rot)], act_q,
                                                                    act_s, act_km), R)
@@ -866,7 +869,7 @@ def measure_projection(w, steps, warmup, per_row=False, comparators=False, cpu_b
     else:
         quant_b2b, _ = _b2b_us(lambda i: fp8q.fp8q_quant_act(x_rot[i % len(x_rot)], act_q, act_s), R)
         relay_b2b, _ = _b2b_us(lambda i: fp8q.fp8q_scale_to_kmajor(act_s, act_km), R)
-    del x_rot
+    del x_rot, w_rot
 
     flops = 2.0 * M * N * K
     kern = fp8q.fp8q_gemm_select(M, N, K)
