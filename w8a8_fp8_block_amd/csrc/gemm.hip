@@ -1493,7 +1493,7 @@ __global__ __launch_bounds__(64 * NWV) void gemm_skinny_kernel(
 // tiles in wave order through LDS: the same products as gemm_skinny_kernel,
 // each wave's blocks added in an order rotated by the workgroup index.
 // Measured at N = 6144, K = 5120 (weights from HBM, graph-timed back-to-back
-// launches): 9.8 / 11.0 / 11.9 us at M = 16 / 17 / 25 against 12.6 / 14.0 /
+// launches): 9.5 / 11.0 / 11.7 us at M = 16 / 17 / 25 against 12.6 / 14.0 /
 // 14.8 us for gemm_skinny_kernel.  What remains above the bare weight stream
 // is the activation reads (every workgroup reads all M x K activation bytes
 // through its vector memory unit ahead of its weight loads: 0.7 us at M = 16,
@@ -1530,6 +1530,7 @@ __global__ __launch_bounds__(512) void gemm_decode_kernel(
     const uint32_t jr = (uint32_t)j + rot;
     return wave + 8 * (jr >= (uint32_t)GW ? jr - GW : jr);
   };
+  const __amdgpu_buffer_rsrc_t rA = make_rsrc(A, M * K);  // M * K < 2^31 here
   v8i af[GW][TM];
   float as[GW][TM], ws[GW][NT];
 #pragma unroll
@@ -1537,12 +1538,14 @@ __global__ __launch_bounds__(512) void gemm_decode_kernel(
     const uint32_t b = min(blk(j), G - 1);  // blocks past G: loaded, not used
 #pragma unroll
     for (int tm = 0; tm < TM; ++tm) {
-      // rows past M load row M - 1 again (their outputs are not stored): a
-      // load under a branch would be waited for inside the branch, one L2
-      // round trip per fragment
+      // rows past M read at an offset beyond the buffer's range, which gives
+      // zeros without a memory request (not a load under a branch: that
+      // load would be waited for inside the branch, one L2 round trip per
+      // fragment)
       const uint32_t m = 16 * tm + l16;
-      const u32x4* ap = reinterpret_cast<const u32x4*>(A + (uint64_t)min(m, M - 1) * K + b * kGroup + 32 * q);
-      af[j][tm] = join(ap[0], ap[1]);
+      const uint32_t off = m < M ? m * K + b * kGroup + 32 * q : 0x80000000u;
+      af[j][tm] = join(__builtin_amdgcn_raw_buffer_load_b128(rA, off, 0, 0),
+                       __builtin_amdgcn_raw_buffer_load_b128(rA, off + 16, 0, 0));
       as[j][tm] = As[(uint64_t)b * Mp + min(m, Mp - 1)];
     }
 #pragma unroll
