@@ -114,6 +114,8 @@ def parse():
     p.add_argument("--gemm-sweep", action="store_true",
                    help="the GEMM's single-pass kernels and split-K counts over M at three "
                         "projection shapes with cold caches (the split-K selector's measurement)")
+    p.add_argument("--sweep-m", default=None,
+                   help="comma-separated row counts for --gemm-sweep (default: its 15)")
     p.add_argument("--cpu-sweep", action="store_true",
                    help="instead of the benchmark, time the CPU oracle on the host cores: "
                         "quantizer + relayout per quantizer-sweep shape (all threads and one), "
@@ -446,7 +448,7 @@ def ffn_sweep(reps=15):
                           "rule_ok": t[auto] <= 1.03 * min(t[1], t[2])}), flush=True)
 
 
-def gemm_sweep(reps=10):
+def gemm_sweep(reps=10, ms=None):
     """The block-scaled GEMM over M at three projection shapes, cold caches:
     the automatic single-pass kernel, the 128x128 tiled kernel and its split-K
     form at 2..12 splits (median of `reps` calls each, all variants taking turns,
@@ -462,7 +464,7 @@ def gemm_sweep(reps=10):
     flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
     for N, K in ((5120, 17408), (6144, 5120), (17408, 5120)):
         wq, wsc = quantize_weights_gpu(torch.randn((N, K), generator=gen, device=dev) * 0.02)
-        for M in (16, 32, 64, 65, 96, 128, 192, 256, 384, 512, 768, 1024, 1168, 1536, 2048):
+        for M in ms or (16, 32, 64, 65, 96, 128, 192, 256, 384, 512, 768, 1024, 1168, 1536, 2048):
             x = torch.randn((M, K), generator=gen, device=dev).to(torch.bfloat16)
             q = torch.empty((M, K), dtype=torch.uint8, device=dev)
             srm = torch.empty((M, K // 128), dtype=torch.float32, device=dev)
@@ -1072,7 +1074,7 @@ def main():
         ffn_sweep()
         return
     if args.gemm_sweep:
-        gemm_sweep()
+        gemm_sweep(ms=[int(v) for v in args.sweep_m.split(",")] if args.sweep_m else None)
         return
 
     import torch

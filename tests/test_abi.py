@@ -340,17 +340,18 @@ def test_splitk_workspace_bytes():
 
 
 def test_splitk_select():
-    """Split count above 64 rows, outside the 256x128 kernel's range, with
+    """Split count above 64 rows (from 33 rows for a weight matrix of at
+    least 64 MiB), outside the 256x128 kernel's range, with
     c = min(floor(K/1280), 6): min(floor(256 / tiles), c) if at least 2,
     else min(floor(512 / tiles), c), 1 below 2; 0 for a bad N or K."""
     def sel(M, N, K):
         return fp8q.fp8q_gemm_splitk_select(M, N, K, 256)
-    for M, want in ((16, 1), (64, 1), (65, 6), (128, 6), (129, 3), (256, 3), (257, 2), (384, 2),
+    for M, want in ((16, 1), (32, 1), (33, 6), (64, 6), (65, 6), (128, 6), (129, 3), (256, 3), (257, 2), (384, 2),
                     (385, 3), (512, 3), (513, 2), (768, 2), (769, 1), (1168, 1), (2048, 1)):
         assert sel(M, 5120, 17408) == want, M
-    for M, want in ((65, 4), (256, 2), (384, 3), (512, 2), (640, 2), (768, 1)):
-        assert sel(M, 6144, 5120) == want, M
-    for M, want in ((65, 3), (128, 3), (129, 1)):
+    for M, want in ((33, 1), (64, 1), (65, 4), (256, 2), (384, 3), (512, 2), (640, 2), (768, 1)):
+        assert sel(M, 6144, 5120) == want, M      # 31 MB of weights: no split up to 64 rows
+    for M, want in ((32, 1), (33, 3), (64, 3), (65, 3), (128, 3), (129, 1)):
         assert sel(M, 17408, 5120) == want, M
     assert sel(300, 128, 2560) == 2        # K/1280 = 2 caps it
     assert sel(300, 128, 2432) == 1        # fewer than 20 K blocks: no split

@@ -127,9 +127,10 @@ def test_splitk_repeatable(orc):
         assert np.array_equal(o1, o2)
 
 
-@pytest.mark.parametrize("M,N,K", [(512, 5120, 17408), (200, 6144, 5120)])
+@pytest.mark.parametrize("M,N,K", [(512, 5120, 17408), (200, 6144, 5120), (48, 5120, 17408)])
 def test_splitk_projection_shapes_full(orc, M, N, K):
-    """Medium row counts at the down- and a gate/up-projection shape, with the
+    """Medium row counts at the down- and a gate/up-projection shape (48 rows:
+    split from 33 rows for a weight matrix of 64 MiB or more), with the
     automatic split count and one more: all M*N outputs against the oracle."""
     a, a_s, wq, ws = _random_operands(orc, M, N, K, M + K, "laplace")
     log(f"oracle M={M} N={N} K={K}: full fp64 product")
@@ -142,7 +143,8 @@ def test_splitk_projection_shapes_full(orc, M, N, K):
         assert_tol(o, ref, f"M{M}N{N}K{K}s{splits}")
 
 
-@pytest.mark.parametrize("M,N,K", [(200, 1024, 5120), (96, 6144, 5120), (40, 512, 2048)])
+@pytest.mark.parametrize("M,N,K", [(200, 1024, 5120), (96, 6144, 5120), (40, 512, 2048),
+                                   (64, 17408, 5120)])
 def test_proj_splitk(orc, M, N, K):
     """fp8q_proj_splitk: the quantizer's codes and both scale layouts as
     fp8q_proj writes them (bit-exact against the oracle), the output equal bit

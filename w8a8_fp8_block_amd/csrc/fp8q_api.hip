@@ -261,20 +261,28 @@ int gemm_auto_kernel(uint32_t M, uint32_t N, uint32_t cus) {
 // three-stage form), else floor(2 CUs / tiles) (one round of two 128x128
 // workgroups per CU, two stages), at most K/1280 (10 K blocks a split) and
 // 6, for more than kSplitMinM rows and wherever the single-pass choice is
-// not the 256 x 128 kernel.  Cold
+// not the 256 x 128 kernel; from kSplitMidM + 1 to kSplitMinM rows only for
+// a weight matrix of at least kSplitMidMinWeights bytes.  Cold
 // caches (bench.py --gemm-sweep, 256 CUs), us single-pass -> split-K: N=5120,
 // K=17408: 87 -> 46 at M=65, 135 -> 55 at M=192, 143 -> 73 at M=384, 143 ->
 // 87 at M=512, 144 -> 109 at M=768; N=6144, K=5120: 32 -> 23 at M=65, 47 ->
 // 32 at M=192, 51 -> 39 at M=384; N=17408, K=5120: 55 -> 47 at M=65.  A
 // count past one round (M=512, N=5120: 4 splits, 640 workgroups) was up to
-// 30% slower than the one below it; beyond 512 tiles no count helped.
+// 30% slower than the one below it; beyond 512 tiles no count helped.  At
+// M = 33 .. 64 (the fragment-layout skinny kernel with one 64-row tile) the
+// split is 4-20% faster for N = 5120, K = 17408 and 3-5% for N = 17408,
+// K = 5120 (89 MB of weights each), and 2-10% slower for N = 6144, K = 5120
+// (31 MB): the threshold sits between those three measured shapes.
 constexpr uint32_t kSplitMinBlocks = 10;
 constexpr uint32_t kSplitMax = 6;
 constexpr uint32_t kSplitMinM = 64;
+constexpr uint32_t kSplitMidM = 32;
+constexpr uint64_t kSplitMidMinWeights = 64ull << 20;
 constexpr uint32_t kSplitMaxUser = 64;  // bound of an explicit split count
 
 uint32_t splitk_auto(uint32_t M, uint32_t N, uint32_t K, uint32_t cus) {
-  if (M <= kSplitMinM || gemm_auto_kernel(M, N, cus) == 5) return 1;
+  if (M <= kSplitMidM || gemm_auto_kernel(M, N, cus) == 5) return 1;
+  if (M <= kSplitMinM && (uint64_t)N * K < kSplitMidMinWeights) return 1;
   const uint64_t tiles = (uint64_t)((M + 127) / 128) * (N / 128);
   const uint64_t cap = std::min<uint64_t>(K / kGroup / kSplitMinBlocks, kSplitMax);
   // prefer a count whose grid fits one workgroup per CU (the three-stage
