@@ -7,7 +7,9 @@ One step = one pass of the whole projection over one batch of synthetic
 input, already resident in HBM: activation quantizer -> scale relayout ->
 block-scaled FP8 GEMM (the calls fp8q_proj makes, issued separately so that
 each kernel can be bracketed by events; for small batches the quantizer
-writes the K-major scales itself, as fp8q_proj does).
+writes the K-major scales itself, as fp8q_proj does).  Before the W warmup
+steps, untimed steps run for SETTLE_S seconds so that the device's power
+control has settled (recorded as "settle" in each configuration).
 
 Default workload: the large prefill projection M=4576, K=17408, N=5120,
 Laplace(0,1) activations with 0.5% outlier channels x50, weights N(0,0.02)
@@ -16,7 +18,8 @@ quantized per 128x128 block.  Prints ONE JSON line:
   value           whole-step TFLOP/s = 2*M*N*K / step time
   roofline        the GEMM (dominant kernel) against the dense FP8 MFMA peak
                   (HBM peak for the weight-streaming skinny kernel): duration
-                  from HIP events around each GEMM launch of the timed steps;
+                  from HIP events around each GEMM launch of the timed steps
+                  (events without the system-scope fence, KernelEvents);
                   also R back-to-back launches between two events cycling
                   through weight copies of >= 600 MB (streamed from HBM, not
                   the 256 MB last-level cache), with the shader clock then
@@ -705,19 +708,25 @@ def _b2b_us(fn, R, graph=True):
     one HIP graph and replayed between two HIP events, so that no host launch
     gap sits between the kernels (launches from Python are ~10 us apart,
     longer than the small kernels); plain launches between two events if the
-    capture fails.  Returns (us, method)."""
+    capture fails.  The timed replay follows B2B_SETTLE_S seconds of the same
+    replays.  Returns (us, method)."""
     import torch
     fn(0)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def settle(run):  # the same launches until the power control has settled
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < B2B_SETTLE_S:
+            run()
+            torch.cuda.synchronize()
     if graph:
         try:
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
                 for i in range(R):
                     fn(i)
-            g.replay()
-            torch.cuda.synchronize()
+            settle(g.replay)
             e0.record()
             g.replay()
             e1.record()
@@ -729,12 +738,123 @@ def _b2b_us(fn, R, graph=True):
             print(f"[bench] graph capture failed ({str(ex).splitlines()[0][:120]}); "
                   "timing plain launches", file=sys.stderr, flush=True)
             torch.cuda.synchronize()
+
+    def launches():
+        for i in range(R):
+            fn(i)
+    settle(launches)
     e0.record()
-    for i in range(R):
-        fn(i)
+    launches()
     e1.record()
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) * 1e3 / R, "stream"
+
+
+# Untimed steps run before the warmup steps, for at least this long: under
+# this load the device's power controller overshoots and recovers over the
+# first few tens of milliseconds (one trace: the large prefill GEMM at 404 us,
+# then 520-530 us, then back to a steady ~400 us within ~25 ms), so a short
+# warmup would leave that transient inside the timed steps.
+SETTLE_S = 0.3
+# the same before each back-to-back measurement (replays of its graph)
+B2B_SETTLE_S = 0.15
+
+
+def _settle(step, seconds):
+    """Run step(i) in bursts of 8 (synchronising after each burst) until
+    `seconds` of wall time have passed.  Returns (steps run, host time per
+    step spent issuing the launches, wall time per step): a step whose issue
+    time is most of its wall time is bound by the host's launches, not the
+    GPU."""
+    import torch
+    t0, n, issue = time.perf_counter(), 0, 0.0
+    while True:
+        t1 = time.perf_counter()
+        for _ in range(8):
+            step(n)
+            n += 1
+        issue += time.perf_counter() - t1
+        torch.cuda.synchronize()
+        if time.perf_counter() - t0 >= seconds:
+            return n, issue / n, (time.perf_counter() - t0) / n
+
+
+def _spin_cycles_per_us():
+    """Cycles of torch.cuda._sleep per microsecond on this device (its spin
+    counts a hardware counter; timed once with events)."""
+    import torch
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda._sleep(1000)
+    e0.record()
+    torch.cuda._sleep(2_000_000)
+    e1.record()
+    torch.cuda.synchronize()
+    return 2_000_000 / (e0.elapsed_time(e1) * 1e3)
+
+
+class KernelEvents:
+    """HIP timing events created with hipEventDisableSystemFence, for the
+    per-kernel times inside the timed steps.  A default event (torch's) is a
+    system-scope release: recording it writes back and invalidates L2, which
+    is charged to the interval it closes and leaves the next kernel a cold L2.
+    These events stamp the same points on the stream (each marker waits for
+    the work before it) without that fence, so an interval is the kernel's
+    own time, as a kernel trace reports it; the region's start and end keep
+    torch's fenced events.  Calls torch's HIP runtime (already loaded)."""
+
+    _lib = None
+
+    @classmethod
+    def _hip(cls):
+        if cls._lib is None:
+            import ctypes
+            import torch
+            lib = ctypes.CDLL(os.path.join(os.path.dirname(torch.__file__), "lib", "libamdhip64.so"))
+            lib.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+            lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+            lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                ctypes.c_void_p]
+            lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+            for f in ("hipEventCreateWithFlags", "hipEventRecord", "hipEventElapsedTime",
+                      "hipEventDestroy"):
+                getattr(lib, f).restype = ctypes.c_int
+            cls._lib = lib
+        return cls._lib
+
+    def __init__(self, n):
+        import ctypes
+        lib = self._hip()
+        self.ev = []
+        for _ in range(n):
+            e = ctypes.c_void_p()
+            rc = lib.hipEventCreateWithFlags(ctypes.byref(e), 0x20000000)  # hipEventDisableSystemFence
+            if rc != 0:
+                raise RuntimeError(f"hipEventCreateWithFlags failed ({rc})")
+            self.ev.append(e)
+
+    def record(self, i, stream):
+        rc = self._hip().hipEventRecord(self.ev[i], ctypes_stream(stream))
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord failed ({rc})")
+
+    def elapsed_us(self, i, j):
+        import ctypes
+        ms = ctypes.c_float()
+        rc = self._hip().hipEventElapsedTime(ctypes.byref(ms), self.ev[i], self.ev[j])
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return ms.value * 1e3
+
+    def __del__(self):
+        lib = KernelEvents._lib
+        if lib is not None:
+            for e in getattr(self, "ev", []):
+                lib.hipEventDestroy(e)
+
+
+def ctypes_stream(stream):
+    import ctypes
+    return ctypes.c_void_p(stream.cuda_stream)
 
 
 class ClockStamps:
@@ -819,40 +939,58 @@ def measure_projection(w, steps, warmup, per_row=False, comparators=False, cpu_b
 
     def step(i, ev=None):
         xi, wi = x_rot[i % len(x_rot)], w_rot[i % len(w_rot)]
-        if ev: ev[0].record(stream)
+        if ev: ev.record(4 * (i - warmup), stream)
         if fused:
             fp8q.fp8q_quant_act_kmajor(xi, act_q, act_s, act_km)
         else:
             fp8q.fp8q_quant_act(xi, act_q, act_s)
-        if ev: ev[1].record(stream)
+        if ev: ev.record(4 * (i - warmup) + 1, stream)
         if not fused:
             fp8q.fp8q_scale_to_kmajor(act_s, act_km)
-        if ev: ev[2].record(stream)
+        if ev: ev.record(4 * (i - warmup) + 2, stream)
         gemm(act_q, act_km, wi, ws, out)
-        if ev: ev[3].record(stream)
+        if ev: ev.record(4 * (i - warmup) + 3, stream)
 
+    settle_steps, issue_s, settle_step_s = _settle(step, SETTLE_S)
+    # Where issuing a step's launches from Python takes most of its wall time
+    # (the small workloads), the GPU would idle between kernels, inside the
+    # event intervals; there the timed steps are all issued behind a GPU spin
+    # (torch.cuda._sleep) long enough to cover their issue, so that they run
+    # back to back as a graph or a native caller would run them, and the wall
+    # time starts once the GPU has reached the first of them.
+    host_bound = issue_s > 0.5 * settle_step_s
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    evs = KernelEvents(4 * steps)
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
-    print(f"[bench] timing {steps} steps of {w.desc}", file=sys.stderr, flush=True)
+    spin_us = 1.5 * issue_s * 1e6 * steps + 2000.0 if host_bound else 0.0
+    if spin_us:
+        cyc = _spin_cycles_per_us()
+    print(f"[bench] timing {steps} steps of {w.desc}" +
+          (f" (issued behind a {spin_us / 1e3:.1f} ms spin)" if spin_us else ""),
+          file=sys.stderr, flush=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
+    if spin_us:
+        torch.cuda._sleep(int(spin_us * cyc))
     clock.start()
     t_start.record(stream)
     for i in range(steps):
-        step(warmup + i, evs[i])
+        step(warmup + i, evs)
     t_end.record(stream)
     clock.stop()
+    if spin_us:
+        t_start.synchronize()
+        wall0 = time.perf_counter()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     gpu_ms = t_start.elapsed_time(t_end)
     ms_per_step = max(gpu_ms, wall * 1e3) / steps
-    quant_us = np.array([e[0].elapsed_time(e[1]) for e in evs]) * 1e3
-    relay_us = np.array([e[1].elapsed_time(e[2]) for e in evs]) * 1e3
-    gemm_us = np.array([e[2].elapsed_time(e[3]) for e in evs]) * 1e3
+    quant_us = np.array([evs.elapsed_us(4 * i, 4 * i + 1) for i in range(steps)])
+    relay_us = np.array([evs.elapsed_us(4 * i + 1, 4 * i + 2) for i in range(steps)])
+    gemm_us = np.array([evs.elapsed_us(4 * i + 2, 4 * i + 3) for i in range(steps)])
     step_clock = clock.result()
     # the same step captured R times into one HIP graph (no host launch gaps)
     step_graph_us, step_graph_how = _b2b_us(lambda i: step(i), R)
@@ -926,6 +1064,10 @@ def measure_projection(w, steps, warmup, per_row=False, comparators=False, cpu_b
         "roofline": roofline,
         "act_quant": act_quant,
         "clock": step_clock,
+        "settle": {"seconds": SETTLE_S, "steps": settle_steps},
+        "issue": {"host_us_per_step": round(issue_s * 1e6, 1),
+                  "settle_wall_us_per_step": round(settle_step_s * 1e6, 1),
+                  "timed_steps_issued_behind_spin_ms": round(spin_us / 1e3, 2)},
     }
     if not fused:
         rb = 4 * M * G + 4 * m_pad(M) * G
@@ -1139,6 +1281,7 @@ def main():
         "act_quant": main_entry["act_quant"],
         "cpu_baseline": main_entry.get("cpu_baseline"),
         "clock": main_entry["clock"],
+        "settle": main_entry["settle"],
     }
     if "relayout" in main_entry:
         rec["relayout"] = main_entry["relayout"]
