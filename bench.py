@@ -27,6 +27,8 @@ quantized per 128x128 block.  Prints ONE JSON line:
                   the same two ways
   clock           sustained shader clock over the timed steps, per XCD, from
                   clock stamps (fp8q_clock_stamp) before and after
+  step_graph_us   the same step captured R times into one HIP graph and
+                  replayed (no events, no host launches between kernels)
   cpu_baseline    the CPU oracle on a bounded sample of the same workload
   bf16_comparator the same GEMM in bf16 over the dequantized weights (our
                   bf16 MFMA kernel and hipBLASLt), and the FP8 speedup
@@ -937,19 +939,23 @@ def measure_projection(w, steps, warmup, per_row=False, comparators=False, cpu_b
     clock = ClockStamps(fp8q, dev)
     x_rot, w_rot = _rotation(x), _rotation(wq)
 
+    # timed step j records events 3j+1 (after the quantizer), 3j+2 (after the
+    # relayout) and 3j+3 (after the GEMM); event 3j, recorded by the step
+    # before (event 0 by the first), opens its quantizer interval
     def step(i, ev=None):
         xi, wi = x_rot[i % len(x_rot)], w_rot[i % len(w_rot)]
-        if ev: ev.record(4 * (i - warmup), stream)
+        j = i - warmup
+        if ev and j == 0: ev.record(0, stream)
         if fused:
             fp8q.fp8q_quant_act_kmajor(xi, act_q, act_s, act_km)
         else:
             fp8q.fp8q_quant_act(xi, act_q, act_s)
-        if ev: ev.record(4 * (i - warmup) + 1, stream)
+        if ev: ev.record(3 * j + 1, stream)
         if not fused:
             fp8q.fp8q_scale_to_kmajor(act_s, act_km)
-        if ev: ev.record(4 * (i - warmup) + 2, stream)
+        if ev: ev.record(3 * j + 2, stream)
         gemm(act_q, act_km, wi, ws, out)
-        if ev: ev.record(4 * (i - warmup) + 3, stream)
+        if ev: ev.record(3 * j + 3, stream)
 
     settle_steps, issue_s, settle_step_s = _settle(step, SETTLE_S)
     # Where issuing a step's launches from Python takes most of its wall time
@@ -962,7 +968,7 @@ def measure_projection(w, steps, warmup, per_row=False, comparators=False, cpu_b
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
-    evs = KernelEvents(4 * steps)
+    evs = KernelEvents(3 * steps + 1)
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     spin_us = 1.5 * issue_s * 1e6 * steps + 2000.0 if host_bound else 0.0
@@ -988,9 +994,9 @@ def measure_projection(w, steps, warmup, per_row=False, comparators=False, cpu_b
     wall = time.perf_counter() - wall0
     gpu_ms = t_start.elapsed_time(t_end)
     ms_per_step = max(gpu_ms, wall * 1e3) / steps
-    quant_us = np.array([evs.elapsed_us(4 * i, 4 * i + 1) for i in range(steps)])
-    relay_us = np.array([evs.elapsed_us(4 * i + 1, 4 * i + 2) for i in range(steps)])
-    gemm_us = np.array([evs.elapsed_us(4 * i + 2, 4 * i + 3) for i in range(steps)])
+    quant_us = np.array([evs.elapsed_us(3 * i, 3 * i + 1) for i in range(steps)])
+    relay_us = np.array([evs.elapsed_us(3 * i + 1, 3 * i + 2) for i in range(steps)])
+    gemm_us = np.array([evs.elapsed_us(3 * i + 2, 3 * i + 3) for i in range(steps)])
     step_clock = clock.result()
     # the same step captured R times into one HIP graph (no host launch gaps)
     step_graph_us, step_graph_how = _b2b_us(lambda i: step(i), R)
@@ -1282,6 +1288,9 @@ def main():
         "cpu_baseline": main_entry.get("cpu_baseline"),
         "clock": main_entry["clock"],
         "settle": main_entry["settle"],
+        "step_graph_us": main_entry["step_graph_us"],
+        "step_graph_tflops": main_entry["step_graph_tflops"],
+        "step_graph_method": main_entry["step_graph_method"],
     }
     if "relayout" in main_entry:
         rec["relayout"] = main_entry["relayout"]
