@@ -15,7 +15,9 @@ Default workload: the large prefill projection M=4576, K=17408, N=5120,
 Laplace(0,1) activations with 0.5% outlier channels x50, weights N(0,0.02)
 quantized per 128x128 block.  Prints ONE JSON line:
 
-  value           whole-step TFLOP/s = 2*M*N*K / step time
+  value           whole-step TFLOP/s = 2*M*N*K / step time (the timed steps'
+                  span between two HIP events on the stream, over K;
+                  timed_region also holds the host's wall time of it)
   roofline        the GEMM (dominant kernel) against the dense FP8 MFMA peak
                   (HBM peak for the weight-streaming skinny kernel): duration
                   from HIP events around each GEMM launch of the timed steps
@@ -993,7 +995,13 @@ def measure_projection(w, steps, warmup, per_row=False, comparators=False, cpu_b
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     gpu_ms = t_start.elapsed_time(t_end)
-    ms_per_step = max(gpu_ms, wall * 1e3) / steps
+    # The step time is the timed steps' span between the two events on the
+    # stream.  The host's wall time over the same stretch (kept in the line)
+    # starts on an idle device and adds ~0.65 ms before the first kernel
+    # runs, which no step of a running job pays; where the steps were issued
+    # behind the spin it starts once the device reached them, and the larger
+    # of the two is taken.
+    ms_per_step = (max(gpu_ms, wall * 1e3) if spin_us else gpu_ms) / steps
     quant_us = np.array([evs.elapsed_us(3 * i, 3 * i + 1) for i in range(steps)])
     relay_us = np.array([evs.elapsed_us(3 * i + 1, 3 * i + 2) for i in range(steps)])
     gemm_us = np.array([evs.elapsed_us(3 * i + 2, 3 * i + 3) for i in range(steps)])
@@ -1071,6 +1079,7 @@ def measure_projection(w, steps, warmup, per_row=False, comparators=False, cpu_b
         "act_quant": act_quant,
         "clock": step_clock,
         "settle": {"seconds": SETTLE_S, "steps": settle_steps},
+        "timed_region": {"gpu_event_ms": round(gpu_ms, 4), "wall_ms": round(wall * 1e3, 4)},
         "issue": {"host_us_per_step": round(issue_s * 1e6, 1),
                   "settle_wall_us_per_step": round(settle_step_s * 1e6, 1),
                   "timed_steps_issued_behind_spin_ms": round(spin_us / 1e3, 2)},
@@ -1288,6 +1297,7 @@ def main():
         "cpu_baseline": main_entry.get("cpu_baseline"),
         "clock": main_entry["clock"],
         "settle": main_entry["settle"],
+        "timed_region": main_entry["timed_region"],
         "step_graph_us": main_entry["step_graph_us"],
         "step_graph_tflops": main_entry["step_graph_tflops"],
         "step_graph_method": main_entry["step_graph_method"],
