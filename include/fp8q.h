@@ -278,10 +278,13 @@ fp8q_status fp8q_gemm_blockscaled_splitk(const uint8_t *a_e4m3, const float *a_s
  * split):
  *   min(floor(C / T), c) if that is at least 2 (one workgroup per CU),
  *   else min(floor(2C / T), c) (two per CU)
- * when M > 64 and fp8q_gemm_select_cus does not pick the 256x128 kernel
- * (id 5), and 1 (no split) otherwise or when that count is below 2.  0 if N
- * or K is not a positive multiple of 128 or cu_count is 0.  Pure host
- * function. */
+ * when fp8q_gemm_select_cus does not pick the 256x128 kernel (id 5) and
+ * either M > 64 or 33 <= M <= 64 with N*K >= 64 MiB and M above the columns
+ * a workgroup of the skinny path owns (at most 4*ceil(N/(4*W)) for its W =
+ * min(max(C, ceil(N/128)), N/16) workgroups: 20 at N = 5120, 68 at N =
+ * 17408 on 256 CUs); 1 (no split) otherwise or when that count is below 2.
+ * 0 if N or K is not a positive multiple of 128 or cu_count is 0.  Pure
+ * host function. */
 uint32_t fp8q_gemm_splitk_select_cus(uint32_t M, uint32_t N, uint32_t K, uint32_t cu_count);
 
 /* fp8q_gemm_splitk_select_cus for the current HIP device (256 compute
@@ -515,7 +518,7 @@ fp8q_status fp8q_ffn_gate_up(const uint8_t *x_e4m3, const float *x_scale_km,
                              uint32_t H, uint32_t I, hipStream_t stream);
 
 /* Variant fp8q_ffn takes with variant 0: 1 (fused gate/up kernel) for
- * M >= 33, 2 (separate gate and up GEMMs, then fp8q_silu_mul_quant) below;
+ * M >= 65, 2 (separate gate and up GEMMs, then fp8q_silu_mul_quant) below;
  * -1 if H or I is not a positive multiple of 128.  Pure host function. */
 int fp8q_ffn_select(uint32_t M, uint32_t H, uint32_t I);
 

@@ -226,8 +226,9 @@ def test_gemm_bf16_validation():
 def test_ffn_select_and_workspace():
     assert fp8q.fp8q_ffn_select(16, 5120, 17408) == 2
     assert fp8q.fp8q_ffn_select(32, 5120, 17408) == 2
-    assert fp8q.fp8q_ffn_select(33, 5120, 17408) == 1
-    assert fp8q.fp8q_ffn_select(64, 5120, 17408) == 1
+    assert fp8q.fp8q_ffn_select(33, 5120, 17408) == 2
+    assert fp8q.fp8q_ffn_select(64, 5120, 17408) == 2
+    assert fp8q.fp8q_ffn_select(65, 5120, 17408) == 1
     assert fp8q.fp8q_ffn_select(4576, 5120, 17408) == 1
     assert fp8q.fp8q_ffn_select(16, 5000, 17408) == -1
     M, H, I = 4576, 5120, 17408
@@ -246,7 +247,8 @@ def test_ffn_select_and_workspace():
     assert fp8q.fp8q_ffn_workspace_bytes(M, H, I, 2) == base + 2 * a256(2 * M * I)
     assert fp8q.fp8q_ffn_workspace_bytes(M, H, I, 0) == base
     assert fp8q.fp8q_ffn_workspace_bytes(16, H, I, 0) == fp8q.fp8q_ffn_workspace_bytes(16, H, I, 2)
-    assert fp8q.fp8q_ffn_workspace_bytes(33, H, I, 0) == fp8q.fp8q_ffn_workspace_bytes(33, H, I, 1)
+    assert fp8q.fp8q_ffn_workspace_bytes(64, H, I, 0) == fp8q.fp8q_ffn_workspace_bytes(64, H, I, 2)
+    assert fp8q.fp8q_ffn_workspace_bytes(65, H, I, 0) == fp8q.fp8q_ffn_workspace_bytes(65, H, I, 1)
     assert fp8q.fp8q_ffn_workspace_bytes(M, H, I, 3) == 0
     assert fp8q.fp8q_ffn_workspace_bytes(M, 100, I, 1) == 0
 
@@ -341,7 +343,8 @@ def test_splitk_workspace_bytes():
 
 def test_splitk_select():
     """Split count above 64 rows (from 33 rows for a weight matrix of at
-    least 64 MiB), outside the 256x128 kernel's range, with
+    least 64 MiB whose skinny workgroups own fewer columns than M: 20 at
+    N = 5120, 68 at N = 17408 on 256 CUs), outside the 256x128 kernel's range, with
     c = min(floor(K/1280), 6): min(floor(256 / tiles), c) if at least 2,
     else min(floor(512 / tiles), c), 1 below 2; 0 for a bad N or K."""
     def sel(M, N, K):
@@ -351,8 +354,8 @@ def test_splitk_select():
         assert sel(M, 5120, 17408) == want, M
     for M, want in ((33, 1), (64, 1), (65, 4), (256, 2), (384, 3), (512, 2), (640, 2), (768, 1)):
         assert sel(M, 6144, 5120) == want, M      # 31 MB of weights: no split up to 64 rows
-    for M, want in ((32, 1), (33, 3), (64, 3), (65, 3), (128, 3), (129, 1)):
-        assert sel(M, 17408, 5120) == want, M
+    for M, want in ((32, 1), (33, 1), (64, 1), (65, 3), (128, 3), (129, 1)):
+        assert sel(M, 17408, 5120) == want, M   # 68 skinny columns a workgroup: no split to 64 rows
     assert sel(300, 128, 2560) == 2        # K/1280 = 2 caps it
     assert sel(300, 128, 2432) == 1        # fewer than 20 K blocks: no split
     assert sel(4576, 5120, 17408) == 1     # the 256x128 kernel's pick: no split

@@ -130,7 +130,8 @@ def test_splitk_repeatable(orc):
 @pytest.mark.parametrize("M,N,K", [(512, 5120, 17408), (200, 6144, 5120), (48, 5120, 17408)])
 def test_splitk_projection_shapes_full(orc, M, N, K):
     """Medium row counts at the down- and a gate/up-projection shape (48 rows:
-    split from 33 rows for a weight matrix of 64 MiB or more), with the
+    split from 33 rows for a weight matrix of 64 MiB or more whose skinny
+    workgroups own fewer columns than that: 20 at N = 5120), with the
     automatic split count and one more: all M*N outputs against the oracle."""
     a, a_s, wq, ws = _random_operands(orc, M, N, K, M + K, "laplace")
     log(f"oracle M={M} N={N} K={K}: full fp64 product")
@@ -150,7 +151,8 @@ def test_proj_splitk(orc, M, N, K):
     fp8q_proj writes them (bit-exact against the oracle), the output equal bit
     for bit to fp8q_gemm_blockscaled_splitk (splits = 0) on those codes, and
     within the projection tolerance of the oracle; where the selector does not
-    split (M = 40) the workspace may be absent and the output is fp8q_proj's."""
+    split (M = 40; M = 64 at N = 17408, whose skinny workgroups own 68
+    columns) the workspace may be absent and the output is fp8q_proj's."""
     rng = np.random.default_rng(M + N)
     x = synth.f32_to_bf16_bits((rng.standard_normal((M, K)) *
                                 np.exp(rng.uniform(-2, 2, (M, 1)))).astype(np.float32))

@@ -270,9 +270,14 @@ int gemm_auto_kernel(uint32_t M, uint32_t N, uint32_t cus) {
 // count past one round (M=512, N=5120: 4 splits, 640 workgroups) was up to
 // 30% slower than the one below it; beyond 512 tiles no count helped.  At
 // M = 33 .. 64 (the fragment-layout skinny kernel with one 64-row tile) the
-// split is 4-20% faster for N = 5120, K = 17408 and 3-5% for N = 17408,
-// K = 5120 (89 MB of weights each), and 2-10% slower for N = 6144, K = 5120
-// (31 MB): the threshold sits between those three measured shapes.
+// split pays only where the weight matrix is large (at least
+// kSplitMidMinWeights) and the rows outnumber the skinny kernel's columns
+// per workgroup, so that its activation reads exceed its weight reads:
+// N = 5120, K = 17408 (20 columns a workgroup): split 42.4 / 42.8 / 44.3 us
+// against skinny 43.9 / 49.1 / 54.2 at M = 33 / 48 / 64; N = 17408,
+// K = 5120 (68 columns): skinny 37.5 / 38.9 / 40.3 against split 43.6 /
+// 45.4 / 46.7; N = 6144, K = 5120 (31 MB): skinny 18.6-21.8 against split
+// 20.5-22.1.
 constexpr uint32_t kSplitMinBlocks = 10;
 constexpr uint32_t kSplitMax = 6;
 constexpr uint32_t kSplitMinM = 64;
@@ -282,7 +287,9 @@ constexpr uint32_t kSplitMaxUser = 64;  // bound of an explicit split count
 
 uint32_t splitk_auto(uint32_t M, uint32_t N, uint32_t K, uint32_t cus) {
   if (M <= kSplitMidM || gemm_auto_kernel(M, N, cus) == 5) return 1;
-  if (M <= kSplitMinM && (uint64_t)N * K < kSplitMidMinWeights) return 1;
+  if (M <= kSplitMinM &&
+      ((uint64_t)N * K < kSplitMidMinWeights || M <= skinny_columns(M, N, cus)))
+    return 1;
   const uint64_t tiles = (uint64_t)((M + 127) / 128) * (N / 128);
   const uint64_t cap = std::min<uint64_t>(K / kGroup / kSplitMinBlocks, kSplitMax);
   // prefer a count whose grid fits one workgroup per CU (the three-stage
@@ -436,14 +443,15 @@ fp8q_status run_proj(const char* fn, const uint16_t* x_bf16, const uint8_t* w_e4
 
 // ---- dense FFN ----
 // fp8q_ffn's automatic choice: the fused gate/up kernel (one pass over both
-// weight matrices, no bf16 gate/up round trip through HBM) from 33 rows on;
-// below, the separate path, whose skinny GEMMs (16- and 32-row tiles) stream
-// the weights with one workgroup per CU.  Measured on the whole call at
-// H=5120, I=17408 with the last-level cache flushed before each call (the
-// weights of one layer are not resident in serving): separate 91.6 vs fused
-// 115.3 us at M=16, 107.6 vs 121.7 at M=32; fused 131.0 vs 145.6 at M=33,
-// 453 vs 475 at M=1168, 1368 vs 1454 at M=4576.
-constexpr uint32_t kFfnFusedMinM = 33;
+// weight matrices, no bf16 gate/up round trip through HBM) from 65 rows on;
+// up to 64, the separate path, whose skinny GEMMs (16-, 32- and 64-row
+// tiles) stream the weights with one workgroup per CU.  Measured on the
+// whole call at H=5120, I=17408 with the last-level cache flushed before
+// each call (the weights of one layer are not resident in serving):
+// separate 89.5 vs fused 114.9 us at M=16, 106.6 vs 121.0 at M=32, 119.4
+// vs 126.4 at M=33, 126.5 vs 129.0 at M=64; fused 129.3 vs 156.6 at M=80,
+// 446 vs 458 at M=1168, 1328 vs 1374 at M=4576.
+constexpr uint32_t kFfnFusedMinM = 65;
 
 int ffn_auto_variant(uint32_t M) { return M >= kFfnFusedMinM ? 1 : 2; }
 

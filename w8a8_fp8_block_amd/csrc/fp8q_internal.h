@@ -82,6 +82,9 @@ uint64_t gemm_streamk_workspace_bytes(uint32_t cus);
 hipError_t launch_gemm_streamk(const uint8_t* a, const float* a_s_km, const uint8_t* w,
                                const float* w_s, uint16_t* out, void* workspace, uint32_t M,
                                uint32_t N, uint32_t K, uint32_t cus, bool forced, hipStream_t s);
+// Columns (weight rows) a workgroup of the skinny path owns at most for this
+// shape (one workgroup per CU up to 64 rows).
+uint32_t skinny_columns(uint32_t M, uint32_t N, uint32_t cu_count);
 hipError_t launch_gemm_skinny(const uint8_t* a, const float* a_s_km, const uint8_t* w,
                               const float* w_s, uint16_t* out, uint32_t M, uint32_t N,
                               uint32_t K, uint32_t cu_count, bool row_scaled, hipStream_t s);

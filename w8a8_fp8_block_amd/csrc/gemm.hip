@@ -1368,7 +1368,9 @@ __global__ __launch_bounds__(64 * NWV) void gemm_skinny_kernel(
     const uint8_t* __restrict__ A, const float* __restrict__ As, const uint8_t* __restrict__ W,
     const float* __restrict__ Ws, uint16_t* __restrict__ out, uint32_t M, uint32_t N, uint32_t K,
     uint32_t Mp, uint32_t units_base, uint32_t units_rem) {
-  __shared__ v4f red[NWV][TN][TM][64];
+  // partial sums of the waves (dynamic LDS: NWV*TN*TM KB)
+  extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
+  v4f(*red)[TN][TM][64] = reinterpret_cast<v4f(*)[TN][TM][64]>(smem);
   const uint32_t lane = threadIdx.x & 63, wave = threadIdx.x >> 6, w = blockIdx.x;
   // this workgroup's columns, in units of 4
   const uint32_t c0 = 4 * (w * units_base + min(w, units_rem));
@@ -1680,8 +1682,10 @@ bool launch_decode(const uint8_t* a, const float* a_s_km, const uint8_t* w, cons
   return true;
 }
 
+// waves per workgroup: 8 where the partial sums of 8 fit in 64 KB, else 4
+// where those of 4 fit in 128 KB (one wave per SIMD), else 2
 constexpr int skinny_waves(int tm, int tn) {
-  return (64 / (tn * tm) >= 8) ? 8 : (64 / (tn * tm) >= 4) ? 4 : 2;
+  return (64 / (tn * tm) >= 8) ? 8 : (128 / (tn * tm) >= 4) ? 4 : 2;
 }
 constexpr int skinny_unroll(int tm, int tn) {
   const int fixed = 4 * tn * tm + 4 * tn + 3 * tm + 20, per = 9 * tn + 9 * tm;
@@ -1697,14 +1701,25 @@ template <int TM, int TN, bool ROW>
 hipError_t launch_skinny_tn(const uint8_t* a, const float* a_s_km, const uint8_t* w,
                             const float* w_s, uint16_t* out, uint32_t M, uint32_t N, uint32_t K,
                             uint32_t grid, uint32_t base, uint32_t rem, hipStream_t s) {
-  // static LDS for the partial sums: NWV*TN*TM KB <= 64 KB.  Registers: about
+  // LDS for the partial sums: NWV*TN*TM KB <= 128 KB.  Registers: about
   // 4*TN*TM accumulators + 4*TN + 3*TM + 20 fixed, 9*TN + 9*TM per K block in
   // flight, within ~200 (two waves per SIMD, NWV = 8) or ~440 (one wave).
   constexpr int NWV = skinny_waves(TM, TN);
   constexpr int U = skinny_unroll(TM, TN);
-  static_assert(NWV * TN * TM <= 64, "LDS for the partial sums");
+  constexpr uint32_t LDS = NWV * TN * TM * 1024;
+  static_assert(LDS <= 128 * 1024, "LDS for the partial sums");
+  if constexpr (LDS > 64 * 1024) {
+    static std::atomic<bool> attr_set{false};  // idempotent: racing threads repeat it
+    if (!attr_set.load(std::memory_order_acquire)) {
+      hipError_t e = hipFuncSetAttribute(
+          reinterpret_cast<const void*>(&gemm_skinny_kernel<TM, TN, NWV, U, ROW>),
+          hipFuncAttributeMaxDynamicSharedMemorySize, LDS);
+      if (e != hipSuccess) return e;
+      attr_set.store(true, std::memory_order_release);
+    }
+  }
   const uint32_t row_tiles = (M + 16 * TM - 1) / (16 * TM);
-  gemm_skinny_kernel<TM, TN, NWV, U, ROW><<<dim3(grid, row_tiles), dim3(64 * NWV), 0, s>>>(
+  gemm_skinny_kernel<TM, TN, NWV, U, ROW><<<dim3(grid, row_tiles), dim3(64 * NWV), LDS, s>>>(
       a, a_s_km, w, w_s, out, M, N, K, m_pad16(M), base, rem);
   return hipGetLastError();
 }
@@ -1775,6 +1790,12 @@ hipError_t launch_gemm_tiled(const uint8_t* a, const float* a_s_km, const uint8_
                              int cfg, bool row_scaled, hipStream_t s) {
   return row_scaled ? launch_gemm_tiled_t<true>(a, a_s_km, w, w_s, out, M, N, K, cfg, s)
                     : launch_gemm_tiled_t<false>(a, a_s_km, w, w_s, out, M, N, K, cfg, s);
+}
+
+uint32_t skinny_columns(uint32_t M, uint32_t N, uint32_t cu_count) {
+  uint32_t grid = 0, base = 0, rem = 0, tn = 0;
+  skinny_grid(M, N, cu_count, grid, base, rem, tn);
+  return 4 * (base + (rem ? 1 : 0));
 }
 
 hipError_t launch_gemm_skinny(const uint8_t* a, const float* a_s_km, const uint8_t* w,
