@@ -1682,14 +1682,30 @@ bool launch_decode(const uint8_t* a, const float* a_s_km, const uint8_t* w, cons
   return true;
 }
 
-// waves per workgroup: 8 where the partial sums of 8 fit in 64 KB, else 4
-// where those of 4 fit in 128 KB (one wave per SIMD), else 2
-constexpr int skinny_waves(int tm, int tn) {
-  return (64 / (tn * tm) >= 8) ? 8 : (128 / (tn * tm) >= 4) ? 4 : 2;
+// Registers of a skinny wave: about 4*TN*TM accumulators + 4*TN + 3*TM + 20
+// fixed, 9*TN + 9*TM per K block in flight.
+constexpr int skinny_fixed_regs(int tm, int tn) { return 4 * tn * tm + 4 * tn + 3 * tm + 20; }
+constexpr int skinny_block_regs(int tm, int tn) { return 9 * tn + 9 * tm; }
+// Two waves per SIMD with two K blocks in flight each, where their partial
+// sums fit in 128 KB of LDS and their registers in ~242: measured against one
+// wave per SIMD with four blocks in flight at TM = 2, TN = 6 (17-32 rows,
+// N = 17408, K = 5120, cold caches): 28.9 / 30.1 / 30.8 against 31.4 / 32.5 /
+// 33.2 us at M = 17 / 25 / 32.
+constexpr bool skinny_two_per_simd(int tm, int tn) {
+  return 8 * tn * tm <= 128 && skinny_fixed_regs(tm, tn) + 2 * skinny_block_regs(tm, tn) <= 242;
 }
+// waves per workgroup: 8 where the partial sums of 8 fit in 64 KB or the
+// rule above holds, else 4 where those of 4 fit in 128 KB (one wave per
+// SIMD), else 2
+constexpr int skinny_waves(int tm, int tn) {
+  return (64 / (tn * tm) >= 8 || skinny_two_per_simd(tm, tn)) ? 8 : (128 / (tn * tm) >= 4) ? 4 : 2;
+}
+// K blocks in flight per wave: what the register budget leaves (~200 a wave
+// at two waves per SIMD, 242 where the rule above admitted the eight waves,
+// ~440 at one)
 constexpr int skinny_unroll(int tm, int tn) {
-  const int fixed = 4 * tn * tm + 4 * tn + 3 * tm + 20, per = 9 * tn + 9 * tm;
-  const int uf = ((skinny_waves(tm, tn) == 8 ? 200 : 440) - fixed) / per;
+  const int budget = skinny_waves(tm, tn) != 8 ? 440 : (64 / (tn * tm) >= 8) ? 200 : 242;
+  const int uf = (budget - skinny_fixed_regs(tm, tn)) / skinny_block_regs(tm, tn);
   return uf > 8 ? 8 : uf < 1 ? 1 : uf;
 }
 // the template arguments the skinny dispatch picks: row tiles TM of 16 rows,
@@ -1701,9 +1717,7 @@ template <int TM, int TN, bool ROW>
 hipError_t launch_skinny_tn(const uint8_t* a, const float* a_s_km, const uint8_t* w,
                             const float* w_s, uint16_t* out, uint32_t M, uint32_t N, uint32_t K,
                             uint32_t grid, uint32_t base, uint32_t rem, hipStream_t s) {
-  // LDS for the partial sums: NWV*TN*TM KB <= 128 KB.  Registers: about
-  // 4*TN*TM accumulators + 4*TN + 3*TM + 20 fixed, 9*TN + 9*TM per K block in
-  // flight, within ~200 (two waves per SIMD, NWV = 8) or ~440 (one wave).
+  // LDS for the partial sums: NWV*TN*TM KB <= 128 KB; registers as above.
   constexpr int NWV = skinny_waves(TM, TN);
   constexpr int U = skinny_unroll(TM, TN);
   constexpr uint32_t LDS = NWV * TN * TM * 1024;
