@@ -1686,23 +1686,23 @@ bool launch_decode(const uint8_t* a, const float* a_s_km, const uint8_t* w, cons
 // fixed, 9*TN + 9*TM per K block in flight.
 constexpr int skinny_fixed_regs(int tm, int tn) { return 4 * tn * tm + 4 * tn + 3 * tm + 20; }
 constexpr int skinny_block_regs(int tm, int tn) { return 9 * tn + 9 * tm; }
-// Two waves per SIMD with two K blocks in flight each, where their partial
-// sums fit in 128 KB of LDS and their registers in ~242: measured against one
-// wave per SIMD with four blocks in flight at TM = 2, TN = 6 (17-32 rows,
-// N = 17408, K = 5120, cold caches): 28.9 / 30.1 / 30.8 against 31.4 / 32.5 /
-// 33.2 us at M = 17 / 25 / 32.
-constexpr bool skinny_two_per_simd(int tm, int tn) {
-  return 8 * tn * tm <= 128 && skinny_fixed_regs(tm, tn) + 2 * skinny_block_regs(tm, tn) <= 242;
-}
-// waves per workgroup: 8 where the partial sums of 8 fit in 64 KB or the
-// rule above holds, else 4 where those of 4 fit in 128 KB (one wave per
-// SIMD), else 2
+// Two waves per SIMD wherever the partial sums of eight fit in 128 KB of LDS,
+// with the K blocks in flight that ~242 registers a wave leave (at least
+// one).  Measured against one wave per SIMD with more blocks in flight (cold
+// caches): TM = 2, TN = 6 (17-32 rows, N = 17408, K = 5120; two blocks
+// against four): 28.9 / 30.1 / 30.8 against 31.4 / 32.5 / 33.2 us at M = 17
+// / 25 / 32; TM = 4, TN = 4 (65-128 rows in 64-row tiles, 64 columns a
+// workgroup; one block against four): 78.4-80.3 against 87.1-90.0 us at
+// N = 5120, K = 17408 and 28.4-30.5 against 32.0-34.2 at N = 6144, K = 5120.
+constexpr bool skinny_two_per_simd(int tm, int tn) { return 8 * tn * tm <= 128; }
+// waves per workgroup: 8 where the rule above holds, else 4 where the
+// partial sums of 4 fit in 128 KB (one wave per SIMD), else 2
 constexpr int skinny_waves(int tm, int tn) {
-  return (64 / (tn * tm) >= 8 || skinny_two_per_simd(tm, tn)) ? 8 : (128 / (tn * tm) >= 4) ? 4 : 2;
+  return skinny_two_per_simd(tm, tn) ? 8 : (128 / (tn * tm) >= 4) ? 4 : 2;
 }
 // K blocks in flight per wave: what the register budget leaves (~200 a wave
-// at two waves per SIMD, 242 where the rule above admitted the eight waves,
-// ~440 at one)
+// at two waves per SIMD where eight waves' partial sums fit in 64 KB, as
+// first tuned; 242 for the wider configurations; ~440 at one wave per SIMD)
 constexpr int skinny_unroll(int tm, int tn) {
   const int budget = skinny_waves(tm, tn) != 8 ? 440 : (64 / (tn * tm) >= 8) ? 200 : 242;
   const int uf = (budget - skinny_fixed_regs(tm, tn)) / skinny_block_regs(tm, tn);
