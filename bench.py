@@ -45,7 +45,8 @@ quantized per 128x128 block.  Prints ONE JSON line:
 
 Other modes (one JSON line each, not the benchmark line): --quant-sweep,
 --dequant, --ffn <workload> (the dense FFN chain), --ffn-sweep (its
-selector), --gemm-sweep (split-K), --cpu-sweep (the CPU oracle baseline
+selector), --gemm-sweep (split-K, cold caches), --gemm-sweep-b2b (split-K up to
+64 rows, back to back), --cpu-sweep (the CPU oracle baseline
 per shape), --copy-mib N.
 
 Only one GPU is used; --gpus above 1 exits with a message.
@@ -121,8 +122,13 @@ def parse():
     p.add_argument("--gemm-sweep", action="store_true",
                    help="the GEMM's single-pass kernels and split-K counts over M at three "
                         "projection shapes with cold caches (the split-K selector's measurement)")
+    p.add_argument("--gemm-sweep-b2b", action="store_true",
+                   help="the GEMM's single pass and split-K counts up to 64 rows at three "
+                        "projection shapes, back to back over rotating weight copies (the "
+                        "split-K selector's measurement for those rows)")
     p.add_argument("--sweep-m", default=None,
-                   help="comma-separated row counts for --gemm-sweep (default: its 15)")
+                   help="comma-separated row counts for --gemm-sweep (default: its 15) or "
+                        "--gemm-sweep-b2b (default: its 14)")
     p.add_argument("--cpu-sweep", action="store_true",
                    help="instead of the benchmark, time the CPU oracle on the host cores: "
                         "quantizer + relayout per quantizer-sweep shape (all threads and one), "
@@ -509,6 +515,49 @@ def gemm_sweep(reps=10, ms=None):
                   flush=True)
             del wsp, x, q, srm, skm, out
         del wq, wsc
+
+
+def gemm_sweep_b2b(R=20, ms=None):
+    """The block-scaled GEMM up to 64 rows at three projection shapes, as
+    layers run in a model: each variant's R launches back to back (one HIP
+    graph, _b2b_us) cycling through copies of the weights that together
+    exceed the last-level cache, so every launch streams its weights from
+    HBM.  Variants: the automatic single-pass kernel and
+    fp8q_gemm_blockscaled_splitk at 2, 3, 4 and 6 splits (and the automatic
+    count); the split count fp8q_gemm_splitk_select picks and whether it is
+    within 3% of the fastest.  Normal activations, quantized by the library;
+    weights normal(0, 0.02), block-quantized."""
+    import torch
+    import w8a8_fp8_block_amd as fp8q
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(7)
+    for N, K in ((5120, 17408), (6144, 5120), (17408, 5120)):
+        wq, wsc = quantize_weights_gpu(torch.randn((N, K), generator=gen, device=dev) * 0.02)
+        w_rot = _rotation(wq)
+        for M in ms or (1, 2, 4, 8, 12, 16, 24, 32, 33, 40, 48, 56, 64, 65):
+            x = torch.randn((M, K), generator=gen, device=dev).to(torch.bfloat16)
+            q = torch.empty((M, K), dtype=torch.uint8, device=dev)
+            srm = torch.empty((M, K // 128), dtype=torch.float32, device=dev)
+            skm = torch.empty((K // 128, fp8q.fp8q_m_pad(M)), dtype=torch.float32, device=dev)
+            fp8q.fp8q_quant_act_kmajor(x, q, srm, skm)
+            out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+            sel = fp8q.fp8q_gemm_splitk_select(M, N, K)
+            t = {"single": _b2b_us(lambda i: fp8q.fp8q_gemm_blockscaled(
+                q, skm, w_rot[i % len(w_rot)], wsc, out), R)[0]}
+            for S in sorted({2, 3, 4, 6} | ({sel} if sel >= 2 else set())):
+                wsp = torch.empty((S * M * N,), dtype=torch.float32, device=dev)
+                t[f"s{S}"] = _b2b_us(lambda i: fp8q.fp8q_gemm_blockscaled_splitk(
+                    q, skm, w_rot[i % len(w_rot)], wsc, out, wsp, splits=S), R)[0]
+                del wsp
+            t = {v: round(u, 2) for v, u in t.items()}
+            best = min(t, key=t.get)
+            chosen = t["single"] if sel < 2 else t[f"s{sel}"]
+            print(json.dumps({"M": M, "N": N, "K": K, "auto_kernel": fp8q.fp8q_gemm_select(M, N, K),
+                              "us": t, "best": best, "splitk_auto": sel,
+                              "rule_ok": chosen <= 1.03 * t[best]}), flush=True)
+            del x, q, srm, skm, out
+        del w_rot, wq, wsc
 
 
 def cpu_sweep():
@@ -1232,6 +1281,9 @@ def main():
         return
     if args.gemm_sweep:
         gemm_sweep(ms=[int(v) for v in args.sweep_m.split(",")] if args.sweep_m else None)
+        return
+    if args.gemm_sweep_b2b:
+        gemm_sweep_b2b(ms=[int(v) for v in args.sweep_m.split(",")] if args.sweep_m else None)
         return
 
     import torch

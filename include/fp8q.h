@@ -251,7 +251,10 @@ fp8q_status fp8q_gemm_blockscaled_ex(const uint8_t *a_e4m3, const float *a_scale
  *    range s covering [s*(K/128)/splits, (s+1)*(K/128)/splits); each tile's
  *    range sums are written in fp32 to the workspace as part[s][M][N], then a
  *    second kernel forms out = bf16_rne(part[0] + part[1] + ... +
- *    part[splits-1]), added in that order;
+ *    part[splits-1]), added in that order.  Up to 64 rows, where W =
+ *    min(max(floor(C/splits), 1), N/16) workgroups a split (C compute units)
+ *    own at most 128 columns each (4*ceil(N/(4W))), the skinny kernel's split
+ *    form computes the range sums, else the 128x128 tiled kernel's;
  *  - stream-K (splits = 0 where fp8q_gemm_streamk_select says 1): the form
  *    of fp8q_gemm_blockscaled_streamk below on one workgroup per CU.
  * Results are reproducible run to run; they differ from the single-pass
@@ -275,14 +278,15 @@ fp8q_status fp8q_gemm_blockscaled_splitk(const uint8_t *a_e4m3, const float *a_s
 /* The split count fp8q_gemm_blockscaled_splitk takes for splits = 0 on a
  * device with C = cu_count compute units, with T = ceil(M/128) * (N/128)
  * tiles of 128x128 and c = min(floor(K/1280), 6) (at least 10 K blocks a
- * split):
- *   min(floor(C / T), c) if that is at least 2 (one workgroup per CU),
- *   else min(floor(2C / T), c) (two per CU)
- * when fp8q_gemm_select_cus does not pick the 256x128 kernel (id 5) and
- * either M > 64 or 33 <= M <= 64 with N*K >= 64 MiB and M above the columns
- * a workgroup of the skinny path owns (at most 4*ceil(N/(4*W)) for its W =
- * min(max(C, ceil(N/128)), N/16) workgroups: 20 at N = 5120, 68 at N =
- * 17408 on 256 CUs); 1 (no split) otherwise or when that count is below 2.
+ * split), when fp8q_gemm_select_cus does not pick the 256x128 kernel (id 5):
+ *  - M > 64: the tiled count, min(floor(C / T), c) if that is at least 2
+ *    (one workgroup per CU), else min(floor(2C / T), c) (two per CU);
+ *  - 8 <= M <= 64 where the automatic kernel is not the decode kernel
+ *    (fp8q_gemm_kernel_name): the largest s <= min(floor(C*L/N), c) whose
+ *    skinny split ranges (4*ceil(N/(4W)) columns, W as above) are at most
+ *    L = 96 columns (M <= 32) or 64 (M > 32) if s >= 2; where no such s
+ *    exists, from M = 24 the tiled count;
+ * 1 (no split) otherwise (M < 8 among them) or when the count is below 2.
  * 0 if N or K is not a positive multiple of 128 or cu_count is 0.  Pure
  * host function. */
 uint32_t fp8q_gemm_splitk_select_cus(uint32_t M, uint32_t N, uint32_t K, uint32_t cu_count);

@@ -342,20 +342,23 @@ def test_splitk_workspace_bytes():
 
 
 def test_splitk_select():
-    """Split count above 64 rows (from 33 rows for a weight matrix of at
-    least 64 MiB whose skinny workgroups own fewer columns than M: 20 at
-    N = 5120, 68 at N = 17408 on 256 CUs), outside the 256x128 kernel's range, with
+    """Split count above 64 rows, outside the 256x128 kernel's range, with
     c = min(floor(K/1280), 6): min(floor(256 / tiles), c) if at least 2,
-    else min(floor(512 / tiles), c), 1 below 2; 0 for a bad N or K."""
+    else min(floor(512 / tiles), c), 1 below 2; from 8 to 64 rows, where the
+    decode kernel does not take the shape, the most splits, at most c, whose
+    skinny column ranges hold at most 96 columns (up to 32 rows) or 64
+    (33-64 rows), else from 24 rows the tiled count; 0 for a bad N or K."""
     def sel(M, N, K):
         return fp8q.fp8q_gemm_splitk_select(M, N, K, 256)
-    for M, want in ((16, 1), (32, 1), (33, 6), (64, 6), (65, 6), (128, 6), (129, 3), (256, 3), (257, 2), (384, 2),
-                    (385, 3), (512, 3), (513, 2), (768, 2), (769, 1), (1168, 1), (2048, 1)):
+    for M, want in ((1, 1), (7, 1), (8, 4), (16, 4), (32, 4), (33, 3), (64, 3), (65, 6), (128, 6), (129, 3),
+                    (256, 3), (257, 2), (384, 2), (385, 3), (512, 3), (513, 2), (768, 2), (769, 1), (1168, 1),
+                    (2048, 1)):
         assert sel(M, 5120, 17408) == want, M
-    for M, want in ((33, 1), (64, 1), (65, 4), (256, 2), (384, 3), (512, 2), (640, 2), (768, 1)):
-        assert sel(M, 6144, 5120) == want, M      # 31 MB of weights: no split up to 64 rows
-    for M, want in ((32, 1), (33, 1), (64, 1), (65, 3), (128, 3), (129, 1)):
-        assert sel(M, 17408, 5120) == want, M   # 68 skinny columns a workgroup: no split to 64 rows
+    for M, want in ((8, 1), (32, 1), (33, 2), (64, 2), (65, 4), (256, 2), (384, 3), (512, 2), (640, 2), (768, 1)):
+        assert sel(M, 6144, 5120) == want, M      # the decode kernel up to 32 rows: no split
+    for M, want in ((16, 1), (23, 1), (24, 3), (33, 3), (64, 3), (65, 3), (128, 3), (129, 1)):
+        assert sel(M, 17408, 5120) == want, M   # skinny ranges too wide: the tiled count from 24 rows
+    assert sel(25, 6144, 8192) == 4        # 96 columns a workgroup
     assert sel(300, 128, 2560) == 2        # K/1280 = 2 caps it
     assert sel(300, 128, 2432) == 1        # fewer than 20 K blocks: no split
     assert sel(4576, 5120, 17408) == 1     # the 256x128 kernel's pick: no split

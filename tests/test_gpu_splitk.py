@@ -127,12 +127,17 @@ def test_splitk_repeatable(orc):
         assert np.array_equal(o1, o2)
 
 
-@pytest.mark.parametrize("M,N,K", [(512, 5120, 17408), (200, 6144, 5120), (48, 5120, 17408)])
+@pytest.mark.parametrize("M,N,K", [(512, 5120, 17408), (200, 6144, 5120), (48, 5120, 17408),
+                                   (16, 5120, 17408), (25, 6144, 8192), (40, 17408, 5120)])
 def test_splitk_projection_shapes_full(orc, M, N, K):
-    """Medium row counts at the down- and a gate/up-projection shape (48 rows:
-    split from 33 rows for a weight matrix of 64 MiB or more whose skinny
-    workgroups own fewer columns than that: 20 at N = 5120), with the
-    automatic split count and one more: all M*N outputs against the oracle."""
+    """Medium and decode row counts at the down- and gate/up-projection
+    shapes, with the automatic split count, 2 and one above the automatic
+    count: all M*N outputs against the oracle.  Up to 64 rows the splits run
+    the skinny kernel's split form where its column ranges hold at most 128
+    columns (48 rows: 2, 3 and 4 splits of 40, 64 and 80 columns a
+    workgroup; 16 rows: 2, 4 and 5, 40 to 104 columns; 25 rows at N = 6144,
+    K = 8192: 2, 4 and 5), else the tiled split form (40 rows at N = 17408:
+    2, 3 and 4 splits, whose skinny ranges would hold 136 columns or more)."""
     a, a_s, wq, ws = _random_operands(orc, M, N, K, M + K, "laplace")
     log(f"oracle M={M} N={N} K={K}: full fp64 product")
     ref = orc.gemm_ref(a, a_s, wq, ws)
@@ -151,8 +156,9 @@ def test_proj_splitk(orc, M, N, K):
     fp8q_proj writes them (bit-exact against the oracle), the output equal bit
     for bit to fp8q_gemm_blockscaled_splitk (splits = 0) on those codes, and
     within the projection tolerance of the oracle; where the selector does not
-    split (M = 40; M = 64 at N = 17408, whose skinny workgroups own 68
-    columns) the workspace may be absent and the output is fp8q_proj's."""
+    split (M = 40 at K = 2048: fewer than 20 K blocks) the workspace may be
+    absent and the output is fp8q_proj's.  M = 64 at N = 17408 takes the
+    tiled split form (3 splits)."""
     rng = np.random.default_rng(M + N)
     x = synth.f32_to_bf16_bits((rng.standard_normal((M, K)) *
                                 np.exp(rng.uniform(-2, 2, (M, 1)))).astype(np.float32))

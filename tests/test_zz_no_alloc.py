@@ -34,8 +34,9 @@ def test_noalloc_splitk_matches_the_workspace_entry(orc):
     L = fp8q.lib()
     stream = torch.cuda.current_stream().cuda_stream
     # (M, N, K, splits): the first fills 31.5 MB of the 32 MiB scratch with
-    # the automatic count (3); the second is smaller, with a forced count
-    for M, N, K, splits in ((512, 5120, 17408, 0), (200, 1024, 5120, 3)):
+    # the automatic count (3); the second is smaller, with a forced count;
+    # the third, smaller again, runs the skinny kernel's split form (48 rows)
+    for M, N, K, splits in ((512, 5120, 17408, 0), (200, 1024, 5120, 3), (48, 5120, 17408, 0)):
         a, a_s, wq, ws = _operands(orc, M, N, K, M + N)
         eff = splits or fp8q.fp8q_gemm_splitk_select(M, N, K)
         assert eff >= 2

@@ -256,42 +256,59 @@ int gemm_auto_kernel(uint32_t M, uint32_t N, uint32_t cus) {
   return c_pp <= c_128 ? 5 : 1;
 }
 
-// Split-K (fp8q_gemm_blockscaled_splitk): splits = floor(CUs / tiles) when
-// that is at least 2 (the split grid fits one workgroup per CU and runs the
-// three-stage form), else floor(2 CUs / tiles) (one round of two 128x128
-// workgroups per CU, two stages), at most K/1280 (10 K blocks a split) and
-// 6, for more than kSplitMinM rows and wherever the single-pass choice is
-// not the 256 x 128 kernel; from kSplitMidM + 1 to kSplitMinM rows only for
-// a weight matrix of at least kSplitMidMinWeights bytes.  Cold
-// caches (bench.py --gemm-sweep, 256 CUs), us single-pass -> split-K: N=5120,
+// Split-K (fp8q_gemm_blockscaled_splitk).  Above kSplitMinM rows, wherever
+// the single-pass choice is not the 256 x 128 kernel: the 128x128 tiled
+// kernel's split form with splits = floor(CUs / tiles) when that is at least
+// 2 (the split grid fits one workgroup per CU and runs the three-stage form),
+// else floor(2 CUs / tiles) (one round of two workgroups per CU, two
+// stages), at most K/1280 (10 K blocks a split) and 6.  Cold caches
+// (bench.py --gemm-sweep, 256 CUs), us single-pass -> split-K: N=5120,
 // K=17408: 87 -> 46 at M=65, 135 -> 55 at M=192, 143 -> 73 at M=384, 143 ->
 // 87 at M=512, 144 -> 109 at M=768; N=6144, K=5120: 32 -> 23 at M=65, 47 ->
 // 32 at M=192, 51 -> 39 at M=384; N=17408, K=5120: 55 -> 47 at M=65.  A
 // count past one round (M=512, N=5120: 4 splits, 640 workgroups) was up to
-// 30% slower than the one below it; beyond 512 tiles no count helped.  At
-// M = 33 .. 64 (the fragment-layout skinny kernel with one 64-row tile) the
-// split pays only where the weight matrix is large (at least
-// kSplitMidMinWeights) and the rows outnumber the skinny kernel's columns
-// per workgroup, so that its activation reads exceed its weight reads:
-// N = 5120, K = 17408 (20 columns a workgroup): split 42.4 / 42.8 / 44.3 us
-// against skinny 43.9 / 49.1 / 54.2 at M = 33 / 48 / 64; N = 17408,
-// K = 5120 (68 columns): skinny 37.5 / 38.9 / 40.3 against split 43.6 /
-// 45.4 / 46.7; N = 6144, K = 5120 (31 MB): skinny 18.6-21.8 against split
-// 20.5-22.1.
+// 30% slower than the one below it; beyond 512 tiles no count helped.
+// Up to kSplitMinM rows, where the decode kernel does not take the shape and
+// from kSplitSkinnyMinM rows: the skinny kernel's split form
+// (launch_skinny_split) with the most splits, at most K/1280 and 6, whose
+// column ranges stay within 96 columns a workgroup up to kSplitMidM rows and
+// 64 beyond; where no count fits (wide N), from kSplitTiledMinM rows the
+// tiled split form with the count of the rule above.  Fixed on back-to-back
+// launches over rotating weight copies (bench.py --gemm-sweep-b2b, 256 CUs,
+// us single-pass -> split): N = 5120, K = 17408: 24.7 -> 24.5 (4 splits) at
+// M = 8, 27.4 -> 25.2 at 16, 35.4 -> 27.3 at 32, 41.1 -> 33.0 (3 splits) at
+// 33, 51.5 -> 36.1 at 64, while at M <= 4 the single pass was 0.5-1.2 us
+// ahead and 6 splits (124 columns) 1-2 us behind 4; N = 17408, K = 5120
+// (tiled, 3 splits): 26.5 -> 24.8 at M = 24, 34.6 -> 26.4 at 33, 37.1 ->
+// 29.8 at 64, 0.2-1.4 us behind at M <= 16; N = 6144, K = 5120: 2 splits
+// 16.4-18.0 against 16.3-19.4 at M = 33-64.  With a 512 MiB write before
+// each call (bench.py --gemm-sweep) the form that streams the weights
+// fastest loses the most (N = 17408, M = 32: the tiled split 43.4 against
+// the skinny kernel's 31.1 us; N = 6144, M = 16: the decode kernel 17.0
+// against 4 splits' 16.0), probably because the write leaves the
+// last-level cache full of dirty lines whose write-back shares HBM with the
+// weight stream.  Layers run back to back in a model, so the back-to-back
+// figures decide.
 constexpr uint32_t kSplitMinBlocks = 10;
 constexpr uint32_t kSplitMax = 6;
 constexpr uint32_t kSplitMinM = 64;
 constexpr uint32_t kSplitMidM = 32;
-constexpr uint64_t kSplitMidMinWeights = 64ull << 20;
+constexpr uint32_t kSplitSkinnyMinM = 8;
+constexpr uint32_t kSplitTiledMinM = 24;
 constexpr uint32_t kSplitMaxUser = 64;  // bound of an explicit split count
 
 uint32_t splitk_auto(uint32_t M, uint32_t N, uint32_t K, uint32_t cus) {
-  if (M <= kSplitMidM || gemm_auto_kernel(M, N, cus) == 5) return 1;
-  if (M <= kSplitMinM &&
-      ((uint64_t)N * K < kSplitMidMinWeights || M <= skinny_columns(M, N, cus)))
-    return 1;
-  const uint64_t tiles = (uint64_t)((M + 127) / 128) * (N / 128);
+  if (M == 0 || gemm_auto_kernel(M, N, cus) == 5) return 1;
   const uint64_t cap = std::min<uint64_t>(K / kGroup / kSplitMinBlocks, kSplitMax);
+  if (M <= kSplitMinM) {
+    if (M < kSplitSkinnyMinM || decode_takes(M, N, K, cus)) return 1;
+    const uint32_t colmax = M <= kSplitMidM ? 96 : 64;
+    uint64_t sk = std::min<uint64_t>((uint64_t)cus * colmax / N, cap);
+    while (sk >= 2 && skinny_split_columns(N, (uint32_t)sk, cus) > colmax) --sk;
+    if (sk >= 2) return (uint32_t)sk;
+    if (M < kSplitTiledMinM) return 1;
+  }
+  const uint64_t tiles = (uint64_t)((M + 127) / 128) * (N / 128);
   // prefer a count whose grid fits one workgroup per CU (the three-stage
   // form), else one round of two per CU
   const uint64_t s1 = std::min<uint64_t>(cus / tiles, cap);

@@ -82,9 +82,21 @@ uint64_t gemm_streamk_workspace_bytes(uint32_t cus);
 hipError_t launch_gemm_streamk(const uint8_t* a, const float* a_s_km, const uint8_t* w,
                                const float* w_s, uint16_t* out, void* workspace, uint32_t M,
                                uint32_t N, uint32_t K, uint32_t cus, bool forced, hipStream_t s);
-// Columns (weight rows) a workgroup of the skinny path owns at most for this
-// shape (one workgroup per CU up to 64 rows).
-uint32_t skinny_columns(uint32_t M, uint32_t N, uint32_t cu_count);
+// Split-K form of the skinny kernel for M <= 64 (block-scaled weights): the
+// partials of `splits` K ranges in part [splits, M, N], then the ordered
+// reduction into out.  False, with nothing launched, where M > 64 or the
+// column ranges of cus / splits workgroups would exceed 128 columns.
+bool launch_skinny_split(const uint8_t* a, const float* a_s_km, const uint8_t* w,
+                         const float* w_s, uint16_t* out, float* part, uint32_t M, uint32_t N,
+                         uint32_t K, uint32_t splits, uint32_t cus, hipStream_t s,
+                         hipError_t& err);
+// Whether the skinny path runs the decode kernel (the whole weight slice of
+// a workgroup in LDS) for this shape.
+bool decode_takes(uint32_t M, uint32_t N, uint32_t K, uint32_t cu_count);
+// Workgroups per split and columns a workgroup owns at most in the skinny
+// kernel's split form with `splits` K ranges on `cus` compute units.
+uint32_t skinny_split_grid(uint32_t N, uint32_t splits, uint32_t cus);
+uint32_t skinny_split_columns(uint32_t N, uint32_t splits, uint32_t cus);
 hipError_t launch_gemm_skinny(const uint8_t* a, const float* a_s_km, const uint8_t* w,
                               const float* w_s, uint16_t* out, uint32_t M, uint32_t N,
                               uint32_t K, uint32_t cu_count, bool row_scaled, hipStream_t s);

@@ -382,6 +382,10 @@ hipError_t launch_splitk_128_t(const uint8_t* a, const float* a_s_km, const uint
                                uint32_t N, uint32_t K, uint32_t splits, uint32_t cus,
                                hipStream_t s) {
   if (N % 128 != 0 || splits < 2 || splits > K / kGroup) return hipErrorInvalidValue;
+  // up to 64 rows: the skinny kernel's split form (its weight loads go to
+  // registers, and its ranges of columns hold the rows' activations once)
+  hipError_t serr = hipSuccess;
+  if (launch_skinny_split(a, a_s_km, w, w_s, out, part, M, N, K, splits, cus, s, serr)) return serr;
   const uint64_t wgs = (uint64_t)((M + 127) / 128) * (N / 128) * splits;
   hipError_t e = wgs <= cus
                      ? launch_splitk_cfg<3>(a, a_s_km, w, w_s, part, M, N, K, splits, s)
@@ -1363,11 +1367,15 @@ hipError_t launch_pp_sk_cfg(const uint8_t* a, const float* a_s_km, const uint8_t
 // loaded once for all tiles, and the NWV partial tiles are summed through
 // LDS in wave order.
 // ------------------------------------------------------------------------
-template <int TM, int TN, int NWV, int U, bool ROW>
+// SPLIT: the K blocks are cut into gridDim.z contiguous ranges; workgroup
+// (w, y, z) sums range z and stores its fp32 partial tile to part[z][M][N],
+// which splitk_reduce_kernel adds in split order (block-scaled weights only).
+template <int TM, int TN, int NWV, int U, bool ROW, bool SPLIT = false>
 __global__ __launch_bounds__(64 * NWV) void gemm_skinny_kernel(
     const uint8_t* __restrict__ A, const float* __restrict__ As, const uint8_t* __restrict__ W,
     const float* __restrict__ Ws, uint16_t* __restrict__ out, uint32_t M, uint32_t N, uint32_t K,
-    uint32_t Mp, uint32_t units_base, uint32_t units_rem) {
+    uint32_t Mp, uint32_t units_base, uint32_t units_rem, float* __restrict__ part = nullptr) {
+  static_assert(!(SPLIT && ROW), "split form for block-scaled weights only");
   // partial sums of the waves (dynamic LDS: NWV*TN*TM KB)
   extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
   v4f(*red)[TN][TM][64] = reinterpret_cast<v4f(*)[TN][TM][64]>(smem);
@@ -1405,13 +1413,16 @@ __global__ __launch_bounds__(64 * NWV) void gemm_skinny_kernel(
 #pragma unroll
     for (int tm = 0; tm < TM; ++tm) acc[t][tm] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
-  for (uint32_t kb0 = wave; kb0 < G; kb0 += NWV * U) {
+  // this workgroup's K blocks [kbeg, kend): all of them, or split z's range
+  const uint32_t kbeg = SPLIT ? blockIdx.z * G / gridDim.z : 0;
+  const uint32_t kend = SPLIT ? (blockIdx.z + 1) * G / gridDim.z : G;
+  for (uint32_t kb0 = kbeg + wave; kb0 < kend; kb0 += NWV * U) {
     v8i wf[U][TN], af[U][TM];
     float as[U][TM], ws[U][TN];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const uint32_t k = kb0 + u * NWV;
-      if (k < G) {
+      if (k < kend) {
 #pragma unroll
         for (int t = 0; t < TN; ++t) {
           if ((uint32_t)t < nt) {
@@ -1434,7 +1445,7 @@ __global__ __launch_bounds__(64 * NWV) void gemm_skinny_kernel(
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      if (kb0 + u * NWV < G) {
+      if (kb0 + u * NWV < kend) {
 #pragma unroll
         for (int t = 0; t < TN; ++t) {
           if ((uint32_t)t < nt) {
@@ -1471,7 +1482,12 @@ __global__ __launch_bounds__(64 * NWV) void gemm_skinny_kernel(
           s *= v4f{r.x, r.y, r.z, r.w};
         }
       }
-      if (m < M && n < c1) *reinterpret_cast<uint2*>(out + (uint64_t)m * N + n) = pack_bf16x4(s);
+      if (m < M && n < c1) {
+        if constexpr (SPLIT)
+          *reinterpret_cast<v4f*>(part + ((uint64_t)blockIdx.z * M + m) * N + n) = s;
+        else
+          *reinterpret_cast<uint2*>(out + (uint64_t)m * N + n) = pack_bf16x4(s);
+      }
     }
   }
 }
@@ -1713,10 +1729,11 @@ constexpr int skinny_unroll(int tm, int tn) {
 uint32_t skinny_tm(uint32_t M) { return M <= 16 ? 1 : M <= 32 ? 2 : 4; }
 uint32_t skinny_tn(uint32_t tn) { return tn <= 2 ? 2 : tn <= 4 ? 4 : tn <= 6 ? 6 : 8; }
 
-template <int TM, int TN, bool ROW>
+template <int TM, int TN, bool ROW, bool SPLIT = false>
 hipError_t launch_skinny_tn(const uint8_t* a, const float* a_s_km, const uint8_t* w,
                             const float* w_s, uint16_t* out, uint32_t M, uint32_t N, uint32_t K,
-                            uint32_t grid, uint32_t base, uint32_t rem, hipStream_t s) {
+                            uint32_t grid, uint32_t base, uint32_t rem, hipStream_t s,
+                            uint32_t splits = 1, float* part = nullptr) {
   // LDS for the partial sums: NWV*TN*TM KB <= 128 KB; registers as above.
   constexpr int NWV = skinny_waves(TM, TN);
   constexpr int U = skinny_unroll(TM, TN);
@@ -1726,26 +1743,31 @@ hipError_t launch_skinny_tn(const uint8_t* a, const float* a_s_km, const uint8_t
     static std::atomic<bool> attr_set{false};  // idempotent: racing threads repeat it
     if (!attr_set.load(std::memory_order_acquire)) {
       hipError_t e = hipFuncSetAttribute(
-          reinterpret_cast<const void*>(&gemm_skinny_kernel<TM, TN, NWV, U, ROW>),
+          reinterpret_cast<const void*>(&gemm_skinny_kernel<TM, TN, NWV, U, ROW, SPLIT>),
           hipFuncAttributeMaxDynamicSharedMemorySize, LDS);
       if (e != hipSuccess) return e;
       attr_set.store(true, std::memory_order_release);
     }
   }
   const uint32_t row_tiles = (M + 16 * TM - 1) / (16 * TM);
-  gemm_skinny_kernel<TM, TN, NWV, U, ROW><<<dim3(grid, row_tiles), dim3(64 * NWV), LDS, s>>>(
-      a, a_s_km, w, w_s, out, M, N, K, m_pad16(M), base, rem);
+  gemm_skinny_kernel<TM, TN, NWV, U, ROW, SPLIT>
+      <<<dim3(grid, row_tiles, splits), dim3(64 * NWV), LDS, s>>>(a, a_s_km, w, w_s, out, M, N, K,
+                                                                  m_pad16(M), base, rem, part);
   return hipGetLastError();
 }
 
-template <int TM, bool ROW>
+template <int TM, bool ROW, bool SPLIT = false>
 hipError_t launch_skinny_tm(const uint8_t* a, const float* a_s_km, const uint8_t* w,
                             const float* w_s, uint16_t* out, uint32_t M, uint32_t N, uint32_t K,
-                            uint32_t grid, uint32_t base, uint32_t rem, uint32_t tn, hipStream_t s) {
-  if (tn <= 2) return launch_skinny_tn<TM, 2, ROW>(a, a_s_km, w, w_s, out, M, N, K, grid, base, rem, s);
-  if (tn <= 4) return launch_skinny_tn<TM, 4, ROW>(a, a_s_km, w, w_s, out, M, N, K, grid, base, rem, s);
-  if (tn <= 6) return launch_skinny_tn<TM, 6, ROW>(a, a_s_km, w, w_s, out, M, N, K, grid, base, rem, s);
-  return launch_skinny_tn<TM, 8, ROW>(a, a_s_km, w, w_s, out, M, N, K, grid, base, rem, s);
+                            uint32_t grid, uint32_t base, uint32_t rem, uint32_t tn, hipStream_t s,
+                            uint32_t splits = 1, float* part = nullptr) {
+#define FP8Q_SKINNY(TN_) \
+  launch_skinny_tn<TM, TN_, ROW, SPLIT>(a, a_s_km, w, w_s, out, M, N, K, grid, base, rem, s, splits, part)
+  if (tn <= 2) return FP8Q_SKINNY(2);
+  if (tn <= 4) return FP8Q_SKINNY(4);
+  if (tn <= 6) return FP8Q_SKINNY(6);
+  return FP8Q_SKINNY(8);
+#undef FP8Q_SKINNY
 }
 
 }  // namespace
@@ -1806,10 +1828,19 @@ hipError_t launch_gemm_tiled(const uint8_t* a, const float* a_s_km, const uint8_
                     : launch_gemm_tiled_t<false>(a, a_s_km, w, w_s, out, M, N, K, cfg, s);
 }
 
-uint32_t skinny_columns(uint32_t M, uint32_t N, uint32_t cu_count) {
-  uint32_t grid = 0, base = 0, rem = 0, tn = 0;
+bool decode_takes(uint32_t M, uint32_t N, uint32_t K, uint32_t cu_count) {
+  uint32_t grid = 0, base = 0, rem = 0, tn = 0, tm = 0, gw = 0, lds = 0;
   skinny_grid(M, N, cu_count, grid, base, rem, tn);
-  return 4 * (base + (rem ? 1 : 0));
+  return decode_plan(M, K, base, rem, tm, gw, lds);
+}
+
+uint32_t skinny_split_grid(uint32_t N, uint32_t splits, uint32_t cus) {
+  return max(1u, min(max(cus / max(splits, 1u), 1u), N / 16));
+}
+
+uint32_t skinny_split_columns(uint32_t N, uint32_t splits, uint32_t cus) {
+  const uint32_t units = N / 4, grid = skinny_split_grid(N, splits, cus);
+  return 4 * ((units + grid - 1) / grid);
 }
 
 hipError_t launch_gemm_skinny(const uint8_t* a, const float* a_s_km, const uint8_t* w,
@@ -1817,6 +1848,37 @@ hipError_t launch_gemm_skinny(const uint8_t* a, const float* a_s_km, const uint8
                               uint32_t cu_count, bool row_scaled, hipStream_t s) {
   return row_scaled ? launch_gemm_skinny_t<true>(a, a_s_km, w, w_s, out, M, N, K, cu_count, s)
                     : launch_gemm_skinny_t<false>(a, a_s_km, w, w_s, out, M, N, K, cu_count, s);
+}
+
+// Split-K form of the skinny kernel (up to 64 rows, block-scaled weights):
+// splits * W workgroups, W = cus / splits column ranges (at least 16 columns
+// each, at most 128), each summing its split's K range into part[split];
+// then the reduction.  False (nothing launched) where the ranges would be
+// wider than 128 columns.
+bool launch_skinny_split(const uint8_t* a, const float* a_s_km, const uint8_t* w,
+                         const float* w_s, uint16_t* out, float* part, uint32_t M, uint32_t N,
+                         uint32_t K, uint32_t splits, uint32_t cus, hipStream_t s,
+                         hipError_t& err) {
+  if (M == 0 || M > 64 || splits < 2) return false;
+  const uint32_t units = N / 4;
+  const uint32_t grid = skinny_split_grid(N, splits, cus);
+  const uint32_t base = units / grid, rem = units % grid;
+  const uint32_t cols = skinny_split_columns(N, splits, cus);
+  if (cols > 128) return false;
+  const uint32_t tn = (cols + 15) / 16;
+  switch ((M + 15) / 16) {
+    case 1: err = launch_skinny_tm<1, false, true>(a, a_s_km, w, w_s, nullptr, M, N, K, grid, base, rem, tn, s, splits, part); break;
+    case 2: err = launch_skinny_tm<2, false, true>(a, a_s_km, w, w_s, nullptr, M, N, K, grid, base, rem, tn, s, splits, part); break;
+    default: err = launch_skinny_tm<4, false, true>(a, a_s_km, w, w_s, nullptr, M, N, K, grid, base, rem, tn, s, splits, part); break;
+  }
+  if (err != hipSuccess) return true;
+  const uint64_t quads = (uint64_t)M * N / 4;
+  const uint64_t blocks = (quads + 255) / 256;
+  const uint32_t rgrid = (uint32_t)(blocks < 4096 ? blocks : 4096);
+  splitk_reduce_kernel<<<dim3(rgrid), dim3(256), 0, s>>>(reinterpret_cast<const v4f*>(part),
+                                                         reinterpret_cast<uint2*>(out), quads, splits);
+  err = hipGetLastError();
+  return true;
 }
 
 void gemm_skinny_kernel_name(uint32_t M, uint32_t N, uint32_t K, uint32_t cu_count,
