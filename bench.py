@@ -991,8 +991,11 @@ def measure_projection(w, steps, warmup, per_row=False, comparators=False, cpu_b
     x_rot, w_rot = _rotation(x), _rotation(wq)
 
     # timed step j records events 3j+1 (after the quantizer), 3j+2 (after the
-    # relayout) and 3j+3 (after the GEMM); event 3j, recorded by the step
-    # before (event 0 by the first), opens its quantizer interval
+    # relayout; not where the quantizer writes the K-major scales itself: an
+    # event record right behind another costs ~4 us of device time, and the
+    # GEMM interval then opens at 3j+1) and 3j+3 (after the GEMM); event 3j,
+    # recorded by the step before (event 0 by the first), opens its quantizer
+    # interval
     def step(i, ev=None):
         xi, wi = x_rot[i % len(x_rot)], w_rot[i % len(w_rot)]
         j = i - warmup
@@ -1004,7 +1007,7 @@ def measure_projection(w, steps, warmup, per_row=False, comparators=False, cpu_b
         if ev: ev.record(3 * j + 1, stream)
         if not fused:
             fp8q.fp8q_scale_to_kmajor(act_s, act_km)
-        if ev: ev.record(3 * j + 2, stream)
+        if ev and not fused: ev.record(3 * j + 2, stream)
         gemm(act_q, act_km, wi, ws, out)
         if ev: ev.record(3 * j + 3, stream)
 
@@ -1052,8 +1055,9 @@ def measure_projection(w, steps, warmup, per_row=False, comparators=False, cpu_b
     # of the two is taken.
     ms_per_step = (max(gpu_ms, wall * 1e3) if spin_us else gpu_ms) / steps
     quant_us = np.array([evs.elapsed_us(3 * i, 3 * i + 1) for i in range(steps)])
-    relay_us = np.array([evs.elapsed_us(3 * i + 1, 3 * i + 2) for i in range(steps)])
-    gemm_us = np.array([evs.elapsed_us(3 * i + 2, 3 * i + 3) for i in range(steps)])
+    g0 = 1 if fused else 2
+    relay_us = None if fused else np.array([evs.elapsed_us(3 * i + 1, 3 * i + 2) for i in range(steps)])
+    gemm_us = np.array([evs.elapsed_us(3 * i + g0, 3 * i + 3) for i in range(steps)])
     step_clock = clock.result()
     # the same step captured R times into one HIP graph (no host launch gaps)
     step_graph_us, step_graph_how = _b2b_us(lambda i: step(i), R)

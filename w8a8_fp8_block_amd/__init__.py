@@ -147,16 +147,30 @@ def _optr(t) -> int:
     return 0 if t is None else _ptr(t)
 
 
+_raw_stream = None
+
+
 def _stream(stream=None) -> int:
+    """The HIP stream handle to launch on: `stream`'s, else torch's current
+    stream on the current device (read through torch's raw-handle query
+    where the build has it: ~0.4 us against ~2.7 us for building a Stream
+    object, per call, on the host)."""
+    global _raw_stream
     import torch
-    s = torch.cuda.current_stream() if stream is None else stream
-    return s.cuda_stream
+    if stream is not None:
+        return stream.cuda_stream
+    if _raw_stream is None:
+        q = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+        _raw_stream = ((lambda: q(torch.cuda.current_device())) if q is not None
+                       else (lambda: torch.cuda.current_stream().cuda_stream))
+    return _raw_stream()
 
 
 def _dims(t, nd):
-    if t.dim() != nd:
-        raise ValueError(f"expected a {nd}-d tensor, got shape {tuple(t.shape)}")
-    return tuple(int(d) for d in t.shape)
+    shape = t.shape
+    if len(shape) != nd:
+        raise ValueError(f"expected a {nd}-d tensor, got shape {tuple(shape)}")
+    return shape
 
 
 # ------------------------------------------------------------------ API
