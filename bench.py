@@ -730,6 +730,15 @@ def m_pad(m):
     return (m + 15) // 16 * 16
 
 
+def quant_kernel_name(M, K, fused):
+    """The quantizer kernel fp8q_proj runs: with both scale layouts the flat
+    kernel up to 2^17 scale groups and its tiled form beyond."""
+    if not fused:
+        return "quant_a_kernel"
+    return ("quant_a_tile_kernel" if M * (K // 128) > 1 << 17 else "quant_a_kernel") + \
+        " (both scale layouts)"
+
+
 def quant_bytes(M, K):
     """Algorithmic bytes of the quantizer: 2 read + 1 written per element and
     one fp32 scale per 128-group."""
@@ -1108,7 +1117,7 @@ def measure_projection(w, steps, warmup, per_row=False, comparators=False, cpu_b
         roofline["back_to_back_shader_ghz"] = gemm_b2b_clock["shader_ghz"]
     qb = quant_bytes(M, K) + (4 * m_pad(M) * G if fused else 0)
     qavg = float(np.mean(quant_us))
-    act_quant = {"kernel": "quant_a_kernel (K-major scales too)" if fused else "quant_a_kernel",
+    act_quant = {"kernel": quant_kernel_name(M, K, fused),
                  "achieved": round(qb / qavg / 1e3, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                  "frac": round(qb / qavg / 1e3 / HBM_PEAK_GBS, 4),
                  "avg_launch_us": round(qavg, 2), **_pct(quant_us),
@@ -1211,8 +1220,9 @@ def _comparators(fp8q, dev, stream, x, act_q, wq, ws, per_row, M, N, K, gemm_b2b
 
 def measure_quant_shape(w, R=20, cpu_budget=0.3):
     """The act-quant + scale-relayout step on one quantizer-sweep shape, as
-    fp8q_proj runs it (one kernel writing both scale layouts up to 2^17 scale
-    groups, else the quantizer and the relayout): back-to-back launches over
+    fp8q_proj runs it (one kernel writing both scale layouts up to 2^19 scale
+    groups, else the quantizer and the relayout; with the row-major-only
+    quantizer timed beside the one kernel, for reference): back-to-back launches over
     rotating input copies (at least 600 MB where 64 copies reach it), the
     quantizer's GB/s against the HBM peak, and the oracle on a bounded
     sample."""
@@ -1230,6 +1240,7 @@ def measure_quant_shape(w, R=20, cpu_budget=0.3):
     if fused:
         tq, how = _b2b_us(lambda i: fp8q.fp8q_quant_act_kmajor(x_rot[i % len(x_rot)], q, s, km), R)
         tr = 0.0
+        t_rm, _ = _b2b_us(lambda i: fp8q.fp8q_quant_act(x_rot[i % len(x_rot)], q, s), R)
     else:
         tq, how = _b2b_us(lambda i: fp8q.fp8q_quant_act(x_rot[i % len(x_rot)], q, s), R)
         tr, _ = _b2b_us(lambda i: fp8q.fp8q_scale_to_kmajor(s, km), R)
@@ -1237,7 +1248,8 @@ def measure_quant_shape(w, R=20, cpu_budget=0.3):
     qb = quant_bytes(M, K) + (4 * m_pad(M) * G if fused else 0)
     rb = 4 * M * G + 4 * m_pad(M) * G
     e = {"M": M, "K": K, "path": "fused (both scale layouts)" if fused else "quantizer + relayout",
-         "roofline": {"bound": "hbm", "kernel": "quant_a_kernel", "achieved": round(qb / tq / 1e3, 1),
+         "roofline": {"bound": "hbm", "kernel": quant_kernel_name(M, K, fused),
+                      "achieved": round(qb / tq / 1e3, 1),
                       "peak": HBM_PEAK_GBS, "unit": "GB/s",
                       "frac": round(qb / tq / 1e3 / HBM_PEAK_GBS, 4), "traffic": None,
                       "back_to_back_us": round(tq, 2), "back_to_back_method": B2B_METHOD[how],
@@ -1246,6 +1258,13 @@ def measure_quant_shape(w, R=20, cpu_budget=0.3):
          "step_GBs": round((qb + (rb if not fused else 0)) / (tq + tr) / 1e3, 1)}
     if not fused:
         e["relayout_back_to_back_us"] = round(tr, 2)
+    else:
+        # the row-major-only quantizer (fp8q_quant_act, no K-major output) on
+        # the same input: what the step would pay before a separate relayout
+        qrm = quant_bytes(M, K)
+        e["rowmajor_quantizer"] = {"kernel": "quant_a_kernel (row-major scales only)",
+                                   "back_to_back_us": round(t_rm, 2),
+                                   "frac": round(qrm / t_rm / 1e3 / HBM_PEAK_GBS, 4)}
     if cpu_budget:
         e["cpu_baseline"] = cpu_baseline_quant(w, x_bits, cpu_budget)
     return e

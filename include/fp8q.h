@@ -436,7 +436,7 @@ fp8q_status fp8q_gemm_bf16(const uint16_t *x_bf16, const uint16_t *w_bf16,
 /* ----------------------------------------------------------- projection */
 
 /* 1 if fp8q_proj quantizes with the fused kernel that writes both scale
- * layouts (M*(K/128) <= 2^17 scale groups), 0 if it runs the quantizer and
+ * layouts (M*(K/128) <= 2^19 scale groups), 0 if it runs the quantizer and
  * the relayout separately.  Pure host function. */
 int fp8q_proj_quant_fused(uint32_t M, uint32_t K);
 
@@ -543,7 +543,7 @@ size_t fp8q_ffn_workspace_bytes(uint32_t M, uint32_t H, uint32_t I, int variant)
  *                    variant 2 gate and up) afterwards
  *   variant          0 auto (fp8q_ffn_select), 1 fused gate/up, 2 separate;
  *                    both give bit-identical results
- * Launches: the quantizer (and the scale relayout beyond 2^17 scale groups,
+ * Launches: the quantizer (and the scale relayout beyond 2^19 scale groups,
  * as fp8q_proj), the gate/up stage, the down GEMM (split-K, as
  * fp8q_gemm_blockscaled_splitk with splits = 0, where that splits); all on
  * `stream`.

@@ -184,13 +184,13 @@ def test_selectors_default_to_a_full_device_without_one():
 
 
 def test_proj_quant_fused():
-    """fp8q_proj fuses the relayout into the quantizer up to 2^17 scale groups."""
+    """fp8q_proj fuses the relayout into the quantizer up to 2^19 scale groups."""
     assert fp8q.fp8q_proj_quant_fused(16, 5120)
-    assert fp8q.fp8q_proj_quant_fused(1168, 5120)           # 46720 groups
-    assert not fp8q.fp8q_proj_quant_fused(1168, 17408)      # 158848 groups
-    assert fp8q.fp8q_proj_quant_fused(3276, 5120)           # 131040 groups
-    assert not fp8q.fp8q_proj_quant_fused(3277, 5120)       # 131080 groups
-    assert not fp8q.fp8q_proj_quant_fused(4576, 17408)
+    assert fp8q.fp8q_proj_quant_fused(1168, 17408)          # 158848 groups
+    assert fp8q.fp8q_proj_quant_fused(4576, 6144)           # 219648 groups
+    assert fp8q.fp8q_proj_quant_fused(13107, 5120)          # 524280 groups
+    assert not fp8q.fp8q_proj_quant_fused(13108, 5120)      # 524320 groups
+    assert not fp8q.fp8q_proj_quant_fused(4576, 17408)      # 622336 groups
 
 
 def test_rowscaled_and_dequant_validation():

@@ -324,9 +324,9 @@ def test_gemm_rowmajor_scales_fail(orc):
         assert rel > 10 * RTOL and exc > 10
 
 
-# a shape past the fused-quantizer limit (1000 * 17408/128 = 136000 scale
-# groups > 2^17), so fp8q_proj runs the quantizer and the relayout separately
-_PROJ_SPLIT = synth.Workload("proj_split", 1000, 17408, 256, "laplace", 87, 50.0)
+# a shape past the fused-quantizer limit (3900 * 17408/128 = 530400 scale
+# groups > 2^19), so fp8q_proj runs the quantizer and the relayout separately
+_PROJ_SPLIT = synth.Workload("proj_split", 3900, 17408, 256, "laplace", 87, 50.0)
 
 
 @pytest.mark.parametrize("name,M", [("tiny", None), ("decode", 16), ("decode", 17), ("decode", 25),

@@ -95,8 +95,11 @@ def test_quant_gemm_workload_activations(orc, name):
 
 
 @pytest.mark.parametrize("M,K", [(1, 128), (1, 5120), (2, 384), (17, 640), (25, 6144), (33, 17408),
-                                 (255, 1152)])
+                                 (255, 1152), (1011, 17280)])
 def test_quant_ragged(orc, M, K):
+    """Ragged token counts and K; (1011, 17280) is past 2^17 groups, where the
+    K-major output takes the tiled form: 135 groups a row (not a multiple of
+    its 8-group tiles) and 13 pad slots that span two of its 8-row tiles."""
     rng = np.random.default_rng(M * 1000 + K)
     x = synth.f32_to_bf16_bits((rng.standard_normal((M, K)) *
                                 np.exp(rng.uniform(-20, 20, (M, 1)))).astype(np.float32))

@@ -160,11 +160,11 @@ def test_gemm_rowscaled_exact_cases(orc):
         assert np.array_equal(_gemm_row_gpu(orc, a, a_s, wq, s_row, kern), ref), kern
 
 
-@pytest.mark.parametrize("M,K", [(25, 5120), (1000, 17408)])
+@pytest.mark.parametrize("M,K", [(25, 5120), (3900, 17408)])
 def test_proj_rowscaled_end_to_end(orc, M, K):
     N = 256
     x, a, a_s, wq, s_row = _row_operands(orc, M, N, K, seed=M + K, dist="laplace")
-    assert fp8q.fp8q_proj_quant_fused(M, K) == (M * (K // 128) <= 1 << 17)
+    assert fp8q.fp8q_proj_quant_fused(M, K) == (M * (K // 128) <= 1 << 19)
     ref = orc.gemm_ref(a, a_s, wq, s_row)
     out = Guarded((M, N), torch.int16)
     aq = Guarded((M, K), torch.uint8)

@@ -236,11 +236,15 @@ fp8q_status run_quant(const char* fn, const uint16_t* x, uint8_t* q, float* srm,
 constexpr uint32_t kSkinnyAutoMaxM = 64;
 constexpr uint32_t kSkinnyWideMaxM = 128;
 constexpr uint32_t kSkinnyWideMaxN = 8192;
-// fp8q_proj writes the K-major scales from the quantizer itself (one launch
-// fewer) up to this many scale groups; beyond it the quantizer's scattered
-// K-major stores cost more than the separate relayout launch (measured:
-// 8.5 vs 16.5 us at M*K/128 = 46720, 69 vs 56 us at 622336).
-constexpr uint64_t kFusedKmajorMaxGroups = 1u << 17;
+// fp8q_proj writes the K-major scales from the quantizer itself (its tiled
+// form, one launch fewer) up to this many scale groups.  Back to back over
+// rotating inputs, quantizer + relayout -> tiled quantizer: 7.7 -> 5.9 us at
+// M = 1168, K = 5120; 15.2 -> 13.0 at M = 1168, K = 17408; 16.4 -> 14.6 /
+// 18.6 -> 16.7 at M = 4576, K = 5120 / 6144.  Beyond it the two are within
+// 1% (42.1 / 41.7 us at M = 4576, K = 17408; 138.8 / 138.9 at M = 16384,
+// K = 17408) and the row-major quantizer alone runs 8% faster than the
+// tiled one there (38.6 against 41.7 us), so the separate relayout stays.
+constexpr uint64_t kFusedKmajorMaxGroups = 1u << 19;
 constexpr uint32_t kTailRuleMinM = 512;
 
 int gemm_auto_kernel(uint32_t M, uint32_t N, uint32_t cus) {

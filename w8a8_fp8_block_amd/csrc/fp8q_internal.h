@@ -19,6 +19,14 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 // kQuantAWaves waves per workgroup.
 constexpr uint32_t kQuantAWaves = 4;
 constexpr uint32_t kQuantAGroupsPerWg = 8 * kQuantAWaves;
+// Its form with the K-major scales beyond kQuantTileMinGroups groups:
+// workgroups of kQuantTileRows waves, each covering kQuantTileRows token
+// rows x kQuantTileGroups groups (wave v: row v of the tile, one group per 8
+// lanes).  Up to that many groups the flat order writes the K-major scales
+// itself (back to back: 2.55-3.02 us at M = 16 / 25 against 2.55-3.18 for
+// the tiles, 5.31 / 6.41 against 5.57 / 6.94 at M = 1168, K = 5120 / 6144).
+constexpr uint32_t kQuantTileRows = 8, kQuantTileGroups = 8;
+constexpr uint64_t kQuantTileMinGroups = 1u << 17;
 // Variant B: K-grouped; a workgroup covers kQuantBGroupsPerWg consecutive
 // groups of one token row, kQuantBRounds groups per 16-lane row.
 constexpr uint32_t kQuantBWaves = 4;

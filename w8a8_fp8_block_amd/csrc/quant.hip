@@ -49,18 +49,15 @@ __device__ __forceinline__ void write_scales(float s, uint64_t g, float* __restr
   }
 }
 
-// Variant A (fine-grained): flat over groups; 8 lanes per group, lane l
-// holding elements 8l..8l+7 and 64+8l..64+8l+7 (each of the two loads covers
-// the group's 256 bytes contiguously across its 8 lanes).  Against 16 lanes
-// of 8 values this halves the per-group work per value (butterfly, scale,
-// reciprocal, addresses) at the same bytes in flight per lane.  The codes,
-// which nothing reads back soon, are stored non-temporally.
-__global__ __launch_bounds__(64 * kQuantAWaves) void quant_a_kernel(
-    const u32x4* __restrict__ x, u32x2* __restrict__ q, float* __restrict__ srm,
-    float* __restrict__ skm, uint64_t ngroups, uint32_t M, uint32_t G, uint32_t Mp) {
-  const uint64_t g = (uint64_t)blockIdx.x * kQuantAGroupsPerWg + (threadIdx.x >> 3);
-  const uint32_t l = threadIdx.x & 7;
-  if (g >= ngroups) return;  // uniform over the group's 8 lanes
+// Variant A (fine-grained): 8 lanes per group, lane l holding elements
+// 8l..8l+7 and 64+8l..64+8l+7 (each of the two loads covers the group's 256
+// bytes contiguously across its 8 lanes).  Against 16 lanes of 8 values this
+// halves the per-group work per value (butterfly, scale, reciprocal,
+// addresses) at the same bytes in flight per lane.  The codes, which nothing
+// reads back soon, are stored non-temporally.  Quantizes group g (this
+// lane's share) and returns its scale.
+__device__ __forceinline__ float quant_group_a(const u32x4* __restrict__ x, u32x2* __restrict__ q,
+                                               uint64_t g, uint32_t l) {
   const u32x4 v0 = __builtin_nontemporal_load(&x[g * 16 + l]);
   const u32x4 v1 = __builtin_nontemporal_load(&x[g * 16 + 8 + l]);
   const uint32_t mag = 0x7FFF7FFFu;
@@ -80,7 +77,55 @@ __global__ __launch_bounds__(64 * kQuantAWaves) void quant_a_kernel(
   quotients<16>(xv, s, qv);
   __builtin_nontemporal_store(u32x2{encode4(qv), encode4(qv + 4)}, &q[g * 16 + l]);
   __builtin_nontemporal_store(u32x2{encode4(qv + 8), encode4(qv + 12)}, &q[g * 16 + 8 + l]);
+  return s;
+}
+
+// Flat over the M*(K/128) groups, kQuantAGroupsPerWg consecutive groups per
+// workgroup; the K-major scales too where skm is given (4-byte stores
+// strided by Mp, cheap up to kQuantTileMinGroups groups).
+__global__ __launch_bounds__(64 * kQuantAWaves) void quant_a_kernel(
+    const u32x4* __restrict__ x, u32x2* __restrict__ q, float* __restrict__ srm,
+    float* __restrict__ skm, uint64_t ngroups, uint32_t M, uint32_t G, uint32_t Mp) {
+  const uint64_t g = (uint64_t)blockIdx.x * kQuantAGroupsPerWg + (threadIdx.x >> 3);
+  const uint32_t l = threadIdx.x & 7;
+  if (g >= ngroups) return;  // uniform over the group's 8 lanes
+  const float s = quant_group_a(x, q, g, l);
   if (l == 0) write_scales(s, g, srm, skm, M, G, Mp);
+}
+
+// With the K-major scales beyond kQuantTileMinGroups groups: the same
+// per-group work, the groups dealt in
+// tiles of kQuantTileRows token rows x kQuantTileGroups groups, one tile per
+// workgroup, wave v taking row m0 + v (8 consecutive groups: 2 KB of
+// contiguous input, as in the flat order).  The tile's 64 scales meet in
+// LDS, and two waves store them: row-major as 8 runs of 8 and K-major as 8
+// runs of 8, each run one whole 32-byte sector.  (Without the staging one
+// of the layouts is written 4 bytes at a time from different waves: 2.6-6%
+// slower than the row-major quantizer plus the separate relayout from
+// M = 4576, K = 17408 on.)  The row tiles run to Mp = ceil16(M), so that
+// the K-major pad slots M .. Mp-1 are written (+0.0) by the same stores.
+__global__ __launch_bounds__(64 * kQuantTileRows) void quant_a_tile_kernel(
+    const u32x4* __restrict__ x, u32x2* __restrict__ q, float* __restrict__ srm,
+    float* __restrict__ skm, uint32_t M, uint32_t G, uint32_t Mp, uint32_t gtiles) {
+  __shared__ float ts[kQuantTileRows][kQuantTileGroups];
+  const uint32_t wave = threadIdx.x >> 6, lane = threadIdx.x & 63, l = lane & 7;
+  const uint32_t m0 = (blockIdx.x / gtiles) * kQuantTileRows;
+  const uint32_t g0 = (blockIdx.x % gtiles) * kQuantTileGroups;
+  {
+    const uint32_t m = m0 + wave, gg = g0 + (lane >> 3);
+    if (m < M && gg < G) {  // uniform over the group's 8 lanes
+      const float s = quant_group_a(x, q, (uint64_t)m * G + gg, l);
+      if (l == 0) ts[wave][lane >> 3] = s;
+    }
+  }
+  __syncthreads();
+  if (wave == 0 && srm) {
+    const uint32_t r = lane >> 3, c = lane & 7, m = m0 + r, gg = g0 + c;
+    if (m < M && gg < G) srm[(uint64_t)m * G + gg] = ts[r][c];
+  } else if (wave == 1) {
+    const uint32_t c = lane >> 3, r = lane & 7, m = m0 + r, gg = g0 + c;
+    if (m < Mp && gg < G) skm[(uint64_t)gg * Mp + m] = m < M ? ts[r][c] : 0.0f;
+  }
 }
 
 // Variant B (K-grouped): workgroup (m, by) covers groups
@@ -117,6 +162,14 @@ hipError_t launch_quant_a(const uint16_t* x, uint8_t* q, float* scale_rm, float*
                           uint32_t M, uint32_t K, hipStream_t s) {
   const uint32_t G = K / kGroup;
   const uint64_t ngroups = (uint64_t)M * G;
+  if (scale_km && ngroups > kQuantTileMinGroups) {
+    const uint32_t gtiles = (G + kQuantTileGroups - 1) / kQuantTileGroups;
+    const uint64_t grid = (uint64_t)((m_pad16(M) + kQuantTileRows - 1) / kQuantTileRows) * gtiles;
+    quant_a_tile_kernel<<<dim3((uint32_t)grid), dim3(64 * kQuantTileRows), 0, s>>>(
+        reinterpret_cast<const u32x4*>(x), reinterpret_cast<u32x2*>(q), scale_rm, scale_km, M, G,
+        m_pad16(M), gtiles);
+    return hipGetLastError();
+  }
   const uint64_t grid = (ngroups + kQuantAGroupsPerWg - 1) / kQuantAGroupsPerWg;
   quant_a_kernel<<<dim3((uint32_t)grid), dim3(64 * kQuantAWaves), 0, s>>>(
       reinterpret_cast<const u32x4*>(x), reinterpret_cast<u32x2*>(q), scale_rm, scale_km,
