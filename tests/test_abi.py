@@ -359,6 +359,13 @@ def test_splitk_select():
     for M, want in ((16, 1), (23, 1), (24, 3), (33, 3), (64, 3), (65, 3), (128, 3), (129, 1)):
         assert sel(M, 17408, 5120) == want, M   # skinny ranges too wide: the tiled count from 24 rows
     assert sel(25, 6144, 8192) == 4        # 96 columns a workgroup
+    # on 128 CUs: fewer workgroups a split, so fewer splits keep the ranges
+    # within 96 / 64 columns; the decode kernel's slices no longer fit LDS
+    s128 = lambda M, N, K: fp8q.fp8q_gemm_splitk_select(M, N, K, 128)
+    assert s128(16, 5120, 17408) == 2      # 64 workgroups of 80 columns
+    assert s128(48, 5120, 17408) == 3      # no skinny count fits 64 columns: the tiled count
+    assert s128(16, 6144, 5120) == 2       # 48 columns a CU exceed the decode kernel's 32
+    assert s128(4, 5120, 17408) == 1
     assert sel(300, 128, 2560) == 2        # K/1280 = 2 caps it
     assert sel(300, 128, 2432) == 1        # fewer than 20 K blocks: no split
     assert sel(4576, 5120, 17408) == 1     # the 256x128 kernel's pick: no split
