@@ -8,11 +8,12 @@ cover, for the first: one and two 16-row tiles (M = 3, 16, 20, 25, 32),
 ranges of one and of one and a half 16-column tiles, ranges of unequal width
 (N = 5248: 1312 four-column units over the workgroups), K ending in a
 partial 1 KB row piece (K = 1280, 2176); for the second: up to 64 rows and
-wider ranges (N = 10240 .. 32768), and beyond 64 rows (M = 100: two 64-row
-tiles, 64 columns a workgroup); between them every wave count the skinny
-kernel takes (8 waves at two and four row tiles with up to eight column
-tiles where their partial sums fit in 128 KB, 4 beyond).  Both weight-scale
-formats throughout.
+wider ranges (N = 10240 .. 32768), 48-row tiles (M = 40, 45: three 16-row
+tiles), and beyond 64 rows (M = 100: two 64-row tiles, 64 columns a
+workgroup); between them every wave count the skinny kernel takes (8 waves
+at two, three and four row tiles with up to eight column tiles where their
+partial sums fit in 128 KB, 4 beyond: M = 45, N = 17408).  Both
+weight-scale formats throughout.
 """
 import numpy as np
 import pytest
@@ -58,7 +59,8 @@ def _run(orc, a, a_s, wq, ws, per_row):
 
 CASES = [(3, 6144, 1280), (16, 5248, 2048), (32, 6144, 3072), (17, 4096, 5120),
          (25, 6144, 5120), (25, 17408, 1152), (64, 6144, 5120), (16, 32768, 512),
-         (40, 10240, 2176), (64, 20480, 384), (25, 28672, 1024), (100, 6144, 2048)]
+         (40, 10240, 2176), (64, 20480, 384), (25, 28672, 1024), (100, 6144, 2048),
+         (45, 17408, 5120)]
 
 
 @pytest.mark.parametrize("per_row", [False, True], ids=["block", "row"])

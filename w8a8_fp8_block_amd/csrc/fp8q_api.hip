@@ -280,8 +280,8 @@ int gemm_auto_kernel(uint32_t M, uint32_t N, uint32_t cus) {
 // tiled split form with the count of the rule above.  Fixed on back-to-back
 // launches over rotating weight copies (bench.py --gemm-sweep-b2b, 256 CUs,
 // us single-pass -> split): N = 5120, K = 17408: 24.7 -> 24.5 (4 splits) at
-// M = 8, 27.4 -> 25.2 at 16, 35.4 -> 27.3 at 32, 41.1 -> 33.0 (3 splits) at
-// 33, 51.5 -> 36.1 at 64, while at M <= 4 the single pass was 0.5-1.2 us
+// M = 8, 27.4 -> 25.2 at 16, 35.4 -> 27.3 at 32, 36.7 -> 30.3 (3 splits) at
+// 33 (48-row tiles), 51.4 -> 36.2 at 64, while at M <= 4 the single pass was 0.5-1.2 us
 // ahead and 6 splits (124 columns) 1-2 us behind 4; N = 17408, K = 5120
 // (tiled, 3 splits): 26.5 -> 24.8 at M = 24, 34.6 -> 26.4 at 33, 37.1 ->
 // 29.8 at 64, 0.2-1.4 us behind at M <= 16; N = 6144, K = 5120: 2 splits
@@ -465,8 +465,8 @@ fp8q_status run_proj(const char* fn, const uint16_t* x_bf16, const uint8_t* w_e4
 // ---- dense FFN ----
 // fp8q_ffn's automatic choice: the fused gate/up kernel (one pass over both
 // weight matrices, no bf16 gate/up round trip through HBM) from 65 rows on;
-// up to 64, the separate path, whose skinny GEMMs (16-, 32- and 64-row
-// tiles) stream the weights with one workgroup per CU.  Measured on the
+// up to 64, the separate path, whose skinny GEMMs (16-, 32-, 48- and
+// 64-row tiles) stream the weights with one workgroup per CU.  Measured on the
 // whole call at H=5120, I=17408 with the last-level cache flushed before
 // each call (the weights of one layer are not resident in serving):
 // separate 89.5 vs fused 114.9 us at M=16, 106.6 vs 121.0 at M=32, 119.4

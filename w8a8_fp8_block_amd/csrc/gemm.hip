@@ -1725,8 +1725,14 @@ constexpr int skinny_unroll(int tm, int tn) {
   return uf > 8 ? 8 : uf < 1 ? 1 : uf;
 }
 // the template arguments the skinny dispatch picks: row tiles TM of 16 rows,
-// column tiles TN of 16 columns
-uint32_t skinny_tm(uint32_t M) { return M <= 16 ? 1 : M <= 32 ? 2 : 4; }
+// column tiles TN of 16 columns.  TM = 3 for 33-48 rows: against TM = 4 it
+// leaves the registers for two K blocks in flight at TN = 4 (one at TM =
+// 4) and loads a quarter fewer activation fragments; back to back over
+// rotating weights, M = 33 / 48: single pass 41.1 / 46.4 -> 36.7 / 42.9 us
+// at N = 5120, K = 17408 (3 splits 33.0 / 35.0 -> 30.3 / 32.8), 34.6 / 35.9
+// -> 31.8 / 33.4 at N = 17408, K = 5120, 16.3 / 17.8 -> 15.2 / 16.9 at
+// N = 6144, K = 5120.
+uint32_t skinny_tm(uint32_t M) { return M <= 16 ? 1 : M <= 32 ? 2 : M <= 48 ? 3 : 4; }
 uint32_t skinny_tn(uint32_t tn) { return tn <= 2 ? 2 : tn <= 4 ? 4 : tn <= 6 ? 6 : 8; }
 
 template <int TM, int TN, bool ROW, bool SPLIT = false>
@@ -1816,6 +1822,7 @@ hipError_t launch_gemm_skinny_t(const uint8_t* a, const float* a_s_km, const uin
   switch ((M + 15) / 16) {
     case 1: return launch_skinny_tm<1, ROW>(a, a_s_km, w, w_s, out, M, N, K, grid, base, rem, tn, s);
     case 2: return launch_skinny_tm<2, ROW>(a, a_s_km, w, w_s, out, M, N, K, grid, base, rem, tn, s);
+    case 3: return launch_skinny_tm<3, ROW>(a, a_s_km, w, w_s, out, M, N, K, grid, base, rem, tn, s);
     default: return launch_skinny_tm<4, ROW>(a, a_s_km, w, w_s, out, M, N, K, grid, base, rem, tn, s);
   }
 }
@@ -1869,6 +1876,7 @@ bool launch_skinny_split(const uint8_t* a, const float* a_s_km, const uint8_t* w
   switch ((M + 15) / 16) {
     case 1: err = launch_skinny_tm<1, false, true>(a, a_s_km, w, w_s, nullptr, M, N, K, grid, base, rem, tn, s, splits, part); break;
     case 2: err = launch_skinny_tm<2, false, true>(a, a_s_km, w, w_s, nullptr, M, N, K, grid, base, rem, tn, s, splits, part); break;
+    case 3: err = launch_skinny_tm<3, false, true>(a, a_s_km, w, w_s, nullptr, M, N, K, grid, base, rem, tn, s, splits, part); break;
     default: err = launch_skinny_tm<4, false, true>(a, a_s_km, w, w_s, nullptr, M, N, K, grid, base, rem, tn, s, splits, part); break;
   }
   if (err != hipSuccess) return true;
