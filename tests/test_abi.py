@@ -388,6 +388,21 @@ def test_splitk_select_follows_the_cu_count():
     assert sel(65, 5120, 17408, 0) == 0
 
 
+def test_splitk_select_small_m_is_total():
+    """Up to 64 rows, over odd and extreme CU counts: the automatic count is
+    1 or lies in [2, min(K/1280, 6)], and no shape splits below 8 rows."""
+    sel = fp8q.fp8q_gemm_splitk_select
+    for cus in (1, 7, 32, 128, 256, 304, 1024):
+        for N in (128, 1024, 5120, 6144, 17408, 28672):
+            for K in (1280, 5120, 17408):
+                cap = min(K // 1280, 6)
+                for M in range(1, 65):
+                    s = sel(M, N, K, cus)
+                    assert s == 1 or 2 <= s <= cap, (M, N, K, cus, s)
+                    if M < 8:
+                        assert s == 1, (M, N, K, cus, s)
+
+
 def test_ffn_workspace_holds_split_partials():
     H, I = 5120, 17408
     for M in (300, 512, 1168):
