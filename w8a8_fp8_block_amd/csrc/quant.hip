@@ -99,10 +99,11 @@ __global__ __launch_bounds__(64 * kQuantAWaves) void quant_a_kernel(
 // workgroup, wave v taking row m0 + v (8 consecutive groups: 2 KB of
 // contiguous input, as in the flat order).  The tile's 64 scales meet in
 // LDS, and two waves store them: row-major as 8 runs of 8 and K-major as 8
-// runs of 8, each run one whole 32-byte sector.  (Without the staging one
-// of the layouts is written 4 bytes at a time from different waves: 2.6-6%
-// slower than the row-major quantizer plus the separate relayout from
-// M = 4576, K = 17408 on.)  The row tiles run to Mp = ceil16(M), so that
+// runs of 8, each run one whole 32-byte sector.  (Tiles without the
+// staging, each wave taking one group column of the 8 rows, wrote the
+// row-major scales 4 bytes at a time from different waves: 6-9% slower
+// than the row-major quantizer plus the separate relayout from M = 4576,
+// K = 17408 on.)  The row tiles run to Mp = ceil16(M), so that
 // the K-major pad slots M .. Mp-1 are written (+0.0) by the same stores.
 __global__ __launch_bounds__(64 * kQuantTileRows) void quant_a_tile_kernel(
     const u32x4* __restrict__ x, u32x2* __restrict__ q, float* __restrict__ srm,
