@@ -223,7 +223,7 @@ int fp8q_gemm_select(uint32_t M, uint32_t N, uint32_t K);
 const char *fp8q_gemm_kernel_name(uint32_t M, uint32_t N, uint32_t K, int kernel);
 
 /* As fp8q_gemm_blockscaled with the kernel forced: 0 = auto (2 for
- * M <= 64 and for M <= 128 when N <= 8192, 1 below 512 rows; from 512 rows
+ * M <= 64 and for M <= 128 when N <= 8192, 1 below 129 rows; from 129 rows
  * on 5 or 1, whichever needs fewer rounds of workgroups on the device's CUs
  * when a last round of at most one 128x128 workgroup per CU counts as half a
  * round; 5 on a tie), 1 =

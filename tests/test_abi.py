@@ -116,7 +116,7 @@ def test_gemm_validation():
 
 def test_gemm_select():
     """Auto GEMM choice: skinny kernel up to 64 rows (and up to 128 rows when
-    N <= 8192), 128x128 tiles below 512 rows; from 512 rows on the kernel with
+    N <= 8192), 128x128 tiles below 129 rows; from 129 rows on the kernel with
     fewer rounds of workgroups on 256 CUs (ping-pong: tiles of 256x128 in
     rounds of 256; 128x128: workgroups in rounds of 512, a last round of at
     most 256 counting half), ties to the ping-pong kernel; bad N/K -> -1 (pure
@@ -127,8 +127,9 @@ def test_gemm_select():
                     (512, 1), (768, 1), (1024, 5), (1168, 5), (1536, 5), (2047, 1), (2048, 1),
                     (3072, 5), (4576, 5), (16384, 5)):
         assert sel(M, 5120, 17408, 256) == want, M
-    for M, want in ((64, 2), (65, 1), (128, 1), (640, 1), (768, 5), (1024, 1), (1168, 5),
-                    (1536, 1), (2048, 1), (3072, 1), (4576, 5)):
+    for M, want in ((64, 2), (65, 1), (128, 1), (129, 5), (192, 5), (256, 5), (320, 1), (384, 1),
+                    (448, 1), (511, 1), (640, 1), (768, 5), (1024, 1), (1168, 5), (1536, 1), (2048, 1),
+                    (3072, 1), (4576, 5)):
         assert sel(M, 17408, 5120, 256) == want, M
     for M, want in ((768, 5), (1024, 5), (1168, 5), (1536, 1), (2048, 1), (3072, 1), (4576, 1)):
         assert sel(M, 6144, 5120, 256) == want, M
@@ -140,7 +141,7 @@ def test_gemm_select():
 
 
 def _rounds_rule(M, N, cus):
-    """The documented round-count rule from 512 rows on, in half rounds."""
+    """The documented round-count rule from 129 rows on, in half rounds."""
     nt = N // 128
     t_pp, t_128 = (M + 255) // 256 * nt, (M + 127) // 128 * nt
     c_pp = 2 * -(-t_pp // cus)
@@ -165,11 +166,11 @@ def test_gemm_select_follows_the_cu_count():
     assert sel(640, 17408, 5120, 32) == 1
     for cus in (32, 80, 128, 200, 256, 304):
         for N in (5120, 6144, 17408):
-            for M in (512, 640, 1000, 1168, 2048, 3000, 4576, 9999):
+            for M in (129, 200, 256, 300, 512, 640, 1000, 1168, 2048, 3000, 4576, 9999):
                 assert sel(M, N, 5120, cus) == _rounds_rule(M, N, cus), (M, N, cus)
     # below the round rule's range the CU count does not matter
     for cus in (32, 256):
-        assert sel(64, 5120, 17408, cus) == 2 and sel(300, 17408, 5120, cus) == 1
+        assert sel(64, 5120, 17408, cus) == 2 and sel(100, 17408, 5120, cus) == 1
 
 
 def test_selectors_default_to_a_full_device_without_one():

@@ -222,7 +222,7 @@ fp8q_status run_quant(const char* fn, const uint16_t* x, uint8_t* q, float* srm,
 // N = 5120: 88 / 90 / 92 us at M = 80 / 128 / 192 against 112-134 /
 // 117-146 / 134 us for the tiled kernels; at N = 6144, K = 5120: 32-34 us
 // against 41-52 us up to M = 128, no gain beyond); 128 x 128 tiles (two
-// workgroups per CU) below kTailRuleMinM rows.  From there on the choice
+// workgroups per CU) below kRoundRuleMinM rows.  From there on the choice
 // between them and the ping-pong 256 x 128 kernel (one workgroup per CU, a
 // few percent faster per full round) follows the last, partial round of
 // workgroups on the device's CUs: a ping-pong round costs one unit whether
@@ -232,7 +232,14 @@ fp8q_status run_quant(const char* fn, const uint16_t* x, uint8_t* q, float* srm,
 // go to the ping-pong kernel.  Back-to-back launches on one box at N = 17408
 // and 6144 (K = 5120) and N = 5120 (K = 17408), M = 640 .. 4576: the rule
 // picks the faster kernel at all 22 shapes, by 3-12% (M = 1168, N = 5120:
-// 108 vs 124 us; N = 6144, M = 4576: 128 x 128 tiles, 159 vs 164 us).
+// 108 vs 124 us; N = 6144, M = 4576: 128 x 128 tiles, 159 vs 164 us).  From
+// 129 rows to 511 (same method, M = 129 / 192 / 256 / 320 / 384 / 448 /
+// 511) it picks the faster one at all 7 at N = 17408 (the ping-pong kernel
+// to 256 rows, one round of 136 tiles: 39.2 / 45.2 / 51.7 against 46.5 /
+// 52.2 / 60.3 us), and the 128 x 128 kernel, as before, at N = 5120 and
+// 6144, where the ping-pong kernel was 4-12% faster at M = 129, 320 and 384
+// (a half-full ping-pong round against a light 128 x 128 one); those shapes
+// take split-K where a workspace is at hand.
 constexpr uint32_t kSkinnyAutoMaxM = 64;
 constexpr uint32_t kSkinnyWideMaxM = 128;
 constexpr uint32_t kSkinnyWideMaxN = 8192;
@@ -245,11 +252,12 @@ constexpr uint32_t kSkinnyWideMaxN = 8192;
 // K = 17408) and the row-major quantizer alone runs 8% faster than the
 // tiled one there (38.6 against 41.7 us), so the separate relayout stays.
 constexpr uint64_t kFusedKmajorMaxGroups = 1u << 19;
-constexpr uint32_t kTailRuleMinM = 512;
+constexpr uint32_t kTailRuleMinM = 512;  // the stream-K form from here
+constexpr uint32_t kRoundRuleMinM = 129;
 
 int gemm_auto_kernel(uint32_t M, uint32_t N, uint32_t cus) {
   if (M <= kSkinnyAutoMaxM || (M <= kSkinnyWideMaxM && N <= kSkinnyWideMaxN)) return 2;
-  if (M < kTailRuleMinM) return 1;
+  if (M < kRoundRuleMinM) return 1;
   const uint64_t c = cus ? cus : 1;
   const uint64_t nt = N / kGroup;
   const uint64_t t_pp = (M + 255) / 256 * nt, t_128 = (M + 127) / 128 * nt;
